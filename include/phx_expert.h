@@ -1,0 +1,174 @@
+/*
+ * phx_expert.h -- C ABI of a flow-matching action-expert decision on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * One decision integrates S flow-matching Euler steps of an NL-layer
+ * decoder over M action rows per request.  Every layer's action rows attend
+ * to a prefix key/value cache that is written once and read by every step,
+ * and to the action rows themselves.  Sources, cited by page title and
+ * section:
+ *   - "FlashRT-PAI: Fast Kernels Are Not Fast Pipelines for Physical AI
+ *     Inference": section 2.1 (Figure 1a: the pi0.5 decision, a prefix of
+ *     about 500 to 800 tokens writing its K/V, an 18-layer expert over ten
+ *     action rows and ten flow steps; a deployment fixes views, context
+ *     bucket, action horizon and step count), section 3.4 and Appendix A.1
+ *     (static buffers, swap windows and state regions at fixed addresses; a
+ *     versioned C interface with shape and plan checks; the caller owns
+ *     input freshness), section 3.2 (fused producers: residual + norm,
+ *     RoPE with the QKV split and cache write, GeGLU in the GEMM epilogue).
+ *   - "PhyAI" paper, section 4.2 (Graph replay: the prefix K/V, the
+ *     timestep table and every layer's AdaRMS modulation table are prepared
+ *     before denoising and the whole step loop is replayed as one graph;
+ *     Kernel fusion: one QKV GEMM, merged gate/up with GeGLU, AdaRMSNorm).
+ *
+ * Ownership.  The library owns every device allocation it makes and frees it
+ * in phx_expert_destroy.  Pointers passed in stay owned by the caller and must
+ * stay valid until the given stream has passed the call.  Calls on one handle
+ * must not overlap: the handle keeps one working set.
+ *
+ * Errors.  Every int-returning call returns PHX_OK (0) or a negative PHX_E_*
+ * code and leaves a message for phx_last_error() in the calling thread.  On
+ * error the handle is unchanged.  Nothing throws across this boundary.
+ */
+#ifndef PHX_EXPERT_H
+#define PHX_EXPERT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PHX_ABI_VERSION 1u
+
+/* return codes */
+#define PHX_OK 0
+#define PHX_E_INVALID (-1)     /* NULL pointer or a bad argument value */
+#define PHX_E_VERSION (-2)     /* abi_version or struct_size does not match this library */
+#define PHX_E_SHAPE (-3)       /* outside the prepared plan: prefix_len > capacity, bad request index,
+                                  or a shape this build does not support */
+#define PHX_E_STATE (-4)       /* a prerequisite is missing: decide before every request has a prefix */
+#define PHX_E_NOMEM (-5)       /* device allocation failed */
+#define PHX_E_HIP (-6)         /* a HIP runtime call failed; the message names it */
+
+/* element types of weights and prefix K/V */
+#define PHX_DTYPE_F32 0
+#define PHX_DTYPE_BF16 1
+
+/* execution flags */
+#define PHX_FLAG_NO_GRAPH 1u   /* launch the step loop's kernels directly instead of replaying the
+                                  captured graph (same kernels, same results; for diagnosis) */
+
+/* A HIP stream (hipStream_t is a pointer to this incomplete type). NULL means
+   the default stream. */
+typedef struct ihipStream_t* phx_stream_t;
+
+/*
+ * Deployment shape, fixed for the life of a handle.  Notation of the pages'
+ * pi0.5 shape in brackets.
+ */
+typedef struct phx_expert_config {
+  uint32_t abi_version;      /* PHX_ABI_VERSION */
+  uint32_t struct_size;      /* sizeof(phx_expert_config) */
+  int32_t layers;            /* NL decoder layers [18] */
+  int32_t width;             /* D residual width [1024]; multiple of 32 */
+  int32_t n_heads;           /* H query heads [8] */
+  int32_t head_dim;          /* Dh [256]; multiple of 16, at most 256 */
+  int32_t n_kv_heads;        /* KVH key/value heads [1: multi-query]; divides H */
+  int32_t mlp_hidden;        /* F GeGLU hidden width [4096]; multiple of 32 */
+  int32_t state_dim;         /* A action dimension [32]; multiple of 32 */
+  int32_t rows;              /* M action rows per request [10] */
+  int32_t batch;             /* B requests per decision; B*M <= 160 */
+  int32_t prefix_capacity;   /* C context bucket: most prefix rows a request may load [768] */
+  int32_t steps;             /* S Euler steps [10] */
+  int32_t time_emb_dim;      /* E sinusoidal time-embedding width [1024]; multiple of 32 */
+  float tau0;                /* flow time of the first step [1.0] */
+  float dt;                  /* Euler step [-0.1]: tau_k = tau0 + k*dt, x += dt*v */
+  float rms_eps;             /* [1e-6], inside the square root */
+  float rope_base;           /* [10000] */
+  int32_t weight_dtype;      /* PHX_DTYPE_F32 or PHX_DTYPE_BF16 */
+  int32_t kv_dtype;          /* must equal weight_dtype */
+  uint32_t flags;            /* PHX_FLAG_* */
+} phx_expert_config;
+
+typedef struct phx_expert phx_expert;
+
+/*
+ * Checks a configuration without touching the GPU (pure host code).
+ * Returns PHX_OK, PHX_E_INVALID (NULL), PHX_E_VERSION or PHX_E_SHAPE.
+ */
+int phx_expert_validate_config(const phx_expert_config* cfg);
+
+/*
+ * Size in bytes of the weight blob phx_expert_create expects for cfg.
+ * The blob is one contiguous array of weight_dtype elements; every matrix is
+ * [in][out] row-major (a projection is y = x . W):
+ *   W_in   [A][D]
+ *   for each layer: W_qkv [D][(H+2*KVH)*Dh]  (q heads, then k heads, then v heads)
+ *                   W_o   [H*Dh][D]
+ *                   W_gu  [D][2F]            (gate g = first F columns, up u = last F)
+ *                   W_down[F][D]
+ *   W_out  [D][A]
+ *   W_mod  [2*NL+1][E][2D]  (norm 2l precedes attention in layer l, 2l+1 the MLP,
+ *                            2*NL the velocity head; first D outputs scale, last D shift)
+ * There are no biases.
+ */
+int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes);
+
+/*
+ * Builds a handle: allocates its device arenas, copies and re-tiles the
+ * weights into the layout its kernels stream, builds the step-conditioning
+ * table (sinusoidal embedding of every tau_k and all 2*NL+1 modulation
+ * projections, kept for the life of the handle), and captures the step loop
+ * as one HIP graph.
+ *   weights: host or device pointer to weights_bytes bytes in the layout
+ *            above; the caller may free it once the call returns.
+ *   stream:  stream the set-up work is ordered on; the call returns after it
+ *            has finished.
+ * Returns PHX_OK, PHX_E_INVALID, PHX_E_VERSION, PHX_E_SHAPE, PHX_E_NOMEM or
+ * PHX_E_HIP.  *out is set only on success.
+ */
+int phx_expert_create(const phx_expert_config* cfg, const void* weights, size_t weights_bytes,
+                      phx_stream_t stream, phx_expert** out);
+
+/*
+ * Loads (replaces) the prefix context of one request: the prefix keys and
+ * values every layer attends to, already rotary-encoded as the prefix model
+ * wrote them.
+ *   request:    0 <= request < batch.
+ *   k, v:       device pointers, [layers][prefix_len][n_kv_heads*head_dim] of
+ *               kv_dtype; copied into the handle's state region (V is stored
+ *               transposed).  May be NULL when prefix_len == 0.
+ *   prefix_len: 0 <= prefix_len <= prefix_capacity; the request's action rows
+ *               sit at positions prefix_len .. prefix_len+rows-1.
+ * Asynchronous on stream.  Returns PHX_OK, PHX_E_INVALID, PHX_E_SHAPE or
+ * PHX_E_HIP.
+ */
+int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, const void* v,
+                              int32_t prefix_len, phx_stream_t stream);
+
+/*
+ * One decision: x = noise; S Euler steps of the expert; actions = x.
+ *   noise, actions: device pointers to float32 [batch][rows][state_dim]
+ *                   (they may be the same buffer).
+ * Stream-ordered and asynchronous: copy in, graph replay, copy out.  The
+ * caller synchronizes.  Returns PHX_OK, PHX_E_INVALID, PHX_E_STATE (a
+ * request has no loaded prefix) or PHX_E_HIP.
+ */
+int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_stream_t stream);
+
+/* Frees every device allocation of the handle. NULL-safe. Synchronizes the
+   handle's internal stream first. */
+void phx_expert_destroy(phx_expert* h);
+
+/* Message of the last failing call in this thread ("" if none). */
+const char* phx_last_error(void);
+
+/* Number of kernel launches one decision replays (graph nodes). */
+int phx_expert_kernels_per_decision(const phx_expert* h, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

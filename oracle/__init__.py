@@ -1,0 +1,211 @@
+"""CPU oracle for one flow-matching action-expert decision (double precision).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never imports, links or calls it, and it
+imports nothing from the product.
+
+The arithmetic lives in ``oracle.c`` (plain C, fixed-order loops, OpenMP only
+across independent outputs); this module builds it with gcc and marshals
+numpy arrays through ctypes.  Every function cites, in ``oracle.c``, the
+passage of the pages it follows.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(library routines, closed forms, invariants, a tiny brute-force composition
+and a mutation sweep); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (-O3, no fast-math, OpenMP)."""
+    cmd = ["gcc", "-O3", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC", "-I", _HERE, "-o", out, src, "-lm"]
+    subprocess.check_call(cmd)
+    return out
+
+
+class OrcConfig(ctypes.Structure):
+    _fields_ = [
+        ("layers", ctypes.c_int), ("width", ctypes.c_int), ("n_heads", ctypes.c_int),
+        ("head_dim", ctypes.c_int), ("n_kv_heads", ctypes.c_int), ("mlp_hidden", ctypes.c_int),
+        ("state_dim", ctypes.c_int), ("rows", ctypes.c_int), ("batch", ctypes.c_int),
+        ("capacity", ctypes.c_int), ("steps", ctypes.c_int), ("time_emb_dim", ctypes.c_int),
+        ("tau0", ctypes.c_double), ("dt", ctypes.c_double), ("rms_eps", ctypes.c_double),
+        ("rope_base", ctypes.c_double),
+    ]
+
+
+_DP = ctypes.POINTER(ctypes.c_double)
+_FP = ctypes.POINTER(ctypes.c_float)
+_IP = ctypes.POINTER(ctypes.c_int)
+
+
+def load(path: str = LIB_PATH):
+    """Load (building first if absent) and return the ctypes library."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        build(out=path)
+    lib = ctypes.CDLL(path)
+    lib.orc_weight_count.argtypes = [ctypes.POINTER(OrcConfig)]
+    lib.orc_weight_count.restype = ctypes.c_size_t
+    lib.orc_time_embedding.argtypes = [ctypes.c_int, ctypes.c_double, _DP]
+    lib.orc_modulation.argtypes = [ctypes.c_int, ctypes.c_int, _FP, _DP, _DP]
+    lib.orc_ada_rmsnorm.argtypes = [ctypes.c_int, ctypes.c_int, _DP, _DP, ctypes.c_double, _DP]
+    lib.orc_matmul.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _DP, _FP, _DP]
+    lib.orc_rope.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _IP, ctypes.c_double, _DP]
+    lib.orc_gelu_tanh.argtypes = [ctypes.c_double]
+    lib.orc_gelu_tanh.restype = ctypes.c_double
+    lib.orc_attention.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  _DP, _DP, _DP, _FP, _FP, ctypes.c_size_t, _DP]
+    lib.orc_attention.restype = ctypes.c_double
+    lib.orc_decide.argtypes = [ctypes.POINTER(OrcConfig), _FP, _FP, _FP, _IP, _FP, _DP, _DP, _DP]
+    lib.orc_decide.restype = ctypes.c_int
+    lib.orc_last_softmax_dev.restype = ctypes.c_double
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _d(a):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(_DP)
+
+
+def _f(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data_as(_FP)
+
+
+def make_config(cfg: dict) -> OrcConfig:
+    return OrcConfig(
+        layers=cfg["layers"], width=cfg["width"], n_heads=cfg["n_heads"], head_dim=cfg["head_dim"],
+        n_kv_heads=cfg["n_kv_heads"], mlp_hidden=cfg["mlp_hidden"], state_dim=cfg["state_dim"],
+        rows=cfg["rows"], batch=cfg["batch"], capacity=cfg["capacity"], steps=cfg["steps"],
+        time_emb_dim=cfg["time_emb_dim"], tau0=cfg["tau0"], dt=cfg["dt"], rms_eps=cfg["rms_eps"],
+        rope_base=cfg["rope_base"])
+
+
+def weight_count(cfg: dict, lib=None) -> int:
+    lib = lib or load()
+    c = make_config(cfg)
+    return int(lib.orc_weight_count(ctypes.byref(c)))
+
+
+def time_embedding(E: int, tau: float, lib=None) -> np.ndarray:
+    lib = lib or load()
+    out = np.zeros(E, dtype=np.float64)
+    lib.orc_time_embedding(E, tau, out.ctypes.data_as(_DP))
+    return out
+
+
+def modulation(e: np.ndarray, W_mod_n: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    E, D2 = W_mod_n.shape
+    out = np.zeros(D2, dtype=np.float64)
+    e, pe = _d(e)
+    W, pW = _f(W_mod_n)
+    lib.orc_modulation(E, D2 // 2, pW, pe, out.ctypes.data_as(_DP))
+    return out
+
+
+def ada_rmsnorm(h: np.ndarray, mod: np.ndarray, eps: float, lib=None) -> np.ndarray:
+    lib = lib or load()
+    M, D = h.shape
+    out = np.zeros((M, D), dtype=np.float64)
+    h, ph = _d(h)
+    mod, pm = _d(mod)
+    lib.orc_ada_rmsnorm(M, D, ph, pm, eps, out.ctypes.data_as(_DP))
+    return out
+
+
+def matmul(x: np.ndarray, W: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    M, K = x.shape
+    K2, N = W.shape
+    assert K == K2
+    out = np.zeros((M, N), dtype=np.float64)
+    x, px = _d(x)
+    W, pW = _f(W)
+    lib.orc_matmul(M, K, N, px, pW, out.ctypes.data_as(_DP))
+    return out
+
+
+def rope(x: np.ndarray, n_heads: int, head_dim: int, pos, base: float, lib=None) -> np.ndarray:
+    lib = lib or load()
+    M = x.shape[0]
+    y = np.array(x, dtype=np.float64, order="C", copy=True).reshape(M, n_heads * head_dim)
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    lib.orc_rope(M, n_heads, head_dim, p.ctypes.data_as(_IP), base, y.ctypes.data_as(_DP))
+    return y.reshape(x.shape)
+
+
+def gelu_tanh(z) -> np.ndarray:
+    lib = load()
+    z = np.asarray(z, dtype=np.float64)
+    return np.vectorize(lambda v: lib.orc_gelu_tanh(float(v)))(z) if z.ndim else lib.orc_gelu_tanh(float(z))
+
+
+def attention(q, ka, va, Kp, Vp, n_heads: int, n_kv_heads: int, head_dim: int, lib=None):
+    """q [M][H*Dh], ka/va [M][KVH*Dh] (float64), Kp/Vp [L][KVH*Dh] float32.
+    Returns (o [M][H*Dh], largest |sum p - 1|)."""
+    lib = lib or load()
+    M = q.shape[0]
+    L = Kp.shape[0]
+    q, pq = _d(q)
+    ka, pka = _d(ka)
+    va, pva = _d(va)
+    if L == 0:  # no prefix rows: pass a dummy row that is never read
+        Kp = Vp = np.zeros((1, n_kv_heads * head_dim), np.float32)
+    Kp, pK = _f(Kp)
+    Vp, pV = _f(Vp)
+    o = np.zeros((M, n_heads * head_dim), dtype=np.float64)
+    dev = lib.orc_attention(M, n_heads, n_kv_heads, head_dim, L, pq, pka, pva, pK, pV,
+                            n_kv_heads * head_dim, o.ctypes.data_as(_DP))
+    return o, dev
+
+
+def decide(cfg: dict, weights: np.ndarray, kv_k, kv_v, lens, noise, trace: bool = False,
+           velocity: bool = False, lib=None) -> dict:
+    """Run one decision.  weights: float32 blob in the documented order.
+    kv_k/kv_v: float32 [B][NL][C][KVH*Dh] (may be None when C == 0).
+    Returns {"actions": [B][M][A] float64, "trace": ..., "velocity": ...,
+    "softmax_dev": float}."""
+    lib = lib or load()
+    c = make_config(cfg)
+    n_w = int(lib.orc_weight_count(ctypes.byref(c)))
+    weights, pw = _f(weights)
+    if weights.size != n_w:
+        raise ValueError(f"weight blob has {weights.size} values, expected {n_w}")
+    B, M, A, NL, D, S = cfg["batch"], cfg["rows"], cfg["state_dim"], cfg["layers"], cfg["width"], cfg["steps"]
+    if kv_k is not None:
+        kv_k, pk = _f(kv_k)
+        kv_v, pv = _f(kv_v)
+    else:
+        pk = pv = None
+    lens_a = np.ascontiguousarray(lens, dtype=np.int32)
+    noise, pn = _f(noise)
+    actions = np.zeros((B, M, A), dtype=np.float64)
+    tr = np.zeros((S, NL + 1, B * M, D), dtype=np.float64) if trace else None
+    vel = np.zeros((S, B * M, A), dtype=np.float64) if velocity else None
+    rc = lib.orc_decide(ctypes.byref(c), pw, pk, pv, lens_a.ctypes.data_as(_IP), pn,
+                        actions.ctypes.data_as(_DP),
+                        tr.ctypes.data_as(_DP) if tr is not None else None,
+                        vel.ctypes.data_as(_DP) if vel is not None else None)
+    if rc != 0:
+        raise ValueError(f"orc_decide rejected its arguments (rc={rc})")
+    return {"actions": actions, "trace": tr, "velocity": vel, "softmax_dev": lib.orc_last_softmax_dev()}

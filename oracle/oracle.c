@@ -1,0 +1,292 @@
+/*
+ * oracle.c -- plain double-precision CPU reference for one decision of a
+ * pi0.5-style flow-matching action expert.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h): the HIP library never links or
+ * calls this file, and this file includes nothing from the library.
+ *
+ * The steps follow the pages in their order:
+ *   - a prefix key/value cache written once and read by every denoising step,
+ *     an action expert of NL layers over M action rows, integrated over S
+ *     flow-matching Euler steps ("FlashRT-PAI", section 2.1, Figure 1a;
+ *     "PhyAI", section 4.2 Graph replay);
+ *   - the sinusoidal timestep table and each norm's adaptive-RMSNorm
+ *     modulation built once per step index, 2*NL+1 projections
+ *     ("Introducing PhyAI", How we optimize PI0.5 and GR00T; "FlashRT-PAI",
+ *     Figure 3 caption);
+ *   - per layer: adaptive RMSNorm, one Q/K/V projection, RoPE on Q and K,
+ *     attention of the action rows to the prefix and to themselves
+ *     (head_dim 256 in the pages' shape), output projection + residual,
+ *     adaptive RMSNorm, merged gate/up projection, GeGLU, down projection +
+ *     residual ("PhyAI", section 4.2 Kernel fusion and Profiled operator
+ *     selection; "FlashRT-PAI", section 3.2);
+ *   - a final adaptive RMSNorm, the velocity projection and x += dt * v.
+ *
+ * Where the pages are silent the readings are: no biases; modulation gives
+ * (scale, shift) with y*(1+scale)+shift; eps inside the square root;
+ * rotate-half RoPE pairing j with j+Dh/2, theta_j = base^(-2j/Dh), action row
+ * i at position L+i, prefix keys stored already rotated; the softmax scale is
+ * 1/sqrt(Dh); GELU in its tanh form; the time embedding is [sin | cos] with
+ * frequencies 10000^(-j/(E/2)).
+ *
+ * Everything is double precision.  Loops run in a fixed order; OpenMP only
+ * splits independent outputs, so results do not depend on the thread count.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double g_last_softmax_dev = 0.0;
+
+double orc_last_softmax_dev(void) { return g_last_softmax_dev; }
+
+size_t orc_weight_count(const orc_config* c) {
+  size_t D = (size_t)c->width, A = (size_t)c->state_dim, F = (size_t)c->mlp_hidden;
+  size_t qkv = (size_t)(c->n_heads + 2 * c->n_kv_heads) * (size_t)c->head_dim;
+  size_t hd = (size_t)c->n_heads * (size_t)c->head_dim;
+  size_t per_layer = D * qkv + hd * D + D * 2 * F + F * D;
+  size_t norms = 2 * (size_t)c->layers + 1;
+  return A * D + (size_t)c->layers * per_layer + D * A + norms * (size_t)c->time_emb_dim * 2 * D;
+}
+
+void orc_time_embedding(int E, double tau, double* e) {
+  int half = E / 2;
+  for (int j = 0; j < half; ++j) {
+    double w = pow(10000.0, -(double)j / (double)half);
+    e[j] = sin(tau * w);
+    e[half + j] = cos(tau * w);
+  }
+}
+
+void orc_modulation(int E, int D, const float* Wmod_n, const double* e, double* mod) {
+  int n2 = 2 * D;
+#pragma omp parallel for schedule(static)
+  for (int c = 0; c < n2; ++c) {
+    double s = 0.0;
+    for (int j = 0; j < E; ++j) s += e[j] * (double)Wmod_n[(size_t)j * n2 + c];
+    mod[c] = s;
+  }
+}
+
+void orc_ada_rmsnorm(int M, int D, const double* h, const double* mod, double eps, double* out) {
+  const double* scale = mod;
+  const double* shift = mod + D;
+  for (int m = 0; m < M; ++m) {
+    const double* y = h + (size_t)m * D;
+    double ss = 0.0;
+    for (int d = 0; d < D; ++d) ss += y[d] * y[d];
+    double r = 1.0 / sqrt(ss / (double)D + eps);
+    for (int d = 0; d < D; ++d) out[(size_t)m * D + d] = y[d] * r * (1.0 + scale[d]) + shift[d];
+  }
+}
+
+void orc_matmul(int M, int K, int N, const double* x, const float* W, double* y) {
+  /* Independent output columns are split into blocks across threads; each
+   * output still sums k = 0..K-1 in order. */
+  const int blk = 64;
+  int nblk = (N + blk - 1) / blk;
+#pragma omp parallel for schedule(static)
+  for (int b = 0; b < nblk; ++b) {
+    int n0 = b * blk, n1 = n0 + blk < N ? n0 + blk : N;
+    for (int m = 0; m < M; ++m) {
+      double* yr = y + (size_t)m * N;
+      for (int n = n0; n < n1; ++n) yr[n] = 0.0;
+      for (int k = 0; k < K; ++k) {
+        double xv = x[(size_t)m * K + k];
+        const float* wr = W + (size_t)k * N;
+        for (int n = n0; n < n1; ++n) yr[n] += xv * (double)wr[n];
+      }
+    }
+  }
+}
+
+void orc_rope(int M, int nh, int Dh, const int* pos, double base, double* x) {
+  int half = Dh / 2;
+  for (int m = 0; m < M; ++m) {
+    for (int j = 0; j < half; ++j) {
+      double theta = pow(base, -2.0 * (double)j / (double)Dh);
+      double ang = (double)pos[m] * theta;
+      double c = cos(ang), s = sin(ang);
+      for (int hh = 0; hh < nh; ++hh) {
+        double* v = x + (size_t)m * nh * Dh + (size_t)hh * Dh;
+        double a = v[j], b = v[j + half];
+        v[j] = a * c - b * s;
+        v[j + half] = b * c + a * s;
+      }
+    }
+  }
+}
+
+double orc_gelu_tanh(double z) {
+  const double k = sqrt(2.0 / M_PI);
+  return 0.5 * z * (1.0 + tanh(k * (z + 0.044715 * z * z * z)));
+}
+
+double orc_attention(int M, int H, int KVH, int Dh, int L, const double* q, const double* ka, const double* va,
+                     const float* Kp, const float* Vp, size_t kv_stride, double* o) {
+  int T = L + M;
+  int group = H / KVH;
+  int kvd = KVH * Dh;
+  double scale = 1.0 / sqrt((double)Dh);
+  double worst = 0.0;
+#pragma omp parallel for schedule(static) reduction(max : worst)
+  for (int mh = 0; mh < M * H; ++mh) {
+    int m = mh / H, hh = mh % H, g = hh / group;
+    const double* qv = q + (size_t)m * H * Dh + (size_t)hh * Dh;
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    /* logits q.k / sqrt(Dh) over prefix keys then action keys */
+    for (int t = 0; t < T; ++t) {
+      double s = 0.0;
+      if (t < L) {
+        const float* kr = Kp + (size_t)t * kv_stride + (size_t)g * Dh;
+        for (int d = 0; d < Dh; ++d) s += qv[d] * (double)kr[d];
+      } else {
+        const double* kr = ka + (size_t)(t - L) * kvd + (size_t)g * Dh;
+        for (int d = 0; d < Dh; ++d) s += qv[d] * kr[d];
+      }
+      logit[t] = s * scale;
+    }
+    /* softmax (max subtracted) */
+    double mx = -INFINITY;
+    for (int t = 0; t < T; ++t) if (logit[t] > mx) mx = logit[t];
+    double den = 0.0;
+    for (int t = 0; t < T; ++t) { logit[t] = exp(logit[t] - mx); den += logit[t]; }
+    double psum = 0.0;
+    for (int t = 0; t < T; ++t) { logit[t] /= den; psum += logit[t]; }
+    double dev = fabs(psum - 1.0);
+    if (dev > worst) worst = dev;
+    /* o = sum_t p_t v_t */
+    double* ov = o + (size_t)m * H * Dh + (size_t)hh * Dh;
+    for (int d = 0; d < Dh; ++d) ov[d] = 0.0;
+    for (int t = 0; t < T; ++t) {
+      double p = logit[t];
+      if (t < L) {
+        const float* vr = Vp + (size_t)t * kv_stride + (size_t)g * Dh;
+        for (int d = 0; d < Dh; ++d) ov[d] += p * (double)vr[d];
+      } else {
+        const double* vr = va + (size_t)(t - L) * kvd + (size_t)g * Dh;
+        for (int d = 0; d < Dh; ++d) ov[d] += p * vr[d];
+      }
+    }
+    free(logit);
+  }
+  return worst;
+}
+
+static int check_cfg(const orc_config* c) {
+  if (!c) return -1;
+  if (c->layers < 0 || c->width <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || (c->head_dim & 1)) return -1;
+  if (c->n_kv_heads <= 0 || c->n_heads % c->n_kv_heads) return -1;
+  if (c->mlp_hidden <= 0 || c->state_dim <= 0 || c->rows <= 0 || c->batch <= 0 || c->capacity < 0) return -1;
+  if (c->steps < 0 || c->time_emb_dim <= 0 || (c->time_emb_dim & 1)) return -1;
+  return 0;
+}
+
+int orc_decide(const orc_config* c, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
+               const float* noise, double* actions, double* trace, double* velocity) {
+  if (check_cfg(c) || !weights || !noise || !actions || !lens) return -1;
+  const int NL = c->layers, D = c->width, H = c->n_heads, Dh = c->head_dim, KVH = c->n_kv_heads;
+  const int F = c->mlp_hidden, A = c->state_dim, M = c->rows, B = c->batch, C = c->capacity, S = c->steps;
+  const int E = c->time_emb_dim;
+  const int BM = B * M;
+  const int hd = H * Dh, kvd = KVH * Dh, nqkv = hd + 2 * kvd;
+  for (int b = 0; b < B; ++b)
+    if (lens[b] < 0 || lens[b] > C) return -1;
+  if (C > 0 && (!kv_k || !kv_v)) return -1;
+
+  /* weight offsets, in the documented blob order */
+  const float* W_in = weights;
+  size_t off = (size_t)A * D;
+  size_t per_layer = (size_t)D * nqkv + (size_t)hd * D + (size_t)D * 2 * F + (size_t)F * D;
+  const float* layer0 = weights + off;
+  off += (size_t)NL * per_layer;
+  const float* W_out = weights + off;
+  off += (size_t)D * A;
+  const float* W_mod = weights + off;
+  const int n_norm = 2 * NL + 1;
+
+  double* x = (double*)malloc(sizeof(double) * (size_t)BM * A);
+  double* h = (double*)malloc(sizeof(double) * (size_t)BM * D);
+  double* n = (double*)malloc(sizeof(double) * (size_t)BM * D);
+  double* qkv = (double*)malloc(sizeof(double) * (size_t)BM * nqkv);
+  double* q = (double*)malloc(sizeof(double) * (size_t)M * hd);
+  double* ka = (double*)malloc(sizeof(double) * (size_t)M * kvd);
+  double* va = (double*)malloc(sizeof(double) * (size_t)M * kvd);
+  double* o = (double*)malloc(sizeof(double) * (size_t)BM * hd);
+  double* proj = (double*)malloc(sizeof(double) * (size_t)BM * (D > A ? D : A));
+  double* gu = (double*)malloc(sizeof(double) * (size_t)BM * 2 * F);
+  double* act = (double*)malloc(sizeof(double) * (size_t)BM * F);
+  double* e = (double*)malloc(sizeof(double) * (size_t)E);
+  double* mod = (double*)malloc(sizeof(double) * (size_t)n_norm * 2 * D);
+  int* pos = (int*)malloc(sizeof(int) * (size_t)M);
+  double worst = 0.0;
+
+  for (int i = 0; i < BM * A; ++i) x[i] = (double)noise[i];
+
+  for (int k = 0; k < S; ++k) {
+    /* step conditioning: depends only on the step index */
+    double tau = c->tau0 + (double)k * c->dt;
+    orc_time_embedding(E, tau, e);
+    for (int nn = 0; nn < n_norm; ++nn)
+      orc_modulation(E, D, W_mod + (size_t)nn * E * 2 * D, e, mod + (size_t)nn * 2 * D);
+
+    /* input projection */
+    orc_matmul(BM, A, D, x, W_in, h);
+    if (trace) memcpy(trace + ((size_t)k * (NL + 1)) * BM * D, h, sizeof(double) * (size_t)BM * D);
+
+    for (int l = 0; l < NL; ++l) {
+      const float* W_qkv = layer0 + (size_t)l * per_layer;
+      const float* W_o = W_qkv + (size_t)D * nqkv;
+      const float* W_gu = W_o + (size_t)hd * D;
+      const float* W_down = W_gu + (size_t)D * 2 * F;
+
+      /* attention block */
+      orc_ada_rmsnorm(BM, D, h, mod + (size_t)(2 * l) * 2 * D, c->rms_eps, n);
+      orc_matmul(BM, D, nqkv, n, W_qkv, qkv);
+      for (int b = 0; b < B; ++b) {
+        int L = lens[b];
+        for (int m = 0; m < M; ++m) {
+          const double* src = qkv + (size_t)(b * M + m) * nqkv;
+          memcpy(q + (size_t)m * hd, src, sizeof(double) * hd);
+          memcpy(ka + (size_t)m * kvd, src + hd, sizeof(double) * kvd);
+          memcpy(va + (size_t)m * kvd, src + hd + kvd, sizeof(double) * kvd);
+          pos[m] = L + m;
+        }
+        orc_rope(M, H, Dh, pos, c->rope_base, q);
+        orc_rope(M, KVH, Dh, pos, c->rope_base, ka);
+        const float* Kp = kv_k ? kv_k + ((size_t)b * NL + l) * (size_t)C * kvd : NULL;
+        const float* Vp = kv_v ? kv_v + ((size_t)b * NL + l) * (size_t)C * kvd : NULL;
+        double dev = orc_attention(M, H, KVH, Dh, L, q, ka, va, Kp, Vp, (size_t)kvd, o + (size_t)b * M * hd);
+        if (dev > worst) worst = dev;
+      }
+      orc_matmul(BM, hd, D, o, W_o, proj);
+      for (int i = 0; i < BM * D; ++i) h[i] += proj[i];
+
+      /* MLP block */
+      orc_ada_rmsnorm(BM, D, h, mod + (size_t)(2 * l + 1) * 2 * D, c->rms_eps, n);
+      orc_matmul(BM, D, 2 * F, n, W_gu, gu);
+      for (int r = 0; r < BM; ++r)
+        for (int f = 0; f < F; ++f) {
+          double g = gu[(size_t)r * 2 * F + f], u = gu[(size_t)r * 2 * F + F + f];
+          act[(size_t)r * F + f] = orc_gelu_tanh(g) * u;
+        }
+      orc_matmul(BM, F, D, act, W_down, proj);
+      for (int i = 0; i < BM * D; ++i) h[i] += proj[i];
+      if (trace) memcpy(trace + ((size_t)k * (NL + 1) + l + 1) * BM * D, h, sizeof(double) * (size_t)BM * D);
+    }
+
+    /* velocity head and Euler update */
+    orc_ada_rmsnorm(BM, D, h, mod + (size_t)(2 * NL) * 2 * D, c->rms_eps, n);
+    orc_matmul(BM, D, A, n, W_out, proj);
+    if (velocity) memcpy(velocity + (size_t)k * BM * A, proj, sizeof(double) * (size_t)BM * A);
+    for (int i = 0; i < BM * A; ++i) x[i] += c->dt * proj[i];
+  }
+
+  for (int i = 0; i < BM * A; ++i) actions[i] = x[i];
+  g_last_softmax_dev = worst;
+  free(x); free(h); free(n); free(qkv); free(q); free(ka); free(va); free(o); free(proj);
+  free(gu); free(act); free(e); free(mod); free(pos);
+  return 0;
+}

@@ -1,0 +1,109 @@
+/*
+ * oracle.h -- plain, slow CPU reference for one flow-matching action-expert
+ * decision, in double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this code: only the tests, the package smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code with the HIP
+ * library; the two agree only on the documented input formats.
+ *
+ * Sources (the pages this follows, cited by title and section):
+ *   [PhyAI]   "PhyAI" paper, section 4.2 (Kernel fusion; Graph replay;
+ *             Profiled operator selection).
+ *   [Blog]    "Introducing PhyAI: Real-Time Physical AI at the Edge, Scalable
+ *             Rollouts in the Cloud", section "How we optimize PI0.5 and GR00T".
+ *   [FlashRT] "FlashRT-PAI: Fast Kernels Are Not Fast Pipelines for Physical
+ *             AI Inference", section 2.1 (Figure 1a), section 3.2 (fusion),
+ *             Figure 3 caption (37 modulation projections), Appendix A.1.
+ *
+ * Weight blob (all float32, values as the caller stored them; every matrix is
+ * [in][out] row-major, so a projection is y = x . W):
+ *   W_in   [A][D]
+ *   per layer l = 0..NL-1:
+ *     W_qkv  [D][(H + 2*KVH)*Dh]   output columns: q heads, then k heads, then v heads
+ *     W_o    [H*Dh][D]
+ *     W_gu   [D][2F]               first F columns are the gate g, last F the up u
+ *     W_down [F][D]
+ *   W_out  [D][A]
+ *   W_mod  [2*NL+1][E][2D]         norm n: first D outputs scale, last D shift;
+ *                                  norm 2l before attention, 2l+1 before the MLP,
+ *                                  2*NL the final norm.
+ * Prefix K/V (float32): [B][NL][C][KVH*Dh]; request b uses rows t < len[b].
+ * Noise / actions: [B][M][A].
+ */
+#ifndef PHX_ORACLE_H
+#define PHX_ORACLE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct orc_config {
+  int layers;       /* NL */
+  int width;        /* D  */
+  int n_heads;      /* H  */
+  int head_dim;     /* Dh (even) */
+  int n_kv_heads;   /* KVH, divides H */
+  int mlp_hidden;   /* F  */
+  int state_dim;    /* A  */
+  int rows;         /* M: action rows per request */
+  int batch;        /* B  */
+  int capacity;     /* C: prefix rows stored per request and layer */
+  int steps;        /* S  */
+  int time_emb_dim; /* E (even) */
+  double tau0;      /* flow time of the first step */
+  double dt;        /* Euler step (negative: tau runs from 1 towards 0) */
+  double rms_eps;
+  double rope_base;
+} orc_config;
+
+/* Number of float32 values in the weight blob for cfg. */
+size_t orc_weight_count(const orc_config* cfg);
+
+/* e[j] = sin(tau*w_j), e[E/2+j] = cos(tau*w_j), w_j = 10000^(-j/(E/2)). */
+void orc_time_embedding(int E, double tau, double* e);
+
+/* mod[c] = sum_j e[j] * Wmod_n[j][c] for c < 2D (scale | shift). */
+void orc_modulation(int E, int D, const float* Wmod_n, const double* e, double* mod);
+
+/* out[m][d] = h[m][d] / sqrt(mean_d h[m][.]^2 + eps) * (1 + scale[d]) + shift[d]. */
+void orc_ada_rmsnorm(int M, int D, const double* h, const double* mod, double eps, double* out);
+
+/* y[m][n] = sum_k x[m][k] * W[k][n], k summed in increasing order. */
+void orc_matmul(int M, int K, int N, const double* x, const float* W, double* y);
+
+/* Rotate-half RoPE in place on x[M][nh*Dh]; row m sits at position pos[m]. */
+void orc_rope(int M, int nh, int Dh, const int* pos, double base, double* x);
+
+/* tanh-form GELU. */
+double orc_gelu_tanh(double z);
+
+/*
+ * Attention of one request: M query rows, H query heads sharing KVH key/value
+ * heads.  Keys are the L prefix rows (Kp/Vp [L][KVH*Dh], stride kv_stride
+ * floats between rows) followed by the M action rows ka/va [M][KVH*Dh]; every
+ * query row sees all L+M keys.  o [M][H*Dh].  Returns the largest
+ * |sum(p) - 1| over all softmax rows.
+ */
+double orc_attention(int M, int H, int KVH, int Dh, int L, const double* q, const double* ka, const double* va,
+                     const float* Kp, const float* Vp, size_t kv_stride, double* o);
+
+/*
+ * One decision.  actions [B][M][A] receives the integrated state.  If
+ * trace is non-NULL it receives the residual stream h after the input
+ * projection and after every layer of every step:
+ * [S][NL+1][B*M][D] doubles.  If velocity is non-NULL it receives v of every
+ * step: [S][B*M][A].  Returns 0, or -1 on a bad argument.
+ */
+int orc_decide(const orc_config* cfg, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
+               const float* noise, double* actions, double* trace, double* velocity);
+
+/* Largest |sum(p) - 1| seen by any softmax row of the last orc_decide call. */
+double orc_last_softmax_dev(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,308 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function takes a loaded oracle library (ctypes handle) and
+raises AssertionError when the oracle disagrees with:
+  * a library routine (numpy matmul, torch rms_norm, torch GELU, torch
+    scaled-dot-product attention, complex multiplication for RoPE);
+  * a closed form or invariant (time embedding at tau = 0, unit pair norms,
+    RoPE relative-position property, softmax rows summing to one, uniform
+    attention when queries vanish, zero velocity head, dt = 0, ...);
+  * a tiny brute-force composition of torch primitives (double precision).
+
+The same battery runs against the real oracle (must pass) and against
+deliberately mutated copies of its source (each must fail at least one pin),
+which shows that a plausible slip anywhere in the oracle is caught.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+import phx_inputs
+
+TIGHT = 1e-10
+
+
+def _close(a, b, tol=TIGHT, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol * scale, f"{what}: max abs err {err:.3e} > {tol * scale:.3e}"
+
+
+# ---------------------------------------------------------------- per-op pins
+
+def pin_time_embedding(lib):
+    E = 16
+    e0 = oracle.time_embedding(E, 0.0, lib)
+    assert np.all(e0[:8] == 0.0) and np.all(e0[8:] == 1.0), "tau=0 must give [0..0 | 1..1]"
+    tau = 0.7
+    e = oracle.time_embedding(E, tau, lib)
+    _close(e[0], math.sin(tau), what="lowest frequency is 1")
+    _close(e[8], math.cos(tau), what="cos half follows sin half")
+    _close(e[:8] ** 2 + e[8:] ** 2, np.ones(8), what="unit pair norm")
+    # recover the frequencies at tiny tau: geometric with ratio 10000^(-1/(E/2))
+    small = 1e-7
+    es = oracle.time_embedding(E, small, lib)
+    w = es[:8] / small
+    _close(w[1:] / w[:-1], np.full(7, 10000.0 ** (-1.0 / 8)), tol=1e-6, what="geometric frequencies")
+    _close(w[0], 1.0, tol=1e-6, what="first frequency")
+
+
+def pin_modulation(lib):
+    g = np.random.default_rng(1)
+    E, D = 32, 12
+    W = g.standard_normal((E, 2 * D)).astype(np.float32)
+    e = g.standard_normal(E)
+    _close(oracle.modulation(e, W, lib), e @ W.astype(np.float64), what="modulation vs numpy")
+
+
+def pin_matmul(lib):
+    g = np.random.default_rng(2)
+    x = g.standard_normal((5, 7))
+    W = g.standard_normal((7, 130)).astype(np.float32)
+    _close(oracle.matmul(x, W, lib), x @ W.astype(np.float64), what="matmul vs numpy")
+
+
+def pin_ada_rmsnorm(lib):
+    g = np.random.default_rng(3)
+    M, D, eps = 4, 24, 1e-3
+    h = g.standard_normal((M, D)) * 3.0
+    mod = g.standard_normal(2 * D)
+    ref = F.rms_norm(torch.tensor(h), (D,), weight=torch.tensor(1.0 + mod[:D]), eps=eps) + torch.tensor(mod[D:])
+    _close(oracle.ada_rmsnorm(h, mod, eps, lib), ref.numpy(), what="AdaRMSNorm vs torch rms_norm")
+    zero = np.zeros(2 * D)
+    ref0 = F.rms_norm(torch.tensor(h), (D,), eps=eps)
+    _close(oracle.ada_rmsnorm(h, zero, eps, lib), ref0.numpy(), what="zero modulation is plain RMSNorm")
+
+
+def pin_rope(lib):
+    g = np.random.default_rng(4)
+    M, nh, Dh, base = 5, 3, 8, 10000.0
+    half = Dh // 2
+    x = g.standard_normal((M, nh * Dh))
+    pos = np.array([0, 1, 7, 100, 12345], dtype=np.int32)
+    y = oracle.rope(x, nh, Dh, pos, base, lib).reshape(M, nh, Dh)
+    xr = x.reshape(M, nh, Dh)
+    z = xr[..., :half] + 1j * xr[..., half:]
+    theta = base ** (-2.0 * np.arange(half) / Dh)
+    zr = z * np.exp(1j * pos[:, None, None] * theta[None, None, :])
+    _close(y[..., :half], zr.real, what="RoPE real part vs complex rotation")
+    _close(y[..., half:], zr.imag, what="RoPE imaginary part vs complex rotation")
+    _close(y[0], xr[0], what="RoPE is the identity at position 0")
+    # relative position: <R(m) q, R(n) k> depends only on m - n
+    q = g.standard_normal((1, Dh))
+    k = g.standard_normal((1, Dh))
+    d1 = oracle.rope(q, 1, Dh, [9], base, lib) @ oracle.rope(k, 1, Dh, [4], base, lib).T
+    d2 = oracle.rope(q, 1, Dh, [25], base, lib) @ oracle.rope(k, 1, Dh, [20], base, lib).T
+    _close(d1, d2, tol=1e-9, what="RoPE relative-position property")
+
+
+def pin_gelu(lib):
+    z = np.linspace(-6, 6, 97)
+    ours = np.array([lib.orc_gelu_tanh(float(v)) for v in z])
+    ref = F.gelu(torch.tensor(z), approximate="tanh").numpy()
+    _close(ours, ref, what="GELU tanh vs torch")
+    erf_ref = F.gelu(torch.tensor(z)).numpy()
+    assert np.max(np.abs(ours - erf_ref)) < 2e-3, "tanh GELU within 2e-3 of erf GELU"
+
+
+def _sdpa(q, ka, va, Kp, Vp, H, KVH, Dh):
+    M = q.shape[0]
+    kfull = np.concatenate([Kp.astype(np.float64), ka], axis=0) if Kp.shape[0] else ka
+    vfull = np.concatenate([Vp.astype(np.float64), va], axis=0) if Vp.shape[0] else va
+    T = kfull.shape[0]
+    group = H // KVH
+    qt = torch.tensor(q.reshape(M, H, Dh)).permute(1, 0, 2)            # [H, M, Dh]
+    kt = torch.tensor(kfull.reshape(T, KVH, Dh)).permute(1, 0, 2)      # [KVH, T, Dh]
+    vt = torch.tensor(vfull.reshape(T, KVH, Dh)).permute(1, 0, 2)
+    kt = kt.repeat_interleave(group, dim=0).contiguous()
+    vt = vt.repeat_interleave(group, dim=0).contiguous()
+    o = F.scaled_dot_product_attention(qt[None], kt[None], vt[None])[0]  # [H, M, Dh]
+    return o.permute(1, 0, 2).reshape(M, H * Dh).numpy()
+
+
+def pin_attention(lib):
+    g = np.random.default_rng(5)
+    for (H, KVH, Dh) in [(2, 1, 4), (4, 2, 8), (8, 1, 16)]:
+        for L in (0, 1, 3, 37):
+            for M in (1, 3, 10):
+                q = g.standard_normal((M, H * Dh)) * 2.0
+                ka = g.standard_normal((M, KVH * Dh))
+                va = g.standard_normal((M, KVH * Dh))
+                Kp = g.standard_normal((L, KVH * Dh)).astype(np.float32)
+                Vp = g.standard_normal((L, KVH * Dh)).astype(np.float32)
+                o, dev = oracle.attention(q, ka, va, Kp, Vp, H, KVH, Dh, lib)
+                _close(o, _sdpa(q, ka, va, Kp, Vp, H, KVH, Dh), tol=1e-9, what=f"attention H{H} KVH{KVH} L{L} M{M}")
+                assert dev < 1e-12, "softmax rows must sum to one"
+    # values identically one give outputs identically one
+    H, KVH, Dh, L, M = 4, 1, 8, 11, 3
+    q = g.standard_normal((M, H * Dh))
+    o, _ = oracle.attention(q, g.standard_normal((M, Dh)), np.ones((M, Dh)),
+                            g.standard_normal((L, Dh)).astype(np.float32), np.ones((L, Dh), np.float32), H, KVH, Dh, lib)
+    _close(o, np.ones_like(o), what="V == 1 gives o == 1")
+    # zero queries: uniform weights, o = mean of all value rows
+    va = g.standard_normal((M, Dh))
+    Vp = g.standard_normal((L, Dh)).astype(np.float32)
+    o, _ = oracle.attention(np.zeros((M, H * Dh)), g.standard_normal((M, Dh)), va,
+                            g.standard_normal((L, Dh)).astype(np.float32), Vp, H, KVH, Dh, lib)
+    mean = np.concatenate([Vp.astype(np.float64), va]).mean(axis=0)
+    _close(o, np.tile(mean, (M, H)), what="q == 0 gives the mean of the values")
+
+
+# ---------------------------------------------------------- whole-decision pins
+
+def tiny_cfg(**kw):
+    cfg = dict(id=97, layers=2, width=8, n_heads=2, head_dim=4, n_kv_heads=1, mlp_hidden=8, state_dim=3,
+               rows=3, batch=2, capacity=5, steps=2, time_emb_dim=8, tau0=1.0, dt=-0.5, rms_eps=1e-6,
+               rope_base=10000.0, dtype="f32", weight_std=0.5, prefix_lens=[0, 5])
+    cfg.update(kw)
+    return cfg
+
+
+def torch_decide(cfg, inp):
+    """Brute force: the decision composed from torch double-precision
+    primitives (sin/cos, matmul, rms_norm, complex rotation, scaled dot
+    product attention, tanh GELU)."""
+    W = inp["weights"]
+    NL, D, H, Dh, KVH = cfg["layers"], cfg["width"], cfg["n_heads"], cfg["head_dim"], cfg["n_kv_heads"]
+    F_, A, M, B, S, E = cfg["mlp_hidden"], cfg["state_dim"], cfg["rows"], cfg["batch"], cfg["steps"], cfg["time_emb_dim"]
+    t = lambda name: torch.tensor(phx_inputs.view(W, cfg, name).astype(np.float64))
+    Wmod = t("W_mod")
+    x = torch.tensor(inp["noise"].astype(np.float64)).reshape(B * M, A)
+    half = Dh // 2
+    theta = torch.pow(torch.tensor(cfg["rope_base"], dtype=torch.float64), -2.0 * torch.arange(half, dtype=torch.float64) / Dh)
+    freqs = torch.pow(torch.tensor(10000.0, dtype=torch.float64), -torch.arange(E // 2, dtype=torch.float64) / (E // 2))
+
+    def rot(v, pos, nh):
+        v = v.reshape(-1, nh, Dh)
+        z = torch.complex(v[..., :half], v[..., half:])
+        ang = pos[:, None, None].to(torch.float64) * theta[None, None, :]
+        z = z * torch.polar(torch.ones_like(ang), ang)
+        return torch.cat([z.real, z.imag], dim=-1).reshape(-1, nh * Dh)
+
+    def norm(hh, m):
+        return F.rms_norm(hh, (D,), weight=1.0 + m[:D], eps=cfg["rms_eps"]) + m[D:]
+
+    for k in range(S):
+        tau = cfg["tau0"] + k * cfg["dt"]
+        e = torch.cat([torch.sin(tau * freqs), torch.cos(tau * freqs)])
+        mods = [e @ Wmod[n] for n in range(2 * NL + 1)]
+        h = x @ t("W_in")
+        for l in range(NL):
+            n1 = norm(h, mods[2 * l])
+            qkv = n1 @ t(f"W_qkv.{l}")
+            o_all = []
+            for b in range(B):
+                L = int(inp["lens"][b])
+                rows = slice(b * M, (b + 1) * M)
+                pos = torch.arange(L, L + M)
+                q = rot(qkv[rows, :H * Dh], pos, H)
+                ka = rot(qkv[rows, H * Dh:(H + KVH) * Dh], pos, KVH)
+                va = qkv[rows, (H + KVH) * Dh:]
+                Kp = torch.tensor(inp["kv_k"][b, l, :L].astype(np.float64))
+                Vp = torch.tensor(inp["kv_v"][b, l, :L].astype(np.float64))
+                kf = torch.cat([Kp, ka]).reshape(L + M, KVH, Dh).permute(1, 0, 2).repeat_interleave(H // KVH, 0)
+                vf = torch.cat([Vp, va]).reshape(L + M, KVH, Dh).permute(1, 0, 2).repeat_interleave(H // KVH, 0)
+                qh = q.reshape(M, H, Dh).permute(1, 0, 2)
+                o = F.scaled_dot_product_attention(qh[None], kf.contiguous()[None], vf.contiguous()[None])[0]
+                o_all.append(o.permute(1, 0, 2).reshape(M, H * Dh))
+            h = h + torch.cat(o_all) @ t(f"W_o.{l}")
+            n2 = norm(h, mods[2 * l + 1])
+            gu = n2 @ t(f"W_gu.{l}")
+            h = h + (F.gelu(gu[:, :F_], approximate="tanh") * gu[:, F_:]) @ t(f"W_down.{l}")
+        v = norm(h, mods[2 * NL]) @ t("W_out")
+        x = x + cfg["dt"] * v
+    return x.reshape(B, M, A).numpy()
+
+
+def _run(cfg, inp, lib, **kw):
+    return oracle.decide(cfg, inp["weights"], inp["kv_k"], inp["kv_v"], inp["lens"], inp["noise"], lib=lib, **kw)
+
+
+def pin_decide_brute_force(lib):
+    for kw in [dict(), dict(n_heads=4, n_kv_heads=2, prefix_lens=[3, 1]), dict(batch=1, prefix_lens=[5], steps=1),
+               dict(rows=1, prefix_lens=[2, 0]), dict(layers=1, steps=3, dt=-1.0 / 3)]:
+        cfg = tiny_cfg(**kw)
+        inp = phx_inputs.make_inputs(cfg, seed=3)
+        out = _run(cfg, inp, lib)
+        _close(out["actions"], torch_decide(cfg, inp), tol=1e-9, what=f"decision vs torch composition {kw}")
+        assert out["softmax_dev"] < 1e-12
+
+
+def pin_decide_invariants(lib):
+    cfg = tiny_cfg()
+    inp = phx_inputs.make_inputs(cfg, seed=4)
+    base = _run(cfg, inp, lib, velocity=True)
+    # zero velocity head: actions are the noise, bit for bit
+    w0 = inp["weights"].copy()
+    phx_inputs.view(w0, cfg, "W_out")[:] = 0.0
+    out = _run(cfg, dict(inp, weights=w0), lib)
+    assert np.array_equal(out["actions"], inp["noise"].astype(np.float64)), "W_out == 0 must return the noise"
+    # dt == 0 leaves the state unchanged
+    out = _run(dict(cfg, dt=0.0), inp, lib)
+    assert np.array_equal(out["actions"], inp["noise"].astype(np.float64)), "dt == 0 must return the noise"
+    # one step: x1 = x0 + dt * v(x0, tau0), v reported by the same run
+    one = _run(dict(cfg, steps=1), inp, lib, velocity=True)
+    _close(one["actions"].reshape(-1, cfg["state_dim"]),
+           inp["noise"].reshape(-1, cfg["state_dim"]) + cfg["dt"] * one["velocity"][0], what="single Euler step")
+    _close(one["velocity"][0], base["velocity"][0], what="first-step velocity independent of step count")
+    # zero up-projection: the MLP adds nothing, same as a zero down-projection
+    wu = inp["weights"].copy()
+    wd = inp["weights"].copy()
+    for l in range(cfg["layers"]):
+        phx_inputs.view(wu, cfg, f"W_gu.{l}")[:, cfg["mlp_hidden"]:] = 0.0
+        phx_inputs.view(wd, cfg, f"W_down.{l}")[:] = 0.0
+    _close(_run(cfg, dict(inp, weights=wu), lib)["actions"], _run(cfg, dict(inp, weights=wd), lib)["actions"],
+           what="zero up-projection == zero down-projection")
+    # poison beyond the prefix length is never read
+    kp = inp["kv_k"].copy()
+    vp = inp["kv_v"].copy()
+    for b, L in enumerate(inp["lens"]):
+        kp[b, :, L:] = np.nan
+        vp[b, :, L:] = 1e30
+    out = _run(cfg, dict(inp, kv_k=kp, kv_v=vp), lib)
+    assert np.array_equal(out["actions"], base["actions"]), "rows past the prefix length must not matter"
+    # requests are independent: request 1 alone equals request 1 in the batch
+    one_cfg = dict(cfg, batch=1, prefix_lens=[int(inp["lens"][1])])
+    single = dict(weights=inp["weights"], kv_k=inp["kv_k"][1:2], kv_v=inp["kv_v"][1:2], lens=inp["lens"][1:2],
+                  noise=inp["noise"][1:2])
+    _close(_run(one_cfg, single, lib)["actions"][0], base["actions"][1], tol=1e-12, what="batch independence")
+    # swapping two requests swaps their results
+    sw = dict(weights=inp["weights"], kv_k=inp["kv_k"][::-1].copy(), kv_v=inp["kv_v"][::-1].copy(),
+              lens=inp["lens"][::-1].copy(), noise=inp["noise"][::-1].copy())
+    _close(_run(cfg, sw, lib)["actions"][::-1], base["actions"], tol=1e-12, what="request permutation")
+    # no layers: v = AdaRMS(x W_in) W_out with the final modulation
+    c0 = dict(cfg, layers=0, steps=1)
+    inp0 = phx_inputs.make_inputs(c0, seed=5)
+    out0 = _run(c0, inp0, lib, velocity=True)
+    W = inp0["weights"]
+    x = inp0["noise"].reshape(-1, c0["state_dim"]).astype(np.float64)
+    e = np.concatenate([np.sin(1.0 * 10000.0 ** (-np.arange(4) / 4)), np.cos(1.0 * 10000.0 ** (-np.arange(4) / 4))])
+    mod = e @ phx_inputs.view(W, c0, "W_mod")[0].astype(np.float64)
+    h = torch.tensor(x @ phx_inputs.view(W, c0, "W_in").astype(np.float64))
+    n = (F.rms_norm(h, (c0["width"],), weight=torch.tensor(1.0 + mod[:8]), eps=c0["rms_eps"]) + torch.tensor(mod[8:])).numpy()
+    _close(out0["velocity"][0], n @ phx_inputs.view(W, c0, "W_out").astype(np.float64), what="zero-layer velocity")
+
+
+ALL_PINS = [pin_time_embedding, pin_modulation, pin_matmul, pin_ada_rmsnorm, pin_rope, pin_gelu, pin_attention,
+            pin_decide_brute_force, pin_decide_invariants]
+
+
+def run_all(lib):
+    """Run every pin; return the names of the pins that failed."""
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except (ValueError, FloatingPointError, RuntimeError):
+            failed.append(pin.__name__)
+    return failed
