@@ -1,0 +1,128 @@
+"""ctypes binding of libphx_expert.so, with the C ABI's names.
+
+Argument marshalling only: every step of the decision runs in the library's
+HIP kernels.  torch supplies device memory and streams.  There is no CPU
+fallback: if the library is missing the import of this module's functions
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libphx_expert.so")
+
+PHX_ABI_VERSION = 1
+PHX_OK, PHX_E_INVALID, PHX_E_VERSION, PHX_E_SHAPE, PHX_E_STATE, PHX_E_NOMEM, PHX_E_HIP = 0, -1, -2, -3, -4, -5, -6
+PHX_DTYPE_F32, PHX_DTYPE_BF16 = 0, 1
+PHX_FLAG_NO_GRAPH = 1
+
+# every function include/phx_expert.h declares
+EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_expert_create",
+            "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_destroy", "phx_last_error",
+            "phx_expert_kernels_per_decision")
+
+
+class phx_expert_config(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32), ("struct_size", ctypes.c_uint32),
+        ("layers", ctypes.c_int32), ("width", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("mlp_hidden", ctypes.c_int32),
+        ("state_dim", ctypes.c_int32), ("rows", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("prefix_capacity", ctypes.c_int32), ("steps", ctypes.c_int32), ("time_emb_dim", ctypes.c_int32),
+        ("tau0", ctypes.c_float), ("dt", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+        ("weight_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+    ]
+
+
+class PhxError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with flow_matching_action_decision_amd/build.py "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    CP = ctypes.POINTER(phx_expert_config)
+    lib.phx_expert_validate_config.argtypes = [CP]
+    lib.phx_expert_weights_bytes.argtypes = [CP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.phx_expert_create.argtypes = [CP, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
+    lib.phx_expert_load_prefix_kv.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_int32, P]
+    lib.phx_expert_decide.argtypes = [P, P, P, P]
+    lib.phx_expert_destroy.argtypes = [P]
+    lib.phx_expert_destroy.restype = None
+    lib.phx_last_error.restype = ctypes.c_char_p
+    lib.phx_expert_kernels_per_decision.argtypes = [P, ctypes.POINTER(ctypes.c_int)]
+    _lib = lib
+    return lib
+
+
+def make_config(cfg: dict, flags: int = 0) -> phx_expert_config:
+    """phx_expert_config from a workload dict (phx_inputs naming)."""
+    dt = PHX_DTYPE_BF16 if cfg["dtype"] == "bf16" else PHX_DTYPE_F32
+    return phx_expert_config(
+        abi_version=PHX_ABI_VERSION, struct_size=ctypes.sizeof(phx_expert_config),
+        layers=cfg["layers"], width=cfg["width"], n_heads=cfg["n_heads"], head_dim=cfg["head_dim"],
+        n_kv_heads=cfg["n_kv_heads"], mlp_hidden=cfg["mlp_hidden"], state_dim=cfg["state_dim"], rows=cfg["rows"],
+        batch=cfg["batch"], prefix_capacity=cfg["capacity"], steps=cfg["steps"], time_emb_dim=cfg["time_emb_dim"],
+        tau0=cfg["tau0"], dt=cfg["dt"], rms_eps=cfg["rms_eps"], rope_base=cfg["rope_base"],
+        weight_dtype=dt, kv_dtype=dt, flags=flags | int(cfg.get("flags", 0)))
+
+
+def _check(rc: int):
+    if rc != PHX_OK:
+        raise PhxError(rc, load_library().phx_last_error().decode())
+
+
+def phx_last_error() -> str:
+    return load_library().phx_last_error().decode()
+
+
+def phx_expert_validate_config(cfg: phx_expert_config) -> int:
+    return load_library().phx_expert_validate_config(ctypes.byref(cfg))
+
+
+def phx_expert_weights_bytes(cfg: phx_expert_config) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().phx_expert_weights_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def phx_expert_create(cfg: phx_expert_config, weights_ptr: int, weights_bytes: int, stream: int = 0) -> int:
+    h = ctypes.c_void_p(0)
+    _check(load_library().phx_expert_create(ctypes.byref(cfg), ctypes.c_void_p(weights_ptr), weights_bytes,
+                                            ctypes.c_void_p(stream), ctypes.byref(h)))
+    return h.value
+
+
+def phx_expert_load_prefix_kv(h: int, request: int, k_ptr: int, v_ptr: int, prefix_len: int, stream: int = 0):
+    _check(load_library().phx_expert_load_prefix_kv(ctypes.c_void_p(h), request, ctypes.c_void_p(k_ptr),
+                                                    ctypes.c_void_p(v_ptr), prefix_len, ctypes.c_void_p(stream)))
+
+
+def phx_expert_decide(h: int, noise_ptr: int, actions_ptr: int, stream: int = 0):
+    _check(load_library().phx_expert_decide(ctypes.c_void_p(h), ctypes.c_void_p(noise_ptr),
+                                            ctypes.c_void_p(actions_ptr), ctypes.c_void_p(stream)))
+
+
+def phx_expert_destroy(h: int):
+    if h:
+        load_library().phx_expert_destroy(ctypes.c_void_p(h))
+
+
+def phx_expert_kernels_per_decision(h: int) -> int:
+    n = ctypes.c_int(0)
+    _check(load_library().phx_expert_kernels_per_decision(ctypes.c_void_p(h), ctypes.byref(n)))
+    return n.value

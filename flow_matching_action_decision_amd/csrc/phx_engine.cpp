@@ -1,0 +1,517 @@
+// Host engine and C ABI of the action-expert decision (see include/phx_expert.h).
+//
+// A handle owns three kinds of device memory, the buffer roles the pages
+// describe ("FlashRT-PAI", section 3.4 and Appendix A.1):
+//   static : re-tiled weights and the step-conditioning table (modulation of
+//            every norm at every tau_k), written once at create;
+//   state  : per-request prefix K/V caches (with room for the action rows),
+//            prefix lengths and the decoder position table, written by
+//            phx_expert_load_prefix_kv and read by every step;
+//   working: the state x, residual stream h, sums of squares, q, o, the GeGLU
+//            activation and split partials, reused by every layer.
+// The step loop (S steps x NL layers) is captured once into a HIP graph whose
+// nodes see only fixed addresses ("PhyAI", section 4.2 Graph replay).
+#include "phx_expert.h"
+#include "phx_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace phx;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define PHX_HIP(call)                                                                                 \
+  do {                                                                                                \
+    hipError_t e_ = (call);                                                                           \
+    if (e_ != hipSuccess) return fail(PHX_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_));     \
+  } while (0)
+
+struct GemmPlan {
+  int NT = 0, KT = 0, KSW = 1, NW = 4;
+};
+
+GemmPlan make_plan(int K, int N, int target_wgs) {
+  GemmPlan p;
+  p.KT = K / TILE_K;
+  p.NT = N / TILE_N;
+  p.NW = (p.KT % 4 == 0) ? 4 : 1;
+  p.KSW = 1;
+  while (p.NT * p.KSW < target_wgs && p.KT % (p.KSW * 2 * p.NW) == 0) p.KSW *= 2;
+  return p;
+}
+
+
+bool is_device_pointer(const void* p) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+}  // namespace
+
+struct phx_expert {
+  phx_expert_config cfg{};
+  int dtype = 1;
+  size_t esz = 2;
+  int BM = 0, MT = 1, NTD = 0, ss_ld = 0, Ctot = 0, SMAX = 0, GMP = 0, QT = 1, NN = 0;
+  size_t kv_layer = 0;  // elements of one layer's cache (all requests)
+  GemmPlan p_in, p_qkv, p_o, p_gu, p_down, p_out;
+  // static
+  void* wt = nullptr;
+  size_t off_in = 0, off_out = 0;
+  std::vector<size_t> off_qkv, off_o, off_gu, off_down;
+  float* modtab = nullptr;
+  // state
+  void* kc = nullptr;
+  void* vtc = nullptr;
+  int* lens = nullptr;
+  float2* rope = nullptr;
+  std::vector<int> loaded;
+  // working
+  float* x = nullptr;
+  float* h = nullptr;
+  float* ss = nullptr;
+  void* q = nullptr;
+  void* o = nullptr;
+  void* act = nullptr;
+  float* part_o = nullptr;
+  float2* part_ml = nullptr;
+  float* gpart = nullptr;
+  unsigned* counters = nullptr;
+  // execution
+  hipStream_t cap = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int nodes = 0;
+  std::vector<void*> allocs;
+};
+
+namespace {
+
+void release(phx_expert* h) {
+  if (!h) return;
+  if (h->cap) (void)hipStreamSynchronize(h->cap);
+  if (h->exec) (void)hipGraphExecDestroy(h->exec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  for (void* p : h->allocs) (void)hipFree(p);
+  if (h->cap) (void)hipStreamDestroy(h->cap);
+  delete h;
+}
+
+int alloc(phx_expert* h, void** p, size_t bytes, const char* what) {
+  hipError_t e = hipMalloc(p, bytes < 256 ? 256 : bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PHX_E_NOMEM, "device allocation of %zu bytes for %s failed: %s", bytes, what, hipGetErrorString(e));
+  }
+  h->allocs.push_back(*p);
+  return PHX_OK;
+}
+
+size_t weight_elems(const phx_expert_config* c) {
+  const size_t D = c->width, A = c->state_dim, F = c->mlp_hidden, E = c->time_emb_dim, NL = c->layers;
+  const size_t qkv = (size_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  const size_t hd = (size_t)c->n_heads * c->head_dim;
+  const size_t per_layer = D * qkv + hd * D + D * 2 * F + F * D;
+  return A * D + NL * per_layer + D * A + (2 * NL + 1) * E * 2 * D;
+}
+
+// Enqueue one decision's step loop on stream s (graph capture or direct).
+int enqueue_steps(phx_expert* h, hipStream_t s, int* nodes) {
+  const phx_expert_config& c = h->cfg;
+  const int D = c.width, H = c.n_heads, Dh = c.head_dim, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim;
+  const int M = c.rows, B = c.batch, NL = c.layers;
+  const int D2 = 2 * D;
+  int n = 0;
+  for (int k = 0; k < c.steps; ++k) {
+    const float* mod_k = h->modtab + (size_t)k * h->NN * D2;
+    // a1: input projection h = x . W_in
+    {
+      GemmArgs g{};
+      g.W = (const char*)h->wt + h->off_in * h->esz;
+      g.KT = h->p_in.KT; g.NT = h->p_in.NT; g.KSW = h->p_in.KSW; g.rows = h->BM;
+      g.X = h->x; g.ldx = A;
+      g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
+      g.part = h->gpart; g.counters = h->counters;
+      PHX_HIP(launch_gemm(h->dtype, h->p_in.NW, h->MT, PRO_XF32, EPI_STORE_H, g, s));
+      ++n;
+    }
+    for (int l = 0; l < NL; ++l) {
+      void* kc_l = (char*)h->kc + (size_t)l * h->kv_layer * h->esz;
+      void* vtc_l = (char*)h->vtc + (size_t)l * h->kv_layer * h->esz;
+      // a2: AdaRMSNorm + QKV + RoPE, k and v written into the action-row cache slots
+      {
+        GemmArgs g{};
+        g.W = (const char*)h->wt + h->off_qkv[l] * h->esz;
+        g.KT = h->p_qkv.KT; g.NT = h->p_qkv.NT; g.KSW = h->p_qkv.KSW; g.rows = h->BM;
+        g.h = h->h; g.ss = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D; g.eps = c.rms_eps;
+        g.mod = mod_k + (size_t)(2 * l) * D2;
+        g.part = h->gpart; g.counters = h->counters;
+        g.q = h->q; g.kc = kc_l; g.vtc = vtc_l; g.lens = h->lens; g.rope = h->rope;
+        g.M = M; g.H = H; g.KVH = KVH; g.Dh = Dh; g.Ctot = h->Ctot;
+        PHX_HIP(launch_gemm(h->dtype, h->p_qkv.NW, h->MT, PRO_NORM, EPI_QKV, g, s));
+        ++n;
+      }
+      // a3: split-KV multi-query attention, then the fixed-order combine
+      {
+        AttnArgs at{};
+        at.q = h->q; at.kc = kc_l; at.vtc = vtc_l; at.lens = h->lens;
+        at.part_o = h->part_o; at.part_ml = h->part_ml;
+        at.M = M; at.H = H; at.KVH = KVH; at.Dh = Dh; at.Ctot = h->Ctot; at.SMAX = h->SMAX; at.GMP = h->GMP;
+        at.scale = (float)(1.0 / std::sqrt((double)Dh));
+        PHX_HIP(launch_attention(h->dtype, h->QT, at, B, s));
+        CombineArgs cb{};
+        cb.part_o = h->part_o; cb.part_ml = h->part_ml; cb.lens = h->lens; cb.o = h->o;
+        cb.M = M; cb.H = H; cb.KVH = KVH; cb.Dh = Dh; cb.SMAX = h->SMAX; cb.GMP = h->GMP;
+        PHX_HIP(launch_combine(h->dtype, cb, B, s));
+        n += 2;
+      }
+      // a4: out-projection + residual
+      {
+        GemmArgs g{};
+        g.W = (const char*)h->wt + h->off_o[l] * h->esz;
+        g.KT = h->p_o.KT; g.NT = h->p_o.NT; g.KSW = h->p_o.KSW; g.rows = h->BM;
+        g.X = h->o; g.ldx = H * Dh;
+        g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
+        g.part = h->gpart; g.counters = h->counters;
+        PHX_HIP(launch_gemm(h->dtype, h->p_o.NW, h->MT, PRO_X, EPI_RESID, g, s));
+        ++n;
+      }
+      // a5: AdaRMSNorm + gate/up + GeGLU
+      {
+        GemmArgs g{};
+        g.W = (const char*)h->wt + h->off_gu[l] * h->esz;
+        g.KT = h->p_gu.KT; g.NT = h->p_gu.NT; g.KSW = h->p_gu.KSW; g.rows = h->BM;
+        g.h = h->h; g.ss = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D; g.eps = c.rms_eps;
+        g.mod = mod_k + (size_t)(2 * l + 1) * D2;
+        g.part = h->gpart; g.counters = h->counters;
+        g.act = h->act; g.F = F;
+        PHX_HIP(launch_gemm(h->dtype, h->p_gu.NW, h->MT, PRO_NORM, EPI_GEGLU, g, s));
+        ++n;
+      }
+      // a6: down-projection + residual
+      {
+        GemmArgs g{};
+        g.W = (const char*)h->wt + h->off_down[l] * h->esz;
+        g.KT = h->p_down.KT; g.NT = h->p_down.NT; g.KSW = h->p_down.KSW; g.rows = h->BM;
+        g.X = h->act; g.ldx = F;
+        g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
+        g.part = h->gpart; g.counters = h->counters;
+        PHX_HIP(launch_gemm(h->dtype, h->p_down.NW, h->MT, PRO_X, EPI_RESID, g, s));
+        ++n;
+      }
+    }
+    // a7: final AdaRMSNorm + velocity projection + Euler update
+    {
+      GemmArgs g{};
+      g.W = (const char*)h->wt + h->off_out * h->esz;
+      g.KT = h->p_out.KT; g.NT = h->p_out.NT; g.KSW = h->p_out.KSW; g.rows = h->BM;
+      g.h = h->h; g.ss = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D; g.eps = c.rms_eps;
+      g.mod = mod_k + (size_t)(2 * NL) * D2;
+      g.part = h->gpart; g.counters = h->counters;
+      g.x = h->x; g.dt = c.dt; g.A = A;
+      PHX_HIP(launch_gemm(h->dtype, h->p_out.NW, h->MT, PRO_NORM, EPI_EULER, g, s));
+      ++n;
+    }
+  }
+  if (nodes) *nodes = n;
+  return PHX_OK;
+}
+
+int mt_for_rows(int rows) {
+  const int need = (rows + 15) / 16;
+  if (need <= 1) return 1;
+  if (need <= 2) return 2;
+  if (need <= 4) return 4;
+  return 10;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* phx_last_error(void) { return g_err.c_str(); }
+
+int phx_expert_validate_config(const phx_expert_config* c) {
+  if (!c) return fail(PHX_E_INVALID, "config is NULL");
+  if (c->abi_version != PHX_ABI_VERSION)
+    return fail(PHX_E_VERSION, "abi_version %u, library implements %u", c->abi_version, PHX_ABI_VERSION);
+  if (c->struct_size != sizeof(phx_expert_config))
+    return fail(PHX_E_VERSION, "struct_size %u, library expects %zu", c->struct_size, sizeof(phx_expert_config));
+  if (c->layers < 1 || c->layers > 256) return fail(PHX_E_SHAPE, "layers %d outside [1, 256]", c->layers);
+  if (c->width < 128 || c->width % 128) return fail(PHX_E_SHAPE, "width %d must be a positive multiple of 128", c->width);
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+    return fail(PHX_E_SHAPE, "head_dim %d must be 64, 128 or 256", c->head_dim);
+  if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads)
+    return fail(PHX_E_SHAPE, "n_kv_heads %d must divide n_heads %d", c->n_kv_heads, c->n_heads);
+  if ((c->n_heads * c->head_dim) % 128)
+    return fail(PHX_E_SHAPE, "n_heads*head_dim %d must be a multiple of 128", c->n_heads * c->head_dim);
+  if (c->mlp_hidden < 128 || c->mlp_hidden % 128)
+    return fail(PHX_E_SHAPE, "mlp_hidden %d must be a positive multiple of 128", c->mlp_hidden);
+  if (c->state_dim < 32 || c->state_dim % 32)
+    return fail(PHX_E_SHAPE, "state_dim %d must be a positive multiple of 32", c->state_dim);
+  if (c->rows < 1 || c->batch < 1 || c->rows * c->batch > 160)
+    return fail(PHX_E_SHAPE, "rows*batch = %d must be in [1, 160]", c->rows * c->batch);
+  if ((c->n_heads / c->n_kv_heads) * c->rows > 128)
+    return fail(PHX_E_SHAPE, "query rows per kv head (n_heads/n_kv_heads*rows = %d) must be at most 128",
+                (c->n_heads / c->n_kv_heads) * c->rows);
+  if (c->prefix_capacity < 0 || c->prefix_capacity > 65536)
+    return fail(PHX_E_SHAPE, "prefix_capacity %d outside [0, 65536]", c->prefix_capacity);
+  if (c->steps < 1 || c->steps > 1000) return fail(PHX_E_SHAPE, "steps %d outside [1, 1000]", c->steps);
+  if (c->time_emb_dim < 2 || c->time_emb_dim % 2 || c->time_emb_dim > 65536)
+    return fail(PHX_E_SHAPE, "time_emb_dim %d must be even and at most 65536", c->time_emb_dim);
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(PHX_E_INVALID, "rms_eps must be positive");
+  if (!(c->rope_base > 0.f) || !std::isfinite(c->rope_base)) return fail(PHX_E_INVALID, "rope_base must be positive");
+  if (!std::isfinite(c->tau0) || !std::isfinite(c->dt)) return fail(PHX_E_INVALID, "tau0 and dt must be finite");
+  if (c->weight_dtype != PHX_DTYPE_F32 && c->weight_dtype != PHX_DTYPE_BF16)
+    return fail(PHX_E_INVALID, "weight_dtype %d unknown", c->weight_dtype);
+  if (c->kv_dtype != c->weight_dtype) return fail(PHX_E_SHAPE, "kv_dtype must equal weight_dtype");
+  if (c->flags & ~PHX_FLAG_NO_GRAPH) return fail(PHX_E_INVALID, "unknown flags 0x%x", c->flags);
+  return PHX_OK;
+}
+
+int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(PHX_E_INVALID, "bytes is NULL");
+  int rc = phx_expert_validate_config(cfg);
+  if (rc) return rc;
+  *bytes = weight_elems(cfg) * (cfg->weight_dtype == PHX_DTYPE_BF16 ? 2 : 4);
+  return PHX_OK;
+}
+
+int phx_expert_kernels_per_decision(const phx_expert* h, int* count) {
+  if (!h || !count) return fail(PHX_E_INVALID, "NULL argument");
+  *count = h->nodes;
+  return PHX_OK;
+}
+
+static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
+  const phx_expert_config& c = h->cfg;
+  const int D = c.width, H = c.n_heads, Dh = c.head_dim, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim;
+  const int M = c.rows, B = c.batch, NL = c.layers, S = c.steps, E = c.time_emb_dim;
+  h->dtype = c.weight_dtype == PHX_DTYPE_BF16 ? 1 : 0;
+  h->esz = h->dtype ? 2 : 4;
+  h->BM = B * M;
+  h->MT = mt_for_rows(h->BM);
+  h->NTD = D / 16;
+  h->ss_ld = 16 * h->MT;
+  h->SMAX = (int)((c.prefix_capacity + M + ATTN_KEYS - 1) / ATTN_KEYS);
+  h->Ctot = h->SMAX * ATTN_KEYS;
+  const int GM = (H / KVH) * M;
+  h->QT = (GM + 15) / 16;
+  h->GMP = h->QT * 16;
+  h->NN = 2 * NL + 1;
+  h->kv_layer = (size_t)B * KVH * h->Ctot * Dh;
+  const int qkvN = (H + 2 * KVH) * Dh;
+
+  h->p_in = make_plan(A, D, 1);
+  h->p_qkv = make_plan(D, qkvN, 256);
+  h->p_o = make_plan(H * Dh, D, 256);
+  h->p_gu = make_plan(D, 2 * F, 256);
+  h->p_down = make_plan(F, D, 256);
+  h->p_out = make_plan(D, A, 256);
+  if (h->p_in.NW != 1)  // the input projection kernel runs one wave per workgroup
+    h->p_in.NW = 1;
+
+  int rc;
+  hipDeviceProp_t prop;
+  int dev = 0;
+  PHX_HIP(hipGetDevice(&dev));
+  PHX_HIP(hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(PHX_E_HIP, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  PHX_HIP(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
+
+  // ---- static: tiled weights (everything but W_mod) ----
+  size_t off = 0;
+  h->off_in = off;
+  off += (size_t)A * D;
+  for (int l = 0; l < NL; ++l) {
+    h->off_qkv.push_back(off); off += (size_t)D * qkvN;
+    h->off_o.push_back(off); off += (size_t)H * Dh * D;
+    h->off_gu.push_back(off); off += (size_t)D * 2 * F;
+    h->off_down.push_back(off); off += (size_t)F * D;
+  }
+  h->off_out = off;
+  off += (size_t)D * A;
+  const size_t tiled_elems = off;
+  const size_t total_elems = weight_elems(&c);
+  if ((rc = alloc(h, &h->wt, tiled_elems * h->esz, "tiled weights"))) return rc;
+
+  const void* src = weights;
+  void* staging = nullptr;
+  if (!is_device_pointer(weights)) {
+    if ((rc = alloc(h, &staging, total_elems * h->esz, "weight staging"))) return rc;
+    PHX_HIP(hipMemcpyAsync(staging, weights, total_elems * h->esz, hipMemcpyHostToDevice, stream));
+    src = staging;
+  }
+  // the blob has the same order as the tiled arena, plus W_mod at the end
+  const char* sb = (const char*)src;
+  auto retile = [&](size_t o, int K, int N, int kind, int param) -> int {
+    PHX_HIP(launch_retile(h->dtype, sb + o * h->esz, (char*)h->wt + o * h->esz, K, N, kind, param, stream));
+    return PHX_OK;
+  };
+  if ((rc = retile(h->off_in, A, D, COL_IDENT, 0))) return rc;
+  for (int l = 0; l < NL; ++l) {
+    if ((rc = retile(h->off_qkv[l], D, qkvN, COL_ROPE, Dh))) return rc;
+    if ((rc = retile(h->off_o[l], H * Dh, D, COL_IDENT, 0))) return rc;
+    if ((rc = retile(h->off_gu[l], D, 2 * F, COL_GEGLU, F))) return rc;
+    if ((rc = retile(h->off_down[l], F, D, COL_IDENT, 0))) return rc;
+  }
+  if ((rc = retile(h->off_out, D, A, COL_IDENT, 0))) return rc;
+
+  // ---- static: step-conditioning table, built once for the handle's life ----
+  void* etab = nullptr;
+  if ((rc = alloc(h, &etab, (size_t)S * E * sizeof(double), "time embedding"))) return rc;
+  if ((rc = alloc(h, (void**)&h->modtab, (size_t)S * h->NN * 2 * D * sizeof(float), "modulation table"))) return rc;
+  PHX_HIP(launch_time_embedding((double*)etab, S, E, c.tau0, c.dt, stream));
+  PHX_HIP(launch_modulation(h->dtype, sb + off * h->esz, (const double*)etab, h->modtab, S, h->NN, E, 2 * D, stream));
+
+  // ---- state and working memory ----
+  const size_t cache_bytes = (size_t)NL * h->kv_layer * h->esz;
+  if ((rc = alloc(h, &h->kc, cache_bytes, "key cache"))) return rc;
+  if ((rc = alloc(h, &h->vtc, cache_bytes, "value cache"))) return rc;
+  if ((rc = alloc(h, (void**)&h->lens, (size_t)B * sizeof(int), "prefix lengths"))) return rc;
+  if ((rc = alloc(h, (void**)&h->rope, (size_t)B * M * (Dh / 2) * sizeof(float2), "position table"))) return rc;
+  if ((rc = alloc(h, (void**)&h->x, (size_t)h->BM * A * sizeof(float), "state"))) return rc;
+  if ((rc = alloc(h, (void**)&h->h, (size_t)h->BM * D * sizeof(float), "residual stream"))) return rc;
+  if ((rc = alloc(h, (void**)&h->ss, (size_t)h->NTD * h->ss_ld * sizeof(float), "sums of squares"))) return rc;
+  if ((rc = alloc(h, &h->q, (size_t)h->BM * H * Dh * h->esz, "queries"))) return rc;
+  if ((rc = alloc(h, &h->o, (size_t)h->BM * H * Dh * h->esz, "attention output"))) return rc;
+  if ((rc = alloc(h, &h->act, (size_t)h->BM * F * h->esz, "GeGLU activation"))) return rc;
+  const size_t part_rows = (size_t)B * KVH * h->SMAX * h->GMP;
+  if ((rc = alloc(h, (void**)&h->part_o, part_rows * Dh * sizeof(float), "attention partials"))) return rc;
+  if ((rc = alloc(h, (void**)&h->part_ml, part_rows * sizeof(float2), "attention statistics"))) return rc;
+  size_t gp = 0, maxnt = 0;
+  for (const GemmPlan* p : {&h->p_in, &h->p_qkv, &h->p_o, &h->p_gu, &h->p_down, &h->p_out}) {
+    if (p->KSW > 1) gp = std::max(gp, (size_t)p->NT * p->KSW * h->MT * 256);
+    maxnt = std::max(maxnt, (size_t)p->NT);
+  }
+  if ((rc = alloc(h, (void**)&h->gpart, std::max(gp, (size_t)1) * sizeof(float), "split partials"))) return rc;
+  if ((rc = alloc(h, (void**)&h->counters, maxnt * sizeof(unsigned), "split counters"))) return rc;
+  PHX_HIP(hipMemsetAsync(h->kc, 0, cache_bytes, stream));
+  PHX_HIP(hipMemsetAsync(h->vtc, 0, cache_bytes, stream));
+  PHX_HIP(hipMemsetAsync(h->lens, 0, (size_t)B * sizeof(int), stream));
+  PHX_HIP(hipMemsetAsync(h->rope, 0, (size_t)B * M * (Dh / 2) * sizeof(float2), stream));
+  PHX_HIP(hipMemsetAsync(h->ss, 0, (size_t)h->NTD * h->ss_ld * sizeof(float), stream));
+  PHX_HIP(hipMemsetAsync(h->counters, 0, maxnt * sizeof(unsigned), stream));
+  PHX_HIP(hipMemsetAsync(h->x, 0, (size_t)h->BM * A * sizeof(float), stream));
+  PHX_HIP(hipMemsetAsync(h->h, 0, (size_t)h->BM * D * sizeof(float), stream));
+  PHX_HIP(hipStreamSynchronize(stream));
+  // set-up scratch is no longer needed
+  for (void* p : {etab, staging}) {
+    if (!p) continue;
+    for (size_t i = 0; i < h->allocs.size(); ++i)
+      if (h->allocs[i] == p) {
+        (void)hipFree(p);
+        h->allocs.erase(h->allocs.begin() + (long)i);
+        break;
+      }
+  }
+  h->loaded.assign(B, 0);
+
+  // ---- capture the step loop ----
+  if (!(c.flags & PHX_FLAG_NO_GRAPH)) {
+    PHX_HIP(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+    rc = enqueue_steps(h, h->cap, &h->nodes);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(h->cap, &g);
+    if (rc) {
+      if (g) (void)hipGraphDestroy(g);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(PHX_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    h->graph = g;
+    PHX_HIP(hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0));
+  } else {
+    h->nodes = c.steps * (2 + 6 * NL);
+  }
+  return PHX_OK;
+}
+
+int phx_expert_create(const phx_expert_config* cfg, const void* weights, size_t weights_bytes, phx_stream_t stream,
+                      phx_expert** out) {
+  if (!out) return fail(PHX_E_INVALID, "out is NULL");
+  int rc = phx_expert_validate_config(cfg);
+  if (rc) return rc;
+  if (!weights) return fail(PHX_E_INVALID, "weights is NULL");
+  const size_t want = weight_elems(cfg) * (cfg->weight_dtype == PHX_DTYPE_BF16 ? 2 : 4);
+  if (weights_bytes != want) return fail(PHX_E_SHAPE, "weights_bytes %zu, expected %zu", weights_bytes, want);
+  phx_expert* h = new (std::nothrow) phx_expert();
+  if (!h) return fail(PHX_E_NOMEM, "host allocation failed");
+  h->cfg = *cfg;
+  rc = create_impl(h, weights, (hipStream_t)stream);
+  if (rc) {
+    std::string msg = g_err;
+    release(h);
+    g_err = msg;
+    return rc;
+  }
+  *out = h;
+  g_err.clear();
+  return PHX_OK;
+}
+
+int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, const void* v, int32_t prefix_len,
+                              phx_stream_t stream) {
+  if (!h) return fail(PHX_E_INVALID, "handle is NULL");
+  const phx_expert_config& c = h->cfg;
+  if (request < 0 || request >= c.batch) return fail(PHX_E_SHAPE, "request %d outside [0, %d)", request, c.batch);
+  if (prefix_len < 0 || prefix_len > c.prefix_capacity)
+    return fail(PHX_E_SHAPE, "prefix_len %d outside [0, %d]", prefix_len, c.prefix_capacity);
+  if (prefix_len > 0 && (!k || !v)) return fail(PHX_E_INVALID, "k or v is NULL");
+  if (prefix_len > 0 && (!is_device_pointer(k) || !is_device_pointer(v)))
+    return fail(PHX_E_INVALID, "k and v must be device pointers");
+  hipStream_t s = (hipStream_t)stream;
+  PHX_HIP(launch_load_prefix(h->dtype, k, v, h->kc, h->vtc, c.layers, c.batch, c.n_kv_heads, c.head_dim, h->Ctot,
+                             request, prefix_len, s));
+  PHX_HIP(launch_position_table(h->lens, h->rope, request, prefix_len, c.rows, c.head_dim, (double)c.rope_base, s));
+  h->loaded[request] = 1;
+  g_err.clear();
+  return PHX_OK;
+}
+
+int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_stream_t stream) {
+  if (!h) return fail(PHX_E_INVALID, "handle is NULL");
+  if (!noise || !actions) return fail(PHX_E_INVALID, "noise or actions is NULL");
+  for (int b = 0; b < h->cfg.batch; ++b)
+    if (!h->loaded[b]) return fail(PHX_E_STATE, "request %d has no prefix loaded", b);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t xb = (size_t)h->BM * h->cfg.state_dim * sizeof(float);
+  PHX_HIP(hipMemcpyAsync(h->x, noise, xb, hipMemcpyDefault, s));
+  if (h->exec) {
+    PHX_HIP(hipGraphLaunch(h->exec, s));
+  } else {
+    int rc = enqueue_steps(h, s, nullptr);
+    if (rc) return rc;
+  }
+  PHX_HIP(hipMemcpyAsync(actions, h->x, xb, hipMemcpyDefault, s));
+  g_err.clear();
+  return PHX_OK;
+}
+
+void phx_expert_destroy(phx_expert* h) { release(h); }
+
+}  // extern "C"

@@ -40,6 +40,12 @@
 extern "C" {
 #endif
 
+#if defined(__GNUC__) || defined(__clang__)
+#define PHX_API __attribute__((visibility("default")))
+#else
+#define PHX_API
+#endif
+
 #define PHX_ABI_VERSION 1u
 
 /* return codes */
@@ -72,17 +78,17 @@ typedef struct phx_expert_config {
   uint32_t abi_version;      /* PHX_ABI_VERSION */
   uint32_t struct_size;      /* sizeof(phx_expert_config) */
   int32_t layers;            /* NL decoder layers [18] */
-  int32_t width;             /* D residual width [1024]; multiple of 32 */
+  int32_t width;             /* D residual width [1024]; multiple of 128 */
   int32_t n_heads;           /* H query heads [8] */
-  int32_t head_dim;          /* Dh [256]; multiple of 16, at most 256 */
+  int32_t head_dim;          /* Dh [256]; 64, 128 or 256; n_heads*head_dim a multiple of 128 */
   int32_t n_kv_heads;        /* KVH key/value heads [1: multi-query]; divides H */
-  int32_t mlp_hidden;        /* F GeGLU hidden width [4096]; multiple of 32 */
+  int32_t mlp_hidden;        /* F GeGLU hidden width [4096]; multiple of 128 */
   int32_t state_dim;         /* A action dimension [32]; multiple of 32 */
-  int32_t rows;              /* M action rows per request [10] */
+  int32_t rows;              /* M action rows per request [10]; n_heads/n_kv_heads*rows <= 128 */
   int32_t batch;             /* B requests per decision; B*M <= 160 */
-  int32_t prefix_capacity;   /* C context bucket: most prefix rows a request may load [768] */
+  int32_t prefix_capacity;   /* C context bucket: most prefix rows a request may load [768]; <= 65536 */
   int32_t steps;             /* S Euler steps [10] */
-  int32_t time_emb_dim;      /* E sinusoidal time-embedding width [1024]; multiple of 32 */
+  int32_t time_emb_dim;      /* E sinusoidal time-embedding width [1024]; even */
   float tau0;                /* flow time of the first step [1.0] */
   float dt;                  /* Euler step [-0.1]: tau_k = tau0 + k*dt, x += dt*v */
   float rms_eps;             /* [1e-6], inside the square root */
@@ -98,7 +104,7 @@ typedef struct phx_expert phx_expert;
  * Checks a configuration without touching the GPU (pure host code).
  * Returns PHX_OK, PHX_E_INVALID (NULL), PHX_E_VERSION or PHX_E_SHAPE.
  */
-int phx_expert_validate_config(const phx_expert_config* cfg);
+PHX_API int phx_expert_validate_config(const phx_expert_config* cfg);
 
 /*
  * Size in bytes of the weight blob phx_expert_create expects for cfg.
@@ -114,7 +120,7 @@ int phx_expert_validate_config(const phx_expert_config* cfg);
  *                            2*NL the velocity head; first D outputs scale, last D shift)
  * There are no biases.
  */
-int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes);
+PHX_API int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes);
 
 /*
  * Builds a handle: allocates its device arenas, copies and re-tiles the
@@ -129,7 +135,7 @@ int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes);
  * Returns PHX_OK, PHX_E_INVALID, PHX_E_VERSION, PHX_E_SHAPE, PHX_E_NOMEM or
  * PHX_E_HIP.  *out is set only on success.
  */
-int phx_expert_create(const phx_expert_config* cfg, const void* weights, size_t weights_bytes,
+PHX_API int phx_expert_create(const phx_expert_config* cfg, const void* weights, size_t weights_bytes,
                       phx_stream_t stream, phx_expert** out);
 
 /*
@@ -145,7 +151,7 @@ int phx_expert_create(const phx_expert_config* cfg, const void* weights, size_t 
  * Asynchronous on stream.  Returns PHX_OK, PHX_E_INVALID, PHX_E_SHAPE or
  * PHX_E_HIP.
  */
-int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, const void* v,
+PHX_API int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, const void* v,
                               int32_t prefix_len, phx_stream_t stream);
 
 /*
@@ -156,17 +162,17 @@ int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, con
  * caller synchronizes.  Returns PHX_OK, PHX_E_INVALID, PHX_E_STATE (a
  * request has no loaded prefix) or PHX_E_HIP.
  */
-int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_stream_t stream);
+PHX_API int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_stream_t stream);
 
 /* Frees every device allocation of the handle. NULL-safe. Synchronizes the
    handle's internal stream first. */
-void phx_expert_destroy(phx_expert* h);
+PHX_API void phx_expert_destroy(phx_expert* h);
 
 /* Message of the last failing call in this thread ("" if none). */
-const char* phx_last_error(void);
+PHX_API const char* phx_last_error(void);
 
 /* Number of kernel launches one decision replays (graph nodes). */
-int phx_expert_kernels_per_decision(const phx_expert* h, int* count);
+PHX_API int phx_expert_kernels_per_decision(const phx_expert* h, int* count);
 
 #ifdef __cplusplus
 }
