@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of one pi0.5-shape action-expert decision on one MI355X.
+
+A "step" of this benchmark is one whole decision: S = 10 flow-matching Euler
+steps of the 18-layer expert over 10 action rows attending to a 768-token
+prefix K/V cache, replayed from the library's captured HIP graph.  Inputs
+(weights, prefix K/V, noise) are synthetic and seeded, and resident in HBM
+before the timed region starts.
+
+Prints ONE JSON line (see --help for the knobs).  Besides the wall-clock
+figure it carries:
+  * "roofline": the dominant kernel's algorithmic bytes per launch divided by
+    its average launch duration, timed here with HIP events on the stream the
+    kernel runs on, against MI355X's 8 TB/s HBM peak;
+  * "cpu_baseline": the CPU oracle timed on a bounded sample of the same
+    workload on this host's cores (a reported baseline, not the target).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import phx_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+WORKLOAD = "pi05_expert_bf16"
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_pi05_expert_bf16.json")
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg: dict) -> dict:
+    """Bytes one decision must move at least once per Euler step: every
+    weight matrix of the step loop, the valid prefix K/V rows of every layer,
+    and the fp32 modulation rows the norms read."""
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    D, A, F = cfg["width"], cfg["state_dim"], cfg["mlp_hidden"]
+    H, KVH, Dh, NL = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["layers"]
+    qkv = (H + 2 * KVH) * Dh
+    w_layer = (D * qkv + H * Dh * D + D * 2 * F + F * D) * esz
+    w_step = NL * w_layer + 2 * A * D * esz
+    lens = phx_inputs.prefix_lengths(cfg)
+    kv_step = int(sum(2 * NL * int(L) * KVH * Dh * esz for L in lens))
+    mod_step = (2 * NL + 1) * 2 * D * 4
+    S = cfg["steps"]
+    return dict(weights_per_step=w_step, kv_per_step=kv_step, mod_per_step=mod_step,
+                per_decision=S * (w_step + kv_step + mod_step))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("phx_kernels.hip", "phx_engine.cpp", "phx_internal.h"):
+        with open(os.path.join(ROOT, "flow_matching_action_decision_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def omp_threads() -> int:
+    import ctypes
+    try:
+        return int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+    except OSError:
+        return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_baseline(cfg: dict, inp: dict, budget_s: float) -> dict:
+    """Time the oracle, unchanged, on a bounded sample: the first s Euler
+    steps of the same decision (s chosen so the sample takes about budget_s),
+    scaled to ms per full decision."""
+    import oracle
+    lib = oracle.load()
+    probe = dict(cfg, steps=1)
+    t0 = time.perf_counter()
+    oracle.decide(probe, inp["weights"], inp["kv_k"], inp["kv_v"], inp["lens"], inp["noise"], lib=lib)
+    t1 = time.perf_counter()
+    per_step = t1 - t0
+    s = int(max(1, min(cfg["steps"], budget_s // max(per_step, 1e-9))))
+    if s > 1:
+        t0 = time.perf_counter()
+        oracle.decide(dict(cfg, steps=s), inp["weights"], inp["kv_k"], inp["kv_v"], inp["lens"], inp["noise"], lib=lib)
+        t1 = time.perf_counter()
+        per_step = (t1 - t0) / s
+    return {"value": round(per_step * cfg["steps"] * 1e3, 1), "unit": "ms/decision", "cores": omp_threads(),
+            "kind": "oracle",
+            "sample": f"first {s} of {cfg['steps']} Euler steps of the same {cfg['layers']}-layer decision "
+                      f"(double-precision oracle, OpenMP), scaled to a full decision"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed decisions")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed decisions before the timed region")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--kernel-reps", type=int, default=50, help="timed launches of the dominant kernel")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one device-to-device copy of 256 MiB (a kernel of known traffic, to scale "
+                         "profiler byte counters against)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decision path has no multi-GPU mode (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only (WORLD_SIZE > 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (the decision runs only in the HIP library)", file=sys.stderr)
+        sys.exit(1)
+    from flow_matching_action_decision_amd.expert import Expert
+    from flow_matching_action_decision_amd import binding
+
+    cfg = phx_inputs.workload(WORKLOAD)
+    log(f"bench: generating inputs for {WORKLOAD}")
+    inp = phx_inputs.make_inputs(cfg, args.seed)
+    ab = algorithmic_bytes(cfg)
+
+    log("bench: creating handle")
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    keep = ex.load_all(inp)
+    noise = torch.from_numpy(inp["noise"]).cuda()
+    out = torch.empty_like(noise)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        ex.decide(noise, out)
+    torch.cuda.synchronize()
+
+    # timed region: K decisions back to back
+    log(f"bench: timing {args.steps} decisions")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        ex.decide(noise, out)
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = total_ms / args.steps
+    log(f"bench: {ms:.4f} ms/decision (p50 {np.percentile(per, 50):.4f}, p95 {np.percentile(per, 95):.4f})")
+
+    # dominant kernel: duration of its launches, timed with HIP events on the
+    # stream it runs on
+    dom = ex.time_dominant_kernel(args.kernel_reps)
+    kernel_hash = kernel_source_hash()
+    traffic = measured_traffic(kernel_hash)
+    achieved = dom["bytes_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom["name"], "bytes_per_launch": dom["bytes_per_launch"],
+                "us_per_launch": round(dom["ms_per_launch"] * 1e3, 3), "kernel_hash": kernel_hash}
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    first = out.cpu().numpy()
+    assert np.all(np.isfinite(first)), "non-finite actions"
+    nk = ex.kernels_per_decision()
+    del keep
+    ex.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg, inp, args.cpu_budget_s)
+
+    hbm_gbs = ab["per_decision"] / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "ms/decision (pi0.5-shape, 18L x 10 steps) + % peak HBM GB/s, 1 GPU",
+        "value": round(ms, 4), "unit": "ms/decision", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 prefix K/V, N(0,1) noise)",
+        "config": {"workload": WORKLOAD, "layers": cfg["layers"], "euler_steps": cfg["steps"],
+                   "action_rows": cfg["rows"], "prefix_len": int(inp["lens"][0]), "width": cfg["width"],
+                   "heads": f"{cfg['n_heads']}x{cfg['head_dim']} / {cfg['n_kv_heads']} kv",
+                   "mlp_hidden": cfg["mlp_hidden"], "batch": cfg["batch"]},
+        "decisions_per_s": round(1000.0 / ms, 1),
+        "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
+        "algorithmic_bytes_per_decision": ab["per_decision"],
+        "hbm_gbs": round(hbm_gbs, 1), "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "kernels_per_decision": nk,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,9 +6,9 @@ calls through ctypes and ``expert`` wraps them around torch device tensors.
 """
 from .binding import (PHX_DTYPE_BF16, PHX_DTYPE_F32, PHX_FLAG_NO_GRAPH, PhxError, load_library, make_config,
                       phx_expert_create, phx_expert_decide, phx_expert_destroy, phx_expert_kernels_per_decision,
-                      phx_expert_load_prefix_kv, phx_expert_validate_config, phx_expert_weights_bytes,
+                      phx_expert_launch_node, phx_expert_load_prefix_kv, phx_expert_node_info, phx_expert_validate_config, phx_expert_weights_bytes,
                       phx_last_error)
 
 __all__ = ["PHX_DTYPE_BF16", "PHX_DTYPE_F32", "PHX_FLAG_NO_GRAPH", "PhxError", "load_library", "make_config",
            "phx_expert_create", "phx_expert_decide", "phx_expert_destroy", "phx_expert_kernels_per_decision",
-           "phx_expert_load_prefix_kv", "phx_expert_validate_config", "phx_expert_weights_bytes", "phx_last_error"]
+           "phx_expert_launch_node", "phx_expert_load_prefix_kv", "phx_expert_node_info", "phx_expert_validate_config", "phx_expert_weights_bytes", "phx_last_error"]

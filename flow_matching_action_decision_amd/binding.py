@@ -21,7 +21,10 @@ PHX_FLAG_NO_GRAPH = 1
 # every function include/phx_expert.h declares
 EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_expert_create",
             "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_destroy", "phx_last_error",
-            "phx_expert_kernels_per_decision")
+            "phx_expert_kernels_per_decision", "phx_expert_node_info", "phx_expert_launch_node")
+
+NODE_KINDS = {1: "in_proj", 2: "norm_qkv_rope", 3: "attention", 4: "attention_combine", 5: "out_proj_resid",
+              6: "norm_gateup_geglu", 7: "down_proj_resid", 8: "norm_out_proj_euler"}
 
 
 class phx_expert_config(ctypes.Structure):
@@ -34,6 +37,11 @@ class phx_expert_config(ctypes.Structure):
         ("tau0", ctypes.c_float), ("dt", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
         ("weight_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
     ]
+
+
+class phx_node_info(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("step", ctypes.c_int32), ("layer", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("bytes", ctypes.c_uint64), ("name", ctypes.c_char * 32)]
 
 
 class PhxError(RuntimeError):
@@ -65,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phx_expert_destroy.restype = None
     lib.phx_last_error.restype = ctypes.c_char_p
     lib.phx_expert_kernels_per_decision.argtypes = [P, ctypes.POINTER(ctypes.c_int)]
+    lib.phx_expert_node_info.argtypes = [P, ctypes.c_int32, ctypes.POINTER(phx_node_info)]
+    lib.phx_expert_launch_node.argtypes = [P, ctypes.c_int32, P]
     _lib = lib
     return lib
 
@@ -126,3 +136,13 @@ def phx_expert_kernels_per_decision(h: int) -> int:
     n = ctypes.c_int(0)
     _check(load_library().phx_expert_kernels_per_decision(ctypes.c_void_p(h), ctypes.byref(n)))
     return n.value
+
+
+def phx_expert_node_info(h: int, node: int) -> dict:
+    info = phx_node_info()
+    _check(load_library().phx_expert_node_info(ctypes.c_void_p(h), node, ctypes.byref(info)))
+    return dict(kind=info.kind, step=info.step, layer=info.layer, bytes=int(info.bytes), name=info.name.decode())
+
+
+def phx_expert_launch_node(h: int, node: int, stream: int = 0):
+    _check(load_library().phx_expert_launch_node(ctypes.c_void_p(h), node, ctypes.c_void_p(stream)))

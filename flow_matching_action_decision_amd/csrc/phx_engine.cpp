@@ -49,6 +49,17 @@ struct GemmPlan {
   int NT = 0, KT = 0, KSW = 1, NW = 4;
 };
 
+// One kernel launch of the step loop.
+struct Node {
+  int kind = 0, step = 0, layer = 0;
+  uint64_t bytes = 0;  // algorithmic HBM bytes of one launch (weights and modulation rows)
+  char name[32] = {0};
+  GemmArgs g{};
+  int nw = 1, pro = 0, epi = 0;
+  AttnArgs at{};
+  CombineArgs cb{};
+};
+
 GemmPlan make_plan(int K, int N, int target_wgs) {
   GemmPlan p;
   p.KT = K / TILE_K;
@@ -90,6 +101,7 @@ struct phx_expert {
   int* lens = nullptr;
   float2* rope = nullptr;
   std::vector<int> loaded;
+  std::vector<int> lens_host;  // prefix lengths as last loaded (host copy)
   // working
   float* x = nullptr;
   float* h = nullptr;
@@ -106,6 +118,7 @@ struct phx_expert {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   int nodes = 0;
+  std::vector<Node> node_list;
   std::vector<void*> allocs;
 };
 
@@ -139,105 +152,140 @@ size_t weight_elems(const phx_expert_config* c) {
   return A * D + NL * per_layer + D * A + (2 * NL + 1) * E * 2 * D;
 }
 
-// Enqueue one decision's step loop on stream s (graph capture or direct).
-int enqueue_steps(phx_expert* h, hipStream_t s, int* nodes) {
+// Build the node list of one decision's step loop: every kernel launch, in
+// order, with its arguments.  The graph is captured from this list, and the
+// diagnostic entry point relaunches single entries of it.
+int build_nodes(phx_expert* h) {
   const phx_expert_config& c = h->cfg;
   const int D = c.width, H = c.n_heads, Dh = c.head_dim, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim;
-  const int M = c.rows, B = c.batch, NL = c.layers;
+  const int M = c.rows, NL = c.layers;
   const int D2 = 2 * D;
-  int n = 0;
+  const size_t esz = h->esz;
+  h->node_list.clear();
+  auto gemm_node = [&](int kind, int k, int l, const GemmPlan& p, int pro, int epi, const GemmArgs& g, int K, int N,
+                       const char* name) {
+    Node nd{};
+    nd.kind = kind; nd.step = k; nd.layer = l; nd.g = g; nd.nw = p.NW; nd.pro = pro; nd.epi = epi;
+    nd.bytes = (uint64_t)K * N * esz + (pro == PRO_NORM ? (uint64_t)D2 * sizeof(float) : 0);
+    std::snprintf(nd.name, sizeof(nd.name), "%s", name);
+    h->node_list.push_back(nd);
+  };
   for (int k = 0; k < c.steps; ++k) {
     const float* mod_k = h->modtab + (size_t)k * h->NN * D2;
     // a1: input projection h = x . W_in
     {
       GemmArgs g{};
-      g.W = (const char*)h->wt + h->off_in * h->esz;
+      g.W = (const char*)h->wt + h->off_in * esz;
       g.KT = h->p_in.KT; g.NT = h->p_in.NT; g.KSW = h->p_in.KSW; g.rows = h->BM;
       g.X = h->x; g.ldx = A;
       g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
       g.part = h->gpart; g.counters = h->counters;
-      PHX_HIP(launch_gemm(h->dtype, h->p_in.NW, h->MT, PRO_XF32, EPI_STORE_H, g, s));
-      ++n;
+      gemm_node(PHX_NODE_IN_PROJ, k, -1, h->p_in, PRO_XF32, EPI_STORE_H, g, A, D, "in_proj");
     }
     for (int l = 0; l < NL; ++l) {
-      void* kc_l = (char*)h->kc + (size_t)l * h->kv_layer * h->esz;
-      void* vtc_l = (char*)h->vtc + (size_t)l * h->kv_layer * h->esz;
+      void* kc_l = (char*)h->kc + (size_t)l * h->kv_layer * esz;
+      void* vtc_l = (char*)h->vtc + (size_t)l * h->kv_layer * esz;
       // a2: AdaRMSNorm + QKV + RoPE, k and v written into the action-row cache slots
       {
         GemmArgs g{};
-        g.W = (const char*)h->wt + h->off_qkv[l] * h->esz;
+        g.W = (const char*)h->wt + h->off_qkv[l] * esz;
         g.KT = h->p_qkv.KT; g.NT = h->p_qkv.NT; g.KSW = h->p_qkv.KSW; g.rows = h->BM;
         g.h = h->h; g.ss = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D; g.eps = c.rms_eps;
         g.mod = mod_k + (size_t)(2 * l) * D2;
         g.part = h->gpart; g.counters = h->counters;
         g.q = h->q; g.kc = kc_l; g.vtc = vtc_l; g.lens = h->lens; g.rope = h->rope;
         g.M = M; g.H = H; g.KVH = KVH; g.Dh = Dh; g.Ctot = h->Ctot;
-        PHX_HIP(launch_gemm(h->dtype, h->p_qkv.NW, h->MT, PRO_NORM, EPI_QKV, g, s));
-        ++n;
+        gemm_node(PHX_NODE_NORM_QKV_ROPE, k, l, h->p_qkv, PRO_NORM, EPI_QKV, g, D, (H + 2 * KVH) * Dh,
+                  "norm_qkv_rope");
       }
       // a3: split-KV multi-query attention, then the fixed-order combine
       {
-        AttnArgs at{};
+        Node nd{};
+        nd.kind = PHX_NODE_ATTENTION; nd.step = k; nd.layer = l;
+        AttnArgs& at = nd.at;
         at.q = h->q; at.kc = kc_l; at.vtc = vtc_l; at.lens = h->lens;
         at.part_o = h->part_o; at.part_ml = h->part_ml;
         at.M = M; at.H = H; at.KVH = KVH; at.Dh = Dh; at.Ctot = h->Ctot; at.SMAX = h->SMAX; at.GMP = h->GMP;
         at.scale = (float)(1.0 / std::sqrt((double)Dh));
-        PHX_HIP(launch_attention(h->dtype, h->QT, at, B, s));
-        CombineArgs cb{};
+        nd.bytes = 0;  // depends on the loaded prefix lengths: computed by phx_expert_node_info
+        std::snprintf(nd.name, sizeof(nd.name), "attention");
+        h->node_list.push_back(nd);
+        Node nc{};
+        nc.kind = PHX_NODE_ATTN_COMBINE; nc.step = k; nc.layer = l;
+        CombineArgs& cb = nc.cb;
         cb.part_o = h->part_o; cb.part_ml = h->part_ml; cb.lens = h->lens; cb.o = h->o;
         cb.M = M; cb.H = H; cb.KVH = KVH; cb.Dh = Dh; cb.SMAX = h->SMAX; cb.GMP = h->GMP;
-        PHX_HIP(launch_combine(h->dtype, cb, B, s));
-        n += 2;
+        nc.bytes = 0;
+        std::snprintf(nc.name, sizeof(nc.name), "attention_combine");
+        h->node_list.push_back(nc);
       }
       // a4: out-projection + residual
       {
         GemmArgs g{};
-        g.W = (const char*)h->wt + h->off_o[l] * h->esz;
+        g.W = (const char*)h->wt + h->off_o[l] * esz;
         g.KT = h->p_o.KT; g.NT = h->p_o.NT; g.KSW = h->p_o.KSW; g.rows = h->BM;
         g.X = h->o; g.ldx = H * Dh;
         g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
         g.part = h->gpart; g.counters = h->counters;
-        PHX_HIP(launch_gemm(h->dtype, h->p_o.NW, h->MT, PRO_X, EPI_RESID, g, s));
-        ++n;
+        gemm_node(PHX_NODE_OUT_PROJ_RESID, k, l, h->p_o, PRO_X, EPI_RESID, g, H * Dh, D, "out_proj_resid");
       }
       // a5: AdaRMSNorm + gate/up + GeGLU
       {
         GemmArgs g{};
-        g.W = (const char*)h->wt + h->off_gu[l] * h->esz;
+        g.W = (const char*)h->wt + h->off_gu[l] * esz;
         g.KT = h->p_gu.KT; g.NT = h->p_gu.NT; g.KSW = h->p_gu.KSW; g.rows = h->BM;
         g.h = h->h; g.ss = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D; g.eps = c.rms_eps;
         g.mod = mod_k + (size_t)(2 * l + 1) * D2;
         g.part = h->gpart; g.counters = h->counters;
         g.act = h->act; g.F = F;
-        PHX_HIP(launch_gemm(h->dtype, h->p_gu.NW, h->MT, PRO_NORM, EPI_GEGLU, g, s));
-        ++n;
+        gemm_node(PHX_NODE_NORM_GATEUP_GEGLU, k, l, h->p_gu, PRO_NORM, EPI_GEGLU, g, D, 2 * F, "norm_gateup_geglu");
       }
       // a6: down-projection + residual
       {
         GemmArgs g{};
-        g.W = (const char*)h->wt + h->off_down[l] * h->esz;
+        g.W = (const char*)h->wt + h->off_down[l] * esz;
         g.KT = h->p_down.KT; g.NT = h->p_down.NT; g.KSW = h->p_down.KSW; g.rows = h->BM;
         g.X = h->act; g.ldx = F;
         g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
         g.part = h->gpart; g.counters = h->counters;
-        PHX_HIP(launch_gemm(h->dtype, h->p_down.NW, h->MT, PRO_X, EPI_RESID, g, s));
-        ++n;
+        gemm_node(PHX_NODE_DOWN_PROJ_RESID, k, l, h->p_down, PRO_X, EPI_RESID, g, F, D, "down_proj_resid");
       }
     }
     // a7: final AdaRMSNorm + velocity projection + Euler update
     {
       GemmArgs g{};
-      g.W = (const char*)h->wt + h->off_out * h->esz;
+      g.W = (const char*)h->wt + h->off_out * esz;
       g.KT = h->p_out.KT; g.NT = h->p_out.NT; g.KSW = h->p_out.KSW; g.rows = h->BM;
       g.h = h->h; g.ss = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D; g.eps = c.rms_eps;
       g.mod = mod_k + (size_t)(2 * NL) * D2;
       g.part = h->gpart; g.counters = h->counters;
       g.x = h->x; g.dt = c.dt; g.A = A;
-      PHX_HIP(launch_gemm(h->dtype, h->p_out.NW, h->MT, PRO_NORM, EPI_EULER, g, s));
-      ++n;
+      gemm_node(PHX_NODE_NORM_OUT_EULER, k, -1, h->p_out, PRO_NORM, EPI_EULER, g, D, A, "norm_out_proj_euler");
     }
   }
-  if (nodes) *nodes = n;
+  return PHX_OK;
+}
+
+int launch_node(phx_expert* h, const Node& nd, hipStream_t s) {
+  switch (nd.kind) {
+    case PHX_NODE_ATTENTION:
+      PHX_HIP(launch_attention(h->dtype, h->QT, nd.at, h->cfg.batch, s));
+      break;
+    case PHX_NODE_ATTN_COMBINE:
+      PHX_HIP(launch_combine(h->dtype, nd.cb, h->cfg.batch, s));
+      break;
+    default:
+      PHX_HIP(launch_gemm(h->dtype, nd.nw, h->MT, nd.pro, nd.epi, nd.g, s));
+  }
+  return PHX_OK;
+}
+
+// Enqueue one decision's step loop on stream s (graph capture or direct).
+int enqueue_steps(phx_expert* h, hipStream_t s) {
+  for (const Node& nd : h->node_list) {
+    int rc = launch_node(h, nd, s);
+    if (rc) return rc;
+  }
   return PHX_OK;
 }
 
@@ -431,11 +479,14 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
       }
   }
   h->loaded.assign(B, 0);
+  h->lens_host.assign(B, 0);
 
   // ---- capture the step loop ----
+  if ((rc = build_nodes(h))) return rc;
+  h->nodes = (int)h->node_list.size();
   if (!(c.flags & PHX_FLAG_NO_GRAPH)) {
     PHX_HIP(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
-    rc = enqueue_steps(h, h->cap, &h->nodes);
+    rc = enqueue_steps(h, h->cap);
     hipGraph_t g = nullptr;
     hipError_t e = hipStreamEndCapture(h->cap, &g);
     if (rc) {
@@ -445,8 +496,6 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
     if (e != hipSuccess) return fail(PHX_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
     h->graph = g;
     PHX_HIP(hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0));
-  } else {
-    h->nodes = c.steps * (2 + 6 * NL);
   }
   return PHX_OK;
 }
@@ -489,6 +538,7 @@ int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, con
                              request, prefix_len, s));
   PHX_HIP(launch_position_table(h->lens, h->rope, request, prefix_len, c.rows, c.head_dim, (double)c.rope_base, s));
   h->loaded[request] = 1;
+  h->lens_host[request] = prefix_len;
   g_err.clear();
   return PHX_OK;
 }
@@ -504,10 +554,41 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
   if (h->exec) {
     PHX_HIP(hipGraphLaunch(h->exec, s));
   } else {
-    int rc = enqueue_steps(h, s, nullptr);
+    int rc = enqueue_steps(h, s);
     if (rc) return rc;
   }
   PHX_HIP(hipMemcpyAsync(actions, h->x, xb, hipMemcpyDefault, s));
+  g_err.clear();
+  return PHX_OK;
+}
+
+int phx_expert_node_info(const phx_expert* h, int32_t node, phx_node_info* info) {
+  if (!h || !info) return fail(PHX_E_INVALID, "NULL argument");
+  if (node < 0 || node >= h->nodes) return fail(PHX_E_SHAPE, "node %d outside [0, %d)", node, h->nodes);
+  const Node& nd = h->node_list[(size_t)node];
+  std::memset(info, 0, sizeof(*info));
+  info->kind = nd.kind;
+  info->step = nd.step;
+  info->layer = nd.layer;
+  info->bytes = nd.bytes;
+  if (nd.kind == PHX_NODE_ATTENTION) {
+    // valid prefix rows plus the action rows, keys and values, of every request
+    const phx_expert_config& c = h->cfg;
+    uint64_t rows = 0;
+    for (int b = 0; b < c.batch; ++b) rows += (uint64_t)h->lens_host[(size_t)b] + (uint64_t)c.rows;
+    info->bytes = 2 * rows * (uint64_t)c.n_kv_heads * c.head_dim * h->esz;
+  }
+  std::snprintf(info->name, sizeof(info->name), "%s", nd.name);
+  return PHX_OK;
+}
+
+int phx_expert_launch_node(phx_expert* h, int32_t node, phx_stream_t stream) {
+  if (!h) return fail(PHX_E_INVALID, "handle is NULL");
+  if (node < 0 || node >= h->nodes) return fail(PHX_E_SHAPE, "node %d outside [0, %d)", node, h->nodes);
+  for (int b = 0; b < h->cfg.batch; ++b)
+    if (!h->loaded[(size_t)b]) return fail(PHX_E_STATE, "request %d has no prefix loaded", b);
+  int rc = launch_node(h, h->node_list[(size_t)node], (hipStream_t)stream);
+  if (rc) return rc;
   g_err.clear();
   return PHX_OK;
 }

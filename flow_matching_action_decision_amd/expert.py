@@ -78,6 +78,41 @@ class Expert:
     def kernels_per_decision(self) -> int:
         return B.phx_expert_kernels_per_decision(self.h)
 
+    def nodes(self) -> list:
+        """Every kernel launch of one decision, in replay order."""
+        return [B.phx_expert_node_info(self.h, i) for i in range(self.kernels_per_decision())]
+
+    def time_dominant_kernel(self, reps: int = 50) -> dict:
+        """Average duration of one launch of the kernel that streams the most
+        algorithmic bytes per decision.  Each launch (the first Euler step's
+        launches of that kernel, all layers in turn, `reps` rounds) is
+        bracketed by HIP events on the handle's stream."""
+        torch = self.torch
+        nodes = self.nodes()
+        per_kind = {}
+        for n in nodes:
+            per_kind[n["kind"]] = per_kind.get(n["kind"], 0) + n["bytes"]
+        kind = max(per_kind, key=per_kind.get)
+        idx = [i for i, n in enumerate(nodes) if n["kind"] == kind and n["step"] == 0]
+        stream = torch.cuda.current_stream(self.device)
+        for i in idx:  # warm
+            B.phx_expert_launch_node(self.h, i, self.stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps * len(idx))]
+        torch.cuda.synchronize(self.device)
+        j = 0
+        for _ in range(reps):
+            for i in idx:
+                a, b = ev[j]
+                a.record(stream)
+                B.phx_expert_launch_node(self.h, i, self.stream)
+                b.record(stream)
+                j += 1
+        torch.cuda.synchronize(self.device)
+        ms = [a.elapsed_time(b) for a, b in ev]
+        return dict(name=nodes[idx[0]]["name"], kind=kind, launches=len(ms),
+                    ms_per_launch=float(sum(ms) / len(ms)), bytes_per_launch=nodes[idx[0]]["bytes"])
+
     def close(self):
         if getattr(self, "h", 0):
             self.torch.cuda.synchronize(self.device)

@@ -174,6 +174,43 @@ PHX_API const char* phx_last_error(void);
 /* Number of kernel launches one decision replays (graph nodes). */
 PHX_API int phx_expert_kernels_per_decision(const phx_expert* h, int* count);
 
+/*
+ * Diagnostics: the kernel launches of one decision, in replay order, so a
+ * caller can time or profile them one at a time.
+ */
+#define PHX_NODE_IN_PROJ 1           /* h = x . W_in */
+#define PHX_NODE_NORM_QKV_ROPE 2     /* adaptive RMSNorm, one QKV projection, RoPE on q and k */
+#define PHX_NODE_ATTENTION 3         /* split-KV multi-query attention over prefix + action rows */
+#define PHX_NODE_ATTN_COMBINE 4      /* fixed-order merge of the key splits */
+#define PHX_NODE_OUT_PROJ_RESID 5    /* h += o . W_o */
+#define PHX_NODE_NORM_GATEUP_GEGLU 6 /* adaptive RMSNorm, merged gate/up projection, GeGLU */
+#define PHX_NODE_DOWN_PROJ_RESID 7   /* h += a . W_down */
+#define PHX_NODE_NORM_OUT_EULER 8    /* final adaptive RMSNorm, velocity projection, x += dt * v */
+
+typedef struct phx_node_info {
+  int32_t kind;    /* PHX_NODE_* */
+  int32_t step;    /* Euler step index */
+  int32_t layer;   /* decoder layer, -1 outside the layer stack */
+  int32_t reserved;
+  uint64_t bytes;  /* algorithmic HBM bytes of one launch: the weights it streams (plus the
+                      modulation rows of a norm), or the valid prefix and action K/V rows */
+  char name[32];
+} phx_node_info;
+
+/* Describes launch `node` (0 <= node < kernels_per_decision).  Returns PHX_OK,
+   PHX_E_INVALID or PHX_E_SHAPE. */
+PHX_API int phx_expert_node_info(const phx_expert* h, int32_t node, phx_node_info* info);
+
+/*
+ * Launches kernel `node` of the step loop once on stream, with the arguments
+ * it has in the captured graph.  It reads the handle's weights and prefix
+ * state and overwrites its working buffers (the state x, residual stream,
+ * queries, attention partials, action-row cache slots), so the next decision
+ * is unaffected: decide starts by copying in the noise.  Returns PHX_OK,
+ * PHX_E_INVALID, PHX_E_SHAPE, PHX_E_STATE or PHX_E_HIP.
+ */
+PHX_API int phx_expert_launch_node(phx_expert* h, int32_t node, phx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

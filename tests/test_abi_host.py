@@ -1,0 +1,100 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every
+function include/phx_expert.h declares, and its pure-host calls (config
+validation, blob size) behave as documented.  No compute calls."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import phx_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "phx_expert.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"PHX_API\s+[\w\s\*]+?\b(phx_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from flow_matching_action_decision_amd import binding
+    return binding.load_library()
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("phx_expert_create", "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_destroy"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from flow_matching_action_decision_amd import binding
+    names = _declared()
+    assert set(names) == set(binding.EXPORTED), "binding and header disagree"
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_struct_layout_matches_header(lib):
+    from flow_matching_action_decision_amd import binding
+    # 14 int32-sized fields + 4 floats + 3 int32 = 21 * 4 bytes
+    assert ctypes.sizeof(binding.phx_expert_config) == 84
+    assert ctypes.sizeof(binding.phx_node_info) == 56
+
+
+def _cfg(**kw):
+    from flow_matching_action_decision_amd import binding
+    c = binding.make_config(phx_inputs.workload("pi05_expert_bf16"))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_validate_accepts_the_workloads(lib):
+    from flow_matching_action_decision_amd import binding
+    for name in phx_inputs.WORKLOADS:
+        c = binding.make_config(phx_inputs.workload(name))
+        assert binding.phx_expert_validate_config(c) == 0, binding.phx_last_error()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("abi_version", 99, -2), ("struct_size", 12, -2), ("layers", 0, -3), ("width", 1000, -3),
+    ("head_dim", 96, -3), ("n_kv_heads", 3, -3), ("mlp_hidden", 100, -3), ("state_dim", 7, -3),
+    ("rows", 0, -3), ("batch", 17, -3), ("prefix_capacity", -1, -3), ("steps", 0, -3),
+    ("time_emb_dim", 3, -3), ("rms_eps", 0.0, -1), ("rope_base", -1.0, -1), ("weight_dtype", 7, -1),
+    ("kv_dtype", 0, -3), ("flags", 0x80, -1),
+])
+def test_validate_rejects(lib, field, value, code):
+    from flow_matching_action_decision_amd import binding
+    c = _cfg(**{field: value})
+    assert binding.phx_expert_validate_config(c) == code
+    assert binding.phx_last_error()
+
+
+def test_validate_null(lib):
+    assert lib.phx_expert_validate_config(None) == -1
+
+
+def test_weights_bytes_matches_the_input_layout(lib):
+    from flow_matching_action_decision_amd import binding
+    for name in phx_inputs.WORKLOADS:
+        cfg = phx_inputs.workload(name)
+        esz = 2 if cfg["dtype"] == "bf16" else 4
+        assert binding.phx_expert_weights_bytes(binding.make_config(cfg)) == phx_inputs.weight_count(cfg) * esz
+
+
+def test_null_handles_are_rejected_without_a_gpu(lib):
+    assert lib.phx_expert_load_prefix_kv(None, 0, None, None, 0, None) == -1
+    assert lib.phx_expert_decide(None, None, None, None) == -1
+    n = ctypes.c_int(0)
+    assert lib.phx_expert_kernels_per_decision(None, ctypes.byref(n)) == -1
+    assert lib.phx_expert_launch_node(None, 0, None) == -1
+    lib.phx_expert_destroy(None)  # NULL-safe
+    out = ctypes.c_void_p(0)
+    from flow_matching_action_decision_amd import binding
+    c = _cfg()
+    assert lib.phx_expert_create(ctypes.byref(c), None, 0, None, ctypes.byref(out)) == -1
+    assert out.value is None
