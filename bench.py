@@ -64,7 +64,7 @@ def algorithmic_bytes(cfg: dict) -> dict:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("phx_kernels.hip", "phx_engine.cpp", "phx_internal.h"):
+    for f in ("phx_kernels.hip", "phx_decide.hip", "phx_decide.h", "phx_engine.cpp", "phx_internal.h"):
         with open(os.path.join(ROOT, "flow_matching_action_decision_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

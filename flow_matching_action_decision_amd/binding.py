@@ -17,14 +17,18 @@ PHX_ABI_VERSION = 1
 PHX_OK, PHX_E_INVALID, PHX_E_VERSION, PHX_E_SHAPE, PHX_E_STATE, PHX_E_NOMEM, PHX_E_HIP = 0, -1, -2, -3, -4, -5, -6
 PHX_DTYPE_F32, PHX_DTYPE_BF16 = 0, 1
 PHX_FLAG_NO_GRAPH = 1
+PHX_FLAG_MULTI_KERNEL = 2
+PHX_FLAG_TIMELINE = 4
 
 # every function include/phx_expert.h declares
 EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_expert_create",
             "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_destroy", "phx_last_error",
-            "phx_expert_kernels_per_decision", "phx_expert_node_info", "phx_expert_launch_node")
+            "phx_expert_kernels_per_decision", "phx_expert_node_info", "phx_expert_launch_node",
+            "phx_expert_status", "phx_expert_timeline")
 
 NODE_KINDS = {1: "in_proj", 2: "norm_qkv_rope", 3: "attention", 4: "attention_combine", 5: "out_proj_resid",
-              6: "norm_gateup_geglu", 7: "down_proj_resid", 8: "norm_out_proj_euler"}
+              6: "norm_gateup_geglu", 7: "down_proj_resid", 8: "norm_out_proj_euler", 9: "decision_kernel",
+              10: "tag_advance"}
 
 
 class phx_expert_config(ctypes.Structure):
@@ -75,6 +79,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phx_expert_kernels_per_decision.argtypes = [P, ctypes.POINTER(ctypes.c_int)]
     lib.phx_expert_node_info.argtypes = [P, ctypes.c_int32, ctypes.POINTER(phx_node_info)]
     lib.phx_expert_launch_node.argtypes = [P, ctypes.c_int32, P]
+    lib.phx_expert_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+    lib.phx_expert_timeline.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_size_t,
+                                        ctypes.POINTER(ctypes.c_size_t)]
     _lib = lib
     return lib
 
@@ -146,3 +153,24 @@ def phx_expert_node_info(h: int, node: int) -> dict:
 
 def phx_expert_launch_node(h: int, node: int, stream: int = 0):
     _check(load_library().phx_expert_launch_node(ctypes.c_void_p(h), node, ctypes.c_void_p(stream)))
+
+
+def phx_expert_status(h: int) -> int:
+    st = ctypes.c_uint32(0)
+    _check(load_library().phx_expert_status(ctypes.c_void_p(h), ctypes.byref(st)))
+    return st.value
+
+
+def phx_expert_timeline(h: int):
+    """Per-workgroup phase timeline as a numpy array [workgroups][events] of
+    uint32 ticks of the 100 MHz real-time counter."""
+    import numpy as np
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    lib.phx_expert_timeline(ctypes.c_void_p(h), None, 0, ctypes.byref(n))
+    if n.value == 0:
+        _check(PHX_E_STATE)
+    out = np.zeros(n.value, dtype=np.uint32)
+    _check(lib.phx_expert_timeline(ctypes.c_void_p(h), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), n.value,
+                                   ctypes.byref(n)))
+    return out.reshape(256, -1)

@@ -75,6 +75,13 @@ class Expert:
         B.phx_expert_decide(self.h, noise.data_ptr(), out.data_ptr(), self.stream)
         return out
 
+    def status(self) -> int:
+        """0 if the last decision completed; nonzero if the persistent kernel gave up waiting."""
+        return B.phx_expert_status(self.h)
+
+    def timeline(self):
+        return B.phx_expert_timeline(self.h)
+
     def kernels_per_decision(self) -> int:
         return B.phx_expert_kernels_per_decision(self.h)
 
@@ -93,7 +100,8 @@ class Expert:
         for n in nodes:
             per_kind[n["kind"]] = per_kind.get(n["kind"], 0) + n["bytes"]
         kind = max(per_kind, key=per_kind.get)
-        idx = [i for i, n in enumerate(nodes) if n["kind"] == kind and n["step"] == 0]
+        first_step = min(n["step"] for n in nodes if n["kind"] == kind)
+        idx = [i for i, n in enumerate(nodes) if n["kind"] == kind and n["step"] == first_step]
         stream = torch.cuda.current_stream(self.device)
         for i in idx:  # warm
             B.phx_expert_launch_node(self.h, i, self.stream)

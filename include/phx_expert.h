@@ -63,8 +63,12 @@ extern "C" {
 #define PHX_DTYPE_BF16 1
 
 /* execution flags */
-#define PHX_FLAG_NO_GRAPH 1u   /* launch the step loop's kernels directly instead of replaying the
-                                  captured graph (same kernels, same results; for diagnosis) */
+#define PHX_FLAG_NO_GRAPH 1u   /* launch the multi-kernel step loop's kernels directly instead of
+                                  replaying the captured graph (same kernels, same results; for diagnosis) */
+#define PHX_FLAG_MULTI_KERNEL 2u  /* run the multi-kernel graph even where the persistent decision kernel
+                                     applies (for comparison) */
+#define PHX_FLAG_TIMELINE 4u   /* persistent kernel: record a per-workgroup phase timeline (see
+                                  phx_expert_timeline) */
 
 /* A HIP stream (hipStream_t is a pointer to this incomplete type). NULL means
    the default stream. */
@@ -186,6 +190,9 @@ PHX_API int phx_expert_kernels_per_decision(const phx_expert* h, int* count);
 #define PHX_NODE_NORM_GATEUP_GEGLU 6 /* adaptive RMSNorm, merged gate/up projection, GeGLU */
 #define PHX_NODE_DOWN_PROJ_RESID 7   /* h += a . W_down */
 #define PHX_NODE_NORM_OUT_EULER 8    /* final adaptive RMSNorm, velocity projection, x += dt * v */
+#define PHX_NODE_DECISION 9          /* the persistent kernel that runs a whole decision (launching it
+                                        diagnostically also advances the exchange tags) */
+#define PHX_NODE_TAG_ADVANCE 10      /* advances the persistent kernel's exchange tags */
 
 typedef struct phx_node_info {
   int32_t kind;    /* PHX_NODE_* */
@@ -210,6 +217,32 @@ PHX_API int phx_expert_node_info(const phx_expert* h, int32_t node, phx_node_inf
  * PHX_E_INVALID, PHX_E_SHAPE, PHX_E_STATE or PHX_E_HIP.
  */
 PHX_API int phx_expert_launch_node(phx_expert* h, int32_t node, phx_stream_t stream);
+
+/*
+ * Status of the last decision of the persistent decision kernel
+ * (synchronous; call after the stream has passed the decision).  0 means it
+ * completed; 1 means a workgroup waited longer than its limit (0.5 s) for
+ * data another workgroup should have produced, the decision gave up, and its
+ * actions were filled with NaN.  Always 0 for the multi-kernel path.
+ * Returns PHX_OK, PHX_E_INVALID or PHX_E_HIP.
+ */
+PHX_API int phx_expert_status(const phx_expert* h, uint32_t* status);
+
+/*
+ * Phase timeline of the last decision of a handle created with
+ * PHX_FLAG_TIMELINE (synchronous).  The persistent kernel is one launch, so
+ * a profiler sees one kernel; this records, per workgroup, the 100 MHz
+ * real-time counter (low 32 bits) when its compute waves finished each phase:
+ * out[wg * E + e] with E = 3 + steps * (2 + 7 * layers) events: e = 0 start;
+ * for step k, base b = 1 + k * (2 + 7 * layers): b input projection, then
+ * b + 1 + 7 l + {0 qkv, 1 attention, 2 combine, 3 out projection, 4 gate/up,
+ * 5 down, 6 residual add} for layer l, then b + 1 + 7 * layers velocity head;
+ * E - 2 compute end, E - 1 weight streaming end.  256 workgroups.
+ * If out is NULL or capacity is too small, *count receives the size needed
+ * and PHX_E_SHAPE is returned.  Returns PHX_OK, PHX_E_INVALID, PHX_E_STATE
+ * (no timeline), PHX_E_SHAPE or PHX_E_HIP.
+ */
+PHX_API int phx_expert_timeline(const phx_expert* h, uint32_t* out, size_t capacity, size_t* count);
 
 #ifdef __cplusplus
 }

@@ -64,7 +64,17 @@ def test_pi05_expert_bf16_workload():
     for o in outs:
         assert np.array_equal(o, outs[0]), "replays must be bit-identical"
     say(f"  kernels per decision: {nk}")
+    assert nk == 2, "the pi0.5 shape runs as one persistent decision kernel plus its tag advance"
+
+
+def test_pi05_expert_bf16_multi_kernel_path():
+    """The same workload through the multi-kernel graph (forced by flag)."""
+    from flow_matching_action_decision_amd import PHX_FLAG_MULTI_KERNEL
+    cfg = phx_inputs.workload("pi05_expert_bf16")
+    inp = phx_inputs.make_inputs(cfg, 0)
+    outs, nk = gpu_decide(cfg, inp, flags=PHX_FLAG_MULTI_KERNEL)
     assert nk == cfg["steps"] * (2 + 6 * cfg["layers"])
+    assert_close(outs[0], oracle_decide(cfg, inp), TOL_BF16, what="pi05 multi-kernel")
 
 
 def test_rollout_b16_sampled_requests():
