@@ -125,13 +125,11 @@ struct phx_expert {
   // persistent decision kernel (pi0.5 shape, one request)
   bool persistent = false;
   dec::Args dargs{};
-  void* aux = nullptr;
-  void* ex = nullptr;
+  void* arena = nullptr;      // exchange words, then the auxiliary tables (dec::AUX0)
   void* kvt = nullptr;
   int n_chunks = 0;
-  unsigned seq_host = 0;      // decisions launched since the exchange arena was last cleared
-  unsigned seq_limit = 0;     // clear the arena before the tag space wraps
-  size_t ex_bytes = 0;
+  unsigned seq_host = 0;      // decisions launched since the exchange words were last cleared
+  unsigned seq_limit = 0;     // clear them before the tag space wraps
 };
 
 namespace {
@@ -323,173 +321,97 @@ bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop
   if (n_chunks + 1 > dec::MAX_CHUNKS) return false;
   if (prop.multiProcessorCount != dec::G) return false;
   if (prop.maxSharedMemoryPerMultiProcessor < 160 * 1024) return false;
+  // every arena must stay within the 32-bit range of a buffer resource
+  if (dec::w_elems(c.layers) * 2ull >= (1ull << 32)) return false;
+  const unsigned long long arena = (unsigned long long)dec::AUX0 + dec::AUX_TAB +
+                                   (unsigned long long)c.steps * dec::step_bytes(c.layers) +
+                                   (unsigned long long)dec::G * dec::timeline_events(c.steps, c.layers) * 4ull;
+  if (arena >= (1ull << 31)) return false;
   return true;
-}
-
-// Workgroup roles of the persistent kernel.  Every workgroup takes one
-// gate/up n-tile pair and one down-projection block; attention workgroup
-// (head h, chunk c) is c + 32 h, so the heads of a key chunk share an XCD
-// (workgroup i runs on XCD i % 8) and its K/V tiles are fetched from HBM once
-// into that XCD's L2; the 64 residual-column owners and the 80 QKV n-tile
-// pairs go to workgroups without prefix K/V first, so that each workgroup
-// streams about the same number of tiles per layer.
-std::vector<dec::Role> make_roles(int n_chunks) {
-  std::vector<dec::Role> roles(dec::G);
-  for (int i = 0; i < dec::G; ++i) {
-    dec::Role& r = roles[(size_t)i];
-    r.qkv_nt0 = 0; r.n_qkv = 0; r.owner = -1; r.attn_h = -1; r.attn_c = -1; r.comb_h = -1; r.comb_s = -1;
-    r.gu_nt0 = (int16_t)(2 * i); r.n_gu = 2;
-    r.dn_kq = (int16_t)(i / dec::DN_NQ); r.dn_nq = (int16_t)(i % dec::DN_NQ);
-    r.out_nt = -1;
-    for (int q = 0; q < 4; ++q) r.pad[q] = 0;
-  }
-  for (int hh = 0; hh < dec::H; ++hh)
-    for (int ch = 0; ch <= n_chunks; ++ch) {
-      dec::Role& r = roles[(size_t)(ch + 32 * hh)];
-      r.attn_h = (int16_t)hh;
-      r.attn_c = (int16_t)ch;
-    }
-  std::vector<int> order;
-  for (int i = 0; i < dec::G; ++i)
-    if (!(roles[(size_t)i].attn_c >= 0 && roles[(size_t)i].attn_c < n_chunks)) order.push_back(i);
-  for (int i = 0; i < dec::G; ++i)
-    if (roles[(size_t)i].attn_c >= 0 && roles[(size_t)i].attn_c < n_chunks) order.push_back(i);
-  size_t pos = 0;
-  for (int j = 0; j < dec::NTD; ++j) roles[(size_t)order[pos++ % order.size()]].owner = (int16_t)j;
-  for (int p = 0; p < dec::NT_QKV / 2; ++p) {
-    dec::Role& r = roles[(size_t)order[pos++ % order.size()]];
-    r.qkv_nt0 = (int16_t)(2 * p);
-    r.n_qkv = 2;
-  }
-  for (int hh = 0; hh < dec::H; ++hh)
-    for (int sl = 0; sl < 8; ++sl) {
-      dec::Role& r = roles[(size_t)(32 * hh + 16 + sl)];
-      r.comb_h = (int16_t)hh;
-      r.comb_s = (int16_t)sl;
-    }
-  roles[dec::G - 2].out_nt = 0;
-  roles[dec::G - 1].out_nt = 1;
-  return roles;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int enqueue_persistent(phx_expert* h, hipStream_t s) {
   PHX_HIP(dec::launch_decide(h->dargs, s));
-  PHX_HIP(dec::launch_decide_advance(h->aux, h->dargs.o_seq, s));
+  PHX_HIP(dec::launch_decide_advance(h->arena, s));
   return PHX_OK;
 }
 
-// Everything the persistent path needs after the weights are tiled: the
-// auxiliary arena (step tables, shift . W tables, position table, state,
-// roles, counters), the exchange arena, the attention-tiled prefix K/V, and a
-// two-node graph (decision kernel, tag advance).
+// Everything the persistent path needs after the weights are tiled: one
+// arena holding the exchange words and then the auxiliary tables (counters,
+// state, position table, per-step scale and shift . W tables, timeline), the
+// attention-tiled prefix K/V, and a two-node graph (decision kernel, tag
+// advance).  Workgroup roles are a function of the workgroup index and the
+// chunk count, computed in the kernel.
 int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_off_elems) {
   const phx_expert_config& c = h->cfg;
-  const int S = c.steps, NL = c.layers, E = c.time_emb_dim, M = c.rows;
+  const int S = c.steps, NL = c.layers, E = c.time_emb_dim;
   h->n_chunks = (c.prefix_capacity + dec::CHUNK - 1) / dec::CHUNK;
-  dec::Args& a = h->dargs;
-  size_t o = 0;
-  auto take = [&](size_t bytes) { const size_t r = o; o = align256(o + bytes); return r; };
-  a.o_mod = (unsigned)take((size_t)S * h->NN * 2 * dec::D * sizeof(float));
-  a.o_swqkv = (unsigned)take((size_t)S * NL * dec::NQKV * sizeof(float));
-  a.o_swgu = (unsigned)take((size_t)S * NL * 2 * dec::F * sizeof(float));
-  a.o_swout = (unsigned)take((size_t)S * dec::A * sizeof(float));
-  a.o_rope = (unsigned)take((size_t)M * (dec::DH / 2) * sizeof(float2));
-  a.o_lens = (unsigned)take(sizeof(int));
-  a.o_x = (unsigned)take((size_t)M * dec::A * sizeof(float));
-  a.o_roles = (unsigned)take((size_t)dec::G * sizeof(dec::Role));
-  a.o_status = (unsigned)take(sizeof(unsigned));
-  a.o_seq = (unsigned)take(sizeof(unsigned));
-  a.o_tl = 0;
-  if (c.flags & PHX_FLAG_TIMELINE)
-    a.o_tl = (unsigned)take((size_t)dec::G * dec::timeline_events(S, NL) * sizeof(unsigned));
-  const size_t aux_bytes = o;
+  const bool timeline = (c.flags & PHX_FLAG_TIMELINE) != 0;
+  const size_t arena_bytes = (size_t)dec::AUX0 + dec::aux_bytes(S, NL, timeline);
   int rc;
-  if ((rc = alloc(h, &h->aux, aux_bytes, "auxiliary arena"))) return rc;
-  PHX_HIP(hipMemsetAsync(h->aux, 0, aux_bytes, stream));
-  char* ab = (char*)h->aux;
-  h->modtab = (float*)(ab + a.o_mod);
-  h->rope = (float2*)(ab + a.o_rope);
-  h->lens = (int*)(ab + a.o_lens);
-  h->x = (float*)(ab + a.o_x);
+  if ((rc = alloc(h, &h->arena, arena_bytes, "decision arena"))) return rc;
+  PHX_HIP(hipMemsetAsync(h->arena, 0, arena_bytes, stream));
+  char* aux = (char*)h->arena + dec::AUX0;
+  h->rope = (float2*)(aux + dec::AUX_ROPE);
+  h->lens = (int*)(aux + dec::AUX_LENS);
+  h->x = (float*)(aux + dec::AUX_X);
 
-  // step-conditioning table, then the shift . W products of every norm
+  // step-conditioning table, then per step: the scales of every norm and the
+  // shift . W products of the QKV, gate/up and velocity-head norms
   void* etab = nullptr;
   if ((rc = alloc(h, &etab, (size_t)S * E * sizeof(double), "time embedding"))) return rc;
+  if ((rc = alloc(h, (void**)&h->modtab, (size_t)S * h->NN * 2 * dec::D * sizeof(float), "modulation table")))
+    return rc;
   PHX_HIP(launch_time_embedding((double*)etab, S, E, c.tau0, c.dt, stream));
   PHX_HIP(launch_modulation(h->dtype, sb + mod_off_elems * h->esz, (const double*)etab, h->modtab, S, h->NN, E,
                             2 * dec::D, stream));
-  const long long lstride = (long long)(h->off_qkv.size() > 1 ? h->off_qkv[1] - h->off_qkv[0] : 0);
+  PHX_HIP(dec::launch_scale_table(h->modtab, S, h->NN, h->arena, NL, stream));
+  const long long lstride = (long long)dec::W_LAYER;
+  const size_t ks = dec::step_bytes(NL) / sizeof(float);
+  char* tab = aux + dec::AUX_TAB;
   PHX_HIP(dec::launch_shift_table(sb + h->off_qkv[0] * h->esz, lstride, h->modtab, h->NN, 2, 0, S, NL, dec::NQKV,
-                                  COL_ROPE, dec::DH, (float*)(ab + a.o_swqkv), stream));
+                                  COL_ROPE, dec::DH, (float*)(tab + dec::st_swqkv(NL)), ks, stream));
   PHX_HIP(dec::launch_shift_table(sb + h->off_gu[0] * h->esz, lstride, h->modtab, h->NN, 2, 1, S, NL, 2 * dec::F,
-                                  COL_GEGLU, dec::F, (float*)(ab + a.o_swgu), stream));
+                                  COL_GEGLU, dec::F, (float*)(tab + dec::st_swgu(NL)), ks, stream));
   PHX_HIP(dec::launch_shift_table(sb + h->off_out * h->esz, 0, h->modtab, h->NN, 0, 2 * NL, S, 1, dec::A, COL_IDENT,
-                                  0, (float*)(ab + a.o_swout), stream));
-  const std::vector<dec::Role> roles = make_roles(h->n_chunks);
-  PHX_HIP(hipMemcpyAsync(ab + a.o_roles, roles.data(), roles.size() * sizeof(dec::Role), hipMemcpyHostToDevice,
-                         stream));
-
-  // exchange arena: every buffer twice (by step-layer parity)
-  const size_t words[dec::NX] = {
-      (size_t)dec::RP * (dec::D / 2),                                   // X_HS
-      (size_t)dec::RP * dec::NTD,                                       // X_SS
-      (size_t)(dec::H + 2) * dec::RP * (dec::DH / 2),                   // X_Q
-      (size_t)dec::H * dec::MAX_CHUNKS * dec::RP * (dec::DH + 2),       // X_ATT (outputs, then max/sum)
-      (size_t)dec::RP * (dec::HD / 2),                                  // X_O
-      (size_t)dec::RP * (dec::D / 2),                                   // X_HS1
-      (size_t)dec::RP * dec::NTD,                                       // X_SS1
-      (size_t)dec::RP * (dec::F / 2),                                   // X_A
-      (size_t)dec::DN_KQ * dec::RP * dec::D,                            // X_DP
-      (size_t)dec::RP * (dec::A / 2),                                   // X_X
-  };
-  size_t eo = 0;
-  for (int t = 0; t < dec::NX; ++t)
-    for (int p = 0; p < 2; ++p) {
-      a.ex_off[t][p] = (unsigned)eo;
-      eo = align256(eo + words[t] * 8);
-    }
-  h->ex_bytes = eo;
-  if ((rc = alloc(h, &h->ex, eo, "exchange arena"))) return rc;
-  PHX_HIP(hipMemsetAsync(h->ex, 0, eo, stream));
+                                  0, (float*)(tab + dec::st_swout(NL)), ks, stream));
 
   // attention-tiled prefix K/V
   const size_t kvt_bytes = (size_t)NL * h->n_chunks * 64 * dec::TILE_BYTES;
-  if ((rc = alloc(h, &h->kvt, kvt_bytes, "attention key/value tiles"))) return rc;
-  PHX_HIP(hipMemsetAsync(h->kvt, 0, kvt_bytes, stream));
+  if ((rc = alloc(h, &h->kvt, std::max(kvt_bytes, (size_t)dec::TILE_BYTES), "attention key/value tiles"))) return rc;
+  PHX_HIP(hipMemsetAsync(h->kvt, 0, std::max(kvt_bytes, (size_t)dec::TILE_BYTES), stream));
   PHX_HIP(hipStreamSynchronize(stream));
-  for (size_t i = 0; i < h->allocs.size(); ++i)
-    if (h->allocs[i] == etab) {
-      (void)hipFree(etab);
-      h->allocs.erase(h->allocs.begin() + (long)i);
-      break;
-    }
+  for (void* p : {etab, (void*)h->modtab})
+    for (size_t i = 0; i < h->allocs.size(); ++i)
+      if (h->allocs[i] == p) {
+        (void)hipFree(p);
+        h->allocs.erase(h->allocs.begin() + (long)i);
+        break;
+      }
+  h->modtab = nullptr;
 
+  // the kernel addresses the tiled weights with compile-time offsets
+  if (h->off_in != 0 || h->off_qkv[0] != dec::W_QKV0 || h->off_o[0] != dec::W_O0 || h->off_gu[0] != dec::W_GU0 ||
+      h->off_down[0] != dec::W_DN0 || h->off_out != dec::w_out(NL) ||
+      (NL > 1 && h->off_qkv[1] - h->off_qkv[0] != dec::W_LAYER))
+    return fail(PHX_E_SHAPE, "tiled weight layout differs from the decision kernel's");
+
+  dec::Args& a = h->dargs;
   a.wt = h->wt;
-  a.wt_bytes = (unsigned)((h->off_out + (size_t)dec::D * dec::A) * h->esz);
-  a.off_in = (long long)h->off_in;
-  a.off_qkv = (long long)h->off_qkv[0];
-  a.off_o = (long long)h->off_o[0];
-  a.off_gu = (long long)h->off_gu[0];
-  a.off_dn = (long long)h->off_down[0];
-  a.off_out = (long long)h->off_out;
-  a.lstride = lstride;
   a.kvt = h->kvt;
+  a.arena = h->arena;
+  a.wt_bytes = (unsigned)(dec::w_elems(NL) * 2ull);
   a.kvt_bytes = (unsigned)kvt_bytes;
-  a.kv_lstride = (long long)h->n_chunks * 64 * 512;
-  a.aux = h->aux;
-  a.aux_bytes = (unsigned)aux_bytes;
-  a.ex = h->ex;
-  a.ex_bytes = (unsigned)eo;
+  a.arena_bytes = (unsigned)arena_bytes;
+  a.tl = timeline ? 1u : 0u;
   a.S = S;
   a.NL = NL;
-  a.R = M;
-  a.M = M;
+  a.R = c.rows;
   a.n_chunks = h->n_chunks;
   a.dt = c.dt;
   a.eps = c.rms_eps;
-  a.timeout_ticks = 50u * 1000u * 1000u;  // 0.5 s at the 100 MHz real-time counter
   const unsigned expd = dec::exchanges_per_decision(S, NL);
   h->seq_limit = (unsigned)((0xffffffffull / expd) - 2);
   h->seq_host = 0;
@@ -800,9 +722,8 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
   const size_t xb = (size_t)h->BM * h->cfg.state_dim * sizeof(float);
   if (h->persistent && h->seq_host >= h->seq_limit) {
     // exchange tags would wrap: start the tag space over on cleared buffers
-    PHX_HIP(hipMemsetAsync(h->ex, 0, h->ex_bytes, s));
-    PHX_HIP(hipMemsetAsync((char*)h->aux + h->dargs.o_seq, 0, sizeof(unsigned), s));
-    PHX_HIP(hipMemsetAsync((char*)h->aux + h->dargs.o_status, 0, sizeof(unsigned), s));
+    PHX_HIP(hipMemsetAsync(h->arena, 0, dec::EX_BYTES, s));
+    PHX_HIP(hipMemsetAsync((char*)h->arena + dec::AUX0, 0, dec::AUX_LENS, s));  // status and counter
     h->seq_host = 0;
   }
   PHX_HIP(hipMemcpyAsync(h->x, noise, xb, hipMemcpyDefault, s));
@@ -862,7 +783,7 @@ int phx_expert_launch_node(phx_expert* h, int32_t node, phx_stream_t stream) {
     if (rc) return rc;
     ++h->seq_host;
   } else if (h->persistent) {
-    PHX_HIP(dec::launch_decide_advance(h->aux, h->dargs.o_seq, (hipStream_t)stream));
+    PHX_HIP(dec::launch_decide_advance(h->arena, (hipStream_t)stream));
     ++h->seq_host;
   } else {
     rc = launch_node(h, h->node_list[(size_t)node], (hipStream_t)stream);
@@ -877,8 +798,8 @@ int phx_expert_status(const phx_expert* h, uint32_t* status) {
   *status = 0;
   if (!h->persistent) return PHX_OK;
   uint32_t w[2] = {0, 0};  // failing decision + 1, and the counter (already advanced past the last decision)
-  PHX_HIP(hipMemcpy(&w[0], (const char*)h->aux + h->dargs.o_status, sizeof(uint32_t), hipMemcpyDeviceToHost));
-  PHX_HIP(hipMemcpy(&w[1], (const char*)h->aux + h->dargs.o_seq, sizeof(uint32_t), hipMemcpyDeviceToHost));
+  PHX_HIP(hipMemcpy(w, (const char*)h->arena + dec::AUX0 + dec::AUX_STATUS, 2 * sizeof(uint32_t),
+                    hipMemcpyDeviceToHost));
   *status = (w[0] != 0 && w[0] == w[1]) ? 1u : 0u;
   return PHX_OK;
 }
@@ -886,13 +807,14 @@ int phx_expert_status(const phx_expert* h, uint32_t* status) {
 int phx_expert_timeline(const phx_expert* h, uint32_t* out, size_t capacity, size_t* count) {
   if (!h || !count) return fail(PHX_E_INVALID, "NULL argument");
   *count = 0;
-  if (!h->persistent || h->dargs.o_tl == 0) return fail(PHX_E_STATE, "no timeline: create the handle with PHX_FLAG_TIMELINE");
+  if (!h->persistent || h->dargs.tl == 0) return fail(PHX_E_STATE, "no timeline: create the handle with PHX_FLAG_TIMELINE");
   const size_t n = (size_t)dec::G * dec::timeline_events(h->cfg.steps, h->cfg.layers);
   if (!out || capacity < n) {
     *count = n;
     return fail(PHX_E_SHAPE, "timeline needs %zu words", n);
   }
-  PHX_HIP(hipMemcpy(out, (const char*)h->aux + h->dargs.o_tl, n * sizeof(uint32_t), hipMemcpyDeviceToHost));
+  PHX_HIP(hipMemcpy(out, (const char*)h->arena + dec::AUX0 + dec::aux_timeline(h->cfg.steps, h->cfg.layers),
+                    n * sizeof(uint32_t), hipMemcpyDeviceToHost));
   *count = n;
   return PHX_OK;
 }
