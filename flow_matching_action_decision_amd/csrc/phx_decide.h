@@ -39,7 +39,7 @@ constexpr int NT_OUT = A / 16;      // 2
 constexpr int DN_KQ = 16;           // down projection: K groups of 8 k-tiles
 constexpr int DN_NQ = 16;           // and N groups of 4 n-tiles
 constexpr int CHUNK = 64;           // prefix keys per attention workgroup
-constexpr int MAX_CHUNKS = 31;      // prefix chunks + the action chunk, per head
+constexpr int MAX_CHUNKS = 16;      // prefix chunks + the action chunk, per head (one merge round)
 constexpr int G = 256;              // workgroups (one per CU)
 constexpr int RP = 16;              // padded action rows
 constexpr int TILE_BYTES = 1024;    // one 16x32 bf16 MFMA A tile

@@ -332,7 +332,6 @@ struct PB {
 template <int N, typename AF>
 __device__ __attribute__((always_inline)) inline void ll_poll(Ctx& c, const PB& pb, AF addr, unsigned tag,
                                                               u32x4 (&v)[N]) {
-  static_assert(N <= 64, "one probe lane per load");
   const unsigned t0 = now_ticks();
   unsigned spins = 0;
   while (true) {
@@ -348,8 +347,12 @@ __device__ __attribute__((always_inline)) inline void ll_poll(Ctx& c, const PB& 
 #pragma unroll
     for (int i = 0; i < N; ++i) acc |= (v[i][1] ^ tag) | (v[i][3] ^ tag);
     if (__ballot(acc != 0u) == 0ull) return;
+#ifdef PHX_POLL_RELOAD
+    keep_waiting(c, t0, spins);
+    continue;
+#endif
     // probe addresses: lane i takes load i's first stale word; lanes without
-    // a stale load repeat the first probe address
+    // a stale load repeat the highest stale load's probe
     unsigned pa = 0;
     bool any = false;
 #pragma unroll
@@ -358,7 +361,7 @@ __device__ __attribute__((always_inline)) inline void ll_poll(Ctx& c, const PB& 
       if (m != 0ull) {
         const LA la = addr(b, i);
         const unsigned a = __builtin_amdgcn_readfirstlane(la.so) + (unsigned)__shfl((int)la.vo, __builtin_ctzll(m));
-        pa = (c.lane == i || !any) ? a : pa;  // spare lanes repeat the highest stale load's probe
+        pa = (c.lane == i || !any) ? a : pa;
         any = true;
       }
     }
@@ -569,14 +572,19 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
   const unsigned slot = slot_of(c, k, l);
   const float scale = 0.0625f;  // 1/sqrt(256)
   const unsigned vo = ((unsigned)c.crow * (DH / 2) + 4u * (unsigned)c.g) * 8u;
-  // q of this head as 8 B fragments (dims 32 s + 8 g + [0, 8))
+  // q of this head as 8 B fragments (dims 32 s + 8 g + [0, 8)): wave w polls
+  // fragments 2w, 2w + 1 and the four waves share them through LDS
   bf16x8 qf[8];
   {
-    u32x4 v[16];
-    const PB pb{vo, 0u, xoff<X_Q>(slot) + (unsigned)(c.attn_h * RP) * (DH / 2) * 8u, 0u, 0u};
-    ll_poll<16>(c, pb, [](const PB& b, int i) { return frag_la(b.v0, b.s0, 128u, i); }, tag_of(c, slot, X_Q), v);
+    u32x4 v[4];
+    const PB pb{vo, 0u, xoff<X_Q>(slot) + (unsigned)(c.attn_h * RP) * (DH / 2) * 8u + 256u * (unsigned)c.wave, 0u, 0u};
+    ll_poll<4>(c, pb, [](const PB& b, int i) { return frag_la(b.v0, b.s0, 128u, i); }, tag_of(c, slot, X_Q), v);
+    u32x4* qs = (u32x4*)red_take(c);  // [8 fragments][64 lanes]
+    qs[(2 * c.wave) * 64 + c.lane] = __builtin_bit_cast(u32x4, frag_of(v[0], v[1]));
+    qs[(2 * c.wave + 1) * 64 + c.lane] = __builtin_bit_cast(u32x4, frag_of(v[2], v[3]));
+    cw_barrier(c);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = frag_of(v[2 * s], v[2 * s + 1]);
+    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, qs[s * 64 + c.lane]);
   }
   const unsigned p0 = (unsigned)k * c.n_step + c.n_in + (unsigned)l * c.n_layer + c.o_attn;
   wait_tiles(c, p0, 64);
@@ -715,7 +723,13 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
 }
 
 // merges the key chunks of head h for dims [32 s, 32 s + 32) and writes the
-// normalised attention output as bf16 pairs
+// normalised attention output as bf16 pairs.  Wave w polls chunks w, w + 4,
+// w + 8, w + 12: per chunk one load of the (max, sum) pairs (lane: row
+// lane % 16) and four loads of dims 32 s + 2 dp, + 1 of rows rg + 4 j.  The
+// (max, sum) pairs go to LDS; every lane then forms the row statistics over
+// all chunks and the weight exp(m_c - M) / L of each of its (chunk, row)
+// pairs once, so the merge itself is plain multiply-adds.  The four waves'
+// partial sums meet in LDS and each wave finishes one row group.
 __device__ __attribute__((always_inline)) inline void ph_comb(Ctx& c, int k, int l) {
   refresh(c);
   if (c.comb_h < 0) return;
@@ -726,20 +740,14 @@ __device__ __attribute__((always_inline)) inline void ph_comb(Ctx& c, int k, int
   const unsigned ob = xoff<X_ATT>(slot);
   const unsigned mlb = ob + X_ML;
   const int dp = c.lane & 15, rg = c.lane >> 4;
-  float M[4], Lsum[4], acc0[4], acc1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    M[i] = -INFINITY;
-    Lsum[i] = 0.f;
-    acc0[i] = acc1[i] = 0.f;
-  }
-  // chunks w, w + 4, w + 8, w + 12 of this wave in one poll (rounds of four):
-  // per chunk one load of the (max, sum) pairs (lane: row lane % 16, clamped)
-  // and four loads of dims 32 sl + 2 dp, + 1 of rows rg + 4 j (clamped)
-  for (int base = c.wave; base < nch; base += 4 * NCOMPUTE) {
-    u32x4 v[20];
-    const int R = c.R;
-    const int mrow = (c.lane & 15) < R ? (c.lane & 15) : R - 1;
+  const int R = c.R;
+  f32x4* red = red_take(c);
+  float* mls = (float*)red;                       // [MAX_CHUNKS][RP] max, then [MAX_CHUNKS][RP] sum
+  f32x4* part = red + (2 * MAX_CHUNKS * RP) / 4;  // [4 waves][2][64 lanes] partial sums (rows rg + 4i, 2 dims)
+  const int base = c.wave;
+  u32x4 v[20];
+  {
+    const int mrow = dp < R ? dp : R - 1;
     const PB pb{(unsigned)mrow * 16u, (unsigned)(2 * dp) * 8u, mlb + (unsigned)(hd * MAX_CHUNKS + base) * RP * 16u,
                 ob + ((unsigned)(hd * MAX_CHUNKS + base) * RP * DH + 32u * (unsigned)sl) * 8u, (unsigned)base};
     auto addr = [&](const PB& b, int i) -> LA {
@@ -751,55 +759,60 @@ __device__ __attribute__((always_inline)) inline void ph_comb(Ctx& c, int k, int
       return LA{b.v1 + row * DH * 8u, b.s1 + (unsigned)(NCOMPUTE * q) * RP * DH * 8u, need};
     };
     ll_poll<20>(c, pb, addr, tag, v);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int cc = base + NCOMPUTE * q;
+    if (cc < nch && c.lane < RP) {
+      mls[cc * RP + c.lane] = as_f(v[5 * q][0]);
+      mls[(MAX_CHUNKS + cc) * RP + c.lane] = as_f(v[5 * q][2]);
+    }
+  }
+  cw_barrier(c);
+  // statistics of row lane % 16 over every chunk (a chunk without valid keys has max -inf and sum 0)
+  float M = -INFINITY;
+  for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, mls[cc * RP + dp]);
+  float L = 0.f;
+  for (int cc = 0; cc < nch; ++cc) {
+    const float m = mls[cc * RP + dp];
+    if (m != -INFINITY) L += fexp(m - M) * mls[(MAX_CHUNKS + cc) * RP + dp];
+  }
+  const float invL = frcp(L);
+  float acc0[4], acc1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = rg + 4 * i;
+    const float Mr = __shfl(M, row), iLr = __shfl(invL, row);
+    acc0[i] = acc1[i] = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (base + NCOMPUTE * q >= nch) break;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mc = as_f((unsigned)__shfl((int)v[5 * q][0], rg + 4 * i));
-        const float lc = as_f((unsigned)__shfl((int)v[5 * q][2], rg + 4 * i));
-        if (mc != -INFINITY) {
-          const float mn = fmaxf(M[i], mc);
-          const float sa = M[i] == -INFINITY ? 0.f : fexp(M[i] - mn);
-          const float sb = fexp(mc - mn);
-          acc0[i] = acc0[i] * sa + as_f(v[5 * q + 1 + i][0]) * sb;
-          acc1[i] = acc1[i] * sa + as_f(v[5 * q + 1 + i][2]) * sb;
-          Lsum[i] = Lsum[i] * sa + lc * sb;
-          M[i] = mn;
-        }
+      const int cc = base + NCOMPUTE * q;
+      if (cc < nch) {
+        const float m = mls[cc * RP + row];
+        const float wgt = m == -INFINITY ? 0.f : fexp(m - Mr) * iLr;
+        acc0[i] += wgt * as_f(v[5 * q + 1 + i][0]);
+        acc1[i] += wgt * as_f(v[5 * q + 1 + i][2]);
       }
     }
   }
-  f32x4* red = red_take(c);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[(c.wave * 4 + i) * 64 + c.lane] = f32x4{M[i], Lsum[i], acc0[i], acc1[i]};
+  part[(c.wave * 2 + 0) * 64 + c.lane] = f32x4{acc0[0], acc1[0], acc0[1], acc1[1]};
+  part[(c.wave * 2 + 1) * 64 + c.lane] = f32x4{acc0[2], acc1[2], acc0[3], acc1[3]};
   cw_barrier(c);
-  if (c.wave == 0) {
-    const unsigned tag_o = tag_of(c, slot, X_O);
-    const unsigned obase = xoff<X_O>(slot);
+  {
+    // wave w finishes rows rg + 4w of every lane's dims, summing the waves in order
+    const int i = c.wave;
+    const float* pf = (const float*)part;
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float m = -INFINITY, s = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int w = 0; w < NCOMPUTE; ++w) {
-        const f32x4 p = red[(w * 4 + i) * 64 + c.lane];
-        if (p[0] != -INFINITY) {
-          const float mn = fmaxf(m, p[0]);
-          const float sa = m == -INFINITY ? 0.f : fexp(m - mn);
-          const float sb = fexp(p[0] - mn);
-          a0 = a0 * sa + p[2] * sb;
-          a1 = a1 * sa + p[3] * sb;
-          s = s * sa + p[1] * sb;
-          m = mn;
-        }
-      }
-      const int rw = rg + 4 * i;
-      if (rw < c.R) {
-        const float inv = frcp(s);
-        ll_store1(c, obase + ((unsigned)rw * (HD / 2) + (unsigned)(hd * (DH / 2) + 16 * sl + dp)) * 8u,
-                  pack_bf16(a0 * inv, a1 * inv), tag_o);
-      }
+    for (int w = 0; w < NCOMPUTE; ++w) {
+      const float* e = pf + ((w * 2 + (i >> 1)) * 64 + c.lane) * 4 + 2 * (i & 1);
+      a0 += e[0];
+      a1 += e[1];
     }
+    const int rw = rg + 4 * i;
+    if (rw < R)
+      ll_store1(c, xoff<X_O>(slot) + ((unsigned)rw * (HD / 2) + (unsigned)(hd * (DH / 2) + 16 * sl + dp)) * 8u,
+                pack_bf16(a0, a1), tag_of(c, slot, X_O));
   }
 }
 
