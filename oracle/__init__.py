@@ -76,6 +76,11 @@ def load(path: str = LIB_PATH):
     lib.orc_decide.argtypes = [ctypes.POINTER(OrcConfig), _FP, _FP, _FP, _IP, _FP, _DP, _DP, _DP]
     lib.orc_decide.restype = ctypes.c_int
     lib.orc_last_softmax_dev.restype = ctypes.c_double
+    lib.orc_ada_layernorm.argtypes = [ctypes.c_int, ctypes.c_int, _DP, _DP, _DP, ctypes.c_double, _DP]
+    lib.orc_dit.argtypes = [ctypes.POINTER(OrcConfig), _FP, _FP, _DP, _DP]
+    lib.orc_dit.restype = ctypes.c_int
+    lib.orc_dit_weight_count.argtypes = [ctypes.POINTER(OrcConfig)]
+    lib.orc_dit_weight_count.restype = ctypes.c_size_t
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -103,6 +108,8 @@ def make_config(cfg: dict) -> OrcConfig:
 def weight_count(cfg: dict, lib=None) -> int:
     lib = lib or load()
     c = make_config(cfg)
+    if cfg.get("block", "decoder") == "dit":
+        return int(lib.orc_dit_weight_count(ctypes.byref(c)))
     return int(lib.orc_weight_count(ctypes.byref(c)))
 
 
@@ -209,3 +216,35 @@ def decide(cfg: dict, weights: np.ndarray, kv_k, kv_v, lens, noise, trace: bool 
     if rc != 0:
         raise ValueError(f"orc_decide rejected its arguments (rc={rc})")
     return {"actions": actions, "trace": tr, "velocity": vel, "softmax_dev": lib.orc_last_softmax_dev()}
+
+
+def ada_layernorm(h: np.ndarray, scale: np.ndarray, shift: np.ndarray, eps: float, lib=None) -> np.ndarray:
+    lib = lib or load()
+    h, ph = _d(h)
+    M, D = h.shape
+    scale, ps = _d(scale)
+    shift, pb = _d(shift)
+    out = np.zeros((M, D), dtype=np.float64)
+    lib.orc_ada_layernorm(M, D, ph, ps, pb, eps, out.ctypes.data_as(_DP))
+    return out
+
+
+def dit(cfg: dict, weights: np.ndarray, x, trace: bool = False, lib=None) -> dict:
+    """One DiT-style step over the cfg["rows"] tokens of x [T][D] (float32).
+    Returns {"out": [T][D] float64, "trace": [NL][T][D] or None,
+    "softmax_dev": float}."""
+    lib = lib or load()
+    c = make_config(cfg)
+    n_w = int(lib.orc_dit_weight_count(ctypes.byref(c)))
+    weights, pw = _f(weights)
+    if weights.size != n_w:
+        raise ValueError(f"weight blob has {weights.size} values, expected {n_w}")
+    T, D, NL = cfg["rows"], cfg["width"], cfg["layers"]
+    x, px = _f(np.asarray(x).reshape(T, D))
+    out = np.zeros((T, D), dtype=np.float64)
+    tr = np.zeros((NL, T, D), dtype=np.float64) if trace else None
+    rc = lib.orc_dit(ctypes.byref(c), pw, px, out.ctypes.data_as(_DP),
+                     tr.ctypes.data_as(_DP) if tr is not None else None)
+    if rc != 0:
+        raise ValueError(f"orc_dit rejected its arguments (rc={rc})")
+    return {"out": out, "trace": tr, "softmax_dev": lib.orc_last_softmax_dev()}

@@ -290,3 +290,99 @@ int orc_decide(const orc_config* c, const float* weights, const float* kv_k, con
   free(gu); free(act); free(e); free(mod); free(pos);
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * DiT-style block (adaLN-Zero): "Scalable Diffusion Models with
+ * Transformers" block structure as the large-token step uses it -- a
+ * LayerNorm without affine whose output is modulated by (1 + scale) and
+ * shift, a residual branch multiplied by a gate, for attention and MLP.
+ * ------------------------------------------------------------------------ */
+
+void orc_ada_layernorm(int M, int D, const double* h, const double* scale, const double* shift, double eps,
+                       double* out) {
+  for (int m = 0; m < M; ++m) {
+    const double* r = h + (size_t)m * D;
+    double mean = 0.0;
+    for (int d = 0; d < D; ++d) mean += r[d];
+    mean /= (double)D;
+    double var = 0.0;
+    for (int d = 0; d < D; ++d) var += (r[d] - mean) * (r[d] - mean);
+    var /= (double)D;
+    double inv = 1.0 / sqrt(var + eps);
+    for (int d = 0; d < D; ++d) out[(size_t)m * D + d] = shift[d] + (1.0 + scale[d]) * ((r[d] - mean) * inv);
+  }
+}
+
+size_t orc_dit_weight_count(const orc_config* c) {
+  size_t D = (size_t)c->width, F = (size_t)c->mlp_hidden, hd = (size_t)c->n_heads * c->head_dim;
+  size_t per_block = D * 3 * hd + hd * D + D * F + F * D;
+  return (size_t)c->layers * per_block + (size_t)c->layers * (size_t)c->time_emb_dim * 6 * D;
+}
+
+int orc_dit(const orc_config* c, const float* weights, const float* x_in, double* out, double* trace) {
+  if (check_cfg(c) || !weights || !x_in || !out || c->n_kv_heads != c->n_heads) return -1;
+  const int NL = c->layers, D = c->width, H = c->n_heads, Dh = c->head_dim, F = c->mlp_hidden;
+  const int T = c->rows, E = c->time_emb_dim;
+  const int hd = H * Dh;
+  const size_t per_block = (size_t)D * 3 * hd + (size_t)hd * D + (size_t)D * F + (size_t)F * D;
+  const float* W_mod = weights + (size_t)NL * per_block;
+
+  double* x = (double*)malloc(sizeof(double) * (size_t)T * D);
+  double* n = (double*)malloc(sizeof(double) * (size_t)T * D);
+  double* qkv = (double*)malloc(sizeof(double) * (size_t)T * 3 * hd);
+  double* q = (double*)malloc(sizeof(double) * (size_t)T * hd);
+  double* k = (double*)malloc(sizeof(double) * (size_t)T * hd);
+  double* v = (double*)malloc(sizeof(double) * (size_t)T * hd);
+  double* o = (double*)malloc(sizeof(double) * (size_t)T * hd);
+  double* proj = (double*)malloc(sizeof(double) * (size_t)T * D);
+  double* up = (double*)malloc(sizeof(double) * (size_t)T * F);
+  double* e = (double*)malloc(sizeof(double) * (size_t)E);
+  double* mod = (double*)malloc(sizeof(double) * (size_t)6 * D);
+  double worst = 0.0;
+
+  for (size_t i = 0; i < (size_t)T * D; ++i) x[i] = (double)x_in[i];
+  orc_time_embedding(E, c->tau0, e);
+  for (int b = 0; b < NL; ++b) {
+    const float* W_qkv = weights + (size_t)b * per_block;
+    const float* W_o = W_qkv + (size_t)D * 3 * hd;
+    const float* W_up = W_o + (size_t)hd * D;
+    const float* W_down = W_up + (size_t)D * F;
+    /* modulation: m[c] = sum_j e[j] * W_mod[b][j][c], c < 6D */
+    const float* Wm = W_mod + (size_t)b * E * 6 * D;
+    for (int cc = 0; cc < 6 * D; ++cc) {
+      double s = 0.0;
+      for (int j = 0; j < E; ++j) s += e[j] * (double)Wm[(size_t)j * 6 * D + cc];
+      mod[cc] = s;
+    }
+    const double *shift_a = mod, *scale_a = mod + D, *gate_a = mod + 2 * D;
+    const double *shift_m = mod + 3 * D, *scale_m = mod + 4 * D, *gate_m = mod + 5 * D;
+
+    /* attention branch */
+    orc_ada_layernorm(T, D, x, scale_a, shift_a, c->rms_eps, n);
+    orc_matmul(T, D, 3 * hd, n, W_qkv, qkv);
+    for (int t = 0; t < T; ++t) {
+      const double* src = qkv + (size_t)t * 3 * hd;
+      memcpy(q + (size_t)t * hd, src, sizeof(double) * hd);
+      memcpy(k + (size_t)t * hd, src + hd, sizeof(double) * hd);
+      memcpy(v + (size_t)t * hd, src + 2 * hd, sizeof(double) * hd);
+    }
+    double dev = orc_attention(T, H, H, Dh, 0, q, k, v, NULL, NULL, 0, o);
+    if (dev > worst) worst = dev;
+    orc_matmul(T, hd, D, o, W_o, proj);
+    for (int t = 0; t < T; ++t)
+      for (int d = 0; d < D; ++d) x[(size_t)t * D + d] += gate_a[d] * proj[(size_t)t * D + d];
+
+    /* MLP branch */
+    orc_ada_layernorm(T, D, x, scale_m, shift_m, c->rms_eps, n);
+    orc_matmul(T, D, F, n, W_up, up);
+    for (size_t i = 0; i < (size_t)T * F; ++i) up[i] = orc_gelu_tanh(up[i]);
+    orc_matmul(T, F, D, up, W_down, proj);
+    for (int t = 0; t < T; ++t)
+      for (int d = 0; d < D; ++d) x[(size_t)t * D + d] += gate_m[d] * proj[(size_t)t * D + d];
+    if (trace) memcpy(trace + (size_t)b * T * D, x, sizeof(double) * (size_t)T * D);
+  }
+  memcpy(out, x, sizeof(double) * (size_t)T * D);
+  g_last_softmax_dev = worst;
+  free(x); free(n); free(qkv); free(q); free(k); free(v); free(o); free(proj); free(up); free(e); free(mod);
+  return 0;
+}

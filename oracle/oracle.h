@@ -100,8 +100,38 @@ double orc_attention(int M, int H, int KVH, int Dh, int L, const double* q, cons
 int orc_decide(const orc_config* cfg, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
                const float* noise, double* actions, double* trace, double* velocity);
 
-/* Largest |sum(p) - 1| seen by any softmax row of the last orc_decide call. */
+/* Largest |sum(p) - 1| seen by any softmax row of the last orc_decide or
+   orc_dit call. */
 double orc_last_softmax_dev(void);
+
+/*
+ * Adaptive LayerNorm without a learned affine (the DiT-style block):
+ * out[m][d] = (h[m][d] - mean) / sqrt(var + eps) * (1 + scale[d]) + shift[d],
+ * mean and (biased) variance over the row's D entries.
+ */
+void orc_ada_layernorm(int M, int D, const double* h, const double* scale, const double* shift, double eps,
+                       double* out);
+
+/*
+ * One DiT-style denoise step over T = cfg->rows tokens (the large-token
+ * workload; cfg->n_kv_heads must equal cfg->n_heads).  Weight blob (float32):
+ *   for each block b < NL: W_qkv [D][3*H*Dh] (q heads, k heads, v heads),
+ *                          W_o [H*Dh][D], W_up [D][F], W_down [F][D];
+ *   W_mod [NL][E][6D]: block b's modulation, in the order shift, scale, gate
+ *                      of the attention branch, then shift, scale, gate of
+ *                      the MLP branch (D outputs each).
+ * Per block, with e the sinusoid of tau0 and m_b = e . W_mod[b]:
+ *   n = AdaLN(x; scale_a, shift_a);  o = Attention(n W_qkv) over all T tokens
+ *   (no mask, no rotary positions);  x += gate_a * (o W_o)
+ *   n = AdaLN(x; scale_m, shift_m);  x += gate_m * (GELU_tanh(n W_up) W_down)
+ * x_in [T][D] float; out [T][D] receives x after the last block.  If trace is
+ * non-NULL it receives x after every block: [NL][T][D].  Returns 0, or -1 on
+ * a bad argument.
+ */
+int orc_dit(const orc_config* cfg, const float* weights, const float* x_in, double* out, double* trace);
+
+/* Number of float32 values in the DiT-style weight blob for cfg. */
+size_t orc_dit_weight_count(const orc_config* cfg);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,10 @@ Recipe (stated once, used everywhere):
     too (they must never be read);
   * noise: N(0, 1) float32, [B][M][A];
   * prefix lengths: fixed for single-request workloads; for the rollout batch
-    drawn uniformly from {512, 640, 768, 800}.
+    drawn uniformly from {512, 640, 768, 800};
+  * large-token workloads: the video-action chunk draws its cache like the
+    prefix K/V above (4096 of 8192 rows used) and its 256 chunk rows as the
+    noise; the DiT-style step draws its 4128 token rows x [T][D] as the noise.
 
 The prefix K/V stands in for the key/value cache a vision-language prefix of
 about 500 to 800 tokens would write; random values match its shape and bytes,
@@ -30,7 +33,8 @@ import numpy as np
 T_WEIGHTS, T_KV_K, T_KV_V, T_NOISE, T_LENS = 1, 2, 3, 4, 5
 
 _BASE = dict(width=1024, n_heads=8, head_dim=256, n_kv_heads=1, mlp_hidden=4096, state_dim=32, rows=10,
-             time_emb_dim=1024, tau0=1.0, dt=-0.1, rms_eps=1e-6, rope_base=10000.0, weight_std=0.02)
+             time_emb_dim=1024, tau0=1.0, dt=-0.1, rms_eps=1e-6, rope_base=10000.0, weight_std=0.02,
+             block="decoder")
 
 WORKLOADS = {
     # one decoder layer, one Euler step, float32 throughout, 64-token prefix
@@ -42,6 +46,18 @@ WORKLOADS = {
     # 16 independent requests, ragged prefixes drawn from {512,640,768,800}, capacity 800
     "rollout_b16_bf16": dict(_BASE, id=2, layers=18, batch=16, capacity=800, steps=10, dtype="bf16",
                              prefix_lens="draw"),
+    # video-action chunk denoise: 256 new tokens over a 4096-token cache (capacity 8192), width 2048,
+    # 16 heads x 128 with full K/V heads, GeGLU 8192, 8 layers, 5 steps of dt = -0.2; the state is the
+    # chunk itself (in/out linears 2048 x 2048)
+    "va_chunk_bf16": dict(_BASE, id=3, layers=8, width=2048, n_heads=16, head_dim=128, n_kv_heads=16,
+                          mlp_hidden=8192, state_dim=2048, rows=256, batch=1, capacity=8192, steps=5, dt=-0.2,
+                          dtype="bf16", prefix_lens=[4096]),
+    # DiT-style denoise step: 4096 video + 32 action tokens, full bidirectional self-attention, width 3072,
+    # 24 heads x 128, GELU MLP 12288, adaLN-Zero modulation (shift, scale, gate) from the tau = 1 embedding,
+    # 4 blocks, one step, output = residual stream
+    "wam_dit_bf16": dict(_BASE, id=4, block="dit", layers=4, width=3072, n_heads=24, head_dim=128,
+                         n_kv_heads=24, mlp_hidden=12288, state_dim=3072, rows=4128, batch=1, capacity=0,
+                         steps=1, dt=0.0, dtype="bf16", prefix_lens=[0]),
 }
 
 RAGGED_CHOICES = (512, 640, 768, 800)
@@ -76,6 +92,8 @@ def weight_count(cfg: dict) -> int:
     D, A, F = cfg["width"], cfg["state_dim"], cfg["mlp_hidden"]
     H, KVH, Dh, NL, E = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["layers"], cfg["time_emb_dim"]
     qkv = (H + 2 * KVH) * Dh
+    if cfg.get("block", "decoder") == "dit":
+        return NL * (D * qkv + H * Dh * D + D * F + F * D) + NL * E * 6 * D
     per_layer = D * qkv + H * Dh * D + D * 2 * F + F * D
     return A * D + NL * per_layer + D * A + (2 * NL + 1) * E * 2 * D
 
@@ -141,6 +159,15 @@ def weight_slices(cfg: dict) -> dict:
         out[name] = (off, shape)
         off += int(np.prod(shape))
 
+    if cfg.get("block", "decoder") == "dit":
+        for l in range(NL):
+            put(f"W_qkv.{l}", (D, qkv))
+            put(f"W_o.{l}", (H * Dh, D))
+            put(f"W_up.{l}", (D, F))
+            put(f"W_down.{l}", (F, D))
+        put("W_mod", (NL, E, 6 * D))
+        assert off == weight_count(cfg)
+        return out
     put("W_in", (A, D))
     for l in range(NL):
         put(f"W_qkv.{l}", (D, qkv))

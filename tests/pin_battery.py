@@ -291,8 +291,120 @@ def pin_decide_invariants(lib):
     _close(out0["velocity"][0], n @ phx_inputs.view(W, c0, "W_out").astype(np.float64), what="zero-layer velocity")
 
 
+# ---------------------------------------------------------------- DiT-style step
+
+def pin_ada_layernorm(lib):
+    g = np.random.default_rng(11)
+    h = g.standard_normal((5, 12)) * 3.0 + 1.5
+    scale = g.standard_normal(12) * 0.3
+    shift = g.standard_normal(12) * 0.3
+    got = oracle.ada_layernorm(h, scale, shift, 1e-6, lib=lib)
+    ref = F.layer_norm(torch.tensor(h), (12,), eps=1e-6).numpy() * (1.0 + scale) + shift
+    _close(got, ref, what="adaptive LayerNorm vs torch layer_norm")
+    # closed form: a row (1, 3) has mean 2, variance 1
+    two = oracle.ada_layernorm(np.array([[1.0, 3.0]]), np.zeros(2), np.zeros(2), 0.0, lib=lib)
+    _close(two, np.array([[-1.0, 1.0]]), what="LayerNorm of (1, 3)")
+
+
+def tiny_dit_cfg(**kw):
+    cfg = dict(id=96, block="dit", layers=2, width=8, n_heads=2, head_dim=4, n_kv_heads=2, mlp_hidden=12,
+               state_dim=8, rows=5, batch=1, capacity=0, steps=1, time_emb_dim=8, tau0=1.0, dt=0.0, rms_eps=1e-6,
+               rope_base=10000.0, dtype="f32", weight_std=0.5, prefix_lens=[0])
+    cfg.update(kw)
+    return cfg
+
+
+def torch_dit(cfg, W, x):
+    """Brute force: the DiT-style step composed from torch double-precision
+    primitives (sin/cos, matmul, layer_norm, scaled dot product attention,
+    tanh GELU)."""
+    NL, D, H, Dh, F_, E = cfg["layers"], cfg["width"], cfg["n_heads"], cfg["head_dim"], cfg["mlp_hidden"], cfg["time_emb_dim"]
+    T = cfg["rows"]
+    t = lambda name: torch.tensor(phx_inputs.view(W, cfg, name).astype(np.float64))
+    freqs = torch.pow(torch.tensor(10000.0, dtype=torch.float64), -torch.arange(E // 2, dtype=torch.float64) / (E // 2))
+    tau = cfg["tau0"]
+    e = torch.cat([torch.sin(tau * freqs), torch.cos(tau * freqs)])
+    x = torch.tensor(np.asarray(x, dtype=np.float64).reshape(T, D))
+    Wmod = t("W_mod")
+    for b in range(NL):
+        m = e @ Wmod[b]
+        sh_a, sc_a, g_a, sh_m, sc_m, g_m = [m[i * D:(i + 1) * D] for i in range(6)]
+        n = F.layer_norm(x, (D,), eps=cfg["rms_eps"]) * (1 + sc_a) + sh_a
+        qkv = n @ t(f"W_qkv.{b}")
+        q, k, v = [qkv[:, i * H * Dh:(i + 1) * H * Dh].reshape(T, H, Dh).permute(1, 0, 2).contiguous() for i in range(3)]
+        o = F.scaled_dot_product_attention(q[None], k[None], v[None])[0].permute(1, 0, 2).reshape(T, H * Dh)
+        x = x + g_a * (o @ t(f"W_o.{b}"))
+        n = F.layer_norm(x, (D,), eps=cfg["rms_eps"]) * (1 + sc_m) + sh_m
+        x = x + g_m * (F.gelu(n @ t(f"W_up.{b}"), approximate="tanh") @ t(f"W_down.{b}"))
+    return x.numpy()
+
+
+def _dit(cfg, W, x, lib):
+    return oracle.dit(cfg, W, x, lib=lib)["out"]
+
+
+def pin_dit_brute_force(lib):
+    for kw in [dict(), dict(rows=1), dict(n_heads=4, head_dim=2, n_kv_heads=4), dict(layers=1, rows=7)]:
+        cfg = tiny_dit_cfg(**kw)
+        inp = phx_inputs.make_inputs(cfg, seed=6)
+        x = inp["noise"].reshape(cfg["rows"], cfg["width"])
+        r = oracle.dit(cfg, inp["weights"], x, lib=lib)
+        _close(r["out"], torch_dit(cfg, inp["weights"], x), tol=1e-9, what=f"DiT step vs torch composition {kw}")
+        assert r["softmax_dev"] < 1e-12
+
+
+def pin_dit_invariants(lib):
+    cfg = tiny_dit_cfg()
+    D, T = cfg["width"], cfg["rows"]
+    inp = phx_inputs.make_inputs(cfg, seed=7)
+    W = inp["weights"]
+    x = inp["noise"].reshape(T, D)
+    xd = x.astype(np.float64)
+    base = _dit(cfg, W, x, lib)
+    assert not np.allclose(base, xd), "the random step must change its input"
+    # zero gates: both residual branches vanish, the step is the identity, bit for bit
+    wg = W.copy()
+    wm = phx_inputs.view(wg, cfg, "W_mod")
+    wm[:, :, 2 * D:3 * D] = 0.0
+    wm[:, :, 5 * D:6 * D] = 0.0
+    assert np.array_equal(_dit(cfg, wg, x, lib), xd), "zero gates must give the identity"
+    # zero output projections of both branches: the identity as well
+    wz = W.copy()
+    for b in range(cfg["layers"]):
+        phx_inputs.view(wz, cfg, f"W_o.{b}")[:] = 0.0
+        phx_inputs.view(wz, cfg, f"W_down.{b}")[:] = 0.0
+    assert np.array_equal(_dit(cfg, wz, x, lib), xd), "zero branch outputs must give the identity"
+    # no positions and no mask: permuting the tokens permutes the result
+    perm = np.array([3, 0, 4, 1, 2])
+    _close(_dit(cfg, W, x[perm], lib), base[perm], tol=1e-12, what="token permutation equivariance")
+    # one block, MLP off, zero queries: every token attends uniformly, so the
+    # attention branch adds gate_a * (mean over tokens of v) . W_o to every row
+    c1 = dict(cfg, layers=1)
+    in1 = phx_inputs.make_inputs(c1, seed=8)
+    W1 = in1["weights"].copy()
+    phx_inputs.view(W1, c1, "W_qkv.0")[:, :D] = 0.0
+    phx_inputs.view(W1, c1, "W_down.0")[:] = 0.0
+    x1 = in1["noise"].reshape(T, D)
+    E = c1["time_emb_dim"]
+    e = oracle.time_embedding(E, c1["tau0"], lib=lib)
+    m = e @ phx_inputs.view(W1, c1, "W_mod")[0].astype(np.float64)
+    n = oracle.ada_layernorm(x1.astype(np.float64), m[D:2 * D], m[:D], c1["rms_eps"], lib=lib)
+    v = n @ phx_inputs.view(W1, c1, "W_qkv.0")[:, 2 * D:].astype(np.float64)
+    want = x1 + m[2 * D:3 * D] * (v.mean(axis=0) @ phx_inputs.view(W1, c1, "W_o.0").astype(np.float64))
+    _close(_dit(c1, W1, x1, lib), want, what="uniform attention closed form")
+    # a single token attends only to itself: attention returns its own v
+    c2 = dict(c1, rows=1)
+    x2 = x1[:1]
+    n2 = n[:1]
+    v2 = n2 @ phx_inputs.view(W1, c2, "W_qkv.0")[:, 2 * D:].astype(np.float64)
+    W2 = in1["weights"].copy()
+    phx_inputs.view(W2, c2, "W_down.0")[:] = 0.0
+    want2 = x2 + m[2 * D:3 * D] * (v2 @ phx_inputs.view(W2, c2, "W_o.0").astype(np.float64))
+    _close(_dit(c2, W2, x2, lib), want2, what="single-token attention is the identity on v")
+
+
 ALL_PINS = [pin_time_embedding, pin_modulation, pin_matmul, pin_ada_rmsnorm, pin_rope, pin_gelu, pin_attention,
-            pin_decide_brute_force, pin_decide_invariants]
+            pin_decide_brute_force, pin_decide_invariants, pin_ada_layernorm, pin_dit_brute_force, pin_dit_invariants]
 
 
 def run_all(lib):

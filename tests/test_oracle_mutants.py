@@ -47,6 +47,18 @@ MUTANTS = [
      "orc_matmul(BM, hd, D, o, W_o, proj);\n      for (int i = 0; i < BM * D; ++i) h[i] = proj[i];"),
     ("decide: RoPE not applied to keys", "orc_rope(M, KVH, Dh, pos, c->rope_base, ka);", ""),
     ("decide: final norm uses first modulation", "mod + (size_t)(2 * NL) * 2 * D", "mod"),
+    ("layernorm: mean not subtracted", "var += (r[d] - mean) * (r[d] - mean);", "var += r[d] * r[d];"),
+    ("layernorm: eps dropped", "1.0 / sqrt(var + eps);", "1.0 / sqrt(var);"),
+    ("dit: scale and shift swapped", "const double *shift_a = mod, *scale_a = mod + D, *gate_a = mod + 2 * D;",
+     "const double *scale_a = mod, *shift_a = mod + D, *gate_a = mod + 2 * D;"),
+    ("dit: MLP gate dropped", "x[(size_t)t * D + d] += gate_m[d] * proj[(size_t)t * D + d];",
+     "x[(size_t)t * D + d] += proj[(size_t)t * D + d];"),
+    ("dit: MLP uses attention modulation", "const double *shift_m = mod + 3 * D, *scale_m = mod + 4 * D, *gate_m = mod + 5 * D;",
+     "const double *shift_m = mod, *scale_m = mod + D, *gate_m = mod + 5 * D;"),
+    ("dit: value rows taken from keys", "memcpy(v + (size_t)t * hd, src + 2 * hd, sizeof(double) * hd);",
+     "memcpy(v + (size_t)t * hd, src + hd, sizeof(double) * hd);"),
+    ("dit: GELU left out", "for (size_t i = 0; i < (size_t)T * F; ++i) up[i] = orc_gelu_tanh(up[i]);", ""),
+    ("dit: modulation from the wrong block", "const float* Wm = W_mod + (size_t)b * E * 6 * D;", "const float* Wm = W_mod;"),
 ]
 
 
