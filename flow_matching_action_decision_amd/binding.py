@@ -13,12 +13,14 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libphx_expert.so")
 
-PHX_ABI_VERSION = 1
+PHX_ABI_VERSION = 2
 PHX_OK, PHX_E_INVALID, PHX_E_VERSION, PHX_E_SHAPE, PHX_E_STATE, PHX_E_NOMEM, PHX_E_HIP = 0, -1, -2, -3, -4, -5, -6
 PHX_DTYPE_F32, PHX_DTYPE_BF16 = 0, 1
 PHX_FLAG_NO_GRAPH = 1
 PHX_FLAG_MULTI_KERNEL = 2
 PHX_FLAG_TIMELINE = 4
+PHX_BLOCK_DECODER, PHX_BLOCK_DIT = 0, 1
+PHX_MASK_FULL = 0
 
 # every function include/phx_expert.h declares
 EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_expert_create",
@@ -40,6 +42,7 @@ class phx_expert_config(ctypes.Structure):
         ("prefix_capacity", ctypes.c_int32), ("steps", ctypes.c_int32), ("time_emb_dim", ctypes.c_int32),
         ("tau0", ctypes.c_float), ("dt", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
         ("weight_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("block_kind", ctypes.c_int32), ("mask_kind", ctypes.c_int32),
     ]
 
 
@@ -95,7 +98,9 @@ def make_config(cfg: dict, flags: int = 0) -> phx_expert_config:
         n_kv_heads=cfg["n_kv_heads"], mlp_hidden=cfg["mlp_hidden"], state_dim=cfg["state_dim"], rows=cfg["rows"],
         batch=cfg["batch"], prefix_capacity=cfg["capacity"], steps=cfg["steps"], time_emb_dim=cfg["time_emb_dim"],
         tau0=cfg["tau0"], dt=cfg["dt"], rms_eps=cfg["rms_eps"], rope_base=cfg["rope_base"],
-        weight_dtype=dt, kv_dtype=dt, flags=flags | int(cfg.get("flags", 0)))
+        weight_dtype=dt, kv_dtype=dt, flags=flags | int(cfg.get("flags", 0)),
+        block_kind=PHX_BLOCK_DIT if cfg.get("block", "decoder") == "dit" else PHX_BLOCK_DECODER,
+        mask_kind=PHX_MASK_FULL)
 
 
 def _check(rc: int):

@@ -158,6 +158,7 @@ size_t weight_elems(const phx_expert_config* c) {
   const size_t D = c->width, A = c->state_dim, F = c->mlp_hidden, E = c->time_emb_dim, NL = c->layers;
   const size_t qkv = (size_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
   const size_t hd = (size_t)c->n_heads * c->head_dim;
+  if (c->block_kind == PHX_BLOCK_DIT) return NL * (D * qkv + hd * D + D * F + F * D) + NL * E * 6 * D;
   const size_t per_layer = D * qkv + hd * D + D * 2 * F + F * D;
   return A * D + NL * per_layer + D * A + (2 * NL + 1) * E * 2 * D;
 }
@@ -471,11 +472,29 @@ int phx_expert_validate_config(const phx_expert_config* c) {
     return fail(PHX_E_SHAPE, "mlp_hidden %d must be a positive multiple of 128", c->mlp_hidden);
   if (c->state_dim < 32 || c->state_dim % 32)
     return fail(PHX_E_SHAPE, "state_dim %d must be a positive multiple of 32", c->state_dim);
-  if (c->rows < 1 || c->batch < 1 || c->rows * c->batch > 160)
-    return fail(PHX_E_SHAPE, "rows*batch = %d must be in [1, 160]", c->rows * c->batch);
-  if ((c->n_heads / c->n_kv_heads) * c->rows > 128)
+  if (c->block_kind != PHX_BLOCK_DECODER && c->block_kind != PHX_BLOCK_DIT)
+    return fail(PHX_E_INVALID, "block_kind %d unknown", c->block_kind);
+  if (c->mask_kind != PHX_MASK_FULL) return fail(PHX_E_INVALID, "mask_kind %d unknown", c->mask_kind);
+  if (c->rows < 1 || c->batch < 1) return fail(PHX_E_SHAPE, "rows and batch must be positive");
+  const bool tokens = c->block_kind == PHX_BLOCK_DIT || (long long)c->rows * c->batch > 160;
+  if (tokens) {
+    // the large-token plan: one chunk of many rows
+    if (c->batch != 1 || c->rows > 16384)
+      return fail(PHX_E_SHAPE, "more than 160 rows needs batch 1 and rows <= 16384 (rows %d, batch %d)", c->rows,
+                  c->batch);
+    if (c->weight_dtype != PHX_DTYPE_BF16) return fail(PHX_E_SHAPE, "more than 160 rows needs bf16 weights");
+    if (c->head_dim != 128) return fail(PHX_E_SHAPE, "more than 160 rows needs head_dim 128");
+    if (c->state_dim % 128) return fail(PHX_E_SHAPE, "more than 160 rows needs state_dim a multiple of 128");
+    if (c->block_kind == PHX_BLOCK_DIT) {
+      if (c->state_dim != c->width) return fail(PHX_E_SHAPE, "the DiT-style block needs state_dim == width");
+      if (c->n_kv_heads != c->n_heads) return fail(PHX_E_SHAPE, "the DiT-style block needs n_kv_heads == n_heads");
+      if (c->prefix_capacity != 0) return fail(PHX_E_SHAPE, "the DiT-style block has no prefix (capacity 0)");
+      if (c->steps != 1) return fail(PHX_E_SHAPE, "the DiT-style block runs one step");
+    }
+  } else if ((c->n_heads / c->n_kv_heads) * c->rows > 128) {
     return fail(PHX_E_SHAPE, "query rows per kv head (n_heads/n_kv_heads*rows = %d) must be at most 128",
                 (c->n_heads / c->n_kv_heads) * c->rows);
+  }
   if (c->prefix_capacity < 0 || c->prefix_capacity > 65536)
     return fail(PHX_E_SHAPE, "prefix_capacity %d outside [0, 65536]", c->prefix_capacity);
   if (c->steps < 1 || c->steps > 1000) return fail(PHX_E_SHAPE, "steps %d outside [1, 1000]", c->steps);

@@ -46,7 +46,7 @@ extern "C" {
 #define PHX_API
 #endif
 
-#define PHX_ABI_VERSION 1u
+#define PHX_ABI_VERSION 2u
 
 /* return codes */
 #define PHX_OK 0
@@ -70,6 +70,18 @@ extern "C" {
 #define PHX_FLAG_TIMELINE 4u   /* persistent kernel: record a per-workgroup phase timeline (see
                                   phx_expert_timeline) */
 
+/* block kinds */
+#define PHX_BLOCK_DECODER 0  /* adaptive RMSNorm (scale, shift), RoPE, GeGLU MLP, residual adds; in- and
+                                out-linears around the stack and an Euler update per step (the pi0.5
+                                action expert, and the video-action chunk at width 2048) */
+#define PHX_BLOCK_DIT 1      /* DiT-style adaLN-Zero block: LayerNorm without affine modulated by
+                                (1 + scale) and shift, gated attention and GELU-MLP residual branches,
+                                no rotary positions; one pass over the tokens, no in/out linears and no
+                                Euler update (state_dim = width, steps = 1, prefix_capacity = 0) */
+
+/* attention masks */
+#define PHX_MASK_FULL 0      /* every row sees every prefix key and every row of its own chunk */
+
 /* A HIP stream (hipStream_t is a pointer to this incomplete type). NULL means
    the default stream. */
 typedef struct ihipStream_t* phx_stream_t;
@@ -88,8 +100,11 @@ typedef struct phx_expert_config {
   int32_t n_kv_heads;        /* KVH key/value heads [1: multi-query]; divides H */
   int32_t mlp_hidden;        /* F GeGLU hidden width [4096]; multiple of 128 */
   int32_t state_dim;         /* A action dimension [32]; multiple of 32 */
-  int32_t rows;              /* M action rows per request [10]; n_heads/n_kv_heads*rows <= 128 */
-  int32_t batch;             /* B requests per decision; B*M <= 160 */
+  int32_t rows;              /* M action rows per request [10] (tokens of the chunk for the large-token
+                                workloads); B*M <= 160 with n_heads/n_kv_heads*rows <= 128, or B = 1 and
+                                161 <= M <= 16384 (large-token plan: bf16, head_dim 128, width,
+                                mlp_hidden and state_dim multiples of 128) */
+  int32_t batch;             /* B requests per decision */
   int32_t prefix_capacity;   /* C context bucket: most prefix rows a request may load [768]; <= 65536 */
   int32_t steps;             /* S Euler steps [10] */
   int32_t time_emb_dim;      /* E sinusoidal time-embedding width [1024]; even */
@@ -100,6 +115,8 @@ typedef struct phx_expert_config {
   int32_t weight_dtype;      /* PHX_DTYPE_F32 or PHX_DTYPE_BF16 */
   int32_t kv_dtype;          /* must equal weight_dtype */
   uint32_t flags;            /* PHX_FLAG_* */
+  int32_t block_kind;        /* PHX_BLOCK_DECODER or PHX_BLOCK_DIT */
+  int32_t mask_kind;         /* PHX_MASK_FULL */
 } phx_expert_config;
 
 typedef struct phx_expert phx_expert;
@@ -122,6 +139,10 @@ PHX_API int phx_expert_validate_config(const phx_expert_config* cfg);
  *   W_out  [D][A]
  *   W_mod  [2*NL+1][E][2D]  (norm 2l precedes attention in layer l, 2l+1 the MLP,
  *                            2*NL the velocity head; first D outputs scale, last D shift)
+ * For PHX_BLOCK_DIT:
+ *   for each block: W_qkv [D][3*H*Dh] (q, k, v heads), W_o [H*Dh][D], W_up [D][F], W_down [F][D]
+ *   W_mod  [NL][E][6D]      (block b: shift, scale, gate of the attention branch, then shift,
+ *                            scale, gate of the MLP branch, D outputs each)
  * There are no biases.
  */
 PHX_API int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes);
@@ -159,7 +180,9 @@ PHX_API int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void
                               int32_t prefix_len, phx_stream_t stream);
 
 /*
- * One decision: x = noise; S Euler steps of the expert; actions = x.
+ * One decision: x = noise; S Euler steps of the expert; actions = x.  For
+ * PHX_BLOCK_DIT, one pass of the block stack over the tokens: noise holds the
+ * token rows x, actions receives the residual stream after the last block.
  *   noise, actions: device pointers to float32 [batch][rows][state_dim]
  *                   (they may be the same buffer).
  * Stream-ordered and asynchronous: copy in, graph replay, copy out.  The

@@ -40,8 +40,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_struct_layout_matches_header(lib):
     from flow_matching_action_decision_amd import binding
-    # 14 int32-sized fields + 4 floats + 3 int32 = 21 * 4 bytes
-    assert ctypes.sizeof(binding.phx_expert_config) == 84
+    # 14 int32-sized fields + 4 floats + 5 int32 = 23 * 4 bytes
+    assert ctypes.sizeof(binding.phx_expert_config) == 92
     assert ctypes.sizeof(binding.phx_node_info) == 56
 
 
@@ -65,7 +65,7 @@ def test_validate_accepts_the_workloads(lib):
     ("head_dim", 96, -3), ("n_kv_heads", 3, -3), ("mlp_hidden", 100, -3), ("state_dim", 7, -3),
     ("rows", 0, -3), ("batch", 17, -3), ("prefix_capacity", -1, -3), ("steps", 0, -3),
     ("time_emb_dim", 3, -3), ("rms_eps", 0.0, -1), ("rope_base", -1.0, -1), ("weight_dtype", 7, -1),
-    ("kv_dtype", 0, -3), ("flags", 0x80, -1),
+    ("kv_dtype", 0, -3), ("flags", 0x80, -1), ("block_kind", 5, -1), ("mask_kind", 1, -1),
 ])
 def test_validate_rejects(lib, field, value, code):
     from flow_matching_action_decision_amd import binding
@@ -98,3 +98,17 @@ def test_null_handles_are_rejected_without_a_gpu(lib):
     c = _cfg()
     assert lib.phx_expert_create(ctypes.byref(c), None, 0, None, ctypes.byref(out)) == -1
     assert out.value is None
+
+
+@pytest.mark.parametrize("name,field,value", [
+    ("wam_dit_bf16", "state_dim", 1024), ("wam_dit_bf16", "n_kv_heads", 8), ("wam_dit_bf16", "prefix_capacity", 64),
+    ("wam_dit_bf16", "steps", 2), ("wam_dit_bf16", "head_dim", 64), ("wam_dit_bf16", "weight_dtype", 0),
+    ("va_chunk_bf16", "batch", 2), ("va_chunk_bf16", "state_dim", 2000), ("va_chunk_bf16", "rows", 20000),
+])
+def test_validate_rejects_large_token_shapes(lib, name, field, value):
+    from flow_matching_action_decision_amd import binding
+    c = binding.make_config(phx_inputs.workload(name))
+    setattr(c, field, value)
+    if field == "weight_dtype":
+        c.kv_dtype = value
+    assert binding.phx_expert_validate_config(c) == -3, f"{name}: {field}={value} accepted"
