@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libphx_expert.so")
-SOURCES = ["phx_kernels.hip", "phx_decide.hip", "phx_engine.cpp"]
+SOURCES = ["phx_kernels.hip", "phx_decide.hip", "phx_tokens.hip", "phx_engine.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -14,6 +14,7 @@
 #include "phx_expert.h"
 #include "phx_internal.h"
 #include "phx_decide.h"
+#include "phx_tokens.h"
 
 #include <hip/hip_runtime.h>
 
@@ -60,6 +61,25 @@ struct Node {
   int nw = 1, pro = 0, epi = 0;
   AttnArgs at{};
   CombineArgs cb{};
+};
+
+// One kernel launch of the large-token plan.
+enum TokOp : int { TOP_CVT = 0, TOP_NORM = 1, TOP_GEMM = 2, TOP_ATTN = 3, TOP_COMBINE = 4 };
+
+struct TokNode {
+  int kind = 0, step = 0, layer = 0, op = 0, epi = 0;
+  uint64_t bytes = 0;  // weights streamed plus activation rows read and written
+  char name[32] = {0};
+  tok::GemmT g{};
+  tok::AttnT a{};
+  // TOP_NORM / TOP_CVT
+  int norm_kind = 0;  // 0 RMS, 1 LayerNorm
+  const float* src = nullptr;
+  const float* scale = nullptr;
+  const float* shift = nullptr;
+  float eps = 0.f;
+  void* dst = nullptr;
+  int cols = 0;
 };
 
 GemmPlan make_plan(int K, int N, int target_wgs) {
@@ -130,6 +150,18 @@ struct phx_expert {
   int n_chunks = 0;
   unsigned seq_host = 0;      // decisions launched since the exchange words were last cleared
   unsigned seq_limit = 0;     // clear them before the tag space wraps
+  // large-token plan (a chunk of many rows, or the DiT-style block)
+  bool tokens = false;
+  int Mp = 0;                 // rows padded to tok::ROW_PAD
+  int splits = 1;             // attention key splits
+  std::vector<TokNode> tnodes;
+  void* xb = nullptr;         // bf16 state rows (input projection operand)
+  void* nb = nullptr;         // bf16 normalised rows
+  void* qkv = nullptr;        // bf16 q | k | v rows
+  void* tk = nullptr;         // prefix keys [NL][C][KVH*Dh]
+  void* tv = nullptr;         // prefix values, same layout
+  float* po = nullptr;        // attention partials of the key splits
+  float* pml = nullptr;
 };
 
 namespace {
@@ -292,7 +324,16 @@ int launch_node(phx_expert* h, const Node& nd, hipStream_t s) {
 }
 
 // Enqueue one decision's step loop on stream s (graph capture or direct).
+int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s);
+
 int enqueue_steps(phx_expert* h, hipStream_t s) {
+  if (h->tokens) {
+    for (const TokNode& nd : h->tnodes) {
+      int rc = launch_tok(h, nd, s);
+      if (rc) return rc;
+    }
+    return PHX_OK;
+  }
   for (const Node& nd : h->node_list) {
     int rc = launch_node(h, nd, s);
     if (rc) return rc;
@@ -314,6 +355,7 @@ int mt_for_rows(int rows) {
 // multi-kernel graph.
 bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop) {
   if (c.flags & (PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL)) return false;
+  if (c.block_kind != PHX_BLOCK_DECODER) return false;
   if (c.weight_dtype != PHX_DTYPE_BF16 || c.kv_dtype != PHX_DTYPE_BF16) return false;
   if (c.width != dec::D || c.n_heads != dec::H || c.head_dim != dec::DH || c.n_kv_heads != 1) return false;
   if (c.mlp_hidden != dec::F || c.state_dim != dec::A) return false;
@@ -330,8 +372,6 @@ bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop
   if (arena >= (1ull << 31)) return false;
   return true;
 }
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int enqueue_persistent(phx_expert* h, hipStream_t s) {
   PHX_HIP(dec::launch_decide(h->dargs, s));
@@ -445,6 +485,217 @@ int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t 
   if (e != hipSuccess) return fail(PHX_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
   h->graph = g;
   PHX_HIP(hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0));
+  return PHX_OK;
+}
+
+
+bool uses_tokens(const phx_expert_config& c) {
+  return c.block_kind == PHX_BLOCK_DIT || (long long)c.rows * c.batch > 160;
+}
+
+int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s) {
+  const int M = h->cfg.rows;
+  switch (nd.op) {
+    case TOP_CVT:
+      PHX_HIP(tok::launch_tcvt(nd.src, nd.dst, M, h->Mp, nd.cols, s));
+      break;
+    case TOP_NORM:
+      PHX_HIP(tok::launch_tnorm(nd.norm_kind, nd.src, nd.scale, nd.shift, nd.eps, nd.dst, M, h->Mp, nd.cols, s));
+      break;
+    case TOP_GEMM:
+      PHX_HIP(tok::launch_tgemm(nd.epi, nd.g, s));
+      break;
+    case TOP_ATTN:
+      PHX_HIP(tok::launch_tattn(nd.a, s));
+      break;
+    case TOP_COMBINE:
+      PHX_HIP(tok::launch_tcombine(nd.a, s));
+      break;
+    default:
+      return fail(PHX_E_INVALID, "unknown token-plan op %d", nd.op);
+  }
+  return PHX_OK;
+}
+
+// The launches of one large-token decision.  Decoder block (a chunk of rows
+// over a prefix cache): per Euler step the state goes to bf16, the input
+// projection, then per layer RMS norm, QKV with RoPE, attention over prefix
+// plus chunk keys, out-projection + residual, RMS norm, gate/up with GeGLU,
+// down-projection + residual; then the final norm and the velocity
+// projection with the Euler update.  DiT-style block: per block LayerNorm
+// with shift and scale, QKV, attention over the tokens, gated out-projection
+// residual, LayerNorm, up with GELU, gated down-projection residual.
+int build_tok_nodes(phx_expert* h) {
+  const phx_expert_config& c = h->cfg;
+  const bool dit = c.block_kind == PHX_BLOCK_DIT;
+  const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = c.rows;
+  const int NL = c.layers, C = c.prefix_capacity;
+  const int HD = H * tok::DH, NQKV = (H + 2 * KVH) * tok::DH, kvd = KVH * tok::DH;
+  const int Mp = h->Mp;
+  h->tnodes.clear();
+  auto name_of = [](TokNode& nd, const char* name) { std::snprintf(nd.name, sizeof(nd.name), "%s", name); };
+  auto gemm = [&](int kind, int k, int l, int epi, const void* a, size_t w_off, int K, int N, void* out, int ldo,
+                  const float* gate, const char* name) {
+    TokNode nd{};
+    nd.kind = kind; nd.step = k; nd.layer = l; nd.op = TOP_GEMM; nd.epi = epi;
+    tok::GemmT& g = nd.g;
+    g.a = a; g.w = (const char*)h->wt + w_off * 2; g.out = out; g.gate = gate; g.rope = h->rope;
+    g.rot_cols = (H + KVH) * tok::DH; g.dt = c.dt; g.M = M; g.Mp = Mp; g.K = K; g.N = N; g.ldo = ldo;
+    const int out_cols = epi == tok::EP_GEGLU ? N / 2 : N;
+    const int out_esz = (epi == tok::EP_RESID || epi == tok::EP_EULER || epi == tok::EP_F32) ? 4 : 2;
+    const uint64_t rmw = (epi == tok::EP_RESID || epi == tok::EP_EULER) ? 2 : 1;
+    nd.bytes = (uint64_t)K * N * 2 + (uint64_t)M * K * 2 + rmw * (uint64_t)M * out_cols * out_esz +
+               (gate ? (uint64_t)N * 4 : 0);
+    name_of(nd, name);
+    h->tnodes.push_back(nd);
+  };
+  auto norm = [&](int k, int l, int kind, const float* scale, const float* shift, const char* name) {
+    TokNode nd{};
+    nd.kind = PHX_NODE_ROW_NORM; nd.step = k; nd.layer = l; nd.op = TOP_NORM;
+    nd.norm_kind = kind; nd.src = h->h; nd.scale = scale; nd.shift = shift; nd.eps = c.rms_eps; nd.dst = h->nb;
+    nd.cols = D;
+    nd.bytes = (uint64_t)M * D * 4 + (uint64_t)Mp * D * 2 + 2ull * D * 4;
+    name_of(nd, name);
+    h->tnodes.push_back(nd);
+  };
+  auto attention = [&](int k, int l, const void* kp, const void* vp) {
+    TokNode nd{};
+    nd.kind = PHX_NODE_ATTENTION; nd.step = k; nd.layer = l; nd.op = TOP_ATTN;
+    tok::AttnT& a = nd.a;
+    a.qkv = h->qkv; a.ldqkv = NQKV; a.kp = kp; a.vp = vp; a.lens = dit ? nullptr : h->lens;
+    a.M = M; a.H = H; a.KVH = KVH; a.o = h->o; a.po = h->po; a.pml = h->pml; a.splits = h->splits;
+    a.scale = (float)(1.0 / std::sqrt((double)tok::DH));
+    name_of(nd, "attention");
+    h->tnodes.push_back(nd);
+    if (h->splits > 1) {
+      TokNode cb = nd;
+      cb.kind = PHX_NODE_ATTN_COMBINE; cb.op = TOP_COMBINE;
+      cb.bytes = (uint64_t)h->splits * M * (HD + 2 * H) * 4 + (uint64_t)M * HD * 2;
+      name_of(cb, "attention_combine");
+      h->tnodes.push_back(cb);
+    }
+  };
+  if (dit) {
+    for (int l = 0; l < NL; ++l) {
+      const float* mod = h->modtab + (size_t)l * 6 * D;  // shift, scale, gate (attention), then (MLP)
+      norm(0, l, 1, mod + D, mod, "layernorm_attn");
+      gemm(PHX_NODE_QKV, 0, l, tok::EP_BF16, h->nb, h->off_qkv[l], D, NQKV, h->qkv, NQKV, nullptr, "qkv");
+      attention(0, l, nullptr, nullptr);
+      gemm(PHX_NODE_OUT_PROJ_RESID, 0, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, mod + 2 * D,
+           "out_proj_gated_resid");
+      norm(0, l, 1, mod + 4 * D, mod + 3 * D, "layernorm_mlp");
+      gemm(PHX_NODE_GATEUP, 0, l, tok::EP_GELU, h->nb, h->off_gu[l], D, F, h->act, F, nullptr, "up_gelu");
+      gemm(PHX_NODE_DOWN_PROJ_RESID, 0, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, mod + 5 * D,
+           "down_proj_gated_resid");
+    }
+    return PHX_OK;
+  }
+  const int NN = 2 * NL + 1;
+  for (int k = 0; k < c.steps; ++k) {
+    const float* mod_k = h->modtab + (size_t)k * NN * 2 * D;  // per norm: scale, then shift
+    {
+      TokNode nd{};
+      nd.kind = PHX_NODE_STATE_CVT; nd.step = k; nd.layer = -1; nd.op = TOP_CVT;
+      nd.src = h->x; nd.dst = h->xb; nd.cols = A;
+      nd.bytes = (uint64_t)M * A * 4 + (uint64_t)Mp * A * 2;
+      name_of(nd, "state_to_bf16");
+      h->tnodes.push_back(nd);
+    }
+    gemm(PHX_NODE_IN_PROJ, k, -1, tok::EP_F32, h->xb, h->off_in, A, D, h->h, D, nullptr, "in_proj");
+    for (int l = 0; l < NL; ++l) {
+      const float* m1 = mod_k + (size_t)(2 * l) * 2 * D;
+      const float* m2 = mod_k + (size_t)(2 * l + 1) * 2 * D;
+      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn");
+      gemm(PHX_NODE_QKV, k, l, tok::EP_ROPE, h->nb, h->off_qkv[l], D, NQKV, h->qkv, NQKV, nullptr, "qkv_rope");
+      attention(k, l, (const char*)h->tk + (size_t)l * C * kvd * 2, (const char*)h->tv + (size_t)l * C * kvd * 2);
+      gemm(PHX_NODE_OUT_PROJ_RESID, k, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, nullptr,
+           "out_proj_resid");
+      norm(k, l, 0, m2, m2 + D, "rmsnorm_mlp");
+      gemm(PHX_NODE_GATEUP, k, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu");
+      gemm(PHX_NODE_DOWN_PROJ_RESID, k, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, nullptr,
+           "down_proj_resid");
+    }
+    const float* mf = mod_k + (size_t)(2 * NL) * 2 * D;
+    norm(k, -1, 0, mf, mf + D, "rmsnorm_final");
+    gemm(PHX_NODE_OUT_EULER, k, -1, tok::EP_EULER, h->nb, h->off_out, D, A, h->x, A, nullptr, "out_proj_euler");
+  }
+  return PHX_OK;
+}
+
+// Set-up of the large-token plan after the weights are tiled: modulation
+// table, state and working rows, the prefix cache, and the captured graph.
+int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_off) {
+  const phx_expert_config& c = h->cfg;
+  const bool dit = c.block_kind == PHX_BLOCK_DIT;
+  const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = c.rows;
+  const int NL = c.layers, S = c.steps, E = c.time_emb_dim, C = c.prefix_capacity;
+  const int HD = H * tok::DH, NQKV = (H + 2 * KVH) * tok::DH, kvd = KVH * tok::DH;
+  const int Mp = (M + tok::ROW_PAD - 1) / tok::ROW_PAD * tok::ROW_PAD;
+  h->Mp = Mp;
+  int rc;
+  // modulation: decoder [S][2NL+1][2D] (scale | shift per norm); DiT [NL][6D] at tau0
+  const int MS = dit ? 1 : S, NN = dit ? NL : 2 * NL + 1, MW = dit ? 6 * D : 2 * D;
+  void* etab = nullptr;
+  if ((rc = alloc(h, &etab, (size_t)MS * E * sizeof(double), "time embedding"))) return rc;
+  if ((rc = alloc(h, (void**)&h->modtab, (size_t)MS * NN * MW * sizeof(float), "modulation table"))) return rc;
+  PHX_HIP(launch_time_embedding((double*)etab, MS, E, c.tau0, c.dt, stream));
+  PHX_HIP(launch_modulation(1, sb + mod_off * 2, (const double*)etab, h->modtab, MS, NN, E, MW, stream));
+
+  // attention key splits: enough workgroups to cover the chip, at least four key blocks per split
+  const long long q_wgs = (long long)((M + 63) / 64) * H;
+  const int max_blocks = (C + M + 63) / 64;
+  h->splits = 1;
+  while (q_wgs * h->splits < 512 && max_blocks / (h->splits * 2) >= 4) h->splits *= 2;
+
+  struct Buf { void** p; size_t bytes; const char* what; };
+  std::vector<Buf> bufs = {
+      {(void**)&h->h, (size_t)Mp * D * 4, "residual rows"},
+      {&h->nb, (size_t)Mp * D * 2, "normalised rows"},
+      {&h->qkv, (size_t)Mp * NQKV * 2, "qkv rows"},
+      {&h->o, (size_t)Mp * HD * 2, "attention output rows"},
+      {&h->act, (size_t)Mp * F * 2, "MLP activation rows"},
+  };
+  if (!dit) {
+    bufs.push_back({(void**)&h->x, (size_t)Mp * A * 4, "state rows"});
+    bufs.push_back({&h->xb, (size_t)Mp * A * 2, "bf16 state rows"});
+    bufs.push_back({&h->tk, (size_t)NL * C * kvd * 2, "prefix keys"});
+    bufs.push_back({&h->tv, (size_t)NL * C * kvd * 2, "prefix values"});
+    bufs.push_back({(void**)&h->lens, sizeof(int), "prefix length"});
+    bufs.push_back({(void**)&h->rope, (size_t)M * (tok::DH / 2) * sizeof(float2), "position table"});
+  }
+  if (h->splits > 1) {
+    bufs.push_back({(void**)&h->po, (size_t)h->splits * M * HD * 4, "attention partials"});
+    bufs.push_back({(void**)&h->pml, (size_t)h->splits * M * H * 2 * 4, "attention statistics"});
+  }
+  for (const Buf& b : bufs) {
+    if ((rc = alloc(h, b.p, b.bytes, b.what))) return rc;
+    PHX_HIP(hipMemsetAsync(*b.p, 0, b.bytes, stream));
+  }
+  PHX_HIP(hipStreamSynchronize(stream));
+  for (size_t i = 0; i < h->allocs.size(); ++i)
+    if (h->allocs[i] == etab) {
+      (void)hipFree(etab);
+      h->allocs.erase(h->allocs.begin() + (long)i);
+      break;
+    }
+
+  if ((rc = build_tok_nodes(h))) return rc;
+  h->nodes = (int)h->tnodes.size();
+  if (!(c.flags & PHX_FLAG_NO_GRAPH)) {
+    PHX_HIP(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+    rc = PHX_OK;
+    for (const TokNode& nd : h->tnodes)
+      if ((rc = launch_tok(h, nd, h->cap))) break;
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(h->cap, &g);
+    if (rc) {
+      if (g) (void)hipGraphDestroy(g);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(PHX_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    h->graph = g;
+    PHX_HIP(hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0));
+  }
   return PHX_OK;
 }
 
@@ -563,17 +814,21 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
   PHX_HIP(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
 
   // ---- static: tiled weights (everything but W_mod) ----
+  // decoder blob: W_in, per layer [W_qkv, W_o, W_gu, W_down], W_out, W_mod;
+  // DiT-style blob: per block [W_qkv, W_o, W_up, W_down], W_mod
+  const bool dit = c.block_kind == PHX_BLOCK_DIT;
+  const int gu_cols = dit ? F : 2 * F;
   size_t off = 0;
   h->off_in = off;
-  off += (size_t)A * D;
+  if (!dit) off += (size_t)A * D;
   for (int l = 0; l < NL; ++l) {
     h->off_qkv.push_back(off); off += (size_t)D * qkvN;
     h->off_o.push_back(off); off += (size_t)H * Dh * D;
-    h->off_gu.push_back(off); off += (size_t)D * 2 * F;
+    h->off_gu.push_back(off); off += (size_t)D * gu_cols;
     h->off_down.push_back(off); off += (size_t)F * D;
   }
   h->off_out = off;
-  off += (size_t)D * A;
+  if (!dit) off += (size_t)D * A;
   const size_t tiled_elems = off;
   const size_t total_elems = weight_elems(&c);
   if ((rc = alloc(h, &h->wt, tiled_elems * h->esz, "tiled weights"))) return rc;
@@ -591,14 +846,29 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
     PHX_HIP(launch_retile(h->dtype, sb + o * h->esz, (char*)h->wt + o * h->esz, K, N, kind, param, stream));
     return PHX_OK;
   };
-  if ((rc = retile(h->off_in, A, D, COL_IDENT, 0))) return rc;
+  if (!dit && (rc = retile(h->off_in, A, D, COL_IDENT, 0))) return rc;
   for (int l = 0; l < NL; ++l) {
-    if ((rc = retile(h->off_qkv[l], D, qkvN, COL_ROPE, Dh))) return rc;
+    if ((rc = retile(h->off_qkv[l], D, qkvN, dit ? COL_IDENT : COL_ROPE, Dh))) return rc;
     if ((rc = retile(h->off_o[l], H * Dh, D, COL_IDENT, 0))) return rc;
-    if ((rc = retile(h->off_gu[l], D, 2 * F, COL_GEGLU, F))) return rc;
+    if ((rc = retile(h->off_gu[l], D, gu_cols, dit ? COL_IDENT : COL_GEGLU, F))) return rc;
     if ((rc = retile(h->off_down[l], F, D, COL_IDENT, 0))) return rc;
   }
-  if ((rc = retile(h->off_out, D, A, COL_IDENT, 0))) return rc;
+  if (!dit && (rc = retile(h->off_out, D, A, COL_IDENT, 0))) return rc;
+
+  h->tokens = uses_tokens(c);
+  if (h->tokens) {
+    rc = create_tokens(h, sb, stream, off);
+    if (rc) return rc;
+    for (size_t i = 0; i < h->allocs.size(); ++i)
+      if (staging && h->allocs[i] == staging) {
+        (void)hipFree(staging);
+        h->allocs.erase(h->allocs.begin() + (long)i);
+        break;
+      }
+    h->loaded.assign(B, dit ? 1 : 0);  // the DiT-style block has no prefix to load
+    h->lens_host.assign(B, 0);
+    return PHX_OK;
+  }
 
   h->persistent = persistent_eligible(c, prop);
   if (h->persistent) {
@@ -719,7 +989,21 @@ int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, con
   if (prefix_len > 0 && (!is_device_pointer(k) || !is_device_pointer(v)))
     return fail(PHX_E_INVALID, "k and v must be device pointers");
   hipStream_t s = (hipStream_t)stream;
-  if (h->persistent) {
+  if (h->tokens && c.block_kind == PHX_BLOCK_DIT) {
+    h->loaded[request] = 1;  // capacity 0: nothing to copy
+    g_err.clear();
+    return PHX_OK;
+  }
+  if (h->tokens) {
+    // [NL][L][kvd] -> [NL][C][kvd]; rows beyond L are never read
+    const size_t row = (size_t)c.n_kv_heads * c.head_dim * 2;
+    if (prefix_len > 0) {
+      PHX_HIP(hipMemcpy2DAsync(h->tk, (size_t)c.prefix_capacity * row, k, (size_t)prefix_len * row,
+                               (size_t)prefix_len * row, (size_t)c.layers, hipMemcpyDeviceToDevice, s));
+      PHX_HIP(hipMemcpy2DAsync(h->tv, (size_t)c.prefix_capacity * row, v, (size_t)prefix_len * row,
+                               (size_t)prefix_len * row, (size_t)c.layers, hipMemcpyDeviceToDevice, s));
+    }
+  } else if (h->persistent) {
     PHX_HIP(dec::launch_attn_tiles(k, v, h->kvt, c.layers, prefix_len, h->n_chunks, s));
   } else {
     PHX_HIP(launch_load_prefix(h->dtype, k, v, h->kc, h->vtc, c.layers, c.batch, c.n_kv_heads, c.head_dim, h->Ctot,
@@ -745,7 +1029,9 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
     PHX_HIP(hipMemsetAsync((char*)h->arena + dec::AUX0, 0, dec::AUX_LENS, s));  // status and counter
     h->seq_host = 0;
   }
-  PHX_HIP(hipMemcpyAsync(h->x, noise, xb, hipMemcpyDefault, s));
+  // the DiT-style block integrates nothing: its state is the residual stream itself
+  float* state = (h->tokens && h->cfg.block_kind == PHX_BLOCK_DIT) ? h->h : h->x;
+  PHX_HIP(hipMemcpyAsync(state, noise, xb, hipMemcpyDefault, s));
   if (h->exec) {
     PHX_HIP(hipGraphLaunch(h->exec, s));
   } else {
@@ -753,7 +1039,7 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
     if (rc) return rc;
   }
   if (h->persistent) ++h->seq_host;
-  PHX_HIP(hipMemcpyAsync(actions, h->x, xb, hipMemcpyDefault, s));
+  PHX_HIP(hipMemcpyAsync(actions, state, xb, hipMemcpyDefault, s));
   g_err.clear();
   return PHX_OK;
 }
@@ -761,8 +1047,23 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
 int phx_expert_node_info(const phx_expert* h, int32_t node, phx_node_info* info) {
   if (!h || !info) return fail(PHX_E_INVALID, "NULL argument");
   if (node < 0 || node >= h->nodes) return fail(PHX_E_SHAPE, "node %d outside [0, %d)", node, h->nodes);
-  const Node& nd = h->node_list[(size_t)node];
   std::memset(info, 0, sizeof(*info));
+  if (h->tokens) {
+    const TokNode& tn = h->tnodes[(size_t)node];
+    info->kind = tn.kind;
+    info->step = tn.step;
+    info->layer = tn.layer;
+    info->bytes = tn.bytes;
+    if (tn.kind == PHX_NODE_ATTENTION) {
+      // query rows, the valid prefix keys and values, the chunk's own key and value rows, the output
+      const phx_expert_config& c = h->cfg;
+      const uint64_t kvd = (uint64_t)c.n_kv_heads * c.head_dim, hd = (uint64_t)c.n_heads * c.head_dim;
+      info->bytes = 2 * ((uint64_t)h->lens_host[0] * kvd * 2 + (uint64_t)c.rows * (hd + kvd) * 2);
+    }
+    std::snprintf(info->name, sizeof(info->name), "%s", tn.name);
+    return PHX_OK;
+  }
+  const Node& nd = h->node_list[(size_t)node];
   info->kind = nd.kind;
   info->step = nd.step;
   info->layer = nd.layer;
@@ -804,6 +1105,9 @@ int phx_expert_launch_node(phx_expert* h, int32_t node, phx_stream_t stream) {
   } else if (h->persistent) {
     PHX_HIP(dec::launch_decide_advance(h->arena, (hipStream_t)stream));
     ++h->seq_host;
+  } else if (h->tokens) {
+    rc = launch_tok(h, h->tnodes[(size_t)node], (hipStream_t)stream);
+    if (rc) return rc;
   } else {
     rc = launch_node(h, h->node_list[(size_t)node], (hipStream_t)stream);
     if (rc) return rc;

@@ -1,0 +1,72 @@
+// Internal interface of the large-token kernels (phx_tokens.hip) used by the
+// host engine.  Not part of the public ABI.
+//
+// The large-token plan runs one chunk of many rows (256 video-action tokens
+// over a 4096-token cache, or 4128 DiT-style tokens) through the same block
+// structure as the action expert.  There every projection has hundreds to
+// thousands of rows, so the GEMMs are MFMA-bound and attention is a
+// flash-style pass over key blocks; the plan is a graph of kernels, one per
+// sublayer step, over row-major activations padded to 64 rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace phx {
+namespace tok {
+
+constexpr int ROW_PAD = 128;  // activation buffers hold rows padded to this multiple
+constexpr int DH = 128;      // head dim of the large-token plan
+
+// GEMM epilogues
+enum Epi : int {
+  EP_BF16 = 0,   // out bf16 [rows][N] = acc
+  EP_ROPE = 1,   // out bf16 = acc with rotary encoding of the first rot_cols columns (tile order: pairs
+                 // (j, j + 64) side by side); cos/sin per row from rope [rows][64]
+  EP_GEGLU = 2,  // tile order: gate f and up f side by side; out bf16 [rows][N/2] = GELU_tanh(g) * u
+  EP_GELU = 3,   // out bf16 = GELU_tanh(acc)
+  EP_RESID = 4,  // out f32 [rows][N] += (gate ? gate[n] : 1) * acc
+  EP_EULER = 5,  // out f32 [rows][N] += dt * acc
+  EP_F32 = 6,    // out f32 [rows][N] = acc
+};
+
+struct GemmT {
+  const void* a;       // bf16 activations [Mp][K], row-major
+  const void* w;       // tiled bf16 weights of a [K][N] matrix (16-column x 32-row tiles, n-tile major)
+  void* out;           // see Epi
+  const float* gate;   // EP_RESID: per-column factor, or nullptr
+  const float2* rope;  // EP_ROPE: (cos, sin) [M][64]
+  int rot_cols;        // EP_ROPE: columns [0, rot_cols) are rotated (query and key heads)
+  float dt;            // EP_EULER
+  int M, Mp, K, N;     // real rows, padded rows, reduction length, output columns (tile order)
+  int ldo;             // output row stride in elements
+};
+
+struct AttnT {
+  const void* qkv;   // bf16 [Mp][ldqkv]: query heads from column 0, key heads from H*DH, value heads from (H+KVH)*DH
+  int ldqkv;
+  const void* kp;    // prefix keys of this layer, bf16 [rows][KVH*DH] (rows < L valid)
+  const void* vp;    // prefix values, same layout
+  const int* lens;   // device: L = lens[0] prefix keys, read at launch; nullptr for no prefix
+  int M, H, KVH;     // chunk rows (queries and chunk keys), query heads, key/value heads
+  void* o;           // bf16 [Mp][H*DH] normalised output (splits == 1)
+  float* po;         // splits > 1: unnormalised partial outputs [splits][Mp][H*DH] f32
+  float* pml;        // splits > 1: (max, sum) [splits][Mp][H] f32x2
+  int splits;
+  float scale;       // 1/sqrt(DH)
+};
+
+hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s);
+// kind 0: RMS, 1: LayerNorm (mean subtracted); out[r][d] = bf16(norm(h[r])[d] * (1 + scale[d]) + shift[d]) for
+// r < M, zeros for M <= r < Mp
+hipError_t launch_tnorm(int kind, const float* h, const float* scale, const float* shift, float eps, void* out, int M,
+                        int Mp, int D, hipStream_t s);
+// out[r][d] = bf16(x[r][d]) for r < M, zeros for M <= r < Mp
+hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStream_t s);
+hipError_t launch_tattn(const AttnT& a, hipStream_t s);
+// merges the key splits into the normalised bf16 output
+hipError_t launch_tcombine(const AttnT& a, hipStream_t s);
+
+}  // namespace tok
+}  // namespace phx

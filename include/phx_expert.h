@@ -216,6 +216,12 @@ PHX_API int phx_expert_kernels_per_decision(const phx_expert* h, int* count);
 #define PHX_NODE_DECISION 9          /* the persistent kernel that runs a whole decision (launching it
                                         diagnostically also advances the exchange tags) */
 #define PHX_NODE_TAG_ADVANCE 10      /* advances the persistent kernel's exchange tags */
+/* launches of the large-token plan (more than 160 rows, or the DiT-style block) */
+#define PHX_NODE_ROW_NORM 11         /* adaptive RMSNorm or LayerNorm of the residual rows into bf16 rows */
+#define PHX_NODE_QKV 12              /* QKV projection of the normalised rows (RoPE on q and k in the decoder) */
+#define PHX_NODE_GATEUP 13           /* gate/up projection with GeGLU, or up projection with GELU */
+#define PHX_NODE_OUT_EULER 14        /* velocity projection and x += dt * v */
+#define PHX_NODE_STATE_CVT 15        /* state x to bf16 rows for the input projection */
 
 typedef struct phx_node_info {
   int32_t kind;    /* PHX_NODE_* */

@@ -13,6 +13,16 @@ import phx_inputs
 # activations with fp32 accumulation vs the double-precision oracle
 TOL_BF16 = dict(max_abs=2e-2, rel_l2=1e-2)
 TOL_F32 = dict(max_abs=1e-4, rel_l2=1e-4)
+# The DiT-style step returns the residual stream itself: 1.6M values of
+# standard deviation ~1.3 in the one-block full-width case (12.7M at full
+# size) instead of a few hundred actions.  Each GEMM whose activation operand
+# is rounded to bf16 (RNE, unit roundoff 2^-8) carries a relative error of
+# about 2^-8/sqrt(3) = 2.3e-3 of its result, so one block's MLP branch is off
+# by ~3e-3 of its size and the output by ~2e-3 (rel-L2); the largest of 1.6M
+# such errors lands near 11 of their standard deviations, ~2.5e-2.  The bar
+# keeps the rel-L2 limit and allows max-abs 5e-2, with every row's cosine
+# similarity at least 0.9999 so that no row can hide a local mistake.
+TOL_TOKENS = dict(max_abs=5e-2, rel_l2=1e-2, worst_row_cos=0.9999)
 
 
 def say(msg: str):
@@ -63,6 +73,8 @@ def assert_close(gpu, ref, tol, what=""):
     assert m["finite"], f"{what}: non-finite output"
     assert m["max_abs"] <= tol["max_abs"], f"{what}: max_abs {m['max_abs']:.3e} > {tol['max_abs']}"
     assert m["rel_l2"] <= tol["rel_l2"], f"{what}: rel_l2 {m['rel_l2']:.3e} > {tol['rel_l2']}"
+    if "worst_row_cos" in tol:
+        assert m["cos_worst_row"] >= tol["worst_row_cos"], f"{what}: worst row cosine {m['cos_worst_row']:.6f}"
     return m
 
 
