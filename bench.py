@@ -7,6 +7,11 @@ prefix K/V cache, replayed from the library's captured HIP graph.  Inputs
 (weights, prefix K/V, noise) are synthetic and seeded, and resident in HBM
 before the timed region starts.
 
+--workload va_chunk_bf16 (256-row video-action chunk over a 4096-row cache,
+8 layers x 5 steps) or wam_dit_bf16 (DiT-style step over 4128 tokens, 4
+blocks) measures the large-token plan instead; those are MFMA-bound, so their
+roofline is the dominant GEMM's TFLOP/s against the bf16 dense peak.
+
 Prints ONE JSON line (see --help for the knobs).  Besides the wall-clock
 figure it carries:
   * "roofline": the dominant kernel's algorithmic bytes per launch divided by
@@ -35,7 +40,9 @@ if ROOT not in sys.path:
 import phx_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 WORKLOAD = "pi05_expert_bf16"
+TOKEN_WORKLOADS = ("va_chunk_bf16", "wam_dit_bf16")
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_pi05_expert_bf16.json")
 
@@ -62,9 +69,48 @@ def algorithmic_bytes(cfg: dict) -> dict:
                 per_decision=S * (w_step + kv_step + mod_step))
 
 
-def kernel_source_hash() -> str:
+def token_flops(cfg: dict) -> dict:
+    """Algorithmic FLOPs and bytes of one large-token decision: every GEMM
+    (2 per multiply-add) and attention (QK^T and PV over prefix + chunk keys),
+    and every weight, valid cache row and modulation row once per step."""
+    D, A, F, M = cfg["width"], cfg["state_dim"], cfg["mlp_hidden"], cfg["rows"]
+    H, KVH, Dh, NL, S = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["layers"], cfg["steps"]
+    dit = cfg.get("block", "decoder") == "dit"
+    L = int(phx_inputs.prefix_lengths(cfg)[0])
+    qkv, hd = (H + 2 * KVH) * Dh, H * Dh
+    up = F if dit else 2 * F
+    gemm_layer = 2 * M * (D * qkv + hd * D + D * up + F * D)
+    attn_layer = 4 * M * (L + M) * hd
+    io = 0 if dit else 2 * 2 * M * A * D
+    w_step = 2 * (NL * (D * qkv + hd * D + D * up + F * D) + (0 if dit else 2 * A * D))
+    kv_step = 2 * 2 * NL * L * KVH * Dh
+    mod_step = 4 * (NL * 6 * D if dit else (2 * NL + 1) * 2 * D)
+    return dict(flops_per_decision=S * (NL * (gemm_layer + attn_layer) + io),
+                gemm_flops_per_decision=S * (NL * gemm_layer + io), attn_flops_per_decision=S * NL * attn_layer,
+                bytes_per_decision=S * (w_step + kv_step + mod_step))
+
+
+def node_flops(cfg: dict, kind: int) -> int:
+    """FLOPs of one launch of a large-token plan kernel kind."""
+    from flow_matching_action_decision_amd.binding import PHX_NODE as K
+    D, A, F, M = cfg["width"], cfg["state_dim"], cfg["mlp_hidden"], cfg["rows"]
+    H, KVH, Dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    dit = cfg.get("block", "decoder") == "dit"
+    L = int(phx_inputs.prefix_lengths(cfg)[0])
+    return {K["IN_PROJ"]: 2 * M * A * D, K["QKV"]: 2 * M * D * (H + 2 * KVH) * Dh,
+            K["ATTENTION"]: 4 * M * (L + M) * H * Dh, K["OUT_PROJ_RESID"]: 2 * M * H * Dh * D,
+            K["GATEUP"]: 2 * M * D * (F if dit else 2 * F), K["DOWN_PROJ_RESID"]: 2 * M * F * D,
+            K["OUT_EULER"]: 2 * M * D * A}.get(kind, 0)
+
+
+DECISION_KERNEL_SOURCES = ("phx_decide.hip", "phx_decide.h")
+TOKEN_KERNEL_SOURCES = ("phx_tokens.hip", "phx_tokens.h")
+
+
+def kernel_source_hash(files=DECISION_KERNEL_SOURCES) -> str:
+    """Hash of the sources of the timed kernel (its code and launch shape)."""
     h = hashlib.sha256()
-    for f in ("phx_kernels.hip", "phx_decide.hip", "phx_decide.h", "phx_engine.cpp", "phx_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "flow_matching_action_decision_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -117,6 +163,7 @@ def cpu_baseline(cfg: dict, inp: dict, budget_s: float) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default=WORKLOAD, choices=(WORKLOAD,) + TOKEN_WORKLOADS)
     ap.add_argument("--steps", type=int, default=200, help="timed decisions")
     ap.add_argument("--warmup", type=int, default=20, help="untimed decisions before the timed region")
     ap.add_argument("--seed", type=int, default=0)
@@ -143,6 +190,8 @@ def main():
     from flow_matching_action_decision_amd.expert import Expert
     from flow_matching_action_decision_amd import binding
 
+    if args.workload != WORKLOAD:
+        return bench_tokens(args)
     cfg = phx_inputs.workload(WORKLOAD)
     log(f"bench: generating inputs for {WORKLOAD}")
     inp = phx_inputs.make_inputs(cfg, args.seed)
@@ -226,6 +275,143 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_tokens(args):
+    """The large-token workloads: decision time, per-kind kernel breakdown,
+    and the dominant GEMM against the MFMA bf16 peak."""
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+
+    name = args.workload
+    cfg = phx_inputs.workload(name)
+    dit = cfg.get("block", "decoder") == "dit"
+    log(f"bench: generating inputs for {name}")
+    inp = phx_inputs.make_inputs(cfg, args.seed)
+    fl = token_flops(cfg)
+    log("bench: creating handle")
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    keep = ex.load_all(inp)
+    noise = torch.from_numpy(inp["noise"]).cuda()
+    out = torch.empty_like(noise)
+    stream = torch.cuda.current_stream()
+    steps = min(args.steps, 50)
+    warm = min(args.warmup, 5)
+    for _ in range(warm):
+        ex.decide(noise, out)
+    torch.cuda.synchronize()
+    log(f"bench: timing {steps} decisions")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        ex.decide(noise, out)
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / steps
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+    log(f"bench: {ms:.4f} ms/decision")
+
+    # per-kind breakdown over the first step's launches, and the dominant kind by FLOPs
+    nodes = ex.nodes()
+    first = [i for i, n in enumerate(nodes) if n["step"] == 0]
+    t = ex.time_nodes(first, reps=max(3, min(args.kernel_reps, 10)))
+    kinds = {}
+    for i, tm in zip(first, t):
+        n = nodes[i]
+        k = kinds.setdefault(n["name"], dict(kind=n["kind"], launches=0, ms=0.0, flops=0))
+        k["launches"] += 1
+        k["ms"] += tm
+        k["flops"] += node_flops(cfg, n["kind"])
+    for nm, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
+        tf = k["flops"] / (k["ms"] * 1e-3) / 1e12 if k["flops"] else 0.0
+        log(f"  {nm:24s} x{k['launches']:3d}  {k['ms'] * 1e3 / k['launches']:9.1f} us/launch  {tf:7.1f} TFLOP/s")
+    dom_name = max(kinds, key=lambda nm: kinds[nm]["flops"])
+    dk = kinds[dom_name]
+    us = dk["ms"] * 1e3 / dk["launches"]
+    f_launch = dk["flops"] // dk["launches"]
+    achieved = f_launch / (us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom_name,
+                "flops_per_launch": f_launch, "us_per_launch": round(us, 3),
+                "kernel_hash": kernel_source_hash(TOKEN_KERNEL_SOURCES)}
+    res = out.cpu().numpy()
+    assert np.all(np.isfinite(res)), "non-finite output"
+    nk = ex.kernels_per_decision()
+    del keep
+    ex.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline_tokens(cfg, inp, fl)
+
+    tflops = fl["flops_per_decision"] / (ms * 1e-3) / 1e12
+    hbm = fl["bytes_per_decision"] / (ms * 1e-3) / 1e9
+    line = {
+        "metric": f"ms/decision ({name}) + % of MFMA bf16 peak, 1 GPU",
+        "value": round(ms, 4), "unit": "ms/decision", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 cache, N(0,1) state)",
+        "config": {"workload": name, "block": "dit" if dit else "decoder", "layers": cfg["layers"],
+                   "euler_steps": cfg["steps"], "rows": cfg["rows"],
+                   "prefix_len": int(phx_inputs.prefix_lengths(cfg)[0]), "width": cfg["width"],
+                   "heads": f"{cfg['n_heads']}x{cfg['head_dim']} / {cfg['n_kv_heads']} kv",
+                   "mlp_hidden": cfg["mlp_hidden"]},
+        "decisions_per_s": round(1000.0 / ms, 2),
+        "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
+        "flops_per_decision": fl["flops_per_decision"], "tflops": round(tflops, 1),
+        "mfma_frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "algorithmic_bytes_per_decision": fl["bytes_per_decision"], "hbm_gbs": round(hbm, 1),
+        "kernels_per_decision": nk, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_tokens(cfg: dict, inp: dict, fl: dict) -> dict:
+    """Time the oracle, unchanged, on a bounded slice of the same workload
+    (one layer of one step for the chunk; one block over 528 tokens for the
+    DiT-style step) and scale by the FLOP ratio to a whole decision."""
+    import oracle
+    lib = oracle.load()
+    if cfg.get("block", "decoder") == "dit":
+        sc = dict(cfg, layers=1, rows=528)
+        x = inp["noise"][0, :528]
+        wsl = phx_inputs.weight_slices(cfg)
+        ssl = phx_inputs.weight_slices(sc)
+        w = np.empty(phx_inputs.weight_count(sc), dtype=np.float32)
+        for nm, (off, shape) in ssl.items():
+            if nm == "W_mod":
+                o2, sh2 = wsl["W_mod"]
+                w[off:off + int(np.prod(shape))] = inp["weights"][o2:o2 + int(np.prod(shape))]
+            else:
+                o2, _ = wsl[nm]
+                w[off:off + int(np.prod(shape))] = inp["weights"][o2:o2 + int(np.prod(shape))]
+        t0 = time.perf_counter()
+        oracle.dit(sc, w, x, lib=lib)
+        dt_s = time.perf_counter() - t0
+        what = "one block over 528 of the 4128 tokens"
+    else:
+        sc = dict(cfg, layers=1, steps=1)
+        wsl = phx_inputs.weight_slices(cfg)
+        ssl = phx_inputs.weight_slices(sc)
+        w = np.empty(phx_inputs.weight_count(sc), dtype=np.float32)
+        for nm, (off, shape) in ssl.items():
+            n = int(np.prod(shape))
+            o2, _ = wsl[nm]
+            w[off:off + n] = inp["weights"][o2:o2 + n]
+        t0 = time.perf_counter()
+        oracle.decide(sc, w, inp["kv_k"][:, :1], inp["kv_v"][:, :1], inp["lens"], inp["noise"], lib=lib)
+        dt_s = time.perf_counter() - t0
+        what = "one layer of one Euler step (with the in- and out-projections)"
+    fs = token_flops(sc)["flops_per_decision"]
+    return {"value": round(dt_s * fl["flops_per_decision"] / fs * 1e3, 1), "unit": "ms/decision",
+            "cores": omp_threads(), "kind": "oracle",
+            "sample": f"{what} (double-precision oracle, OpenMP), scaled by FLOPs to a full decision"}
 
 
 if __name__ == "__main__":

@@ -20,6 +20,10 @@ PHX_FLAG_NO_GRAPH = 1
 PHX_FLAG_MULTI_KERNEL = 2
 PHX_FLAG_TIMELINE = 4
 PHX_BLOCK_DECODER, PHX_BLOCK_DIT = 0, 1
+# launch kinds reported by phx_expert_node_info
+PHX_NODE = dict(IN_PROJ=1, NORM_QKV_ROPE=2, ATTENTION=3, ATTN_COMBINE=4, OUT_PROJ_RESID=5, NORM_GATEUP_GEGLU=6,
+                DOWN_PROJ_RESID=7, NORM_OUT_EULER=8, DECISION=9, TAG_ADVANCE=10, ROW_NORM=11, QKV=12, GATEUP=13,
+                OUT_EULER=14, STATE_CVT=15)
 PHX_MASK_FULL = 0
 
 # every function include/phx_expert.h declares

@@ -154,12 +154,15 @@ struct phx_expert {
   bool tokens = false;
   int Mp = 0;                 // rows padded to tok::ROW_PAD
   int splits = 1;             // attention key splits
+  int n_cu = 0;               // compute units of the device
+  float* tpart = nullptr;     // GEMM split partials of the large-token plan
   std::vector<TokNode> tnodes;
   void* xb = nullptr;         // bf16 state rows (input projection operand)
   void* nb = nullptr;         // bf16 normalised rows
-  void* qkv = nullptr;        // bf16 q | k | v rows
-  void* tk = nullptr;         // prefix keys [NL][C][KVH*Dh]
-  void* tv = nullptr;         // prefix values, same layout
+  void* qkv = nullptr;        // bf16 query rows [Mp][H*Dh]
+  int R = 0;                  // key rows per layer: prefix capacity plus the chunk, padded to 64
+  void* tk = nullptr;         // key rows [layers][R][KVH*Dh]: prefix, then the chunk from row L
+  void* tv = nullptr;         // values [layers][KVH][R*Dh] in the attention's fragment order
   float* po = nullptr;        // attention partials of the key splits
   float* pml = nullptr;
 };
@@ -529,7 +532,7 @@ int build_tok_nodes(phx_expert* h) {
   const phx_expert_config& c = h->cfg;
   const bool dit = c.block_kind == PHX_BLOCK_DIT;
   const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = c.rows;
-  const int NL = c.layers, C = c.prefix_capacity;
+  const int NL = c.layers;
   const int HD = H * tok::DH, NQKV = (H + 2 * KVH) * tok::DH, kvd = KVH * tok::DH;
   const int Mp = h->Mp;
   h->tnodes.clear();
@@ -540,7 +543,8 @@ int build_tok_nodes(phx_expert* h) {
     nd.kind = kind; nd.step = k; nd.layer = l; nd.op = TOP_GEMM; nd.epi = epi;
     tok::GemmT& g = nd.g;
     g.a = a; g.w = (const char*)h->wt + w_off * 2; g.out = out; g.gate = gate; g.rope = h->rope;
-    g.rot_cols = (H + KVH) * tok::DH; g.dt = c.dt; g.M = M; g.Mp = Mp; g.K = K; g.N = N; g.ldo = ldo;
+    g.rot_cols = dit ? 0 : (H + KVH) * tok::DH; g.dt = c.dt; g.M = M; g.Mp = Mp; g.K = K; g.N = N; g.ldo = ldo;
+    tok::plan_gemm(g, h->n_cu);
     const int out_cols = epi == tok::EP_GEGLU ? N / 2 : N;
     const int out_esz = (epi == tok::EP_RESID || epi == tok::EP_EULER || epi == tok::EP_F32) ? 4 : 2;
     const uint64_t rmw = (epi == tok::EP_RESID || epi == tok::EP_EULER) ? 2 : 1;
@@ -558,11 +562,19 @@ int build_tok_nodes(phx_expert* h) {
     name_of(nd, name);
     h->tnodes.push_back(nd);
   };
-  auto attention = [&](int k, int l, const void* kp, const void* vp) {
+  const int R = h->R;
+  auto layer_k = [&](int l) { return (char*)h->tk + (dit ? 0 : (size_t)l * R * kvd * 2); };
+  auto layer_v = [&](int l) { return (char*)h->tv + (dit ? 0 : (size_t)l * R * kvd * 2); };
+  auto qkv = [&](int k, int l, const char* name) {
+    gemm(PHX_NODE_QKV, k, l, tok::EP_QKV, h->nb, h->off_qkv[l], D, NQKV, h->qkv, HD, nullptr, name);
+    tok::GemmT& g = h->tnodes.back().g;
+    g.kj = layer_k(l); g.vt = layer_v(l); g.lens = dit ? nullptr : h->lens; g.H = H; g.KVH = KVH; g.nj = R / 32;
+  };
+  auto attention = [&](int k, int l) {
     TokNode nd{};
     nd.kind = PHX_NODE_ATTENTION; nd.step = k; nd.layer = l; nd.op = TOP_ATTN;
     tok::AttnT& a = nd.a;
-    a.qkv = h->qkv; a.ldqkv = NQKV; a.kp = kp; a.vp = vp; a.lens = dit ? nullptr : h->lens;
+    a.q = h->qkv; a.ldq = HD; a.kj = layer_k(l); a.vt = layer_v(l); a.lens = dit ? nullptr : h->lens; a.R = R;
     a.M = M; a.H = H; a.KVH = KVH; a.o = h->o; a.po = h->po; a.pml = h->pml; a.splits = h->splits;
     a.scale = (float)(1.0 / std::sqrt((double)tok::DH));
     name_of(nd, "attention");
@@ -579,8 +591,8 @@ int build_tok_nodes(phx_expert* h) {
     for (int l = 0; l < NL; ++l) {
       const float* mod = h->modtab + (size_t)l * 6 * D;  // shift, scale, gate (attention), then (MLP)
       norm(0, l, 1, mod + D, mod, "layernorm_attn");
-      gemm(PHX_NODE_QKV, 0, l, tok::EP_BF16, h->nb, h->off_qkv[l], D, NQKV, h->qkv, NQKV, nullptr, "qkv");
-      attention(0, l, nullptr, nullptr);
+      qkv(0, l, "qkv");
+      attention(0, l);
       gemm(PHX_NODE_OUT_PROJ_RESID, 0, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, mod + 2 * D,
            "out_proj_gated_resid");
       norm(0, l, 1, mod + 4 * D, mod + 3 * D, "layernorm_mlp");
@@ -606,8 +618,8 @@ int build_tok_nodes(phx_expert* h) {
       const float* m1 = mod_k + (size_t)(2 * l) * 2 * D;
       const float* m2 = mod_k + (size_t)(2 * l + 1) * 2 * D;
       norm(k, l, 0, m1, m1 + D, "rmsnorm_attn");
-      gemm(PHX_NODE_QKV, k, l, tok::EP_ROPE, h->nb, h->off_qkv[l], D, NQKV, h->qkv, NQKV, nullptr, "qkv_rope");
-      attention(k, l, (const char*)h->tk + (size_t)l * C * kvd * 2, (const char*)h->tv + (size_t)l * C * kvd * 2);
+      qkv(k, l, "qkv_rope");
+      attention(k, l);
       gemm(PHX_NODE_OUT_PROJ_RESID, k, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, nullptr,
            "out_proj_resid");
       norm(k, l, 0, m2, m2 + D, "rmsnorm_mlp");
@@ -629,7 +641,7 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   const bool dit = c.block_kind == PHX_BLOCK_DIT;
   const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = c.rows;
   const int NL = c.layers, S = c.steps, E = c.time_emb_dim, C = c.prefix_capacity;
-  const int HD = H * tok::DH, NQKV = (H + 2 * KVH) * tok::DH, kvd = KVH * tok::DH;
+  const int HD = H * tok::DH, kvd = KVH * tok::DH;
   const int Mp = (M + tok::ROW_PAD - 1) / tok::ROW_PAD * tok::ROW_PAD;
   h->Mp = Mp;
   int rc;
@@ -641,9 +653,12 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   PHX_HIP(launch_time_embedding((double*)etab, MS, E, c.tau0, c.dt, stream));
   PHX_HIP(launch_modulation(1, sb + mod_off * 2, (const double*)etab, h->modtab, MS, NN, E, MW, stream));
 
+  // key rows: the prefix capacity plus the chunk, padded to whole 64-key blocks
+  h->R = (C + M + 63) / 64 * 64;
+  const int R = h->R;
   // attention key splits: enough workgroups to cover the chip, at least four key blocks per split
-  const long long q_wgs = (long long)((M + 63) / 64) * H;
-  const int max_blocks = (C + M + 63) / 64;
+  const long long q_wgs = (long long)((M + 127) / 128) * H;
+  const int max_blocks = R / 64;
   h->splits = 1;
   while (q_wgs * h->splits < 512 && max_blocks / (h->splits * 2) >= 4) h->splits *= 2;
 
@@ -651,15 +666,15 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   std::vector<Buf> bufs = {
       {(void**)&h->h, (size_t)Mp * D * 4, "residual rows"},
       {&h->nb, (size_t)Mp * D * 2, "normalised rows"},
-      {&h->qkv, (size_t)Mp * NQKV * 2, "qkv rows"},
+      {&h->qkv, (size_t)Mp * HD * 2, "query rows"},
+      {&h->tk, (size_t)(dit ? 1 : NL) * R * kvd * 2, "key rows"},
+      {&h->tv, (size_t)(dit ? 1 : NL) * R * kvd * 2, "value fragments"},
       {&h->o, (size_t)Mp * HD * 2, "attention output rows"},
       {&h->act, (size_t)Mp * F * 2, "MLP activation rows"},
   };
   if (!dit) {
     bufs.push_back({(void**)&h->x, (size_t)Mp * A * 4, "state rows"});
     bufs.push_back({&h->xb, (size_t)Mp * A * 2, "bf16 state rows"});
-    bufs.push_back({&h->tk, (size_t)NL * C * kvd * 2, "prefix keys"});
-    bufs.push_back({&h->tv, (size_t)NL * C * kvd * 2, "prefix values"});
     bufs.push_back({(void**)&h->lens, sizeof(int), "prefix length"});
     bufs.push_back({(void**)&h->rope, (size_t)M * (tok::DH / 2) * sizeof(float2), "position table"});
   }
@@ -681,6 +696,16 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
 
   if ((rc = build_tok_nodes(h))) return rc;
   h->nodes = (int)h->tnodes.size();
+  size_t part = 0;
+  for (const TokNode& nd : h->tnodes)
+    if (nd.op == TOP_GEMM) part = std::max(part, tok::gemm_part_elems(nd.g));
+  if (part) {
+    if ((rc = alloc(h, (void**)&h->tpart, part * sizeof(float), "GEMM split partials"))) return rc;
+    for (TokNode& nd : h->tnodes)
+      if (nd.op == TOP_GEMM) nd.g.part = h->tpart;
+  }
+  PHX_HIP(tok::prepare_gemm());
+  PHX_HIP(tok::prepare_attention());
   if (!(c.flags & PHX_FLAG_NO_GRAPH)) {
     PHX_HIP(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
     rc = PHX_OK;
@@ -848,7 +873,7 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
   };
   if (!dit && (rc = retile(h->off_in, A, D, COL_IDENT, 0))) return rc;
   for (int l = 0; l < NL; ++l) {
-    if ((rc = retile(h->off_qkv[l], D, qkvN, dit ? COL_IDENT : COL_ROPE, Dh))) return rc;
+    if ((rc = retile(h->off_qkv[l], D, qkvN, COL_ROPE, Dh))) return rc;
     if ((rc = retile(h->off_o[l], H * Dh, D, COL_IDENT, 0))) return rc;
     if ((rc = retile(h->off_gu[l], D, gu_cols, dit ? COL_IDENT : COL_GEGLU, F))) return rc;
     if ((rc = retile(h->off_down[l], F, D, COL_IDENT, 0))) return rc;
@@ -856,6 +881,7 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
   if (!dit && (rc = retile(h->off_out, D, A, COL_IDENT, 0))) return rc;
 
   h->tokens = uses_tokens(c);
+  h->n_cu = prop.multiProcessorCount;
   if (h->tokens) {
     rc = create_tokens(h, sb, stream, off);
     if (rc) return rc;
@@ -995,14 +1021,13 @@ int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, con
     return PHX_OK;
   }
   if (h->tokens) {
-    // [NL][L][kvd] -> [NL][C][kvd]; rows beyond L are never read
+    // keys [NL][L][kvd] -> rows 0..L-1 of each layer's key rows (rows from L on are the chunk's, or
+    // masked); values into the fragment order, zeros from key L on
     const size_t row = (size_t)c.n_kv_heads * c.head_dim * 2;
-    if (prefix_len > 0) {
-      PHX_HIP(hipMemcpy2DAsync(h->tk, (size_t)c.prefix_capacity * row, k, (size_t)prefix_len * row,
-                               (size_t)prefix_len * row, (size_t)c.layers, hipMemcpyDeviceToDevice, s));
-      PHX_HIP(hipMemcpy2DAsync(h->tv, (size_t)c.prefix_capacity * row, v, (size_t)prefix_len * row,
-                               (size_t)prefix_len * row, (size_t)c.layers, hipMemcpyDeviceToDevice, s));
-    }
+    if (prefix_len > 0)
+      PHX_HIP(hipMemcpy2DAsync(h->tk, (size_t)h->R * row, k, (size_t)prefix_len * row, (size_t)prefix_len * row,
+                               (size_t)c.layers, hipMemcpyDeviceToDevice, s));
+    PHX_HIP(tok::launch_vt_load(v, h->tv, c.layers, prefix_len, h->R, c.n_kv_heads, s));
   } else if (h->persistent) {
     PHX_HIP(dec::launch_attn_tiles(k, v, h->kvt, c.layers, prefix_len, h->n_chunks, s));
   } else {

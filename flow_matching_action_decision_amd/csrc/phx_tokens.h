@@ -22,8 +22,9 @@ constexpr int DH = 128;      // head dim of the large-token plan
 // GEMM epilogues
 enum Epi : int {
   EP_BF16 = 0,   // out bf16 [rows][N] = acc
-  EP_ROPE = 1,   // out bf16 = acc with rotary encoding of the first rot_cols columns (tile order: pairs
-                 // (j, j + 64) side by side); cos/sin per row from rope [rows][64]
+  EP_QKV = 1,    // tile order: rotary pairs (j, j + 64) side by side per head; rotary encoding of the
+                 // first rot_cols columns (cos/sin per row from rope [rows][64]); query heads to out
+                 // [rows][ldo], key heads to key row L + row of kj, value heads into vt (fragment order)
   EP_GEGLU = 2,  // tile order: gate f and up f side by side; out bf16 [rows][N/2] = GELU_tanh(g) * u
   EP_GELU = 3,   // out bf16 = GELU_tanh(acc)
   EP_RESID = 4,  // out f32 [rows][N] += (gate ? gate[n] : 1) * acc
@@ -36,19 +37,32 @@ struct GemmT {
   const void* w;       // tiled bf16 weights of a [K][N] matrix (16-column x 32-row tiles, n-tile major)
   void* out;           // see Epi
   const float* gate;   // EP_RESID: per-column factor, or nullptr
-  const float2* rope;  // EP_ROPE: (cos, sin) [M][64]
-  int rot_cols;        // EP_ROPE: columns [0, rot_cols) are rotated (query and key heads)
+  const float2* rope;  // EP_QKV: (cos, sin) [M][64]
+  int rot_cols;        // EP_QKV: columns [0, rot_cols) are rotated (query and key heads), 0 for none
+  void* kj;            // EP_QKV: key rows [R][KVH*DH] of this layer
+  void* vt;            // EP_QKV: values of this layer in fragment order, [KVH][R*DH]
+  const int* lens;     // EP_QKV: device prefix length L (chunk row r is key L + r), nullptr for 0
+  int H, KVH, nj;      // EP_QKV: query heads, kv heads, 32-key steps of kj/vt (R / 32)
   float dt;            // EP_EULER
   int M, Mp, K, N;     // real rows, padded rows, reduction length, output columns (tile order)
   int ldo;             // output row stride in elements
+  int tile;            // workgroup tile shape (set by plan_gemm)
+  int splits;          // k splits (set by plan_gemm); > 1 needs part
+  float* part;         // split partials [splits][Mp][N] f32
 };
 
+// Chooses the tile shape and k splits of g for a chip of n_cu compute units.
+void plan_gemm(GemmT& g, int n_cu);
+// f32 elements of split partials g needs (0 without splits).
+size_t gemm_part_elems(const GemmT& g);
+
 struct AttnT {
-  const void* qkv;   // bf16 [Mp][ldqkv]: query heads from column 0, key heads from H*DH, value heads from (H+KVH)*DH
-  int ldqkv;
-  const void* kp;    // prefix keys of this layer, bf16 [rows][KVH*DH] (rows < L valid)
-  const void* vp;    // prefix values, same layout
+  const void* q;     // bf16 queries [Mp][ldq], head h from column h*DH
+  int ldq;
+  const void* kj;    // bf16 key rows of this layer [R][KVH*DH]: prefix rows, then the chunk's rows from row L
+  const void* vt;    // bf16 values of this layer in fragment order [KVH][R*DH]
   const int* lens;   // device: L = lens[0] prefix keys, read at launch; nullptr for no prefix
+  int R;             // key rows allocated (multiple of 64, >= L + M)
   int M, H, KVH;     // chunk rows (queries and chunk keys), query heads, key/value heads
   void* o;           // bf16 [Mp][H*DH] normalised output (splits == 1)
   float* po;         // splits > 1: unnormalised partial outputs [splits][Mp][H*DH] f32
@@ -57,6 +71,8 @@ struct AttnT {
   float scale;       // 1/sqrt(DH)
 };
 
+// Lets every GEMM instantiation use the LDS its tile needs (call once per device, outside graph capture).
+hipError_t prepare_gemm();
 hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s);
 // kind 0: RMS, 1: LayerNorm (mean subtracted); out[r][d] = bf16(norm(h[r])[d] * (1 + scale[d]) + shift[d]) for
 // r < M, zeros for M <= r < Mp
@@ -64,9 +80,13 @@ hipError_t launch_tnorm(int kind, const float* h, const float* scale, const floa
                         int Mp, int D, hipStream_t s);
 // out[r][d] = bf16(x[r][d]) for r < M, zeros for M <= r < Mp
 hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStream_t s);
+// Lets the attention kernel use its LDS ring (call once per device, outside graph capture).
+hipError_t prepare_attention();
 hipError_t launch_tattn(const AttnT& a, hipStream_t s);
 // merges the key splits into the normalised bf16 output
 hipError_t launch_tcombine(const AttnT& a, hipStream_t s);
+// Prefix values v [NL][L][KVH*DH] into the fragment order vt [NL][KVH][R*DH] (zeros for keys L..R-1).
+hipError_t launch_vt_load(const void* v, void* vt, int NL, int L, int R, int KVH, hipStream_t s);
 
 }  // namespace tok
 }  // namespace phx

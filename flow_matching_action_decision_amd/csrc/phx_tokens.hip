@@ -15,6 +15,9 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
+#include <cmath>
+
 namespace phx {
 namespace tok {
 
@@ -45,123 +48,313 @@ __device__ inline f32x4 mma16(const s16x4& a, const s16x4& b, const f32x4& c) {
 }
 
 // ------------------------------------------------------------------ GEMM
-// Workgroup of 4 waves covering output columns [64 NTW bx, +64 NTW) and rows
-// [16 MTW by, +16 MTW).  Wave w owns n-tiles 4 NTW bx + NTW w + [0, NTW) and
-// all MTW m-tiles.  Per 32-row k-step the workgroup stages its activation
-// rows in LDS once, in fragment order (m-tile, lane), and every wave reads
-// its weight tiles straight from the arena.
-template <int NTW, int MTW, int EPI>
-__global__ __launch_bounds__(256) void k_tgemm(GemmT g) {
-  constexpr int BM = 16 * MTW;
-  __shared__ u32x4 as[MTW * 64];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int nt0 = (blockIdx.x * 4 + wave) * NTW;
-  const int m0 = blockIdx.y * BM;
-  const int KT = g.K / 32;
-  const bf16* A = (const bf16*)g.a;
-  const bf16* W = (const bf16*)g.w;
-  f32x4 acc[NTW][MTW];
+// Workgroup of 4 waves covering output columns [BN bx, +BN) (BN = 64 WN) and
+// rows [BM by, +BM) (BM = 16 WM); wave w owns n-tiles WN (4 bx + w) + [0, WN)
+// and all WM m-tiles, so per 32-deep k-step it runs WN x WM MFMAs on WN weight
+// fragments and the WM activation fragments the four waves share.
+//
+// Both operands reach LDS straight from memory (buffer loads with the LDS
+// bit, no registers in between), each 1 KiB load already in MFMA fragment
+// order: a weight fragment is one contiguous tile of the arena; an activation
+// fragment is 16 rows x 64 bytes.  The k-steps rotate through an NSTAGE-deep
+// ring; every wave waits for its own loads with an explicit vmcnt and a
+// barrier publishes the stage, so NSTAGE - 1 k-steps are in flight while one
+// is multiplied.  With split > 1 workgroup z multiplies k-steps [z KT/split,
+// (z+1) KT/split) and stores its raw sums for an ordered reduction.
+constexpr int NSTAGE = 4;
+
+template <int WN, int WM>
+struct Tile {
+  static constexpr int BN = 64 * WN, BM = 16 * WM;
+  static constexpr int FR = WM + 4 * WN;  // 1 KiB fragments per k-step
+  static constexpr int PW = WM / 4 + WN;  // loads per wave per k-step
+  static constexpr int LDS = NSTAGE * FR * 1024;
+};
+
+__device__ inline u32x4 rsrc_words(const void* p, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)p;
+  return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// one 1 KiB fragment into LDS at M0 + 16 lane
+__device__ inline void dma_frag(unsigned lds, unsigned voff, u32x4 rs, unsigned soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rs),
+               "s"(soff)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// barrier without the fence __syncthreads implies (that fence would wait for
+// every load in flight); the empty asm statements keep LDS accesses on their side
+__device__ inline void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Values of one kv head in the order the attention's PV step reads them: for
+// each 32-key step j and 16-dim tile dt, one 1 KiB MFMA fragment in which
+// lane (d % 16) + 16 g holds dim d and the keys 32 j + 4 g + [0, 4) (elements
+// 0..3) and 32 j + 16 + 4 g + [0, 4) (elements 4..7).
+__device__ inline size_t vt_index(int kvh, int nj, int t, int d) {
+  const int j = t >> 5, kk = t & 31, rr = kk & 15;
+  const int e = (rr & 3) + 4 * (kk >> 4), ln = (d & 15) + 16 * (rr >> 2);
+  return ((((size_t)kvh * nj + j) * 8 + (d >> 4)) * 64 + ln) * 8 + e;
+}
+
+// inverse of vt_index within one kv head's plane
+__device__ inline void vt_key_dim(int i, int& t, int& d) {
+  const int e = i & 7, ln = (i >> 3) & 63, dt = (i >> 9) & 7, j = i >> 12;
+  d = 16 * dt + (ln & 15);
+  t = 32 * j + 16 * (e >> 2) + 4 * (ln >> 4) + (e & 3);
+}
+
+// output columns 4 gq + [0, 4) of n-tile nt (tile order) of one row
+template <int EPI>
+__device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const f32x4& v) {
+  if constexpr (EPI == EP_BF16 || EPI == EP_GELU) {
+    float y[4];
 #pragma unroll
-  for (int n = 0; n < NTW; ++n)
-#pragma unroll
-    for (int m = 0; m < MTW; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kt = 0; kt < KT; ++kt) {
-    // stage: thread t moves rows p*64 + t/4 (k chunk t%4) of the block
-#pragma unroll
-    for (int p = 0; p < (BM + 63) / 64; ++p) {
-      const int r = p * 64 + (t >> 2);
-      if (r < BM) {
-        const u32x4 v = *(const u32x4*)(A + (size_t)(m0 + r) * g.K + kt * 32 + 8 * (t & 3));
-        as[(r >> 4) * 64 + (r & 15) + 16 * (t & 3)] = v;
+    for (int i = 0; i < 4; ++i) y[i] = EPI == EP_GELU ? gelu_tanh(v[i]) : v[i];
+    *(u32x2*)((bf16*)g.out + (size_t)row * g.ldo + nt * 16 + 4 * gq) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+  } else if constexpr (EPI == EP_QKV) {
+    // tile order of a head (query heads, then key heads, then value heads):
+    // the values are dims j, j + 1, j + 64, j + 65 with j = 8 (nt % 8) + 2 gq
+    const int hh = nt >> 3, j = 8 * (nt & 7) + 2 * gq;
+    float y0 = v[0], y1 = v[1], y2 = v[2], y3 = v[3];
+    if (hh * DH < g.rot_cols) {
+      const float2 a = g.rope[(size_t)row * (DH / 2) + j];
+      const float2 b = g.rope[(size_t)row * (DH / 2) + j + 1];
+      y0 = v[0] * a.x - v[2] * a.y;
+      y2 = v[2] * a.x + v[0] * a.y;
+      y1 = v[1] * b.x - v[3] * b.y;
+      y3 = v[3] * b.x + v[1] * b.y;
+    }
+    const int L = g.lens ? g.lens[0] : 0;
+    if (hh < g.H) {
+      bf16* o = (bf16*)g.out + (size_t)row * g.ldo + hh * DH + j;
+      *(unsigned*)o = pack2(y0, y1);
+      *(unsigned*)(o + DH / 2) = pack2(y2, y3);
+    } else if (hh < g.H + g.KVH) {
+      bf16* o = (bf16*)g.kj + (size_t)(L + row) * (g.KVH * DH) + (hh - g.H) * DH + j;
+      *(unsigned*)o = pack2(y0, y1);
+      *(unsigned*)(o + DH / 2) = pack2(y2, y3);
+    } else {
+      const int kvh = hh - g.H - g.KVH, t = L + row;
+      bf16* vt = (bf16*)g.vt;
+      vt[vt_index(kvh, g.nj, t, j)] = (bf16)y0;
+      vt[vt_index(kvh, g.nj, t, j + 1)] = (bf16)y1;
+      vt[vt_index(kvh, g.nj, t, j + DH / 2)] = (bf16)y2;
+      vt[vt_index(kvh, g.nj, t, j + DH / 2 + 1)] = (bf16)y3;
+    }
+  } else if constexpr (EPI == EP_GEGLU) {
+    // features 8 nt + 2 gq + {0, 1}: gate in v[0], v[1], up in v[2], v[3]
+    const int f = 8 * nt + 2 * gq;
+    *(unsigned*)((bf16*)g.out + (size_t)row * g.ldo + f) = pack2(gelu_tanh(v[0]) * v[2], gelu_tanh(v[1]) * v[3]);
+  } else {
+    float* o = (float*)g.out + (size_t)row * g.ldo + nt * 16 + 4 * gq;
+    f32x4 cur = EPI == EP_F32 ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)o;
+    if constexpr (EPI == EP_RESID) {
+      if (g.gate) {
+        const f32x4 gt = *(const f32x4*)(g.gate + nt * 16 + 4 * gq);
+        cur += gt * v;
+      } else {
+        cur += v;
       }
+    } else if constexpr (EPI == EP_EULER) {
+      cur += g.dt * v;
+    } else {
+      cur = v;
     }
-    bf16x8 wf[NTW];
-#pragma unroll
-    for (int n = 0; n < NTW; ++n)
-      wf[n] = __builtin_bit_cast(bf16x8, *(const u32x4*)(W + (((size_t)(nt0 + n) * KT + kt) * 64 + lane) * 8));
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < MTW; ++m) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, as[m * 64 + lane]);
-#pragma unroll
-      for (int n = 0; n < NTW; ++n) acc[n][m] = mma32(wf[n], af, acc[n][m]);
-    }
-    __syncthreads();
+    *(f32x4*)o = cur;
   }
-  // epilogue: lane holds columns 4 (lane / 16) + [0, 4) of each n-tile (tile
-  // order) for row lane % 16 of each m-tile
+}
+
+template <int WN, int WM, int EPI>
+__global__ __launch_bounds__(256) void k_tgemm(GemmT g) {
+  using T = Tile<WN, WM>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nt0 = (blockIdx.x * 4 + wave) * WN;
+  const int m0 = blockIdx.y * T::BM;
+  const int KT = g.K / 32;
+  const int per = KT / g.splits;
+  const int kb = blockIdx.z * per;
+  const int nk = per;
+  const unsigned lds0 = (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)smem);
+  const u32x4 ra = rsrc_words(g.a, (unsigned)((size_t)g.Mp * g.K * 2));
+  const u32x4 rw = rsrc_words(g.w, (unsigned)((size_t)g.K * g.N * 2));
+  // this wave's activation fragments: m-tiles wave * WM/4 + i; lane: row 16 m + lane % 16, k chunk lane / 16
+  unsigned voa[WM / 4];
+#pragma unroll
+  for (int i = 0; i < WM / 4; ++i) {
+    const int m = wave * (WM / 4) + i;
+    voa[i] = (unsigned)(((size_t)(m0 + 16 * m + (lane & 15)) * g.K + 8 * (lane >> 4)) * 2);
+  }
+  const unsigned vow = (unsigned)lane * 16u;
+  auto issue = [&](int s) {
+    const int kt = kb + s;
+    const unsigned st = lds0 + (unsigned)((s % NSTAGE) * T::FR * 1024);
+#pragma unroll
+    for (int i = 0; i < WM / 4; ++i)
+      dma_frag(st + (unsigned)((wave * (WM / 4) + i) * 1024), voa[i], ra, (unsigned)(kt * 64));
+#pragma unroll
+    for (int n = 0; n < WN; ++n)
+      dma_frag(st + (unsigned)((WM + wave * WN + n) * 1024), vow, rw,
+               (unsigned)(((size_t)(nt0 + n) * KT + kt) * 1024));
+  };
+  f32x4 acc[WN][WM];
+#pragma unroll
+  for (int n = 0; n < WN; ++n)
+#pragma unroll
+    for (int m = 0; m < WM; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < nk) issue(s);
+  for (int s = 0; s < nk; ++s) {
+    const int ahead = min(NSTAGE - 2, nk - 1 - s);  // later k-steps already issued
+    if (ahead >= 2) wait_vm<2 * T::PW>();
+    else if (ahead == 1) wait_vm<T::PW>();
+    else wait_vm<0>();
+    wg_barrier();  // stage s is in LDS for every wave; every wave is done with stage s - 1
+    if (s + NSTAGE - 1 < nk) issue(s + NSTAGE - 1);
+    const unsigned char* st = smem + (s % NSTAGE) * T::FR * 1024;
+    bf16x8 wf[WN];
+#pragma unroll
+    for (int n = 0; n < WN; ++n) wf[n] = *(const bf16x8*)(st + (WM + wave * WN + n) * 1024 + lane * 16);
+#pragma unroll
+    for (int m = 0; m < WM; ++m) {
+      const bf16x8 af = *(const bf16x8*)(st + m * 1024 + lane * 16);
+#pragma unroll
+      for (int n = 0; n < WN; ++n) acc[n][m] = mma32(wf[n], af, acc[n][m]);
+    }
+  }
+  // lane holds columns 4 (lane / 16) + [0, 4) of each n-tile (tile order) for
+  // row lane % 16 of each m-tile
   const int gq = lane >> 4;
 #pragma unroll
-  for (int m = 0; m < MTW; ++m) {
+  for (int m = 0; m < WM; ++m) {
     const int row = m0 + 16 * m + (lane & 15);
     if (row >= g.M) continue;
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) {
-      const int nt = nt0 + n;
-      const f32x4 v = acc[n][m];
-      if constexpr (EPI == EP_BF16 || EPI == EP_GELU) {
-        float y[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = EPI == EP_GELU ? gelu_tanh(v[i]) : v[i];
-        *(u32x2*)((bf16*)g.out + (size_t)row * g.ldo + nt * 16 + 4 * gq) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
-      } else if constexpr (EPI == EP_ROPE) {
-        // tile order of a head: pairs (j, j + 64), j = 8 (nt % 8) + 2 gq + (i & 1)
-        const int hh = nt >> 3, j = 8 * (nt & 7) + 2 * gq;
-        const int c0 = hh * DH + j;
-        float y0 = v[0], y1 = v[1], y2 = v[2], y3 = v[3];
-        if (c0 < g.rot_cols) {
-          const float2 a = g.rope[(size_t)row * (DH / 2) + j];
-          const float2 b = g.rope[(size_t)row * (DH / 2) + j + 1];
-          y0 = v[0] * a.x - v[2] * a.y;
-          y2 = v[2] * a.x + v[0] * a.y;
-          y1 = v[1] * b.x - v[3] * b.y;
-          y3 = v[3] * b.x + v[1] * b.y;
-        }
-        bf16* o = (bf16*)g.out + (size_t)row * g.ldo;
-        *(unsigned*)(o + c0) = pack2(y0, y1);
-        *(unsigned*)(o + c0 + DH / 2) = pack2(y2, y3);
-      } else if constexpr (EPI == EP_GEGLU) {
-        // features 8 nt + 2 gq + {0, 1}: gate in v[0], v[1], up in v[2], v[3]
-        const int f = 8 * nt + 2 * gq;
-        *(unsigned*)((bf16*)g.out + (size_t)row * g.ldo + f) = pack2(gelu_tanh(v[0]) * v[2], gelu_tanh(v[1]) * v[3]);
-      } else {
-        float* o = (float*)g.out + (size_t)row * g.ldo + nt * 16 + 4 * gq;
-        f32x4 cur = EPI == EP_F32 ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)o;
-        if constexpr (EPI == EP_RESID) {
-          if (g.gate) {
-            const f32x4 gt = *(const f32x4*)(g.gate + nt * 16 + 4 * gq);
-            cur += gt * v;
-          } else {
-            cur += v;
-          }
-        } else if constexpr (EPI == EP_EULER) {
-          cur += g.dt * v;
-        } else {
-          cur = v;
-        }
-        *(f32x4*)o = cur;
-      }
+    for (int n = 0; n < WN; ++n) {
+      if (g.splits > 1)
+        *(f32x4*)(g.part + ((size_t)blockIdx.z * g.Mp + row) * g.N + (nt0 + n) * 16 + 4 * gq) = acc[n][m];
+      else
+        epi_store<EPI>(g, row, nt0 + n, gq, acc[n][m]);
     }
   }
+}
+
+// sums the split partials in split order, then the epilogue
+template <int EPI>
+__global__ void k_tsplit(GemmT g) {
+  const int groups = g.N / 4;
+  const size_t total = (size_t)g.M * groups;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int row = (int)(i / groups), c = (int)(i % groups) * 4;
+    f32x4 v = *(const f32x4*)(g.part + (size_t)row * g.N + c);
+    for (int z = 1; z < g.splits; ++z) v += *(const f32x4*)(g.part + ((size_t)z * g.Mp + row) * g.N + c);
+    epi_store<EPI>(g, row, c >> 4, (c & 15) >> 2, v);
+  }
+}
+
+struct TileCfg {
+  int wn, wm;
+};
+constexpr TileCfg TILES[] = {{4, 8}, {2, 8}, {2, 4}, {1, 4}};
+constexpr int N_TILES = sizeof(TILES) / sizeof(TILES[0]);
+
+void plan_gemm(GemmT& g, int n_cu) {
+  const int KT = g.K / 32;
+  double best = 1e300;
+  g.tile = -1;
+  g.splits = 1;
+  for (int i = 0; i < N_TILES; ++i) {
+    const int bn = 64 * TILES[i].wn, bm = 16 * TILES[i].wm;
+    if (g.N % bn || g.Mp % bm) continue;
+    const long long wgs = (long long)(g.N / bn) * (g.Mp / bm);
+    int sp = 1;
+    while (wgs * sp < n_cu && KT % (2 * sp) == 0 && KT / (2 * sp) >= 8) sp *= 2;
+    // time estimate: HBM bytes (weights once, split partials written and read), bytes pulled into
+    // the CUs (every row block re-reads its weight columns, every column block its rows), MFMA
+    // work, each scaled by how evenly the workgroups fill the chip
+    const double hbm = 2.0 * g.K * g.N + (sp > 1 ? 8.0 * sp * g.Mp * g.N : 0.0);
+    const double pulled = 2.0 * g.K * ((double)g.N * (g.Mp / bm) + (double)g.Mp * (g.N / bn));
+    const double flops = 2.0 * g.Mp * g.N * g.K;
+    const double units = (double)wgs * sp, rounds = std::ceil(units / n_cu);
+    const double t = std::max(std::max(hbm / 5e12, pulled / (n_cu * 100e9)), flops / 1.6e15) * rounds * n_cu / units;
+    if (t < best * 0.97) {
+      best = t;
+      g.tile = i;
+      g.splits = sp;
+    }
+  }
+}
+
+size_t gemm_part_elems(const GemmT& g) { return g.splits > 1 ? (size_t)g.splits * g.Mp * g.N : 0; }
+
+template <int WN, int WM, int EPI>
+hipError_t allow_lds() {
+  return hipFuncSetAttribute((const void*)k_tgemm<WN, WM, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             Tile<WN, WM>::LDS);
+}
+
+template <int EPI>
+hipError_t allow_lds_e() {
+  hipError_t e;
+  if ((e = allow_lds<4, 8, EPI>()) != hipSuccess) return e;
+  if ((e = allow_lds<2, 8, EPI>()) != hipSuccess) return e;
+  if ((e = allow_lds<2, 4, EPI>()) != hipSuccess) return e;
+  return allow_lds<1, 4, EPI>();
+}
+
+hipError_t prepare_gemm() {
+  hipError_t e;
+  if ((e = allow_lds_e<EP_BF16>()) != hipSuccess) return e;
+  if ((e = allow_lds_e<EP_QKV>()) != hipSuccess) return e;
+  if ((e = allow_lds_e<EP_GEGLU>()) != hipSuccess) return e;
+  if ((e = allow_lds_e<EP_GELU>()) != hipSuccess) return e;
+  if ((e = allow_lds_e<EP_RESID>()) != hipSuccess) return e;
+  if ((e = allow_lds_e<EP_EULER>()) != hipSuccess) return e;
+  return allow_lds_e<EP_F32>();
+}
+
+template <int WN, int WM, int EPI>
+hipError_t launch_tile(const GemmT& g, hipStream_t s) {
+  using T = Tile<WN, WM>;
+  hipLaunchKernelGGL((k_tgemm<WN, WM, EPI>), dim3(g.N / T::BN, g.Mp / T::BM, g.splits), dim3(256), T::LDS, s, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.splits == 1) return e;
+  const size_t total = (size_t)g.M * (g.N / 4);
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_tsplit<EPI>, dim3(blocks), dim3(256), 0, s, g);
+  return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_tgemm_e(const GemmT& g, hipStream_t s) {
-  // the larger block when it still gives the chip >= 256 workgroups
-  const long long big = (long long)(g.N / 128) * (g.Mp / 128);
-  if (g.Mp % 128 == 0 && g.N % 128 == 0 && big >= 256) {
-    hipLaunchKernelGGL((k_tgemm<2, 8, EPI>), dim3(g.N / 128, g.Mp / 128), dim3(256), 0, s, g);
-  } else {
-    hipLaunchKernelGGL((k_tgemm<1, 4, EPI>), dim3(g.N / 64, g.Mp / 64), dim3(256), 0, s, g);
+  switch (g.tile) {
+    case 0: return launch_tile<4, 8, EPI>(g, s);
+    case 1: return launch_tile<2, 8, EPI>(g, s);
+    case 2: return launch_tile<2, 4, EPI>(g, s);
+    case 3: return launch_tile<1, 4, EPI>(g, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
-  if (g.K % 32 || g.N % 64 || g.Mp % ROW_PAD || g.M > g.Mp) return hipErrorInvalidValue;
+  if (g.K % 32 || g.N % 64 || g.Mp % ROW_PAD || g.M > g.Mp || g.tile < 0 || g.tile >= N_TILES) return hipErrorInvalidValue;
+  if (g.splits < 1 || (g.K / 32) % g.splits || (g.splits > 1 && !g.part)) return hipErrorInvalidValue;
+  if ((size_t)g.Mp * g.K * 2 >= (1ull << 32) || (size_t)g.K * g.N * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   switch (epi) {
     case EP_BF16: return launch_tgemm_e<EP_BF16>(g, s);
-    case EP_ROPE: return launch_tgemm_e<EP_ROPE>(g, s);
+    case EP_QKV: return launch_tgemm_e<EP_QKV>(g, s);
     case EP_GEGLU: return launch_tgemm_e<EP_GEGLU>(g, s);
     case EP_GELU: return launch_tgemm_e<EP_GELU>(g, s);
     case EP_RESID: return launch_tgemm_e<EP_RESID>(g, s);
@@ -240,155 +433,193 @@ hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStrea
 }
 
 // ------------------------------------------------------------- attention
-// Workgroup (64 queries, head h, key split s); wave w owns queries 16 w.
-// Keys are the L prefix rows followed by the M chunk rows; the split takes a
-// contiguous range of 64-key blocks.  Per block:
-//   S^T = K . Q^T with 16x16x16 MFMAs: the K block sits in LDS as A fragments
-//     (lane: key lane % 16, dims 4 (lane / 16) + [0, 4) of a 16-dim step) and
-//     the wave's queries as B fragments in registers, so each lane ends with
-//     keys 4 (lane / 16) + [0, 4) of one query (lane % 16);
-//   online softmax per query (the four lanes of a query combine with two
-//     shuffles);
-//   O^T += V^T . P^T: V^T sits in LDS as A fragments (lane: dim lane % 16,
-//     keys 4 (lane / 16) + [0, 4)), and P^T is exactly the S^T register
-//     layout, so the probabilities feed the next MFMA without a shuffle.
-constexpr int KB = 64;  // keys per block
-
-__device__ inline const bf16* key_row(const AttnT& a, int L, int t, bool value) {
-  const int kvd = a.KVH * DH;
-  if (t < L) return (const bf16*)(value ? a.vp : a.kp) + (size_t)t * kvd;
-  return (const bf16*)a.qkv + (size_t)(t - L) * a.ldqkv + (a.H + (value ? a.KVH : 0)) * DH;
-}
+// Workgroup (128 queries, head h, key split); wave w owns queries 32 w as two
+// 16-query tiles.  Keys are the L prefix rows followed by the M chunk rows,
+// read from the joint key rows and the fragment-ordered values (see
+// vt_index); a split takes a contiguous range of 64-key blocks.  Per block:
+//   S^T = K . Q^T with 16x16x32 MFMAs: K fragments (lane: key lane % 16, dims
+//     8 (lane / 16) + [0, 8) of a 32-dim step) come from LDS, the wave's
+//     queries sit in registers as B fragments, so each lane ends with keys
+//     4 (lane / 16) + [0, 4) of each 16-key tile for one query;
+//   online softmax per query in base 2 (the four lanes of a query combine
+//     with two shuffles);
+//   O^T += V^T . P^T: two 16-key tiles of probabilities form the B fragment
+//     of one 32-key step as they lie in the registers (k index 8 g + e is key
+//     4 g + e for e < 4 and 16 + 4 g + e - 4 for e >= 4), and the value
+//     fragments are stored in that same key order.
+// K and V^T blocks (16 KiB each) stream into a two-stage LDS ring with
+// direct loads, the next block in flight while the current one is used.
+// Workgroups of one head run on one XCD so its keys and values stay in that
+// XCD's L2.
+constexpr int KB = 64;     // keys per block
+constexpr int AQ = 128;    // queries per workgroup
+constexpr int ASTAGE = 2;  // LDS stages
+constexpr int ASTAGE_BYTES = 32 * 1024;
 
 __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
-  __shared__ u32x2 kf[4 * 8 * 64];  // [key tile][dim step][lane] 4 bf16
-  __shared__ u32x2 vf[8 * 4 * 64];  // [dim tile][key tile][lane] 4 bf16
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int h = blockIdx.y, split = blockIdx.z;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nqb = (a.M + AQ - 1) / AQ;
+  const int per_head = nqb * a.splits;
+  const int bid = blockIdx.x;
+  int h, r;
+  if (a.H % 8 == 0) {
+    const int i = bid >> 3;
+    h = (bid & 7) + 8 * (i / per_head);
+    r = i % per_head;
+  } else {
+    h = bid / per_head;
+    r = bid % per_head;
+  }
+  const int qb = r / a.splits, split = r % a.splits;
   const int kvh = h / (a.H / a.KVH);
-  const int q0 = blockIdx.x * 64 + 16 * wave;
-  const int L = a.lens ? a.lens[0] : 0;
+  const int kvd = a.KVH * DH;
+  const int L = a.lens ? __builtin_amdgcn_readfirstlane(a.lens[0]) : 0;
   const int T = L + a.M;
   const int nblk = (T + KB - 1) / KB;
   const int per = (nblk + a.splits - 1) / a.splits;
   const int b0 = split * per, b1 = min(nblk, b0 + per);
-  const int gq = lane >> 4, qr = lane & 15;
-  // this wave's queries as B fragments of Q^T: dims 16 ds + 4 gq + [0, 4) of query q0 + qr
-  s16x4 qf[8];
-  {
-    const int q = min(q0 + qr, a.M - 1);
-    const bf16* qp = (const bf16*)a.qkv + (size_t)q * a.ldqkv + h * DH;
+  const int g4 = lane >> 4, qr = lane & 15;
+  const int q0 = qb * AQ + 32 * wave;
+  // queries as B fragments of Q^T: dims 32 ds + 8 g4 + [0, 8) of query q0 + 16 qt + qr
+  bf16x8 qf[2][4];
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) qf[ds] = __builtin_bit_cast(s16x4, *(const u32x2*)(qp + 16 * ds + 4 * gq));
+  for (int qt = 0; qt < 2; ++qt) {
+    const int q = min(q0 + 16 * qt + qr, a.M - 1);
+    const bf16* qp = (const bf16*)a.q + (size_t)q * a.ldq + h * DH + 8 * g4;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) qf[qt][ds] = *(const bf16x8*)(qp + 32 * ds);
   }
-  f32x4 oacc[8];
+  const unsigned lds0 = (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)smem);
+  const u32x4 rk = rsrc_words(a.kj, (unsigned)((size_t)a.R * kvd * 2));
+  const u32x4 rv = rsrc_words(a.vt, (unsigned)((size_t)a.KVH * a.R * DH * 2));
+  // wave w moves K fragments (key tile w, dim steps 0..3) and value fragments 4 w .. 4 w + 3
+  unsigned vok[4];
 #pragma unroll
-  for (int d = 0; d < 8; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int ds = 0; ds < 4; ++ds) vok[ds] = (unsigned)(((16 * wave + qr) * kvd + kvh * DH + 32 * ds + 8 * g4) * 2);
+  const unsigned vov = (unsigned)lane * 16u;
+  const int nj = a.R / 32;
+  auto issue = [&](int b) {
+    const unsigned st = lds0 + (unsigned)((b % ASTAGE) * ASTAGE_BYTES);
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      dma_frag(st + (unsigned)((4 * wave + ds) * 1024), vok[ds], rk, (unsigned)(b * KB * kvd * 2));
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      dma_frag(st + 16384u + (unsigned)((4 * wave + f) * 1024), vov, rv,
+               (unsigned)((((size_t)kvh * nj + 2 * b) * 8 + 4 * wave + f) * 1024));
+  };
+  const float sl2 = a.scale * 1.4426950408889634f;  // scores in base 2
+  f32x4 oacc[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) oacc[qt][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  if (b0 < b1) issue(b0);
   for (int b = b0; b < b1; ++b) {
-    const int k0 = b * KB;
-    // stage K (A fragments) and V^T (A fragments): thread t moves 8 dims (16 bytes) of key t / 16 ... for
-    // four passes of 16 keys
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int kl = p * 16 + (t >> 4);  // key within the block
-      const int dc = (t & 15) * 8;       // first of 8 dims
-      const int key = k0 + kl;
-      u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
-      if (key < T) {
-        kv = *(const u32x4*)(key_row(a, L, key, false) + kvh * DH + dc);
-        vv = *(const u32x4*)(key_row(a, L, key, true) + kvh * DH + dc);
-      }
-      // K fragment: key tile kl/16, dim step dc/16, lane (kl % 16) + 16 * ((dc % 16) / 4)
-      const int kt = kl >> 4, ds = dc >> 4, lk = (kl & 15) + 16 * ((dc & 15) >> 2);
-      kf[(kt * 8 + ds) * 64 + lk] = u32x2{kv[0], kv[1]};
-      kf[(kt * 8 + ds) * 64 + lk + 16] = u32x2{kv[2], kv[3]};
-      // V^T fragment: dim tile d/16, key tile kl/16, lane (d % 16) + 16 * ((kl % 16) / 4), element kl % 4
-      unsigned short* vs = (unsigned short*)vf;
-      const unsigned vw[4] = {vv[0], vv[1], vv[2], vv[3]};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = dc + e;
-        const int li = (d & 15) + 16 * ((kl & 15) >> 2);
-        vs[(((d >> 4) * 4 + kt) * 64 + li) * 4 + (kl & 3)] = (unsigned short)(vw[e >> 1] >> (16 * (e & 1)));
-      }
-    }
-    __syncthreads();
-    // scores
-    f32x4 st[4];
+    wait_vm<0>();
+    wg_barrier();  // block b is in LDS for every wave; every wave is done with block b - 1
+    if (b + 1 < b1) issue(b + 1);
+    const unsigned char* st = smem + (b % ASTAGE) * ASTAGE_BYTES;
+    f32x4 sc[2][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds)
-        st[kt] = mma16(__builtin_bit_cast(s16x4, kf[(kt * 8 + ds) * 64 + lane]), qf[ds], st[kt]);
+      for (int ds = 0; ds < 4; ++ds) {
+        const bf16x8 kf = *(const bf16x8*)(st + (kt * 4 + ds) * 1024 + lane * 16);
+        sc[0][kt] = mma32(kf, qf[0][ds], sc[0][kt]);
+        sc[1][kt] = mma32(kf, qf[1][ds], sc[1][kt]);
+      }
     }
-    float mx = -INFINITY;
+    const int k0 = b * KB;
+    bf16x8 pf[2][2];
+    float corr[2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * kt + 4 * gq + i;
-        const float sv = key < T ? st[kt][i] * a.scale : -INFINITY;
-        st[kt][i] = sv;
-        mx = fmaxf(mx, sv);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float corr = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
-    float ls = 0.f;
-    s16x4 pf[4];
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * kt + 4 * g4 + i;
+          const float sv = key < T ? sc[qt][kt][i] * sl2 : -INFINITY;
+          sc[qt][kt][i] = sv;
+          mx = fmaxf(mx, sv);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[qt], mx);
+      corr[qt] = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - m_new);
+      float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = st[kt][i] == -INFINITY ? 0.f : expf(st[kt][i] - m_new);
-        ls += p;
-        pf[kt][i] = (short)bits((bf16)p);
-      }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * corr + ls;
-    m_run = m_new;
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = sc[qt][kt][i] == -INFINITY ? 0.f : exp2f(sc[qt][kt][i] - m_new);
+          ls += p;
+          pf[qt][kt >> 1][4 * (kt & 1) + i] = (bf16)p;
+        }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      l_run[qt] = l_run[qt] * corr[qt] + ls;
+      m_run[qt] = m_new;
+    }
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      f32x4 acc = oacc[d] * corr;
+      f32x4 a0 = oacc[0][d] * corr[0], a1 = oacc[1][d] * corr[1];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) acc = mma16(__builtin_bit_cast(s16x4, vf[(d * 4 + kt) * 64 + lane]), pf[kt], acc);
-      oacc[d] = acc;
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 vf = *(const bf16x8*)(st + 16384 + (j * 8 + d) * 1024 + lane * 16);
+        a0 = mma32(vf, pf[0][j], a0);
+        a1 = mma32(vf, pf[1][j], a1);
+      }
+      oacc[0][d] = a0;
+      oacc[1][d] = a1;
     }
   }
-  // lane holds dims 16 d + 4 gq + [0, 4) of query q0 + qr
-  const int q = q0 + qr;
-  if (q >= a.M) return;
-  if (a.splits == 1) {
-    const float inv = 1.0f / l_run;
-    bf16* op = (bf16*)a.o + (size_t)q * (a.H * DH) + h * DH;
+  // lane holds dims 16 d + 4 g4 + [0, 4) of query q0 + 16 qt + qr
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
-      *(u32x2*)(op + 16 * d + 4 * gq) =
-          u32x2{pack2(oacc[d][0] * inv, oacc[d][1] * inv), pack2(oacc[d][2] * inv, oacc[d][3] * inv)};
-  } else {
-    float* po = a.po + ((size_t)split * a.M + q) * (a.H * DH) + h * DH;
+  for (int qt = 0; qt < 2; ++qt) {
+    const int q = q0 + 16 * qt + qr;
+    if (q >= a.M) continue;
+    if (a.splits == 1) {
+      const float inv = 1.0f / l_run[qt];
+      bf16* op = (bf16*)a.o + (size_t)q * (a.H * DH) + h * DH;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) *(f32x4*)(po + 16 * d + 4 * gq) = oacc[d];
-    if (gq == 0) {
-      float* ml = a.pml + (((size_t)split * a.M + q) * a.H + h) * 2;
-      ml[0] = m_run;
-      ml[1] = l_run;
+      for (int d = 0; d < 8; ++d)
+        *(u32x2*)(op + 16 * d + 4 * g4) = u32x2{pack2(oacc[qt][d][0] * inv, oacc[qt][d][1] * inv),
+                                                pack2(oacc[qt][d][2] * inv, oacc[qt][d][3] * inv)};
+    } else {
+      float* po = a.po + ((size_t)split * a.M + q) * (a.H * DH) + h * DH;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) *(f32x4*)(po + 16 * d + 4 * g4) = oacc[qt][d];
+      if (g4 == 0) {
+        float* ml = a.pml + (((size_t)split * a.M + q) * a.H + h) * 2;
+        ml[0] = m_run[qt];
+        ml[1] = l_run[qt];
+      }
     }
   }
+}
+
+hipError_t prepare_attention() {
+  return hipFuncSetAttribute((const void*)k_tattn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             ASTAGE * ASTAGE_BYTES);
 }
 
 hipError_t launch_tattn(const AttnT& a, hipStream_t s) {
-  if (a.M < 1 || a.H % a.KVH || a.splits < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_tattn, dim3((a.M + 63) / 64, a.H, a.splits), dim3(256), 0, s, a);
+  if (a.M < 1 || a.H % a.KVH || a.splits < 1 || a.R % KB || a.R < a.M) return hipErrorInvalidValue;
+  if ((size_t)a.R * a.KVH * DH * 2 >= (1ull << 32)) return hipErrorInvalidValue;
+  const int blocks = ((a.M + AQ - 1) / AQ) * a.splits * a.H;
+  hipLaunchKernelGGL(k_tattn, dim3(blocks), dim3(256), ASTAGE * ASTAGE_BYTES, s, a);
   return hipGetLastError();
 }
 
-// out[q][h*DH + d] = sum_s e^(m_s - m) O_s / sum_s e^(m_s - m) l_s, splits in order
+// out[q][h*DH + d] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, splits in order
 __global__ void k_tcombine(AttnT a) {
   const size_t total = (size_t)a.M * a.H * DH;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
@@ -402,7 +633,7 @@ __global__ void k_tcombine(AttnT a) {
     for (int s = 0; s < a.splits; ++s) {
       const float ms = a.pml[(((size_t)s * a.M + q) * a.H + h) * 2];
       if (ms == -INFINITY) continue;
-      const float w = expf(ms - m);
+      const float w = exp2f(ms - m);
       num += w * a.po[((size_t)s * a.M + q) * (a.H * DH) + h * DH + d];
       den += w * a.pml[(((size_t)s * a.M + q) * a.H + h) * 2 + 1];
     }
@@ -414,6 +645,28 @@ hipError_t launch_tcombine(const AttnT& a, hipStream_t s) {
   const size_t total = (size_t)a.M * a.H * DH;
   const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
   hipLaunchKernelGGL(k_tcombine, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Prefix values into the fragment order: keys t < L from v [NL][L][KVH*DH],
+// zeros for L <= t < R.
+__global__ void k_vt_load(const bf16* __restrict__ v, bf16* __restrict__ vt, int NL, int L, int R, int KVH) {
+  const size_t plane = (size_t)R * DH;  // one kv head of one layer
+  const size_t total = (size_t)NL * KVH * plane;
+  const int kvd = KVH * DH;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t lp = i / plane;
+    const int l = (int)(lp / KVH), kvh = (int)(lp % KVH);
+    int t, d;
+    vt_key_dim((int)(i % plane), t, d);
+    vt[i] = t < L ? v[((size_t)l * L + t) * kvd + kvh * DH + d] : (bf16)0.0f;
+  }
+}
+
+hipError_t launch_vt_load(const void* v, void* vt, int NL, int L, int R, int KVH, hipStream_t s) {
+  const size_t total = (size_t)NL * KVH * R * DH;
+  const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
+  hipLaunchKernelGGL(k_vt_load, dim3(blocks), dim3(256), 0, s, (const bf16*)v, (bf16*)vt, NL, L, R, KVH);
   return hipGetLastError();
 }
 

@@ -89,6 +89,25 @@ class Expert:
         """Every kernel launch of one decision, in replay order."""
         return [B.phx_expert_node_info(self.h, i) for i in range(self.kernels_per_decision())]
 
+    def time_nodes(self, idx: list, reps: int = 20) -> list:
+        """Average duration (ms) of each launch in idx, relaunched on its own
+        `reps` times, each bracketed by HIP events on the handle's stream."""
+        torch = self.torch
+        stream = torch.cuda.current_stream(self.device)
+        for i in idx:  # warm
+            B.phx_expert_launch_node(self.h, i, self.stream)
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+              for _ in idx]
+        torch.cuda.synchronize(self.device)
+        for r in range(reps):
+            for j, i in enumerate(idx):
+                a, b = ev[j][r]
+                a.record(stream)
+                B.phx_expert_launch_node(self.h, i, self.stream)
+                b.record(stream)
+        torch.cuda.synchronize(self.device)
+        return [float(sum(a.elapsed_time(b) for a, b in e) / reps) for e in ev]
+
     def time_dominant_kernel(self, reps: int = 50) -> dict:
         """Average duration of one launch of the kernel that streams the most
         algorithmic bytes per decision.  Each launch (the first Euler step's
