@@ -545,12 +545,12 @@ int build_tok_nodes(phx_expert* h) {
     g.a = a; g.w = (const char*)h->wt + w_off * 2; g.out = out; g.gate = gate; g.rope = h->rope;
     g.rot_cols = dit ? 0 : (H + KVH) * tok::DH; g.dt = c.dt; g.M = M; g.Mp = Mp; g.K = K; g.N = N; g.ldo = ldo;
     tok::plan_gemm(g, h->n_cu);
+    std::snprintf(nd.name, sizeof(nd.name), "%s %s/%d", name, tok::tile_name(g.tile), g.splits);
     const int out_cols = epi == tok::EP_GEGLU ? N / 2 : N;
     const int out_esz = (epi == tok::EP_RESID || epi == tok::EP_EULER || epi == tok::EP_F32) ? 4 : 2;
     const uint64_t rmw = (epi == tok::EP_RESID || epi == tok::EP_EULER) ? 2 : 1;
     nd.bytes = (uint64_t)K * N * 2 + (uint64_t)M * K * 2 + rmw * (uint64_t)M * out_cols * out_esz +
                (gate ? (uint64_t)N * 4 : 0);
-    name_of(nd, name);
     h->tnodes.push_back(nd);
   };
   auto norm = [&](int k, int l, int kind, const float* scale, const float* shift, const char* name) {

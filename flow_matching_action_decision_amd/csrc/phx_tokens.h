@@ -53,6 +53,8 @@ struct GemmT {
 
 // Chooses the tile shape and k splits of g for a chip of n_cu compute units.
 void plan_gemm(GemmT& g, int n_cu);
+// Columns x rows of a planned tile shape, for diagnostics.
+const char* tile_name(int tile);
 // f32 elements of split partials g needs (0 without splits).
 size_t gemm_part_elems(const GemmT& g);
 

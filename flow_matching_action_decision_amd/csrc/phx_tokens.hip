@@ -56,20 +56,32 @@ __device__ inline f32x4 mma16(const s16x4& a, const s16x4& b, const f32x4& c) {
 // Both operands reach LDS straight from memory (buffer loads with the LDS
 // bit, no registers in between), each 1 KiB load already in MFMA fragment
 // order: a weight fragment is one contiguous tile of the arena; an activation
-// fragment is 16 rows x 64 bytes.  The k-steps rotate through an NSTAGE-deep
-// ring; every wave waits for its own loads with an explicit vmcnt and a
-// barrier publishes the stage, so NSTAGE - 1 k-steps are in flight while one
-// is multiplied.  With split > 1 workgroup z multiplies k-steps [z KT/split,
-// (z+1) KT/split) and stores its raw sums for an ordered reduction.
+// fragment is 16 rows x 64 bytes.  A stage holds KS k-steps; stages rotate
+// through an NSTAGE-deep ring; every wave waits for its own loads with an
+// explicit vmcnt and a barrier publishes the stage, so NSTAGE - 1 stages are
+// in flight while one is multiplied.  With split > 1 workgroup z multiplies
+// k-steps [z KT/split, (z+1) KT/split) and stores its raw sums for an ordered
+// reduction.
 constexpr int NSTAGE = 4;
+constexpr int KS = 1;
+static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the stage waits cover up to two stages in flight");
 
 template <int WN, int WM>
 struct Tile {
   static constexpr int BN = 64 * WN, BM = 16 * WM;
   static constexpr int FR = WM + 4 * WN;  // 1 KiB fragments per k-step
   static constexpr int PW = WM / 4 + WN;  // loads per wave per k-step
-  static constexpr int LDS = NSTAGE * FR * 1024;
+  static constexpr int STAGE = KS * FR * 1024;
+  static constexpr int LDS = NSTAGE * STAGE;
 };
+
+// workgroup bid of gx x gy x nz -> output tile (bx, by) and split z
+__device__ inline void tile_of(int bid, int gx, int gy, int nz, int& bx, int& by, int& z) {
+  z = bid / (gx * gy);
+  const int t = bid - z * gx * gy;
+  bx = t % gx;
+  by = t / gx;
+}
 
 __device__ inline u32x4 rsrc_words(const void* p, unsigned bytes) {
   const unsigned long long b = (unsigned long long)p;
@@ -180,12 +192,14 @@ __global__ __launch_bounds__(256) void k_tgemm(GemmT g) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int nt0 = (blockIdx.x * 4 + wave) * WN;
-  const int m0 = blockIdx.y * T::BM;
+  int bx, by, bz;
+  tile_of(blockIdx.x, g.N / T::BN, g.Mp / T::BM, g.splits, bx, by, bz);
+  const int nt0 = (bx * 4 + wave) * WN;
+  const int m0 = by * T::BM;
   const int KT = g.K / 32;
   const int per = KT / g.splits;
-  const int kb = blockIdx.z * per;
-  const int nk = per;
+  const int kb = bz * per;
+  const int ns = per / KS;  // stages
   const unsigned lds0 = (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)smem);
   const u32x4 ra = rsrc_words(g.a, (unsigned)((size_t)g.Mp * g.K * 2));
   const u32x4 rw = rsrc_words(g.w, (unsigned)((size_t)g.K * g.N * 2));
@@ -198,15 +212,19 @@ __global__ __launch_bounds__(256) void k_tgemm(GemmT g) {
   }
   const unsigned vow = (unsigned)lane * 16u;
   auto issue = [&](int s) {
-    const int kt = kb + s;
-    const unsigned st = lds0 + (unsigned)((s % NSTAGE) * T::FR * 1024);
+    const unsigned st = lds0 + (unsigned)((s % NSTAGE) * T::STAGE);
 #pragma unroll
-    for (int i = 0; i < WM / 4; ++i)
-      dma_frag(st + (unsigned)((wave * (WM / 4) + i) * 1024), voa[i], ra, (unsigned)(kt * 64));
+    for (int kk = 0; kk < KS; ++kk) {
+      const int kt = kb + s * KS + kk;
+      const unsigned sk = st + (unsigned)(kk * T::FR * 1024);
 #pragma unroll
-    for (int n = 0; n < WN; ++n)
-      dma_frag(st + (unsigned)((WM + wave * WN + n) * 1024), vow, rw,
-               (unsigned)(((size_t)(nt0 + n) * KT + kt) * 1024));
+      for (int i = 0; i < WM / 4; ++i)
+        dma_frag(sk + (unsigned)((wave * (WM / 4) + i) * 1024), voa[i], ra, (unsigned)(kt * 64));
+#pragma unroll
+      for (int n = 0; n < WN; ++n)
+        dma_frag(sk + (unsigned)((WM + wave * WN + n) * 1024), vow, rw,
+                 (unsigned)(((size_t)(nt0 + n) * KT + kt) * 1024));
+    }
   };
   f32x4 acc[WN][WM];
 #pragma unroll
@@ -215,23 +233,27 @@ __global__ __launch_bounds__(256) void k_tgemm(GemmT g) {
     for (int m = 0; m < WM; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < nk) issue(s);
-  for (int s = 0; s < nk; ++s) {
-    const int ahead = min(NSTAGE - 2, nk - 1 - s);  // later k-steps already issued
-    if (ahead >= 2) wait_vm<2 * T::PW>();
-    else if (ahead == 1) wait_vm<T::PW>();
+    if (s < ns) issue(s);
+  for (int s = 0; s < ns; ++s) {
+    // stage s must be in; the later stages already issued may still be in flight
+    const int ahead = min(NSTAGE - 2, ns - 1 - s);
+    if (ahead >= 2) wait_vm<2 * KS * T::PW>();
+    else if (ahead == 1) wait_vm<KS * T::PW>();
     else wait_vm<0>();
     wg_barrier();  // stage s is in LDS for every wave; every wave is done with stage s - 1
-    if (s + NSTAGE - 1 < nk) issue(s + NSTAGE - 1);
-    const unsigned char* st = smem + (s % NSTAGE) * T::FR * 1024;
-    bf16x8 wf[WN];
+    if (s + NSTAGE - 1 < ns) issue(s + NSTAGE - 1);
 #pragma unroll
-    for (int n = 0; n < WN; ++n) wf[n] = *(const bf16x8*)(st + (WM + wave * WN + n) * 1024 + lane * 16);
+    for (int kk = 0; kk < KS; ++kk) {
+      const unsigned char* st = smem + (s % NSTAGE) * T::STAGE + kk * T::FR * 1024;
+      bf16x8 wf[WN];
 #pragma unroll
-    for (int m = 0; m < WM; ++m) {
-      const bf16x8 af = *(const bf16x8*)(st + m * 1024 + lane * 16);
+      for (int n = 0; n < WN; ++n) wf[n] = *(const bf16x8*)(st + (WM + wave * WN + n) * 1024 + lane * 16);
 #pragma unroll
-      for (int n = 0; n < WN; ++n) acc[n][m] = mma32(wf[n], af, acc[n][m]);
+      for (int m = 0; m < WM; ++m) {
+        const bf16x8 af = *(const bf16x8*)(st + m * 1024 + lane * 16);
+#pragma unroll
+        for (int n = 0; n < WN; ++n) acc[n][m] = mma32(wf[n], af, acc[n][m]);
+      }
     }
   }
   // lane holds columns 4 (lane / 16) + [0, 4) of each n-tile (tile order) for
@@ -244,7 +266,7 @@ __global__ __launch_bounds__(256) void k_tgemm(GemmT g) {
 #pragma unroll
     for (int n = 0; n < WN; ++n) {
       if (g.splits > 1)
-        *(f32x4*)(g.part + ((size_t)blockIdx.z * g.Mp + row) * g.N + (nt0 + n) * 16 + 4 * gq) = acc[n][m];
+        *(f32x4*)(g.part + ((size_t)bz * g.Mp + row) * g.N + (nt0 + n) * 16 + 4 * gq) = acc[n][m];
       else
         epi_store<EPI>(g, row, nt0 + n, gq, acc[n][m]);
     }
@@ -280,7 +302,8 @@ void plan_gemm(GemmT& g, int n_cu) {
     if (g.N % bn || g.Mp % bm) continue;
     const long long wgs = (long long)(g.N / bn) * (g.Mp / bm);
     int sp = 1;
-    while (wgs * sp < n_cu && KT % (2 * sp) == 0 && KT / (2 * sp) >= 8) sp *= 2;
+    if (KT % KS) return;
+    while (wgs * sp < n_cu && KT % (2 * sp * KS) == 0 && KT / (2 * sp) >= 8) sp *= 2;
     // time estimate: HBM bytes (weights once, split partials written and read), bytes pulled into
     // the CUs (every row block re-reads its weight columns, every column block its rows), MFMA
     // work, each scaled by how evenly the workgroups fill the chip
@@ -295,6 +318,11 @@ void plan_gemm(GemmT& g, int n_cu) {
       g.splits = sp;
     }
   }
+}
+
+const char* tile_name(int tile) {
+  static const char* names[N_TILES] = {"256x128", "128x128", "128x64", "64x64"};
+  return tile >= 0 && tile < N_TILES ? names[tile] : "?";
 }
 
 size_t gemm_part_elems(const GemmT& g) { return g.splits > 1 ? (size_t)g.splits * g.Mp * g.N : 0; }
@@ -328,7 +356,8 @@ hipError_t prepare_gemm() {
 template <int WN, int WM, int EPI>
 hipError_t launch_tile(const GemmT& g, hipStream_t s) {
   using T = Tile<WN, WM>;
-  hipLaunchKernelGGL((k_tgemm<WN, WM, EPI>), dim3(g.N / T::BN, g.Mp / T::BM, g.splits), dim3(256), T::LDS, s, g);
+  hipLaunchKernelGGL((k_tgemm<WN, WM, EPI>), dim3((g.N / T::BN) * (g.Mp / T::BM) * g.splits), dim3(256), T::LDS, s,
+                     g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.splits == 1) return e;
   const size_t total = (size_t)g.M * (g.N / 4);
@@ -350,7 +379,7 @@ hipError_t launch_tgemm_e(const GemmT& g, hipStream_t s) {
 
 hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
   if (g.K % 32 || g.N % 64 || g.Mp % ROW_PAD || g.M > g.Mp || g.tile < 0 || g.tile >= N_TILES) return hipErrorInvalidValue;
-  if (g.splits < 1 || (g.K / 32) % g.splits || (g.splits > 1 && !g.part)) return hipErrorInvalidValue;
+  if (g.splits < 1 || (g.K / 32) % (g.splits * KS) || (g.splits > 1 && !g.part)) return hipErrorInvalidValue;
   if ((size_t)g.Mp * g.K * 2 >= (1ull << 32) || (size_t)g.K * g.N * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   switch (epi) {
     case EP_BF16: return launch_tgemm_e<EP_BF16>(g, s);
