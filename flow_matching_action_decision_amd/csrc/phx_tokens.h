@@ -47,6 +47,7 @@ struct GemmT {
   int M, Mp, K, N;     // real rows, padded rows, reduction length, output columns (tile order)
   int ldo;             // output row stride in elements
   int tile;            // workgroup tile shape (set by plan_gemm)
+  int kern;            // 0: LDS-ring kernel, 1: register-fed kernel (set by plan_gemm)
   int splits;          // k splits (set by plan_gemm); > 1 needs part
   float* part;         // split partials [splits][Mp][N] f32
 };

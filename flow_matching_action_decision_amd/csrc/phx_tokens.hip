@@ -51,31 +51,40 @@ __device__ inline f32x4 mma16(const s16x4& a, const s16x4& b, const f32x4& c) {
 // Workgroup of 4 waves covering output columns [BN bx, +BN) (BN = 64 WN) and
 // rows [BM by, +BM) (BM = 16 WM); wave w owns n-tiles WN (4 bx + w) + [0, WN)
 // and all WM m-tiles, so per 32-deep k-step it runs WN x WM MFMAs on WN weight
-// fragments and the WM activation fragments the four waves share.
+// fragments and the WM activation fragments the four waves share.  Two ways
+// to feed it, chosen per GEMM by the planner:
 //
-// Both operands reach LDS straight from memory (buffer loads with the LDS
-// bit, no registers in between), each 1 KiB load already in MFMA fragment
-// order: a weight fragment is one contiguous tile of the arena; an activation
-// fragment is 16 rows x 64 bytes.  A stage holds KS k-steps; stages rotate
-// through an NSTAGE-deep ring; every wave waits for its own loads with an
-// explicit vmcnt and a barrier publishes the stage, so NSTAGE - 1 stages are
-// in flight while one is multiplied.  With split > 1 workgroup z multiplies
-// k-steps [z KT/split, (z+1) KT/split) and stores its raw sums for an ordered
-// reduction.
-constexpr int NSTAGE = 4;
-constexpr int KS = 1;
+// k_tgemm_ring (few rows: the weights stream from HBM once and latency rules):
+// both operands reach LDS straight from memory (buffer loads with the LDS bit,
+// no registers in between), each 1 KiB load already in MFMA fragment order (a
+// weight tile, or 16 activation rows x 64 bytes), through an NSTAGE-deep ring;
+// every wave waits for its own loads with an explicit vmcnt and a barrier
+// publishes the stage, so NSTAGE - 1 k-steps are in flight.
+//
+// k_tgemm_reg (many rows: MFMA-bound, and LDS bandwidth is the limit): a
+// wave's weight fragments are its own, so they go from memory straight into
+// registers WPD k-steps ahead; only the shared activation rows pass through a
+// double-buffered LDS block, fetched two k-steps ahead; two workgroups per CU.
+// All its loads are ordinary loads, so the compiler's own waits track them.
+//
+// With split > 1 workgroup z multiplies k-steps [z KT/split, (z+1) KT/split)
+// and stores its raw sums for an ordered reduction.
+constexpr int NSTAGE = 4;  // ring stages (k_tgemm_ring)
+constexpr int WPD = 2;     // weight prefetch distance in k-steps (k_tgemm_reg)
+constexpr int UNR = 4;     // k_tgemm_reg main-loop unroll: its register rings rotate with it
 static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the stage waits cover up to two stages in flight");
+static_assert(WPD < UNR && UNR % 2 == 0, "the weight ring holds UNR k-steps, the activation ring 2");
 
 template <int WN, int WM>
 struct Tile {
   static constexpr int BN = 64 * WN, BM = 16 * WM;
-  static constexpr int FR = WM + 4 * WN;  // 1 KiB fragments per k-step
-  static constexpr int PW = WM / 4 + WN;  // loads per wave per k-step
-  static constexpr int STAGE = KS * FR * 1024;
+  static constexpr int FR = WM + 4 * WN;  // ring: 1 KiB fragments per k-step
+  static constexpr int PW = WM / 4 + WN;  // ring: loads per wave per k-step
+  static constexpr int STAGE = FR * 1024;
   static constexpr int LDS = NSTAGE * STAGE;
+  static constexpr int AP = BM / 64;      // reg: 16-byte activation pieces per thread per k-step
 };
 
-// workgroup bid of gx x gy x nz -> output tile (bx, by) and split z
 __device__ inline void tile_of(int bid, int gx, int gy, int nz, int& bx, int& by, int& z) {
   z = bid / (gx * gy);
   const int t = bid - z * gx * gy;
@@ -187,8 +196,9 @@ __device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const 
 }
 
 template <int WN, int WM, int EPI>
-__global__ __launch_bounds__(256) void k_tgemm(GemmT g) {
+__global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   using T = Tile<WN, WM>;
+  constexpr int KS = 1;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -273,6 +283,101 @@ __global__ __launch_bounds__(256) void k_tgemm(GemmT g) {
   }
 }
 
+template <int WN, int WM, int EPI>
+__global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
+  using T = Tile<WN, WM>;
+  __shared__ u32x4 as[2][WM * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  int bx, by, bz;
+  tile_of(blockIdx.x, g.N / T::BN, g.Mp / T::BM, g.splits, bx, by, bz);
+  const int nt0 = (bx * 4 + wave) * WN;
+  const int m0 = by * T::BM;
+  const int KT = g.K / 32;
+  const int per = KT / g.splits;
+  const int kb = bz * per;
+  // activation pieces of this thread: rows p*64 + tid/4, k chunk tid%4
+  const u32x4* arow[T::AP];
+  int aslot[T::AP];
+#pragma unroll
+  for (int p = 0; p < T::AP; ++p) {
+    const int r = p * 64 + (tid >> 2);
+    arow[p] = (const u32x4*)((const bf16*)g.a + (size_t)(m0 + r) * g.K + 8 * (tid & 3));
+    aslot[p] = (r >> 4) * 64 + (r & 15) + 16 * (tid & 3);
+  }
+  const u32x4* wbase[WN];
+#pragma unroll
+  for (int n = 0; n < WN; ++n) wbase[n] = (const u32x4*)g.w + ((size_t)(nt0 + n) * KT + kb) * 64 + lane;
+  f32x4 acc[WN][WM];
+#pragma unroll
+  for (int n = 0; n < WN; ++n)
+#pragma unroll
+    for (int m = 0; m < WM; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 wr[UNR][WN];    // weight fragments, k-step s in slot s % UNR
+  u32x4 ar[2][T::AP];   // activation pieces, k-step s in slot s % 2
+  // prologue: activations of k-steps 0 and 1, weights of k-steps 0 .. WPD-1
+#pragma unroll
+  for (int p = 0; p < T::AP; ++p) ar[0][p] = arow[p][(kb + 0) * 4];
+  if (per > 1) {
+#pragma unroll
+    for (int p = 0; p < T::AP; ++p) ar[1][p] = arow[p][(kb + 1) * 4];
+  }
+#pragma unroll
+  for (int j = 0; j < WPD; ++j)
+    if (j < per) {
+#pragma unroll
+      for (int n = 0; n < WN; ++n) wr[j][n] = wbase[n][(size_t)j * 64];
+    }
+#pragma unroll
+  for (int p = 0; p < T::AP; ++p) as[0][aslot[p]] = ar[0][p];
+  __syncthreads();
+  for (int s0 = 0; s0 < per; s0 += UNR) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int s = s0 + j;
+      if (s < per) {
+        // fetch ahead: activations of s + 2 (into the slot k-step s has left), weights of s + WPD
+        if (s + 2 < per) {
+#pragma unroll
+          for (int p = 0; p < T::AP; ++p) ar[j & 1][p] = arow[p][(kb + s + 2) * 4];
+        }
+        if (s + WPD < per) {
+#pragma unroll
+          for (int n = 0; n < WN; ++n) wr[(j + WPD) % UNR][n] = wbase[n][(size_t)(s + WPD) * 64];
+        }
+        // stage the activations of s + 1 for the next k-step
+        if (s + 1 < per) {
+#pragma unroll
+          for (int p = 0; p < T::AP; ++p) as[(j + 1) & 1][aslot[p]] = ar[(j + 1) & 1][p];
+        }
+        const u32x4* st = as[j & 1];
+#pragma unroll
+        for (int m = 0; m < WM; ++m) {
+          const bf16x8 af = __builtin_bit_cast(bf16x8, st[m * 64 + lane]);
+#pragma unroll
+          for (int n = 0; n < WN; ++n) acc[n][m] = mma32(__builtin_bit_cast(bf16x8, wr[j][n]), af, acc[n][m]);
+        }
+        __syncthreads();
+      }
+    }
+  }
+  // lane holds columns 4 (lane / 16) + [0, 4) of each n-tile (tile order) for
+  // row lane % 16 of each m-tile
+  const int gq = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < WM; ++m) {
+    const int row = m0 + 16 * m + (lane & 15);
+    if (row >= g.M) continue;
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+      if (g.splits > 1)
+        *(f32x4*)(g.part + ((size_t)bz * g.Mp + row) * g.N + (nt0 + n) * 16 + 4 * gq) = acc[n][m];
+      else
+        epi_store<EPI>(g, row, nt0 + n, gq, acc[n][m]);
+    }
+  }
+}
+
 // sums the split partials in split order, then the epilogue
 template <int EPI>
 __global__ void k_tsplit(GemmT g) {
@@ -294,6 +399,9 @@ constexpr int N_TILES = sizeof(TILES) / sizeof(TILES[0]);
 
 void plan_gemm(GemmT& g, int n_cu) {
   const int KT = g.K / 32;
+  // few rows: the weights stream once from HBM and the ring's deeper look-ahead wins; many rows: the
+  // register-fed kernel halves the LDS traffic per MFMA
+  g.kern = g.Mp >= 1024 ? 1 : 0;
   double best = 1e300;
   g.tile = -1;
   g.splits = 1;
@@ -302,8 +410,7 @@ void plan_gemm(GemmT& g, int n_cu) {
     if (g.N % bn || g.Mp % bm) continue;
     const long long wgs = (long long)(g.N / bn) * (g.Mp / bm);
     int sp = 1;
-    if (KT % KS) return;
-    while (wgs * sp < n_cu && KT % (2 * sp * KS) == 0 && KT / (2 * sp) >= 8) sp *= 2;
+    while (wgs * sp < n_cu && KT % (2 * sp) == 0 && KT / (2 * sp) >= 8) sp *= 2;
     // time estimate: HBM bytes (weights once, split partials written and read), bytes pulled into
     // the CUs (every row block re-reads its weight columns, every column block its rows), MFMA
     // work, each scaled by how evenly the workgroups fill the chip
@@ -329,7 +436,7 @@ size_t gemm_part_elems(const GemmT& g) { return g.splits > 1 ? (size_t)g.splits 
 
 template <int WN, int WM, int EPI>
 hipError_t allow_lds() {
-  return hipFuncSetAttribute((const void*)k_tgemm<WN, WM, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  return hipFuncSetAttribute((const void*)k_tgemm_ring<WN, WM, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
                              Tile<WN, WM>::LDS);
 }
 
@@ -356,8 +463,11 @@ hipError_t prepare_gemm() {
 template <int WN, int WM, int EPI>
 hipError_t launch_tile(const GemmT& g, hipStream_t s) {
   using T = Tile<WN, WM>;
-  hipLaunchKernelGGL((k_tgemm<WN, WM, EPI>), dim3((g.N / T::BN) * (g.Mp / T::BM) * g.splits), dim3(256), T::LDS, s,
-                     g);
+  const dim3 grid((g.N / T::BN) * (g.Mp / T::BM) * g.splits);
+  if (g.kern == 0)
+    hipLaunchKernelGGL((k_tgemm_ring<WN, WM, EPI>), grid, dim3(256), T::LDS, s, g);
+  else
+    hipLaunchKernelGGL((k_tgemm_reg<WN, WM, EPI>), grid, dim3(256), 0, s, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.splits == 1) return e;
   const size_t total = (size_t)g.M * (g.N / 4);
@@ -379,7 +489,7 @@ hipError_t launch_tgemm_e(const GemmT& g, hipStream_t s) {
 
 hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
   if (g.K % 32 || g.N % 64 || g.Mp % ROW_PAD || g.M > g.Mp || g.tile < 0 || g.tile >= N_TILES) return hipErrorInvalidValue;
-  if (g.splits < 1 || (g.K / 32) % (g.splits * KS) || (g.splits > 1 && !g.part)) return hipErrorInvalidValue;
+  if (g.splits < 1 || (g.K / 32) % g.splits || (g.splits > 1 && !g.part)) return hipErrorInvalidValue;
   if ((size_t)g.Mp * g.K * 2 >= (1ull << 32) || (size_t)g.K * g.N * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   switch (epi) {
     case EP_BF16: return launch_tgemm_e<EP_BF16>(g, s);

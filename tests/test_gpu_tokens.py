@@ -74,6 +74,11 @@ def test_va_small_gqa():
     _va_case(va_small(n_heads=4, n_kv_heads=2, name="va_small_gqa"))
 
 
+def test_va_many_rows():
+    """1030 rows: the GEMMs take the register-fed kernel (1024 rows or more)."""
+    _va_case(va_small(rows=1030, prefix_lens=[100], name="va_1030"))
+
+
 @pytest.mark.parametrize("L", [0, 1, 63, 300])
 def test_va_prefix_edges(L):
     # 161 rows: the smallest chunk the large-token plan takes; 300 = the full capacity
@@ -162,6 +167,11 @@ def test_dit_small_rows_multiple_of_padding():
     _dit_case(dit_small(rows=256, name="dit_256"))
 
 
+def test_dit_many_rows():
+    """1100 tokens (ragged): the GEMMs take the register-fed kernel."""
+    _dit_case(dit_small(rows=1100, name="dit_1100"))
+
+
 def test_dit_uniform_attention_closed_form():
     """W_q = 0 makes every attention row uniform, so o is the mean of the value
     rows; the oracle is pinned to that closed form, and here the GPU follows."""
@@ -218,9 +228,11 @@ def test_dit_full_permutation_equivariance():
                  what="permuted")
 
 
-def test_dit_full_width_one_block():
-    """One block at full width, heads and MLP, over 528 tokens (four 128-row
-    tiles and a ragged 16-row tail), element by element."""
-    cfg = phx_inputs.workload("wam_dit_bf16", layers=1, rows=528)
-    cfg["name"] = "dit_1block_528"
+@pytest.mark.parametrize("rows", [528, 1100])
+def test_dit_full_width_one_block(rows):
+    """One block at full width, heads and MLP, element by element: 528 tokens
+    (four 128-row tiles and a ragged 16-row tail, LDS-ring GEMMs) and 1100
+    tokens (register-fed GEMMs, ragged 76-row tail)."""
+    cfg = phx_inputs.workload("wam_dit_bf16", layers=1, rows=rows)
+    cfg["name"] = f"dit_1block_{rows}"
     _dit_case(cfg)
