@@ -57,9 +57,10 @@ __device__ inline f32x4 mma16(const s16x4& a, const s16x4& b, const f32x4& c) {
 // k_tgemm_ring (few rows: the weights stream from HBM once and latency rules):
 // both operands reach LDS straight from memory (buffer loads with the LDS bit,
 // no registers in between), each 1 KiB load already in MFMA fragment order (a
-// weight tile, or 16 activation rows x 64 bytes), through an NSTAGE-deep ring;
-// every wave waits for its own loads with an explicit vmcnt and a barrier
-// publishes the stage, so NSTAGE - 1 k-steps are in flight.
+// weight tile, or 16 activation rows x 64 bytes), through a ring of NS = 4
+// stages (deeper rings measured slower: fewer workgroups fit a CU); every
+// wave waits for its own loads with an explicit vmcnt and a barrier publishes
+// the stage, so NS - 1 k-steps are in flight.
 //
 // k_tgemm_reg (many rows: MFMA-bound, and LDS bandwidth is the limit): a
 // wave's weight fragments are its own, so they go from memory straight into
@@ -69,10 +70,8 @@ __device__ inline f32x4 mma16(const s16x4& a, const s16x4& b, const f32x4& c) {
 //
 // With split > 1 workgroup z multiplies k-steps [z KT/split, (z+1) KT/split)
 // and stores its raw sums for an ordered reduction.
-constexpr int NSTAGE = 4;  // ring stages (k_tgemm_ring)
 constexpr int WPD = 2;     // weight prefetch distance in k-steps (k_tgemm_reg)
 constexpr int UNR = 4;     // k_tgemm_reg main-loop unroll: its register rings rotate with it
-static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the stage waits cover up to two stages in flight");
 static_assert(WPD < UNR && UNR % 2 == 0, "the weight ring holds UNR k-steps, the activation ring 2");
 
 template <int WN, int WM>
@@ -81,7 +80,9 @@ struct Tile {
   static constexpr int FR = WM + 4 * WN;  // ring: 1 KiB fragments per k-step
   static constexpr int PW = WM / 4 + WN;  // ring: loads per wave per k-step
   static constexpr int STAGE = FR * 1024;
-  static constexpr int LDS = NSTAGE * STAGE;
+  static constexpr int NS = 4;
+  static constexpr int LDS = NS * STAGE;
+  static_assert((NS - 2) * PW <= 63, "vmcnt holds at most 63 loads");
   static constexpr int AP = BM / 64;      // reg: 16-byte activation pieces per thread per k-step
 };
 
@@ -107,6 +108,17 @@ __device__ inline void dma_frag(unsigned lds, unsigned voff, u32x4 rs, unsigned 
 template <int N>
 __device__ inline void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most PW * min(ahead, A) loads are in flight
+template <int PW, int A>
+__device__ inline void wait_ahead(int ahead) {
+  if constexpr (A <= 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= A) wait_vm<PW * A>();
+    else wait_ahead<PW, A - 1>(ahead);
+  }
 }
 
 // barrier without the fence __syncthreads implies (that fence would wait for
@@ -210,6 +222,7 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   const int per = KT / g.splits;
   const int kb = bz * per;
   const int ns = per / KS;  // stages
+  constexpr int NS = T::NS;
   const unsigned lds0 = (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)smem);
   const u32x4 ra = rsrc_words(g.a, (unsigned)((size_t)g.Mp * g.K * 2));
   const u32x4 rw = rsrc_words(g.w, (unsigned)((size_t)g.K * g.N * 2));
@@ -222,7 +235,7 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   }
   const unsigned vow = (unsigned)lane * 16u;
   auto issue = [&](int s) {
-    const unsigned st = lds0 + (unsigned)((s % NSTAGE) * T::STAGE);
+    const unsigned st = lds0 + (unsigned)((s % NS) * T::STAGE);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int kt = kb + s * KS + kk;
@@ -242,19 +255,16 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
 #pragma unroll
     for (int m = 0; m < WM; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
+  for (int s = 0; s < NS - 1; ++s)
     if (s < ns) issue(s);
   for (int s = 0; s < ns; ++s) {
     // stage s must be in; the later stages already issued may still be in flight
-    const int ahead = min(NSTAGE - 2, ns - 1 - s);
-    if (ahead >= 2) wait_vm<2 * KS * T::PW>();
-    else if (ahead == 1) wait_vm<KS * T::PW>();
-    else wait_vm<0>();
+    wait_ahead<KS * T::PW, NS - 2>(ns - 1 - s);
     wg_barrier();  // stage s is in LDS for every wave; every wave is done with stage s - 1
-    if (s + NSTAGE - 1 < ns) issue(s + NSTAGE - 1);
+    if (s + NS - 1 < ns) issue(s + NS - 1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const unsigned char* st = smem + (s % NSTAGE) * T::STAGE + kk * T::FR * 1024;
+      const unsigned char* st = smem + (s % NS) * T::STAGE + kk * T::FR * 1024;
       bf16x8 wf[WN];
 #pragma unroll
       for (int n = 0; n < WN; ++n) wf[n] = *(const bf16x8*)(st + (WM + wave * WN + n) * 1024 + lane * 16);
@@ -296,18 +306,31 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
   const int KT = g.K / 32;
   const int per = KT / g.splits;
   const int kb = bz * per;
+  // Buffer loads with a fixed per-lane offset and a per-k-step scalar offset:
+  // no address arithmetic in the loop, so no register of an in-flight load is
+  // reused for an address (which would force a wait for every load).
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.a), (short)0, (int)((size_t)g.Mp * g.K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.w), (short)0, (int)((size_t)g.K * g.N * 2), 0x00020000);
   // activation pieces of this thread: rows p*64 + tid/4, k chunk tid%4
-  const u32x4* arow[T::AP];
-  int aslot[T::AP];
+  int avo[T::AP], aslot[T::AP];
 #pragma unroll
   for (int p = 0; p < T::AP; ++p) {
     const int r = p * 64 + (tid >> 2);
-    arow[p] = (const u32x4*)((const bf16*)g.a + (size_t)(m0 + r) * g.K + 8 * (tid & 3));
+    avo[p] = (int)(((size_t)(m0 + r) * g.K + 8 * (tid & 3)) * 2);
     aslot[p] = (r >> 4) * 64 + (r & 15) + 16 * (tid & 3);
   }
-  const u32x4* wbase[WN];
+  const int wvo = lane * 16;
+  int wso[WN];
 #pragma unroll
-  for (int n = 0; n < WN; ++n) wbase[n] = (const u32x4*)g.w + ((size_t)(nt0 + n) * KT + kb) * 64 + lane;
+  for (int n = 0; n < WN; ++n) wso[n] = (int)(((size_t)(nt0 + n) * KT + kb) * 1024);
+  auto ld_a = [&](int p, int s) -> u32x4 {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, avo[p], (kb + s) * 64, 0));
+  };
+  auto ld_w = [&](int n, int s) -> u32x4 {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wvo, wso[n] + s * 1024, 0));
+  };
   f32x4 acc[WN][WM];
 #pragma unroll
   for (int n = 0; n < WN; ++n)
@@ -317,50 +340,52 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
   u32x4 ar[2][T::AP];   // activation pieces, k-step s in slot s % 2
   // prologue: activations of k-steps 0 and 1, weights of k-steps 0 .. WPD-1
 #pragma unroll
-  for (int p = 0; p < T::AP; ++p) ar[0][p] = arow[p][(kb + 0) * 4];
+  for (int p = 0; p < T::AP; ++p) ar[0][p] = ld_a(p, 0);
   if (per > 1) {
 #pragma unroll
-    for (int p = 0; p < T::AP; ++p) ar[1][p] = arow[p][(kb + 1) * 4];
+    for (int p = 0; p < T::AP; ++p) ar[1][p] = ld_a(p, 1);
   }
 #pragma unroll
   for (int j = 0; j < WPD; ++j)
     if (j < per) {
 #pragma unroll
-      for (int n = 0; n < WN; ++n) wr[j][n] = wbase[n][(size_t)j * 64];
+      for (int n = 0; n < WN; ++n) wr[j][n] = ld_w(n, j);
     }
 #pragma unroll
   for (int p = 0; p < T::AP; ++p) as[0][aslot[p]] = ar[0][p];
   __syncthreads();
-  for (int s0 = 0; s0 < per; s0 += UNR) {
+  // one k-step: fetch ahead, stage the next activations, multiply, barrier
+  auto step = [&](int s, int j, bool fetch, bool stage) {
+    if (fetch) {
+      // activations of s + 2 (into the slot k-step s has left), weights of s + WPD
 #pragma unroll
-    for (int j = 0; j < UNR; ++j) {
-      const int s = s0 + j;
-      if (s < per) {
-        // fetch ahead: activations of s + 2 (into the slot k-step s has left), weights of s + WPD
-        if (s + 2 < per) {
+      for (int p = 0; p < T::AP; ++p) ar[j & 1][p] = ld_a(p, s + 2);
 #pragma unroll
-          for (int p = 0; p < T::AP; ++p) ar[j & 1][p] = arow[p][(kb + s + 2) * 4];
-        }
-        if (s + WPD < per) {
-#pragma unroll
-          for (int n = 0; n < WN; ++n) wr[(j + WPD) % UNR][n] = wbase[n][(size_t)(s + WPD) * 64];
-        }
-        // stage the activations of s + 1 for the next k-step
-        if (s + 1 < per) {
-#pragma unroll
-          for (int p = 0; p < T::AP; ++p) as[(j + 1) & 1][aslot[p]] = ar[(j + 1) & 1][p];
-        }
-        const u32x4* st = as[j & 1];
-#pragma unroll
-        for (int m = 0; m < WM; ++m) {
-          const bf16x8 af = __builtin_bit_cast(bf16x8, st[m * 64 + lane]);
-#pragma unroll
-          for (int n = 0; n < WN; ++n) acc[n][m] = mma32(__builtin_bit_cast(bf16x8, wr[j][n]), af, acc[n][m]);
-        }
-        __syncthreads();
-      }
+      for (int n = 0; n < WN; ++n) wr[(j + WPD) % UNR][n] = ld_w(n, s + WPD);
     }
+    if (stage) {
+#pragma unroll
+      for (int p = 0; p < T::AP; ++p) as[(j + 1) & 1][aslot[p]] = ar[(j + 1) & 1][p];
+    }
+    const u32x4* st = as[j & 1];
+#pragma unroll
+    for (int m = 0; m < WM; ++m) {
+      const bf16x8 af = __builtin_bit_cast(bf16x8, st[m * 64 + lane]);
+#pragma unroll
+      for (int n = 0; n < WN; ++n) acc[n][m] = mma32(__builtin_bit_cast(bf16x8, wr[j][n]), af, acc[n][m]);
+    }
+    __syncthreads();
+  };
+  // The steady loop has no conditions (per is a multiple of UNR), so the
+  // compiler's waits can count the loads in flight exactly; the last UNR
+  // k-steps fetch and stage only what remains.
+  int s0 = 0;
+  for (; s0 + UNR < per; s0 += UNR) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) step(s0 + j, j, true, true);
   }
+#pragma unroll
+  for (int j = 0; j < UNR; ++j) step(s0 + j, j, j + 2 < UNR && j + WPD < UNR, j + 1 < UNR);
   // lane holds columns 4 (lane / 16) + [0, 4) of each n-tile (tile order) for
   // row lane % 16 of each m-tile
   const int gq = lane >> 4;
@@ -394,7 +419,7 @@ __global__ void k_tsplit(GemmT g) {
 struct TileCfg {
   int wn, wm;
 };
-constexpr TileCfg TILES[] = {{4, 8}, {2, 8}, {2, 4}, {1, 4}};
+constexpr TileCfg TILES[] = {{4, 8}, {2, 8}, {2, 4}, {1, 4}, {2, 16}, {1, 16}};
 constexpr int N_TILES = sizeof(TILES) / sizeof(TILES[0]);
 
 void plan_gemm(GemmT& g, int n_cu) {
@@ -410,7 +435,7 @@ void plan_gemm(GemmT& g, int n_cu) {
     if (g.N % bn || g.Mp % bm) continue;
     const long long wgs = (long long)(g.N / bn) * (g.Mp / bm);
     int sp = 1;
-    while (wgs * sp < n_cu && KT % (2 * sp) == 0 && KT / (2 * sp) >= 8) sp *= 2;
+    while (wgs * sp < n_cu && KT % (2 * sp * UNR) == 0 && KT / (2 * sp) >= 8) sp *= 2;
     // time estimate: HBM bytes (weights once, split partials written and read), bytes pulled into
     // the CUs (every row block re-reads its weight columns, every column block its rows), MFMA
     // work, each scaled by how evenly the workgroups fill the chip
@@ -418,7 +443,9 @@ void plan_gemm(GemmT& g, int n_cu) {
     const double pulled = 2.0 * g.K * ((double)g.N * (g.Mp / bm) + (double)g.Mp * (g.N / bn));
     const double flops = 2.0 * g.Mp * g.N * g.K;
     const double units = (double)wgs * sp, rounds = std::ceil(units / n_cu);
-    const double t = std::max(std::max(hbm / 5e12, pulled / (n_cu * 100e9)), flops / 1.6e15) * rounds * n_cu / units;
+    double t = std::max(std::max(hbm / 5e12, pulled / (n_cu * 100e9)), flops / 1.6e15) * rounds * n_cu / units;
+    // the register-fed kernel is LDS-bound: the widest tile (most MFMAs per fragment read) measured fastest
+    if (g.kern == 1 && i == 0) t *= 0.5;
     if (t < best * 0.97) {
       best = t;
       g.tile = i;
@@ -428,7 +455,7 @@ void plan_gemm(GemmT& g, int n_cu) {
 }
 
 const char* tile_name(int tile) {
-  static const char* names[N_TILES] = {"256x128", "128x128", "128x64", "64x64"};
+  static const char* names[N_TILES] = {"256x128", "128x128", "128x64", "64x64", "128x256", "64x256"};
   return tile >= 0 && tile < N_TILES ? names[tile] : "?";
 }
 
@@ -446,7 +473,9 @@ hipError_t allow_lds_e() {
   if ((e = allow_lds<4, 8, EPI>()) != hipSuccess) return e;
   if ((e = allow_lds<2, 8, EPI>()) != hipSuccess) return e;
   if ((e = allow_lds<2, 4, EPI>()) != hipSuccess) return e;
-  return allow_lds<1, 4, EPI>();
+  if ((e = allow_lds<1, 4, EPI>()) != hipSuccess) return e;
+  if ((e = allow_lds<2, 16, EPI>()) != hipSuccess) return e;
+  return allow_lds<1, 16, EPI>();
 }
 
 hipError_t prepare_gemm() {
@@ -483,13 +512,15 @@ hipError_t launch_tgemm_e(const GemmT& g, hipStream_t s) {
     case 1: return launch_tile<2, 8, EPI>(g, s);
     case 2: return launch_tile<2, 4, EPI>(g, s);
     case 3: return launch_tile<1, 4, EPI>(g, s);
+    case 4: return launch_tile<2, 16, EPI>(g, s);
+    case 5: return launch_tile<1, 16, EPI>(g, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
   if (g.K % 32 || g.N % 64 || g.Mp % ROW_PAD || g.M > g.Mp || g.tile < 0 || g.tile >= N_TILES) return hipErrorInvalidValue;
-  if (g.splits < 1 || (g.K / 32) % g.splits || (g.splits > 1 && !g.part)) return hipErrorInvalidValue;
+  if (g.splits < 1 || (g.K / 32) % (g.splits * UNR) || (g.splits > 1 && !g.part)) return hipErrorInvalidValue;
   if ((size_t)g.Mp * g.K * 2 >= (1ull << 32) || (size_t)g.K * g.N * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   switch (epi) {
     case EP_BF16: return launch_tgemm_e<EP_BF16>(g, s);
