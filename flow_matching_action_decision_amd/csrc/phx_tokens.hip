@@ -661,6 +661,13 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) qf[qt][ds] = *(const bf16x8*)(qp + 32 * ds);
   }
+  // Wait for the query loads here, once: left to the first use inside the
+  // block loop, the compiler's wait would also cover the next block's LDS
+  // loads issued just before it (it does not see those), every block.
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) asm volatile("" : "+v"(qf[qt][ds]));
   const unsigned lds0 = (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)smem);
   const u32x4 rk = rsrc_words(a.kj, (unsigned)((size_t)a.R * kvd * 2));
   const u32x4 rv = rsrc_words(a.vt, (unsigned)((size_t)a.KVH * a.R * DH * 2));
@@ -706,41 +713,61 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
       }
     }
     const int k0 = b * KB;
+    // keys at or past T exist only in the last block
+    if (k0 + KB > T) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + 16 * kt + 4 * g4 + i >= T) sc[qt][kt][i] = -INFINITY;
+    }
+    // Lazy rescaling: the reference m (base 2) of a query moves only when some
+    // score of the wave exceeds it by more than 8, so the probabilities stay
+    // below 2^8 and most blocks neither reduce across lanes nor rescale O.
+    // The four lanes of a query always share one m (their probabilities meet
+    // in the same MFMA).  Per-lane partial sums l are reduced at the end.
     bf16x8 pf[2][2];
-    float corr[2];
+    float corr[2] = {1.f, 1.f};
+    bool moved[2] = {false, false};
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * kt + 4 * g4 + i;
-          const float sv = key < T ? sc[qt][kt][i] * sl2 : -INFINITY;
-          sc[qt][kt][i] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qt], mx);
-      corr[qt] = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - m_new);
-      float ls = 0.f;
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[qt][kt][i]);
+      mx *= sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[qt] + 8.0f) != 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[qt], mx);
+        corr[qt] = exp2f(m_run[qt] - m_new);  // 0 on the first block (m_run = -inf)
+        l_run[qt] *= corr[qt];
+        m_run[qt] = m_new;
+        moved[qt] = true;
+      }
+      const float mneg = -m_run[qt];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = sc[qt][kt][i] == -INFINITY ? 0.f : exp2f(sc[qt][kt][i] - m_new);
-          ls += p;
+          const float p = exp2f(fmaf(sc[qt][kt][i], sl2, mneg));
+          l_run[qt] += p;
           pf[qt][kt >> 1][4 * (kt & 1) + i] = (bf16)p;
         }
-      ls += __shfl_xor(ls, 16);
-      ls += __shfl_xor(ls, 32);
-      l_run[qt] = l_run[qt] * corr[qt] + ls;
-      m_run[qt] = m_new;
+    }
+    if (moved[0] || moved[1]) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        oacc[0][d] *= corr[0];
+        oacc[1][d] *= corr[1];
+      }
     }
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      f32x4 a0 = oacc[0][d] * corr[0], a1 = oacc[1][d] * corr[1];
+      f32x4 a0 = oacc[0][d], a1 = oacc[1][d];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const bf16x8 vf = *(const bf16x8*)(st + 16384 + (j * 8 + d) * 1024 + lane * 16);
@@ -752,6 +779,11 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
     }
   }
   // lane holds dims 16 d + 4 g4 + [0, 4) of query q0 + 16 qt + qr
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    l_run[qt] += __shfl_xor(l_run[qt], 16);
+    l_run[qt] += __shfl_xor(l_run[qt], 32);
+  }
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int q = q0 + 16 * qt + qr;
