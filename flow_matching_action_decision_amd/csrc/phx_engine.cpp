@@ -660,7 +660,7 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   const long long q_wgs = (long long)((M + 127) / 128) * H;
   const int max_blocks = R / 64;
   h->splits = 1;
-  while (q_wgs * h->splits < 512 && max_blocks / (h->splits * 2) >= 4) h->splits *= 2;
+  while (q_wgs * h->splits < 256 && max_blocks / (h->splits * 2) >= 4) h->splits *= 2;
 
   struct Buf { void** p; size_t bytes; const char* what; };
   std::vector<Buf> bufs = {
