@@ -42,6 +42,7 @@ import phx_inputs  # noqa: E402
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 WORKLOAD = "pi05_expert_bf16"
+BATCH_WORKLOADS = ("rollout_b16_bf16",)
 TOKEN_WORKLOADS = ("va_chunk_bf16", "wam_dit_bf16")
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_pi05_expert_bf16.json")
@@ -163,7 +164,7 @@ def cpu_baseline(cfg: dict, inp: dict, budget_s: float) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", default=WORKLOAD, choices=(WORKLOAD,) + TOKEN_WORKLOADS)
+    ap.add_argument("--workload", default=WORKLOAD, choices=(WORKLOAD,) + BATCH_WORKLOADS + TOKEN_WORKLOADS)
     ap.add_argument("--steps", type=int, default=200, help="timed decisions")
     ap.add_argument("--warmup", type=int, default=20, help="untimed decisions before the timed region")
     ap.add_argument("--seed", type=int, default=0)
@@ -190,10 +191,11 @@ def main():
     from flow_matching_action_decision_amd.expert import Expert
     from flow_matching_action_decision_amd import binding
 
-    if args.workload != WORKLOAD:
+    if args.workload in TOKEN_WORKLOADS:
         return bench_tokens(args)
-    cfg = phx_inputs.workload(WORKLOAD)
-    log(f"bench: generating inputs for {WORKLOAD}")
+    name = args.workload
+    cfg = phx_inputs.workload(name)
+    log(f"bench: generating inputs for {name}")
     inp = phx_inputs.make_inputs(cfg, args.seed)
     ab = algorithmic_bytes(cfg)
 
@@ -229,8 +231,9 @@ def main():
     # dominant kernel: duration of its launches, timed with HIP events on the
     # stream it runs on
     dom = ex.time_dominant_kernel(args.kernel_reps)
-    kernel_hash = kernel_source_hash()
-    traffic = measured_traffic(kernel_hash)
+    batch = name != WORKLOAD  # the rollout batch runs the multi-kernel graph
+    kernel_hash = kernel_source_hash(("phx_kernels.hip", "phx_internal.h") if batch else DECISION_KERNEL_SOURCES)
+    traffic = None if batch else measured_traffic(kernel_hash)
     achieved = dom["bytes_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -257,17 +260,21 @@ def main():
         cpu = cpu_baseline(cfg, inp, args.cpu_budget_s)
 
     hbm_gbs = ab["per_decision"] / (ms * 1e-3) / 1e9
+    lens = [int(L) for L in inp["lens"]]
     line = {
-        "metric": "ms/decision (pi0.5-shape, 18L x 10 steps) + % peak HBM GB/s, 1 GPU",
+        "metric": ("ms/decision (pi0.5-shape, 18L x 10 steps) + % peak HBM GB/s, 1 GPU" if not batch else
+                   f"ms/decision ({name}: {cfg['batch']} requests, 18L x 10 steps) + % peak HBM GB/s, 1 GPU"),
         "value": round(ms, 4), "unit": "ms/decision", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 prefix K/V, N(0,1) noise)",
-        "config": {"workload": WORKLOAD, "layers": cfg["layers"], "euler_steps": cfg["steps"],
-                   "action_rows": cfg["rows"], "prefix_len": int(inp["lens"][0]), "width": cfg["width"],
+        "config": {"workload": name, "layers": cfg["layers"], "euler_steps": cfg["steps"],
+                   "action_rows": cfg["rows"], "prefix_len": lens[0] if not batch else lens, "width": cfg["width"],
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} / {cfg['n_kv_heads']} kv",
                    "mlp_hidden": cfg["mlp_hidden"], "batch": cfg["batch"]},
         "decisions_per_s": round(1000.0 / ms, 1),
         "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
+        **({"requests_per_s": round(1000.0 * cfg["batch"] / ms, 1),
+            "ms_per_request_amortised": round(ms / cfg["batch"], 4)} if batch else {}),
         "algorithmic_bytes_per_decision": ab["per_decision"],
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "kernels_per_decision": nk,

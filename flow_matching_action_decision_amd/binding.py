@@ -30,11 +30,16 @@ PHX_MASK_FULL = 0
 EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_expert_create",
             "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_destroy", "phx_last_error",
             "phx_expert_kernels_per_decision", "phx_expert_node_info", "phx_expert_launch_node",
-            "phx_expert_status", "phx_expert_timeline")
+            "phx_expert_status", "phx_expert_timeline", "phx_expert_capsule_bytes", "phx_expert_capsule_regions",
+            "phx_expert_capsule_save", "phx_expert_capsule_restore")
 
 NODE_KINDS = {1: "in_proj", 2: "norm_qkv_rope", 3: "attention", 4: "attention_combine", 5: "out_proj_resid",
               6: "norm_gateup_geglu", 7: "down_proj_resid", 8: "norm_out_proj_euler", 9: "decision_kernel",
-              10: "tag_advance"}
+              10: "tag_advance", 11: "row_norm", 12: "qkv", 13: "gateup", 14: "out_proj_euler", 15: "state_cvt"}
+
+
+class phx_capsule_region(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 24), ("offset", ctypes.c_uint64), ("bytes", ctypes.c_uint64)]
 
 
 class phx_expert_config(ctypes.Structure):
@@ -89,6 +94,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phx_expert_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
     lib.phx_expert_timeline.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_size_t,
                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.phx_expert_capsule_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.phx_expert_capsule_regions.argtypes = [P, ctypes.POINTER(phx_capsule_region), ctypes.c_int32,
+                                               ctypes.POINTER(ctypes.c_int32)]
+    lib.phx_expert_capsule_save.argtypes = [P, P, ctypes.c_size_t, P]
+    lib.phx_expert_capsule_restore.argtypes = [P, P, ctypes.c_size_t, P]
     _lib = lib
     return lib
 
@@ -183,3 +193,28 @@ def phx_expert_timeline(h: int):
     _check(lib.phx_expert_timeline(ctypes.c_void_p(h), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), n.value,
                                    ctypes.byref(n)))
     return out.reshape(256, -1)
+
+
+def phx_expert_capsule_bytes(h: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().phx_expert_capsule_bytes(ctypes.c_void_p(h), ctypes.byref(n)))
+    return n.value
+
+
+def phx_expert_capsule_regions(h: int) -> list:
+    lib = load_library()
+    n = ctypes.c_int32(0)
+    _check(lib.phx_expert_capsule_regions(ctypes.c_void_p(h), None, 0, ctypes.byref(n)))
+    arr = (phx_capsule_region * max(n.value, 1))()
+    _check(lib.phx_expert_capsule_regions(ctypes.c_void_p(h), arr, n.value, ctypes.byref(n)))
+    return [dict(name=arr[i].name.decode(), offset=int(arr[i].offset), bytes=int(arr[i].bytes)) for i in range(n.value)]
+
+
+def phx_expert_capsule_save(h: int, capsule: int, nbytes: int, stream: int = 0):
+    _check(load_library().phx_expert_capsule_save(ctypes.c_void_p(h), ctypes.c_void_p(capsule), nbytes,
+                                                  ctypes.c_void_p(stream)))
+
+
+def phx_expert_capsule_restore(h: int, capsule: int, nbytes: int, stream: int = 0):
+    _check(load_library().phx_expert_capsule_restore(ctypes.c_void_p(h), ctypes.c_void_p(capsule), nbytes,
+                                                     ctypes.c_void_p(stream)))

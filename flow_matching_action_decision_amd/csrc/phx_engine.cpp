@@ -93,6 +93,8 @@ GemmPlan make_plan(int K, int N, int target_wgs) {
 }
 
 
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
 bool is_device_pointer(const void* p) {
   hipPointerAttribute_t attr;
   hipError_t e = hipPointerGetAttributes(&attr, p);
@@ -156,6 +158,10 @@ struct phx_expert {
   int splits = 1;             // attention key splits
   int n_cu = 0;               // compute units of the device
   float* tpart = nullptr;     // GEMM split partials of the large-token plan
+  // execution-state capsules: a pinned header staging area and the event of its last copy
+  void* cap_host = nullptr;
+  size_t cap_host_bytes = 0;
+  hipEvent_t cap_event = nullptr;
   std::vector<TokNode> tnodes;
   void* xb = nullptr;         // bf16 state rows (input projection operand)
   void* nb = nullptr;         // bf16 normalised rows
@@ -172,6 +178,11 @@ namespace {
 void release(phx_expert* h) {
   if (!h) return;
   if (h->cap) (void)hipStreamSynchronize(h->cap);
+  if (h->cap_event) {
+    (void)hipEventSynchronize(h->cap_event);
+    (void)hipEventDestroy(h->cap_event);
+  }
+  if (h->cap_host) (void)hipHostFree(h->cap_host);
   if (h->exec) (void)hipGraphExecDestroy(h->exec);
   if (h->graph) (void)hipGraphDestroy(h->graph);
   for (void* p : h->allocs) (void)hipFree(p);
@@ -724,6 +735,116 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   return PHX_OK;
 }
 
+
+// ---------------------------------------------------------------- capsules
+// The declared state regions of a handle: what phx_expert_load_prefix_kv
+// writes and every decision reads (the stored prefix K/V, the prefix lengths,
+// the decoder position table), in a fixed order per plan.
+struct StateRegion {
+  const char* name;
+  void* ptr;
+  size_t bytes;
+};
+
+std::vector<StateRegion> state_regions(const phx_expert* h) {
+  const phx_expert_config& c = h->cfg;
+  std::vector<StateRegion> r;
+  if (h->tokens) {
+    if (c.block_kind == PHX_BLOCK_DIT) return r;  // no prefix: nothing persists between decisions
+    const size_t kv = (size_t)c.layers * h->R * c.n_kv_heads * c.head_dim * 2;
+    r.push_back({"key_rows", h->tk, kv});
+    r.push_back({"value_fragments", h->tv, kv});
+    r.push_back({"prefix_lengths", h->lens, sizeof(int)});
+    r.push_back({"position_table", h->rope, (size_t)c.rows * (c.head_dim / 2) * sizeof(float2)});
+  } else if (h->persistent) {
+    r.push_back({"attention_kv_tiles", h->kvt, (size_t)h->dargs.kvt_bytes});
+    r.push_back({"prefix_lengths", h->lens, sizeof(int)});
+    r.push_back({"position_table", h->rope, (size_t)c.rows * (c.head_dim / 2) * sizeof(float2)});
+  } else {
+    const size_t kv = (size_t)c.layers * h->kv_layer * h->esz;
+    r.push_back({"key_cache", h->kc, kv});
+    r.push_back({"value_cache", h->vtc, kv});
+    r.push_back({"prefix_lengths", h->lens, (size_t)c.batch * sizeof(int)});
+    r.push_back({"position_table", h->rope, (size_t)c.batch * c.rows * (c.head_dim / 2) * sizeof(float2)});
+  }
+  return r;
+}
+
+constexpr uint32_t CAPSULE_MAGIC = 0x43584850u;  // "PHXC"
+constexpr uint32_t CAPSULE_VERSION = 1u;
+constexpr int CAPSULE_MAX_REGIONS = 8;
+
+struct CapsuleEntry {
+  char name[24];
+  uint64_t offset;  // bytes from the start of the capsule
+  uint64_t bytes;
+};
+
+// Capsule layout: this header, then per request (prefix length, loaded flag)
+// as int32 pairs, then every region at a 256-byte aligned offset.
+struct CapsuleHeader {
+  uint32_t magic, version;
+  uint64_t fingerprint;  // plan: configuration, execution path, region sizes
+  uint64_t total_bytes;
+  uint32_t n_regions, batch;
+  CapsuleEntry region[CAPSULE_MAX_REGIONS];
+};
+
+uint64_t fnv1a(uint64_t h, const void* p, size_t n) {
+  const unsigned char* b = (const unsigned char*)p;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= b[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+size_t capsule_head_bytes(const phx_expert* h) {
+  return align_up(sizeof(CapsuleHeader) + (size_t)h->cfg.batch * 2 * sizeof(int32_t), 256);
+}
+
+// header of this handle's capsule (host state included)
+CapsuleHeader capsule_layout(const phx_expert* h, const std::vector<StateRegion>& regs) {
+  CapsuleHeader hd{};
+  hd.magic = CAPSULE_MAGIC;
+  hd.version = CAPSULE_VERSION;
+  hd.batch = (uint32_t)h->cfg.batch;
+  hd.n_regions = (uint32_t)regs.size();
+  uint64_t fp = 1469598103934665603ull;
+  fp = fnv1a(fp, &h->cfg, sizeof(h->cfg));
+  const int path = h->tokens ? 2 : h->persistent ? 1 : 0;
+  fp = fnv1a(fp, &path, sizeof(path));
+  size_t off = capsule_head_bytes(h);
+  for (size_t i = 0; i < regs.size(); ++i) {
+    CapsuleEntry& e = hd.region[i];
+    std::snprintf(e.name, sizeof(e.name), "%s", regs[i].name);
+    e.offset = off;
+    e.bytes = regs[i].bytes;
+    fp = fnv1a(fp, &e.bytes, sizeof(e.bytes));
+    off = align_up(off + regs[i].bytes, 256);
+  }
+  hd.total_bytes = off;
+  hd.fingerprint = fp;
+  return hd;
+}
+
+int capsule_staging(phx_expert* h, size_t bytes) {
+  if (!h->cap_event) PHX_HIP(hipEventCreateWithFlags(&h->cap_event, hipEventDisableTiming));
+  PHX_HIP(hipEventSynchronize(h->cap_event));  // the previous header copy has finished
+  if (h->cap_host_bytes < bytes) {
+    if (h->cap_host) PHX_HIP(hipHostFree(h->cap_host));
+    h->cap_host = nullptr;
+    h->cap_host_bytes = 0;
+    hipError_t e = hipHostMalloc(&h->cap_host, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PHX_E_NOMEM, "pinned capsule staging of %zu bytes failed: %s", bytes, hipGetErrorString(e));
+    }
+    h->cap_host_bytes = bytes;
+  }
+  return PHX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1164,6 +1285,90 @@ int phx_expert_timeline(const phx_expert* h, uint32_t* out, size_t capacity, siz
   PHX_HIP(hipMemcpy(out, (const char*)h->arena + dec::AUX0 + dec::aux_timeline(h->cfg.steps, h->cfg.layers),
                     n * sizeof(uint32_t), hipMemcpyDeviceToHost));
   *count = n;
+  return PHX_OK;
+}
+
+int phx_expert_capsule_bytes(const phx_expert* h, size_t* bytes) {
+  if (!h || !bytes) return fail(PHX_E_INVALID, "NULL argument");
+  *bytes = capsule_layout(h, state_regions(h)).total_bytes;
+  g_err.clear();
+  return PHX_OK;
+}
+
+int phx_expert_capsule_regions(const phx_expert* h, phx_capsule_region* out, int32_t capacity, int32_t* count) {
+  if (!h || !count) return fail(PHX_E_INVALID, "NULL argument");
+  const std::vector<StateRegion> regs = state_regions(h);
+  const CapsuleHeader hd = capsule_layout(h, regs);
+  *count = (int32_t)regs.size();
+  if (out && capacity < (int32_t)regs.size()) return fail(PHX_E_SHAPE, "capsule has %zu regions", regs.size());
+  for (size_t i = 0; out && i < regs.size(); ++i) {
+    std::memset(&out[i], 0, sizeof(out[i]));
+    std::snprintf(out[i].name, sizeof(out[i].name), "%s", hd.region[i].name);
+    out[i].offset = hd.region[i].offset;
+    out[i].bytes = hd.region[i].bytes;
+  }
+  g_err.clear();
+  return PHX_OK;
+}
+
+int phx_expert_capsule_save(phx_expert* h, void* capsule, size_t bytes, phx_stream_t stream) {
+  if (!h || !capsule) return fail(PHX_E_INVALID, "NULL argument");
+  const std::vector<StateRegion> regs = state_regions(h);
+  const CapsuleHeader hd = capsule_layout(h, regs);
+  if (bytes < hd.total_bytes) return fail(PHX_E_SHAPE, "capsule of %zu bytes, needs %llu", bytes,
+                                          (unsigned long long)hd.total_bytes);
+  if (!is_device_pointer(capsule)) return fail(PHX_E_INVALID, "the capsule must be device memory");
+  hipStream_t s = (hipStream_t)stream;
+  const size_t head = capsule_head_bytes(h);
+  int rc = capsule_staging(h, head);
+  if (rc) return rc;
+  unsigned char* st = (unsigned char*)h->cap_host;
+  std::memset(st, 0, head);
+  std::memcpy(st, &hd, sizeof(hd));
+  int32_t* hs = (int32_t*)(st + sizeof(CapsuleHeader));
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    hs[2 * b] = h->lens_host[(size_t)b];
+    hs[2 * b + 1] = h->loaded[(size_t)b];
+  }
+  PHX_HIP(hipMemcpyAsync(capsule, st, head, hipMemcpyHostToDevice, s));
+  PHX_HIP(hipEventRecord(h->cap_event, s));
+  for (size_t i = 0; i < regs.size(); ++i)
+    PHX_HIP(hipMemcpyAsync((char*)capsule + hd.region[i].offset, regs[i].ptr, regs[i].bytes, hipMemcpyDeviceToDevice,
+                           s));
+  g_err.clear();
+  return PHX_OK;
+}
+
+int phx_expert_capsule_restore(phx_expert* h, const void* capsule, size_t bytes, phx_stream_t stream) {
+  if (!h || !capsule) return fail(PHX_E_INVALID, "NULL argument");
+  const std::vector<StateRegion> regs = state_regions(h);
+  const CapsuleHeader want = capsule_layout(h, regs);
+  if (bytes < want.total_bytes) return fail(PHX_E_SHAPE, "capsule of %zu bytes, needs %llu", bytes,
+                                            (unsigned long long)want.total_bytes);
+  if (!is_device_pointer(capsule)) return fail(PHX_E_INVALID, "the capsule must be device memory");
+  hipStream_t s = (hipStream_t)stream;
+  const size_t head = capsule_head_bytes(h);
+  int rc = capsule_staging(h, head);
+  if (rc) return rc;
+  // the header is needed on the host: read it in stream order and wait for it
+  PHX_HIP(hipMemcpyAsync(h->cap_host, capsule, head, hipMemcpyDeviceToHost, s));
+  PHX_HIP(hipStreamSynchronize(s));
+  CapsuleHeader hd;
+  std::memcpy(&hd, h->cap_host, sizeof(hd));
+  if (hd.magic != CAPSULE_MAGIC || hd.version != CAPSULE_VERSION)
+    return fail(PHX_E_INVALID, "not a capsule of this library (magic 0x%08x, version %u)", hd.magic, hd.version);
+  if (hd.fingerprint != want.fingerprint || hd.n_regions != want.n_regions || hd.total_bytes != want.total_bytes)
+    return fail(PHX_E_SHAPE, "capsule plan fingerprint %016llx does not match this handle's %016llx",
+                (unsigned long long)hd.fingerprint, (unsigned long long)want.fingerprint);
+  for (size_t i = 0; i < regs.size(); ++i)
+    PHX_HIP(hipMemcpyAsync(regs[i].ptr, (const char*)capsule + hd.region[i].offset, regs[i].bytes,
+                           hipMemcpyDeviceToDevice, s));
+  const int32_t* hs = (const int32_t*)((const unsigned char*)h->cap_host + sizeof(CapsuleHeader));
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    h->lens_host[(size_t)b] = hs[2 * b];
+    h->loaded[(size_t)b] = hs[2 * b + 1];
+  }
+  g_err.clear();
   return PHX_OK;
 }
 

@@ -82,6 +82,25 @@ class Expert:
     def timeline(self):
         return B.phx_expert_timeline(self.h)
 
+    def capsule_bytes(self) -> int:
+        return B.phx_expert_capsule_bytes(self.h)
+
+    def capsule_regions(self) -> list:
+        return B.phx_expert_capsule_regions(self.h)
+
+    def capsule_save(self, capsule=None):
+        """Snapshot the state regions into a device uint8 tensor (allocated if
+        not given); returns it."""
+        torch = self.torch
+        n = self.capsule_bytes()
+        if capsule is None:
+            capsule = torch.empty(n, dtype=torch.uint8, device=self.device)
+        B.phx_expert_capsule_save(self.h, capsule.data_ptr(), capsule.numel(), self.stream)
+        return capsule
+
+    def capsule_restore(self, capsule):
+        B.phx_expert_capsule_restore(self.h, capsule.data_ptr(), capsule.numel(), self.stream)
+
     def kernels_per_decision(self) -> int:
         return B.phx_expert_kernels_per_decision(self.h)
 

@@ -273,6 +273,46 @@ PHX_API int phx_expert_status(const phx_expert* h, uint32_t* status);
  */
 PHX_API int phx_expert_timeline(const phx_expert* h, uint32_t* out, size_t capacity, size_t* count);
 
+/*
+ * Execution-state capsules ("FlashRT-PAI", section 3.4 and Table 6): snapshot,
+ * restore and fork of a handle's declared state regions, the ones
+ * phx_expert_load_prefix_kv writes and every decision reads -- the stored
+ * prefix K/V (in the handle's own layout), the prefix lengths and the decoder
+ * position table -- by device-to-device copies into one caller-owned device
+ * buffer.  The buffer starts with a header: a magic word, a plan fingerprint
+ * (a hash of the configuration, the execution path and the region sizes),
+ * the region list (names, offsets, lengths) and each request's prefix length
+ * and loaded flag.  Weights and step tables stay resident and are not part of
+ * a capsule.  Capsules are process-local and plan-specific: restore accepts
+ * only a capsule whose fingerprint matches the handle's, i.e. one saved by a
+ * handle created with the same configuration (fork = save on one handle,
+ * restore on another).  A decision after restore reproduces, bit for bit, the
+ * decision the saving handle would have made.  The DiT-style block keeps no
+ * state between decisions: its capsule is the header alone.
+ */
+typedef struct phx_capsule_region {
+  char name[24];
+  uint64_t offset;  /* bytes from the start of the capsule */
+  uint64_t bytes;
+} phx_capsule_region;
+
+/* Size in bytes of this handle's capsule. */
+PHX_API int phx_expert_capsule_bytes(const phx_expert* h, size_t* bytes);
+/* The capsule's regions; with out == NULL only *count is set.  PHX_E_SHAPE if
+   capacity is too small. */
+PHX_API int phx_expert_capsule_regions(const phx_expert* h, phx_capsule_region* out, int32_t capacity,
+                                       int32_t* count);
+/* Snapshot: stream-ordered copies of the state regions into capsule (device
+   memory of at least phx_expert_capsule_bytes bytes).  Asynchronous; the
+   caller keeps capsule alive until stream has passed the call. */
+PHX_API int phx_expert_capsule_save(phx_expert* h, void* capsule, size_t bytes, phx_stream_t stream);
+/* Restore (or fork into this handle): waits for stream to read the header,
+   checks the magic word and the plan fingerprint (PHX_E_SHAPE on a mismatch,
+   PHX_E_INVALID for a buffer that is not a capsule), then copies the regions
+   back in stream order and restores each request's prefix length and loaded
+   flag.  On error the handle is unchanged. */
+PHX_API int phx_expert_capsule_restore(phx_expert* h, const void* capsule, size_t bytes, phx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
