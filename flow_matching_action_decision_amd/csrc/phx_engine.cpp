@@ -64,7 +64,8 @@ struct Node {
 };
 
 // One kernel launch of the large-token plan.
-enum TokOp : int { TOP_CVT = 0, TOP_NORM = 1, TOP_GEMM = 2, TOP_ATTN = 3, TOP_COMBINE = 4 };
+enum TokOp : int { TOP_CVT = 0, TOP_NORM = 1, TOP_GEMM = 2, TOP_ATTN = 3, TOP_COMBINE = 4, TOP_MK_ATTN = 5,
+                   TOP_MK_COMBINE = 6, TOP_MK_GEMM = 7 };
 
 struct TokNode {
   int kind = 0, step = 0, layer = 0, op = 0, epi = 0;
@@ -72,6 +73,10 @@ struct TokNode {
   char name[32] = {0};
   tok::GemmT g{};
   tok::AttnT a{};
+  AttnArgs mat{};     // TOP_MK_ATTN: the batched multi-query attention of the request caches
+  CombineArgs mcb{};  // TOP_MK_COMBINE
+  GemmArgs mg{};      // TOP_MK_GEMM: a small-M projection of the multi-kernel path (state width 32)
+  int mk_nw = 1, mk_pro = 0, mk_epi = 0;
   // TOP_NORM / TOP_CVT
   int norm_kind = 0;  // 0 RMS, 1 LayerNorm
   const float* src = nullptr;
@@ -154,6 +159,8 @@ struct phx_expert {
   unsigned seq_limit = 0;     // clear them before the tag space wraps
   // large-token plan (a chunk of many rows, or the DiT-style block)
   bool tokens = false;
+  bool batched = false;       // the plan for a batch of requests: large-token GEMMs, per-request caches
+  int trows = 0;              // rows of the plan (batch * rows)
   int Mp = 0;                 // rows padded to tok::ROW_PAD
   int splits = 1;             // attention key splits
   int n_cu = 0;               // compute units of the device
@@ -507,8 +514,17 @@ bool uses_tokens(const phx_expert_config& c) {
   return c.block_kind == PHX_BLOCK_DIT || (long long)c.rows * c.batch > 160;
 }
 
+// A bf16 batch of 65..160 rows: the large-token GEMMs on all rows at once
+// (each weight byte serves every request) with the per-request caches and the
+// batched multi-query attention of the multi-kernel path.
+bool uses_batched(const phx_expert_config& c) {
+  const long long rows = (long long)c.rows * c.batch;
+  return c.block_kind == PHX_BLOCK_DECODER && c.weight_dtype == PHX_DTYPE_BF16 && rows > 64 && rows <= 160 &&
+         !(c.flags & PHX_FLAG_MULTI_KERNEL);
+}
+
 int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s) {
-  const int M = h->cfg.rows;
+  const int M = h->trows;
   switch (nd.op) {
     case TOP_CVT:
       PHX_HIP(tok::launch_tcvt(nd.src, nd.dst, M, h->Mp, nd.cols, s));
@@ -524,6 +540,15 @@ int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s) {
       break;
     case TOP_COMBINE:
       PHX_HIP(tok::launch_tcombine(nd.a, s));
+      break;
+    case TOP_MK_ATTN:
+      PHX_HIP(launch_attention(1, h->QT, nd.mat, h->cfg.batch, s));
+      break;
+    case TOP_MK_COMBINE:
+      PHX_HIP(launch_combine(1, nd.mcb, h->cfg.batch, s));
+      break;
+    case TOP_MK_GEMM:
+      PHX_HIP(launch_gemm(1, nd.mk_nw, h->MT, nd.mk_pro, nd.mk_epi, nd.mg, s));
       break;
     default:
       return fail(PHX_E_INVALID, "unknown token-plan op %d", nd.op);
@@ -542,9 +567,9 @@ int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s) {
 int build_tok_nodes(phx_expert* h) {
   const phx_expert_config& c = h->cfg;
   const bool dit = c.block_kind == PHX_BLOCK_DIT;
-  const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = c.rows;
-  const int NL = c.layers;
-  const int HD = H * tok::DH, NQKV = (H + 2 * KVH) * tok::DH, kvd = KVH * tok::DH;
+  const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = h->trows;
+  const int NL = c.layers, Dh = c.head_dim;
+  const int HD = H * Dh, NQKV = (H + 2 * KVH) * Dh, kvd = KVH * Dh;
   const int Mp = h->Mp;
   h->tnodes.clear();
   auto name_of = [](TokNode& nd, const char* name) { std::snprintf(nd.name, sizeof(nd.name), "%s", name); };
@@ -554,7 +579,7 @@ int build_tok_nodes(phx_expert* h) {
     nd.kind = kind; nd.step = k; nd.layer = l; nd.op = TOP_GEMM; nd.epi = epi;
     tok::GemmT& g = nd.g;
     g.a = a; g.w = (const char*)h->wt + w_off * 2; g.out = out; g.gate = gate; g.rope = h->rope;
-    g.rot_cols = dit ? 0 : (H + KVH) * tok::DH; g.dt = c.dt; g.M = M; g.Mp = Mp; g.K = K; g.N = N; g.ldo = ldo;
+    g.rot_cols = dit ? 0 : (H + KVH) * Dh; g.dt = c.dt; g.M = M; g.Mp = Mp; g.K = K; g.N = N; g.ldo = ldo;
     tok::plan_gemm(g, h->n_cu);
     std::snprintf(nd.name, sizeof(nd.name), "%s %s/%d", name, tok::tile_name(g.tile), g.splits);
     const int out_cols = epi == tok::EP_GEGLU ? N / 2 : N;
@@ -577,11 +602,37 @@ int build_tok_nodes(phx_expert* h) {
   auto layer_k = [&](int l) { return (char*)h->tk + (dit ? 0 : (size_t)l * R * kvd * 2); };
   auto layer_v = [&](int l) { return (char*)h->tv + (dit ? 0 : (size_t)l * R * kvd * 2); };
   auto qkv = [&](int k, int l, const char* name) {
-    gemm(PHX_NODE_QKV, k, l, tok::EP_QKV, h->nb, h->off_qkv[l], D, NQKV, h->qkv, HD, nullptr, name);
+    gemm(PHX_NODE_QKV, k, l, h->batched ? tok::EP_QKV_CACHE : tok::EP_QKV, h->nb, h->off_qkv[l], D, NQKV, h->qkv,
+         HD, nullptr, name);
     tok::GemmT& g = h->tnodes.back().g;
     g.kj = layer_k(l); g.vt = layer_v(l); g.lens = dit ? nullptr : h->lens; g.H = H; g.KVH = KVH; g.nj = R / 32;
+    if (h->batched) {
+      g.hd = Dh; g.req_rows = c.rows; g.Ctot = h->Ctot;
+      g.kc = (char*)h->kc + (size_t)l * h->kv_layer * 2;
+      g.vtc = (char*)h->vtc + (size_t)l * h->kv_layer * 2;
+    }
   };
   auto attention = [&](int k, int l) {
+    if (h->batched) {
+      TokNode nd{};
+      nd.kind = PHX_NODE_ATTENTION; nd.step = k; nd.layer = l; nd.op = TOP_MK_ATTN;
+      AttnArgs& at = nd.mat;
+      at.q = h->qkv; at.kc = (char*)h->kc + (size_t)l * h->kv_layer * 2;
+      at.vtc = (char*)h->vtc + (size_t)l * h->kv_layer * 2; at.lens = h->lens;
+      at.part_o = h->part_o; at.part_ml = h->part_ml;
+      at.M = c.rows; at.H = H; at.KVH = KVH; at.Dh = Dh; at.Ctot = h->Ctot; at.SMAX = h->SMAX; at.GMP = h->GMP;
+      at.scale = (float)(1.0 / std::sqrt((double)Dh));
+      name_of(nd, "attention");
+      h->tnodes.push_back(nd);
+      TokNode nc{};
+      nc.kind = PHX_NODE_ATTN_COMBINE; nc.step = k; nc.layer = l; nc.op = TOP_MK_COMBINE;
+      CombineArgs& cb = nc.mcb;
+      cb.part_o = h->part_o; cb.part_ml = h->part_ml; cb.lens = h->lens; cb.o = h->o;
+      cb.M = c.rows; cb.H = H; cb.KVH = KVH; cb.Dh = Dh; cb.SMAX = h->SMAX; cb.GMP = h->GMP;
+      name_of(nc, "attention_combine");
+      h->tnodes.push_back(nc);
+      return;
+    }
     TokNode nd{};
     nd.kind = PHX_NODE_ATTENTION; nd.step = k; nd.layer = l; nd.op = TOP_ATTN;
     tok::AttnT& a = nd.a;
@@ -614,17 +665,34 @@ int build_tok_nodes(phx_expert* h) {
     return PHX_OK;
   }
   const int NN = 2 * NL + 1;
+  // the batched plan keeps the state-width projections (K or N = state_dim, often 32) on the small-M GEMM
+  auto mk_gemm = [&](int kind, int k, const GemmPlan& p, int pro, int epi, const GemmArgs& g, uint64_t bytes,
+                     const char* name) {
+    TokNode nd{};
+    nd.kind = kind; nd.step = k; nd.layer = -1; nd.op = TOP_MK_GEMM; nd.mg = g;
+    nd.mk_nw = p.NW; nd.mk_pro = pro; nd.mk_epi = epi; nd.bytes = bytes;
+    name_of(nd, name);
+    h->tnodes.push_back(nd);
+  };
   for (int k = 0; k < c.steps; ++k) {
     const float* mod_k = h->modtab + (size_t)k * NN * 2 * D;  // per norm: scale, then shift
-    {
+    if (h->batched) {
+      GemmArgs g{};
+      g.W = (const char*)h->wt + h->off_in * 2;
+      g.KT = h->p_in.KT; g.NT = h->p_in.NT; g.KSW = h->p_in.KSW; g.rows = M;
+      g.X = h->x; g.ldx = A;
+      g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
+      g.part = h->gpart; g.counters = h->counters;
+      mk_gemm(PHX_NODE_IN_PROJ, k, h->p_in, PRO_XF32, EPI_STORE_H, g, (uint64_t)A * D * 2, "in_proj");
+    } else {
       TokNode nd{};
       nd.kind = PHX_NODE_STATE_CVT; nd.step = k; nd.layer = -1; nd.op = TOP_CVT;
       nd.src = h->x; nd.dst = h->xb; nd.cols = A;
       nd.bytes = (uint64_t)M * A * 4 + (uint64_t)Mp * A * 2;
       name_of(nd, "state_to_bf16");
       h->tnodes.push_back(nd);
+      gemm(PHX_NODE_IN_PROJ, k, -1, tok::EP_F32, h->xb, h->off_in, A, D, h->h, D, nullptr, "in_proj");
     }
-    gemm(PHX_NODE_IN_PROJ, k, -1, tok::EP_F32, h->xb, h->off_in, A, D, h->h, D, nullptr, "in_proj");
     for (int l = 0; l < NL; ++l) {
       const float* m1 = mod_k + (size_t)(2 * l) * 2 * D;
       const float* m2 = mod_k + (size_t)(2 * l + 1) * 2 * D;
@@ -640,7 +708,17 @@ int build_tok_nodes(phx_expert* h) {
     }
     const float* mf = mod_k + (size_t)(2 * NL) * 2 * D;
     norm(k, -1, 0, mf, mf + D, "rmsnorm_final");
-    gemm(PHX_NODE_OUT_EULER, k, -1, tok::EP_EULER, h->nb, h->off_out, D, A, h->x, A, nullptr, "out_proj_euler");
+    if (h->batched) {
+      GemmArgs g{};
+      g.W = (const char*)h->wt + h->off_out * 2;
+      g.KT = h->p_out.KT; g.NT = h->p_out.NT; g.KSW = h->p_out.KSW; g.rows = M;
+      g.X = h->nb; g.ldx = D; g.D = D;
+      g.part = h->gpart; g.counters = h->counters;
+      g.x = h->x; g.dt = c.dt; g.A = A;
+      mk_gemm(PHX_NODE_OUT_EULER, k, h->p_out, PRO_X, EPI_EULER, g, (uint64_t)D * A * 2, "out_proj_euler");
+    } else {
+      gemm(PHX_NODE_OUT_EULER, k, -1, tok::EP_EULER, h->nb, h->off_out, D, A, h->x, A, nullptr, "out_proj_euler");
+    }
   }
   return PHX_OK;
 }
@@ -650,9 +728,10 @@ int build_tok_nodes(phx_expert* h) {
 int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_off) {
   const phx_expert_config& c = h->cfg;
   const bool dit = c.block_kind == PHX_BLOCK_DIT;
-  const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = c.rows;
+  h->trows = c.rows * c.batch;
+  const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = h->trows;
   const int NL = c.layers, S = c.steps, E = c.time_emb_dim, C = c.prefix_capacity;
-  const int HD = H * tok::DH, kvd = KVH * tok::DH;
+  const int HD = H * c.head_dim, kvd = KVH * c.head_dim;
   const int Mp = (M + tok::ROW_PAD - 1) / tok::ROW_PAD * tok::ROW_PAD;
   h->Mp = Mp;
   int rc;
@@ -678,18 +757,41 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
       {(void**)&h->h, (size_t)Mp * D * 4, "residual rows"},
       {&h->nb, (size_t)Mp * D * 2, "normalised rows"},
       {&h->qkv, (size_t)Mp * HD * 2, "query rows"},
-      {&h->tk, (size_t)(dit ? 1 : NL) * R * kvd * 2, "key rows"},
-      {&h->tv, (size_t)(dit ? 1 : NL) * R * kvd * 2, "value fragments"},
       {&h->o, (size_t)Mp * HD * 2, "attention output rows"},
       {&h->act, (size_t)Mp * F * 2, "MLP activation rows"},
   };
-  if (!dit) {
+  if (h->batched) {
+    // the multi-kernel path's per-request caches, lengths, position table and attention partials
+    h->splits = 1;
+    const size_t cache_bytes = (size_t)NL * h->kv_layer * 2;
+    const size_t part_rows = (size_t)c.batch * KVH * h->SMAX * h->GMP;
+    bufs.push_back({&h->kc, cache_bytes, "key cache"});
+    bufs.push_back({&h->vtc, cache_bytes, "value cache"});
+    bufs.push_back({(void**)&h->x, (size_t)Mp * A * 4, "state rows"});
+    bufs.push_back({&h->xb, (size_t)Mp * A * 2, "bf16 state rows"});
+    bufs.push_back({(void**)&h->lens, (size_t)c.batch * sizeof(int), "prefix lengths"});
+    bufs.push_back({(void**)&h->rope, (size_t)M * (c.head_dim / 2) * sizeof(float2), "position table"});
+    bufs.push_back({(void**)&h->part_o, part_rows * c.head_dim * sizeof(float), "attention partials"});
+    bufs.push_back({(void**)&h->part_ml, part_rows * sizeof(float2), "attention statistics"});
+    // the small-M projections' sums of squares, split partials and counters
+    size_t gp = 1;
+    for (const GemmPlan* p : {&h->p_in, &h->p_out})
+      if (p->KSW > 1) gp = std::max(gp, (size_t)p->NT * p->KSW * h->MT * 256);
+    bufs.push_back({(void**)&h->ss, (size_t)h->NTD * h->ss_ld * sizeof(float), "sums of squares"});
+    bufs.push_back({(void**)&h->gpart, gp * sizeof(float), "split partials"});
+    bufs.push_back({(void**)&h->counters, (size_t)std::max(h->p_in.NT, h->p_out.NT) * sizeof(unsigned),
+                    "split counters"});
+  } else {
+    bufs.push_back({&h->tk, (size_t)(dit ? 1 : NL) * R * kvd * 2, "key rows"});
+    bufs.push_back({&h->tv, (size_t)(dit ? 1 : NL) * R * kvd * 2, "value fragments"});
+  }
+  if (!dit && !h->batched) {
     bufs.push_back({(void**)&h->x, (size_t)Mp * A * 4, "state rows"});
     bufs.push_back({&h->xb, (size_t)Mp * A * 2, "bf16 state rows"});
     bufs.push_back({(void**)&h->lens, sizeof(int), "prefix length"});
     bufs.push_back({(void**)&h->rope, (size_t)M * (tok::DH / 2) * sizeof(float2), "position table"});
   }
-  if (h->splits > 1) {
+  if (h->splits > 1 && !h->batched) {
     bufs.push_back({(void**)&h->po, (size_t)h->splits * M * HD * 4, "attention partials"});
     bufs.push_back({(void**)&h->pml, (size_t)h->splits * M * H * 2 * 4, "attention statistics"});
   }
@@ -749,7 +851,7 @@ struct StateRegion {
 std::vector<StateRegion> state_regions(const phx_expert* h) {
   const phx_expert_config& c = h->cfg;
   std::vector<StateRegion> r;
-  if (h->tokens) {
+  if (h->tokens && !h->batched) {
     if (c.block_kind == PHX_BLOCK_DIT) return r;  // no prefix: nothing persists between decisions
     const size_t kv = (size_t)c.layers * h->R * c.n_kv_heads * c.head_dim * 2;
     r.push_back({"key_rows", h->tk, kv});
@@ -812,7 +914,7 @@ CapsuleHeader capsule_layout(const phx_expert* h, const std::vector<StateRegion>
   hd.n_regions = (uint32_t)regs.size();
   uint64_t fp = 1469598103934665603ull;
   fp = fnv1a(fp, &h->cfg, sizeof(h->cfg));
-  const int path = h->tokens ? 2 : h->persistent ? 1 : 0;
+  const int path = h->batched ? 3 : h->tokens ? 2 : h->persistent ? 1 : 0;
   fp = fnv1a(fp, &path, sizeof(path));
   size_t off = capsule_head_bytes(h);
   for (size_t i = 0; i < regs.size(); ++i) {
@@ -1003,6 +1105,10 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
 
   h->tokens = uses_tokens(c);
   h->n_cu = prop.multiProcessorCount;
+  if (!h->tokens && !persistent_eligible(c, prop) && uses_batched(c)) {
+    h->tokens = true;
+    h->batched = true;
+  }
   if (h->tokens) {
     rc = create_tokens(h, sb, stream, off);
     if (rc) return rc;
@@ -1141,7 +1247,7 @@ int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, con
     g_err.clear();
     return PHX_OK;
   }
-  if (h->tokens) {
+  if (h->tokens && !h->batched) {
     // keys [NL][L][kvd] -> rows 0..L-1 of each layer's key rows (rows from L on are the chunk's, or
     // masked); values into the fragment order, zeros from key L on
     const size_t row = (size_t)c.n_kv_heads * c.head_dim * 2;
@@ -1201,10 +1307,13 @@ int phx_expert_node_info(const phx_expert* h, int32_t node, phx_node_info* info)
     info->layer = tn.layer;
     info->bytes = tn.bytes;
     if (tn.kind == PHX_NODE_ATTENTION) {
-      // query rows, the valid prefix keys and values, the chunk's own key and value rows, the output
+      // query rows, the valid prefix keys and values, the rows' own key and value rows, the output
       const phx_expert_config& c = h->cfg;
       const uint64_t kvd = (uint64_t)c.n_kv_heads * c.head_dim, hd = (uint64_t)c.n_heads * c.head_dim;
-      info->bytes = 2 * ((uint64_t)h->lens_host[0] * kvd * 2 + (uint64_t)c.rows * (hd + kvd) * 2);
+      uint64_t bytes = 0;
+      for (int b = 0; b < c.batch; ++b)
+        bytes += 2 * ((uint64_t)h->lens_host[(size_t)b] * kvd * 2 + (uint64_t)c.rows * (hd + kvd) * 2);
+      info->bytes = bytes;
     }
     std::snprintf(info->name, sizeof(info->name), "%s", tn.name);
     return PHX_OK;

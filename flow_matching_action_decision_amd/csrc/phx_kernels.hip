@@ -581,6 +581,8 @@ static hipError_t gemm_mt(int nw, int pro, int epi, const GemmArgs& a, hipStream
     hipLaunchKernelGGL((k_gemm<T, 4, MT, PRO_NORM, EPI_GEGLU>), grid, dim3(256), 0, s, a);
   } else if (nw == 4 && pro == PRO_NORM && epi == EPI_EULER) {
     hipLaunchKernelGGL((k_gemm<T, 4, MT, PRO_NORM, EPI_EULER>), grid, dim3(256), 0, s, a);
+  } else if (nw == 4 && pro == PRO_X && epi == EPI_EULER) {
+    hipLaunchKernelGGL((k_gemm<T, 4, MT, PRO_X, EPI_EULER>), grid, dim3(256), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -30,6 +30,9 @@ enum Epi : int {
   EP_RESID = 4,  // out f32 [rows][N] += (gate ? gate[n] : 1) * acc
   EP_EULER = 5,  // out f32 [rows][N] += dt * acc
   EP_F32 = 6,    // out f32 [rows][N] = acc
+  EP_QKV_CACHE = 7,  // as EP_QKV for head_dim hd and requests of req_rows rows: queries to out, the rows'
+                     // keys and values into the per-request caches kc [B][KVH][Ctot][hd] and vtc
+                     // [B][KVH][hd][Ctot] at slot lens[b] + i (row r = b * req_rows + i)
 };
 
 struct GemmT {
@@ -43,6 +46,9 @@ struct GemmT {
   void* vt;            // EP_QKV: values of this layer in fragment order, [KVH][R*DH]
   const int* lens;     // EP_QKV: device prefix length L (chunk row r is key L + r), nullptr for 0
   int H, KVH, nj;      // EP_QKV: query heads, kv heads, 32-key steps of kj/vt (R / 32)
+  int hd, req_rows, Ctot;  // EP_QKV_CACHE: head dim, rows per request, cache slots per (request, kv head)
+  void* kc;            // EP_QKV_CACHE: this layer's key cache
+  void* vtc;           // EP_QKV_CACHE: this layer's transposed value cache
   float dt;            // EP_EULER
   int M, Mp, K, N;     // real rows, padded rows, reduction length, output columns (tile order)
   int ldo;             // output row stride in elements

@@ -184,6 +184,38 @@ __device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const 
       vt[vt_index(kvh, g.nj, t, j + DH / 2)] = (bf16)y2;
       vt[vt_index(kvh, g.nj, t, j + DH / 2 + 1)] = (bf16)y3;
     }
+  } else if constexpr (EPI == EP_QKV_CACHE) {
+    // tile order of a head of hd dims: dims j, j + 1, j + hd/2, j + hd/2 + 1, j = 8 (nt % (hd/16)) + 2 gq
+    const int tph = g.hd >> 4, half = g.hd >> 1;
+    const int hh = nt / tph, j = 8 * (nt - hh * tph) + 2 * gq;
+    float y0 = v[0], y1 = v[1], y2 = v[2], y3 = v[3];
+    if (hh < g.H + g.KVH) {
+      const float2 a = g.rope[(size_t)row * half + j];
+      const float2 b = g.rope[(size_t)row * half + j + 1];
+      y0 = v[0] * a.x - v[2] * a.y;
+      y2 = v[2] * a.x + v[0] * a.y;
+      y1 = v[1] * b.x - v[3] * b.y;
+      y3 = v[3] * b.x + v[1] * b.y;
+    }
+    const int req = row / g.req_rows, i = row - req * g.req_rows;
+    if (hh < g.H) {
+      bf16* o = (bf16*)g.out + (size_t)row * g.ldo + hh * g.hd + j;
+      *(unsigned*)o = pack2(y0, y1);
+      *(unsigned*)(o + half) = pack2(y2, y3);
+    } else {
+      const int slot = g.lens[req] + i;
+      if (hh < g.H + g.KVH) {
+        bf16* k = (bf16*)g.kc + (((size_t)req * g.KVH + (hh - g.H)) * g.Ctot + slot) * g.hd + j;
+        *(unsigned*)k = pack2(y0, y1);
+        *(unsigned*)(k + half) = pack2(y2, y3);
+      } else {
+        bf16* vt = (bf16*)g.vtc + ((size_t)req * g.KVH + (hh - g.H - g.KVH)) * g.hd * g.Ctot + slot;
+        vt[(size_t)j * g.Ctot] = (bf16)y0;
+        vt[(size_t)(j + 1) * g.Ctot] = (bf16)y1;
+        vt[(size_t)(j + half) * g.Ctot] = (bf16)y2;
+        vt[(size_t)(j + half + 1) * g.Ctot] = (bf16)y3;
+      }
+    }
   } else if constexpr (EPI == EP_GEGLU) {
     // features 8 nt + 2 gq + {0, 1}: gate in v[0], v[1], up in v[2], v[3]
     const int f = 8 * nt + 2 * gq;
@@ -486,6 +518,7 @@ hipError_t prepare_gemm() {
   if ((e = allow_lds_e<EP_GELU>()) != hipSuccess) return e;
   if ((e = allow_lds_e<EP_RESID>()) != hipSuccess) return e;
   if ((e = allow_lds_e<EP_EULER>()) != hipSuccess) return e;
+  if ((e = allow_lds_e<EP_QKV_CACHE>()) != hipSuccess) return e;
   return allow_lds_e<EP_F32>();
 }
 
@@ -530,6 +563,7 @@ hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
     case EP_RESID: return launch_tgemm_e<EP_RESID>(g, s);
     case EP_EULER: return launch_tgemm_e<EP_EULER>(g, s);
     case EP_F32: return launch_tgemm_e<EP_F32>(g, s);
+    case EP_QKV_CACHE: return launch_tgemm_e<EP_QKV_CACHE>(g, s);
   }
   return hipErrorInvalidValue;
 }

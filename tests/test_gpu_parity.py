@@ -46,6 +46,21 @@ def test_ragged_batch():
     _case(small_cfg(batch=4, prefix_lens=[0, 17, 100, 54]))
 
 
+@pytest.mark.parametrize("shape", [(4, 1, 64, 256), (4, 2, 128, 256), (8, 1, 256, 512)],
+                         ids=["mqa64", "gqa128", "mqa256"])
+def test_batched_plan(shape):
+    """8 requests x 10 rows (80 rows, bf16): the batched plan (large-token
+    GEMMs over all rows, per-request caches, batched attention), ragged
+    prefixes.  Kernel count identifies the plan: per step the input
+    projection, per layer 8 launches, the final norm and velocity projection."""
+    H, KVH, Dh, D = shape
+    cfg = small_cfg(batch=8, prefix_lens=[0, 17, 100, 54, 64, 1, 99, 33], n_heads=H, n_kv_heads=KVH, head_dim=Dh,
+                    width=D)
+    m, inp, out = _case(cfg)
+    _, nk = gpu_decide(cfg, inp)
+    assert nk == cfg["steps"] * (3 + 8 * cfg["layers"])
+
+
 def test_ragged_batch_f32():
     _case(small_cfg(batch=3, prefix_lens=[100, 3, 64], dtype="f32"))
 
