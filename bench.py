@@ -232,13 +232,18 @@ def main():
     # stream it runs on
     dom = ex.time_dominant_kernel(args.kernel_reps)
     batch = name != WORKLOAD  # the rollout batch runs the multi-kernel graph
-    kernel_hash = kernel_source_hash(("phx_kernels.hip", "phx_internal.h") if batch else DECISION_KERNEL_SOURCES)
+    kernel_hash = kernel_source_hash(("phx_kernels.hip", "phx_internal.h") + TOKEN_KERNEL_SOURCES if batch
+                                     else DECISION_KERNEL_SOURCES)
     traffic = None if batch else measured_traffic(kernel_hash)
     achieved = dom["bytes_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom["name"], "bytes_per_launch": dom["bytes_per_launch"],
                 "us_per_launch": round(dom["ms_per_launch"] * 1e3, 3), "kernel_hash": kernel_hash}
+
+    # execution-state capsule: snapshot, restore and fork of the declared state
+    # regions, each timed with HIP events on the handle's stream
+    capsule = capsule_timing(ex, Expert, cfg, inp, stream)
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -278,10 +283,38 @@ def main():
         "algorithmic_bytes_per_decision": ab["per_decision"],
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "kernels_per_decision": nk,
+        "capsule": capsule,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def capsule_timing(ex, Expert, cfg: dict, inp: dict, stream, reps: int = 20) -> dict:
+    """Average ms of a capsule snapshot, a restore into the same handle and a
+    fork into a second handle of the same plan (restore on a fresh handle)."""
+    import torch
+    cap = ex.capsule_save()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(sum(a.elapsed_time(b) for a, b in ev) / reps)
+
+    snap = timed(lambda: ex.capsule_save(cap))
+    rest = timed(lambda: ex.capsule_restore(cap))
+    other = Expert(cfg, inp["weights"], inp["weights_bits"])
+    try:
+        fork = timed(lambda: other.capsule_restore(cap))
+    finally:
+        other.close()
+    return {"bytes": int(cap.numel()), "regions": [r["name"] for r in ex.capsule_regions()],
+            "snapshot_ms": round(snap, 4), "restore_ms": round(rest, 4), "fork_ms": round(fork, 4)}
 
 
 def bench_tokens(args):
