@@ -75,6 +75,11 @@ def load(path: str = LIB_PATH):
     lib.orc_attention.restype = ctypes.c_double
     lib.orc_decide.argtypes = [ctypes.POINTER(OrcConfig), _FP, _FP, _FP, _IP, _FP, _DP, _DP, _DP]
     lib.orc_decide.restype = ctypes.c_int
+    lib.orc_decide_at.argtypes = [ctypes.POINTER(OrcConfig), _FP, _FP, _FP, _IP, _IP, _FP, _DP, _DP, _DP]
+    lib.orc_decide_at.restype = ctypes.c_int
+    lib.orc_commit.argtypes = [ctypes.POINTER(OrcConfig), _FP, _FP, _FP, _IP, _IP, _FP, ctypes.c_double, _DP, _DP,
+                               _DP]
+    lib.orc_commit.restype = ctypes.c_int
     lib.orc_last_softmax_dev.restype = ctypes.c_double
     lib.orc_ada_layernorm.argtypes = [ctypes.c_int, ctypes.c_int, _DP, _DP, _DP, ctypes.c_double, _DP]
     lib.orc_dit.argtypes = [ctypes.POINTER(OrcConfig), _FP, _FP, _DP, _DP]
@@ -187,9 +192,10 @@ def attention(q, ka, va, Kp, Vp, n_heads: int, n_kv_heads: int, head_dim: int, l
 
 
 def decide(cfg: dict, weights: np.ndarray, kv_k, kv_v, lens, noise, trace: bool = False,
-           velocity: bool = False, lib=None) -> dict:
+           velocity: bool = False, lib=None, pos0=None) -> dict:
     """Run one decision.  weights: float32 blob in the documented order.
     kv_k/kv_v: float32 [B][NL][C][KVH*Dh] (may be None when C == 0).
+    pos0: optional [B] base positions (rows of request b at pos0[b] + lens[b] + i).
     Returns {"actions": [B][M][A] float64, "trace": ..., "velocity": ...,
     "softmax_dev": float}."""
     lib = lib or load()
@@ -209,13 +215,49 @@ def decide(cfg: dict, weights: np.ndarray, kv_k, kv_v, lens, noise, trace: bool 
     actions = np.zeros((B, M, A), dtype=np.float64)
     tr = np.zeros((S, NL + 1, B * M, D), dtype=np.float64) if trace else None
     vel = np.zeros((S, B * M, A), dtype=np.float64) if velocity else None
-    rc = lib.orc_decide(ctypes.byref(c), pw, pk, pv, lens_a.ctypes.data_as(_IP), pn,
-                        actions.ctypes.data_as(_DP),
-                        tr.ctypes.data_as(_DP) if tr is not None else None,
-                        vel.ctypes.data_as(_DP) if vel is not None else None)
+    if pos0 is None:
+        rc = lib.orc_decide(ctypes.byref(c), pw, pk, pv, lens_a.ctypes.data_as(_IP), pn,
+                            actions.ctypes.data_as(_DP),
+                            tr.ctypes.data_as(_DP) if tr is not None else None,
+                            vel.ctypes.data_as(_DP) if vel is not None else None)
+    else:
+        pos_a = np.ascontiguousarray(pos0, dtype=np.int32)
+        rc = lib.orc_decide_at(ctypes.byref(c), pw, pk, pv, lens_a.ctypes.data_as(_IP), pos_a.ctypes.data_as(_IP),
+                               pn, actions.ctypes.data_as(_DP),
+                               tr.ctypes.data_as(_DP) if tr is not None else None,
+                               vel.ctypes.data_as(_DP) if vel is not None else None)
     if rc != 0:
         raise ValueError(f"orc_decide rejected its arguments (rc={rc})")
     return {"actions": actions, "trace": tr, "velocity": vel, "softmax_dev": lib.orc_last_softmax_dev()}
+
+
+def commit(cfg: dict, weights: np.ndarray, kv_k, kv_v, lens, x, tau: float, pos0=None, trace: bool = False,
+           lib=None) -> dict:
+    """Commit a decided chunk x [B][M][A] into the history: one pass of the
+    layer stack at flow time tau.  Returns {"k", "v": [B][NL][M][KVH*Dh]
+    float64 (keys after RoPE), "trace": [1][NL+1][B*M][D] or None}."""
+    lib = lib or load()
+    c = make_config(cfg)
+    weights, pw = _f(weights)
+    B, M, NL, D = cfg["batch"], cfg["rows"], cfg["layers"], cfg["width"]
+    kvd = cfg["n_kv_heads"] * cfg["head_dim"]
+    if kv_k is not None:
+        kv_k, pk = _f(kv_k)
+        kv_v, pv = _f(kv_v)
+    else:
+        pk = pv = None
+    lens_a = np.ascontiguousarray(lens, dtype=np.int32)
+    pos_a = np.ascontiguousarray(np.zeros(B) if pos0 is None else pos0, dtype=np.int32)
+    x, px = _f(x)
+    k = np.zeros((B, NL, M, kvd), dtype=np.float64)
+    v = np.zeros((B, NL, M, kvd), dtype=np.float64)
+    tr = np.zeros((1, NL + 1, B * M, D), dtype=np.float64) if trace else None
+    rc = lib.orc_commit(ctypes.byref(c), pw, pk, pv, lens_a.ctypes.data_as(_IP), pos_a.ctypes.data_as(_IP), px,
+                        float(tau), k.ctypes.data_as(_DP), v.ctypes.data_as(_DP),
+                        tr.ctypes.data_as(_DP) if tr is not None else None)
+    if rc != 0:
+        raise ValueError(f"orc_commit rejected its arguments (rc={rc})")
+    return {"k": k, "v": v, "trace": tr}
 
 
 def ada_layernorm(h: np.ndarray, scale: np.ndarray, shift: np.ndarray, eps: float, lib=None) -> np.ndarray:

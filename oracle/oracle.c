@@ -184,8 +184,12 @@ static int check_cfg(const orc_config* c) {
   return 0;
 }
 
-int orc_decide(const orc_config* c, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
-               const float* noise, double* actions, double* trace, double* velocity) {
+/* The decision, with the row positions of request b starting at pos0[b] + lens[b]
+   (pos0 NULL: at lens[b]) and, when kout/vout are given, every layer's keys
+   (after RoPE) and values of the rows captured as [B][NL][M][KVH*Dh]. */
+static int decide_impl(const orc_config* c, const float* weights, const float* kv_k, const float* kv_v,
+                       const int* lens, const int* pos0, const float* noise, double* actions, double* trace,
+                       double* velocity, double* kout, double* vout) {
   if (check_cfg(c) || !weights || !noise || !actions || !lens) return -1;
   const int NL = c->layers, D = c->width, H = c->n_heads, Dh = c->head_dim, KVH = c->n_kv_heads;
   const int F = c->mlp_hidden, A = c->state_dim, M = c->rows, B = c->batch, C = c->capacity, S = c->steps;
@@ -247,15 +251,20 @@ int orc_decide(const orc_config* c, const float* weights, const float* kv_k, con
       orc_matmul(BM, D, nqkv, n, W_qkv, qkv);
       for (int b = 0; b < B; ++b) {
         int L = lens[b];
+        const int base = pos0 ? pos0[b] : 0;
         for (int m = 0; m < M; ++m) {
           const double* src = qkv + (size_t)(b * M + m) * nqkv;
           memcpy(q + (size_t)m * hd, src, sizeof(double) * hd);
           memcpy(ka + (size_t)m * kvd, src + hd, sizeof(double) * kvd);
           memcpy(va + (size_t)m * kvd, src + hd + kvd, sizeof(double) * kvd);
-          pos[m] = L + m;
+          pos[m] = base + L + m;
         }
         orc_rope(M, H, Dh, pos, c->rope_base, q);
         orc_rope(M, KVH, Dh, pos, c->rope_base, ka);
+        if (kout && vout) {
+          memcpy(kout + (((size_t)b * NL + l) * M) * kvd, ka, sizeof(double) * (size_t)M * kvd);
+          memcpy(vout + (((size_t)b * NL + l) * M) * kvd, va, sizeof(double) * (size_t)M * kvd);
+        }
         const float* Kp = kv_k ? kv_k + ((size_t)b * NL + l) * (size_t)C * kvd : NULL;
         const float* Vp = kv_v ? kv_v + ((size_t)b * NL + l) * (size_t)C * kvd : NULL;
         double dev = orc_attention(M, H, KVH, Dh, L, q, ka, va, Kp, Vp, (size_t)kvd, o + (size_t)b * M * hd);
@@ -289,6 +298,35 @@ int orc_decide(const orc_config* c, const float* weights, const float* kv_k, con
   free(x); free(h); free(n); free(qkv); free(q); free(ka); free(va); free(o); free(proj);
   free(gu); free(act); free(e); free(mod); free(pos);
   return 0;
+}
+
+int orc_decide(const orc_config* c, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
+               const float* noise, double* actions, double* trace, double* velocity) {
+  return decide_impl(c, weights, kv_k, kv_v, lens, NULL, noise, actions, trace, velocity, NULL, NULL);
+}
+
+int orc_decide_at(const orc_config* c, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
+                  const int* pos0, const float* noise, double* actions, double* trace, double* velocity) {
+  return decide_impl(c, weights, kv_k, kv_v, lens, pos0, noise, actions, trace, velocity, NULL, NULL);
+}
+
+/* The history update of an autoregressive chunk policy ("FlashRT-PAI" section
+ * 2.1, Figure 1b: the cache over earlier chunks persists from one decision to
+ * the next): one pass of the layer stack over the decided chunk x at flow
+ * time tau -- the same pass a decision step makes, attending to the L cached
+ * rows and the chunk itself -- whose per-layer keys and values of the chunk
+ * rows are what the cache gains. */
+int orc_commit(const orc_config* c, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
+               const int* pos0, const float* x, double tau, double* kout, double* vout, double* trace) {
+  if (!c || !x || !kout || !vout) return -1;
+  orc_config one = *c;
+  one.steps = 1;
+  one.tau0 = tau;
+  double* scratch = (double*)malloc(sizeof(double) * (size_t)c->batch * c->rows * c->state_dim);
+  if (!scratch) return -1;
+  int rc = decide_impl(&one, weights, kv_k, kv_v, lens, pos0, x, scratch, trace, NULL, kout, vout);
+  free(scratch);
+  return rc;
 }
 
 /* ------------------------------------------------------------------------

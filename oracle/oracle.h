@@ -100,6 +100,23 @@ double orc_attention(int M, int H, int KVH, int Dh, int L, const double* q, cons
 int orc_decide(const orc_config* cfg, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
                const float* noise, double* actions, double* trace, double* velocity);
 
+/* orc_decide with the rows of request b at positions pos0[b] + lens[b] + i
+   (the window of a history cache that has dropped its oldest rows keeps
+   absolute positions); pos0 NULL is orc_decide. */
+int orc_decide_at(const orc_config* cfg, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
+                  const int* pos0, const float* noise, double* actions, double* trace, double* velocity);
+
+/*
+ * Commit of a decided chunk into a history cache: one pass of the layer
+ * stack over x [B][M][A] at flow time tau, the rows at positions pos0[b] +
+ * lens[b] + i, attending to the lens[b] cached rows and the chunk.  kout and
+ * vout receive every layer's keys (after RoPE) and values of the chunk rows,
+ * [B][NL][M][KVH*Dh]; trace (optional) the residual stream as for
+ * orc_decide with one step.  Returns 0, or -1 on a bad argument.
+ */
+int orc_commit(const orc_config* cfg, const float* weights, const float* kv_k, const float* kv_v, const int* lens,
+               const int* pos0, const float* x, double tau, double* kout, double* vout, double* trace);
+
 /* Largest |sum(p) - 1| seen by any softmax row of the last orc_decide or
    orc_dit call. */
 double orc_last_softmax_dev(void);

@@ -166,10 +166,12 @@ def tiny_cfg(**kw):
     return cfg
 
 
-def torch_decide(cfg, inp):
+def torch_decide(cfg, inp, pos0=None, capture=None):
     """Brute force: the decision composed from torch double-precision
     primitives (sin/cos, matmul, rms_norm, complex rotation, scaled dot
-    product attention, tanh GELU)."""
+    product attention, tanh GELU).  pos0: base positions per request;
+    capture: a dict that receives every layer's rotated keys and values of
+    the rows of the last step, "k"/"v" [B][NL][M][KVH*Dh]."""
     W = inp["weights"]
     NL, D, H, Dh, KVH = cfg["layers"], cfg["width"], cfg["n_heads"], cfg["head_dim"], cfg["n_kv_heads"]
     F_, A, M, B, S, E = cfg["mlp_hidden"], cfg["state_dim"], cfg["rows"], cfg["batch"], cfg["steps"], cfg["time_emb_dim"]
@@ -202,10 +204,14 @@ def torch_decide(cfg, inp):
             for b in range(B):
                 L = int(inp["lens"][b])
                 rows = slice(b * M, (b + 1) * M)
-                pos = torch.arange(L, L + M)
+                base = 0 if pos0 is None else int(pos0[b])
+                pos = torch.arange(base + L, base + L + M)
                 q = rot(qkv[rows, :H * Dh], pos, H)
                 ka = rot(qkv[rows, H * Dh:(H + KVH) * Dh], pos, KVH)
                 va = qkv[rows, (H + KVH) * Dh:]
+                if capture is not None:
+                    capture.setdefault("k", np.zeros((B, NL, M, KVH * Dh)))[b, l] = ka.numpy()
+                    capture.setdefault("v", np.zeros((B, NL, M, KVH * Dh)))[b, l] = va.numpy()
                 Kp = torch.tensor(inp["kv_k"][b, l, :L].astype(np.float64))
                 Vp = torch.tensor(inp["kv_v"][b, l, :L].astype(np.float64))
                 kf = torch.cat([Kp, ka]).reshape(L + M, KVH, Dh).permute(1, 0, 2).repeat_interleave(H // KVH, 0)
@@ -234,6 +240,32 @@ def pin_decide_brute_force(lib):
         out = _run(cfg, inp, lib)
         _close(out["actions"], torch_decide(cfg, inp), tol=1e-9, what=f"decision vs torch composition {kw}")
         assert out["softmax_dev"] < 1e-12
+
+
+def pin_decide_at_brute_force(lib):
+    """Rows at shifted base positions (the window of a history cache)."""
+    for kw in [dict(), dict(n_heads=4, n_kv_heads=2, prefix_lens=[3, 1])]:
+        cfg = tiny_cfg(**kw)
+        inp = phx_inputs.make_inputs(cfg, seed=5)
+        pos0 = [4, 9]
+        out = oracle.decide(cfg, inp["weights"], inp["kv_k"], inp["kv_v"], inp["lens"], inp["noise"], lib=lib,
+                            pos0=pos0)
+        _close(out["actions"], torch_decide(cfg, inp, pos0=pos0), tol=1e-9, what=f"decision at base positions {kw}")
+
+
+def pin_commit_brute_force(lib):
+    """Commit of a chunk: the per-layer keys (after RoPE) and values of the
+    chunk rows from one pass at flow time tau, against the torch composition
+    run as a one-step decision at tau that records them."""
+    cfg = tiny_cfg()
+    inp = phx_inputs.make_inputs(cfg, seed=6)
+    x = np.random.default_rng(6).standard_normal((cfg["batch"], cfg["rows"], cfg["state_dim"])).astype(np.float32)
+    tau, pos0 = 0.25, [2, 7]
+    got = oracle.commit(cfg, inp["weights"], inp["kv_k"], inp["kv_v"], inp["lens"], x, tau, pos0=pos0, lib=lib)
+    cap = {}
+    torch_decide(dict(cfg, steps=1, tau0=tau), dict(inp, noise=x), pos0=pos0, capture=cap)
+    _close(got["k"], cap["k"], tol=1e-9, what="committed keys vs torch composition")
+    _close(got["v"], cap["v"], tol=1e-9, what="committed values vs torch composition")
 
 
 def pin_decide_invariants(lib):
@@ -404,7 +436,8 @@ def pin_dit_invariants(lib):
 
 
 ALL_PINS = [pin_time_embedding, pin_modulation, pin_matmul, pin_ada_rmsnorm, pin_rope, pin_gelu, pin_attention,
-            pin_decide_brute_force, pin_decide_invariants, pin_ada_layernorm, pin_dit_brute_force, pin_dit_invariants]
+            pin_decide_brute_force, pin_decide_invariants, pin_ada_layernorm, pin_dit_brute_force, pin_dit_invariants,
+            pin_decide_at_brute_force, pin_commit_brute_force]
 
 
 def run_all(lib):

@@ -36,7 +36,12 @@ MUTANTS = [
     ("attention: wrong kv head mapping", "int m = mh / H, hh = mh % H, g = hh / group;",
      "int m = mh / H, hh = mh % H, g = hh % KVH;"),
     ("attention: action keys left out", "int T = L + M;", "int T = L;"),
-    ("decide: action position offset dropped", "pos[m] = L + m;", "pos[m] = m;"),
+    ("decide: action position offset dropped", "pos[m] = base + L + m;", "pos[m] = base + m;"),
+    ("decide: position base dropped", "pos[m] = base + L + m;", "pos[m] = L + m;"),
+    ("commit: values captured as keys",
+     "memcpy(vout + (((size_t)b * NL + l) * M) * kvd, va,", "memcpy(vout + (((size_t)b * NL + l) * M) * kvd, ka,"),
+    ("commit: nothing captured", "        if (kout && vout) {", "        if (0) {"),
+    ("commit: flow time ignored", "  one.tau0 = tau;", "  one.tau0 = c->tau0;"),
     ("decide: Euler sign", "x[i] += c->dt * proj[i];", "x[i] -= c->dt * proj[i];"),
     ("decide: tau schedule sign", "double tau = c->tau0 + (double)k * c->dt;", "double tau = c->tau0 - (double)k * c->dt;"),
     ("decide: gate and up swapped", "act[(size_t)r * F + f] = orc_gelu_tanh(g) * u;",
