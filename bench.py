@@ -381,6 +381,27 @@ def bench_tokens(args):
                 "kernel_hash": kernel_source_hash(TOKEN_KERNEL_SOURCES)}
     res = out.cpu().numpy()
     assert np.all(np.isfinite(res)), "non-finite output"
+    history = None
+    if not dit:
+        # history update: commit the decided chunk into the cache (event-timed on the stream); the
+        # handle's state is restored from a capsule afterwards
+        cap = ex.capsule_save()
+        reps = 8
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            ex.commit_chunk(out[0])
+            b.record(stream)
+        torch.cuda.synchronize()
+        cm = [a.elapsed_time(b) for a, b in ev]
+        ex.capsule_restore(cap)
+        torch.cuda.synchronize()
+        history = {"commit_ms": round(float(np.mean(cm)), 4), "commits": reps,
+                   "rows_per_commit": cfg["rows"], "window": cfg["capacity"],
+                   "history_rows": f"{int(phx_inputs.prefix_lengths(cfg)[0])} -> "
+                                   f"{min(cfg['capacity'], int(phx_inputs.prefix_lengths(cfg)[0]) + reps * cfg['rows'])}"}
+        del cap
     nk = ex.kernels_per_decision()
     del keep
     ex.close()
@@ -407,7 +428,7 @@ def bench_tokens(args):
         "flops_per_decision": fl["flops_per_decision"], "tflops": round(tflops, 1),
         "mfma_frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "algorithmic_bytes_per_decision": fl["bytes_per_decision"], "hbm_gbs": round(hbm, 1),
-        "kernels_per_decision": nk, "roofline": roofline, "cpu_baseline": cpu,
+        "kernels_per_decision": nk, "history_update": history, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

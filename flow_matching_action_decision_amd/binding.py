@@ -31,7 +31,7 @@ EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_exper
             "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_destroy", "phx_last_error",
             "phx_expert_kernels_per_decision", "phx_expert_node_info", "phx_expert_launch_node",
             "phx_expert_status", "phx_expert_timeline", "phx_expert_capsule_bytes", "phx_expert_capsule_regions",
-            "phx_expert_capsule_save", "phx_expert_capsule_restore")
+            "phx_expert_capsule_save", "phx_expert_capsule_restore", "phx_expert_commit_chunk")
 
 NODE_KINDS = {1: "in_proj", 2: "norm_qkv_rope", 3: "attention", 4: "attention_combine", 5: "out_proj_resid",
               6: "norm_gateup_geglu", 7: "down_proj_resid", 8: "norm_out_proj_euler", 9: "decision_kernel",
@@ -99,6 +99,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                ctypes.POINTER(ctypes.c_int32)]
     lib.phx_expert_capsule_save.argtypes = [P, P, ctypes.c_size_t, P]
     lib.phx_expert_capsule_restore.argtypes = [P, P, ctypes.c_size_t, P]
+    lib.phx_expert_commit_chunk.argtypes = [P, P, P]
     _lib = lib
     return lib
 
@@ -218,3 +219,7 @@ def phx_expert_capsule_save(h: int, capsule: int, nbytes: int, stream: int = 0):
 def phx_expert_capsule_restore(h: int, capsule: int, nbytes: int, stream: int = 0):
     _check(load_library().phx_expert_capsule_restore(ctypes.c_void_p(h), ctypes.c_void_p(capsule), nbytes,
                                                      ctypes.c_void_p(stream)))
+
+
+def phx_expert_commit_chunk(h: int, chunk: int, stream: int = 0):
+    _check(load_library().phx_expert_commit_chunk(ctypes.c_void_p(h), ctypes.c_void_p(chunk), ctypes.c_void_p(stream)))

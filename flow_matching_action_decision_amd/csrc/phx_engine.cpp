@@ -165,6 +165,14 @@ struct phx_expert {
   int splits = 1;             // attention key splits
   int n_cu = 0;               // compute units of the device
   float* tpart = nullptr;     // GEMM split partials of the large-token plan
+  // history update of the chunk plan: the commit pass, its graph, the window's position base and
+  // staging for the window shift
+  std::vector<TokNode> cnodes;
+  hipGraph_t cgraph = nullptr;
+  hipGraphExec_t cexec = nullptr;
+  int pos_base = 0;
+  void* tk_tmp = nullptr;
+  void* tv_tmp = nullptr;
   // execution-state capsules: a pinned header staging area and the event of its last copy
   void* cap_host = nullptr;
   size_t cap_host_bytes = 0;
@@ -192,6 +200,8 @@ void release(phx_expert* h) {
   if (h->cap_host) (void)hipHostFree(h->cap_host);
   if (h->exec) (void)hipGraphExecDestroy(h->exec);
   if (h->graph) (void)hipGraphDestroy(h->graph);
+  if (h->cexec) (void)hipGraphExecDestroy(h->cexec);
+  if (h->cgraph) (void)hipGraphDestroy(h->cgraph);
   for (void* p : h->allocs) (void)hipFree(p);
   if (h->cap) (void)hipStreamDestroy(h->cap);
   delete h;
@@ -564,7 +574,7 @@ int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s) {
 // projection with the Euler update.  DiT-style block: per block LayerNorm
 // with shift and scale, QKV, attention over the tokens, gated out-projection
 // residual, LayerNorm, up with GELU, gated down-projection residual.
-int build_tok_nodes(phx_expert* h) {
+int build_tok_nodes(phx_expert* h, bool commit = false) {
   const phx_expert_config& c = h->cfg;
   const bool dit = c.block_kind == PHX_BLOCK_DIT;
   const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = h->trows;
@@ -665,6 +675,34 @@ int build_tok_nodes(phx_expert* h) {
     return PHX_OK;
   }
   const int NN = 2 * NL + 1;
+  if (commit) {
+    // the history update: one pass of the layer stack over the committed chunk at the end flow time
+    // (modulation row S); each layer's QKV writes the chunk's keys and values after the L cached rows,
+    // and the last layer needs nothing after its QKV
+    const int k = c.steps;
+    const float* mod_k = h->modtab + (size_t)k * NN * 2 * D;
+    TokNode nd{};
+    nd.kind = PHX_NODE_STATE_CVT; nd.step = k; nd.layer = -1; nd.op = TOP_CVT;
+    nd.src = h->x; nd.dst = h->xb; nd.cols = A;
+    name_of(nd, "state_to_bf16");
+    h->tnodes.push_back(nd);
+    gemm(PHX_NODE_IN_PROJ, k, -1, tok::EP_F32, h->xb, h->off_in, A, D, h->h, D, nullptr, "in_proj");
+    for (int l = 0; l < NL; ++l) {
+      const float* m1 = mod_k + (size_t)(2 * l) * 2 * D;
+      const float* m2 = mod_k + (size_t)(2 * l + 1) * 2 * D;
+      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn");
+      qkv(k, l, "qkv_rope");
+      if (l + 1 == NL) break;
+      attention(k, l);
+      gemm(PHX_NODE_OUT_PROJ_RESID, k, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, nullptr,
+           "out_proj_resid");
+      norm(k, l, 0, m2, m2 + D, "rmsnorm_mlp");
+      gemm(PHX_NODE_GATEUP, k, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu");
+      gemm(PHX_NODE_DOWN_PROJ_RESID, k, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, nullptr,
+           "down_proj_resid");
+    }
+    return PHX_OK;
+  }
   // the batched plan keeps the state-width projections (K or N = state_dim, often 32) on the small-M GEMM
   auto mk_gemm = [&](int kind, int k, const GemmPlan& p, int pro, int epi, const GemmArgs& g, uint64_t bytes,
                      const char* name) {
@@ -723,6 +761,24 @@ int build_tok_nodes(phx_expert* h) {
   return PHX_OK;
 }
 
+// Captures a node list into a graph on the handle's capture stream.
+int capture_tok(phx_expert* h, const std::vector<TokNode>& list, hipGraph_t* graph, hipGraphExec_t* exec) {
+  PHX_HIP(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+  int rc = PHX_OK;
+  for (const TokNode& nd : list)
+    if ((rc = launch_tok(h, nd, h->cap))) break;
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(h->cap, &g);
+  if (rc) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  if (e != hipSuccess) return fail(PHX_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+  *graph = g;
+  PHX_HIP(hipGraphInstantiate(exec, g, nullptr, nullptr, 0));
+  return PHX_OK;
+}
+
 // Set-up of the large-token plan after the weights are tiled: modulation
 // table, state and working rows, the prefix cache, and the captured graph.
 int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_off) {
@@ -736,7 +792,8 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   h->Mp = Mp;
   int rc;
   // modulation: decoder [S][2NL+1][2D] (scale | shift per norm); DiT [NL][6D] at tau0
-  const int MS = dit ? 1 : S, NN = dit ? NL : 2 * NL + 1, MW = dit ? 6 * D : 2 * D;
+  // (the decoder gets one more step row, at the end flow time tau0 + S dt, for the history update)
+  const int MS = dit ? 1 : S + 1, NN = dit ? NL : 2 * NL + 1, MW = dit ? 6 * D : 2 * D;
   void* etab = nullptr;
   if ((rc = alloc(h, &etab, (size_t)MS * E * sizeof(double), "time embedding"))) return rc;
   if ((rc = alloc(h, (void**)&h->modtab, (size_t)MS * NN * MW * sizeof(float), "modulation table"))) return rc;
@@ -807,32 +864,27 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
       break;
     }
 
+  if (!dit && !h->batched) {
+    if ((rc = build_tok_nodes(h, true))) return rc;
+    h->cnodes.swap(h->tnodes);
+  }
   if ((rc = build_tok_nodes(h))) return rc;
   h->nodes = (int)h->tnodes.size();
   size_t part = 0;
-  for (const TokNode& nd : h->tnodes)
-    if (nd.op == TOP_GEMM) part = std::max(part, tok::gemm_part_elems(nd.g));
+  for (const std::vector<TokNode>* list : {&h->tnodes, &h->cnodes})
+    for (const TokNode& nd : *list)
+      if (nd.op == TOP_GEMM) part = std::max(part, tok::gemm_part_elems(nd.g));
   if (part) {
     if ((rc = alloc(h, (void**)&h->tpart, part * sizeof(float), "GEMM split partials"))) return rc;
-    for (TokNode& nd : h->tnodes)
-      if (nd.op == TOP_GEMM) nd.g.part = h->tpart;
+    for (std::vector<TokNode>* list : {&h->tnodes, &h->cnodes})
+      for (TokNode& nd : *list)
+        if (nd.op == TOP_GEMM) nd.g.part = h->tpart;
   }
   PHX_HIP(tok::prepare_gemm());
   PHX_HIP(tok::prepare_attention());
   if (!(c.flags & PHX_FLAG_NO_GRAPH)) {
-    PHX_HIP(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
-    rc = PHX_OK;
-    for (const TokNode& nd : h->tnodes)
-      if ((rc = launch_tok(h, nd, h->cap))) break;
-    hipGraph_t g = nullptr;
-    hipError_t e = hipStreamEndCapture(h->cap, &g);
-    if (rc) {
-      if (g) (void)hipGraphDestroy(g);
-      return rc;
-    }
-    if (e != hipSuccess) return fail(PHX_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
-    h->graph = g;
-    PHX_HIP(hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0));
+    if ((rc = capture_tok(h, h->tnodes, &h->graph, &h->exec))) return rc;
+    if (!h->cnodes.empty() && (rc = capture_tok(h, h->cnodes, &h->cgraph, &h->cexec))) return rc;
   }
   return PHX_OK;
 }
@@ -882,8 +934,8 @@ struct CapsuleEntry {
   uint64_t bytes;
 };
 
-// Capsule layout: this header, then per request (prefix length, loaded flag)
-// as int32 pairs, then every region at a 256-byte aligned offset.
+// Capsule layout: this header, then per request (prefix length, loaded flag,
+// position base) as int32 triples, then every region at a 256-byte aligned offset.
 struct CapsuleHeader {
   uint32_t magic, version;
   uint64_t fingerprint;  // plan: configuration, execution path, region sizes
@@ -902,7 +954,7 @@ uint64_t fnv1a(uint64_t h, const void* p, size_t n) {
 }
 
 size_t capsule_head_bytes(const phx_expert* h) {
-  return align_up(sizeof(CapsuleHeader) + (size_t)h->cfg.batch * 2 * sizeof(int32_t), 256);
+  return align_up(sizeof(CapsuleHeader) + (size_t)h->cfg.batch * 3 * sizeof(int32_t), 256);
 }
 
 // header of this handle's capsule (host state included)
@@ -1264,6 +1316,51 @@ int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, con
   PHX_HIP(launch_position_table(h->lens, h->rope, request, prefix_len, c.rows, c.head_dim, (double)c.rope_base, s));
   h->loaded[request] = 1;
   h->lens_host[request] = prefix_len;
+  if (request == 0) h->pos_base = 0;  // a new context starts at position 0
+  g_err.clear();
+  return PHX_OK;
+}
+
+int phx_expert_commit_chunk(phx_expert* h, const float* chunk, phx_stream_t stream) {
+  if (!h || !chunk) return fail(PHX_E_INVALID, "NULL argument");
+  if (!h->tokens || h->batched || h->cfg.block_kind != PHX_BLOCK_DECODER || h->cnodes.empty())
+    return fail(PHX_E_SHAPE, "commit needs the large-token decoder plan (one request of more than 160 rows)");
+  if (!h->loaded[0]) return fail(PHX_E_STATE, "request 0 has no prefix loaded");
+  const phx_expert_config& c = h->cfg;
+  const int M = c.rows, C = c.prefix_capacity, NL = c.layers;
+  if (M > C) return fail(PHX_E_SHAPE, "a chunk of %d rows does not fit a window of %d rows", M, C);
+  hipStream_t s = (hipStream_t)stream;
+  // the chunk becomes the state rows; one pass writes its keys and values after the L cached rows
+  PHX_HIP(hipMemcpyAsync(h->x, chunk, (size_t)M * c.state_dim * sizeof(float), hipMemcpyDefault, s));
+  if (h->cexec) {
+    PHX_HIP(hipGraphLaunch(h->cexec, s));
+  } else {
+    for (const TokNode& nd : h->cnodes) {
+      int rc = launch_tok(h, nd, s);
+      if (rc) return rc;
+    }
+  }
+  int L = h->lens_host[0] + M;
+  int base = h->pos_base;
+  if (L > C) {
+    // window: drop the d oldest rows; the kept keys keep their positions (base + row)
+    const int d = L - C;
+    const size_t row = (size_t)c.n_kv_heads * c.head_dim * 2;
+    const size_t kv = (size_t)NL * h->R * row;
+    if (!h->tk_tmp && alloc(h, &h->tk_tmp, kv, "history key staging")) return PHX_E_NOMEM;
+    if (!h->tv_tmp && alloc(h, &h->tv_tmp, kv, "history value staging")) return PHX_E_NOMEM;
+    PHX_HIP(hipMemcpy2DAsync(h->tk_tmp, (size_t)h->R * row, (const char*)h->tk + (size_t)d * row, (size_t)h->R * row,
+                             (size_t)C * row, (size_t)NL, hipMemcpyDeviceToDevice, s));
+    PHX_HIP(hipMemcpyAsync(h->tk, h->tk_tmp, kv, hipMemcpyDeviceToDevice, s));
+    PHX_HIP(tok::launch_vt_shift(h->tv, h->tv_tmp, NL, c.n_kv_heads, h->R, d, L, s));
+    PHX_HIP(hipMemcpyAsync(h->tv, h->tv_tmp, kv, hipMemcpyDeviceToDevice, s));
+    L = C;
+    base += d;
+  }
+  // the next chunk's rows sit after the history
+  PHX_HIP(tok::launch_positions(h->lens, h->rope, L, base + L, M, (double)c.rope_base, s));
+  h->lens_host[0] = L;
+  h->pos_base = base;
   g_err.clear();
   return PHX_OK;
 }
@@ -1436,8 +1533,9 @@ int phx_expert_capsule_save(phx_expert* h, void* capsule, size_t bytes, phx_stre
   std::memcpy(st, &hd, sizeof(hd));
   int32_t* hs = (int32_t*)(st + sizeof(CapsuleHeader));
   for (int b = 0; b < h->cfg.batch; ++b) {
-    hs[2 * b] = h->lens_host[(size_t)b];
-    hs[2 * b + 1] = h->loaded[(size_t)b];
+    hs[3 * b] = h->lens_host[(size_t)b];
+    hs[3 * b + 1] = h->loaded[(size_t)b];
+    hs[3 * b + 2] = b == 0 ? h->pos_base : 0;
   }
   PHX_HIP(hipMemcpyAsync(capsule, st, head, hipMemcpyHostToDevice, s));
   PHX_HIP(hipEventRecord(h->cap_event, s));
@@ -1474,9 +1572,10 @@ int phx_expert_capsule_restore(phx_expert* h, const void* capsule, size_t bytes,
                            hipMemcpyDeviceToDevice, s));
   const int32_t* hs = (const int32_t*)((const unsigned char*)h->cap_host + sizeof(CapsuleHeader));
   for (int b = 0; b < h->cfg.batch; ++b) {
-    h->lens_host[(size_t)b] = hs[2 * b];
-    h->loaded[(size_t)b] = hs[2 * b + 1];
+    h->lens_host[(size_t)b] = hs[3 * b];
+    h->loaded[(size_t)b] = hs[3 * b + 1];
   }
+  h->pos_base = hs[2];
   g_err.clear();
   return PHX_OK;
 }

@@ -96,6 +96,10 @@ hipError_t launch_tattn(const AttnT& a, hipStream_t s);
 hipError_t launch_tcombine(const AttnT& a, hipStream_t s);
 // Prefix values v [NL][L][KVH*DH] into the fragment order vt [NL][KVH][R*DH] (zeros for keys L..R-1).
 hipError_t launch_vt_load(const void* v, void* vt, int NL, int L, int R, int KVH, hipStream_t s);
+// dst = src moved down by d keys (keys t + d < n; zeros after), all layers and kv heads
+hipError_t launch_vt_shift(const void* src, void* dst, int NL, int KVH, int R, int d, int n, hipStream_t s);
+// lens[0] = L and the RoPE table (cos, sin) of M rows at positions pos .. pos + M - 1
+hipError_t launch_positions(int* lens, float2* rope, int L, int pos, int M, double base, hipStream_t s);
 
 }  // namespace tok
 }  // namespace phx

@@ -899,6 +899,46 @@ __global__ void k_vt_load(const bf16* __restrict__ v, bf16* __restrict__ vt, int
   }
 }
 
+// Values in fragment order moved down by d keys (the history window drops
+// its d oldest rows): dst key t = src key t + d for t + d < n, zeros after.
+__global__ void k_vt_shift(const bf16* __restrict__ src, bf16* __restrict__ dst, int NL, int KVH, int R, int d,
+                           int n) {
+  const size_t plane = (size_t)R * DH;
+  const size_t total = (size_t)NL * KVH * plane;
+  const int nj = R / 32;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t pb = i / plane * plane;
+    int t, dd;
+    vt_key_dim((int)(i - pb), t, dd);
+    dst[i] = t + d < n ? src[pb + vt_index(0, nj, t + d, dd)] : (bf16)0.0f;
+  }
+}
+
+hipError_t launch_vt_shift(const void* src, void* dst, int NL, int KVH, int R, int d, int n, hipStream_t s) {
+  const size_t total = (size_t)NL * KVH * R * DH;
+  const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
+  hipLaunchKernelGGL(k_vt_shift, dim3(blocks), dim3(256), 0, s, (const bf16*)src, (bf16*)dst, NL, KVH, R, d, n);
+  return hipGetLastError();
+}
+
+// lens[0] = L; the rows' RoPE table at positions pos .. pos + M - 1 (angles in double)
+__global__ void k_positions(int* lens, float2* rope, int L, int pos, int M, double base) {
+  constexpr int half = DH / 2;
+  if (blockIdx.x == 0 && threadIdx.x == 0) lens[0] = L;
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < M * half; idx += gridDim.x * blockDim.x) {
+    const int i = idx / half, j = idx % half;
+    const double theta = pow(base, -2.0 * (double)j / (double)DH);
+    const double ang = (double)(pos + i) * theta;
+    rope[idx] = make_float2((float)cos(ang), (float)sin(ang));
+  }
+}
+
+hipError_t launch_positions(int* lens, float2* rope, int L, int pos, int M, double base, hipStream_t s) {
+  const int n = M * (DH / 2);
+  hipLaunchKernelGGL(k_positions, dim3((n + 255) / 256), dim3(256), 0, s, lens, rope, L, pos, M, base);
+  return hipGetLastError();
+}
+
 hipError_t launch_vt_load(const void* v, void* vt, int NL, int L, int R, int KVH, hipStream_t s) {
   const size_t total = (size_t)NL * KVH * R * DH;
   const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);

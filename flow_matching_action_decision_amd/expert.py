@@ -82,6 +82,10 @@ class Expert:
     def timeline(self):
         return B.phx_expert_timeline(self.h)
 
+    def commit_chunk(self, chunk):
+        """Commit a chunk (device float32 [rows][state_dim]) into the history."""
+        B.phx_expert_commit_chunk(self.h, chunk.data_ptr(), self.stream)
+
     def capsule_bytes(self) -> int:
         return B.phx_expert_capsule_bytes(self.h)
 

@@ -198,6 +198,22 @@ PHX_API void phx_expert_destroy(phx_expert* h);
 /* Message of the last failing call in this thread ("" if none). */
 PHX_API const char* phx_last_error(void);
 
+/*
+ * History update of a chunk policy ("FlashRT-PAI", section 2.1, Figure 1b: the
+ * cache over earlier chunks persists from one decision to the next and grows
+ * up to a fixed window).  Commits chunk (device or host float32
+ * [rows][state_dim], normally the actions of the last decision) into request
+ * 0's cache: one pass of the layer stack over it at the end flow time tau0 +
+ * steps * dt writes every layer's keys and values of the chunk rows after the
+ * L cached rows, and L grows by rows.  When L would pass prefix_capacity (the
+ * window) the oldest rows are dropped; kept rows keep their positions, and the
+ * next chunk's rows sit after them.  Stream-ordered.  Only for the
+ * large-token decoder plan (one request of more than 160 rows): PHX_E_SHAPE
+ * otherwise, or when rows > prefix_capacity; PHX_E_STATE before a prefix is
+ * loaded.  phx_expert_load_prefix_kv starts a new history at position 0.
+ */
+PHX_API int phx_expert_commit_chunk(phx_expert* h, const float* chunk, phx_stream_t stream);
+
 /* Number of kernel launches one decision replays (graph nodes). */
 PHX_API int phx_expert_kernels_per_decision(const phx_expert* h, int* count);
 

@@ -236,3 +236,81 @@ def test_dit_full_width_one_block(rows):
     cfg = phx_inputs.workload("wam_dit_bf16", layers=1, rows=rows)
     cfg["name"] = f"dit_1block_{rows}"
     _dit_case(cfg)
+
+
+# ------------------------------------------------------------ history update
+
+def _history_case(cfg, name, commits=1):
+    """Decide, commit the decided chunk, decide the next chunk (repeat), and
+    compare every decision with the oracle on the same history: the oracle
+    commits the same chunk (the GPU's decided actions), appends its keys and
+    values, drops the oldest rows past the window, and decides at the
+    window's base position."""
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+    say(f"case history {name} rows={cfg['rows']} C={cfg['capacity']} L={cfg['prefix_lens']} commits={commits}")
+    inp = phx_inputs.make_inputs(cfg, 0)
+    NL, C, M = cfg["layers"], cfg["capacity"], cfg["rows"]
+    L = int(inp["lens"][0])
+    k_hist = inp["kv_k"][0, :, :L].astype(np.float64)
+    v_hist = inp["kv_v"][0, :, :L].astype(np.float64)
+    base = 0
+    tau_end = cfg["tau0"] + cfg["steps"] * cfg["dt"]
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    try:
+        keep = ex.load_all(inp)
+        noise = inp["noise"]
+        for r in range(commits + 1):
+            out = ex.decide(torch.from_numpy(noise).cuda()).cpu().numpy()
+            kk = np.zeros((1, NL, C, k_hist.shape[-1]), dtype=np.float32)
+            vv = np.zeros_like(kk)
+            kk[0, :, :k_hist.shape[1]] = k_hist
+            vv[0, :, :v_hist.shape[1]] = v_hist
+            ref = oracle.decide(cfg, inp["weights"], kk, vv, [k_hist.shape[1]], noise, pos0=[base])["actions"]
+            assert_close(out, ref, TOL_BF16, what=f"{name} decision {r} (history {k_hist.shape[1]}, base {base})")
+            if r == commits:
+                break
+            ex.commit_chunk(torch.from_numpy(out[0]).cuda())
+            got = oracle.commit(cfg, inp["weights"], kk, vv, [k_hist.shape[1]], out, tau_end, pos0=[base])
+            k_hist = np.concatenate([k_hist, got["k"][0]], axis=1)
+            v_hist = np.concatenate([v_hist, got["v"][0]], axis=1)
+            if k_hist.shape[1] > C:
+                d = k_hist.shape[1] - C
+                k_hist, v_hist, base = k_hist[:, d:], v_hist[:, d:], base + d
+            noise = np.random.default_rng(100 + r).standard_normal(noise.shape).astype(np.float32)
+        cap = ex.capsule_save()
+        nz = torch.from_numpy(noise).cuda()
+        first = ex.decide(nz).cpu().numpy().copy()
+        ex.load_all(inp)  # overwrite the history
+        ex.capsule_restore(cap)
+        again = ex.decide(nz).cpu().numpy().copy()
+        del keep
+    finally:
+        ex.close()
+    assert np.array_equal(first, again), "a capsule must carry the history and its window position"
+
+
+def test_history_commit_grows_the_cache():
+    _history_case(va_small(capacity=700, prefix_lens=[150], name="history"), "grow", commits=2)
+
+
+def test_history_window_drops_oldest_rows():
+    # 250 + 200 rows pass the 300-row window: the 150 oldest are dropped, then 200 more
+    _history_case(va_small(capacity=300, prefix_lens=[250], name="window"), "window", commits=2)
+
+
+def test_history_rejects_other_plans():
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+    from flow_matching_action_decision_amd.binding import PhxError
+    from gpu_util import small_cfg
+    cfg = small_cfg()
+    inp = phx_inputs.make_inputs(cfg, 0)
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    try:
+        keep = ex.load_all(inp)
+        with pytest.raises(PhxError):
+            ex.commit_chunk(torch.zeros(cfg["rows"], cfg["state_dim"], device="cuda"))
+        del keep
+    finally:
+        ex.close()
