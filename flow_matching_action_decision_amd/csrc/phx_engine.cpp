@@ -616,8 +616,9 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
          HD, nullptr, name);
     tok::GemmT& g = h->tnodes.back().g;
     g.kj = layer_k(l); g.vt = layer_v(l); g.lens = dit ? nullptr : h->lens; g.H = H; g.KVH = KVH; g.nj = R / 32;
+    g.hd = Dh;
     if (h->batched) {
-      g.hd = Dh; g.req_rows = c.rows; g.Ctot = h->Ctot;
+      g.req_rows = c.rows; g.Ctot = h->Ctot;
       g.kc = (char*)h->kc + (size_t)l * h->kv_layer * 2;
       g.vtc = (char*)h->vtc + (size_t)l * h->kv_layer * 2;
     }
@@ -648,7 +649,8 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     tok::AttnT& a = nd.a;
     a.q = h->qkv; a.ldq = HD; a.kj = layer_k(l); a.vt = layer_v(l); a.lens = dit ? nullptr : h->lens; a.R = R;
     a.M = M; a.H = H; a.KVH = KVH; a.o = h->o; a.po = h->po; a.pml = h->pml; a.splits = h->splits;
-    a.scale = (float)(1.0 / std::sqrt((double)tok::DH));
+    a.scale = (float)(1.0 / std::sqrt((double)Dh));
+    a.hd = Dh;
     name_of(nd, "attention");
     h->tnodes.push_back(nd);
     if (h->splits > 1) {
@@ -846,7 +848,7 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
     bufs.push_back({(void**)&h->x, (size_t)Mp * A * 4, "state rows"});
     bufs.push_back({&h->xb, (size_t)Mp * A * 2, "bf16 state rows"});
     bufs.push_back({(void**)&h->lens, sizeof(int), "prefix length"});
-    bufs.push_back({(void**)&h->rope, (size_t)M * (tok::DH / 2) * sizeof(float2), "position table"});
+    bufs.push_back({(void**)&h->rope, (size_t)M * (c.head_dim / 2) * sizeof(float2), "position table"});
   }
   if (h->splits > 1 && !h->batched) {
     bufs.push_back({(void**)&h->po, (size_t)h->splits * M * HD * 4, "attention partials"});
@@ -1034,7 +1036,8 @@ int phx_expert_validate_config(const phx_expert_config* c) {
       return fail(PHX_E_SHAPE, "more than 160 rows needs batch 1 and rows <= 16384 (rows %d, batch %d)", c->rows,
                   c->batch);
     if (c->weight_dtype != PHX_DTYPE_BF16) return fail(PHX_E_SHAPE, "more than 160 rows needs bf16 weights");
-    if (c->head_dim != 128) return fail(PHX_E_SHAPE, "more than 160 rows needs head_dim 128");
+    if (c->head_dim != 128 && c->head_dim != 256)
+      return fail(PHX_E_SHAPE, "more than 160 rows needs head_dim 128 or 256");
     if (c->state_dim % 128) return fail(PHX_E_SHAPE, "more than 160 rows needs state_dim a multiple of 128");
     if (c->block_kind == PHX_BLOCK_DIT) {
       if (c->state_dim != c->width) return fail(PHX_E_SHAPE, "the DiT-style block needs state_dim == width");
@@ -1306,7 +1309,7 @@ int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, con
     if (prefix_len > 0)
       PHX_HIP(hipMemcpy2DAsync(h->tk, (size_t)h->R * row, k, (size_t)prefix_len * row, (size_t)prefix_len * row,
                                (size_t)c.layers, hipMemcpyDeviceToDevice, s));
-    PHX_HIP(tok::launch_vt_load(v, h->tv, c.layers, prefix_len, h->R, c.n_kv_heads, s));
+    PHX_HIP(tok::launch_vt_load(v, h->tv, c.layers, prefix_len, h->R, c.n_kv_heads, c.head_dim, s));
   } else if (h->persistent) {
     PHX_HIP(dec::launch_attn_tiles(k, v, h->kvt, c.layers, prefix_len, h->n_chunks, s));
   } else {
@@ -1352,13 +1355,13 @@ int phx_expert_commit_chunk(phx_expert* h, const float* chunk, phx_stream_t stre
     PHX_HIP(hipMemcpy2DAsync(h->tk_tmp, (size_t)h->R * row, (const char*)h->tk + (size_t)d * row, (size_t)h->R * row,
                              (size_t)C * row, (size_t)NL, hipMemcpyDeviceToDevice, s));
     PHX_HIP(hipMemcpyAsync(h->tk, h->tk_tmp, kv, hipMemcpyDeviceToDevice, s));
-    PHX_HIP(tok::launch_vt_shift(h->tv, h->tv_tmp, NL, c.n_kv_heads, h->R, d, L, s));
+    PHX_HIP(tok::launch_vt_shift(h->tv, h->tv_tmp, NL, c.n_kv_heads, h->R, d, L, c.head_dim, s));
     PHX_HIP(hipMemcpyAsync(h->tv, h->tv_tmp, kv, hipMemcpyDeviceToDevice, s));
     L = C;
     base += d;
   }
   // the next chunk's rows sit after the history
-  PHX_HIP(tok::launch_positions(h->lens, h->rope, L, base + L, M, (double)c.rope_base, s));
+  PHX_HIP(tok::launch_positions(h->lens, h->rope, L, base + L, M, c.head_dim, (double)c.rope_base, s));
   h->lens_host[0] = L;
   h->pos_base = base;
   g_err.clear();

@@ -17,7 +17,6 @@ namespace phx {
 namespace tok {
 
 constexpr int ROW_PAD = 128;  // activation buffers hold rows padded to this multiple
-constexpr int DH = 128;      // head dim of the large-token plan
 
 // GEMM epilogues
 enum Epi : int {
@@ -42,11 +41,12 @@ struct GemmT {
   const float* gate;   // EP_RESID: per-column factor, or nullptr
   const float2* rope;  // EP_QKV: (cos, sin) [M][64]
   int rot_cols;        // EP_QKV: columns [0, rot_cols) are rotated (query and key heads), 0 for none
-  void* kj;            // EP_QKV: key rows [R][KVH*DH] of this layer
-  void* vt;            // EP_QKV: values of this layer in fragment order, [KVH][R*DH]
+  void* kj;            // EP_QKV: key rows [R][KVH*hd] of this layer
+  void* vt;            // EP_QKV: values of this layer in fragment order, [KVH][R*hd]
   const int* lens;     // EP_QKV: device prefix length L (chunk row r is key L + r), nullptr for 0
   int H, KVH, nj;      // EP_QKV: query heads, kv heads, 32-key steps of kj/vt (R / 32)
-  int hd, req_rows, Ctot;  // EP_QKV_CACHE: head dim, rows per request, cache slots per (request, kv head)
+  int hd, req_rows, Ctot;  // EP_QKV and EP_QKV_CACHE: head dim (128 or 256); EP_QKV_CACHE: rows per request,
+                           // cache slots per (request, kv head)
   void* kc;            // EP_QKV_CACHE: this layer's key cache
   void* vtc;           // EP_QKV_CACHE: this layer's transposed value cache
   float dt;            // EP_EULER
@@ -66,18 +66,20 @@ const char* tile_name(int tile);
 size_t gemm_part_elems(const GemmT& g);
 
 struct AttnT {
-  const void* q;     // bf16 queries [Mp][ldq], head h from column h*DH
+  const void* q;     // bf16 queries [Mp][ldq], head h from column h*hd
   int ldq;
-  const void* kj;    // bf16 key rows of this layer [R][KVH*DH]: prefix rows, then the chunk's rows from row L
-  const void* vt;    // bf16 values of this layer in fragment order [KVH][R*DH]
+  const void* kj;    // bf16 key rows of this layer [R][KVH*hd]: prefix rows, then the chunk's rows from row L
+  const void* vt;    // bf16 values of this layer in fragment order [KVH][R*hd]
   const int* lens;   // device: L = lens[0] prefix keys, read at launch; nullptr for no prefix
   int R;             // key rows allocated (multiple of 64, >= L + M)
   int M, H, KVH;     // chunk rows (queries and chunk keys), query heads, key/value heads
-  void* o;           // bf16 [Mp][H*DH] normalised output (splits == 1)
-  float* po;         // splits > 1: unnormalised partial outputs [splits][Mp][H*DH] f32
+  void* o;           // bf16 [Mp][H*hd] normalised output (splits == 1)
+  float* po;         // splits > 1: unnormalised partial outputs [splits][Mp][H*hd] f32
   float* pml;        // splits > 1: (max, sum) [splits][Mp][H] f32x2
   int splits;
-  float scale;       // 1/sqrt(DH)
+  float scale;       // 1/sqrt(hd)
+  int hd;            // head dim: 128 or 256
+  int causal;        // nonzero: chunk row q sees the prefix and chunk rows 0..q
 };
 
 // Lets every GEMM instantiation use the LDS its tile needs (call once per device, outside graph capture).
@@ -94,12 +96,14 @@ hipError_t prepare_attention();
 hipError_t launch_tattn(const AttnT& a, hipStream_t s);
 // merges the key splits into the normalised bf16 output
 hipError_t launch_tcombine(const AttnT& a, hipStream_t s);
-// Prefix values v [NL][L][KVH*DH] into the fragment order vt [NL][KVH][R*DH] (zeros for keys L..R-1).
-hipError_t launch_vt_load(const void* v, void* vt, int NL, int L, int R, int KVH, hipStream_t s);
+// Prefix values v [NL][L][KVH*hd] into the fragment order vt [NL][KVH][R*hd] (zeros for keys L..R-1).
+hipError_t launch_vt_load(const void* v, void* vt, int NL, int L, int R, int KVH, int hd, hipStream_t s);
+// Values in the fragment order back to rows: v [NL][n][KVH*hd] from keys 0..n-1.
+hipError_t launch_vt_export(const void* vt, void* v, int NL, int n, int R, int KVH, int hd, hipStream_t s);
 // dst = src moved down by d keys (keys t + d < n; zeros after), all layers and kv heads
-hipError_t launch_vt_shift(const void* src, void* dst, int NL, int KVH, int R, int d, int n, hipStream_t s);
-// lens[0] = L and the RoPE table (cos, sin) of M rows at positions pos .. pos + M - 1
-hipError_t launch_positions(int* lens, float2* rope, int L, int pos, int M, double base, hipStream_t s);
+hipError_t launch_vt_shift(const void* src, void* dst, int NL, int KVH, int R, int d, int n, int hd, hipStream_t s);
+// lens[0] = L (lens may be NULL) and the RoPE table (cos, sin) of M rows at positions pos .. pos + M - 1
+hipError_t launch_positions(int* lens, float2* rope, int L, int pos, int M, int hd, double base, hipStream_t s);
 
 }  // namespace tok
 }  // namespace phx

@@ -130,18 +130,19 @@ __device__ inline void wg_barrier() {
 }
 
 // Values of one kv head in the order the attention's PV step reads them: for
-// each 32-key step j and 16-dim tile dt, one 1 KiB MFMA fragment in which
-// lane (d % 16) + 16 g holds dim d and the keys 32 j + 4 g + [0, 4) (elements
-// 0..3) and 32 j + 16 + 4 g + [0, 4) (elements 4..7).
-__device__ inline size_t vt_index(int kvh, int nj, int t, int d) {
+// each 32-key step j and 16-dim tile dt (ndt = head_dim / 16 of them), one
+// 1 KiB MFMA fragment in which lane (d % 16) + 16 g holds dim d and the keys
+// 32 j + 4 g + [0, 4) (elements 0..3) and 32 j + 16 + 4 g + [0, 4) (4..7).
+__device__ inline size_t vt_index(int kvh, int nj, int t, int d, int ndt) {
   const int j = t >> 5, kk = t & 31, rr = kk & 15;
   const int e = (rr & 3) + 4 * (kk >> 4), ln = (d & 15) + 16 * (rr >> 2);
-  return ((((size_t)kvh * nj + j) * 8 + (d >> 4)) * 64 + ln) * 8 + e;
+  return ((((size_t)kvh * nj + j) * ndt + (d >> 4)) * 64 + ln) * 8 + e;
 }
 
 // inverse of vt_index within one kv head's plane
-__device__ inline void vt_key_dim(int i, int& t, int& d) {
-  const int e = i & 7, ln = (i >> 3) & 63, dt = (i >> 9) & 7, j = i >> 12;
+__device__ inline void vt_key_dim(int i, int ndt, int& t, int& d) {
+  const int e = i & 7, ln = (i >> 3) & 63, f = i >> 9;
+  const int dt = f % ndt, j = f / ndt;
   d = 16 * dt + (ln & 15);
   t = 32 * j + 16 * (e >> 2) + 4 * (ln >> 4) + (e & 3);
 }
@@ -155,13 +156,15 @@ __device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const 
     for (int i = 0; i < 4; ++i) y[i] = EPI == EP_GELU ? gelu_tanh(v[i]) : v[i];
     *(u32x2*)((bf16*)g.out + (size_t)row * g.ldo + nt * 16 + 4 * gq) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
   } else if constexpr (EPI == EP_QKV) {
-    // tile order of a head (query heads, then key heads, then value heads):
-    // the values are dims j, j + 1, j + 64, j + 65 with j = 8 (nt % 8) + 2 gq
-    const int hh = nt >> 3, j = 8 * (nt & 7) + 2 * gq;
+    // tile order of a head (query heads, then key heads, then value heads) of
+    // hd dims: the values are dims j, j + 1, j + hd/2, j + hd/2 + 1 with
+    // j = 8 (nt % (hd/16)) + 2 gq
+    const int tph = g.hd >> 4, half = g.hd >> 1;
+    const int hh = nt / tph, j = 8 * (nt - hh * tph) + 2 * gq;
     float y0 = v[0], y1 = v[1], y2 = v[2], y3 = v[3];
-    if (hh * DH < g.rot_cols) {
-      const float2 a = g.rope[(size_t)row * (DH / 2) + j];
-      const float2 b = g.rope[(size_t)row * (DH / 2) + j + 1];
+    if (hh * g.hd < g.rot_cols) {
+      const float2 a = g.rope[(size_t)row * half + j];
+      const float2 b = g.rope[(size_t)row * half + j + 1];
       y0 = v[0] * a.x - v[2] * a.y;
       y2 = v[2] * a.x + v[0] * a.y;
       y1 = v[1] * b.x - v[3] * b.y;
@@ -169,20 +172,20 @@ __device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const 
     }
     const int L = g.lens ? g.lens[0] : 0;
     if (hh < g.H) {
-      bf16* o = (bf16*)g.out + (size_t)row * g.ldo + hh * DH + j;
+      bf16* o = (bf16*)g.out + (size_t)row * g.ldo + hh * g.hd + j;
       *(unsigned*)o = pack2(y0, y1);
-      *(unsigned*)(o + DH / 2) = pack2(y2, y3);
+      *(unsigned*)(o + half) = pack2(y2, y3);
     } else if (hh < g.H + g.KVH) {
-      bf16* o = (bf16*)g.kj + (size_t)(L + row) * (g.KVH * DH) + (hh - g.H) * DH + j;
+      bf16* o = (bf16*)g.kj + (size_t)(L + row) * (g.KVH * g.hd) + (hh - g.H) * g.hd + j;
       *(unsigned*)o = pack2(y0, y1);
-      *(unsigned*)(o + DH / 2) = pack2(y2, y3);
+      *(unsigned*)(o + half) = pack2(y2, y3);
     } else {
       const int kvh = hh - g.H - g.KVH, t = L + row;
       bf16* vt = (bf16*)g.vt;
-      vt[vt_index(kvh, g.nj, t, j)] = (bf16)y0;
-      vt[vt_index(kvh, g.nj, t, j + 1)] = (bf16)y1;
-      vt[vt_index(kvh, g.nj, t, j + DH / 2)] = (bf16)y2;
-      vt[vt_index(kvh, g.nj, t, j + DH / 2 + 1)] = (bf16)y3;
+      vt[vt_index(kvh, g.nj, t, j, tph)] = (bf16)y0;
+      vt[vt_index(kvh, g.nj, t, j + 1, tph)] = (bf16)y1;
+      vt[vt_index(kvh, g.nj, t, j + half, tph)] = (bf16)y2;
+      vt[vt_index(kvh, g.nj, t, j + half + 1, tph)] = (bf16)y3;
     }
   } else if constexpr (EPI == EP_QKV_CACHE) {
     // tile order of a head of hd dims: dims j, j + 1, j + hd/2, j + hd/2 + 1, j = 8 (nt % (hd/16)) + 2 gq
@@ -640,7 +643,9 @@ hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStrea
 // Workgroup (128 queries, head h, key split); wave w owns queries 32 w as two
 // 16-query tiles.  Keys are the L prefix rows followed by the M chunk rows,
 // read from the joint key rows and the fragment-ordered values (see
-// vt_index); a split takes a contiguous range of 64-key blocks.  Per block:
+// vt_index); a split takes a contiguous range of 64-key blocks.  With the
+// causal mask chunk row q sees the prefix and chunk rows up to itself.  Per
+// block:
 //   S^T = K . Q^T with 16x16x32 MFMAs: K fragments (lane: key lane % 16, dims
 //     8 (lane / 16) + [0, 8) of a 32-dim step) come from LDS, the wave's
 //     queries sit in registers as B fragments, so each lane ends with keys
@@ -651,16 +656,26 @@ hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStrea
 //     of one 32-key step as they lie in the registers (k index 8 g + e is key
 //     4 g + e for e < 4 and 16 + 4 g + e - 4 for e >= 4), and the value
 //     fragments are stored in that same key order.
-// K and V^T blocks (16 KiB each) stream into a two-stage LDS ring with
-// direct loads, the next block in flight while the current one is used.
-// Workgroups of one head run on one XCD so its keys and values stay in that
-// XCD's L2.
+// K and V^T blocks (16 KiB each per 128 dims) stream into a two-stage LDS
+// ring with direct loads, the next block in flight while the current one is
+// used.  Workgroups of one head run on one XCD so its keys and values stay in
+// that XCD's L2.
 constexpr int KB = 64;     // keys per block
 constexpr int AQ = 128;    // queries per workgroup
 constexpr int ASTAGE = 2;  // LDS stages
-constexpr int ASTAGE_BYTES = 32 * 1024;
 
+template <int HD>
+struct AttnShape {
+  static constexpr int NDS = HD / 32;               // 32-dim steps of S^T = K . Q^T
+  static constexpr int NDT = HD / 16;               // 16-dim tiles of O^T
+  static constexpr int KBYTES = 4 * NDS * 1024;     // K fragments of one block
+  static constexpr int STAGE = 2 * KBYTES;          // K and V^T of one block
+};
+
+template <int HD>
 __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
+  using S = AttnShape<HD>;
+  constexpr int NDS = S::NDS, NDT = S::NDT;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -678,22 +693,24 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
   }
   const int qb = r / a.splits, split = r % a.splits;
   const int kvh = h / (a.H / a.KVH);
-  const int kvd = a.KVH * DH;
+  const int kvd = a.KVH * HD;
   const int L = a.lens ? __builtin_amdgcn_readfirstlane(a.lens[0]) : 0;
   const int T = L + a.M;
   const int nblk = (T + KB - 1) / KB;
   const int per = (nblk + a.splits - 1) / a.splits;
-  const int b0 = split * per, b1 = min(nblk, b0 + per);
+  const int b0 = split * per;
+  int b1 = min(nblk, b0 + per);
+  if (a.causal) b1 = min(b1, (L + min(qb * AQ + AQ, a.M) - 1) / KB + 1);  // no key past the last query
   const int g4 = lane >> 4, qr = lane & 15;
   const int q0 = qb * AQ + 32 * wave;
   // queries as B fragments of Q^T: dims 32 ds + 8 g4 + [0, 8) of query q0 + 16 qt + qr
-  bf16x8 qf[2][4];
+  bf16x8 qf[2][NDS];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int q = min(q0 + 16 * qt + qr, a.M - 1);
-    const bf16* qp = (const bf16*)a.q + (size_t)q * a.ldq + h * DH + 8 * g4;
+    const bf16* qp = (const bf16*)a.q + (size_t)q * a.ldq + h * HD + 8 * g4;
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) qf[qt][ds] = *(const bf16x8*)(qp + 32 * ds);
+    for (int ds = 0; ds < NDS; ++ds) qf[qt][ds] = *(const bf16x8*)(qp + 32 * ds);
   }
   // Wait for the query loads here, once: left to the first use inside the
   // block loop, the compiler's wait would also cover the next block's LDS
@@ -701,61 +718,66 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) asm volatile("" : "+v"(qf[qt][ds]));
+    for (int ds = 0; ds < NDS; ++ds) asm volatile("" : "+v"(qf[qt][ds]));
   const unsigned lds0 = (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)smem);
   const u32x4 rk = rsrc_words(a.kj, (unsigned)((size_t)a.R * kvd * 2));
-  const u32x4 rv = rsrc_words(a.vt, (unsigned)((size_t)a.KVH * a.R * DH * 2));
-  // wave w moves K fragments (key tile w, dim steps 0..3) and value fragments 4 w .. 4 w + 3
-  unsigned vok[4];
+  const u32x4 rv = rsrc_words(a.vt, (unsigned)((size_t)a.KVH * a.R * HD * 2));
+  // wave w moves the K fragments of key tile w (all dim steps) and value fragments w NDT/2 .. (w+1) NDT/2 - 1
+  unsigned vok[NDS];
 #pragma unroll
-  for (int ds = 0; ds < 4; ++ds) vok[ds] = (unsigned)(((16 * wave + qr) * kvd + kvh * DH + 32 * ds + 8 * g4) * 2);
+  for (int ds = 0; ds < NDS; ++ds)
+    vok[ds] = (unsigned)(((16 * wave + qr) * kvd + kvh * HD + 32 * ds + 8 * g4) * 2);
   const unsigned vov = (unsigned)lane * 16u;
   const int nj = a.R / 32;
   auto issue = [&](int b) {
-    const unsigned st = lds0 + (unsigned)((b % ASTAGE) * ASTAGE_BYTES);
+    const unsigned st = lds0 + (unsigned)((b % ASTAGE) * S::STAGE);
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-      dma_frag(st + (unsigned)((4 * wave + ds) * 1024), vok[ds], rk, (unsigned)(b * KB * kvd * 2));
+    for (int ds = 0; ds < NDS; ++ds)
+      dma_frag(st + (unsigned)((NDS * wave + ds) * 1024), vok[ds], rk, (unsigned)(b * KB * kvd * 2));
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      dma_frag(st + 16384u + (unsigned)((4 * wave + f) * 1024), vov, rv,
-               (unsigned)((((size_t)kvh * nj + 2 * b) * 8 + 4 * wave + f) * 1024));
+    for (int f = 0; f < NDT / 2; ++f)
+      dma_frag(st + (unsigned)(S::KBYTES + ((NDT / 2) * wave + f) * 1024), vov, rv,
+               (unsigned)((((size_t)kvh * nj + 2 * b) * NDT + (NDT / 2) * wave + f) * 1024));
   };
   const float sl2 = a.scale * 1.4426950408889634f;  // scores in base 2
-  f32x4 oacc[2][8];
+  f32x4 oacc[2][NDT];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) oacc[qt][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < NDT; ++d) oacc[qt][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   if (b0 < b1) issue(b0);
   for (int b = b0; b < b1; ++b) {
     wait_vm<0>();
     wg_barrier();  // block b is in LDS for every wave; every wave is done with block b - 1
     if (b + 1 < b1) issue(b + 1);
-    const unsigned char* st = smem + (b % ASTAGE) * ASTAGE_BYTES;
+    const unsigned char* st = smem + (b % ASTAGE) * S::STAGE;
     f32x4 sc[2][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       sc[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       sc[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        const bf16x8 kf = *(const bf16x8*)(st + (kt * 4 + ds) * 1024 + lane * 16);
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8 kf = *(const bf16x8*)(st + (kt * NDS + ds) * 1024 + lane * 16);
         sc[0][kt] = mma32(kf, qf[0][ds], sc[0][kt]);
         sc[1][kt] = mma32(kf, qf[1][ds], sc[1][kt]);
       }
     }
     const int k0 = b * KB;
-    // keys at or past T exist only in the last block
-    if (k0 + KB > T) {
+    // keys at or past T exist only in the last block; causal keys past a query only near the diagonal
+    const bool tail = k0 + KB > T;
+    const bool diag = a.causal && k0 + KB - 1 > L + q0;
+    if (tail || diag) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt) {
+        const int lim = a.causal ? min(T - 1, L + q0 + 16 * qt + qr) : T - 1;  // last key this query sees
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (k0 + 16 * kt + 4 * g4 + i >= T) sc[qt][kt][i] = -INFINITY;
+            if (k0 + 16 * kt + 4 * g4 + i > lim) sc[qt][kt][i] = -INFINITY;
+      }
     }
     // Lazy rescaling: the reference m (base 2) of a query moves only when some
     // score of the wave exceeds it by more than 8, so the probabilities stay
@@ -777,12 +799,13 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run[qt], mx);
-        corr[qt] = exp2f(m_run[qt] - m_new);  // 0 on the first block (m_run = -inf)
+        // 0 on a query's first block (m_run = -inf); a query with no key yet keeps m = -inf
+        corr[qt] = m_new == -INFINITY ? 1.f : exp2f(m_run[qt] - m_new);
         l_run[qt] *= corr[qt];
         m_run[qt] = m_new;
         moved[qt] = true;
       }
-      const float mneg = -m_run[qt];
+      const float mneg = m_run[qt] == -INFINITY ? 0.f : -m_run[qt];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -794,17 +817,17 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
     }
     if (moved[0] || moved[1]) {
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
+      for (int d = 0; d < NDT; ++d) {
         oacc[0][d] *= corr[0];
         oacc[1][d] *= corr[1];
       }
     }
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
+    for (int d = 0; d < NDT; ++d) {
       f32x4 a0 = oacc[0][d], a1 = oacc[1][d];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const bf16x8 vf = *(const bf16x8*)(st + 16384 + (j * 8 + d) * 1024 + lane * 16);
+        const bf16x8 vf = *(const bf16x8*)(st + S::KBYTES + (j * NDT + d) * 1024 + lane * 16);
         a0 = mma32(vf, pf[0][j], a0);
         a1 = mma32(vf, pf[1][j], a1);
       }
@@ -824,15 +847,15 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
     if (q >= a.M) continue;
     if (a.splits == 1) {
       const float inv = 1.0f / l_run[qt];
-      bf16* op = (bf16*)a.o + (size_t)q * (a.H * DH) + h * DH;
+      bf16* op = (bf16*)a.o + (size_t)q * (a.H * HD) + h * HD;
 #pragma unroll
-      for (int d = 0; d < 8; ++d)
+      for (int d = 0; d < NDT; ++d)
         *(u32x2*)(op + 16 * d + 4 * g4) = u32x2{pack2(oacc[qt][d][0] * inv, oacc[qt][d][1] * inv),
                                                 pack2(oacc[qt][d][2] * inv, oacc[qt][d][3] * inv)};
     } else {
-      float* po = a.po + ((size_t)split * a.M + q) * (a.H * DH) + h * DH;
+      float* po = a.po + ((size_t)split * a.M + q) * (a.H * HD) + h * HD;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) *(f32x4*)(po + 16 * d + 4 * g4) = oacc[qt][d];
+      for (int d = 0; d < NDT; ++d) *(f32x4*)(po + 16 * d + 4 * g4) = oacc[qt][d];
       if (g4 == 0) {
         float* ml = a.pml + (((size_t)split * a.M + q) * a.H + h) * 2;
         ml[0] = m_run[qt];
@@ -843,24 +866,31 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
 }
 
 hipError_t prepare_attention() {
-  return hipFuncSetAttribute((const void*)k_tattn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             ASTAGE * ASTAGE_BYTES);
+  hipError_t e = hipFuncSetAttribute((const void*)k_tattn<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     ASTAGE * AttnShape<128>::STAGE);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)k_tattn<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             ASTAGE * AttnShape<256>::STAGE);
 }
 
 hipError_t launch_tattn(const AttnT& a, hipStream_t s) {
   if (a.M < 1 || a.H % a.KVH || a.splits < 1 || a.R % KB || a.R < a.M) return hipErrorInvalidValue;
-  if ((size_t)a.R * a.KVH * DH * 2 >= (1ull << 32)) return hipErrorInvalidValue;
+  if (a.hd != 128 && a.hd != 256) return hipErrorInvalidValue;
+  if ((size_t)a.R * a.KVH * a.hd * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   const int blocks = ((a.M + AQ - 1) / AQ) * a.splits * a.H;
-  hipLaunchKernelGGL(k_tattn, dim3(blocks), dim3(256), ASTAGE * ASTAGE_BYTES, s, a);
+  if (a.hd == 128)
+    hipLaunchKernelGGL(k_tattn<128>, dim3(blocks), dim3(256), ASTAGE * AttnShape<128>::STAGE, s, a);
+  else
+    hipLaunchKernelGGL(k_tattn<256>, dim3(blocks), dim3(256), ASTAGE * AttnShape<256>::STAGE, s, a);
   return hipGetLastError();
 }
 
-// out[q][h*DH + d] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, splits in order
+// out[q][h*hd + d] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, splits in order
 __global__ void k_tcombine(AttnT a) {
-  const size_t total = (size_t)a.M * a.H * DH;
+  const size_t total = (size_t)a.M * a.H * a.hd;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int d = (int)(i % DH);
-    const size_t qh = i / DH;
+    const int d = (int)(i % a.hd);
+    const size_t qh = i / a.hd;
     const int h = (int)(qh % a.H);
     const int q = (int)(qh / a.H);
     float m = -INFINITY;
@@ -870,79 +900,101 @@ __global__ void k_tcombine(AttnT a) {
       const float ms = a.pml[(((size_t)s * a.M + q) * a.H + h) * 2];
       if (ms == -INFINITY) continue;
       const float w = exp2f(ms - m);
-      num += w * a.po[((size_t)s * a.M + q) * (a.H * DH) + h * DH + d];
+      num += w * a.po[((size_t)s * a.M + q) * (a.H * a.hd) + h * a.hd + d];
       den += w * a.pml[(((size_t)s * a.M + q) * a.H + h) * 2 + 1];
     }
-    ((bf16*)a.o)[(size_t)q * (a.H * DH) + h * DH + d] = (bf16)(num / den);
+    ((bf16*)a.o)[(size_t)q * (a.H * a.hd) + h * a.hd + d] = (bf16)(num / den);
   }
 }
 
 hipError_t launch_tcombine(const AttnT& a, hipStream_t s) {
-  const size_t total = (size_t)a.M * a.H * DH;
+  const size_t total = (size_t)a.M * a.H * a.hd;
   const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
   hipLaunchKernelGGL(k_tcombine, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-// Prefix values into the fragment order: keys t < L from v [NL][L][KVH*DH],
+// Prefix values into the fragment order: keys t < L from v [NL][L][KVH*hd],
 // zeros for L <= t < R.
-__global__ void k_vt_load(const bf16* __restrict__ v, bf16* __restrict__ vt, int NL, int L, int R, int KVH) {
-  const size_t plane = (size_t)R * DH;  // one kv head of one layer
+__global__ void k_vt_load(const bf16* __restrict__ v, bf16* __restrict__ vt, int NL, int L, int R, int KVH, int hd) {
+  const size_t plane = (size_t)R * hd;  // one kv head of one layer
   const size_t total = (size_t)NL * KVH * plane;
-  const int kvd = KVH * DH;
+  const int kvd = KVH * hd, ndt = hd / 16;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const size_t lp = i / plane;
     const int l = (int)(lp / KVH), kvh = (int)(lp % KVH);
     int t, d;
-    vt_key_dim((int)(i % plane), t, d);
-    vt[i] = t < L ? v[((size_t)l * L + t) * kvd + kvh * DH + d] : (bf16)0.0f;
+    vt_key_dim((int)(i % plane), ndt, t, d);
+    vt[i] = t < L ? v[((size_t)l * L + t) * kvd + kvh * hd + d] : (bf16)0.0f;
+  }
+}
+
+// Values in fragment order back to rows: v [NL][n][KVH*hd] from the keys t < n of vt.
+__global__ void k_vt_export(const bf16* __restrict__ vt, bf16* __restrict__ v, int NL, int n, int R, int KVH,
+                            int hd) {
+  const int kvd = KVH * hd, ndt = hd / 16, nj = R / 32;
+  const size_t plane = (size_t)R * hd;
+  const size_t total = (size_t)NL * n * kvd;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % kvd);
+    const size_t lt = i / kvd;
+    const int t = (int)(lt % n), l = (int)(lt / n);
+    const int kvh = c / hd, d = c % hd;
+    v[i] = vt[((size_t)l * KVH + kvh) * plane + vt_index(0, nj, t, d, ndt)];
   }
 }
 
 // Values in fragment order moved down by d keys (the history window drops
 // its d oldest rows): dst key t = src key t + d for t + d < n, zeros after.
 __global__ void k_vt_shift(const bf16* __restrict__ src, bf16* __restrict__ dst, int NL, int KVH, int R, int d,
-                           int n) {
-  const size_t plane = (size_t)R * DH;
+                           int n, int hd) {
+  const size_t plane = (size_t)R * hd;
   const size_t total = (size_t)NL * KVH * plane;
-  const int nj = R / 32;
+  const int nj = R / 32, ndt = hd / 16;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const size_t pb = i / plane * plane;
     int t, dd;
-    vt_key_dim((int)(i - pb), t, dd);
-    dst[i] = t + d < n ? src[pb + vt_index(0, nj, t + d, dd)] : (bf16)0.0f;
+    vt_key_dim((int)(i - pb), ndt, t, dd);
+    dst[i] = t + d < n ? src[pb + vt_index(0, nj, t + d, dd, ndt)] : (bf16)0.0f;
   }
 }
 
-hipError_t launch_vt_shift(const void* src, void* dst, int NL, int KVH, int R, int d, int n, hipStream_t s) {
-  const size_t total = (size_t)NL * KVH * R * DH;
-  const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
-  hipLaunchKernelGGL(k_vt_shift, dim3(blocks), dim3(256), 0, s, (const bf16*)src, (bf16*)dst, NL, KVH, R, d, n);
+static int grid_for(size_t total) { return (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535); }
+
+hipError_t launch_vt_shift(const void* src, void* dst, int NL, int KVH, int R, int d, int n, int hd, hipStream_t s) {
+  hipLaunchKernelGGL(k_vt_shift, dim3(grid_for((size_t)NL * KVH * R * hd)), dim3(256), 0, s, (const bf16*)src,
+                     (bf16*)dst, NL, KVH, R, d, n, hd);
+  return hipGetLastError();
+}
+
+hipError_t launch_vt_export(const void* vt, void* v, int NL, int n, int R, int KVH, int hd, hipStream_t s) {
+  if (n < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_vt_export, dim3(grid_for((size_t)NL * n * KVH * hd)), dim3(256), 0, s, (const bf16*)vt,
+                     (bf16*)v, NL, n, R, KVH, hd);
   return hipGetLastError();
 }
 
 // lens[0] = L; the rows' RoPE table at positions pos .. pos + M - 1 (angles in double)
-__global__ void k_positions(int* lens, float2* rope, int L, int pos, int M, double base) {
-  constexpr int half = DH / 2;
-  if (blockIdx.x == 0 && threadIdx.x == 0) lens[0] = L;
+__global__ void k_positions(int* lens, float2* rope, int L, int pos, int M, int hd, double base) {
+  const int half = hd / 2;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && lens) lens[0] = L;
   for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < M * half; idx += gridDim.x * blockDim.x) {
     const int i = idx / half, j = idx % half;
-    const double theta = pow(base, -2.0 * (double)j / (double)DH);
+    const double theta = pow(base, -2.0 * (double)j / (double)hd);
     const double ang = (double)(pos + i) * theta;
     rope[idx] = make_float2((float)cos(ang), (float)sin(ang));
   }
 }
 
-hipError_t launch_positions(int* lens, float2* rope, int L, int pos, int M, double base, hipStream_t s) {
-  const int n = M * (DH / 2);
-  hipLaunchKernelGGL(k_positions, dim3((n + 255) / 256), dim3(256), 0, s, lens, rope, L, pos, M, base);
+hipError_t launch_positions(int* lens, float2* rope, int L, int pos, int M, int hd, double base, hipStream_t s) {
+  const int n = M * (hd / 2);
+  hipLaunchKernelGGL(k_positions, dim3((n + 255) / 256), dim3(256), 0, s, lens, rope, L, pos, M, hd, base);
   return hipGetLastError();
 }
 
-hipError_t launch_vt_load(const void* v, void* vt, int NL, int L, int R, int KVH, hipStream_t s) {
-  const size_t total = (size_t)NL * KVH * R * DH;
-  const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
-  hipLaunchKernelGGL(k_vt_load, dim3(blocks), dim3(256), 0, s, (const bf16*)v, (bf16*)vt, NL, L, R, KVH);
+hipError_t launch_vt_load(const void* v, void* vt, int NL, int L, int R, int KVH, int hd, hipStream_t s) {
+  hipLaunchKernelGGL(k_vt_load, dim3(grid_for((size_t)NL * KVH * R * hd)), dim3(256), 0, s, (const bf16*)v,
+                     (bf16*)vt, NL, L, R, KVH, hd);
   return hipGetLastError();
 }
 

@@ -74,6 +74,11 @@ def test_va_small_gqa():
     _va_case(va_small(n_heads=4, n_kv_heads=2, name="va_small_gqa"))
 
 
+def test_va_head_dim_256():
+    """Heads of 256 (MQA: two query heads over one kv head), width 512."""
+    _va_case(va_small(n_heads=2, head_dim=256, n_kv_heads=1, width=512, name="va_dh256"))
+
+
 def test_va_many_rows():
     """1030 rows: the GEMMs take the register-fed kernel (1024 rows or more)."""
     _va_case(va_small(rows=1030, prefix_lens=[100], name="va_1030"))
@@ -165,6 +170,10 @@ def test_dit_small():
 
 def test_dit_small_rows_multiple_of_padding():
     _dit_case(dit_small(rows=256, name="dit_256"))
+
+
+def test_dit_head_dim_256():
+    _dit_case(dit_small(n_heads=2, head_dim=256, n_kv_heads=2, width=512, state_dim=512, name="dit_dh256"))
 
 
 def test_dit_many_rows():
