@@ -86,6 +86,10 @@ def load(path: str = LIB_PATH):
     lib.orc_dit.restype = ctypes.c_int
     lib.orc_dit_weight_count.argtypes = [ctypes.POINTER(OrcConfig)]
     lib.orc_dit_weight_count.restype = ctypes.c_size_t
+    lib.orc_prefill.argtypes = [ctypes.POINTER(OrcConfig), _FP, _FP, ctypes.c_int, _DP, _DP, _DP]
+    lib.orc_prefill.restype = ctypes.c_int
+    lib.orc_prefill_weight_count.argtypes = [ctypes.POINTER(OrcConfig)]
+    lib.orc_prefill_weight_count.restype = ctypes.c_size_t
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -115,6 +119,8 @@ def weight_count(cfg: dict, lib=None) -> int:
     c = make_config(cfg)
     if cfg.get("block", "decoder") == "dit":
         return int(lib.orc_dit_weight_count(ctypes.byref(c)))
+    if cfg.get("block", "decoder") == "prefill":
+        return int(lib.orc_prefill_weight_count(ctypes.byref(c)))
     return int(lib.orc_weight_count(ctypes.byref(c)))
 
 
@@ -290,3 +296,27 @@ def dit(cfg: dict, weights: np.ndarray, x, trace: bool = False, lib=None) -> dic
     if rc != 0:
         raise ValueError(f"orc_dit rejected its arguments (rc={rc})")
     return {"out": out, "trace": tr, "softmax_dev": lib.orc_last_softmax_dev()}
+
+
+def prefill(cfg: dict, weights: np.ndarray, x, length: int, trace: bool = False, lib=None) -> dict:
+    """Prefix prefill over the first ``length`` token rows of x [>= length][D]
+    (float32).  Returns {"k": [NL][length][KVH*Dh], "v": same (float64),
+    "trace": [NL-1][length][D] or None, "softmax_dev": float}."""
+    lib = lib or load()
+    c = make_config(cfg)
+    n_w = int(lib.orc_prefill_weight_count(ctypes.byref(c)))
+    weights, pw = _f(weights)
+    if weights.size != n_w:
+        raise ValueError(f"weight blob has {weights.size} values, expected {n_w}")
+    D, NL = cfg["width"], cfg["layers"]
+    kvd = cfg["n_kv_heads"] * cfg["head_dim"]
+    T = int(length)
+    x, px = _f(np.asarray(x, dtype=np.float32).reshape(-1, D)[:T])
+    k = np.zeros((NL, T, kvd), dtype=np.float64)
+    v = np.zeros((NL, T, kvd), dtype=np.float64)
+    tr = np.zeros((max(NL - 1, 1), T, D), dtype=np.float64) if trace else None
+    rc = lib.orc_prefill(ctypes.byref(c), pw, px, T, k.ctypes.data_as(_DP), v.ctypes.data_as(_DP),
+                         tr.ctypes.data_as(_DP) if tr is not None else None)
+    if rc != 0:
+        raise ValueError(f"orc_prefill rejected its arguments (rc={rc})")
+    return {"k": k, "v": v, "trace": tr, "softmax_dev": lib.orc_last_softmax_dev()}

@@ -424,3 +424,129 @@ int orc_dit(const orc_config* c, const float* weights, const float* x_in, double
   free(x); free(n); free(qkv); free(q); free(k); free(v); free(o); free(proj); free(up); free(e); free(mod);
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Prefix prefill: the language model that reads the prefix tokens (image and
+ * prompt) and writes the key/value cache the action expert attends to
+ * ("FlashRT-PAI", section 2.1, Figure 1a: an 18-layer PaliGemma language
+ * model over a prefix of about 500 to 800 tokens writes its cache).
+ *
+ * Readings where the pages are silent: a decoder layer of the same family
+ * as the expert's (RMSNorm with a learned per-channel gain, y*(1+g); one QKV
+ * projection; rotate-half RoPE on q and k at positions 0..T-1; attention;
+ * output projection + residual; RMSNorm; GeGLU MLP + residual), no biases,
+ * and a causal mask: token i sees tokens 0..i.  The cache of layer l is its
+ * keys after RoPE and its values.
+ * ------------------------------------------------------------------------ */
+
+size_t orc_prefill_weight_count(const orc_config* c) {
+  size_t D = (size_t)c->width, F = (size_t)c->mlp_hidden;
+  size_t hd = (size_t)c->n_heads * c->head_dim, nqkv = (size_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  size_t per_layer = D * nqkv + hd * D + D * 2 * F + F * D;
+  return (size_t)c->layers * per_layer + 2 * (size_t)c->layers * D;
+}
+
+/* Causal attention of T tokens over their own keys: token i sees t <= i.
+   q [T][H*Dh], k and v [T][KVH*Dh], o [T][H*Dh].  Returns the largest
+   |sum(p) - 1| of any softmax row. */
+static double causal_attention(int T, int H, int KVH, int Dh, const double* q, const double* k, const double* v,
+                               double* o) {
+  const int group = H / KVH, kvd = KVH * Dh;
+  const double scale = 1.0 / sqrt((double)Dh);
+  double worst = 0.0;
+#pragma omp parallel for schedule(static) reduction(max : worst)
+  for (int ih = 0; ih < T * H; ++ih) {
+    const int i = ih / H, hh = ih % H, g = hh / group;
+    const double* qv = q + (size_t)i * H * Dh + (size_t)hh * Dh;
+    double* p = (double*)malloc(sizeof(double) * (size_t)(i + 1));
+    double mx = -INFINITY;
+    for (int t = 0; t <= i; ++t) {
+      const double* kr = k + (size_t)t * kvd + (size_t)g * Dh;
+      double s = 0.0;
+      for (int d = 0; d < Dh; ++d) s += qv[d] * kr[d];
+      p[t] = s * scale;
+      if (p[t] > mx) mx = p[t];
+    }
+    double den = 0.0;
+    for (int t = 0; t <= i; ++t) { p[t] = exp(p[t] - mx); den += p[t]; }
+    double psum = 0.0;
+    for (int t = 0; t <= i; ++t) { p[t] /= den; psum += p[t]; }
+    if (fabs(psum - 1.0) > worst) worst = fabs(psum - 1.0);
+    double* ov = o + (size_t)i * H * Dh + (size_t)hh * Dh;
+    for (int d = 0; d < Dh; ++d) ov[d] = 0.0;
+    for (int t = 0; t <= i; ++t) {
+      const double* vr = v + (size_t)t * kvd + (size_t)g * Dh;
+      for (int d = 0; d < Dh; ++d) ov[d] += p[t] * vr[d];
+    }
+    free(p);
+  }
+  return worst;
+}
+
+int orc_prefill(const orc_config* c, const float* weights, const float* x_in, int T, double* kout, double* vout,
+                double* trace) {
+  if (check_cfg(c) || !weights || !x_in || !kout || !vout || T < 1) return -1;
+  const int NL = c->layers, D = c->width, H = c->n_heads, Dh = c->head_dim, KVH = c->n_kv_heads;
+  const int F = c->mlp_hidden, hd = H * Dh, kvd = KVH * Dh, nqkv = hd + 2 * kvd;
+  const size_t per_layer = (size_t)D * nqkv + (size_t)hd * D + (size_t)D * 2 * F + (size_t)F * D;
+  const float* G = weights + (size_t)NL * per_layer; /* [2NL][D] norm gains */
+
+  double* x = (double*)malloc(sizeof(double) * (size_t)T * D);
+  double* n = (double*)malloc(sizeof(double) * (size_t)T * D);
+  double* qkv = (double*)malloc(sizeof(double) * (size_t)T * nqkv);
+  double* q = (double*)malloc(sizeof(double) * (size_t)T * hd);
+  double* k = (double*)malloc(sizeof(double) * (size_t)T * kvd);
+  double* v = (double*)malloc(sizeof(double) * (size_t)T * kvd);
+  double* o = (double*)malloc(sizeof(double) * (size_t)T * hd);
+  double* proj = (double*)malloc(sizeof(double) * (size_t)T * D);
+  double* gu = (double*)malloc(sizeof(double) * (size_t)T * 2 * F);
+  double* a = (double*)malloc(sizeof(double) * (size_t)T * F);
+  double* mod = (double*)malloc(sizeof(double) * (size_t)2 * D);
+  int* pos = (int*)malloc(sizeof(int) * (size_t)T);
+  double worst = 0.0;
+
+  for (size_t i = 0; i < (size_t)T * D; ++i) x[i] = (double)x_in[i];
+  for (int i = 0; i < T; ++i) pos[i] = i;
+  for (int l = 0; l < NL; ++l) {
+    const float* W_qkv = weights + (size_t)l * per_layer;
+    const float* W_o = W_qkv + (size_t)D * nqkv;
+    const float* W_gu = W_o + (size_t)hd * D;
+    const float* W_down = W_gu + (size_t)D * 2 * F;
+
+    /* RMSNorm with gain: the adaptive form with scale = g, shift = 0 */
+    for (int d = 0; d < D; ++d) { mod[d] = (double)G[(size_t)(2 * l) * D + d]; mod[D + d] = 0.0; }
+    orc_ada_rmsnorm(T, D, x, mod, c->rms_eps, n);
+    orc_matmul(T, D, nqkv, n, W_qkv, qkv);
+    for (int t = 0; t < T; ++t) {
+      const double* src = qkv + (size_t)t * nqkv;
+      memcpy(q + (size_t)t * hd, src, sizeof(double) * hd);
+      memcpy(k + (size_t)t * kvd, src + hd, sizeof(double) * kvd);
+      memcpy(v + (size_t)t * kvd, src + hd + kvd, sizeof(double) * kvd);
+    }
+    orc_rope(T, H, Dh, pos, c->rope_base, q);
+    orc_rope(T, KVH, Dh, pos, c->rope_base, k);
+    memcpy(kout + (size_t)l * T * kvd, k, sizeof(double) * (size_t)T * kvd);
+    memcpy(vout + (size_t)l * T * kvd, v, sizeof(double) * (size_t)T * kvd);
+    /* the rest of the last layer writes no cache */
+    if (l + 1 == NL) break;
+
+    double dev = causal_attention(T, H, KVH, Dh, q, k, v, o);
+    if (dev > worst) worst = dev;
+    orc_matmul(T, hd, D, o, W_o, proj);
+    for (size_t i = 0; i < (size_t)T * D; ++i) x[i] += proj[i];
+
+    for (int d = 0; d < D; ++d) mod[d] = (double)G[(size_t)(2 * l + 1) * D + d];
+    orc_ada_rmsnorm(T, D, x, mod, c->rms_eps, n);
+    orc_matmul(T, D, 2 * F, n, W_gu, gu);
+    for (int t = 0; t < T; ++t)
+      for (int f = 0; f < F; ++f)
+        a[(size_t)t * F + f] = orc_gelu_tanh(gu[(size_t)t * 2 * F + f]) * gu[(size_t)t * 2 * F + F + f];
+    orc_matmul(T, F, D, a, W_down, proj);
+    for (size_t i = 0; i < (size_t)T * D; ++i) x[i] += proj[i];
+    if (trace) memcpy(trace + (size_t)l * T * D, x, sizeof(double) * (size_t)T * D);
+  }
+  g_last_softmax_dev = worst;
+  free(x); free(n); free(qkv); free(q); free(k); free(v); free(o); free(proj); free(gu); free(a); free(mod);
+  free(pos);
+  return 0;
+}

@@ -150,6 +150,27 @@ int orc_dit(const orc_config* cfg, const float* weights, const float* x_in, doub
 /* Number of float32 values in the DiT-style weight blob for cfg. */
 size_t orc_dit_weight_count(const orc_config* cfg);
 
+/*
+ * Prefix prefill over the first T tokens of x_in [T][D] (float32): the
+ * decoder stack that writes the key/value cache the expert reads.  Weight
+ * blob (float32):
+ *   for each layer l < NL: W_qkv [D][(H+2*KVH)*Dh] (q, k, v heads), W_o
+ *                          [H*Dh][D], W_gu [D][2F] (gate, then up), W_down
+ *                          [F][D];
+ *   G [2*NL][D]: RMSNorm gains, row 2l before attention, 2l+1 before the MLP.
+ * Per layer: n = RMSNorm(x) * (1 + g); q, k, v = n W_qkv with RoPE on q and
+ * k at positions 0..T-1; kout[l] = k, vout[l] = v; o = causal attention
+ * (token i sees 0..i, scale 1/sqrt(Dh)); x += o W_o; n = RMSNorm(x) * (1 + g');
+ * x += (GELU_tanh(n W_g) * (n W_u)) W_down.  The last layer stops after its
+ * cache.  kout and vout: [NL][T][KVH*Dh]; trace (optional): x after every
+ * layer but the last, [NL-1][T][D].  Returns 0, or -1 on a bad argument.
+ */
+int orc_prefill(const orc_config* cfg, const float* weights, const float* x_in, int T, double* kout, double* vout,
+                double* trace);
+
+/* Number of float32 values in the prefill weight blob for cfg. */
+size_t orc_prefill_weight_count(const orc_config* cfg);
+
 #ifdef __cplusplus
 }
 #endif

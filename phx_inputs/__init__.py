@@ -17,7 +17,9 @@ Recipe (stated once, used everywhere):
     drawn uniformly from {512, 640, 768, 800};
   * large-token workloads: the video-action chunk draws its cache like the
     prefix K/V above (4096 of 8192 rows used) and its 256 chunk rows as the
-    noise; the DiT-style step draws its 4128 token rows x [T][D] as the noise.
+    noise; the DiT-style step draws its 4128 token rows x [T][D] as the noise;
+    the prefix prefill draws its token rows x [rows][D] as the noise (its
+    norm gains G are part of the one N(0, 0.02) weight draw).
 
 The prefix K/V stands in for the key/value cache a vision-language prefix of
 about 500 to 800 tokens would write; random values match its shape and bytes,
@@ -58,6 +60,12 @@ WORKLOADS = {
     "wam_dit_bf16": dict(_BASE, id=4, block="dit", layers=4, width=3072, n_heads=24, head_dim=128,
                          n_kv_heads=24, mlp_hidden=12288, state_dim=3072, rows=4128, batch=1, capacity=0,
                          steps=1, dt=0.0, dtype="bf16", prefix_lens=[0]),
+    # prefix prefill: the 18-layer language model (width 2048, 8 query heads x 256 over one K/V head,
+    # GeGLU 16384, causal) over a 768-token prefix in an 800-row bucket; writes the K/V the expert reads.
+    # The token rows x [rows][D] are drawn as the noise; prefix_lens holds the prefilled length.
+    "prefix_prefill_bf16": dict(_BASE, id=5, block="prefill", layers=18, width=2048, n_heads=8, head_dim=256,
+                                n_kv_heads=1, mlp_hidden=16384, state_dim=2048, rows=800, batch=1, capacity=0,
+                                steps=1, dt=0.0, dtype="bf16", prefix_lens=[768]),
 }
 
 RAGGED_CHOICES = (512, 640, 768, 800)
@@ -94,6 +102,8 @@ def weight_count(cfg: dict) -> int:
     qkv = (H + 2 * KVH) * Dh
     if cfg.get("block", "decoder") == "dit":
         return NL * (D * qkv + H * Dh * D + D * F + F * D) + NL * E * 6 * D
+    if cfg.get("block", "decoder") == "prefill":
+        return NL * (D * qkv + H * Dh * D + D * 2 * F + F * D) + 2 * NL * D
     per_layer = D * qkv + H * Dh * D + D * 2 * F + F * D
     return A * D + NL * per_layer + D * A + (2 * NL + 1) * E * 2 * D
 
@@ -166,6 +176,15 @@ def weight_slices(cfg: dict) -> dict:
             put(f"W_up.{l}", (D, F))
             put(f"W_down.{l}", (F, D))
         put("W_mod", (NL, E, 6 * D))
+        assert off == weight_count(cfg)
+        return out
+    if cfg.get("block", "decoder") == "prefill":
+        for l in range(NL):
+            put(f"W_qkv.{l}", (D, qkv))
+            put(f"W_o.{l}", (H * Dh, D))
+            put(f"W_gu.{l}", (D, 2 * F))
+            put(f"W_down.{l}", (F, D))
+        put("G", (2 * NL, D))
         assert off == weight_count(cfg)
         return out
     put("W_in", (A, D))

@@ -435,9 +435,155 @@ def pin_dit_invariants(lib):
     _close(_dit(c2, W2, x2, lib), want2, what="single-token attention is the identity on v")
 
 
+# ---------------------------------------------------------------- prefix prefill
+
+def tiny_prefill_cfg(**kw):
+    cfg = dict(id=95, block="prefill", layers=3, width=16, n_heads=4, head_dim=8, n_kv_heads=2, mlp_hidden=12,
+               state_dim=16, rows=7, batch=1, capacity=0, steps=1, time_emb_dim=2, tau0=0.0, dt=0.0, rms_eps=1e-6,
+               rope_base=10000.0, dtype="f32", weight_std=0.3, prefix_lens=[7])
+    cfg.update(kw)
+    return cfg
+
+
+def torch_prefill(cfg, W, x, T):
+    """Brute force: the causal prefill composed from torch double-precision
+    primitives (rms_norm, matmul, rotate-half RoPE from cos/sin, scaled dot
+    product attention with is_causal and the kv heads repeated, tanh GELU).
+    Returns (keys, values) [NL][T][KVH*Dh]."""
+    NL, D, H, Dh, KVH, F_ = (cfg["layers"], cfg["width"], cfg["n_heads"], cfg["head_dim"], cfg["n_kv_heads"],
+                             cfg["mlp_hidden"])
+    t = lambda name: torch.tensor(phx_inputs.view(W, cfg, name).astype(np.float64))
+    G = t("G")
+    x = torch.tensor(np.asarray(x, dtype=np.float64).reshape(-1, D)[:T])
+    half = Dh // 2
+    theta = torch.pow(torch.tensor(cfg["rope_base"], dtype=torch.float64), -2.0 * torch.arange(half, dtype=torch.float64) / Dh)
+    ang = torch.arange(T, dtype=torch.float64)[:, None] * theta[None, :]
+    cos, sin = torch.cos(ang)[:, None, :], torch.sin(ang)[:, None, :]
+
+    def rope(y):  # y [T][nh][Dh]
+        a, b = y[..., :half], y[..., half:]
+        return torch.cat([a * cos - b * sin, b * cos + a * sin], dim=-1)
+
+    ks, vs = [], []
+    for l in range(NL):
+        n = F.rms_norm(x, (D,), eps=cfg["rms_eps"]) * (1 + G[2 * l])
+        qkv = n @ t(f"W_qkv.{l}")
+        q = rope(qkv[:, :H * Dh].reshape(T, H, Dh))
+        k = rope(qkv[:, H * Dh:(H + KVH) * Dh].reshape(T, KVH, Dh))
+        v = qkv[:, (H + KVH) * Dh:].reshape(T, KVH, Dh)
+        ks.append(k.reshape(T, KVH * Dh).numpy().copy())
+        vs.append(v.reshape(T, KVH * Dh).numpy().copy())
+        if l + 1 == NL:
+            break
+        rep = H // KVH
+        kk = k.repeat_interleave(rep, dim=1).permute(1, 0, 2).contiguous()
+        vv = v.repeat_interleave(rep, dim=1).permute(1, 0, 2).contiguous()
+        o = F.scaled_dot_product_attention(q.permute(1, 0, 2)[None], kk[None], vv[None], is_causal=True)[0]
+        x = x + o.permute(1, 0, 2).reshape(T, H * Dh) @ t(f"W_o.{l}")
+        n = F.rms_norm(x, (D,), eps=cfg["rms_eps"]) * (1 + G[2 * l + 1])
+        gu = n @ t(f"W_gu.{l}")
+        x = x + (F.gelu(gu[:, :F_], approximate="tanh") * gu[:, F_:]) @ t(f"W_down.{l}")
+    return np.stack(ks), np.stack(vs)
+
+
+def pin_prefill_brute_force(lib):
+    for kw in [dict(), dict(rows=1, prefix_lens=[1]), dict(n_kv_heads=1, layers=2), dict(n_kv_heads=4, rows=5)]:
+        cfg = tiny_prefill_cfg(**kw)
+        inp = phx_inputs.make_inputs(cfg, seed=9)
+        x = inp["noise"].reshape(cfg["rows"], cfg["width"])
+        for T in sorted({cfg["rows"], max(1, cfg["rows"] - 2)}):
+            r = oracle.prefill(cfg, inp["weights"], x, T, lib=lib)
+            k, v = torch_prefill(cfg, inp["weights"], x, T)
+            _close(r["k"], k, tol=1e-9, what=f"prefill keys vs torch composition {kw} T={T}")
+            _close(r["v"], v, tol=1e-9, what=f"prefill values vs torch composition {kw} T={T}")
+            assert r["softmax_dev"] < 1e-12
+
+
+def pin_prefill_incremental(lib):
+    """One causal pass over T tokens equals decoding them one at a time with a
+    key/value cache: token t's keys and values, in every layer, are what a
+    one-row commit of the expert's layer stack produces over the t cached
+    rows, when the expert's in-projection is the identity and its modulation
+    at flow time 0 is the prefill's gains (with E = 2 the sinusoid at tau = 0
+    is exactly [0, 1], so the modulation is row 1 of W_mod)."""
+    cfg = tiny_prefill_cfg(layers=2)
+    inp = phx_inputs.make_inputs(cfg, seed=10)
+    D, NL, T = cfg["width"], cfg["layers"], cfg["rows"]
+    x = inp["noise"].reshape(T, D)
+    ref = oracle.prefill(cfg, inp["weights"], x, T, lib=lib)
+    ecfg = dict(cfg, block="decoder", state_dim=D, rows=1, capacity=T, time_emb_dim=2, steps=1)
+    we = np.zeros(phx_inputs.weight_count(ecfg), dtype=np.float32)
+    phx_inputs.view(we, ecfg, "W_in")[:] = np.eye(D, dtype=np.float32)
+    for l in range(NL):
+        for name in ("W_qkv", "W_o", "W_gu", "W_down"):
+            phx_inputs.view(we, ecfg, f"{name}.{l}")[:] = phx_inputs.view(inp["weights"], cfg, f"{name}.{l}")
+    wm = phx_inputs.view(we, ecfg, "W_mod")
+    wm[:2 * NL, 1, :D] = phx_inputs.view(inp["weights"], cfg, "G")
+    kvd = cfg["n_kv_heads"] * cfg["head_dim"]
+    kc = np.zeros((1, NL, T, kvd), dtype=np.float32)
+    vc = np.zeros((1, NL, T, kvd), dtype=np.float32)
+    kc[0] = ref["k"].astype(np.float32)
+    vc[0] = ref["v"].astype(np.float32)
+    for t in range(T):
+        got = oracle.commit(ecfg, we, kc, vc, np.array([t], dtype=np.int32), x[t].reshape(1, 1, D), 0.0,
+                            pos0=[0], lib=lib)
+        _close(got["k"][0, :, 0], ref["k"][:, t], tol=1e-6, what=f"prefill keys of token {t} vs one-row commit")
+        _close(got["v"][0, :, 0], ref["v"][:, t], tol=1e-6, what=f"prefill values of token {t} vs one-row commit")
+
+
+def pin_prefill_invariants(lib):
+    cfg = tiny_prefill_cfg()
+    inp = phx_inputs.make_inputs(cfg, seed=11)
+    D, NL, T, H, Dh, KVH = (cfg["width"], cfg["layers"], cfg["rows"], cfg["n_heads"], cfg["head_dim"],
+                            cfg["n_kv_heads"])
+    W = inp["weights"]
+    x = inp["noise"].reshape(T, D)
+    base = oracle.prefill(cfg, W, x, T, lib=lib)
+    # causal: changing token j leaves every earlier token's keys and values unchanged, bit for bit
+    j = 4
+    xp = x.copy()
+    xp[j:] = -xp[j:] + 1.0
+    pert = oracle.prefill(cfg, W, xp, T, lib=lib)
+    assert np.array_equal(pert["k"][:, :j], base["k"][:, :j]) and np.array_equal(pert["v"][:, :j], base["v"][:, :j]), \
+        "tokens before a change must keep their cache"
+    assert not np.allclose(pert["k"][1:, j:], base["k"][1:, j:]), "tokens from the change on must move"
+    # a shorter prefill is the head of a longer one, bit for bit
+    short = oracle.prefill(cfg, W, x, 3, lib=lib)
+    assert np.array_equal(short["k"], base["k"][:, :3]) and np.array_equal(short["v"], base["v"][:, :3])
+    # zero residual branches: the stream stays x, so layer l's cache is the projection of
+    # RMSNorm(x) * (1 + G[2l]) with rotate-half RoPE at positions 0..T-1 on the keys
+    wz = W.copy()
+    for l in range(NL):
+        phx_inputs.view(wz, cfg, f"W_o.{l}")[:] = 0.0
+        phx_inputs.view(wz, cfg, f"W_down.{l}")[:] = 0.0
+    z = oracle.prefill(cfg, wz, x, T, lib=lib)
+    xd = x.astype(np.float64)
+    rms = np.sqrt(np.mean(xd * xd, axis=1, keepdims=True) + cfg["rms_eps"])
+    G = phx_inputs.view(wz, cfg, "G").astype(np.float64)
+    half = Dh // 2
+    for l in range(NL):
+        n = xd / rms * (1.0 + G[2 * l])
+        Wq = phx_inputs.view(wz, cfg, f"W_qkv.{l}").astype(np.float64)
+        k = (n @ Wq[:, H * Dh:(H + KVH) * Dh]).reshape(T, KVH, Dh)
+        v = n @ Wq[:, (H + KVH) * Dh:]
+        # RoPE as a complex rotation of (k_j + i k_{j+half}) by angle p * base^(-2j/Dh)
+        zc = (k[..., :half] + 1j * k[..., half:]) * np.exp(
+            1j * np.arange(T)[:, None, None] * cfg["rope_base"] ** (-2.0 * np.arange(half) / Dh))
+        kr = np.concatenate([zc.real, zc.imag], axis=-1).reshape(T, KVH * Dh)
+        _close(z["k"][l], kr, tol=1e-12, what=f"zero-branch keys, layer {l}")
+        _close(z["v"][l], v, tol=1e-12, what=f"zero-branch values, layer {l}")
+    # the first token attends only to itself: with one layer of queries zeroed the result is unchanged
+    wq = W.copy()
+    phx_inputs.view(wq, cfg, "W_qkv.0")[:, :H * Dh] = 0.0
+    one = oracle.prefill(cfg, wq, x, 1, lib=lib)
+    ref1 = oracle.prefill(cfg, W, x, 1, lib=lib)
+    _close(one["k"], ref1["k"], tol=1e-12, what="a single token's cache does not depend on its queries")
+
+
 ALL_PINS = [pin_time_embedding, pin_modulation, pin_matmul, pin_ada_rmsnorm, pin_rope, pin_gelu, pin_attention,
             pin_decide_brute_force, pin_decide_invariants, pin_ada_layernorm, pin_dit_brute_force, pin_dit_invariants,
-            pin_decide_at_brute_force, pin_commit_brute_force]
+            pin_decide_at_brute_force, pin_commit_brute_force, pin_prefill_brute_force, pin_prefill_incremental,
+            pin_prefill_invariants]
 
 
 def run_all(lib):

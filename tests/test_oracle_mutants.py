@@ -64,6 +64,20 @@ MUTANTS = [
      "memcpy(v + (size_t)t * hd, src + hd, sizeof(double) * hd);"),
     ("dit: GELU left out", "for (size_t i = 0; i < (size_t)T * F; ++i) up[i] = orc_gelu_tanh(up[i]);", ""),
     ("dit: modulation from the wrong block", "const float* Wm = W_mod + (size_t)b * E * 6 * D;", "const float* Wm = W_mod;"),
+    ("prefill: wrong kv head mapping", "const int i = ih / H, hh = ih % H, g = hh / group;",
+     "const int i = ih / H, hh = ih % H, g = hh % KVH;"),
+    ("prefill: MLP norm uses the attention gains", "mod[d] = (double)G[(size_t)(2 * l + 1) * D + d];",
+     "mod[d] = (double)G[(size_t)(2 * l) * D + d];"),
+    ("prefill: positions start at one", "for (int i = 0; i < T; ++i) pos[i] = i;",
+     "for (int i = 0; i < T; ++i) pos[i] = i + 1;"),
+    ("prefill: values captured as keys", "memcpy(vout + (size_t)l * T * kvd, v,", "memcpy(vout + (size_t)l * T * kvd, k,"),
+    ("prefill: RoPE not applied to keys", "orc_rope(T, KVH, Dh, pos, c->rope_base, k);", ""),
+    ("prefill: attention residual replaced", "x[i] += proj[i];\n\n    for (int d = 0; d < D; ++d) mod[d]",
+     "x[i] = proj[i];\n\n    for (int d = 0; d < D; ++d) mod[d]"),
+    ("prefill: gate and up swapped",
+     "orc_gelu_tanh(gu[(size_t)t * 2 * F + f]) * gu[(size_t)t * 2 * F + F + f]",
+     "orc_gelu_tanh(gu[(size_t)t * 2 * F + F + f]) * gu[(size_t)t * 2 * F + f]"),
+    ("prefill: softmax scale dropped", "      p[t] = s * scale;", "      p[t] = s;"),
 ]
 
 
