@@ -11,6 +11,9 @@ before the timed region starts.
 8 layers x 5 steps) or wam_dit_bf16 (DiT-style step over 4128 tokens, 4
 blocks) measures the large-token plan instead; those are MFMA-bound, so their
 roofline is the dominant GEMM's TFLOP/s against the bf16 dense peak.
+--workload prefix_prefill_bf16 times the prefix prefill (18 causal layers of
+width 2048 over 768 tokens in an 800-row bucket, writing the K/V cache), one
+phx_expert_prefill call per step.
 
 Prints ONE JSON line (see --help for the knobs).  Besides the wall-clock
 figure it carries:
@@ -44,6 +47,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 WORKLOAD = "pi05_expert_bf16"
 BATCH_WORKLOADS = ("rollout_b16_bf16",)
 TOKEN_WORKLOADS = ("va_chunk_bf16", "wam_dit_bf16")
+PREFILL_WORKLOADS = ("prefix_prefill_bf16",)
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_pi05_expert_bf16.json")
 
@@ -164,7 +168,8 @@ def cpu_baseline(cfg: dict, inp: dict, budget_s: float) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", default=WORKLOAD, choices=(WORKLOAD,) + BATCH_WORKLOADS + TOKEN_WORKLOADS)
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=(WORKLOAD,) + BATCH_WORKLOADS + TOKEN_WORKLOADS + PREFILL_WORKLOADS)
     ap.add_argument("--steps", type=int, default=200, help="timed decisions")
     ap.add_argument("--warmup", type=int, default=20, help="untimed decisions before the timed region")
     ap.add_argument("--seed", type=int, default=0)
@@ -193,6 +198,8 @@ def main():
 
     if args.workload in TOKEN_WORKLOADS:
         return bench_tokens(args)
+    if args.workload in PREFILL_WORKLOADS:
+        return bench_prefill(args)
     name = args.workload
     cfg = phx_inputs.workload(name)
     log(f"bench: generating inputs for {name}")
@@ -473,6 +480,154 @@ def cpu_baseline_tokens(cfg: dict, inp: dict, fl: dict) -> dict:
     return {"value": round(dt_s * fl["flops_per_decision"] / fs * 1e3, 1), "unit": "ms/decision",
             "cores": omp_threads(), "kind": "oracle",
             "sample": f"{what} (double-precision oracle, OpenMP), scaled by FLOPs to a full decision"}
+
+
+def prefill_flops(cfg: dict, n: int) -> dict:
+    """Algorithmic work of one prefill over n tokens: every GEMM on the n token
+    rows (the last layer only its QKV: nothing after it reaches the cache),
+    causal attention (QK^T and PV over keys 0..i for token i), and bytes: the
+    weights used once, the token rows read, the cache written."""
+    D, F = cfg["width"], cfg["mlp_hidden"]
+    H, KVH, Dh, NL = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["layers"]
+    qkv, hd, kvd = (H + 2 * KVH) * Dh, H * Dh, KVH * Dh
+    rest = hd * D + D * 2 * F + F * D
+    gemm = 2 * n * (NL * D * qkv + (NL - 1) * rest)
+    attn = (NL - 1) * 4 * hd * (n * (n + 1) // 2)
+    byts = 2 * (NL * D * qkv + (NL - 1) * rest) + n * D * 4 + 2 * NL * n * kvd * 2
+    return dict(flops=gemm + attn, gemm_flops=gemm, attn_flops=attn, bytes=byts)
+
+
+def prefill_node_flops(cfg: dict, kind: int, n: int) -> int:
+    """FLOPs of one launch of a prefill kernel kind over n tokens."""
+    from flow_matching_action_decision_amd.binding import PHX_NODE as K
+    D, F = cfg["width"], cfg["mlp_hidden"]
+    H, KVH, Dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    return {K["QKV"]: 2 * n * D * (H + 2 * KVH) * Dh, K["ATTENTION"]: 4 * H * Dh * (n * (n + 1) // 2),
+            K["OUT_PROJ_RESID"]: 2 * n * H * Dh * D, K["GATEUP"]: 2 * n * D * 2 * F,
+            K["DOWN_PROJ_RESID"]: 2 * n * F * D}.get(kind, 0)
+
+
+def bench_prefill(args):
+    """The prefix prefill: time per phx_expert_prefill call (token rows in,
+    every layer's K/V out), per-kind kernel breakdown, and the dominant GEMM
+    against the MFMA bf16 peak."""
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+
+    name = args.workload
+    cfg = phx_inputs.workload(name)
+    n = int(phx_inputs.prefix_lengths(cfg)[0])
+    log(f"bench: generating inputs for {name}")
+    inp = phx_inputs.make_inputs(cfg, args.seed)
+    fl = prefill_flops(cfg, n)
+    log("bench: creating handle")
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    x = torch.from_numpy(np.ascontiguousarray(inp["noise"][0])).cuda()
+    kvd = cfg["n_kv_heads"] * cfg["head_dim"]
+    k = torch.empty((cfg["layers"], n, kvd), dtype=torch.int16, device="cuda")
+    v = torch.empty_like(k)
+    stream = torch.cuda.current_stream()
+    steps = min(args.steps, 50)
+    warm = min(args.warmup, 5)
+    for _ in range(warm):
+        ex.prefill(x, n, k, v)
+    torch.cuda.synchronize()
+    log(f"bench: timing {steps} prefills")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        ex.prefill(x, n, k, v)
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / steps
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+    log(f"bench: {ms:.4f} ms/prefill")
+
+    nodes = ex.nodes()
+    idx = list(range(len(nodes)))
+    t = ex.time_nodes(idx, reps=max(3, min(args.kernel_reps, 10)))
+    kinds = {}
+    for i, tm in zip(idx, t):
+        nd = nodes[i]
+        kk = kinds.setdefault(nd["name"], dict(kind=nd["kind"], launches=0, ms=0.0, flops=0))
+        kk["launches"] += 1
+        kk["ms"] += tm
+        kk["flops"] += prefill_node_flops(cfg, nd["kind"], n)
+    for nm, kk in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
+        tf = kk["flops"] / (kk["ms"] * 1e-3) / 1e12 if kk["flops"] else 0.0
+        log(f"  {nm:24s} x{kk['launches']:3d}  {kk['ms'] * 1e3 / kk['launches']:9.1f} us/launch  {tf:7.1f} TFLOP/s")
+    dom_name = max(kinds, key=lambda nm: kinds[nm]["flops"])
+    dk = kinds[dom_name]
+    us = dk["ms"] * 1e3 / dk["launches"]
+    f_launch = dk["flops"] // dk["launches"]
+    achieved = f_launch / (us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom_name,
+                "flops_per_launch": f_launch, "us_per_launch": round(us, 3),
+                "kernel_hash": kernel_source_hash(TOKEN_KERNEL_SOURCES)}
+    kh = _bf16_bits_to_f32(k)
+    assert np.all(np.isfinite(kh)), "non-finite cache"
+    nk = ex.kernels_per_decision()
+    ex.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline_prefill(cfg, inp, fl)
+
+    tflops = fl["flops"] / (ms * 1e-3) / 1e12
+    line = {
+        "metric": f"ms/prefill ({name}) + % of MFMA bf16 peak, 1 GPU",
+        "value": round(ms, 4), "unit": "ms/prefill", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) bf16 weights and gains, N(0,1) token rows)",
+        "config": {"workload": name, "block": "prefill", "layers": cfg["layers"], "tokens": n,
+                   "bucket_rows": cfg["rows"], "width": cfg["width"],
+                   "heads": f"{cfg['n_heads']}x{cfg['head_dim']} / {cfg['n_kv_heads']} kv",
+                   "mlp_hidden": cfg["mlp_hidden"], "mask": "causal"},
+        "prefills_per_s": round(1000.0 / ms, 2),
+        "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
+        "flops_per_prefill": fl["flops"], "tflops": round(tflops, 1),
+        "mfma_frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "algorithmic_bytes_per_prefill": fl["bytes"], "hbm_gbs": round(fl["bytes"] / (ms * 1e-3) / 1e9, 1),
+        "kernels_per_prefill": nk, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _bf16_bits_to_f32(t) -> np.ndarray:
+    u = t.cpu().numpy().view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32)
+
+
+def cpu_baseline_prefill(cfg: dict, inp: dict, fl: dict) -> dict:
+    """Time the oracle, unchanged, on a bounded sample of the prefill (the
+    first two layers over the first 64 tokens) and scale by the FLOP ratio to
+    the whole prefill."""
+    import oracle
+    lib = oracle.load()
+    n = 64
+    sc = dict(cfg, layers=2)
+    wsl = phx_inputs.weight_slices(cfg)
+    ssl = phx_inputs.weight_slices(sc)
+    w = np.empty(phx_inputs.weight_count(sc), dtype=np.float32)
+    for nm, (off, shape) in ssl.items():
+        m = int(np.prod(shape))
+        o2, _ = wsl[nm]
+        w[off:off + m] = inp["weights"][o2:o2 + m]
+    t0 = time.perf_counter()
+    oracle.prefill(sc, w, inp["noise"][0], n, lib=lib)
+    dt_s = time.perf_counter() - t0
+    fs = prefill_flops(sc, n)["flops"]
+    return {"value": round(dt_s * fl["flops"] / fs * 1e3, 1), "unit": "ms/prefill", "cores": omp_threads(),
+            "kind": "oracle",
+            "sample": f"the first two layers over the first {n} tokens (double-precision oracle, OpenMP), "
+                      f"scaled by FLOPs to the whole prefill"}
 
 
 if __name__ == "__main__":

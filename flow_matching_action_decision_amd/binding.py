@@ -19,19 +19,21 @@ PHX_DTYPE_F32, PHX_DTYPE_BF16 = 0, 1
 PHX_FLAG_NO_GRAPH = 1
 PHX_FLAG_MULTI_KERNEL = 2
 PHX_FLAG_TIMELINE = 4
-PHX_BLOCK_DECODER, PHX_BLOCK_DIT = 0, 1
+PHX_BLOCK_DECODER, PHX_BLOCK_DIT, PHX_BLOCK_PREFILL = 0, 1, 2
+_BLOCKS = dict(decoder=PHX_BLOCK_DECODER, dit=PHX_BLOCK_DIT, prefill=PHX_BLOCK_PREFILL)
 # launch kinds reported by phx_expert_node_info
 PHX_NODE = dict(IN_PROJ=1, NORM_QKV_ROPE=2, ATTENTION=3, ATTN_COMBINE=4, OUT_PROJ_RESID=5, NORM_GATEUP_GEGLU=6,
                 DOWN_PROJ_RESID=7, NORM_OUT_EULER=8, DECISION=9, TAG_ADVANCE=10, ROW_NORM=11, QKV=12, GATEUP=13,
                 OUT_EULER=14, STATE_CVT=15)
-PHX_MASK_FULL = 0
+PHX_MASK_FULL, PHX_MASK_CAUSAL = 0, 1
 
 # every function include/phx_expert.h declares
 EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_expert_create",
             "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_destroy", "phx_last_error",
             "phx_expert_kernels_per_decision", "phx_expert_node_info", "phx_expert_launch_node",
             "phx_expert_status", "phx_expert_timeline", "phx_expert_capsule_bytes", "phx_expert_capsule_regions",
-            "phx_expert_capsule_save", "phx_expert_capsule_restore", "phx_expert_commit_chunk")
+            "phx_expert_capsule_save", "phx_expert_capsule_restore", "phx_expert_commit_chunk",
+            "phx_expert_prefill")
 
 NODE_KINDS = {1: "in_proj", 2: "norm_qkv_rope", 3: "attention", 4: "attention_combine", 5: "out_proj_resid",
               6: "norm_gateup_geglu", 7: "down_proj_resid", 8: "norm_out_proj_euler", 9: "decision_kernel",
@@ -100,6 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phx_expert_capsule_save.argtypes = [P, P, ctypes.c_size_t, P]
     lib.phx_expert_capsule_restore.argtypes = [P, P, ctypes.c_size_t, P]
     lib.phx_expert_commit_chunk.argtypes = [P, P, P]
+    lib.phx_expert_prefill.argtypes = [P, P, ctypes.c_int32, P, P, P]
     _lib = lib
     return lib
 
@@ -114,8 +117,8 @@ def make_config(cfg: dict, flags: int = 0) -> phx_expert_config:
         batch=cfg["batch"], prefix_capacity=cfg["capacity"], steps=cfg["steps"], time_emb_dim=cfg["time_emb_dim"],
         tau0=cfg["tau0"], dt=cfg["dt"], rms_eps=cfg["rms_eps"], rope_base=cfg["rope_base"],
         weight_dtype=dt, kv_dtype=dt, flags=flags | int(cfg.get("flags", 0)),
-        block_kind=PHX_BLOCK_DIT if cfg.get("block", "decoder") == "dit" else PHX_BLOCK_DECODER,
-        mask_kind=PHX_MASK_FULL)
+        block_kind=_BLOCKS[cfg.get("block", "decoder")],
+        mask_kind=PHX_MASK_CAUSAL if cfg.get("block", "decoder") == "prefill" else PHX_MASK_FULL)
 
 
 def _check(rc: int):
@@ -223,3 +226,8 @@ def phx_expert_capsule_restore(h: int, capsule: int, nbytes: int, stream: int = 
 
 def phx_expert_commit_chunk(h: int, chunk: int, stream: int = 0):
     _check(load_library().phx_expert_commit_chunk(ctypes.c_void_p(h), ctypes.c_void_p(chunk), ctypes.c_void_p(stream)))
+
+
+def phx_expert_prefill(h: int, x: int, prefix_len: int, k: int, v: int, stream: int = 0):
+    _check(load_library().phx_expert_prefill(ctypes.c_void_p(h), ctypes.c_void_p(x), prefix_len, ctypes.c_void_p(k),
+                                             ctypes.c_void_p(v), ctypes.c_void_p(stream)))

@@ -222,6 +222,7 @@ size_t weight_elems(const phx_expert_config* c) {
   const size_t qkv = (size_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
   const size_t hd = (size_t)c->n_heads * c->head_dim;
   if (c->block_kind == PHX_BLOCK_DIT) return NL * (D * qkv + hd * D + D * F + F * D) + NL * E * 6 * D;
+  if (c->block_kind == PHX_BLOCK_PREFILL) return NL * (D * qkv + hd * D + D * 2 * F + F * D) + 2 * NL * D;
   const size_t per_layer = D * qkv + hd * D + D * 2 * F + F * D;
   return A * D + NL * per_layer + D * A + (2 * NL + 1) * E * 2 * D;
 }
@@ -521,7 +522,7 @@ int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t 
 
 
 bool uses_tokens(const phx_expert_config& c) {
-  return c.block_kind == PHX_BLOCK_DIT || (long long)c.rows * c.batch > 160;
+  return c.block_kind != PHX_BLOCK_DECODER || (long long)c.rows * c.batch > 160;
 }
 
 // A bf16 batch of 65..160 rows: the large-token GEMMs on all rows at once
@@ -577,6 +578,7 @@ int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s) {
 int build_tok_nodes(phx_expert* h, bool commit = false) {
   const phx_expert_config& c = h->cfg;
   const bool dit = c.block_kind == PHX_BLOCK_DIT;
+  const bool prefill = c.block_kind == PHX_BLOCK_PREFILL;
   const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = h->trows;
   const int NL = c.layers, Dh = c.head_dim;
   const int HD = H * Dh, NQKV = (H + 2 * KVH) * Dh, kvd = KVH * Dh;
@@ -651,7 +653,8 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     a.M = M; a.H = H; a.KVH = KVH; a.o = h->o; a.po = h->po; a.pml = h->pml; a.splits = h->splits;
     a.scale = (float)(1.0 / std::sqrt((double)Dh));
     a.hd = Dh;
-    name_of(nd, "attention");
+    a.causal = prefill ? 1 : 0;
+    name_of(nd, prefill ? "causal_attention" : "attention");
     h->tnodes.push_back(nd);
     if (h->splits > 1) {
       TokNode cb = nd;
@@ -673,6 +676,27 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
       gemm(PHX_NODE_GATEUP, 0, l, tok::EP_GELU, h->nb, h->off_gu[l], D, F, h->act, F, nullptr, "up_gelu");
       gemm(PHX_NODE_DOWN_PROJ_RESID, 0, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, mod + 5 * D,
            "down_proj_gated_resid");
+    }
+    return PHX_OK;
+  }
+  if (prefill) {
+    // the prefix prefill: per layer RMS norm with the layer's gains, QKV with RoPE (the layer's keys and
+    // values land in rows 0.. of its key rows and value fragments), causal attention, out-projection +
+    // residual, RMS norm, gate/up with GeGLU, down-projection + residual; the last layer writes its
+    // cache and needs nothing after its QKV
+    for (int l = 0; l < NL; ++l) {
+      const float* m1 = h->modtab + (size_t)(2 * l) * 2 * D;
+      const float* m2 = h->modtab + (size_t)(2 * l + 1) * 2 * D;
+      norm(0, l, 0, m1, m1 + D, "rmsnorm_attn");
+      qkv(0, l, "qkv_rope");
+      if (l + 1 == NL) break;
+      attention(0, l);
+      gemm(PHX_NODE_OUT_PROJ_RESID, 0, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, nullptr,
+           "out_proj_resid");
+      norm(0, l, 0, m2, m2 + D, "rmsnorm_mlp");
+      gemm(PHX_NODE_GATEUP, 0, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu");
+      gemm(PHX_NODE_DOWN_PROJ_RESID, 0, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, nullptr,
+           "down_proj_resid");
     }
     return PHX_OK;
   }
@@ -786,6 +810,7 @@ int capture_tok(phx_expert* h, const std::vector<TokNode>& list, hipGraph_t* gra
 int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_off) {
   const phx_expert_config& c = h->cfg;
   const bool dit = c.block_kind == PHX_BLOCK_DIT;
+  const bool prefill = c.block_kind == PHX_BLOCK_PREFILL;
   h->trows = c.rows * c.batch;
   const int D = c.width, H = c.n_heads, KVH = c.n_kv_heads, F = c.mlp_hidden, A = c.state_dim, M = h->trows;
   const int NL = c.layers, S = c.steps, E = c.time_emb_dim, C = c.prefix_capacity;
@@ -795,21 +820,38 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   int rc;
   // modulation: decoder [S][2NL+1][2D] (scale | shift per norm); DiT [NL][6D] at tau0
   // (the decoder gets one more step row, at the end flow time tau0 + S dt, for the history update)
+  // (the prefill's norms take its gains: [2NL][2D] rows of scale = g, shift = 0)
   const int MS = dit ? 1 : S + 1, NN = dit ? NL : 2 * NL + 1, MW = dit ? 6 * D : 2 * D;
   void* etab = nullptr;
-  if ((rc = alloc(h, &etab, (size_t)MS * E * sizeof(double), "time embedding"))) return rc;
-  if ((rc = alloc(h, (void**)&h->modtab, (size_t)MS * NN * MW * sizeof(float), "modulation table"))) return rc;
-  PHX_HIP(launch_time_embedding((double*)etab, MS, E, c.tau0, c.dt, stream));
-  PHX_HIP(launch_modulation(1, sb + mod_off * 2, (const double*)etab, h->modtab, MS, NN, E, MW, stream));
+  if (prefill) {
+    const size_t ng = (size_t)2 * NL * D;
+    std::vector<uint16_t> gb(ng);
+    std::vector<float> tab(2 * ng, 0.f);
+    PHX_HIP(hipMemcpyAsync(gb.data(), sb + mod_off * 2, ng * 2, hipMemcpyDeviceToHost, stream));
+    PHX_HIP(hipStreamSynchronize(stream));
+    for (size_t n = 0; n < (size_t)2 * NL; ++n)
+      for (int d = 0; d < D; ++d) {
+        const uint32_t u = (uint32_t)gb[n * D + d] << 16;  // bf16 -> f32 is exact
+        std::memcpy(&tab[n * 2 * D + d], &u, 4);
+      }
+    if ((rc = alloc(h, (void**)&h->modtab, tab.size() * sizeof(float), "norm gains"))) return rc;
+    PHX_HIP(hipMemcpyAsync(h->modtab, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, stream));
+    PHX_HIP(hipStreamSynchronize(stream));
+  } else {
+    if ((rc = alloc(h, &etab, (size_t)MS * E * sizeof(double), "time embedding"))) return rc;
+    if ((rc = alloc(h, (void**)&h->modtab, (size_t)MS * NN * MW * sizeof(float), "modulation table"))) return rc;
+    PHX_HIP(launch_time_embedding((double*)etab, MS, E, c.tau0, c.dt, stream));
+    PHX_HIP(launch_modulation(1, sb + mod_off * 2, (const double*)etab, h->modtab, MS, NN, E, MW, stream));
+  }
 
   // key rows: the prefix capacity plus the chunk, padded to whole 64-key blocks
   h->R = (C + M + 63) / 64 * 64;
   const int R = h->R;
-  // attention key splits: enough workgroups to cover the chip, at least four key blocks per split
+  // attention key splits: enough workgroups to cover the chip, at least two key blocks per split
   const long long q_wgs = (long long)((M + 127) / 128) * H;
   const int max_blocks = R / 64;
   h->splits = 1;
-  while (q_wgs * h->splits < 256 && max_blocks / (h->splits * 2) >= 4) h->splits *= 2;
+  while (q_wgs * h->splits < 256 && max_blocks / (h->splits * 2) >= 2) h->splits *= 2;
 
   struct Buf { void** p; size_t bytes; const char* what; };
   std::vector<Buf> bufs = {
@@ -845,8 +887,10 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
     bufs.push_back({&h->tv, (size_t)(dit ? 1 : NL) * R * kvd * 2, "value fragments"});
   }
   if (!dit && !h->batched) {
-    bufs.push_back({(void**)&h->x, (size_t)Mp * A * 4, "state rows"});
-    bufs.push_back({&h->xb, (size_t)Mp * A * 2, "bf16 state rows"});
+    if (!prefill) {  // the prefill's token rows go straight into the residual rows
+      bufs.push_back({(void**)&h->x, (size_t)Mp * A * 4, "state rows"});
+      bufs.push_back({&h->xb, (size_t)Mp * A * 2, "bf16 state rows"});
+    }
     bufs.push_back({(void**)&h->lens, sizeof(int), "prefix length"});
     bufs.push_back({(void**)&h->rope, (size_t)M * (c.head_dim / 2) * sizeof(float2), "position table"});
   }
@@ -858,15 +902,17 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
     if ((rc = alloc(h, b.p, b.bytes, b.what))) return rc;
     PHX_HIP(hipMemsetAsync(*b.p, 0, b.bytes, stream));
   }
+  // the prefill's tokens sit at positions 0 .. M-1 with no cached rows before them
+  if (prefill) PHX_HIP(tok::launch_positions(h->lens, h->rope, 0, 0, M, c.head_dim, (double)c.rope_base, stream));
   PHX_HIP(hipStreamSynchronize(stream));
-  for (size_t i = 0; i < h->allocs.size(); ++i)
+  for (size_t i = 0; etab && i < h->allocs.size(); ++i)
     if (h->allocs[i] == etab) {
       (void)hipFree(etab);
       h->allocs.erase(h->allocs.begin() + (long)i);
       break;
     }
 
-  if (!dit && !h->batched) {
+  if (!dit && !prefill && !h->batched) {
     if ((rc = build_tok_nodes(h, true))) return rc;
     h->cnodes.swap(h->tnodes);
   }
@@ -906,7 +952,9 @@ std::vector<StateRegion> state_regions(const phx_expert* h) {
   const phx_expert_config& c = h->cfg;
   std::vector<StateRegion> r;
   if (h->tokens && !h->batched) {
-    if (c.block_kind == PHX_BLOCK_DIT) return r;  // no prefix: nothing persists between decisions
+    // the DiT-style step has no prefix, and the prefill hands its cache to the caller:
+    // nothing persists between calls
+    if (c.block_kind != PHX_BLOCK_DECODER) return r;
     const size_t kv = (size_t)c.layers * h->R * c.n_kv_heads * c.head_dim * 2;
     r.push_back({"key_rows", h->tk, kv});
     r.push_back({"value_fragments", h->tv, kv});
@@ -1025,25 +1073,33 @@ int phx_expert_validate_config(const phx_expert_config* c) {
     return fail(PHX_E_SHAPE, "mlp_hidden %d must be a positive multiple of 128", c->mlp_hidden);
   if (c->state_dim < 32 || c->state_dim % 32)
     return fail(PHX_E_SHAPE, "state_dim %d must be a positive multiple of 32", c->state_dim);
-  if (c->block_kind != PHX_BLOCK_DECODER && c->block_kind != PHX_BLOCK_DIT)
+  if (c->block_kind != PHX_BLOCK_DECODER && c->block_kind != PHX_BLOCK_DIT && c->block_kind != PHX_BLOCK_PREFILL)
     return fail(PHX_E_INVALID, "block_kind %d unknown", c->block_kind);
-  if (c->mask_kind != PHX_MASK_FULL) return fail(PHX_E_INVALID, "mask_kind %d unknown", c->mask_kind);
+  if (c->mask_kind != PHX_MASK_FULL && c->mask_kind != PHX_MASK_CAUSAL)
+    return fail(PHX_E_INVALID, "mask_kind %d unknown", c->mask_kind);
+  if ((c->mask_kind == PHX_MASK_CAUSAL) != (c->block_kind == PHX_BLOCK_PREFILL))
+    return fail(PHX_E_SHAPE, "the prefix prefill takes the causal mask, the other blocks the full mask");
   if (c->rows < 1 || c->batch < 1) return fail(PHX_E_SHAPE, "rows and batch must be positive");
-  const bool tokens = c->block_kind == PHX_BLOCK_DIT || (long long)c->rows * c->batch > 160;
+  const bool tokens = c->block_kind != PHX_BLOCK_DECODER || (long long)c->rows * c->batch > 160;
   if (tokens) {
     // the large-token plan: one chunk of many rows
     if (c->batch != 1 || c->rows > 16384)
-      return fail(PHX_E_SHAPE, "more than 160 rows needs batch 1 and rows <= 16384 (rows %d, batch %d)", c->rows,
+      return fail(PHX_E_SHAPE, "the large-token plan needs batch 1 and rows <= 16384 (rows %d, batch %d)", c->rows,
                   c->batch);
-    if (c->weight_dtype != PHX_DTYPE_BF16) return fail(PHX_E_SHAPE, "more than 160 rows needs bf16 weights");
+    if (c->weight_dtype != PHX_DTYPE_BF16) return fail(PHX_E_SHAPE, "the large-token plan needs bf16 weights");
     if (c->head_dim != 128 && c->head_dim != 256)
-      return fail(PHX_E_SHAPE, "more than 160 rows needs head_dim 128 or 256");
-    if (c->state_dim % 128) return fail(PHX_E_SHAPE, "more than 160 rows needs state_dim a multiple of 128");
+      return fail(PHX_E_SHAPE, "the large-token plan needs head_dim 128 or 256");
+    if (c->state_dim % 128) return fail(PHX_E_SHAPE, "the large-token plan needs state_dim a multiple of 128");
     if (c->block_kind == PHX_BLOCK_DIT) {
       if (c->state_dim != c->width) return fail(PHX_E_SHAPE, "the DiT-style block needs state_dim == width");
       if (c->n_kv_heads != c->n_heads) return fail(PHX_E_SHAPE, "the DiT-style block needs n_kv_heads == n_heads");
       if (c->prefix_capacity != 0) return fail(PHX_E_SHAPE, "the DiT-style block has no prefix (capacity 0)");
       if (c->steps != 1) return fail(PHX_E_SHAPE, "the DiT-style block runs one step");
+    }
+    if (c->block_kind == PHX_BLOCK_PREFILL) {
+      if (c->state_dim != c->width) return fail(PHX_E_SHAPE, "the prefix prefill needs state_dim == width");
+      if (c->prefix_capacity != 0) return fail(PHX_E_SHAPE, "the prefix prefill reads no cache (capacity 0)");
+      if (c->steps != 1) return fail(PHX_E_SHAPE, "the prefix prefill runs one pass");
     }
   } else if ((c->n_heads / c->n_kv_heads) * c->rows > 128) {
     return fail(PHX_E_SHAPE, "query rows per kv head (n_heads/n_kv_heads*rows = %d) must be at most 128",
@@ -1118,12 +1174,14 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
 
   // ---- static: tiled weights (everything but W_mod) ----
   // decoder blob: W_in, per layer [W_qkv, W_o, W_gu, W_down], W_out, W_mod;
-  // DiT-style blob: per block [W_qkv, W_o, W_up, W_down], W_mod
+  // DiT-style blob: per block [W_qkv, W_o, W_up, W_down], W_mod;
+  // prefill blob: per layer [W_qkv, W_o, W_gu, W_down], the norm gains
   const bool dit = c.block_kind == PHX_BLOCK_DIT;
+  const bool io = c.block_kind == PHX_BLOCK_DECODER;  // in- and out-linears around the stack
   const int gu_cols = dit ? F : 2 * F;
   size_t off = 0;
   h->off_in = off;
-  if (!dit) off += (size_t)A * D;
+  if (io) off += (size_t)A * D;
   for (int l = 0; l < NL; ++l) {
     h->off_qkv.push_back(off); off += (size_t)D * qkvN;
     h->off_o.push_back(off); off += (size_t)H * Dh * D;
@@ -1131,7 +1189,7 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
     h->off_down.push_back(off); off += (size_t)F * D;
   }
   h->off_out = off;
-  if (!dit) off += (size_t)D * A;
+  if (io) off += (size_t)D * A;
   const size_t tiled_elems = off;
   const size_t total_elems = weight_elems(&c);
   if ((rc = alloc(h, &h->wt, tiled_elems * h->esz, "tiled weights"))) return rc;
@@ -1143,20 +1201,20 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
     PHX_HIP(hipMemcpyAsync(staging, weights, total_elems * h->esz, hipMemcpyHostToDevice, stream));
     src = staging;
   }
-  // the blob has the same order as the tiled arena, plus W_mod at the end
+  // the blob has the same order as the tiled arena, plus W_mod (the gains of the prefill) at the end
   const char* sb = (const char*)src;
   auto retile = [&](size_t o, int K, int N, int kind, int param) -> int {
     PHX_HIP(launch_retile(h->dtype, sb + o * h->esz, (char*)h->wt + o * h->esz, K, N, kind, param, stream));
     return PHX_OK;
   };
-  if (!dit && (rc = retile(h->off_in, A, D, COL_IDENT, 0))) return rc;
+  if (io && (rc = retile(h->off_in, A, D, COL_IDENT, 0))) return rc;
   for (int l = 0; l < NL; ++l) {
     if ((rc = retile(h->off_qkv[l], D, qkvN, COL_ROPE, Dh))) return rc;
     if ((rc = retile(h->off_o[l], H * Dh, D, COL_IDENT, 0))) return rc;
     if ((rc = retile(h->off_gu[l], D, gu_cols, dit ? COL_IDENT : COL_GEGLU, F))) return rc;
     if ((rc = retile(h->off_down[l], F, D, COL_IDENT, 0))) return rc;
   }
-  if (!dit && (rc = retile(h->off_out, D, A, COL_IDENT, 0))) return rc;
+  if (io && (rc = retile(h->off_out, D, A, COL_IDENT, 0))) return rc;
 
   h->tokens = uses_tokens(c);
   h->n_cu = prop.multiProcessorCount;
@@ -1173,7 +1231,7 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
         h->allocs.erase(h->allocs.begin() + (long)i);
         break;
       }
-    h->loaded.assign(B, dit ? 1 : 0);  // the DiT-style block has no prefix to load
+    h->loaded.assign(B, dit || c.block_kind == PHX_BLOCK_PREFILL ? 1 : 0);  // no prefix to load
     h->lens_host.assign(B, 0);
     return PHX_OK;
   }
@@ -1297,6 +1355,8 @@ int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void* k, con
   if (prefix_len > 0 && (!is_device_pointer(k) || !is_device_pointer(v)))
     return fail(PHX_E_INVALID, "k and v must be device pointers");
   hipStream_t s = (hipStream_t)stream;
+  if (c.block_kind == PHX_BLOCK_PREFILL)
+    return fail(PHX_E_INVALID, "a prefix prefill handle reads no prefix (it writes one: phx_expert_prefill)");
   if (h->tokens && c.block_kind == PHX_BLOCK_DIT) {
     h->loaded[request] = 1;  // capacity 0: nothing to copy
     g_err.clear();
@@ -1371,6 +1431,8 @@ int phx_expert_commit_chunk(phx_expert* h, const float* chunk, phx_stream_t stre
 int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_stream_t stream) {
   if (!h) return fail(PHX_E_INVALID, "handle is NULL");
   if (!noise || !actions) return fail(PHX_E_INVALID, "noise or actions is NULL");
+  if (h->cfg.block_kind == PHX_BLOCK_PREFILL)
+    return fail(PHX_E_INVALID, "a prefix prefill handle makes no decision (phx_expert_prefill)");
   for (int b = 0; b < h->cfg.batch; ++b)
     if (!h->loaded[b]) return fail(PHX_E_STATE, "request %d has no prefix loaded", b);
   hipStream_t s = (hipStream_t)stream;
@@ -1392,6 +1454,42 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
   }
   if (h->persistent) ++h->seq_host;
   PHX_HIP(hipMemcpyAsync(actions, state, xb, hipMemcpyDefault, s));
+  g_err.clear();
+  return PHX_OK;
+}
+
+int phx_expert_prefill(phx_expert* h, const float* x, int32_t prefix_len, void* k, void* v, phx_stream_t stream) {
+  if (!h) return fail(PHX_E_INVALID, "handle is NULL");
+  const phx_expert_config& c = h->cfg;
+  if (c.block_kind != PHX_BLOCK_PREFILL) return fail(PHX_E_INVALID, "not a prefix prefill handle");
+  if (prefix_len < 0 || prefix_len > c.rows)
+    return fail(PHX_E_SHAPE, "prefix_len %d outside [0, %d]", prefix_len, c.rows);
+  if (prefix_len == 0) {
+    g_err.clear();
+    return PHX_OK;
+  }
+  if (!x || !k || !v) return fail(PHX_E_INVALID, "x, k or v is NULL");
+  if (!is_device_pointer(k) || !is_device_pointer(v)) return fail(PHX_E_INVALID, "k and v must be device pointers");
+  hipStream_t s = (hipStream_t)stream;
+  // the tokens become the residual rows; rows past the prefix are zeros (finite, and under the
+  // causal mask no earlier row sees them)
+  const size_t xrow = (size_t)c.width * sizeof(float);
+  PHX_HIP(hipMemcpyAsync(h->h, x, (size_t)prefix_len * xrow, hipMemcpyDefault, s));
+  if (prefix_len < c.rows)
+    PHX_HIP(hipMemsetAsync((char*)h->h + (size_t)prefix_len * xrow, 0, (size_t)(c.rows - prefix_len) * xrow, s));
+  if (h->exec) {
+    PHX_HIP(hipGraphLaunch(h->exec, s));
+  } else {
+    for (const TokNode& nd : h->tnodes) {
+      int rc = launch_tok(h, nd, s);
+      if (rc) return rc;
+    }
+  }
+  // every layer's keys (rows) and values (fragment order) of the first prefix_len tokens
+  const size_t kvrow = (size_t)c.n_kv_heads * c.head_dim * 2;
+  PHX_HIP(hipMemcpy2DAsync(k, (size_t)prefix_len * kvrow, h->tk, (size_t)h->R * kvrow, (size_t)prefix_len * kvrow,
+                           (size_t)c.layers, hipMemcpyDeviceToDevice, s));
+  PHX_HIP(tok::launch_vt_export(h->tv, v, c.layers, prefix_len, h->R, c.n_kv_heads, c.head_dim, s));
   g_err.clear();
   return PHX_OK;
 }

@@ -460,8 +460,9 @@ constexpr int N_TILES = sizeof(TILES) / sizeof(TILES[0]);
 void plan_gemm(GemmT& g, int n_cu) {
   const int KT = g.K / 32;
   // few rows: the weights stream once from HBM and the ring's deeper look-ahead wins; many rows: the
-  // register-fed kernel halves the LDS traffic per MFMA
-  g.kern = g.Mp >= 1024 ? 1 : 0;
+  // register-fed kernel halves the LDS traffic per MFMA (from 512 rows on for the long GEMMs, measured on
+  // the 800-row prefill: gate/up 178 -> 123 us, while its 9-GFLOP QKV stayed faster on the ring)
+  g.kern = (g.Mp >= 1024 || (g.Mp >= 512 && 2.0 * g.Mp * g.N * g.K >= 2e10)) ? 1 : 0;
   double best = 1e300;
   g.tile = -1;
   g.splits = 1;
@@ -885,30 +886,38 @@ hipError_t launch_tattn(const AttnT& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// out[q][h*hd + d] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, splits in order
+// out[q][h*hd + d] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, splits in order; one thread per
+// 8 dims of a query and head (two 16-byte partial loads per split, one 16-byte store)
 __global__ void k_tcombine(AttnT a) {
-  const size_t total = (size_t)a.M * a.H * a.hd;
+  const int groups = a.hd / 8;
+  const size_t total = (size_t)a.M * a.H * groups;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int d = (int)(i % a.hd);
-    const size_t qh = i / a.hd;
+    const int g = (int)(i % groups);
+    const size_t qh = i / groups;
     const int h = (int)(qh % a.H);
     const int q = (int)(qh / a.H);
     float m = -INFINITY;
     for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.pml[(((size_t)s * a.M + q) * a.H + h) * 2]);
-    float num = 0.f, den = 0.f;
+    f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
     for (int s = 0; s < a.splits; ++s) {
-      const float ms = a.pml[(((size_t)s * a.M + q) * a.H + h) * 2];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - m);
-      num += w * a.po[((size_t)s * a.M + q) * (a.H * a.hd) + h * a.hd + d];
-      den += w * a.pml[(((size_t)s * a.M + q) * a.H + h) * 2 + 1];
+      const float2 ml = *(const float2*)(a.pml + (((size_t)s * a.M + q) * a.H + h) * 2);
+      if (ml.x == -INFINITY) continue;  // a split with no key this query sees
+      const float w = exp2f(ml.x - m);
+      const float* po = a.po + ((size_t)s * a.M + q) * (a.H * a.hd) + h * a.hd + 8 * g;
+      n0 += w * *(const f32x4*)po;
+      n1 += w * *(const f32x4*)(po + 4);
+      den += w * ml.y;
     }
-    ((bf16*)a.o)[(size_t)q * (a.H * a.hd) + h * a.hd + d] = (bf16)(num / den);
+    *(u32x4*)((bf16*)a.o + (size_t)q * (a.H * a.hd) + h * a.hd + 8 * g) =
+        u32x4{pack2(n0[0] / den, n0[1] / den), pack2(n0[2] / den, n0[3] / den), pack2(n1[0] / den, n1[1] / den),
+              pack2(n1[2] / den, n1[3] / den)};
   }
 }
 
 hipError_t launch_tcombine(const AttnT& a, hipStream_t s) {
-  const size_t total = (size_t)a.M * a.H * a.hd;
+  if (a.hd % 8) return hipErrorInvalidValue;
+  const size_t total = (size_t)a.M * a.H * (a.hd / 8);
   const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
   hipLaunchKernelGGL(k_tcombine, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -86,6 +86,20 @@ class Expert:
         """Commit a chunk (device float32 [rows][state_dim]) into the history."""
         B.phx_expert_commit_chunk(self.h, chunk.data_ptr(), self.stream)
 
+    def prefill(self, x, prefix_len: int, k=None, v=None):
+        """Prefix prefill: x device float32 [>= prefix_len][width]; returns
+        (k, v) device int16 tensors (raw bfloat16) [layers][prefix_len][KVH*Dh],
+        the layout load_prefix_kv takes."""
+        torch = self.torch
+        cfg = self.cfg
+        shape = (cfg["layers"], prefix_len, cfg["n_kv_heads"] * cfg["head_dim"])
+        if k is None:
+            k = torch.empty(shape, dtype=torch.int16, device=self.device)
+        if v is None:
+            v = torch.empty(shape, dtype=torch.int16, device=self.device)
+        B.phx_expert_prefill(self.h, x.data_ptr(), prefix_len, k.data_ptr(), v.data_ptr(), self.stream)
+        return k, v
+
     def capsule_bytes(self) -> int:
         return B.phx_expert_capsule_bytes(self.h)
 

@@ -78,9 +78,16 @@ extern "C" {
                                 (1 + scale) and shift, gated attention and GELU-MLP residual branches,
                                 no rotary positions; one pass over the tokens, no in/out linears and no
                                 Euler update (state_dim = width, steps = 1, prefix_capacity = 0) */
+#define PHX_BLOCK_PREFILL 2  /* prefix prefill: the decoder stack that reads the prefix tokens and writes
+                                the key/value cache an action expert attends to ("FlashRT-PAI", section
+                                2.1, Figure 1a); RMSNorm with a learned gain (1 + g), RoPE at positions
+                                0.., causal attention, GeGLU MLP, residual adds; no in/out linears
+                                (state_dim = width, steps = 1, prefix_capacity = 0, mask
+                                PHX_MASK_CAUSAL, rows = the most prefix tokens one call takes) */
 
 /* attention masks */
 #define PHX_MASK_FULL 0      /* every row sees every prefix key and every row of its own chunk */
+#define PHX_MASK_CAUSAL 1    /* token i sees tokens 0..i (the prefix prefill, and only it) */
 
 /* A HIP stream (hipStream_t is a pointer to this incomplete type). NULL means
    the default stream. */
@@ -115,8 +122,8 @@ typedef struct phx_expert_config {
   int32_t weight_dtype;      /* PHX_DTYPE_F32 or PHX_DTYPE_BF16 */
   int32_t kv_dtype;          /* must equal weight_dtype */
   uint32_t flags;            /* PHX_FLAG_* */
-  int32_t block_kind;        /* PHX_BLOCK_DECODER or PHX_BLOCK_DIT */
-  int32_t mask_kind;         /* PHX_MASK_FULL */
+  int32_t block_kind;        /* PHX_BLOCK_DECODER, PHX_BLOCK_DIT or PHX_BLOCK_PREFILL */
+  int32_t mask_kind;         /* PHX_MASK_FULL, or PHX_MASK_CAUSAL for PHX_BLOCK_PREFILL */
 } phx_expert_config;
 
 typedef struct phx_expert phx_expert;
@@ -143,6 +150,10 @@ PHX_API int phx_expert_validate_config(const phx_expert_config* cfg);
  *   for each block: W_qkv [D][3*H*Dh] (q, k, v heads), W_o [H*Dh][D], W_up [D][F], W_down [F][D]
  *   W_mod  [NL][E][6D]      (block b: shift, scale, gate of the attention branch, then shift,
  *                            scale, gate of the MLP branch, D outputs each)
+ * For PHX_BLOCK_PREFILL:
+ *   for each layer: W_qkv, W_o, W_gu, W_down as for the decoder
+ *   G      [2*NL][D]        (RMSNorm gains: row 2l before attention, 2l+1 before the MLP; the norm
+ *                            is y / rms(y) * (1 + g))
  * There are no biases.
  */
 PHX_API int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes);
@@ -190,6 +201,27 @@ PHX_API int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void
  * request has no loaded prefix) or PHX_E_HIP.
  */
 PHX_API int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_stream_t stream);
+
+/*
+ * Prefix prefill ("FlashRT-PAI", section 2.1, Figure 1a: the language model
+ * reads the prefix tokens and writes the key/value cache the action expert
+ * attends to; the cache is written once per observation).  Runs the
+ * PHX_BLOCK_PREFILL stack over the first prefix_len token rows of x and
+ * writes every layer's keys (after RoPE, positions 0..prefix_len-1) and
+ * values, in the layout phx_expert_load_prefix_kv takes.
+ *   x:          device or host float32 [prefix_len][width], the token rows.
+ *   prefix_len: 0 <= prefix_len <= rows (0 does nothing).  Under the causal
+ *               mask the result for the first prefix_len tokens does not
+ *               depend on the bucket size rows.
+ *   k, v:       device pointers to [layers][prefix_len][n_kv_heads*head_dim]
+ *               of kv_dtype (bf16), owned by the caller; written on stream.
+ * Stream-ordered and asynchronous.  Returns PHX_OK, PHX_E_INVALID (NULL
+ * argument, host k or v, or a handle of another block kind), PHX_E_SHAPE or
+ * PHX_E_HIP.  phx_expert_decide and phx_expert_load_prefix_kv reject a
+ * prefill handle with PHX_E_INVALID.
+ */
+PHX_API int phx_expert_prefill(phx_expert* h, const float* x, int32_t prefix_len, void* k, void* v,
+                               phx_stream_t stream);
 
 /* Frees every device allocation of the handle. NULL-safe. Synchronizes the
    handle's internal stream first. */

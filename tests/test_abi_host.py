@@ -65,13 +65,35 @@ def test_validate_accepts_the_workloads(lib):
     ("head_dim", 96, -3), ("n_kv_heads", 3, -3), ("mlp_hidden", 100, -3), ("state_dim", 7, -3),
     ("rows", 0, -3), ("batch", 17, -3), ("prefix_capacity", -1, -3), ("steps", 0, -3),
     ("time_emb_dim", 3, -3), ("rms_eps", 0.0, -1), ("rope_base", -1.0, -1), ("weight_dtype", 7, -1),
-    ("kv_dtype", 0, -3), ("flags", 0x80, -1), ("block_kind", 5, -1), ("mask_kind", 1, -1),
+    ("kv_dtype", 0, -3), ("flags", 0x80, -1), ("block_kind", 5, -1), ("mask_kind", 7, -1),
+    ("mask_kind", 1, -3),  # the causal mask belongs to the prefix prefill only
 ])
 def test_validate_rejects(lib, field, value, code):
     from flow_matching_action_decision_amd import binding
     c = _cfg(**{field: value})
     assert binding.phx_expert_validate_config(c) == code
     assert binding.phx_last_error()
+
+
+@pytest.mark.parametrize("field,value", [
+    ("mask_kind", 0), ("state_dim", 1024), ("prefix_capacity", 64), ("steps", 2), ("batch", 2), ("head_dim", 64),
+    ("weight_dtype", 0),
+])
+def test_validate_rejects_prefill_shapes(lib, field, value):
+    """The prefix prefill: causal mask, token rows as wide as the stack, no cache of its own, one pass,
+    one request, bf16 and head_dim 128 or 256 (the large-token kernels)."""
+    from flow_matching_action_decision_amd import binding
+    c = binding.make_config(phx_inputs.workload("prefix_prefill_bf16"))
+    assert binding.phx_expert_validate_config(c) == 0, binding.phx_last_error()
+    setattr(c, field, value)
+    if field == "weight_dtype":
+        c.kv_dtype = value
+    assert binding.phx_expert_validate_config(c) == -3
+    assert binding.phx_last_error()
+
+
+def test_prefill_null_arguments_without_a_gpu(lib):
+    assert lib.phx_expert_prefill(None, None, 0, None, None, None) == -1
 
 
 def test_validate_null(lib):
