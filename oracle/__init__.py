@@ -90,6 +90,7 @@ def load(path: str = LIB_PATH):
     lib.orc_prefill.restype = ctypes.c_int
     lib.orc_prefill_weight_count.argtypes = [ctypes.POINTER(OrcConfig)]
     lib.orc_prefill_weight_count.restype = ctypes.c_size_t
+    lib.orc_quantize_i8.argtypes = [ctypes.c_int, ctypes.c_int, _FP, ctypes.POINTER(ctypes.c_int8), _FP]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -320,3 +321,36 @@ def prefill(cfg: dict, weights: np.ndarray, x, length: int, trace: bool = False,
     if rc != 0:
         raise ValueError(f"orc_prefill rejected its arguments (rc={rc})")
     return {"k": k, "v": v, "trace": tr, "softmax_dev": lib.orc_last_softmax_dev()}
+
+
+def quantize_i8(W: np.ndarray, lib=None):
+    """Round-to-nearest int8 codes per output channel of W [K][N] (float32):
+    returns (q int8 [K][N], s float32 [N]) with W ~ s * q."""
+    lib = lib or load()
+    W, pw = _f(np.asarray(W).reshape(W.shape[0], -1))
+    K, N = W.shape
+    q = np.zeros((K, N), dtype=np.int8)
+    s = np.zeros(N, dtype=np.float32)
+    lib.orc_quantize_i8(K, N, pw, q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), s.ctypes.data_as(_FP))
+    return q, s
+
+
+# the projection matrices the 8-bit tier quantises: every layer's four matrices
+W8_MATRICES = ("W_qkv", "W_o", "W_gu", "W_down")
+
+
+def w8_weights(cfg: dict, weights: np.ndarray, slices: dict, lib=None) -> np.ndarray:
+    """The weight blob the 8-bit tier computes with: every layer's W_qkv,
+    W_o, W_gu and W_down replaced by s * q (float64 product rounded to
+    float32, a relative change of at most 2^-24); the other matrices as
+    given.  `slices` maps names to (offset, shape), as phx_inputs lays the
+    blob out."""
+    out = np.array(weights, dtype=np.float32, copy=True)
+    for l in range(cfg["layers"]):
+        for nm in W8_MATRICES:
+            off, shape = slices[f"{nm}.{l}"]
+            n = int(np.prod(shape))
+            W = out[off:off + n].reshape(shape)
+            q, s = quantize_i8(W, lib=lib)
+            out[off:off + n] = (q.astype(np.float64) * s.astype(np.float64)[None, :]).astype(np.float32).reshape(-1)
+    return out

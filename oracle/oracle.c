@@ -550,3 +550,31 @@ int orc_prefill(const orc_config* c, const float* weights, const float* x_in, in
   free(pos);
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * 8-bit weight tier (W8A16): weights quantised offline by round-to-nearest,
+ * activations kept in 16 bits ("PhyAI", section 4.2 Quantization; the
+ * "FlashRT-PAI" precision tiers, Table 4).  Readings where the pages are
+ * silent: symmetric int8 codes per output channel (column n of W [K][N]),
+ * s[n] = max_k |W[k][n]| / 127 and q = W / s rounded to the nearest integer,
+ * ties to even, clamped to [-127, 127]; both divisions in float32; a zero
+ * column has s = 0 and q = 0.  The weight is then s[n] * q[k][n].
+ * ------------------------------------------------------------------------ */
+
+void orc_quantize_i8(int K, int N, const float* W, signed char* q, float* s) {
+  for (int n = 0; n < N; ++n) {
+    float m = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const float a = fabsf(W[(size_t)k * N + n]);
+      if (a > m) m = a;
+    }
+    const float sc = m / 127.0f;
+    s[n] = sc;
+    for (int k = 0; k < K; ++k) {
+      float v = sc > 0.0f ? rintf(W[(size_t)k * N + n] / sc) : 0.0f;
+      if (v > 127.0f) v = 127.0f;
+      if (v < -127.0f) v = -127.0f;
+      q[(size_t)k * N + n] = (signed char)v;
+    }
+  }
+}

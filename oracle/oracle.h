@@ -171,6 +171,14 @@ int orc_prefill(const orc_config* cfg, const float* weights, const float* x_in, 
 /* Number of float32 values in the prefill weight blob for cfg. */
 size_t orc_prefill_weight_count(const orc_config* cfg);
 
+/*
+ * 8-bit weight tier (round-to-nearest, weight-only): per output channel n of
+ * W [K][N] (float32), s[n] = max_k |W[k][n]| / 127 and q[k][n] =
+ * clamp(rint(W[k][n] / s[n]), -127, 127), both divisions in float32, ties to
+ * even; a zero column gives s = 0 and q = 0.  q [K][N], s [N].
+ */
+void orc_quantize_i8(int K, int N, const float* W, signed char* q, float* s);
+
 #ifdef __cplusplus
 }
 #endif

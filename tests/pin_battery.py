@@ -580,10 +580,76 @@ def pin_prefill_invariants(lib):
     _close(one["k"], ref1["k"], tol=1e-12, what="a single token's cache does not depend on its queries")
 
 
+# ---------------------------------------------------------------- 8-bit weight tier
+
+def pin_quantize_i8(lib):
+    """Round-to-nearest int8 codes per output channel: the column maximum
+    maps to +-127, every weight is within half a step of s*q, ties go to the
+    even code, a zero column gives zeros, signs and column order carry
+    through, codes are monotone within a column."""
+    rng = np.random.default_rng(12)
+    K, N = 64, 24
+    W = phx_inputs.bf16_round((rng.standard_normal((K, N)) * 0.02).astype(np.float32))[0].reshape(K, N)
+    W[:, 5] = 0.0                                   # zero column
+    W[:, 6] = 0.0
+    W[3, 6] = -0.75                                 # a single (negative) weight
+    # a column with step exactly 2^-10 (its maximum is 127 * 2^-10) and weights on half steps
+    step = 2.0 ** -10
+    W[:, 7] = 0.0
+    W[0, 7] = 127 * step
+    halves = np.array([0.5, 1.5, 2.5, 3.5, 4.5, -0.5, -1.5, -2.5, -3.5, 126.5, -126.5], dtype=np.float64)
+    W[1:1 + halves.size, 7] = (halves * step).astype(np.float32)
+    q, sc = oracle.quantize_i8(W, lib=lib)
+    assert q.dtype == np.int8 and sc.dtype == np.float32
+    assert int(np.max(np.abs(q.astype(np.int32)))) <= 127
+    for n in range(N):
+        col = W[:, n].astype(np.float64)
+        m = float(np.max(np.abs(col)))
+        if m == 0.0:
+            assert sc[n] == 0.0 and not np.any(q[:, n]), "a zero column has zero scale and codes"
+            continue
+        assert abs(float(sc[n]) * 127.0 - m) <= 1e-6 * m, f"column {n}: scale is not max/127"
+        k = int(np.argmax(np.abs(col)))
+        assert int(q[k, n]) == (127 if col[k] > 0 else -127), f"column {n}: its maximum must map to +-127"
+        # nearest code of the float32 quotient, which is within 127 * 2^-24 of a step of the exact one
+        err = np.abs(col - float(sc[n]) * q[:, n].astype(np.float64))
+        assert float(np.max(err)) <= (0.5 + 1e-5) * float(sc[n]), f"column {n}: not rounded to nearest"
+        order = np.argsort(col, kind="stable")
+        assert np.all(np.diff(q[order, n].astype(np.int32)) >= 0), f"column {n}: codes not monotone"
+    assert sc[7] == np.float32(step)
+    want = np.array([0, 2, 2, 4, 4, 0, -2, -2, -4, 126, -126])
+    assert np.array_equal(q[1:1 + halves.size, 7].astype(np.int32), want), "ties must go to the even code"
+    assert int(q[3, 6]) == -127 and np.count_nonzero(q[:, 6]) == 1
+    # signs and column order carry through
+    qn, sn = oracle.quantize_i8(-W, lib=lib)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, sc)
+    perm = rng.permutation(N)
+    qp, sp = oracle.quantize_i8(np.ascontiguousarray(W[:, perm]), lib=lib)
+    assert np.array_equal(qp, q[:, perm]) and np.array_equal(sp, sc[perm])
+
+
+def pin_w8_weights(lib):
+    """The 8-bit tier's blob: exactly the four layer matrices change, each to
+    s * q within half a quantisation step; everything else is untouched."""
+    cfg = tiny_cfg()
+    inp = phx_inputs.make_inputs(cfg, seed=13)
+    sl = phx_inputs.weight_slices(cfg)
+    w8 = oracle.w8_weights(cfg, inp["weights"], sl, lib=lib)
+    for nm, (off, shape) in sl.items():
+        n = int(np.prod(shape))
+        a, b = inp["weights"][off:off + n].reshape(shape), w8[off:off + n].reshape(shape)
+        if nm.split(".")[0] in oracle.W8_MATRICES:
+            step = np.max(np.abs(a.astype(np.float64)), axis=0) / 127.0
+            assert np.all(np.abs(b - a.astype(np.float64)) <= 0.5 * step[None, :] * (1 + 1e-5) + 1e-12), nm
+            assert not np.array_equal(a, b), f"{nm}: not quantised"
+        else:
+            assert np.array_equal(a, b), f"{nm} must not change"
+
+
 ALL_PINS = [pin_time_embedding, pin_modulation, pin_matmul, pin_ada_rmsnorm, pin_rope, pin_gelu, pin_attention,
             pin_decide_brute_force, pin_decide_invariants, pin_ada_layernorm, pin_dit_brute_force, pin_dit_invariants,
             pin_decide_at_brute_force, pin_commit_brute_force, pin_prefill_brute_force, pin_prefill_incremental,
-            pin_prefill_invariants]
+            pin_prefill_invariants, pin_quantize_i8, pin_w8_weights]
 
 
 def run_all(lib):

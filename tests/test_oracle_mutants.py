@@ -78,6 +78,10 @@ MUTANTS = [
      "orc_gelu_tanh(gu[(size_t)t * 2 * F + f]) * gu[(size_t)t * 2 * F + F + f]",
      "orc_gelu_tanh(gu[(size_t)t * 2 * F + F + f]) * gu[(size_t)t * 2 * F + f]"),
     ("prefill: softmax scale dropped", "      p[t] = s * scale;", "      p[t] = s;"),
+    ("quantize: ties away from zero", "rintf(W[(size_t)k * N + n] / sc)", "roundf(W[(size_t)k * N + n] / sc)"),
+    ("quantize: truncation", "rintf(W[(size_t)k * N + n] / sc)", "truncf(W[(size_t)k * N + n] / sc)"),
+    ("quantize: 128 levels", "const float sc = m / 127.0f;", "const float sc = m / 128.0f;"),
+    ("quantize: scale from the first row", "      if (a > m) m = a;", "      if (k == 0) m = a;"),
 ]
 
 
