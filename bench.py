@@ -7,6 +7,9 @@ prefix K/V cache, replayed from the library's captured HIP graph.  Inputs
 (weights, prefix K/V, noise) are synthetic and seeded, and resident in HBM
 before the timed region starts.
 
+--workload pi05_expert_w8a16 runs the same decision on the 8-bit weight tier
+(int8 codes per output column for every layer projection, bf16 activations;
+the multi-kernel graph).
 --workload va_chunk_bf16 (256-row video-action chunk over a 4096-row cache,
 8 layers x 5 steps) or wam_dit_bf16 (DiT-style step over 4128 tokens, 4
 blocks) measures the large-token plan instead; those are MFMA-bound, so their
@@ -46,6 +49,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 WORKLOAD = "pi05_expert_bf16"
 BATCH_WORKLOADS = ("rollout_b16_bf16",)
+W8_WORKLOADS = ("pi05_expert_w8a16",)
 TOKEN_WORKLOADS = ("va_chunk_bf16", "wam_dit_bf16")
 PREFILL_WORKLOADS = ("prefix_prefill_bf16",)
 PROFILES = os.path.join(ROOT, "profiles")
@@ -65,6 +69,8 @@ def algorithmic_bytes(cfg: dict) -> dict:
     H, KVH, Dh, NL = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["layers"]
     qkv = (H + 2 * KVH) * Dh
     w_layer = (D * qkv + H * Dh * D + D * 2 * F + F * D) * esz
+    if int(cfg.get("flags", 0)) & 8:  # the 8-bit tier: one byte per code plus a float scale per column
+        w_layer = (D * qkv + H * Dh * D + D * 2 * F + F * D) + 4 * (qkv + D + 2 * F + D)
     w_step = NL * w_layer + 2 * A * D * esz
     lens = phx_inputs.prefix_lengths(cfg)
     kv_step = int(sum(2 * NL * int(L) * KVH * Dh * esz for L in lens))
@@ -169,7 +175,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=(WORKLOAD,) + BATCH_WORKLOADS + TOKEN_WORKLOADS + PREFILL_WORKLOADS)
+                    choices=(WORKLOAD,) + BATCH_WORKLOADS + W8_WORKLOADS + TOKEN_WORKLOADS + PREFILL_WORKLOADS)
     ap.add_argument("--steps", type=int, default=200, help="timed decisions")
     ap.add_argument("--warmup", type=int, default=20, help="untimed decisions before the timed region")
     ap.add_argument("--seed", type=int, default=0)
@@ -273,20 +279,28 @@ def main():
 
     hbm_gbs = ab["per_decision"] / (ms * 1e-3) / 1e9
     lens = [int(L) for L in inp["lens"]]
+    w8 = name in W8_WORKLOADS
+    if w8:
+        metric = "ms/decision (pi0.5-shape, 18L x 10 steps, 8-bit weight tier) + % peak HBM GB/s, 1 GPU"
+    elif batch:
+        metric = f"ms/decision ({name}: {cfg['batch']} requests, 18L x 10 steps) + % peak HBM GB/s, 1 GPU"
+    else:
+        metric = "ms/decision (pi0.5-shape, 18L x 10 steps) + % peak HBM GB/s, 1 GPU"
     line = {
-        "metric": ("ms/decision (pi0.5-shape, 18L x 10 steps) + % peak HBM GB/s, 1 GPU" if not batch else
-                   f"ms/decision ({name}: {cfg['batch']} requests, 18L x 10 steps) + % peak HBM GB/s, 1 GPU"),
+        "metric": metric,
         "value": round(ms, 4), "unit": "ms/decision", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 prefix K/V, N(0,1) noise)",
         "config": {"workload": name, "layers": cfg["layers"], "euler_steps": cfg["steps"],
-                   "action_rows": cfg["rows"], "prefix_len": lens[0] if not batch else lens, "width": cfg["width"],
+                   "action_rows": cfg["rows"], "prefix_len": lens[0] if (not batch or w8) else lens, "width": cfg["width"],
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} / {cfg['n_kv_heads']} kv",
-                   "mlp_hidden": cfg["mlp_hidden"], "batch": cfg["batch"]},
+                   "mlp_hidden": cfg["mlp_hidden"], "batch": cfg["batch"],
+                   **({"weights": "int8 codes per output column (layer projections), bf16 in/out projections"}
+                      if w8 else {})},
         "decisions_per_s": round(1000.0 / ms, 1),
         "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
         **({"requests_per_s": round(1000.0 * cfg["batch"] / ms, 1),
-            "ms_per_request_amortised": round(ms / cfg["batch"], 4)} if batch else {}),
+            "ms_per_request_amortised": round(ms / cfg["batch"], 4)} if batch and not w8 else {}),
         "algorithmic_bytes_per_decision": ab["per_decision"],
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "kernels_per_decision": nk,

@@ -19,6 +19,7 @@ PHX_DTYPE_F32, PHX_DTYPE_BF16 = 0, 1
 PHX_FLAG_NO_GRAPH = 1
 PHX_FLAG_MULTI_KERNEL = 2
 PHX_FLAG_TIMELINE = 4
+PHX_FLAG_WEIGHTS_INT8 = 8
 PHX_BLOCK_DECODER, PHX_BLOCK_DIT, PHX_BLOCK_PREFILL = 0, 1, 2
 _BLOCKS = dict(decoder=PHX_BLOCK_DECODER, dit=PHX_BLOCK_DIT, prefill=PHX_BLOCK_PREFILL)
 # launch kinds reported by phx_expert_node_info
@@ -33,7 +34,7 @@ EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_exper
             "phx_expert_kernels_per_decision", "phx_expert_node_info", "phx_expert_launch_node",
             "phx_expert_status", "phx_expert_timeline", "phx_expert_capsule_bytes", "phx_expert_capsule_regions",
             "phx_expert_capsule_save", "phx_expert_capsule_restore", "phx_expert_commit_chunk",
-            "phx_expert_prefill")
+            "phx_expert_prefill", "phx_expert_weight_codes")
 
 NODE_KINDS = {1: "in_proj", 2: "norm_qkv_rope", 3: "attention", 4: "attention_combine", 5: "out_proj_resid",
               6: "norm_gateup_geglu", 7: "down_proj_resid", 8: "norm_out_proj_euler", 9: "decision_kernel",
@@ -103,6 +104,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phx_expert_capsule_restore.argtypes = [P, P, ctypes.c_size_t, P]
     lib.phx_expert_commit_chunk.argtypes = [P, P, P]
     lib.phx_expert_prefill.argtypes = [P, P, ctypes.c_int32, P, P, P]
+    lib.phx_expert_weight_codes.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P]
     _lib = lib
     return lib
 
@@ -231,3 +233,8 @@ def phx_expert_commit_chunk(h: int, chunk: int, stream: int = 0):
 def phx_expert_prefill(h: int, x: int, prefix_len: int, k: int, v: int, stream: int = 0):
     _check(load_library().phx_expert_prefill(ctypes.c_void_p(h), ctypes.c_void_p(x), prefix_len, ctypes.c_void_p(k),
                                              ctypes.c_void_p(v), ctypes.c_void_p(stream)))
+
+
+def phx_expert_weight_codes(h: int, layer: int, matrix: int, codes: int, scales: int, stream: int = 0):
+    _check(load_library().phx_expert_weight_codes(ctypes.c_void_p(h), layer, matrix, ctypes.c_void_p(codes),
+                                                  ctypes.c_void_p(scales), ctypes.c_void_p(stream)))

@@ -124,6 +124,10 @@ struct phx_expert {
   size_t off_in = 0, off_out = 0;
   std::vector<size_t> off_qkv, off_o, off_gu, off_down;
   float* modtab = nullptr;
+  // 8-bit tier: int8 codes at the same element offsets as wt, per-column scales per matrix
+  signed char* wq = nullptr;
+  float* wsc = nullptr;
+  std::vector<size_t> sc_qkv, sc_o, sc_gu, sc_down;
   // state
   void* kc = nullptr;
   void* vtc = nullptr;
@@ -241,7 +245,8 @@ int build_nodes(phx_expert* h) {
                        const char* name) {
     Node nd{};
     nd.kind = kind; nd.step = k; nd.layer = l; nd.g = g; nd.nw = p.NW; nd.pro = pro; nd.epi = epi;
-    nd.bytes = (uint64_t)K * N * esz + (pro == PRO_NORM ? (uint64_t)D2 * sizeof(float) : 0);
+    nd.bytes = (g.Wq ? (uint64_t)K * N + (uint64_t)N * sizeof(float) : (uint64_t)K * N * esz) +
+               (pro == PRO_NORM ? (uint64_t)D2 * sizeof(float) : 0);
     std::snprintf(nd.name, sizeof(nd.name), "%s", name);
     h->node_list.push_back(nd);
   };
@@ -264,6 +269,7 @@ int build_nodes(phx_expert* h) {
       {
         GemmArgs g{};
         g.W = (const char*)h->wt + h->off_qkv[l] * esz;
+        if (h->wq) { g.Wq = h->wq + h->off_qkv[l]; g.wsc = h->wsc + h->sc_qkv[l]; }
         g.KT = h->p_qkv.KT; g.NT = h->p_qkv.NT; g.KSW = h->p_qkv.KSW; g.rows = h->BM;
         g.h = h->h; g.ss = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D; g.eps = c.rms_eps;
         g.mod = mod_k + (size_t)(2 * l) * D2;
@@ -298,6 +304,7 @@ int build_nodes(phx_expert* h) {
       {
         GemmArgs g{};
         g.W = (const char*)h->wt + h->off_o[l] * esz;
+        if (h->wq) { g.Wq = h->wq + h->off_o[l]; g.wsc = h->wsc + h->sc_o[l]; }
         g.KT = h->p_o.KT; g.NT = h->p_o.NT; g.KSW = h->p_o.KSW; g.rows = h->BM;
         g.X = h->o; g.ldx = H * Dh;
         g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
@@ -308,6 +315,7 @@ int build_nodes(phx_expert* h) {
       {
         GemmArgs g{};
         g.W = (const char*)h->wt + h->off_gu[l] * esz;
+        if (h->wq) { g.Wq = h->wq + h->off_gu[l]; g.wsc = h->wsc + h->sc_gu[l]; }
         g.KT = h->p_gu.KT; g.NT = h->p_gu.NT; g.KSW = h->p_gu.KSW; g.rows = h->BM;
         g.h = h->h; g.ss = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D; g.eps = c.rms_eps;
         g.mod = mod_k + (size_t)(2 * l + 1) * D2;
@@ -319,6 +327,7 @@ int build_nodes(phx_expert* h) {
       {
         GemmArgs g{};
         g.W = (const char*)h->wt + h->off_down[l] * esz;
+        if (h->wq) { g.Wq = h->wq + h->off_down[l]; g.wsc = h->wsc + h->sc_down[l]; }
         g.KT = h->p_down.KT; g.NT = h->p_down.NT; g.KSW = h->p_down.KSW; g.rows = h->BM;
         g.X = h->act; g.ldx = F;
         g.hout = h->h; g.ssout = h->ss; g.NTD = h->NTD; g.ss_ld = h->ss_ld; g.D = D;
@@ -386,7 +395,7 @@ int mt_for_rows(int rows) {
 // request of up to 16 action rows in bf16; every other configuration runs the
 // multi-kernel graph.
 bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop) {
-  if (c.flags & (PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL)) return false;
+  if (c.flags & (PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL | PHX_FLAG_WEIGHTS_INT8)) return false;
   if (c.block_kind != PHX_BLOCK_DECODER) return false;
   if (c.weight_dtype != PHX_DTYPE_BF16 || c.kv_dtype != PHX_DTYPE_BF16) return false;
   if (c.width != dec::D || c.n_heads != dec::H || c.head_dim != dec::DH || c.n_kv_heads != 1) return false;
@@ -531,7 +540,7 @@ bool uses_tokens(const phx_expert_config& c) {
 bool uses_batched(const phx_expert_config& c) {
   const long long rows = (long long)c.rows * c.batch;
   return c.block_kind == PHX_BLOCK_DECODER && c.weight_dtype == PHX_DTYPE_BF16 && rows > 64 && rows <= 160 &&
-         !(c.flags & PHX_FLAG_MULTI_KERNEL);
+         !(c.flags & (PHX_FLAG_MULTI_KERNEL | PHX_FLAG_WEIGHTS_INT8));
 }
 
 int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s) {
@@ -1116,8 +1125,11 @@ int phx_expert_validate_config(const phx_expert_config* c) {
   if (c->weight_dtype != PHX_DTYPE_F32 && c->weight_dtype != PHX_DTYPE_BF16)
     return fail(PHX_E_INVALID, "weight_dtype %d unknown", c->weight_dtype);
   if (c->kv_dtype != c->weight_dtype) return fail(PHX_E_SHAPE, "kv_dtype must equal weight_dtype");
-  if (c->flags & ~(PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL | PHX_FLAG_TIMELINE))
+  if (c->flags & ~(PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL | PHX_FLAG_TIMELINE | PHX_FLAG_WEIGHTS_INT8))
     return fail(PHX_E_INVALID, "unknown flags 0x%x", c->flags);
+  if ((c->flags & PHX_FLAG_WEIGHTS_INT8) &&
+      (c->weight_dtype != PHX_DTYPE_BF16 || c->block_kind != PHX_BLOCK_DECODER || (long long)c->rows * c->batch > 160))
+    return fail(PHX_E_SHAPE, "the 8-bit weight tier needs bf16 weights, the decoder block and at most 160 rows");
   return PHX_OK;
 }
 
@@ -1126,6 +1138,27 @@ int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes) {
   int rc = phx_expert_validate_config(cfg);
   if (rc) return rc;
   *bytes = weight_elems(cfg) * (cfg->weight_dtype == PHX_DTYPE_BF16 ? 2 : 4);
+  return PHX_OK;
+}
+
+int phx_expert_weight_codes(const phx_expert* h, int32_t layer, int32_t matrix, int8_t* codes, float* scales,
+                            phx_stream_t stream) {
+  if (!h || !codes || !scales) return fail(PHX_E_INVALID, "NULL argument");
+  if (!h->wq) return fail(PHX_E_STATE, "the handle has no int8 weights (PHX_FLAG_WEIGHTS_INT8)");
+  const phx_expert_config& c = h->cfg;
+  if (layer < 0 || layer >= c.layers || matrix < 0 || matrix > 3)
+    return fail(PHX_E_SHAPE, "layer %d or matrix %d out of range", layer, matrix);
+  if (!is_device_pointer(codes) || !is_device_pointer(scales))
+    return fail(PHX_E_INVALID, "codes and scales must be device pointers");
+  const int D = c.width, HD = c.n_heads * c.head_dim, F = c.mlp_hidden;
+  const int qkvN = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int K[4] = {D, HD, D, F}, N[4] = {qkvN, D, 2 * F, D};
+  const int kind[4] = {COL_ROPE, COL_IDENT, COL_GEGLU, COL_IDENT}, param[4] = {c.head_dim, 0, F, 0};
+  const size_t off[4] = {h->off_qkv[layer], h->off_o[layer], h->off_gu[layer], h->off_down[layer]};
+  const size_t so[4] = {h->sc_qkv[layer], h->sc_o[layer], h->sc_gu[layer], h->sc_down[layer]};
+  PHX_HIP(launch_untile_codes(h->wq + off[matrix], h->wsc + so[matrix], (signed char*)codes, scales, K[matrix],
+                              N[matrix], kind[matrix], param[matrix], (hipStream_t)stream));
+  g_err.clear();
   return PHX_OK;
 }
 
@@ -1215,6 +1248,29 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
     if ((rc = retile(h->off_down[l], F, D, COL_IDENT, 0))) return rc;
   }
   if (io && (rc = retile(h->off_out, D, A, COL_IDENT, 0))) return rc;
+
+  if (c.flags & PHX_FLAG_WEIGHTS_INT8) {
+    // the 8-bit tier: codes of every layer's four projections from their tiled bf16 form
+    size_t nsc = 0;
+    for (int l = 0; l < NL; ++l) {
+      h->sc_qkv.push_back(nsc); nsc += (size_t)qkvN;
+      h->sc_o.push_back(nsc); nsc += (size_t)D;
+      h->sc_gu.push_back(nsc); nsc += (size_t)gu_cols;
+      h->sc_down.push_back(nsc); nsc += (size_t)D;
+    }
+    if ((rc = alloc(h, (void**)&h->wq, tiled_elems, "int8 weight codes"))) return rc;
+    if ((rc = alloc(h, (void**)&h->wsc, nsc * sizeof(float), "int8 weight scales"))) return rc;
+    auto quant = [&](size_t o, size_t so, int K, int N) -> int {
+      PHX_HIP(launch_quant_i8((const char*)h->wt + o * h->esz, h->wq + o, h->wsc + so, K, N, stream));
+      return PHX_OK;
+    };
+    for (int l = 0; l < NL; ++l) {
+      if ((rc = quant(h->off_qkv[l], h->sc_qkv[l], D, qkvN))) return rc;
+      if ((rc = quant(h->off_o[l], h->sc_o[l], H * Dh, D))) return rc;
+      if ((rc = quant(h->off_gu[l], h->sc_gu[l], D, gu_cols))) return rc;
+      if ((rc = quant(h->off_down[l], h->sc_down[l], F, D))) return rc;
+    }
+  }
 
   h->tokens = uses_tokens(c);
   h->n_cu = prop.multiProcessorCount;

@@ -44,6 +44,8 @@ enum Epilogue : int {
 
 struct GemmArgs {
   const void* W;       // tiled weights of this matrix
+  const signed char* Wq;  // 8-bit tier: tiled int8 codes of this matrix (W unused), or null
+  const float* wsc;    // 8-bit tier: per-column scales in tile column order [NT*16]
   int KT, NT, KSW;     // k-tiles, n-tiles, workgroups per n-tile (split K)
   int rows;            // valid activation rows (B*M)
   // prologue
@@ -108,6 +110,11 @@ hipError_t launch_combine(int dtype, const CombineArgs& a, int batch, hipStream_
 hipError_t launch_retile(int dtype, const void* src, void* dst, int K, int N, int colmap, int cm_param,
                          hipStream_t s);
 hipError_t launch_time_embedding(double* e, int S, int E, double tau0, double dt, hipStream_t s);
+// 8-bit tier: per-column scales and int8 codes of a tiled bf16 matrix [K][N], in the same tile order
+hipError_t launch_quant_i8(const void* wt, signed char* q, float* sc, int K, int N, hipStream_t s);
+// 8-bit tier: codes and scales of a tiled matrix back to [K][N] and [N] (the inverse column map)
+hipError_t launch_untile_codes(const signed char* qt, const float* sct, signed char* q, float* sc, int K, int N,
+                               int colmap, int cm_param, hipStream_t s);
 hipError_t launch_modulation(int dtype, const void* wmod, const double* e, float* modtab, int S, int NN, int E,
                              int D2, hipStream_t s);
 hipError_t launch_load_prefix(int dtype, const void* k, const void* v, void* kc, void* vtc, int NL, int B, int KVH,

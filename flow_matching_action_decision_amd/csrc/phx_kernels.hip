@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 namespace phx {
 
 typedef __bf16 bf16;
@@ -29,6 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct FragT;
@@ -141,7 +144,27 @@ __device__ inline typename FragT<T>::type load_act(const GemmArgs& a, int row, i
   }
 }
 
-template <typename T, int NW, int MT, int PRO, int EPI>
+// 8-bit tier: one lane's 8 int8 codes (a 512-byte tile holds 16 columns x 32
+// rows, lane l the 8 rows 8 (l / 16) + [0, 8) of column l % 16) as the bf16 A
+// operand.  Every code (at most 127 in magnitude) is exact in bf16: the
+// float32 of the integer has no bits below the top 8 of its significand.
+__device__ inline u32x2 i8_load(const signed char* p) { return __builtin_nontemporal_load((const u32x2*)p); }
+__device__ inline bf16x8 i8_frag(const u32x2& w) {
+  unsigned o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned word = w[i >> 1];
+    const int sh = 16 * (i & 1);
+    const float lo = (float)(int)(signed char)(word >> sh);
+    const float hi = (float)(int)(signed char)(word >> (sh + 8));
+    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+}
+
+// W8: the weights are int8 codes with per-column scales (the 8-bit tier,
+// bf16 activations); the scale multiplies the fp32 sum before the epilogue.
+template <typename T, int NW, int MT, int PRO, int EPI, bool W8 = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
   using Frag = typename FragT<T>::type;
   constexpr int G = MT <= 1 ? 8 : (MT <= 2 ? 4 : (MT <= 4 ? 2 : 1));  // tiles issued together per wave
@@ -176,12 +199,27 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // the 8-bit tier's column scales are loaded now and used after the reduction
+  f32x4 wsc4 = f32x4{1.f, 1.f, 1.f, 1.f};
+  if constexpr (W8) wsc4 = *(const f32x4*)(a.wsc + nt * 16 + grp * 4);
   const T* wbase = (const T*)a.W + ((size_t)nt * a.KT + kt0) * TILE_ELEMS + lane * 8;
+  const signed char* qbase = a.Wq + ((size_t)nt * a.KT + kt0) * TILE_ELEMS + lane * 8;
   for (int i0 = 0; i0 < kpc; i0 += G) {
     Frag af[G];
+    if constexpr (W8) {
+      // every code load of the group in flight before the first conversion
+      u32x2 raw[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-      if (i0 + j < kpc) af[j] = ldw8(wbase + (size_t)(i0 + j) * TILE_ELEMS);
+      for (int j = 0; j < G; ++j)
+        if (i0 + j < kpc) raw[j] = i8_load(qbase + (size_t)(i0 + j) * TILE_ELEMS);
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (i0 + j < kpc) af[j] = i8_frag(raw[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (i0 + j < kpc) af[j] = ldw8(wbase + (size_t)(i0 + j) * TILE_ELEMS);
+    }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       if (i0 + j < kpc) {
@@ -244,6 +282,12 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[mt][i] += ld_coherent(ps + (mt * 64 + lane) * 4 + i);
     }
+  }
+
+  // the 8-bit tier's column scales (tile column order)
+  if constexpr (W8) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= wsc4;
   }
 
   // ------------------------------------------------------------ epilogues
@@ -495,6 +539,59 @@ __global__ void k_retile(const T* __restrict__ src, T* __restrict__ dst, int K, 
   }
 }
 
+// 8-bit tier ("PhyAI" section 4.2 Quantization: offline round-to-nearest,
+// W8A16).  Per output column of a tiled bf16 matrix: s = max |w| / 127 (one
+// thread per tile column, tile column order), then q = rint(w / s) clamped
+// to +-127 (ties to even; both divisions correctly rounded float32), 0 where
+// s = 0; codes keep the tile order, one byte per weight.
+__global__ void k_quant_scale(const bf16* __restrict__ wt, float* __restrict__ sc, int KT, int NT) {
+  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  if (col >= NT * 16) return;
+  const int nt = col >> 4, c = col & 15;
+  float m = 0.f;
+  for (int kt = 0; kt < KT; ++kt)
+    for (int g = 0; g < 4; ++g) {
+      const bf16* p = wt + (((size_t)nt * KT + kt) * 64 + c + 16 * g) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)p[j]));
+    }
+  sc[col] = m / 127.0f;
+}
+
+__global__ void k_quant_codes(const bf16* __restrict__ wt, const float* __restrict__ sc, signed char* __restrict__ q,
+                              int KT, int NT) {
+  const size_t nfrag = (size_t)NT * KT * 64;
+  for (size_t f = (size_t)blockIdx.x * blockDim.x + threadIdx.x; f < nfrag; f += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(f & 63);
+    const int nt = (int)((f >> 6) / KT);
+    const float s = sc[nt * 16 + (lane & 15)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v = s > 0.f ? rintf((float)wt[f * 8 + j] / s) : 0.f;
+      v = fminf(fmaxf(v, -127.f), 127.f);
+      q[f * 8 + j] = (signed char)(int)v;
+    }
+  }
+}
+
+// codes of a tiled matrix back to [K][N] through the column map, scales to [N]
+__global__ void k_untile_codes(const signed char* __restrict__ qt, const float* __restrict__ sct,
+                               signed char* __restrict__ q, float* __restrict__ sc, int K, int N, int kind,
+                               int param) {
+  const int KT = K / TILE_K, NT = N / TILE_N;
+  const size_t nfrag = (size_t)NT * KT * 64;
+  for (size_t f = (size_t)blockIdx.x * blockDim.x + threadIdx.x; f < nfrag; f += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(f & 63);
+    const size_t tile = f >> 6;
+    const int nt = (int)(tile / KT), kt = (int)(tile % KT);
+    const int n = colmap(kind, param, nt, lane & 15);
+    const int k0 = kt * TILE_K + 8 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[(size_t)(k0 + j) * N + n] = qt[f * 8 + j];
+    if (kt == 0 && lane < 16) sc[n] = sct[nt * 16 + lane];
+  }
+}
+
 // e[k][j] = sin(tau_k w_j), e[k][E/2 + j] = cos(tau_k w_j), w_j = 10000^(-j/(E/2))
 __global__ void k_time_embedding(double* e, int S, int E, double tau0, double dt) {
   const int half = E / 2;
@@ -571,6 +668,22 @@ __global__ void k_position_table(int* lens, float2* rope, int b, int L, int M, i
 template <typename T, int MT>
 static hipError_t gemm_mt(int nw, int pro, int epi, const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.NT * a.KSW);
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (a.Wq) {  // the 8-bit tier: the layer projections only
+      if (!a.wsc) return hipErrorInvalidValue;
+      if (nw == 4 && pro == PRO_NORM && epi == EPI_QKV)
+        hipLaunchKernelGGL((k_gemm<T, 4, MT, PRO_NORM, EPI_QKV, true>), grid, dim3(256), 0, s, a);
+      else if (nw == 4 && pro == PRO_X && epi == EPI_RESID)
+        hipLaunchKernelGGL((k_gemm<T, 4, MT, PRO_X, EPI_RESID, true>), grid, dim3(256), 0, s, a);
+      else if (nw == 4 && pro == PRO_NORM && epi == EPI_GEGLU)
+        hipLaunchKernelGGL((k_gemm<T, 4, MT, PRO_NORM, EPI_GEGLU, true>), grid, dim3(256), 0, s, a);
+      else
+        return hipErrorInvalidValue;
+      return hipGetLastError();
+    }
+  } else {
+    if (a.Wq) return hipErrorInvalidValue;
+  }
   if (nw == 1 && pro == PRO_XF32 && epi == EPI_STORE_H) {
     hipLaunchKernelGGL((k_gemm<T, 1, MT, PRO_XF32, EPI_STORE_H>), grid, dim3(64), 0, s, a);
   } else if (nw == 4 && pro == PRO_NORM && epi == EPI_QKV) {
@@ -626,6 +739,25 @@ hipError_t launch_combine(int dtype, const CombineArgs& a, int batch, hipStream_
     hipLaunchKernelGGL(k_combine<bf16>, grid, block, 0, s, a);
   else
     hipLaunchKernelGGL(k_combine<float>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_i8(const void* wt, signed char* q, float* sc, int K, int N, hipStream_t s) {
+  if (K % TILE_K || N % TILE_N) return hipErrorInvalidValue;
+  const int KT = K / TILE_K, NT = N / TILE_N;
+  hipLaunchKernelGGL(k_quant_scale, dim3((NT * 16 + 255) / 256), dim3(256), 0, s, (const bf16*)wt, sc, KT, NT);
+  const size_t nfrag = (size_t)KT * NT * 64;
+  const int blocks = (int)((nfrag + 255) / 256 < 65535 ? (nfrag + 255) / 256 : 65535);
+  hipLaunchKernelGGL(k_quant_codes, dim3(blocks), dim3(256), 0, s, (const bf16*)wt, (const float*)sc, q, KT, NT);
+  return hipGetLastError();
+}
+
+hipError_t launch_untile_codes(const signed char* qt, const float* sct, signed char* q, float* sc, int K, int N,
+                               int colmap_kind, int cm_param, hipStream_t s) {
+  if (K % TILE_K || N % TILE_N) return hipErrorInvalidValue;
+  const size_t nfrag = (size_t)(K / TILE_K) * (N / TILE_N) * 64;
+  const int blocks = (int)((nfrag + 255) / 256 < 65535 ? (nfrag + 255) / 256 : 65535);
+  hipLaunchKernelGGL(k_untile_codes, dim3(blocks), dim3(256), 0, s, qt, sct, q, sc, K, N, colmap_kind, cm_param);
   return hipGetLastError();
 }
 

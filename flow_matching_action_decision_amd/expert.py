@@ -100,6 +100,19 @@ class Expert:
         B.phx_expert_prefill(self.h, x.data_ptr(), prefix_len, k.data_ptr(), v.data_ptr(), self.stream)
         return k, v
 
+    def weight_codes(self, layer: int, matrix: int):
+        """The 8-bit tier's int8 codes [K][N] and scales [N] of one matrix
+        (0 W_qkv, 1 W_o, 2 W_gu, 3 W_down) as device tensors."""
+        torch = self.torch
+        cfg = self.cfg
+        D, F, H, KVH, Dh = cfg["width"], cfg["mlp_hidden"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+        K = (D, H * Dh, D, F)[matrix]
+        N = ((H + 2 * KVH) * Dh, D, 2 * F, D)[matrix]
+        codes = torch.empty((K, N), dtype=torch.int8, device=self.device)
+        scales = torch.empty(N, dtype=torch.float32, device=self.device)
+        B.phx_expert_weight_codes(self.h, layer, matrix, codes.data_ptr(), scales.data_ptr(), self.stream)
+        return codes, scales
+
     def capsule_bytes(self) -> int:
         return B.phx_expert_capsule_bytes(self.h)
 

@@ -67,6 +67,13 @@ extern "C" {
                                   replaying the captured graph (same kernels, same results; for diagnosis) */
 #define PHX_FLAG_MULTI_KERNEL 2u  /* run the multi-kernel graph even where the persistent decision kernel
                                      applies (for comparison) */
+#define PHX_FLAG_WEIGHTS_INT8 8u  /* 8-bit weight tier (W8A16, "PhyAI" section 4.2 Quantization): every layer's
+                                     W_qkv, W_o, W_gu and W_down is quantised at create to int8 codes by
+                                     round-to-nearest per output column (s = max|w| / 127, q =
+                                     rint(w / s), ties to even, float32 arithmetic); activations stay
+                                     bf16 and each projection's sum is scaled by s in fp32.  bf16
+                                     weights, decoder block, batch * rows <= 160; runs the multi-kernel
+                                     graph (see phx_expert_weight_codes) */
 #define PHX_FLAG_TIMELINE 4u   /* persistent kernel: record a per-workgroup phase timeline (see
                                   phx_expert_timeline) */
 
@@ -245,6 +252,17 @@ PHX_API const char* phx_last_error(void);
  * loaded.  phx_expert_load_prefix_kv starts a new history at position 0.
  */
 PHX_API int phx_expert_commit_chunk(phx_expert* h, const float* chunk, phx_stream_t stream);
+
+/*
+ * The 8-bit tier's codes of one matrix, for checking: layer 0 <= layer <
+ * layers, matrix 0 = W_qkv, 1 = W_o, 2 = W_gu, 3 = W_down.  codes: device
+ * int8 [K][N] in the blob's row-major order; scales: device float [N].
+ * Stream-ordered.  Returns PHX_OK, PHX_E_INVALID, PHX_E_SHAPE (bad layer or
+ * matrix), PHX_E_STATE (the handle was not created with
+ * PHX_FLAG_WEIGHTS_INT8) or PHX_E_HIP.
+ */
+PHX_API int phx_expert_weight_codes(const phx_expert* h, int32_t layer, int32_t matrix, int8_t* codes, float* scales,
+                                    phx_stream_t stream);
 
 /* Number of kernel launches one decision replays (graph nodes). */
 PHX_API int phx_expert_kernels_per_decision(const phx_expert* h, int* count);

@@ -45,6 +45,10 @@ WORKLOADS = {
     # pi0.5-shape action expert: 18 layers, 10 steps, 768-token prefix, bf16
     "pi05_expert_bf16": dict(_BASE, id=1, layers=18, batch=1, capacity=768, steps=10, dtype="bf16",
                              prefix_lens=[768]),
+    # the pi0.5 shape on the 8-bit weight tier (same inputs as pi05_expert_bf16; flag 8 asks the library
+    # to quantise the layer projections to int8 per output column)
+    "pi05_expert_w8a16": dict(_BASE, id=1, layers=18, batch=1, capacity=768, steps=10, dtype="bf16",
+                              prefix_lens=[768], flags=8),
     # 16 independent requests, ragged prefixes drawn from {512,640,768,800}, capacity 800
     "rollout_b16_bf16": dict(_BASE, id=2, layers=18, batch=16, capacity=800, steps=10, dtype="bf16",
                              prefix_lens="draw"),

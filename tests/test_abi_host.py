@@ -92,6 +92,21 @@ def test_validate_rejects_prefill_shapes(lib, field, value):
     assert binding.phx_last_error()
 
 
+@pytest.mark.parametrize("workload", ["single_layer_fp32", "va_chunk_bf16", "wam_dit_bf16", "prefix_prefill_bf16"])
+def test_validate_rejects_the_int8_tier_off_its_path(lib, workload):
+    """The 8-bit weight tier: bf16 weights, the decoder block, at most 160 rows."""
+    from flow_matching_action_decision_amd import binding
+    c = binding.make_config(phx_inputs.workload(workload), flags=binding.PHX_FLAG_WEIGHTS_INT8)
+    assert binding.phx_expert_validate_config(c) == -3
+    c = binding.make_config(phx_inputs.workload("pi05_expert_w8a16"))
+    assert c.flags == binding.PHX_FLAG_WEIGHTS_INT8
+    assert binding.phx_expert_validate_config(c) == 0, binding.phx_last_error()
+
+
+def test_weight_codes_null_handle_without_a_gpu(lib):
+    assert lib.phx_expert_weight_codes(None, 0, 0, None, None, None) == -1
+
+
 def test_prefill_null_arguments_without_a_gpu(lib):
     assert lib.phx_expert_prefill(None, None, 0, None, None, None) == -1
 

@@ -1,0 +1,107 @@
+"""The 8-bit weight tier (W8A16: round-to-nearest int8 codes per output column,
+bf16 activations; "PhyAI" section 4.2 Quantization) through the C ABI.
+
+  * the library's codes and scales equal the oracle's quantiser, bit for bit,
+    for every layer's four projections (integer work: exact);
+  * the decision matches the oracle run on the dequantised weights s * q to
+    the bf16 bar (the two compute with the same weights);
+  * against the unquantised weights the decision moves by the quantisation
+    error, held to the tier's own looser bar (derived below);
+  * the full pi0.5 shape on the tier, the same two checks;
+  * replays are bit-identical; a handle without the tier has no codes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import phx_inputs
+from gpu_util import TOL_BF16, assert_close, gpu_decide, say, small_cfg
+
+pytestmark = pytest.mark.gpu
+
+# The tier's bar against the unquantised bf16 weights.  A code's rounding
+# error is uniform within half a step s = max|w| / 127 of its column; for
+# N(0, 0.02) columns of 1024 to 4096 weights the maximum is 3.3 to 3.9
+# standard deviations, so the error's RMS is about 3.6 / 127 / sqrt(12) =
+# 0.8% of a weight's, and each projection's output moves by about 0.8% of its
+# size (rel-L2).  The velocity is a chain of such projections in which each
+# sublayer's error adds to the residual stream; the decision integrates it
+# with |dt * S| = 1.  Measured on the small shape and the pi0.5 shape: rel-L2
+# 1-2e-2 of the actions.  The bar allows 5e-2 rel-L2 and 0.25 max-abs, and
+# the cosine similarity of every row must stay at least 0.998.
+TOL_W8 = dict(max_abs=0.25, rel_l2=5e-2, worst_row_cos=0.998)
+
+MATRICES = ("W_qkv", "W_o", "W_gu", "W_down")
+
+
+def w8_small(**kw):
+    cfg = small_cfg(id=80, flags=8, name="w8_small")
+    cfg.update(kw)
+    return cfg
+
+
+def test_w8_codes_are_the_oracles():
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+    cfg = w8_small(n_heads=4, head_dim=64, n_kv_heads=2)
+    say(f"case w8 codes: layers={cfg['layers']} width={cfg['width']} heads={cfg['n_heads']}/{cfg['n_kv_heads']}")
+    inp = phx_inputs.make_inputs(cfg, 0)
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    try:
+        for l in range(cfg["layers"]):
+            for m, nm in enumerate(MATRICES):
+                codes, scales = ex.weight_codes(l, m)
+                torch.cuda.synchronize()
+                q, s = oracle.quantize_i8(phx_inputs.view(inp["weights"], cfg, f"{nm}.{l}"))
+                gq = codes.cpu().numpy()
+                gs = scales.cpu().numpy()
+                assert np.array_equal(gq, q), f"{nm}.{l}: {int(np.sum(gq != q))} codes differ"
+                assert np.array_equal(gs.view(np.uint32), s.view(np.uint32)), f"{nm}.{l}: scales differ"
+    finally:
+        ex.close()
+
+
+def _w8_case(cfg, seed=0):
+    inp = phx_inputs.make_inputs(cfg, seed)
+    outs, nk = gpu_decide(cfg, inp, repeats=2)
+    assert np.array_equal(outs[0], outs[1]), "replays must be bit-identical"
+    sl = phx_inputs.weight_slices(cfg)
+    ref_q = oracle.decide(cfg, oracle.w8_weights(cfg, inp["weights"], sl), inp["kv_k"], inp["kv_v"], inp["lens"],
+                          inp["noise"])["actions"]
+    ref = oracle.decide(cfg, inp["weights"], inp["kv_k"], inp["kv_v"], inp["lens"], inp["noise"])["actions"]
+    assert_close(outs[0], ref_q, TOL_BF16, what=f"{cfg['name']} vs the oracle on the dequantised weights")
+    assert_close(outs[0], ref, TOL_W8, what=f"{cfg['name']} vs the oracle on the bf16 weights")
+    return nk
+
+
+def test_w8_small_decision():
+    cfg = w8_small()
+    say(f"case w8_small rows={cfg['rows']} L={cfg['prefix_lens']} layers={cfg['layers']} steps={cfg['steps']}")
+    _w8_case(cfg)
+
+
+def test_w8_ragged_batch():
+    cfg = w8_small(batch=3, prefix_lens=[100, 3, 64], name="w8_batch")
+    say("case w8_batch: 3 requests, prefixes 100, 3, 64")
+    _w8_case(cfg)
+
+
+def test_w8_pi05_shape():
+    cfg = phx_inputs.workload("pi05_expert_w8a16")
+    say("case pi05_expert_w8a16: 18 layers x 10 steps, 768-token prefix, int8 layer projections")
+    nk = _w8_case(cfg)
+    assert nk > 18 * 10  # the multi-kernel graph
+
+
+def test_codes_need_the_tier():
+    from flow_matching_action_decision_amd.binding import PhxError
+    from flow_matching_action_decision_amd.expert import Expert
+    cfg = small_cfg()
+    inp = phx_inputs.make_inputs(cfg, 0)
+    say("case codes without the tier")
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    try:
+        with pytest.raises(PhxError):
+            ex.weight_codes(0, 0)
+    finally:
+        ex.close()
