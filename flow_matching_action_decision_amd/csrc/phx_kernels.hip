@@ -402,6 +402,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   if (kbase >= T_b) return;
   const int G = a.H / a.KVH;
   const int GM = G * a.M;
+  if (w * 16 >= GM) return;  // a wave with no query row (no barrier follows)
   const int r = w * 16 + rloc;
   const bool rvalid = r < GM;
   const int hh = kvh * G + (rvalid ? r / a.M : 0);
@@ -478,32 +479,37 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   if (grp == 0 && rvalid) a.part_ml[pbase + r] = make_float2(mx, lsum);
 }
 
-// one workgroup per query row, one thread per head dimension
+// one thread per 4 dims of a query row (1024 / Dh rows per workgroup); splits in order
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int G = a.H / a.KVH;
   const int GM = G * a.M;
-  const int r = blockIdx.x % GM;
-  const int bk = blockIdx.x / GM;
+  const int tpr = a.Dh / 4;
+  const int rpb = 256 / tpr;
+  const int nrb = (GM + rpb - 1) / rpb;
+  const int bk = blockIdx.x / nrb;
+  const int r = (blockIdx.x - bk * nrb) * rpb + (int)threadIdx.x / tpr;
+  const int d = 4 * ((int)threadIdx.x % tpr);
+  if (r >= GM) return;
   const int b = bk / a.KVH;
   const int kvh = bk - b * a.KVH;
-  const int d = threadIdx.x;
-  if (d >= a.Dh) return;
   const int ns = (a.lens[b] + a.M + ATTN_KEYS - 1) / ATTN_KEYS;
   const size_t base = (size_t)bk * a.SMAX * a.GMP + r;
   float mx = -INFINITY;
   for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[base + (size_t)s * a.GMP].x);
-  float den = 0.f, num = 0.f;
+  float den = 0.f;
+  f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < ns; ++s) {
     const float2 ml = a.part_ml[base + (size_t)s * a.GMP];
     const float wgt = expf(ml.x - mx);
     den += ml.y * wgt;
-    num += wgt * a.part_o[(base + (size_t)s * a.GMP) * a.Dh + d];
+    num += wgt * *(const f32x4*)(a.part_o + (base + (size_t)s * a.GMP) * a.Dh + d);
   }
   const int hh = kvh * G + r / a.M;
   const int i = r % a.M;
   T* op = (T*)a.o + ((size_t)(b * a.M + i) * a.H + hh) * a.Dh + d;
-  *op = (T)(num / den);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) op[j] = (T)(num[j] / den);
 }
 
 // ------------------------------------------------------------ set-up kernels
@@ -734,7 +740,9 @@ hipError_t launch_attention(int dtype, int qt, const AttnArgs& a, int batch, hip
 }
 
 hipError_t launch_combine(int dtype, const CombineArgs& a, int batch, hipStream_t s) {
-  const dim3 grid(batch * a.H * a.M), block(a.Dh < 64 ? 64 : a.Dh);
+  if (a.Dh % 4 || a.Dh > 1024 || 1024 % a.Dh) return hipErrorInvalidValue;
+  const int GM = (a.H / a.KVH) * a.M, rpb = 1024 / a.Dh;
+  const dim3 grid(batch * a.KVH * ((GM + rpb - 1) / rpb)), block(256);
   if (dtype == 1)
     hipLaunchKernelGGL(k_combine<bf16>, grid, block, 0, s, a);
   else

@@ -529,6 +529,7 @@ hipError_t prepare_gemm() {
 template <int WN, int WM, int EPI>
 hipError_t launch_tile(const GemmT& g, hipStream_t s) {
   using T = Tile<WN, WM>;
+  if (g.N % T::BN || g.Mp % T::BM) return hipErrorInvalidValue;  // the grid covers whole tiles only
   const dim3 grid((g.N / T::BN) * (g.Mp / T::BM) * g.splits);
   if (g.kern == 0)
     hipLaunchKernelGGL((k_tgemm_ring<WN, WM, EPI>), grid, dim3(256), T::LDS, s, g);
