@@ -12,6 +12,9 @@ section 2.1, Figure 1a).  Cases:
     an 800-row bucket, 768 tokens) with two layers, sampled: layer 0 on every
     token, both layers on the first 64 tokens (under the causal mask the
     first tokens' cache does not depend on later ones);
+  * the benchmarked shape itself (18 layers): layer 0 on every token, and
+    the first 640 tokens' cache of every layer bit-identical when the later
+    tokens change;
   * prefill -> load_prefix_kv -> decide matches the oracle's prefill feeding
     the oracle's decision;
   * a prefill handle rejects decide, load_prefix_kv and out-of-range lengths.
@@ -180,3 +183,38 @@ def test_prefill_handle_rejects_other_calls():
         torch.cuda.synchronize()
     finally:
         ex.close()
+
+
+def test_prefill_full_shape_properties():
+    """The benchmarked prefill (18 layers, width 2048, 800-row bucket, 768 tokens): layer 0's cache on every
+    token against the oracle, the first 640 tokens' cache of every layer unchanged, bit for bit, when the
+    tokens after them change (causal mask; 640 is a multiple of the 32 queries of a wave), and every layer's
+    cache finite."""
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+    cfg = phx_inputs.workload("prefix_prefill_bf16")
+    n, cut = int(cfg["prefix_lens"][0]), 640
+    say(f"case prefill_full_shape: {cfg['layers']} layers, bucket {cfg['rows']}, {n} tokens, cut {cut}")
+    inp = phx_inputs.make_inputs(cfg, 0)
+    x0 = np.ascontiguousarray(inp["noise"][0])
+    x1 = x0.copy()
+    x1[cut:] = -x1[cut:] + 0.5
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    try:
+        outs = []
+        for xx in (x0, x1):
+            k, v = ex.prefill(torch.from_numpy(xx).cuda(), n)
+            torch.cuda.synchronize()
+            outs.append((_bf16_to_f32(k), _bf16_to_f32(v)))
+    finally:
+        ex.close()
+    (k0, v0), (k1, v1) = outs
+    assert np.all(np.isfinite(k0)) and np.all(np.isfinite(v0))
+    assert np.array_equal(k0[:, :cut], k1[:, :cut]) and np.array_equal(v0[:, :cut], v1[:, :cut])
+    assert not np.array_equal(k0[1:, cut:], k1[1:, cut:]), "tokens after the change must move"
+    one = dict(cfg, layers=1)
+    w1 = inp["weights"][:phx_inputs.weight_count(one)].copy()
+    phx_inputs.view(w1, one, "G")[:] = phx_inputs.view(inp["weights"], cfg, "G")[:2]
+    r0 = oracle.prefill(one, w1, x0, n)
+    assert_close(k0[:1], r0["k"], TOL_TOKENS, what="full shape, layer 0 keys, all tokens")
+    assert_close(v0[:1], r0["v"], TOL_TOKENS, what="full shape, layer 0 values, all tokens")
