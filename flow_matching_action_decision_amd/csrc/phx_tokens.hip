@@ -35,9 +35,20 @@ __device__ inline unsigned short bits(bf16 b) { return __builtin_bit_cast(unsign
 __device__ inline unsigned pack2(float a, float b) {
   return (unsigned)bits((bf16)a) | ((unsigned)bits((bf16)b) << 16);
 }
+// Hardware base-2 exponential (v_exp_f32, about 1 ulp; results below 2^-126
+// flush to zero, which every use here tolerates: softmax terms that small
+// vanish beside the row sum, and tanh saturates long before).  exp2f would
+// add a range fix-up of four more VALU instructions to every call.
+__device__ inline float hexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh-form GELU with tanh(u) = 1 - 2 / (exp(2u) + 1) from the hardware
+// exponential and reciprocal (a few ulp of float32, far below the bf16
+// rounding of every output; exp overflow gives tanh = 1, underflow -1)
 __device__ inline float gelu_tanh(float z) {
   const float k = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * z * (1.0f + tanhf(k * (z + 0.044715f * z * z * z)));
+  const float u = k * (z + 0.044715f * z * z * z);
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(hexp2(2.0f * 1.4426950408889634f * u) + 1.0f);
+  return 0.5f * z * (1.0f + t);
 }
 
 __device__ inline f32x4 mma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -802,7 +813,7 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run[qt], mx);
         // 0 on a query's first block (m_run = -inf); a query with no key yet keeps m = -inf
-        corr[qt] = m_new == -INFINITY ? 1.f : exp2f(m_run[qt] - m_new);
+        corr[qt] = m_new == -INFINITY ? 1.f : hexp2(m_run[qt] - m_new);
         l_run[qt] *= corr[qt];
         m_run[qt] = m_new;
         moved[qt] = true;
@@ -812,7 +823,7 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(fmaf(sc[qt][kt][i], sl2, mneg));
+          const float p = hexp2(fmaf(sc[qt][kt][i], sl2, mneg));
           l_run[qt] += p;
           pf[qt][kt >> 1][4 * (kt & 1) + i] = (bf16)p;
         }
@@ -904,7 +915,7 @@ __global__ void k_tcombine(AttnT a) {
     for (int s = 0; s < a.splits; ++s) {
       const float2 ml = *(const float2*)(a.pml + (((size_t)s * a.M + q) * a.H + h) * 2);
       if (ml.x == -INFINITY) continue;  // a split with no key this query sees
-      const float w = exp2f(ml.x - m);
+      const float w = hexp2(ml.x - m);
       const float* po = a.po + ((size_t)s * a.M + q) * (a.H * a.hd) + h * a.hd + 8 * g;
       n0 += w * *(const f32x4*)po;
       n1 += w * *(const f32x4*)(po + 4);
