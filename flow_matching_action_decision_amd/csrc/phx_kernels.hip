@@ -177,18 +177,53 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
   const int kpc = a.KT / (a.KSW * NW);
   const int kt0 = (ks * NW + w) * kpc;
 
+  // the 8-bit tier's column scales are loaded now and used after the reduction
+  f32x4 wsc4 = f32x4{1.f, 1.f, 1.f, 1.f};
+  if constexpr (W8) wsc4 = *(const f32x4*)(a.wsc + nt * 16 + grp * 4);
+  const T* wbase = (const T*)a.W + ((size_t)nt * a.KT + kt0) * TILE_ELEMS + lane * 8;
+  const signed char* qbase = a.Wq + ((size_t)nt * a.KT + kt0) * TILE_ELEMS + lane * 8;
+  // one group of weight tiles in flight; the first group goes out before the
+  // prologue's own loads, so the HBM stream starts at the kernel's first
+  // instructions instead of after the norm statistics
+  Frag af[G];
+  u32x2 raw[G];
+  auto issue_group = [&](int i0) {
+    if constexpr (W8) {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (i0 + j < kpc) raw[j] = i8_load(qbase + (size_t)(i0 + j) * TILE_ELEMS);
+    } else {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (i0 + j < kpc) af[j] = ldw8(wbase + (size_t)(i0 + j) * TILE_ELEMS);
+    }
+  };
+  issue_group(0);
+
   // adaptive RMSNorm statistics: 1/sqrt(mean(h^2) + eps) per activation row,
-  // from the per-tile sums of squares the producer of h left behind
+  // from the per-tile sums of squares the producer of h left behind (all
+  // loads of a batch issued before the first add; the adds keep tile order)
   float rinv[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) rinv[mt] = 0.f;
   if constexpr (PRO == PRO_NORM) {
+    constexpr int SSU = 16;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int row = mt * 16 + rloc;
       float s = 0.f;
-      if (row < a.rows)
-        for (int t = grp; t < a.NTD; t += 4) s += a.ss[(size_t)t * a.ss_ld + row];
+      if (row < a.rows) {
+        for (int t0 = grp; t0 < a.NTD; t0 += 4 * SSU) {
+          float sv[SSU];
+#pragma unroll
+          for (int u = 0; u < SSU; ++u) {
+            const int t = t0 + 4 * u;
+            sv[u] = t < a.NTD ? a.ss[(size_t)t * a.ss_ld + row] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < SSU; ++u) s += sv[u];
+        }
+      }
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
       rinv[mt] = 1.0f / sqrtf(s / (float)a.D + a.eps);
@@ -199,26 +234,12 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // the 8-bit tier's column scales are loaded now and used after the reduction
-  f32x4 wsc4 = f32x4{1.f, 1.f, 1.f, 1.f};
-  if constexpr (W8) wsc4 = *(const f32x4*)(a.wsc + nt * 16 + grp * 4);
-  const T* wbase = (const T*)a.W + ((size_t)nt * a.KT + kt0) * TILE_ELEMS + lane * 8;
-  const signed char* qbase = a.Wq + ((size_t)nt * a.KT + kt0) * TILE_ELEMS + lane * 8;
   for (int i0 = 0; i0 < kpc; i0 += G) {
-    Frag af[G];
+    if (i0 > 0) issue_group(i0);
     if constexpr (W8) {
-      // every code load of the group in flight before the first conversion
-      u32x2 raw[G];
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-        if (i0 + j < kpc) raw[j] = i8_load(qbase + (size_t)(i0 + j) * TILE_ELEMS);
 #pragma unroll
       for (int j = 0; j < G; ++j)
         if (i0 + j < kpc) af[j] = i8_frag(raw[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-        if (i0 + j < kpc) af[j] = ldw8(wbase + (size_t)(i0 + j) * TILE_ELEMS);
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -275,12 +296,25 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.KSW; ++s) {
-      const float* ps = a.part + ((size_t)(nt * a.KSW + s) * MT) * 256;
+    // a batch of splits' partials in flight at once, summed in split order
+    constexpr int SU = MT <= 1 ? 8 : (MT <= 2 ? 4 : 1);
+    for (int s0 = 0; s0 < a.KSW; s0 += SU) {
+      f32x4 pv[SU][MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int u = 0; u < SU; ++u) {
+        if (s0 + u < a.KSW) {
+          const float* ps = a.part + ((size_t)(nt * a.KSW + s0 + u) * MT) * 256;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] += ld_coherent(ps + (mt * 64 + lane) * 4 + i);
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[u][mt][i] = ld_coherent(ps + (mt * 64 + lane) * 4 + i);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+        if (s0 + u < a.KSW)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] += pv[u][mt];
     }
   }
 
@@ -416,6 +450,16 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   const T* kb = (const T*)a.kc + (size_t)bk * a.Ctot * DH;
   const T* vb = (const T*)a.vtc + (size_t)bk * DH * a.Ctot;
 
+  // the value fragments do not depend on the scores: their loads go out
+  // before the score MFMAs, so they arrive while the softmax runs
+  Frag vf[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const T* vrow = vb + (size_t)(dt * 16 + rloc) * a.Ctot + kbase + grp * 8;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) vf[dt][p] = ld8(vrow + 32 * p);
+  }
+
   f32x4 sacc[2][2];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
@@ -463,9 +507,8 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const T* vrow = vb + (size_t)(dt * 16 + rloc) * a.Ctot + kbase + grp * 8;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) mma(oacc[dt], pf[p], ld8(vrow + 32 * p));
+    for (int p = 0; p < 2; ++p) mma(oacc[dt], pf[p], vf[dt][p]);
   }
 
   const size_t pbase = ((size_t)bk * a.SMAX + s) * a.GMP;
@@ -495,15 +538,38 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int kvh = bk - b * a.KVH;
   const int ns = (a.lens[b] + a.M + ATTN_KEYS - 1) / ATTN_KEYS;
   const size_t base = (size_t)bk * a.SMAX * a.GMP + r;
+  // splits in batches of CU, every load of a batch in flight before the
+  // first use; maxima and sums in split order
+  constexpr int CU = 8;
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[base + (size_t)s * a.GMP].x);
+  for (int s0 = 0; s0 < ns; s0 += CU) {
+    float m[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) m[u] = s0 + u < ns ? a.part_ml[base + (size_t)(s0 + u) * a.GMP].x : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < CU; ++u) mx = fmaxf(mx, m[u]);
+  }
   float den = 0.f;
   f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
-    const float2 ml = a.part_ml[base + (size_t)s * a.GMP];
-    const float wgt = expf(ml.x - mx);
-    den += ml.y * wgt;
-    num += wgt * *(const f32x4*)(a.part_o + (base + (size_t)s * a.GMP) * a.Dh + d);
+  for (int s0 = 0; s0 < ns; s0 += CU) {
+    float2 ml[CU];
+    f32x4 po[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      if (s0 + u < ns) {
+        const size_t e = base + (size_t)(s0 + u) * a.GMP;
+        ml[u] = a.part_ml[e];
+        po[u] = *(const f32x4*)(a.part_o + e * a.Dh + d);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      if (s0 + u < ns) {
+        const float wgt = expf(ml[u].x - mx);
+        den += ml[u].y * wgt;
+        num += wgt * po[u];
+      }
+    }
   }
   const int hh = kvh * G + r / a.M;
   const int i = r % a.M;
