@@ -122,24 +122,20 @@ __device__ inline float gelu_tanh(float z) {
 // n-tile b / KSW and the K chunks (b % KSW)*NW + w of its NW waves; every
 // wave streams KT/(KSW*NW) consecutive tiles.
 
+// activation fragment of a plain (PRO_X) or float32 (PRO_XF32) activation;
+// the normalising prologue forms its fragments in the GEMM loop itself
 template <typename T, int PRO>
-__device__ inline typename FragT<T>::type load_act(const GemmArgs& a, int row, int k0, float rinv, const float* sc1,
-                                                   const float* sh) {
+__device__ inline typename FragT<T>::type load_act(const GemmArgs& a, int row, int k0) {
   using Frag = typename FragT<T>::type;
+  static_assert(PRO == PRO_X || PRO == PRO_XF32, "plain activations only");
   if (row >= a.rows) return zero_frag<Frag>();
   if constexpr (PRO == PRO_X) {
     return ld8((const T*)a.X + (size_t)row * a.ldx + k0);
-  } else if constexpr (PRO == PRO_XF32) {
+  } else {
     f32x8 v = ld8((const float*)a.X + (size_t)row * a.ldx + k0);
     float t[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) t[j] = v[j];
-    return to_frag<T>(t);
-  } else {
-    f32x8 hv = ld8(a.h + (size_t)row * a.D + k0);
-    float t[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = hv[j] * rinv * sc1[j] + sh[j];
     return to_frag<T>(t);
   }
 }
@@ -234,6 +230,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Activation operands in sub-groups of GA tiles: every load of a sub-group
+  // (and of its modulation rows) goes out before the first MFMA that uses
+  // it, so a wave pays one memory round trip per sub-group, not per tile.
+  // The scheduling barriers keep the compiler from interleaving the loads
+  // with the MFMAs again.
+  constexpr int GA = PRO == PRO_NORM ? (MT <= 1 ? 4 : (MT <= 2 ? 2 : 1)) : G;
+  static_assert(G % GA == 0, "activation sub-groups divide the weight group");
   for (int i0 = 0; i0 < kpc; i0 += G) {
     if (i0 > 0) issue_group(i0);
     if constexpr (W8) {
@@ -242,25 +245,54 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
         if (i0 + j < kpc) af[j] = i8_frag(raw[j]);
     }
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (i0 + j < kpc) {
-        const int k0 = (kt0 + i0 + j) * TILE_K + grp * 8;
-        float sc1[8], sh[8];
-        if constexpr (PRO == PRO_NORM) {
-          f32x8 s8 = ld8(a.mod + k0);
-          f32x8 h8 = ld8(a.mod + a.D + k0);
+    for (int a0 = 0; a0 < G; a0 += GA) {
+      if (i0 + a0 >= kpc) break;
+      Frag bfr[GA][MT];
+      if constexpr (PRO == PRO_NORM) {
+        f32x8 s8[GA], m8[GA], h8[GA][MT];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            sc1[q] = 1.0f + s8[q];
-            sh[q] = h8[q];
+        for (int j = 0; j < GA; ++j) {
+          if (i0 + a0 + j < kpc) {
+            const int k0 = (kt0 + i0 + a0 + j) * TILE_K + grp * 8;
+            s8[j] = ld8(a.mod + k0);
+            m8[j] = ld8(a.mod + a.D + k0);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const int row = mt * 16 + rloc;
+              h8[j][mt] = row < a.rows ? ld8(a.h + (size_t)row * a.D + k0) : f32x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            }
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          Frag bfr = load_act<T, PRO>(a, mt * 16 + rloc, k0, rinv[mt], sc1, sh);
-          mma(acc[mt], af[j], bfr);
+        for (int j = 0; j < GA; ++j) {
+          if (i0 + a0 + j < kpc) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              float t[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) t[q] = h8[j][mt][q] * rinv[mt] * (1.0f + s8[j][q]) + m8[j][q];
+              bfr[j][mt] = mt * 16 + rloc < a.rows ? to_frag<T>(t) : zero_frag<Frag>();
+            }
+          }
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < GA; ++j) {
+          if (i0 + a0 + j < kpc) {
+            const int k0 = (kt0 + i0 + a0 + j) * TILE_K + grp * 8;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              bfr[j][mt] = load_act<T, PRO>(a, mt * 16 + rloc, k0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int j = 0; j < GA; ++j)
+        if (i0 + a0 + j < kpc)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) mma(acc[mt], af[a0 + j], bfr[j][mt]);
     }
   }
 
@@ -418,6 +450,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
 // the A operand of O = P . V, and V is stored transposed so its B operand
 // is one contiguous 16-byte read.  Partial (max, sum, unnormalised output)
 // per split are combined by k_combine in split order.
+// This form loads every fragment straight from memory; it runs the float32
+// workloads (bf16 runs k_attn_lds below, which stages the chunk in LDS).
 template <typename T, int DH>
 __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   using Frag = typename FragT<T>::type;
@@ -450,27 +484,70 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
   const T* kb = (const T*)a.kc + (size_t)bk * a.Ctot * DH;
   const T* vb = (const T*)a.vtc + (size_t)bk * DH * a.Ctot;
 
-  // the value fragments do not depend on the scores: their loads go out
-  // before the score MFMAs, so they arrive while the softmax runs
-  Frag vf[DT][2];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const T* vrow = vb + (size_t)(dt * 16 + rloc) * a.Ctot + kbase + grp * 8;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) vf[dt][p] = ld8(vrow + 32 * p);
-  }
-
-  f32x4 sacc[2][2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
+  // Loads in explicit phases, each phase's loads all in flight before the
+  // first use: the key fragments (half of them at a time when they would
+  // not fit the registers), then the value fragments, together with the
+  // keys when both fit and otherwise after the score MFMAs (they do not
+  // depend on the scores, so they arrive while the softmax runs).  The
+  // scheduling barriers keep the compiler from interleaving loads and MFMAs
+  // again, which left about four loads in flight.
+  constexpr int FRAG_REGS = (int)sizeof(Frag) / 4;
+  constexpr int K_REGS = 4 * DS * FRAG_REGS, V_REGS = 2 * DT * FRAG_REGS;
+  constexpr bool K_HALVES = K_REGS > 128;               // float32 at head_dim 256: half the keys at a time
+  constexpr bool V_EARLY = K_REGS + V_REGS <= 128;
+  Frag kf[2][2][DS];
+  auto load_k = [&](int p) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      sacc[p][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int key = kbase + 32 * p + 8 * (rloc >> 2) + 4 * hf + (rloc & 3);
       const T* krow = kb + (size_t)key * DH + grp * 8;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) mma(sacc[p][hf], ld8(krow + ds * 32), qf[ds]);
+      for (int ds = 0; ds < DS; ++ds) kf[p][hf][ds] = ld8(krow + ds * 32);
     }
+  };
+  constexpr bool V_HALVES = V_REGS > 128;               // float32 at head_dim 256: half the keys at a time
+  Frag vf[DT][2];
+  auto load_v = [&](int p) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const T* vrow = vb + (size_t)(dt * 16 + rloc) * a.Ctot + kbase + grp * 8;
+      vf[dt][p] = ld8(vrow + 32 * p);
+    }
+  };
+  f32x4 sacc[2][2];
+  auto scores = [&](int p) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      sacc[p][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) mma(sacc[p][hf], kf[p][hf][ds], qf[ds]);
+    }
+  };
+  if constexpr (K_HALVES) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      load_k(p);
+      __builtin_amdgcn_sched_barrier(0);
+      scores(p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    load_k(0);
+    load_k(1);
+    if constexpr (V_EARLY) {
+      load_v(0);
+      load_v(1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    scores(0);
+    scores(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (!V_EARLY && !V_HALVES) {
+    load_v(0);
+    load_v(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // lane (query row rloc, grp) holds keys kbase + 32p + 8grp + 4hf + ii
   float sv[2][8];
@@ -505,10 +582,164 @@ __global__ __launch_bounds__(512) void k_attn(AttnArgs a) {
 
   f32x4 oacc[DT];
 #pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if constexpr (V_HALVES) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) mma(oacc[dt], pf[p], vf[dt][p]);
+  }
+
+  const size_t pbase = ((size_t)bk * a.SMAX + s) * a.GMP;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int rr = w * 16 + 4 * grp + ii;
+      if (rr < GM) a.part_o[(pbase + rr) * DH + dt * 16 + rloc] = oacc[dt][ii];
+    }
+  if (grp == 0 && rvalid) a.part_ml[pbase + r] = make_float2(mx, lsum);
+}
+
+// bf16 attention of one split with the key chunk staged in LDS.  Every
+// wave of the workgroup needs the whole 64-key chunk (its keys and its
+// value columns); fragment reads straight from memory touch 16 rows per
+// instruction with half of each 128-byte line used, so the five waves of a
+// pi0.5 workgroup pulled ten times the chunk's bytes through the CU's load
+// pipe.  Here the workgroup reads the chunk once with whole-line 16-byte
+// loads (all in flight together), and the waves read their fragments from
+// LDS.  Row strides carry 16 bytes of padding so the 16 rows of a fragment
+// read spread over the banks.  Results are those of k_attn: the same MFMAs
+// in the same order on the same operands.
+template <int DH>
+constexpr int attn_lds_bytes() {
+  return (ATTN_KEYS * (DH + 8) + DH * (ATTN_KEYS + 8)) * 2;
+}
+
+template <int DH>
+__global__ __launch_bounds__(512) void k_attn_lds(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char attn_smem[];
+  constexpr int DS = DH / 32;
+  constexpr int DT = DH / 16;
+  constexpr int KST = DH + 8;         // key row stride in LDS (elements)
+  constexpr int VST = ATTN_KEYS + 8;  // value (dim) row stride in LDS
+  constexpr int KP = ATTN_KEYS * DH / 8, VP = DH * ATTN_KEYS / 8;  // 16-byte pieces
+  constexpr int U = 16;               // pieces per thread and batch
+  bf16* Ks = (bf16*)attn_smem;
+  bf16* Vs = Ks + ATTN_KEYS * KST;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int rloc = lane & 15;
+  const int grp = lane >> 4;
+  const int s = blockIdx.x % a.SMAX;
+  const int bk = blockIdx.x / a.SMAX;  // request * KVH + kv head
+  const int b = bk / a.KVH;
+  const int kvh = bk - b * a.KVH;
+  const int T_b = a.lens[b] + a.M;
+  const int kbase = s * ATTN_KEYS;
+  if (kbase >= T_b) return;  // the whole workgroup: no barrier is skipped
+  const int G = a.H / a.KVH;
+  const int GM = G * a.M;
+  const bool wave_rows = w * 16 < GM;
+  const int r = w * 16 + rloc;
+  const bool rvalid = r < GM;
+  const int hh = kvh * G + (rvalid ? r / a.M : 0);
+  const int i = rvalid ? r % a.M : 0;
+
+  bf16x8 qf[DS];
+  const bf16* qrow = (const bf16*)a.q + ((size_t)(b * a.M + i) * a.H + hh) * DH + grp * 8;
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) qf[ds] = rvalid ? ld8(qrow + ds * 32) : zero_frag<bf16x8>();
+
+  // stage the chunk: key rows kbase .. kbase + 63 and the same columns of
+  // the transposed values (rows past the keys in use are read too; their
+  // probabilities are zero, as in the direct-load kernel)
+  const bf16* kb = (const bf16*)a.kc + (size_t)bk * a.Ctot * DH;
+  const bf16* vb = (const bf16*)a.vtc + (size_t)bk * DH * a.Ctot;
+  for (int i0 = tid; i0 < KP + VP; i0 += U * nthr) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = i0 + u * nthr;
+      if (idx < KP) {
+        const int key = idx / (DH / 8), c = idx % (DH / 8);
+        v[u] = *(const u32x4*)(kb + (size_t)(kbase + key) * DH + c * 8);
+      } else if (idx < KP + VP) {
+        const int j = idx - KP, dim = j / (ATTN_KEYS / 8), c = j % (ATTN_KEYS / 8);
+        v[u] = *(const u32x4*)(vb + (size_t)dim * a.Ctot + kbase + c * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = i0 + u * nthr;
+      if (idx < KP) {
+        const int key = idx / (DH / 8), c = idx % (DH / 8);
+        *(u32x4*)(Ks + key * KST + c * 8) = v[u];
+      } else if (idx < KP + VP) {
+        const int j = idx - KP, dim = j / (ATTN_KEYS / 8), c = j % (ATTN_KEYS / 8);
+        *(u32x4*)(Vs + dim * VST + c * 8) = v[u];
+      }
+    }
+  }
+  __syncthreads();
+  if (!wave_rows) return;  // a wave with no query row (no barrier follows)
+
+  f32x4 sacc[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      sacc[p][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = 32 * p + 8 * (rloc >> 2) + 4 * hf + (rloc & 3);
+      const bf16* krow = Ks + key * KST + grp * 8;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        mma(sacc[p][hf], __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + ds * 32)), qf[ds]);
+    }
+
+  // lane (query row rloc, grp) holds keys kbase + 32p + 8grp + 4hf + ii
+  float sv[2][8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int key = kbase + 32 * p + 8 * grp + 4 * hf + ii;
+        const float v = key < T_b ? sacc[p][hf][ii] * a.scale : -INFINITY;
+        sv[p][4 * hf + ii] = v;
+        mx = fmaxf(mx, v);
+      }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float lsum = 0.f;
+  bf16x8 pf[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    float pv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = expf(sv[p][j] - mx);
+      lsum += pv[j];
+    }
+    pf[p] = to_frag<bf16>(pv);
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  f32x4 oacc[DT];
+#pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16* vrow = Vs + (dt * 16 + rloc) * VST + grp * 8;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) mma(oacc[dt], pf[p], vf[dt][p]);
+    for (int p = 0; p < 2; ++p) mma(oacc[dt], pf[p], __builtin_bit_cast(bf16x8, *(const u32x4*)(vrow + 32 * p)));
   }
 
   const size_t pbase = ((size_t)bk * a.SMAX + s) * a.GMP;
@@ -789,16 +1020,38 @@ hipError_t launch_gemm(int dtype, int nw, int mt, int pro, int epi, const GemmAr
   return dtype == 1 ? gemm_t<bf16>(nw, mt, pro, epi, a, s) : gemm_t<float>(nw, mt, pro, epi, a, s);
 }
 
+template <int DH>
+static hipError_t attn_lds(const dim3& grid, const dim3& block, const AttnArgs& a, hipStream_t s) {
+  static bool attr_set = false;  // LDS beyond the default 64 KiB (head_dim 256)
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_attn_lds<DH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             attn_lds_bytes<DH>());
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_attn_lds<DH>, grid, block, attn_lds_bytes<DH>(), s, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t attn_t(int qt, const AttnArgs& a, int batch, hipStream_t s) {
   const dim3 grid(batch * a.KVH * a.SMAX), block(qt * 64);
-  switch (a.Dh) {
-    case 64: hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((k_attn<T, 256>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (std::is_same<T, bf16>::value) {
+    switch (a.Dh) {
+      case 64: return attn_lds<64>(grid, block, a, s);
+      case 128: return attn_lds<128>(grid, block, a, s);
+      case 256: return attn_lds<256>(grid, block, a, s);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.Dh) {
+      case 64: hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, a); break;
+      case 128: hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, a); break;
+      case 256: hipLaunchKernelGGL((k_attn<T, 256>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_attention(int dtype, int qt, const AttnArgs& a, int batch, hipStream_t s) {
