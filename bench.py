@@ -182,6 +182,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=50, help="timed launches of the dominant kernel")
+    ap.add_argument("--multi-kernel", action="store_true",
+                    help="pi05_expert_bf16 on the captured multi-kernel graph (2 + 6 NL launches per Euler step) "
+                         "instead of the persistent decision kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device-to-device copy of 256 MiB (a kernel of known traffic, to scale "
                          "profiler byte counters against)")
@@ -202,6 +205,10 @@ def main():
     from flow_matching_action_decision_amd.expert import Expert
     from flow_matching_action_decision_amd import binding
 
+    if args.multi_kernel and args.workload != WORKLOAD:
+        print("--multi-kernel applies to pi05_expert_bf16 (the other workloads have one execution path)",
+              file=sys.stderr)
+        sys.exit(2)
     if args.workload in TOKEN_WORKLOADS:
         return bench_tokens(args)
     if args.workload in PREFILL_WORKLOADS:
@@ -212,8 +219,9 @@ def main():
     inp = phx_inputs.make_inputs(cfg, args.seed)
     ab = algorithmic_bytes(cfg)
 
+    mk = bool(args.multi_kernel)
     log("bench: creating handle")
-    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"], flags=binding.PHX_FLAG_MULTI_KERNEL if mk else 0)
     keep = ex.load_all(inp)
     noise = torch.from_numpy(inp["noise"]).cuda()
     out = torch.empty_like(noise)
@@ -244,7 +252,7 @@ def main():
     # dominant kernel: duration of its launches, timed with HIP events on the
     # stream it runs on
     dom = ex.time_dominant_kernel(args.kernel_reps)
-    batch = name != WORKLOAD  # the rollout batch runs the multi-kernel graph
+    batch = name != WORKLOAD or mk  # the rollout batch runs the multi-kernel graph
     kernel_hash = kernel_source_hash(("phx_kernels.hip", "phx_internal.h") + TOKEN_KERNEL_SOURCES if batch
                                      else DECISION_KERNEL_SOURCES)
     traffic = None if batch else measured_traffic(kernel_hash)
@@ -256,7 +264,7 @@ def main():
 
     # execution-state capsule: snapshot, restore and fork of the declared state
     # regions, each timed with HIP events on the handle's stream
-    capsule = capsule_timing(ex, Expert, cfg, inp, stream)
+    capsule = capsule_timing(ex, Expert, cfg, inp, stream, flags=binding.PHX_FLAG_MULTI_KERNEL if mk else 0)
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -282,6 +290,8 @@ def main():
     w8 = name in W8_WORKLOADS
     if w8:
         metric = "ms/decision (pi0.5-shape, 18L x 10 steps, 8-bit weight tier) + % peak HBM GB/s, 1 GPU"
+    elif mk:
+        metric = "ms/decision (pi0.5-shape, 18L x 10 steps, multi-kernel graph) + % peak HBM GB/s, 1 GPU"
     elif batch:
         metric = f"ms/decision ({name}: {cfg['batch']} requests, 18L x 10 steps) + % peak HBM GB/s, 1 GPU"
     else:
@@ -292,15 +302,16 @@ def main():
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 prefix K/V, N(0,1) noise)",
         "config": {"workload": name, "layers": cfg["layers"], "euler_steps": cfg["steps"],
-                   "action_rows": cfg["rows"], "prefix_len": lens[0] if (not batch or w8) else lens, "width": cfg["width"],
+                   "action_rows": cfg["rows"], "prefix_len": lens[0] if cfg["batch"] == 1 else lens, "width": cfg["width"],
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} / {cfg['n_kv_heads']} kv",
                    "mlp_hidden": cfg["mlp_hidden"], "batch": cfg["batch"],
                    **({"weights": "int8 codes per output column (layer projections), bf16 in/out projections"}
-                      if w8 else {})},
+                      if w8 else {}),
+                   **({"path": "multi-kernel graph"} if mk else {})},
         "decisions_per_s": round(1000.0 / ms, 1),
         "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
         **({"requests_per_s": round(1000.0 * cfg["batch"] / ms, 1),
-            "ms_per_request_amortised": round(ms / cfg["batch"], 4)} if batch and not w8 else {}),
+            "ms_per_request_amortised": round(ms / cfg["batch"], 4)} if cfg["batch"] > 1 else {}),
         "algorithmic_bytes_per_decision": ab["per_decision"],
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "kernels_per_decision": nk,
@@ -311,7 +322,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def capsule_timing(ex, Expert, cfg: dict, inp: dict, stream, reps: int = 20) -> dict:
+def capsule_timing(ex, Expert, cfg: dict, inp: dict, stream, reps: int = 20, flags: int = 0) -> dict:
     """Average ms of a capsule snapshot, a restore into the same handle and a
     fork into a second handle of the same plan (restore on a fresh handle)."""
     import torch
@@ -329,7 +340,7 @@ def capsule_timing(ex, Expert, cfg: dict, inp: dict, stream, reps: int = 20) -> 
 
     snap = timed(lambda: ex.capsule_save(cap))
     rest = timed(lambda: ex.capsule_restore(cap))
-    other = Expert(cfg, inp["weights"], inp["weights_bits"])
+    other = Expert(cfg, inp["weights"], inp["weights_bits"], flags=flags)
     try:
         fork = timed(lambda: other.capsule_restore(cap))
     finally:
