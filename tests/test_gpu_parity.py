@@ -214,3 +214,38 @@ def test_error_paths_on_gpu():
     with pytest.raises(p.PhxError) as e:
         p.phx_expert_create(c, 0, 0, 0)
     assert e.value.code == -1
+
+
+@pytest.mark.parametrize("plan", ["graph", "batched", "persistent"])
+def test_nan_prefix_tail_is_never_read(plan):
+    """Each request is first loaded with a full-capacity prefix of NaN and then
+    with its real, shorter prefix.  The decision must give the same bits as a
+    fresh handle loaded only with the real prefixes, and be finite: no key or
+    value row at or past a request's length may reach the result (masked
+    probabilities are zero, and 0 * NaN would still be NaN)."""
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+    if plan == "graph":
+        cfg = small_cfg(name="nan_tail_graph", prefix_lens=[45])
+    elif plan == "batched":
+        cfg = small_cfg(name="nan_tail_batched", batch=8, prefix_lens=[0, 17, 100, 54, 64, 1, 99, 33])
+    else:
+        cfg = phx_inputs.workload("pi05_expert_bf16", prefix_lens=[500])
+    say(f"case {cfg['name']}: NaN prefixes of {cfg['capacity']} rows, then L={cfg['prefix_lens']}")
+    inp = phx_inputs.make_inputs(cfg, 7)
+    C, kvd = cfg["capacity"], cfg["n_kv_heads"] * cfg["head_dim"]
+    nan_bits = np.full((cfg["layers"], C, kvd), 0x7FC0, dtype=np.uint16).view(np.int16)
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    try:
+        nk = torch.from_numpy(nan_bits).cuda()
+        for b in range(cfg["batch"]):
+            ex.load_prefix_kv(b, nk, nk, C)
+        keep = ex.load_all(inp)
+        nz = torch.from_numpy(inp["noise"]).cuda()
+        reloaded = ex.decide(nz).cpu().numpy()
+        del keep, nk
+    finally:
+        ex.close()
+    fresh, _ = gpu_decide(cfg, inp)
+    assert np.all(np.isfinite(reloaded))
+    assert np.array_equal(reloaded, fresh[0])
