@@ -185,6 +185,9 @@ def main():
     ap.add_argument("--multi-kernel", action="store_true",
                     help="pi05_expert_bf16 on the captured multi-kernel graph (2 + 6 NL launches per Euler step) "
                          "instead of the persistent decision kernel")
+    ap.add_argument("--timeline", action="store_true",
+                    help="pi05_expert_bf16 on the persistent kernel with its phase timeline on: prints one JSON "
+                         "line of per-phase critical-path microseconds instead of the benchmark line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device-to-device copy of 256 MiB (a kernel of known traffic, to scale "
                          "profiler byte counters against)")
@@ -209,6 +212,11 @@ def main():
         print("--multi-kernel applies to pi05_expert_bf16 (the other workloads have one execution path)",
               file=sys.stderr)
         sys.exit(2)
+    if args.timeline:
+        if args.workload != WORKLOAD or args.multi_kernel:
+            print("--timeline applies to pi05_expert_bf16 on the persistent kernel", file=sys.stderr)
+            sys.exit(2)
+        return bench_timeline(args)
     if args.workload in TOKEN_WORKLOADS:
         return bench_tokens(args)
     if args.workload in PREFILL_WORKLOADS:
@@ -319,6 +327,69 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(line), flush=True)
+
+
+PHASES = ("qkv", "attention", "combine", "out_proj", "gate_up", "down", "residual_owners")
+
+
+def bench_timeline(args):
+    """Critical path of the persistent decision kernel, phase by phase.
+
+    The handle records, per workgroup, when its compute waves finished each
+    phase of each layer-step (a 100 MHz counter).  A phase's critical time is
+    how far the latest workgroup's stamp moved past the previous phase's
+    latest stamp, averaged over the interior layer-steps (Euler steps 1..S-2,
+    layers 2..NL-3), away from the ramp at the start and the drain at the
+    end.  Also reported: per phase, how long after the previous phase's
+    latest stamp the first and the median workgroup finish it."""
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+    from flow_matching_action_decision_amd import binding
+
+    cfg = phx_inputs.workload(WORKLOAD)
+    inp = phx_inputs.make_inputs(cfg, args.seed)
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"], flags=binding.PHX_FLAG_TIMELINE)
+    keep = ex.load_all(inp)
+    noise = torch.from_numpy(inp["noise"]).cuda()
+    out = torch.empty_like(noise)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(args.warmup, 1)):
+        ex.decide(noise, out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    ex.decide(noise, out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    tl = np.asarray(ex.timeline(), dtype=np.int64)
+    del keep
+    ex.close()
+    S, NL = cfg["steps"], cfg["layers"]
+    crit = np.zeros(len(PHASES))
+    first = np.zeros(len(PHASES))
+    median = np.zeros(len(PHASES))
+    n = 0
+    for k in range(1, S - 1):
+        base = 1 + k * (2 + 7 * NL)
+        for l in range(2, NL - 2):
+            e = base + 1 + 7 * l
+            prev = tl[:, e - 1].max()
+            for p in range(len(PHASES)):
+                col = tl[:, e + p]
+                crit[p] += col.max() - prev
+                first[p] += col.min() - prev
+                median[p] += np.median(col) - prev
+                prev = col.max()
+            n += 1
+    to_us = 0.01 / n  # 100 MHz ticks, averaged
+    line = {"workload": WORKLOAD, "kernel": "decision_kernel", "ms_per_decision_with_timeline": round(ms, 4),
+            "layer_steps_averaged": n,
+            "critical_us": {p: round(float(c * to_us), 2) for p, c in zip(PHASES, crit)},
+            "critical_us_per_layer_step": round(float(crit.sum() * to_us), 2),
+            "first_finish_after_previous_us": {p: round(float(c * to_us), 2) for p, c in zip(PHASES, first)},
+            "median_finish_after_previous_us": {p: round(float(c * to_us), 2) for p, c in zip(PHASES, median)}}
     print(json.dumps(line), flush=True)
 
 
