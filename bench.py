@@ -294,6 +294,7 @@ def main():
         cpu = cpu_baseline(cfg, inp, args.cpu_budget_s)
 
     hbm_gbs = ab["per_decision"] / (ms * 1e-3) / 1e9
+    copy_gbs = measured_copy_gbs()
     lens = [int(L) for L in inp["lens"]]
     w8 = name in W8_WORKLOADS
     if w8:
@@ -322,12 +323,60 @@ def main():
             "ms_per_request_amortised": round(ms / cfg["batch"], 4)} if cfg["batch"] > 1 else {}),
         "algorithmic_bytes_per_decision": ab["per_decision"],
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "hbm_copy_gbs": round(copy_gbs, 1), "hbm_frac_of_copy": round(hbm_gbs / copy_gbs, 4),
         "kernels_per_decision": nk,
         "capsule": capsule,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_copy_gbs(gib: int = 4, reps: int = 50, warm: int = 10) -> float:
+    """Device-to-device copy bandwidth of this GPU: a `gib` GiB buffer copied
+    into another, best of `reps` after `warm` untimed copies; read plus
+    written bytes over the time (a practical ceiling beside the 8 TB/s spec)."""
+    import torch
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(warm):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    stream = torch.cuda.current_stream()
+    for a, b in ev:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    best_ms = min(a.elapsed_time(b) for a, b in ev)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * n / (best_ms * 1e-3) / 1e9
+
+
+def measured_gemm_tflops(n: int = 8192, reps: int = 20, warm: int = 5) -> float:
+    """Dense bf16 GEMM rate of this GPU through the vendor library (torch.matmul,
+    n x n x n), best of `reps` after `warm`: a practical ceiling beside the
+    2.5 PFLOP/s spec."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    for _ in range(warm):
+        torch.matmul(a, b)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    stream = torch.cuda.current_stream()
+    for e0, e1 in ev:
+        e0.record(stream)
+        torch.matmul(a, b)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    best_ms = min(e0.elapsed_time(e1) for e0, e1 in ev)
+    del a, b
+    torch.cuda.empty_cache()
+    return 2.0 * n ** 3 / (best_ms * 1e-3) / 1e12
 
 
 PHASES = ("qkv", "attention", "combine", "out_proj", "gate_up", "down", "residual_owners")
@@ -516,6 +565,7 @@ def bench_tokens(args):
 
     tflops = fl["flops_per_decision"] / (ms * 1e-3) / 1e12
     hbm = fl["bytes_per_decision"] / (ms * 1e-3) / 1e9
+    gemm_tf = measured_gemm_tflops()
     line = {
         "metric": f"ms/decision ({name}) + % of MFMA bf16 peak, 1 GPU",
         "value": round(ms, 4), "unit": "ms/decision", "n_gpus": 1, "steps": steps, "warmup": warm,
@@ -530,6 +580,7 @@ def bench_tokens(args):
         "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
         "flops_per_decision": fl["flops_per_decision"], "tflops": round(tflops, 1),
         "mfma_frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "library_gemm_tflops": round(gemm_tf, 1), "mfma_frac_of_library_gemm": round(tflops / gemm_tf, 4),
         "algorithmic_bytes_per_decision": fl["bytes_per_decision"], "hbm_gbs": round(hbm, 1),
         "kernels_per_decision": nk, "history_update": history, "roofline": roofline, "cpu_baseline": cpu,
     }
@@ -677,6 +728,7 @@ def bench_prefill(args):
         cpu = cpu_baseline_prefill(cfg, inp, fl)
 
     tflops = fl["flops"] / (ms * 1e-3) / 1e12
+    gemm_tf = measured_gemm_tflops()
     line = {
         "metric": f"ms/prefill ({name}) + % of MFMA bf16 peak, 1 GPU",
         "value": round(ms, 4), "unit": "ms/prefill", "n_gpus": 1, "steps": steps, "warmup": warm,
@@ -690,6 +742,7 @@ def bench_prefill(args):
         "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
         "flops_per_prefill": fl["flops"], "tflops": round(tflops, 1),
         "mfma_frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "library_gemm_tflops": round(gemm_tf, 1), "mfma_frac_of_library_gemm": round(tflops / gemm_tf, 4),
         "algorithmic_bytes_per_prefill": fl["bytes"], "hbm_gbs": round(fl["bytes"] / (ms * 1e-3) / 1e9, 1),
         "kernels_per_prefill": nk, "roofline": roofline, "cpu_baseline": cpu,
     }
