@@ -198,11 +198,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
 
   // adaptive RMSNorm statistics: 1/sqrt(mean(h^2) + eps) per activation row,
   // from the per-tile sums of squares the producer of h left behind (all
-  // loads of a batch issued before the first add; the adds keep tile order)
+  // loads of a batch issued before the first add; the adds keep tile order).
+  // For up to two row tiles it runs after the first activation sub-group's
+  // loads are issued, so the statistics and the activations share one
+  // memory round trip; with more rows that would hold too many registers at
+  // once, and it runs first.
   float rinv[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) rinv[mt] = 0.f;
-  if constexpr (PRO == PRO_NORM) {
+  auto norm_stats = [&]() {
     constexpr int SSU = 16;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -224,7 +228,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
       s += __shfl_xor(s, 32);
       rinv[mt] = 1.0f / sqrtf(s / (float)a.D + a.eps);
     }
-  }
+  };
+  constexpr bool STATS_FIRST = MT > 2;
+  if constexpr (PRO == PRO_NORM && STATS_FIRST) norm_stats();
 
   f32x4 acc[MT];
 #pragma unroll
@@ -239,11 +245,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
   static_assert(G % GA == 0, "activation sub-groups divide the weight group");
   for (int i0 = 0; i0 < kpc; i0 += G) {
     if (i0 > 0) issue_group(i0);
-    if constexpr (W8) {
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-        if (i0 + j < kpc) af[j] = i8_frag(raw[j]);
-    }
 #pragma unroll
     for (int a0 = 0; a0 < G; a0 += GA) {
       if (i0 + a0 >= kpc) break;
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
             }
           }
         }
+        if (!STATS_FIRST && a0 == 0 && i0 == 0) norm_stats();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < GA; ++j) {
@@ -287,6 +289,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (W8) {  // codes to bf16 after every load of the sub-group is out
+#pragma unroll
+        for (int j = 0; j < GA; ++j)
+          if (i0 + a0 + j < kpc) af[a0 + j] = i8_frag(raw[a0 + j]);
       }
 #pragma unroll
       for (int j = 0; j < GA; ++j)
