@@ -165,10 +165,35 @@ def cpu_baseline(cfg: dict, inp: dict, budget_s: float) -> dict:
         oracle.decide(dict(cfg, steps=s), inp["weights"], inp["kv_k"], inp["kv_v"], inp["lens"], inp["noise"], lib=lib)
         t1 = time.perf_counter()
         per_step = (t1 - t0) / s
-    return {"value": round(per_step * cfg["steps"] * 1e3, 1), "unit": "ms/decision", "cores": omp_threads(),
+    cores = omp_threads()
+    one = one_thread_step_s(cfg, inp, lib)
+    return {"value": round(per_step * cfg["steps"] * 1e3, 1), "unit": "ms/decision", "cores": cores,
             "kind": "oracle",
             "sample": f"first {s} of {cfg['steps']} Euler steps of the same {cfg['layers']}-layer decision "
-                      f"(double-precision oracle, OpenMP), scaled to a full decision"}
+                      f"(double-precision oracle, OpenMP), scaled to a full decision",
+            **({"value_1_thread": round(one * cfg["steps"] * 1e3, 1),
+                "sample_1_thread": "first Euler step on one OpenMP thread, scaled to a full decision"}
+               if one is not None else {})}
+
+
+def one_thread_step_s(cfg: dict, inp: dict, lib):
+    """Seconds of one Euler step of the oracle on a single OpenMP thread (the
+    process's OpenMP runtime is set to one thread and then restored), or None
+    where the runtime cannot be reached."""
+    import ctypes
+    import oracle
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    before = int(gomp.omp_get_max_threads())
+    gomp.omp_set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.decide(dict(cfg, steps=1), inp["weights"], inp["kv_k"], inp["kv_v"], inp["lens"], inp["noise"], lib=lib)
+        return time.perf_counter() - t0
+    finally:
+        gomp.omp_set_num_threads(before)
 
 
 def main():
