@@ -17,6 +17,10 @@ roofline is the dominant GEMM's TFLOP/s against the bf16 dense peak.
 --workload prefix_prefill_bf16 times the prefix prefill (18 causal layers of
 width 2048 over 768 tokens in an 800-row bucket, writing the K/V cache), one
 phx_expert_prefill call per step.
+--multi-kernel runs the pi0.5 decision on the captured multi-kernel graph
+instead of the persistent decision kernel.
+--timeline prints, instead of the benchmark line, the persistent kernel's
+critical path per phase of a layer-step (from its per-workgroup timeline).
 
 Prints ONE JSON line (see --help for the knobs).  Besides the wall-clock
 figure it carries:
@@ -24,9 +28,13 @@ figure it carries:
     its average launch duration, timed here with HIP events on the stream the
     kernel runs on, against MI355X's 8 TB/s HBM peak;
   * "cpu_baseline": the CPU oracle timed on a bounded sample of the same
-    workload on this host's cores (a reported baseline, not the target).
+    workload on this host's cores, and on one thread (a reported baseline,
+    not the target);
+  * measured ceilings beside the spec peaks: a 4 GiB device copy for the
+    HBM-bound lines, a library 8192^3 bf16 GEMM for the MFMA-bound ones.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload NAME]
+       [--multi-kernel] [--timeline]
 """
 from __future__ import annotations
 
