@@ -611,6 +611,20 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     h->tnodes.push_back(nd);
   };
   auto norm = [&](int k, int l, int kind, const float* scale, const float* shift, const char* name) {
+    // right after a residual GEMM whose k splits end in a reduction launch, the norm runs in that launch
+    if (!h->tnodes.empty()) {
+      TokNode& prev = h->tnodes.back();
+      tok::GemmT& pg = prev.g;
+      if (prev.op == TOP_GEMM && prev.epi == tok::EP_RESID && pg.splits > 1 && pg.out == h->h && pg.N == D &&
+          pg.ldo == D && D <= 256 * 16) {
+        pg.nrm_on = 1; pg.nrm_kind = kind; pg.nrm_scale = scale; pg.nrm_shift = shift; pg.nrm_eps = c.rms_eps;
+        pg.nrm_out = h->nb;
+        prev.bytes += (uint64_t)Mp * D * 2 + 2ull * D * 4;
+        const size_t len = std::strlen(prev.name);
+        std::snprintf(prev.name + len, sizeof(prev.name) - len, "+norm");
+        return;
+      }
+    }
     TokNode nd{};
     nd.kind = PHX_NODE_ROW_NORM; nd.step = k; nd.layer = l; nd.op = TOP_NORM;
     nd.norm_kind = kind; nd.src = h->h; nd.scale = scale; nd.shift = shift; nd.eps = c.rms_eps; nd.dst = h->nb;

@@ -56,6 +56,14 @@ struct GemmT {
   int kern;            // 0: LDS-ring kernel, 1: register-fed kernel (set by plan_gemm)
   int splits;          // k splits (set by plan_gemm); > 1 needs part
   float* part;         // split partials [splits][Mp][N] f32
+  // EP_RESID with splits > 1 and N <= 4096: the row norm that follows, fused into the split reduction
+  // (out = the residual rows [M][N] f32 with ldo = N): nrm_out bf16 [Mp][N] = norm(row) * (1 + scale) + shift,
+  // the rows past M zero; kind 0 RMS, 1 LayerNorm (mean subtracted), as launch_tnorm
+  int nrm_on, nrm_kind;
+  const float* nrm_scale;
+  const float* nrm_shift;
+  float nrm_eps;
+  void* nrm_out;
 };
 
 // Chooses the tile shape and k splits of g for a chip of n_cu compute units.

@@ -462,6 +462,96 @@ __global__ void k_tsplit(GemmT g) {
   }
 }
 
+// The split reduction of a residual GEMM fused with the row norm that
+// follows it (the next GEMM's bf16 input rows), one workgroup per row.
+// Thread t owns the 4-column groups t, t + 256, ... of the row: it loads
+// every split's partials of its groups at once (16-byte loads), sums them
+// in split order and adds them into the residual row (times the gate, if
+// any), as k_tsplit does; then the workgroup normalises the new row as
+// k_tnorm does (sums over the thread's columns in order, the same reduction
+// tree).  Rows M..Mp-1 get zero norm rows.
+constexpr int RN_GROUPS = 4;  // 4-column groups per thread: N <= 256 * 16
+constexpr int RN_SPLITS = 8;  // splits whose loads go out together
+__global__ __launch_bounds__(256) void k_tsplit_resid_norm(GemmT g) {
+  __shared__ float red[8];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int N = g.N;
+  bf16* o = (bf16*)g.nrm_out + (size_t)row * N;
+  if (row >= g.M) {
+    for (int d = t; d < N; d += 256) o[d] = (bf16)0.0f;
+    return;
+  }
+  float* hr = (float*)g.out + (size_t)row * g.ldo;
+  f32x4 v[RN_GROUPS];
+#pragma unroll
+  for (int q = 0; q < RN_GROUPS; ++q) v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < g.splits; z0 += RN_SPLITS) {
+    f32x4 pz[RN_SPLITS][RN_GROUPS];
+#pragma unroll
+    for (int u = 0; u < RN_SPLITS; ++u)
+#pragma unroll
+      for (int q = 0; q < RN_GROUPS; ++q) {
+        const int c = 4 * (t + 256 * q);
+        if (z0 + u < g.splits && c < N) pz[u][q] = *(const f32x4*)(g.part + ((size_t)(z0 + u) * g.Mp + row) * N + c);
+      }
+#pragma unroll
+    for (int u = 0; u < RN_SPLITS; ++u)
+#pragma unroll
+      for (int q = 0; q < RN_GROUPS; ++q)
+        if (z0 + u < g.splits && 4 * (t + 256 * q) < N) v[q] += pz[u][q];
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < RN_GROUPS; ++q) {
+    const int c = 4 * (t + 256 * q);
+    if (c < N) {
+      f32x4 cur = *(const f32x4*)(hr + c);
+      if (g.gate)
+        cur += *(const f32x4*)(g.gate + c) * v[q];
+      else
+        cur += v[q];
+      *(f32x4*)(hr + c) = cur;
+      v[q] = cur;
+    } else {
+      v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    s += (v[q][0] + v[q][1]) + (v[q][2] + v[q][3]);
+  }
+  auto block_sum = [&](float a) -> float {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+    __syncthreads();
+    if ((t & 63) == 0) red[t >> 6] = a;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+  };
+  float mean = 0.f;
+  if (g.nrm_kind == 1) mean = block_sum(s) / (float)N;
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < RN_GROUPS; ++q) {
+    if (4 * (t + 256 * q) < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float cdev = v[q][i] - mean;
+        ss += cdev * cdev;
+      }
+    }
+  }
+  const float inv = 1.0f / sqrtf(block_sum(ss) / (float)N + g.nrm_eps);
+#pragma unroll
+  for (int q = 0; q < RN_GROUPS; ++q) {
+    const int c = 4 * (t + 256 * q);
+    if (c < N) {
+      const f32x4 sc = *(const f32x4*)(g.nrm_scale + c), sh = *(const f32x4*)(g.nrm_shift + c);
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = (v[q][i] - mean) * inv * (1.0f + sc[i]) + sh[i];
+      *(u32x2*)(o + c) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+    }
+  }
+}
+
 struct TileCfg {
   int wn, wm;
 };
@@ -548,6 +638,10 @@ hipError_t launch_tile(const GemmT& g, hipStream_t s) {
     hipLaunchKernelGGL((k_tgemm_reg<WN, WM, EPI>), grid, dim3(256), 0, s, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.splits == 1) return e;
+  if (g.nrm_on) {
+    hipLaunchKernelGGL(k_tsplit_resid_norm, dim3(g.Mp), dim3(256), 0, s, g);
+    return hipGetLastError();
+  }
   const size_t total = (size_t)g.M * (g.N / 4);
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
   hipLaunchKernelGGL(k_tsplit<EPI>, dim3(blocks), dim3(256), 0, s, g);
@@ -570,6 +664,9 @@ hipError_t launch_tgemm_e(const GemmT& g, hipStream_t s) {
 hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
   if (g.K % 32 || g.N % 64 || g.Mp % ROW_PAD || g.M > g.Mp || g.tile < 0 || g.tile >= N_TILES) return hipErrorInvalidValue;
   if (g.splits < 1 || (g.K / 32) % (g.splits * UNR) || (g.splits > 1 && !g.part)) return hipErrorInvalidValue;
+  if (g.nrm_on && (epi != EP_RESID || g.splits < 2 || g.N > 256 * 4 * RN_GROUPS || g.N % 4 || g.ldo != g.N || !g.nrm_out || !g.nrm_scale ||
+                   !g.nrm_shift || (g.nrm_kind != 0 && g.nrm_kind != 1)))
+    return hipErrorInvalidValue;
   if ((size_t)g.Mp * g.K * 2 >= (1ull << 32) || (size_t)g.K * g.N * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   switch (epi) {
     case EP_BF16: return launch_tgemm_e<EP_BF16>(g, s);

@@ -52,13 +52,16 @@ def test_batched_plan(shape):
     """8 requests x 10 rows (80 rows, bf16): the batched plan (large-token
     GEMMs over all rows, per-request caches, batched attention), ragged
     prefixes.  Kernel count identifies the plan: per step the input
-    projection, per layer 8 launches, the final norm and velocity projection."""
+    projection, per layer 8 launches, the final norm and velocity projection;
+    a norm that follows a residual GEMM with k splits runs inside that GEMM's
+    reduction launch, so per layer 6 to 8 nodes."""
     H, KVH, Dh, D = shape
     cfg = small_cfg(batch=8, prefix_lens=[0, 17, 100, 54, 64, 1, 99, 33], n_heads=H, n_kv_heads=KVH, head_dim=Dh,
                     width=D)
     m, inp, out = _case(cfg)
     _, nk = gpu_decide(cfg, inp)
-    assert nk == cfg["steps"] * (3 + 8 * cfg["layers"])
+    L, S = cfg["layers"], cfg["steps"]
+    assert nk % S == 0 and S * (3 + 6 * L) <= nk <= S * (3 + 8 * L)
 
 
 def test_ragged_batch_f32():

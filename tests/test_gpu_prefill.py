@@ -79,8 +79,9 @@ def _case(cfg, lengths, seed=0, tol=TOL_TOKENS):
 
 def test_prefill_small():
     _, _, nk = _case(prefill_small(), [200, 137, 1])
-    # per layer: 2 norms, QKV, attention (+ combine), O, gate/up, down; the last layer stops after its QKV
-    assert nk >= 2 * 7 + 2
+    # per layer: 2 norms, QKV, attention (+ combine), O, gate/up, down, where a norm after a residual GEMM
+    # with k splits runs inside that GEMM's reduction launch; the last layer stops after its QKV
+    assert nk >= 2 * 5 + 2
 
 
 def test_prefill_head_dim_128_two_kv_heads():
