@@ -776,36 +776,62 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int kvh = bk - b * a.KVH;
   const int ns = (a.lens[b] + a.M + ATTN_KEYS - 1) / ATTN_KEYS;
   const size_t base = (size_t)bk * a.SMAX * a.GMP + r;
-  // splits in batches of CU, every load of a batch in flight before the
-  // first use; maxima and sums in split order
-  constexpr int CU = 8;
+  // up to ONE splits (the pi0.5 and rollout shapes): every statistic and
+  // partial in flight at once, one memory round; more splits: batches of
+  // CU, one round for the maxima and one for the sums per batch.  Maxima
+  // and sums in split order either way.
+  constexpr int ONE = 16, CU = 8;
   float mx = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += CU) {
-    float m[CU];
-#pragma unroll
-    for (int u = 0; u < CU; ++u) m[u] = s0 + u < ns ? a.part_ml[base + (size_t)(s0 + u) * a.GMP].x : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < CU; ++u) mx = fmaxf(mx, m[u]);
-  }
   float den = 0.f;
   f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += CU) {
-    float2 ml[CU];
-    f32x4 po[CU];
+  if (ns <= ONE) {
+    float2 ml[ONE];
+    f32x4 po[ONE];
 #pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      if (s0 + u < ns) {
-        const size_t e = base + (size_t)(s0 + u) * a.GMP;
+    for (int u = 0; u < ONE; ++u) {
+      if (u < ns) {
+        const size_t e = base + (size_t)u * a.GMP;
         ml[u] = a.part_ml[e];
         po[u] = *(const f32x4*)(a.part_o + e * a.Dh + d);
       }
     }
 #pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      if (s0 + u < ns) {
+    for (int u = 0; u < ONE; ++u)
+      if (u < ns) mx = fmaxf(mx, ml[u].x);
+#pragma unroll
+    for (int u = 0; u < ONE; ++u) {
+      if (u < ns) {
         const float wgt = expf(ml[u].x - mx);
         den += ml[u].y * wgt;
         num += wgt * po[u];
+      }
+    }
+  } else {
+    for (int s0 = 0; s0 < ns; s0 += CU) {
+      float m[CU];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) m[u] = s0 + u < ns ? a.part_ml[base + (size_t)(s0 + u) * a.GMP].x : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < CU; ++u) mx = fmaxf(mx, m[u]);
+    }
+    for (int s0 = 0; s0 < ns; s0 += CU) {
+      float2 ml[CU];
+      f32x4 po[CU];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        if (s0 + u < ns) {
+          const size_t e = base + (size_t)(s0 + u) * a.GMP;
+          ml[u] = a.part_ml[e];
+          po[u] = *(const f32x4*)(a.part_o + e * a.Dh + d);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        if (s0 + u < ns) {
+          const float wgt = expf(ml[u].x - mx);
+          den += ml[u].y * wgt;
+          num += wgt * po[u];
+        }
       }
     }
   }
