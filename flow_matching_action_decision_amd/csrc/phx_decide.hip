@@ -1097,7 +1097,7 @@ __device__ inline u32x4 rsrc_words(const void* p, unsigned bytes) {
   return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
-constexpr unsigned LOAD_DEPTH = 16;  // tiles in flight per loader wave
+constexpr unsigned LOAD_DEPTH = 24;  // tiles in flight per loader wave (16 measured 2% slower; 28, 32 the same)
 
 // Loader waves wait on LDS only: a global load in their wait loop would make
 // the next use of any loaded register wait for the whole batch of tile loads
@@ -1148,7 +1148,7 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
       dma_tile(WR, (unsigned)c.lane * 16u, off, lds, true);
     ++issued;
     if (issued > LOAD_DEPTH) {
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
       if (c.lane == 0) lds_store(&c.sh->ready[q], issued - LOAD_DEPTH);
     }
   }
