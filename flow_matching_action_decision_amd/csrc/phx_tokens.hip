@@ -1006,17 +1006,44 @@ __global__ void k_tcombine(AttnT a) {
     const int h = (int)(qh % a.H);
     const int q = (int)(qh / a.H);
     float m = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.pml[(((size_t)s * a.M + q) * a.H + h) * 2]);
     f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float2 ml = *(const float2*)(a.pml + (((size_t)s * a.M + q) * a.H + h) * 2);
-      if (ml.x == -INFINITY) continue;  // a split with no key this query sees
-      const float w = hexp2(ml.x - m);
-      const float* po = a.po + ((size_t)s * a.M + q) * (a.H * a.hd) + h * a.hd + 8 * g;
-      n0 += w * *(const f32x4*)po;
-      n1 += w * *(const f32x4*)(po + 4);
-      den += w * ml.y;
+    constexpr int ONE = 8;  // up to ONE splits: every statistic and partial in flight at once, one memory round
+    if (a.splits <= ONE) {
+      float2 ml[ONE];
+      f32x4 p0[ONE], p1[ONE];
+#pragma unroll
+      for (int s = 0; s < ONE; ++s) {
+        if (s < a.splits) {
+          ml[s] = *(const float2*)(a.pml + (((size_t)s * a.M + q) * a.H + h) * 2);
+          const float* po = a.po + ((size_t)s * a.M + q) * (a.H * a.hd) + h * a.hd + 8 * g;
+          p0[s] = *(const f32x4*)po;
+          p1[s] = *(const f32x4*)(po + 4);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < ONE; ++s)
+        if (s < a.splits) m = fmaxf(m, ml[s].x);
+#pragma unroll
+      for (int s = 0; s < ONE; ++s) {
+        if (s < a.splits && ml[s].x != -INFINITY) {  // a split with no key this query sees adds nothing
+          const float w = hexp2(ml[s].x - m);
+          n0 += w * p0[s];
+          n1 += w * p1[s];
+          den += w * ml[s].y;
+        }
+      }
+    } else {
+      for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.pml[(((size_t)s * a.M + q) * a.H + h) * 2]);
+      for (int s = 0; s < a.splits; ++s) {
+        const float2 ml = *(const float2*)(a.pml + (((size_t)s * a.M + q) * a.H + h) * 2);
+        if (ml.x == -INFINITY) continue;  // a split with no key this query sees
+        const float w = hexp2(ml.x - m);
+        const float* po = a.po + ((size_t)s * a.M + q) * (a.H * a.hd) + h * a.hd + 8 * g;
+        n0 += w * *(const f32x4*)po;
+        n1 += w * *(const f32x4*)(po + 4);
+        den += w * ml.y;
+      }
     }
     *(u32x4*)((bf16*)a.o + (size_t)q * (a.H * a.hd) + h * a.hd + 8 * g) =
         u32x4{pack2(n0[0] / den, n0[1] / den), pack2(n0[2] / den, n0[3] / den), pack2(n1[0] / den, n1[1] / den),
