@@ -687,7 +687,9 @@ hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
 __global__ __launch_bounds__(256) void k_tnorm(int kind, const float* __restrict__ h, const float* __restrict__ scale,
                                                const float* __restrict__ shift, float eps, bf16* __restrict__ out,
                                                int M, int D) {
-  constexpr int PER = 16;
+  // thread t owns the 4-column groups t, t + 256, t + 512, t + 768 of its row (16-byte loads), the same
+  // columns and sums as the norm fused into the split reduction (k_tsplit_resid_norm)
+  constexpr int GR = 4;
   __shared__ float red[8];
   const int row = blockIdx.x, t = threadIdx.x;
   bf16* o = out + (size_t)row * D;
@@ -696,13 +698,13 @@ __global__ __launch_bounds__(256) void k_tnorm(int kind, const float* __restrict
     return;
   }
   const float* x = h + (size_t)row * D;
-  float v[PER];
+  f32x4 v[GR];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = t + 256 * i;
-    v[i] = d < D ? x[d] : 0.f;
-    s += v[i];
+  for (int q = 0; q < GR; ++q) {
+    const int c = 4 * (t + 256 * q);
+    v[q] = c < D ? *(const f32x4*)(x + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    s += (v[q][0] + v[q][1]) + (v[q][2] + v[q][3]);
   }
   auto block_sum = [&](float a) -> float {
 #pragma unroll
@@ -716,22 +718,32 @@ __global__ __launch_bounds__(256) void k_tnorm(int kind, const float* __restrict
   if (kind == 1) mean = block_sum(s) / (float)D;
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = t + 256 * i;
-    const float c = d < D ? v[i] - mean : 0.f;
-    ss += c * c;
+  for (int q = 0; q < GR; ++q) {
+    if (4 * (t + 256 * q) < D) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float cdev = v[q][i] - mean;
+        ss += cdev * cdev;
+      }
+    }
   }
   const float inv = 1.0f / sqrtf(block_sum(ss) / (float)D + eps);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = t + 256 * i;
-    if (d < D) o[d] = (bf16)((v[i] - mean) * inv * (1.0f + scale[d]) + shift[d]);
+  for (int q = 0; q < GR; ++q) {
+    const int c = 4 * (t + 256 * q);
+    if (c < D) {
+      const f32x4 sc = *(const f32x4*)(scale + c), sh = *(const f32x4*)(shift + c);
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = (v[q][i] - mean) * inv * (1.0f + sc[i]) + sh[i];
+      *(u32x2*)(o + c) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+    }
   }
 }
 
 hipError_t launch_tnorm(int kind, const float* h, const float* scale, const float* shift, float eps, void* out, int M,
                         int Mp, int D, hipStream_t s) {
-  if (D > 256 * 16 || M > Mp) return hipErrorInvalidValue;
+  if (D > 256 * 16 || D % 4 || M > Mp) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tnorm, dim3(Mp), dim3(256), 0, s, kind, h, scale, shift, eps, (bf16*)out, M, D);
   return hipGetLastError();
 }
