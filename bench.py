@@ -148,6 +148,25 @@ def measured_traffic(kernel_hash: str):
     return t.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo), and the
+    logical cores the process may run on."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    name = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 0
+    return f"{name} ({n} logical cores available)"
+
+
 def omp_threads() -> int:
     import ctypes
     try:
@@ -289,6 +308,8 @@ def main():
     per = np.array([a.elapsed_time(b) for a, b in ev])
     ms = total_ms / args.steps
     log(f"bench: {ms:.4f} ms/decision (p50 {np.percentile(per, 50):.4f}, p95 {np.percentile(per, 95):.4f})")
+    # a decision call returns once enqueued; the status word says the last one ran to its end
+    assert ex.status() == 0, "the last timed decision gave up waiting (persistent kernel status)"
 
     # dominant kernel: duration of its launches, timed with HIP events on the
     # stream it runs on
@@ -325,6 +346,7 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(cfg, inp, args.cpu_budget_s)
+        cpu["cpu_model"] = cpu_model()
 
     hbm_gbs = ab["per_decision"] / (ms * 1e-3) / 1e9
     copy_gbs = measured_copy_gbs()
@@ -595,6 +617,7 @@ def bench_tokens(args):
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_tokens(cfg, inp, fl)
+        cpu["cpu_model"] = cpu_model()
 
     tflops = fl["flops_per_decision"] / (ms * 1e-3) / 1e12
     hbm = fl["bytes_per_decision"] / (ms * 1e-3) / 1e9
@@ -759,6 +782,7 @@ def bench_prefill(args):
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_prefill(cfg, inp, fl)
+        cpu["cpu_model"] = cpu_model()
 
     tflops = fl["flops"] / (ms * 1e-3) / 1e12
     gemm_tf = measured_gemm_tflops()

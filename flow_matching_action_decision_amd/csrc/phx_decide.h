@@ -44,8 +44,9 @@ constexpr int G = 256;              // workgroups (one per CU)
 constexpr int RP = 16;              // padded action rows
 constexpr int TILE_BYTES = 1024;    // one 16x32 bf16 MFMA A tile
 constexpr int TILE_ELEMS = TILE_BYTES / 2;
-constexpr int RING = 124;           // LDS ring of weight tiles per workgroup (with the static shared data
-                                    // 162.4 of the 160 KiB a workgroup may hold; 120 measured 0.6% slower)
+constexpr int RING = 124;           // LDS ring of weight tiles per workgroup (124 KiB; with the static
+                                    // shared data within the 160 KiB a workgroup may hold; 120 measured
+                                    // 0.6% slower)
 constexpr int NCOMPUTE = 4;         // compute waves (waves 0..3); waves 4..7 load
 constexpr int NLOADER = 4;
 constexpr int THREADS = 64 * (NCOMPUTE + NLOADER);
@@ -144,6 +145,9 @@ struct Args {
 };
 
 hipError_t launch_decide(const Args& a, hipStream_t s);
+// workgroups of k_decide one compute unit can hold at once (the kernel needs
+// every one of its G workgroups resident together: at least 1 per CU)
+hipError_t decide_occupancy(int* blocks_per_cu);
 hipError_t launch_decide_advance(void* arena, hipStream_t s);
 // set-up kernels
 // out[k * out_kstride + l * N + n] = sum_d shift(k, norm_stride*l + norm_off)[d] * W_l[d][colmap(n)]

@@ -12,7 +12,7 @@
 // same two ideas take a form that fits MI355X:
 //   * Loader waves (4 per workgroup) stream the workgroup's fixed share of
 //     every weight matrix (and of the prefix K/V for attention workgroups)
-//     into a 120-tile LDS ring, running up to a ring ahead of the compute, so
+//     into a 124-tile LDS ring, running up to a ring ahead of the compute, so
 //     the HBM stream never waits for a sublayer boundary;
 //   * compute waves (4 per workgroup) exchange activations with other
 //     workgroups through tagged 8-byte words (payload | exchange tag) written
@@ -72,6 +72,10 @@ struct Shared {
   s16x4 att_p[NCOMPUTE][64];
   __attribute__((aligned(16))) unsigned char red[2][RED_BYTES];
 };
+// the ring (dynamic) and the static shared data together stay within the
+// 160 KiB of LDS one workgroup may hold
+static_assert(RING * TILE_BYTES + sizeof(Shared) <= 160 * 1024, "LDS budget of one workgroup");
+
 
 __device__ inline Rsrc rsrc(const void* p, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -347,10 +351,6 @@ __device__ __attribute__((always_inline)) inline void ll_poll(Ctx& c, const PB& 
 #pragma unroll
     for (int i = 0; i < N; ++i) acc |= (v[i][1] ^ tag) | (v[i][3] ^ tag);
     if (__ballot(acc != 0u) == 0ull) return;
-#ifdef PHX_POLL_RELOAD
-    keep_waiting(c, t0, spins);
-    continue;
-#endif
     // probe addresses: lane i takes load i's first stale word; lanes without
     // a stale load repeat the highest stale load's probe
     unsigned pa = 0;
@@ -1247,7 +1247,7 @@ __global__ void k_decide_advance(unsigned* seq) {
   if (threadIdx.x == 0 && blockIdx.x == 0) seq[0] = seq[0] + 1u;
 }
 
-hipError_t launch_decide(const Args& a, hipStream_t s) {
+static hipError_t allow_ring_lds() {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_decide, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1255,6 +1255,19 @@ hipError_t launch_decide(const Args& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  return hipSuccess;
+}
+
+hipError_t decide_occupancy(int* blocks_per_cu) {
+  hipError_t e = allow_ring_lds();
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)k_decide, THREADS,
+                                                       RING * TILE_BYTES);
+}
+
+hipError_t launch_decide(const Args& a, hipStream_t s) {
+  hipError_t e = allow_ring_lds();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decide, dim3(G), dim3(THREADS), RING * TILE_BYTES, s, a);
   return hipGetLastError();
 }

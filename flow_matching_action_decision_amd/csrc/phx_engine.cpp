@@ -411,6 +411,10 @@ bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop
                                    (unsigned long long)c.steps * dec::step_bytes(c.layers) +
                                    (unsigned long long)dec::G * dec::timeline_events(c.steps, c.layers) * 4ull;
   if (arena >= (1ull << 31)) return false;
+  // the decision kernel's workgroups wait on each other, so all G of them must be resident at once:
+  // one per compute unit, which its LDS ring and register budget have to allow
+  int per_cu = 0;
+  if (dec::decide_occupancy(&per_cu) != hipSuccess || per_cu < 1) return false;
   return true;
 }
 

@@ -170,7 +170,13 @@ PHX_API int phx_expert_weights_bytes(const phx_expert_config* cfg, size_t* bytes
  * weights into the layout its kernels stream, builds the step-conditioning
  * table (sinusoidal embedding of every tau_k and all 2*NL+1 modulation
  * projections, kept for the life of the handle), and captures the step loop
- * as one HIP graph.
+ * as one HIP graph.  Defined by: "FlashRT-PAI" section 2.2 and Appendix A.1
+ * (a deployment fixes views, context bucket, action horizon and step count;
+ * a versioned interface checks shapes and plans before anything runs) and
+ * section 3.4 / Table 9 (static buffers and state regions live at fixed
+ * addresses for the life of the deployment); "PhyAI" paper section 4.2,
+ * Graph replay (the timestep table and every layer's AdaRMS modulation are
+ * prepared once, before any denoising, and the step loop is captured once).
  *   weights: host or device pointer to weights_bytes bytes in the layout
  *            above; the caller may free it once the call returns.
  *   stream:  stream the set-up work is ordered on; the call returns after it
@@ -184,7 +190,10 @@ PHX_API int phx_expert_create(const phx_expert_config* cfg, const void* weights,
 /*
  * Loads (replaces) the prefix context of one request: the prefix keys and
  * values every layer attends to, already rotary-encoded as the prefix model
- * wrote them.
+ * wrote them.  Defined by: "FlashRT-PAI" section 2.1 / Figure 1a (the prefix
+ * writes its K/V once per observation and every flow step of the expert
+ * reads it) and section 3.4 (a new observation invalidates the context; the
+ * caller owns the freshness of what it loads).
  *   request:    0 <= request < batch.
  *   k, v:       device pointers, [layers][prefix_len][n_kv_heads*head_dim] of
  *               kv_dtype; copied into the handle's state region (V is stored
@@ -201,11 +210,20 @@ PHX_API int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void
  * One decision: x = noise; S Euler steps of the expert; actions = x.  For
  * PHX_BLOCK_DIT, one pass of the block stack over the tokens: noise holds the
  * token rows x, actions receives the residual stream after the last block.
+ * Defined by: "FlashRT-PAI" section 2.1 / Figure 1a (ten flow-matching Euler
+ * steps of the 18-layer expert over ten action rows, x += dt * v) and
+ * section 3.3 (the whole decision replays without host work between
+ * sublayers); "PhyAI" paper section 4.2, Graph replay (one captured graph of
+ * the denoising loop per decision).
  *   noise, actions: device pointers to float32 [batch][rows][state_dim]
  *                   (they may be the same buffer).
  * Stream-ordered and asynchronous: copy in, graph replay, copy out.  The
  * caller synchronizes.  Returns PHX_OK, PHX_E_INVALID, PHX_E_STATE (a
  * request has no loaded prefix) or PHX_E_HIP.
+ * PHX_OK means the decision was enqueued, not that it completed: on the
+ * persistent decision kernel (kernels_per_decision == 2) a decision whose
+ * workgroups could not all make progress gives up after a bounded wait and
+ * writes NaN actions.  After synchronizing, phx_expert_status reports it.
  */
 PHX_API int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_stream_t stream);
 
@@ -231,7 +249,9 @@ PHX_API int phx_expert_prefill(phx_expert* h, const float* x, int32_t prefix_len
                                phx_stream_t stream);
 
 /* Frees every device allocation of the handle. NULL-safe. Synchronizes the
-   handle's internal stream first. */
+   handle's internal stream first.  Defined by: "FlashRT-PAI" Appendix A.1
+   (the engine owns the deployment's buffers from set-up to teardown; the
+   caller's pointers are never freed by it). */
 PHX_API void phx_expert_destroy(phx_expert* h);
 
 /* Message of the last failing call in this thread ("" if none). */
@@ -318,7 +338,10 @@ PHX_API int phx_expert_launch_node(phx_expert* h, int32_t node, phx_stream_t str
  * (synchronous; call after the stream has passed the decision).  0 means it
  * completed; 1 means a workgroup waited longer than its limit (0.5 s) for
  * data another workgroup should have produced, the decision gave up, and its
- * actions were filled with NaN.  Always 0 for the multi-kernel path.
+ * actions were filled with NaN.  That happens only when the GPU cannot hold
+ * all 256 workgroups of the decision kernel at once (another process holds
+ * compute units); phx_expert_create checks that one workgroup fits on every
+ * compute unit.  Always 0 for the graph paths.
  * Returns PHX_OK, PHX_E_INVALID or PHX_E_HIP.
  */
 PHX_API int phx_expert_status(const phx_expert* h, uint32_t* status);

@@ -43,6 +43,8 @@ def gpu_decide(cfg: dict, inp: dict, flags: int = 0, repeats: int = 1, noise=Non
         for _ in range(repeats):
             a = ex.decide(nz)
             torch.cuda.synchronize()
+            # PHX_OK only means enqueued: the status word says the decision ran to its end
+            assert ex.status() == 0, "the decision gave up waiting (persistent kernel status)"
             outs.append(a.cpu().numpy().copy())
         del keep
         return outs, ex.kernels_per_decision()

@@ -6,13 +6,15 @@ graph, the large-token plan, the DiT-style step): decide on context A, save a
 capsule, overwrite the context with B and decide, restore the capsule and
 decide again -- bit-identical to the first decision; restore the capsule
 into a second handle of the same plan that never loaded a context (fork) --
-bit-identical again; a handle of another plan rejects the capsule.
+bit-identical again; the first, restored and forked decisions also match the
+oracle's decision on context A; a handle of another plan rejects the capsule.
 """
 import numpy as np
 import pytest
 
+import oracle
 import phx_inputs
-from gpu_util import say, small_cfg
+from gpu_util import TOL_BF16, TOL_TOKENS, assert_close, oracle_decide, say, small_cfg
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +70,15 @@ def test_capsule_restore_and_fork_bit_exact(plan):
         assert not np.array_equal(first, other)
     assert np.array_equal(first, again), "restore must reproduce the decision bit for bit"
     assert np.array_equal(first, forked), "fork must reproduce the decision bit for bit"
+    # the restored and forked decisions are the decision on context A, not only the handle's own first run
+    if plan == "dit":
+        ref = oracle.dit(cfg, a["weights"], a["noise"][0])["out"]
+        assert_close(again[0], ref, TOL_TOKENS, what="dit restored vs oracle")
+        assert_close(forked[0], ref, TOL_TOKENS, what="dit forked vs oracle")
+    else:
+        ref = oracle_decide(cfg, a)
+        assert_close(again, ref, TOL_BF16, what=f"{plan} restored vs oracle on context A")
+        assert_close(forked, ref, TOL_BF16, what=f"{plan} forked vs oracle on context A")
 
 
 def test_capsule_rejects_another_plan():

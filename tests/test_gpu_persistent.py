@@ -44,6 +44,16 @@ def test_prefix_length_edges(L):
     assert_close(outs[0], oracle_decide(cfg, inp), TOL_BF16, what=f"L={L}")
 
 
+@pytest.mark.parametrize("L", [897, 960])
+def test_largest_capacity(L):
+    """Capacity 960 (15 prefix chunks, the most the kernel takes): the fewest
+    workgroups are free of prefix attention, so some also take a QKV role."""
+    cfg = pcfg(layers=2, steps=2, capacity=960, prefix_lens=[L])
+    inp, outs, nk = _run(cfg)
+    assert nk == 2
+    assert_close(outs[0], oracle_decide(cfg, inp), TOL_BF16, what=f"C=960 L={L}")
+
+
 @pytest.mark.parametrize("rows", [1, 7, 16])
 def test_row_counts(rows):
     cfg = pcfg(rows=rows, capacity=320, prefix_lens=[300])

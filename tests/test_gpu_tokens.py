@@ -162,6 +162,15 @@ def test_va_chunk_full_width_one_layer_one_step():
     _va_case(cfg)
 
 
+@pytest.mark.slow
+def test_va_chunk_full_every_layer_one_step():
+    """Every layer of the video-action chunk (8 layers at full width, heads,
+    rows, cache length and capacity) for one Euler step, element by element."""
+    cfg = phx_inputs.workload("va_chunk_bf16", steps=1)
+    cfg["name"] = "va_chunk_8x1"
+    _va_case(cfg)
+
+
 # ------------------------------------------------------------ DiT-style block
 
 def test_dit_small():
@@ -278,6 +287,7 @@ def _history_case(cfg, name, commits=1):
             ref = oracle.decide(cfg, inp["weights"], kk, vv, [k_hist.shape[1]], noise, pos0=[base])["actions"]
             assert_close(out, ref, TOL_BF16, what=f"{name} decision {r} (history {k_hist.shape[1]}, base {base})")
             if r == commits:
+                last_ref = ref
                 break
             ex.commit_chunk(torch.from_numpy(out[0]).cuda())
             got = oracle.commit(cfg, inp["weights"], kk, vv, [k_hist.shape[1]], out, tau_end, pos0=[base])
@@ -297,6 +307,8 @@ def _history_case(cfg, name, commits=1):
     finally:
         ex.close()
     assert np.array_equal(first, again), "a capsule must carry the history and its window position"
+    # the restored decision is the oracle's decision on its own committed history and window base
+    assert_close(again, last_ref, TOL_BF16, what=f"{name} after restore vs oracle")
 
 
 def test_history_commit_grows_the_cache():
