@@ -240,6 +240,9 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="pi05_expert_bf16 on the persistent kernel with its phase timeline on: prints one JSON "
                          "line of per-phase critical-path microseconds instead of the benchmark line")
+    ap.add_argument("--bf16-act", action="store_true",
+                    help="large-token workloads: plain bf16 GEMM activations (PHX_FLAG_BF16_ACT) instead of the "
+                         "plan's default (paired for the DiT-style step and the prefill)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device-to-device copy of 256 MiB (a kernel of known traffic, to scale "
                          "profiler byte counters against)")
@@ -371,7 +374,8 @@ def main():
                    "mlp_hidden": cfg["mlp_hidden"], "batch": cfg["batch"],
                    **({"weights": "int8 codes per output column (layer projections), bf16 in/out projections"}
                       if w8 else {}),
-                   **({"path": "multi-kernel graph"} if mk else {})},
+                   **({"path": "multi-kernel graph"} if mk else {}),
+                   **({"gemm_activations": "QKV, gate/up and down inputs paired bf16 (hi + lo)"} if batch and not mk and not w8 else {})},
         "decisions_per_s": round(1000.0 / ms, 1),
         "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
         **({"requests_per_s": round(1000.0 * cfg["batch"] / ms, 1),
@@ -434,7 +438,7 @@ def measured_gemm_tflops(n: int = 8192, reps: int = 20, warm: int = 5) -> float:
     return 2.0 * n ** 3 / (best_ms * 1e-3) / 1e12
 
 
-PHASES = ("qkv", "attention", "combine", "out_proj", "gate_up", "down", "residual_owners")
+PHASES = ("qkv", "attention", "merge", "out_proj", "out_proj_allreduce", "gate_up", "down", "down_allreduce")
 
 
 def bench_timeline(args):
@@ -476,9 +480,9 @@ def bench_timeline(args):
     median = np.zeros(len(PHASES))
     n = 0
     for k in range(1, S - 1):
-        base = 1 + k * (2 + 7 * NL)
+        base = 1 + k * (2 + len(PHASES) * NL)
         for l in range(2, NL - 2):
-            e = base + 1 + 7 * l
+            e = base + 1 + len(PHASES) * l
             prev = tl[:, e - 1].max()
             for p in range(len(PHASES)):
                 col = tl[:, e + p]
@@ -537,7 +541,9 @@ def bench_tokens(args):
     inp = phx_inputs.make_inputs(cfg, args.seed)
     fl = token_flops(cfg)
     log("bench: creating handle")
-    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    from flow_matching_action_decision_amd import binding
+    tflags = binding.PHX_FLAG_BF16_ACT if args.bf16_act else 0
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"], flags=tflags)
     keep = ex.load_all(inp)
     noise = torch.from_numpy(inp["noise"]).cuda()
     out = torch.empty_like(noise)
@@ -568,12 +574,18 @@ def bench_tokens(args):
     first = [i for i, n in enumerate(nodes) if n["step"] == 0]
     t = ex.time_nodes(first, reps=max(3, min(args.kernel_reps, 10)))
     kinds = {}
+    # matrix-core work of the paired-activation GEMMs (the DiT-style block's default) beyond the algorithmic FLOPs
+    paired = dit and not args.bf16_act
+    paired_extra = 0
     for i, tm in zip(first, t):
         n = nodes[i]
         k = kinds.setdefault(n["name"], dict(kind=n["kind"], launches=0, ms=0.0, flops=0))
         k["launches"] += 1
         k["ms"] += tm
         k["flops"] += node_flops(cfg, n["kind"])
+        if paired and n["kind"] in (binding.PHX_NODE["QKV"], binding.PHX_NODE["GATEUP"],
+                                    binding.PHX_NODE["DOWN_PROJ_RESID"]):
+            paired_extra += node_flops(cfg, n["kind"])
     for nm, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
         tf = k["flops"] / (k["ms"] * 1e-3) / 1e12 if k["flops"] else 0.0
         log(f"  {nm:24s} x{k['launches']:3d}  {k['ms'] * 1e3 / k['launches']:9.1f} us/launch  {tf:7.1f} TFLOP/s")
@@ -631,8 +643,10 @@ def bench_tokens(args):
                    "euler_steps": cfg["steps"], "rows": cfg["rows"],
                    "prefix_len": int(phx_inputs.prefix_lengths(cfg)[0]), "width": cfg["width"],
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} / {cfg['n_kv_heads']} kv",
-                   "mlp_hidden": cfg["mlp_hidden"]},
+                   "mlp_hidden": cfg["mlp_hidden"],
+                   "gemm_activations": "QKV, gate/up and down inputs paired bf16 (hi + lo)" if paired_extra else "bf16"},
         "decisions_per_s": round(1000.0 / ms, 2),
+        "mfma_flops_executed_per_decision": fl["flops_per_decision"] + paired_extra * cfg["steps"],
         "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
         "flops_per_decision": fl["flops_per_decision"], "tflops": round(tflops, 1),
         "mfma_frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -724,7 +738,8 @@ def bench_prefill(args):
     inp = phx_inputs.make_inputs(cfg, args.seed)
     fl = prefill_flops(cfg, n)
     log("bench: creating handle")
-    ex = Expert(cfg, inp["weights"], inp["weights_bits"])
+    from flow_matching_action_decision_amd import binding
+    ex = Expert(cfg, inp["weights"], inp["weights_bits"], flags=binding.PHX_FLAG_BF16_ACT if args.bf16_act else 0)
     x = torch.from_numpy(np.ascontiguousarray(inp["noise"][0])).cuda()
     kvd = cfg["n_kv_heads"] * cfg["head_dim"]
     k = torch.empty((cfg["layers"], n, kvd), dtype=torch.int16, device="cuda")
@@ -794,7 +809,8 @@ def bench_prefill(args):
         "config": {"workload": name, "block": "prefill", "layers": cfg["layers"], "tokens": n,
                    "bucket_rows": cfg["rows"], "width": cfg["width"],
                    "heads": f"{cfg['n_heads']}x{cfg['head_dim']} / {cfg['n_kv_heads']} kv",
-                   "mlp_hidden": cfg["mlp_hidden"], "mask": "causal"},
+                   "mlp_hidden": cfg["mlp_hidden"], "mask": "causal",
+                   "gemm_activations": "bf16" if args.bf16_act else "QKV, gate/up and down inputs paired bf16 (hi + lo)"},
         "prefills_per_s": round(1000.0 / ms, 2),
         "p50_ms": round(float(np.percentile(per, 50)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
         "flops_per_prefill": fl["flops"], "tflops": round(tflops, 1),

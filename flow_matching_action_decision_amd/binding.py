@@ -20,6 +20,8 @@ PHX_FLAG_NO_GRAPH = 1
 PHX_FLAG_MULTI_KERNEL = 2
 PHX_FLAG_TIMELINE = 4
 PHX_FLAG_WEIGHTS_INT8 = 8
+PHX_FLAG_PAIRED_ACT = 16
+PHX_FLAG_BF16_ACT = 32
 PHX_BLOCK_DECODER, PHX_BLOCK_DIT, PHX_BLOCK_PREFILL = 0, 1, 2
 _BLOCKS = dict(decoder=PHX_BLOCK_DECODER, dit=PHX_BLOCK_DIT, prefill=PHX_BLOCK_PREFILL)
 # launch kinds reported by phx_expert_node_info

@@ -5,10 +5,18 @@
 // one request of up to 16 action rows, pi0.5 shape (width 1024, 8 query heads
 // of 256 over one shared key/value head, GeGLU hidden 4096, action dim 32),
 // bf16 weights.  Every workgroup (one per CU) streams its share of the weights
-// into an LDS ring from dedicated loader waves, and its compute waves exchange
-// activations with the other workgroups through tagged 8-byte words in device
-// memory (payload + exchange tag, written and read at device scope), so no
-// kernel boundary or grid barrier separates the steps of the layer.
+// into an LDS ring from dedicated loader waves; its compute waves exchange
+// activations with other workgroups through self-tagged 4-byte words.
+//
+// The 256 workgroups form 8 groups of 32, one per XCD: workgroups go to the
+// XCDs round-robin (XCD (b + o) mod 8, with an offset o that depends on the
+// hardware queue), so each workgroup reads its XCD from the hardware and
+// takes rank b / 8; the host checks the round-robin pattern before it picks
+// this kernel.
+// XCD x computes query head x and its 1/8 share of every projection, so six
+// of the eight exchanges of a layer stay inside the XCD, in its L2; only the
+// two residual updates (out projection, down projection) cross XCDs, as an
+// all-reduce of eight partial sums that every XCD sums in the same order.
 //
 // Every layout the kernel addresses is fixed here at compile time (the shape
 // is fixed), so the kernel carries no table of offsets in registers.
@@ -23,74 +31,83 @@ namespace dec {
 
 // fixed shape of the persistent path
 constexpr int D = 1024;      // residual width
-constexpr int H = 8;         // query heads
+constexpr int H = 8;         // query heads (one per XCD)
 constexpr int DH = 256;      // head dim
 constexpr int HD = H * DH;   // 2048
 constexpr int F = 4096;      // GeGLU hidden
 constexpr int A = 32;        // action dim
 constexpr int NQKV = (H + 2) * DH;  // 2560 QKV outputs (one key/value head)
-constexpr int NTD = D / 16;         // 64 column blocks of the residual stream (owners)
-constexpr int NT_QKV = NQKV / 16;   // 160
 constexpr int KT_D = D / 32;        // 32 k-tiles over D
 constexpr int KT_HD = HD / 32;      // 64
 constexpr int KT_F = F / 32;        // 128
-constexpr int NT_GU = 2 * F / 16;   // 512
-constexpr int NT_OUT = A / 16;      // 2
-constexpr int DN_KQ = 16;           // down projection: K groups of 8 k-tiles
-constexpr int DN_NQ = 16;           // and N groups of 4 n-tiles
 constexpr int CHUNK = 64;           // prefix keys per attention workgroup
-constexpr int MAX_CHUNKS = 16;      // prefix chunks + the action chunk, per head (one merge round)
+constexpr int MAX_CHUNKS = 16;      // prefix chunks + the action chunk (ranks 0..15 of an XCD)
 constexpr int G = 256;              // workgroups (one per CU)
+constexpr int NX = 8;               // XCDs
+constexpr int WX = G / NX;          // workgroups per XCD
+constexpr int FX = F / NX;          // 512 GeGLU features per XCD
 constexpr int RP = 16;              // padded action rows
 constexpr int TILE_BYTES = 1024;    // one 16x32 bf16 MFMA A tile
 constexpr int TILE_ELEMS = TILE_BYTES / 2;
-constexpr int RING = 124;           // LDS ring of weight tiles per workgroup (124 KiB; with the static
-                                    // shared data within the 160 KiB a workgroup may hold; 120 measured
-                                    // 0.6% slower)
+constexpr int RING = 112;           // LDS ring of weight tiles per workgroup (112 KiB; with the static
+                                    // shared data within the 160 KiB a workgroup may hold)
 constexpr int NCOMPUTE = 4;         // compute waves (waves 0..3); waves 4..7 load
 constexpr int NLOADER = 4;
 constexpr int THREADS = 64 * (NCOMPUTE + NLOADER);
-constexpr int N_OWNER = NTD;        // 64 residual column blocks
-constexpr int N_QKV_PAIRS = NT_QKV / 2;  // 80 workgroups with two QKV n-tiles each
+// roles by rank r = b / 8 inside an XCD
+constexpr int R_QKV = 16;           // ranks 16..25: QKV n-tile pairs of the XCD's 20 QKV n-tiles
+constexpr int N_QKV = 10;
+constexpr int R_MERGE = 16;         // ranks 16..23: merge of the head's key chunks, 32 dims each
+constexpr int R_O = 16;             // ranks 16..31: out projection, 4 n-tiles each
+constexpr int R_VEL = 31;           // velocity head and Euler update (each XCD keeps its own copy of x)
 
 __host__ __device__ constexpr unsigned al256(unsigned x) { return (x + 255u) & ~255u; }
 
-// exchange types (tag space and buffers)
+// Exchange buffers.  A word is 4 bytes whose lowest bit is the buffer's
+// generation tag; activations are a (hi, lo) pair of bf16 halves of one
+// value (hi = bf16(a) in the upper 16 bits, lo = bf16(a - hi) in the lower
+// 16 with its last bit replaced by the tag), sums are float32 with the tag in
+// the last mantissa bit.  Buffers marked local exist once per XCD, written
+// with plain stores and read with non-temporal loads (they meet in that XCD's
+// L2); the others are written and read at device scope.
 enum ExType : int {
-  X_HS = 0,   // owner -> QKV / velocity head: bf16(h * (1 + scale)) pairs, [RP][D/2]
-  X_SS = 1,   // owner -> QKV / velocity head: per-block sums of squares, [RP][NTD]
-  X_Q = 2,    // QKV -> attention: q [H][RP][DH/2], then k [RP][DH/2], then v [RP][DH/2] (bf16 pairs)
-  X_ATT = 3,  // attention -> combine: per (head, chunk) unnormalised output [H][CH][RP][DH] f32, then
-              // (max, sum) [H][CH][RP][2]
-  X_O = 4,    // combine -> out projection: attention output pairs [RP][HD/2]
-  X_HS1 = 5,  // owner -> gate/up: bf16(h1 * (1 + scale)) pairs
-  X_SS1 = 6,
-  X_A = 7,    // gate/up -> down: GeGLU output pairs [RP][F/2]
-  X_DP = 8,   // down -> owner: partial sums [DN_KQ][RP][D] f32
-  X_X = 9,    // velocity head -> input projection: bf16 state pairs [RP][A/2]
-  NX = 10
+  X_N = 0,    // local: norm input h * (1 + scale), pairs [RP][D] (attention norm of a layer, or the final norm)
+  X_SS = 1,   // local: sums of squares of h per owner [RP][WX]
+  X_Q = 2,    // local: q of the XCD's head, pairs [RP][DH]
+  X_AO = 3,   // local: per chunk unnormalised attention output [MAX_CHUNKS][RP][DH] f32
+  X_AML = 4,  // local: per chunk (max, sum, max, sum) [MAX_CHUNKS][RP][4] f32
+  X_O = 5,    // local: attention output of the head, pairs [RP][DH]
+  X_N2 = 6,   // local: MLP norm input, pairs [RP][D]
+  X_SS2 = 7,  // local: [RP][WX]
+  X_A = 8,    // local: GeGLU output of the XCD's features, pairs [RP][FX]
+  X_X = 9,    // local: state x [RP][A] f32
+  X_KV = 10,  // device: action keys and values, pairs [RP][2 DH] (k dims 0..255, v dims 256..511)
+  X_OP = 11,  // device: out-projection partial sums per XCD [NX][RP][D] f32
+  X_DP = 12,  // device: down-projection partial sums per XCD [NX][RP][D] f32
+  NXT = 13
 };
-
-// 8-byte words of each exchange buffer
+__host__ __device__ constexpr bool x_local(int t) { return t <= X_X; }
+// words of one copy of each buffer
 __host__ __device__ constexpr unsigned x_words(int t) {
-  return t == X_HS || t == X_HS1 ? RP * (D / 2)
-         : t == X_SS || t == X_SS1 ? RP * NTD
-         : t == X_Q   ? (H + 2) * RP * (DH / 2)
-         : t == X_ATT ? H * MAX_CHUNKS * RP * (DH + 2)
-         : t == X_O   ? RP * (HD / 2)
-         : t == X_A   ? RP * (F / 2)
-         : t == X_DP  ? DN_KQ * RP * D
-                      : RP * (A / 2);
+  return t == X_N || t == X_N2 ? RP * D
+         : t == X_SS || t == X_SS2 ? RP * WX
+         : t == X_Q || t == X_O ? RP * DH
+         : t == X_AO ? MAX_CHUNKS * RP * DH
+         : t == X_AML ? MAX_CHUNKS * RP * 4
+         : t == X_A ? RP * FX
+         : t == X_X ? RP * A
+         : t == X_KV ? RP * 2 * DH
+                     : NX * RP * D;
 }
-// every buffer exists twice, selected by the parity of the step-layer slot
-__host__ __device__ constexpr unsigned x_stride(int t) { return al256(x_words(t) * 8u); }
+// every buffer exists twice (use parity), local ones once per XCD
+__host__ __device__ constexpr unsigned x_stride(int t) { return al256(x_words(t) * 4u); }
+__host__ __device__ constexpr unsigned x_copies(int t) { return x_local(t) ? 2u * NX : 2u; }
 __host__ __device__ constexpr unsigned x_base(int t) {
   unsigned o = 0;
-  for (int i = 0; i < t; ++i) o += 2u * x_stride(i);
+  for (int i = 0; i < t; ++i) o += x_copies(i) * x_stride(i);
   return o;
 }
-constexpr unsigned EX_BYTES = x_base(NX);
-constexpr unsigned X_ML = H * MAX_CHUNKS * RP * DH * 8u;  // (max, sum) part of X_ATT
+constexpr unsigned EX_BYTES = x_base(NXT);
 
 // Auxiliary arena (device memory, bytes, from AUX0 on in the kernel's arena:
 // it follows the exchange words): counters, state, position table, then one
@@ -99,6 +116,7 @@ constexpr unsigned AUX0 = EX_BYTES;
 constexpr unsigned AUX_STATUS = 0;   // u32: decision counter + 1 of the last decision in which a wait gave up
 constexpr unsigned AUX_SEQ = 4;      // u32 decision counter (tag base), advanced after each decision
 constexpr unsigned AUX_LENS = 8;     // i32 prefix length
+constexpr unsigned AUX_FAILED = 12;  // u32: 1 if the last decision gave up (set after each decision)
 constexpr unsigned AUX_X = 256;      // [RP][A] f32: the noise on entry, the actions on exit
 constexpr unsigned AUX_ROPE = AUX_X + RP * A * 4;        // [RP][DH/2] (cos, sin) of the action rows
 constexpr unsigned AUX_TAB = al256(AUX_ROPE + RP * (DH / 2) * 8);
@@ -109,10 +127,11 @@ __host__ __device__ constexpr unsigned st_swout(int NL) { return st_swgu(NL) + (
 __host__ __device__ constexpr unsigned step_bytes(int NL) { return al256(st_swout(NL) + A * 4u); }
 
 // phase timeline: event 0 = start of the compute waves, then per step the
-// input projection, 7 per layer (qkv, attention, combine, out projection,
-// gate/up, down, residual owner) and the velocity head, then the end of the
-// compute waves and the end of loader wave 0
-__host__ __device__ constexpr int timeline_events(int S, int NL) { return 1 + S * (2 + 7 * NL) + 2; }
+// input projection, 8 per layer (qkv, attention, merge, out projection,
+// out-projection all-reduce, gate/up, down, down all-reduce) and the velocity
+// head, then the end of the compute waves and the end of loader wave 0
+constexpr int PHASES_PER_LAYER = 8;
+__host__ __device__ constexpr int timeline_events(int S, int NL) { return 1 + S * (2 + PHASES_PER_LAYER * NL) + 2; }
 __host__ __device__ constexpr unsigned aux_timeline(int S, int NL) { return AUX_TAB + (unsigned)S * step_bytes(NL); }
 __host__ __device__ constexpr unsigned aux_bytes(int S, int NL, bool timeline) {
   return aux_timeline(S, NL) + (timeline ? (unsigned)G * (unsigned)timeline_events(S, NL) * 4u : 0u);
@@ -129,11 +148,6 @@ constexpr unsigned long long W_DN0 = W_GU0 + (unsigned long long)D * 2 * F;
 __host__ __device__ constexpr unsigned long long w_out(int NL) { return W_QKV0 + (unsigned long long)NL * W_LAYER; }
 __host__ __device__ constexpr unsigned long long w_elems(int NL) { return w_out(NL) + (unsigned long long)D * A; }
 
-// exchanges per decision (tag stride per decision)
-__host__ __device__ constexpr unsigned exchanges_per_decision(int S, int NL) {
-  return (unsigned)S * (unsigned)(NL + 1) * NX;
-}
-
 struct Args {
   const void* wt;   // tiled bf16 weights
   const void* kvt;  // attention-tiled prefix K/V: [NL][n_chunks][64 tiles]
@@ -148,6 +162,10 @@ hipError_t launch_decide(const Args& a, hipStream_t s);
 // workgroups of k_decide one compute unit can hold at once (the kernel needs
 // every one of its G workgroups resident together: at least 1 per CU)
 hipError_t decide_occupancy(int* blocks_per_cu);
+// runs a G-workgroup probe once per process and reports whether workgroups
+// went to the XCDs round-robin in index order (XCD (b + o) mod 8 for one
+// offset o): the kernel's ranks inside an XCD rely on it
+hipError_t decide_placement(bool* ok);
 hipError_t launch_decide_advance(void* arena, hipStream_t s);
 // set-up kernels
 // out[k * out_kstride + l * N + n] = sum_d shift(k, norm_stride*l + norm_off)[d] * W_l[d][colmap(n)]

@@ -4,44 +4,59 @@
 // Why persistent.  At 10 action rows every projection streams its weights
 // once per step and does ~10 MACs per weight element, so a decision is bound
 // by HBM bandwidth (6.37 GB per pi0.5 decision) and by the latency of the
-// ~1300 dependent all-to-all exchanges between sublayers.  A graph of ~1100
-// small kernels pays a node gap plus ramp-up and drain at every boundary; the
-// pages remove those gaps with programmatic dependent launch and by folding
-// the "kernels between GEMMs" into GEMM prologues and epilogues ("FlashRT-PAI",
-// sections 3.2-3.3; "PhyAI" section 4.2 Kernel fusion, Graph replay).  Here the
-// same two ideas take a form that fits MI355X:
-//   * Loader waves (4 per workgroup) stream the workgroup's fixed share of
+// dependent exchanges between sublayers.  A graph of ~1100 small kernels pays
+// a node gap plus ramp-up and drain at every boundary; the pages remove those
+// gaps with programmatic dependent launch and by folding the "kernels between
+// GEMMs" into GEMM prologues and epilogues ("FlashRT-PAI", sections 3.2-3.3;
+// "PhyAI" section 4.2 Kernel fusion, Graph replay).  Here the same two ideas
+// take a form that fits MI355X:
+//   * loader waves (4 per workgroup) stream the workgroup's fixed share of
 //     every weight matrix (and of the prefix K/V for attention workgroups)
-//     into a 124-tile LDS ring, running up to a ring ahead of the compute, so
+//     into a 112-tile LDS ring, running up to a ring ahead of the compute, so
 //     the HBM stream never waits for a sublayer boundary;
 //   * compute waves (4 per workgroup) exchange activations with other
-//     workgroups through tagged 8-byte words (payload | exchange tag) written
-//     and read at device scope (sc1), so a consumer detects both readiness and
-//     data with one load and no barrier or atomic counter is needed.
-// Exchange tags grow with a per-handle decision counter, so buffers never
-// need clearing between decisions.
+//     workgroups through self-tagged 4-byte words: a consumer sees data and
+//     readiness in one load, and no barrier or atomic counter is needed.
+//
+// Layout over the chip.  Workgroup b runs on an XCD x it reads from the
+// hardware, as rank r = b / 8 of that XCD's 32.  XCD x owns query head x and a 1/8 share of
+// every projection: the QKV columns of head x plus 1/8 of the key and value
+// columns, the out-projection rows of head x (a partial sum over the whole
+// width), GeGLU features [512 x, 512 x + 512) (gate/up columns, and the same
+// rows of the down projection: again a partial sum).  So the norm input ->
+// QKV -> attention -> merge -> out projection and the MLP norm input ->
+// gate/up -> down exchanges stay inside the XCD, in its L2 (plain stores,
+// non-temporal loads), and only the two partial sums cross XCDs (device
+// scope), where every XCD's 32 owners add the 8 partials of their 32 residual
+// columns in the same order.  The residual stream is therefore replicated, bit-
+// identically, in every XCD.  Every XCD also runs its own copy of the
+// velocity head and keeps its own copy of the state x.
+//
+// Words.  An activation travels as a (hi, lo) pair of bf16 halves of one
+// float (hi = bf16(a), lo = bf16(a - hi)): a GEMM multiplies both halves by
+// the bf16 weights, so it sees the activation to about 2^-16 rather than
+// bf16's 2^-8.  The lowest bit of every word is its buffer's generation: each
+// buffer exists twice (use parity), and the generation flips every second
+// use, so a word written in an earlier use never passes for a fresh one and
+// no buffer is ever cleared.
 //
 // Fusions (the pages' "kernels between GEMMs"): the adaptive RMSNorm is split
-// into the producer's epilogue (bf16(h * (1 + scale)) and per-block sums of
+// into the producer's epilogue (h * (1 + scale) and per-owner sums of
 // squares) and the consumer's epilogue (row factor 1/rms and the shift term,
 // added as the precomputed product shift . W); RoPE, GeGLU, residual adds and
 // the Euler update are epilogues.  Reductions are in a fixed order, so
 // replays are bit-identical.
 //
-// Register discipline: every layout is a compile-time constant (the shape is
-// fixed), a workgroup's roles are a few integer operations on its index, and
-// a wait that gives up ends the wave instead of unwinding through the phases,
-// so the per-phase control flow stays free of spills.
-//
-// Every global access goes through a buffer resource whose range check turns
-// a stray index into a dropped store or a zero load; every wait is bounded by
-// a wall-clock limit and an abort flag, so a missing producer ends the launch
-// with a status instead of a hang.
+// Every global access goes through a buffer resource; every wait is bounded
+// by a wall-clock limit and an abort flag, so a missing producer ends the
+// launch with a status instead of a hang.
 #include "phx_decide.h"
 #include "phx_internal.h"
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <cstdio>
+#include <cstdlib>
 
 namespace phx {
 namespace dec {
@@ -54,11 +69,17 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
-constexpr int SC1 = 16;                             // cache policy: device-coherent access
+constexpr int SC1 = 16;                                  // cache policy: device-coherent access
+constexpr int NTP = 2;                                   // load policy of XCD-local words: non-temporal (they
+                                                         // bypass the CU's own cache and meet the L2 copy)
+constexpr int LST = 0;                                   // store policy of XCD-local words: plain stores reach
+                                                         // the XCD's L2 (non-temporal stores measured 6% slower)
+constexpr unsigned OOB = 0x80000000u;                    // a buffer offset past every range: no access, zeros
 constexpr unsigned TIMEOUT_TICKS = 50u * 1000u * 1000u;  // 0.5 s of the 100 MHz real-time counter
+constexpr float M_EMPTY = -3.0e38f;                      // running max of a key chunk without valid keys
 
 // LDS layout (static part; the ring is dynamic)
-constexpr int RED_BYTES = NCOMPUTE * 4 * 64 * 16;  // per-wave partial tiles (also reused)
+constexpr int RED_BYTES = 20 * 1024;  // per-phase scratch (partial tiles, staged fragments, statistics)
 
 struct Shared {
   unsigned ready[NLOADER];   // tiles of each loader's sub-stream written to the ring
@@ -69,13 +90,12 @@ struct Shared {
   float rrow[RP];            // 1/rms per action row
   float att_m[NCOMPUTE][RP];
   float att_l[NCOMPUTE][RP];
-  s16x4 att_p[NCOMPUTE][64];
+  s16x4 att_p[NCOMPUTE][2][64];  // probability fragments (hi, lo) of each wave's 16 keys
   __attribute__((aligned(16))) unsigned char red[2][RED_BYTES];
 };
 // the ring (dynamic) and the static shared data together stay within the
 // 160 KiB of LDS one workgroup may hold
 static_assert(RING * TILE_BYTES + sizeof(Shared) <= 160 * 1024, "LDS budget of one workgroup");
-
 
 __device__ inline Rsrc rsrc(const void* p, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -91,16 +111,9 @@ __device__ inline unsigned now_ticks() {
 // directly to an element of an ext_vector_type value to element 0.
 __device__ inline float as_f(unsigned u) { return __builtin_bit_cast(float, u); }
 __device__ inline unsigned as_u(float f) { return __builtin_bit_cast(unsigned, f); }
-__device__ inline short as_s(bf16 b) { return __builtin_bit_cast(short, b); }
+__device__ inline unsigned short bits16(bf16 b) { return __builtin_bit_cast(unsigned short, b); }
 
-__device__ inline unsigned pack_bf16(float a, float b) {
-  const unsigned short ua = __builtin_bit_cast(unsigned short, (bf16)a);
-  const unsigned short ub = __builtin_bit_cast(unsigned short, (bf16)b);
-  return (unsigned)ua | ((unsigned)ub << 16);
-}
-
-// Hardware exp2 / reciprocal / reciprocal square root (about 1 ulp); their
-// error is far below the bf16 rounding of every value they feed.
+// Hardware exp2 / reciprocal / reciprocal square root (about 1 ulp).
 __device__ inline float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ inline float frsq(float x) { return __builtin_amdgcn_rsqf(x); }
@@ -120,53 +133,91 @@ __device__ inline f32x4 mma16(const s16x4& a, const s16x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------- words
+
+// (hi, lo) pair word of a with the generation bit in lo's last bit
+__device__ inline unsigned pair_word(float a, unsigned gen) {
+  const bf16 h = (bf16)a;
+  const bf16 l = (bf16)(a - (float)h);
+  return ((unsigned)bits16(h) << 16) | ((unsigned)bits16(l) & 0xfffeu) | gen;
+}
+// float32 word with the generation bit in the last mantissa bit
+__device__ inline unsigned f32_word(float a, unsigned gen) { return (as_u(a) & ~1u) | gen; }
+// bf16 probability pair (hi, lo) for the P . V products
+__device__ inline void split_bf16(float a, short& hi, short& lo) {
+  const bf16 h = (bf16)a;
+  hi = (short)bits16(h);
+  lo = (short)bits16((bf16)(a - (float)h));
+}
+// value of a float32 word: the generation bit is dropped, so the value does
+// not depend on which use of its buffer it travelled in (replays stay
+// bit-identical)
+__device__ inline float wf(unsigned w) { return as_f(w & ~1u); }
+// nonzero if any of the four words of a 16-byte load is not of generation gen
+__device__ inline unsigned stale4(const u32x4& v, unsigned gen) {
+  return ((v[0] ^ gen) | (v[1] ^ gen) | (v[2] ^ gen) | (v[3] ^ gen)) & 1u;
+}
+// B fragments (8 consecutive k values) of the hi and lo halves of 8 pair words
+__device__ inline bf16x8 frag_hi(const u32x4& v0, const u32x4& v1) {
+  const u32x4 r = {__builtin_amdgcn_perm(v0[1], v0[0], 0x07060302u), __builtin_amdgcn_perm(v0[3], v0[2], 0x07060302u),
+                   __builtin_amdgcn_perm(v1[1], v1[0], 0x07060302u), __builtin_amdgcn_perm(v1[3], v1[2], 0x07060302u)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+// (the lo halves with their generation bit dropped)
+__device__ inline bf16x8 frag_lo(const u32x4& v0, const u32x4& v1) {
+  const unsigned m = 0xfffefffeu;
+  const u32x4 r = {__builtin_amdgcn_perm(v0[1], v0[0], 0x05040100u) & m,
+                   __builtin_amdgcn_perm(v0[3], v0[2], 0x05040100u) & m,
+                   __builtin_amdgcn_perm(v1[1], v1[0], 0x05040100u) & m,
+                   __builtin_amdgcn_perm(v1[3], v1[2], 0x05040100u) & m};
+  return __builtin_bit_cast(bf16x8, r);
+}
+// B fragments of 8 float32 values split into (hi, lo) bf16 halves
+__device__ inline void frag_split_f32(const u32x4& v0, const u32x4& v1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = wf(v0[i]), b = wf(v1[i]);
+    hi[i] = (bf16)a;
+    hi[4 + i] = (bf16)b;
+    lo[i] = (bf16)(a - (float)hi[i]);
+    lo[4 + i] = (bf16)(b - (float)hi[4 + i]);
+  }
+}
+
+// The XCD this workgroup runs on.  Workgroups go to the XCDs round-robin in
+// index order, starting from an XCD that depends on the hardware queue, so
+// the workgroups b of one XCD are one residue of b mod 8 and their ranks
+// b / 8 are 0..31 (the host checks the pattern before it picks this kernel).
+__device__ inline int xcc_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return (int)(v & (unsigned)(NX - 1));
+}
+
 // ------------------------------------------------------------- context
 
 struct Ctx {
   Shared* sh;
   unsigned char* ring;
   Rsrc X;                  // arena: exchange words at 0, auxiliary tables at AUX0
-  unsigned tagbase;
   unsigned seq;            // this decision's counter
-  unsigned redsel;         // which half of the partial-tile scratch the current phase uses
+  unsigned redsel;         // which half of the scratch the current phase uses
   unsigned barn;           // compute-wave barriers passed
   unsigned tl;             // timeline on
   int lane, wave, g, row;  // row = lane % 16, g = lane / 16
   int crow;                // row clamped to the last action row (poll addresses)
   int S, NL, R, nc, L;     // steps, layers, action rows, prefix chunks, prefix length
+  int xcd, rk;             // XCD and rank inside it
   float dt, eps;
-  // roles (negative: none)
-  int owner;               // residual column block: input and out projections, residual adds
-  int qkv0;                // first of two QKV n-tiles
-  int attn_h, attn_c;      // attention head and key chunk (attn_c == nc: the action rows' own keys)
-  int comb_h, comb_s;      // combine of head comb_h, dims [32 comb_s, +32)
-  int out_nt;              // velocity-head n-tile
   // ring positions of this workgroup's tile stream
-  unsigned n_in, n_layer, n_step, o_attn, o_o, o_gu, o_dn;
+  unsigned n_layer, n_step, o_att, o_o, o_gu, o_dn;
 };
 
-// Roles of workgroup b.  Attention workgroup (head h, chunk c) is
-// b = c + 32 h, so the eight heads of one key chunk run on one XCD (b mod 8)
-// and share its L2 copy of the chunk; the combiners of head h are
-// b = 32 h + 16 + s.  The workgroups that attend over no prefix chunk take
-// the 64 owner roles and then the 80 QKV pairs, in the order
-// (b mod 32 - chunks) * 8 + b / 32; if they run out, prefix-attention
-// workgroups follow.  Every workgroup takes two gate/up n-tiles and one
-// (K group, N group) of the down projection; the last two take the velocity
-// head.
-__device__ inline void set_roles(Ctx& c, int b) {
-  const int c32 = b & 31, h = b >> 5;
-  const int nc = c.nc;
-  c.attn_h = c32 <= nc ? h : -1;
-  c.attn_c = c32 <= nc ? c32 : -1;
-  c.comb_h = (c32 >= 16 && c32 < 24) ? h : -1;
-  c.comb_s = (c32 >= 16 && c32 < 24) ? c32 - 16 : -1;
-  const int nfree = 8 * (32 - nc);
-  const int idx = c32 >= nc ? (c32 - nc) * 8 + h : nfree + c32 * 8 + h;
-  c.owner = idx < N_OWNER ? idx : -1;
-  c.qkv0 = (idx >= N_OWNER && idx < N_OWNER + N_QKV_PAIRS) ? 2 * (idx - N_OWNER) : -1;
-  c.out_nt = b >= G - NT_OUT ? b - (G - NT_OUT) : -1;
-}
+__device__ inline bool is_qkv(const Ctx& c) { return c.rk >= R_QKV && c.rk < R_QKV + N_QKV; }
+__device__ inline bool is_att(const Ctx& c) { return c.rk <= c.nc; }
+__device__ inline bool is_merge(const Ctx& c) { return c.rk >= R_MERGE && c.rk < R_MERGE + DH / 32; }
+__device__ inline bool is_o(const Ctx& c) { return c.rk >= R_O; }
+__device__ inline bool is_vel(const Ctx& c) { return c.rk == R_VEL; }
 
 // Passes the context's uniform fields through an empty asm statement.  Every
 // phase starts with it, so that what a phase derives from them (role tests,
@@ -174,28 +225,54 @@ __device__ inline void set_roles(Ctx& c, int b) {
 // all of it out of the step loop and keeps it in registers for the whole
 // kernel, far more than the 102 scalar registers a wave has.
 __device__ __attribute__((always_inline)) inline void refresh(Ctx& c) {
-  asm volatile("" : "+s"(c.owner), "+s"(c.qkv0), "+s"(c.attn_h), "+s"(c.attn_c), "+s"(c.comb_h), "+s"(c.comb_s),
-               "+s"(c.out_nt));
-  asm volatile("" : "+s"(c.n_in), "+s"(c.n_layer), "+s"(c.n_step), "+s"(c.o_attn), "+s"(c.o_o), "+s"(c.o_gu),
-               "+s"(c.o_dn));
-  asm volatile("" : "+s"(c.tagbase), "+s"(c.seq), "+s"(c.S), "+s"(c.NL), "+s"(c.R), "+s"(c.nc), "+s"(c.L),
-               "+s"(c.tl));
+  asm volatile("" : "+s"(c.xcd), "+s"(c.rk), "+s"(c.n_layer), "+s"(c.n_step), "+s"(c.o_att), "+s"(c.o_o),
+               "+s"(c.o_gu), "+s"(c.o_dn));
+  asm volatile("" : "+s"(c.seq), "+s"(c.S), "+s"(c.NL), "+s"(c.R), "+s"(c.nc), "+s"(c.L), "+s"(c.tl));
   asm volatile("" : "+v"(c.lane), "+v"(c.crow));
   c.g = c.lane >> 4;
   c.row = c.lane & 15;
 }
 
-__device__ inline unsigned slot_of(const Ctx& c, int k, int l) { return (unsigned)(k * (c.NL + 1) + l); }
-__device__ inline unsigned tag_of(const Ctx& c, unsigned slot, int t) {
-  return c.tagbase + slot * (unsigned)NX + (unsigned)t + 1u;
+// Use counters.  A buffer type used once per layer-step, once per norm input
+// (NL + 1 per step) or once between steps counts its uses without a gap from
+// one decision to the next (every use writes every word its readers read): use u = seq * n + i (n uses per decision, seq the
+// decision counter) goes to copy u & 1 and carries generation
+// ((u >> 1) + 1) & 1, so two successive uses of a copy always differ in
+// generation.  The counter starts at 0 on zeroed memory (the first use of
+// each copy expects 1), advances by one after every decision, and goes back
+// to 0 when the words are cleared after a decision that gave up.  The
+// counters wrap at 2^32, a multiple of 4, without a break in the pattern.
+struct Use {
+  unsigned par, gen;
+};
+__device__ inline Use use_of(unsigned u) { return Use{u & 1u, ((u >> 1) + 1u) & 1u}; }
+__device__ inline Use use_layer(const Ctx& c, int k, int l) {
+  return use_of(c.seq * (unsigned)(c.S * c.NL) + (unsigned)(k * c.NL + l));
+}
+__device__ inline Use use_norm(const Ctx& c, int k, int l) {
+  return use_of(c.seq * (unsigned)(c.S * (c.NL + 1)) + (unsigned)(k * (c.NL + 1) + l));
+}
+// the state goes from the velocity head to the input projection S - 1 times
+// per decision (the last step writes the actions instead)
+__device__ inline Use use_state(const Ctx& c, int k) { return use_of(c.seq * (unsigned)(c.S - 1) + (unsigned)k); }
+
+// byte offset of buffer T's copy (use parity, this XCD for local buffers)
+template <int T>
+__device__ __attribute__((always_inline)) inline unsigned xb(const Ctx& c, unsigned par) {
+  constexpr unsigned b = x_base(T), st = x_stride(T);
+  if constexpr (x_local(T))
+    return b + (par * NX + (unsigned)c.xcd) * st;
+  else
+    return b + par * st;
 }
 template <int T>
-__device__ __attribute__((always_inline)) inline unsigned xoff(unsigned slot) {
-  constexpr unsigned b = x_base(T), st = x_stride(T);
-  return b + ((slot & 1u) ? st : 0u);
+constexpr int pol_of() {
+  return x_local(T) ? NTP : SC1;
 }
 // byte offset of step k's table block in the arena
-__device__ inline unsigned step_tab(const Ctx& c, int k) { return AUX0 + AUX_TAB + (unsigned)k * step_bytes(c.NL); }
+__device__ inline unsigned step_tab(const Ctx& c, int k) {
+  return AUX0 + AUX_TAB + (unsigned)k * step_bytes(c.NL);
+}
 
 __device__ inline void lds_store(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -222,15 +299,17 @@ __device__ __attribute__((always_inline)) inline void end_wave() { asm volatile(
 
 // Raises the workgroup's abort flag (its other waves leave at their next
 // wait), optionally records the failure in the status word (the decision
-// counter + 1, so no clearing is needed), has the velocity-head workgroups
-// mark their actions NaN, and ends the wave.
+// counter + 1, so no clearing is needed), has the velocity workgroup of XCD 0
+// mark the actions NaN, and ends the wave.
 __device__ __attribute__((always_inline)) inline void leave(Ctx& c, bool record) {
   lds_store(&c.sh->abort, 1u);
   if (record && c.lane == 0) __builtin_amdgcn_raw_buffer_store_b32(c.seq + 1u, c.X, AUX0 + AUX_STATUS, 0, SC1);
-  if (c.out_nt >= 0 && c.wave == 0 && c.row < c.R) {
+  if (is_vel(c) && c.xcd == 0 && c.wave == 0 && c.row < c.R) {
     const unsigned nanv = 0x7fc00000u;
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{nanv, nanv, nanv, nanv}, c.X,
-                                           AUX0 + AUX_X + (unsigned)((c.row * A + 16 * c.out_nt + 4 * c.g) * 4), 0, 0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{nanv, nanv, nanv, nanv}, c.X,
+                                             AUX0 + AUX_X + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4), 0, 0);
   }
   end_wave();
 }
@@ -256,10 +335,7 @@ __device__ inline void cw_barrier(Ctx& c) {
   const unsigned target = c.barn * NCOMPUTE;
   const unsigned t0 = now_ticks();
   unsigned spins = 0;
-  while (lds_load(&c.sh->cwbar) < target) {
-    __builtin_amdgcn_s_sleep(1);
-    keep_waiting(c, t0, spins);
-  }
+  while (lds_load(&c.sh->cwbar) < target) keep_waiting(c, t0, spins);
   cbar();
 }
 
@@ -285,19 +361,20 @@ __device__ inline void release_ring(Ctx& c, unsigned upto) {
   if (c.wave == 0 && c.lane == 0) lds_store(&c.sh->consumed, upto);
 }
 
-// Scratch for cross-wave partial tiles.  Consecutive phases that use it take
-// alternate halves, so a wave that runs ahead into the next phase never
-// overwrites partials a reducer wave is still reading.
-__device__ inline f32x4* red_take(Ctx& c) {
-  f32x4* r = (f32x4*)c.sh->red[c.redsel & 1u];
+// Scratch for one phase.  Consecutive phases take alternate halves, so a wave
+// that runs ahead into the next phase never overwrites what a slower wave of
+// this phase still reads.
+__device__ inline unsigned char* red_take(Ctx& c) {
+  unsigned char* r = c.sh->red[c.redsel & 1u];
   c.redsel += 1u;
   return r;
 }
-__device__ inline f32x4 red_sum(const f32x4* red, int t, int lane) {
-  f32x4 s = red[(0 * 4 + t) * 64 + lane];
-  s += red[(1 * 4 + t) * 64 + lane];
-  s += red[(2 * 4 + t) * 64 + lane];
-  s += red[(3 * 4 + t) * 64 + lane];
+// sum of the four waves' partial tiles t (in wave order)
+__device__ inline f32x4 red_sum(const f32x4* red, int nt, int t, int lane) {
+  f32x4 s = red[(0 * nt + t) * 64 + lane];
+  s += red[(1 * nt + t) * 64 + lane];
+  s += red[(2 * nt + t) * 64 + lane];
+  s += red[(3 * nt + t) * 64 + lane];
   return s;
 }
 
@@ -306,149 +383,87 @@ __device__ inline bf16x8 ring_tile(const Ctx& c, unsigned pos) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// ------------------------------------------------------- tagged exchange
+// acc[t] = sum over k-tiles kk of W(t, kk) . (hi + lo)(kk), the activation
+// pairs of k-tile kk in loads v[2 kk], v[2 kk + 1] and the weight tile at
+// ring position pos(t, kk).  The hi and lo products go to accumulators of
+// their own and the n-tiles are the inner loop, so no MFMA waits for the
+// result of the one before it (2 NT independent chains); the two halves are
+// added at the end.
+template <int NT, int KK, typename PF>
+__device__ __attribute__((always_inline)) inline void gemm_pairs(const Ctx& c, PF pos, const u32x4* v,
+                                                                 f32x4 (&acc)[NT]) {
+  f32x4 ah[NT], al[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ah[t] = al[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 bh = frag_hi(v[2 * kk], v[2 * kk + 1]);
+    const bf16x8 bl = frag_lo(v[2 * kk], v[2 * kk + 1]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bf16x8 w = ring_tile(c, pos(t, kk));
+      ah[t] = mma32(w, bh, ah[t]);
+      al[t] = mma32(w, bl, al[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = ah[t] + al[t];
+}
 
-// Where load i of a poll reads: byte offset `vo` (per lane) + `so` (uniform)
-// in the arena; `need` (uniform) == false skips the load.  Lanes of action
-// rows past R read the last valid row instead (clamped rows), so every lane's
-// words become valid and no per-lane predicate is needed; the memory system
-// merges the duplicate addresses of a wave, and no result of a padded row is
-// ever stored.
+// ------------------------------------------------------------- exchange
+
+// Where load i of a poll reads: per-lane byte offset vo and uniform so in the
+// arena.  Rows past R read the last valid row instead (clamped rows), so
+// every lane's words become valid; the memory system merges the duplicate
+// addresses of a wave, and no result of a padded row is ever stored.
 struct LA {
   unsigned vo, so;
-  bool need;
-};
-// bases of a poll's addresses: per-lane v0, v1 and uniform s0, s1, s2
-struct PB {
-  unsigned v0, v1, s0, s1, s2;
 };
 
-// Polls N 16-byte loads (two tagged words each) until every needed word
-// carries `tag`; addr(b, i) gives load i from the bases b.  A round issues
-// every needed load.  While some are stale, the wave probes with a single
-// load instruction in which lane i reads one stale word of load i (the
-// first stale lane's), until every probed word is fresh, and then starts
-// the next round; so a round moves the whole block only when each of its
-// loads has made progress, and waiting waves read a few cache lines per
-// probe instead of the whole block.  The bases pass through an empty asm
-// statement in every round, so that the compiler computes each address next
-// to its load instead of keeping N addresses live in registers.
-template <int N, typename AF>
-__device__ __attribute__((always_inline)) inline void ll_poll(Ctx& c, const PB& pb, AF addr, unsigned tag,
-                                                              u32x4 (&v)[N]) {
+// Polls N 16-byte loads until every word carries generation gen.  The first
+// round issues every load; each later round issues them again, but a lane
+// whose words of load i are already fresh points load i past the buffer's
+// range (no memory access), so a round moves only what is still stale.
+// Every load of a round is in flight before the first is checked, and no
+// branch separates them.
+template <int POL, int N, typename AF>
+__device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, u32x4 (&v)[N]) {
   const unsigned t0 = now_ticks();
   unsigned spins = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const LA la = addr(i);
+    v[i] = __builtin_amdgcn_raw_buffer_load_b128(c.X, la.vo, __builtin_amdgcn_readfirstlane(la.so), POL);
+  }
   while (true) {
-    PB b = pb;
-    asm volatile("" : "+v"(b.v0), "+v"(b.v1), "+s"(b.s0), "+s"(b.s1), "+s"(b.s2));
+    unsigned stale = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) stale |= stale4(v[i], gen) << i;
+    if (__ballot(stale != 0u) == 0ull) return;
+    keep_waiting(c, t0, spins);
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const LA la = addr(b, i);
-      v[i] = la.need ? __builtin_amdgcn_raw_buffer_load_b128(c.X, la.vo, __builtin_amdgcn_readfirstlane(la.so), SC1)
-                     : u32x4{0u, tag, 0u, tag};
-    }
-    unsigned acc = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) acc |= (v[i][1] ^ tag) | (v[i][3] ^ tag);
-    if (__ballot(acc != 0u) == 0ull) return;
-    // probe addresses: lane i takes load i's first stale word; lanes without
-    // a stale load repeat the highest stale load's probe
-    unsigned pa = 0;
-    bool any = false;
-#pragma unroll
-    for (int i = N - 1; i >= 0; --i) {
-      const unsigned long long m = __ballot(((v[i][1] ^ tag) | (v[i][3] ^ tag)) != 0u);
-      if (m != 0ull) {
-        const LA la = addr(b, i);
-        const unsigned a = __builtin_amdgcn_readfirstlane(la.so) + (unsigned)__shfl((int)la.vo, __builtin_ctzll(m));
-        pa = (c.lane == i || !any) ? a : pa;
-        any = true;
-      }
-    }
-    while (true) {
-      const u32x4 p = __builtin_amdgcn_raw_buffer_load_b128(c.X, pa, 0, SC1);
-      if (__ballot((p[1] != tag) || (p[3] != tag)) == 0ull) break;
-      keep_waiting(c, t0, spins);
+      const LA la = addr(i);
+      const bool st = (stale >> i) & 1u;
+      const u32x4 n =
+          __builtin_amdgcn_raw_buffer_load_b128(c.X, st ? la.vo : OOB, __builtin_amdgcn_readfirstlane(la.so), POL);
+      v[i] = st ? n : v[i];
     }
   }
 }
 
-// B fragments of a pair-word activation buffer: fragment f = loads 2f, 2f+1
-// (16 bytes apart) at base + f * fstride
-__device__ inline LA frag_la(unsigned vo, unsigned s0, unsigned fstride, int i) {
-  return LA{vo + (unsigned)(i >> 1) * fstride + (unsigned)(i & 1) * 16u, s0, true};
+template <int POL>
+__device__ inline void st4(const Ctx& c, unsigned off, const u32x4& w) {
+  __builtin_amdgcn_raw_buffer_store_b128(w, c.X, off, 0, POL);
 }
-
-__device__ inline void ll_store2(Ctx& c, unsigned off, unsigned p0, unsigned p1, unsigned tag) {
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4{p0, tag, p1, tag}, c.X, off, 0, SC1);
+template <int POL>
+__device__ inline void st2(const Ctx& c, unsigned off, const u32x2& w) {
+  __builtin_amdgcn_raw_buffer_store_b64(w, c.X, off, 0, POL);
 }
-__device__ inline void ll_store1(Ctx& c, unsigned off, unsigned p0, unsigned tag) {
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{p0, tag}, c.X, off, 0, SC1);
-}
-
-__device__ inline bf16x8 frag_of(const u32x4& v0, const u32x4& v1) {
-  return __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[2], v1[0], v1[2]});
-}
-
-// Sums of squares: the owners' per-block partials [RP][NTD] are read as 8
-// loads per lane (lane: row lane / 4, owners 16 (lane % 4) + [0, 16)).
-__device__ inline unsigned ss_vo(const Ctx& c) {
-  const int row = c.lane >> 2, part = c.lane & 3;
-  const int crow = row < c.R ? row : c.R - 1;
-  return ((unsigned)crow * NTD + (unsigned)(part * 16)) * 8u;
-}
-// 1/rms per row from those 8 loads, into LDS rrow
-__device__ inline void ss_finish(Ctx& c, const u32x4* v) {
-  const int row = c.lane >> 2, part = c.lane & 3;
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s += as_f(v[i][0]) + as_f(v[i][2]);
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  if (part == 0) c.sh->rrow[row] = frsq(s / (float)D + c.eps);
-}
-
-// Polls a normalised activation (16 rows x D as bf16 pairs, this wave's 8
-// k-tiles: loads 0..15) plus, on wave 0, the owners' sums of squares (loads
-// 16..23), and leaves 1/rms per row in LDS.
-template <int t_hs, int t_ss>
-__device__ inline void poll_normed(Ctx& c, unsigned slot, u32x4 (&v)[24]) {
-  const bool w0 = c.wave == 0;
-  const PB pb{((unsigned)c.crow * (D / 2) + 4u * (unsigned)c.g) * 8u, ss_vo(c),
-              xoff<t_hs>(slot) + (unsigned)(8 * c.wave) * 128u, xoff<t_ss>(slot), 0u};
-  auto addr = [&](const PB& b, int i) -> LA {
-    if (i < 16) return frag_la(b.v0, b.s0, 128u, i);
-    return LA{b.v1 + (unsigned)(i - 16) * 16u, b.s1, w0};
-  };
-  ll_poll<24>(c, pb, addr, tag_of(c, slot, t_hs), v);
-  if (w0) ss_finish(c, v + 16);
-}
-
-// ---------------------------------------------------------------- owner
-
-// (1 + scale) of the owner's four columns for one norm (issue early; use after)
-__device__ inline u32x4 owner_scale_load(const Ctx& c, int k, int norm) {
-  const unsigned off = step_tab(c, k) + (unsigned)((norm * D + 16 * c.owner + 4 * c.g) * 4);
-  return __builtin_amdgcn_raw_buffer_load_b128(c.X, off, 0, 0);
-}
-
-// h (wave 0, lane: cols 16*owner + 4g + i, row) -> bf16(h * (1 + scale)) pairs
-// and per-row sums of squares of this column block, both under the tag of t_hs
-template <int t_hs, int t_ss>
-__device__ inline void owner_publish(Ctx& c, const f32x4& h, const u32x4& sv, unsigned slot) {
-  const int j = c.owner;
-  const unsigned tag = tag_of(c, slot, t_hs);
-  float y[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) y[i] = h[i] * (1.0f + as_f(sv[i]));
-  float s = h[0] * h[0] + h[1] * h[1] + h[2] * h[2] + h[3] * h[3];
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
-  if (c.row < c.R) {
-    ll_store2(c, xoff<t_hs>(slot) + ((unsigned)c.row * (D / 2) + (unsigned)(8 * j + 2 * c.g)) * 8u,
-              pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), tag);
-    if (c.g == 0) ll_store1(c, xoff<t_ss>(slot) + ((unsigned)c.row * NTD + (unsigned)j) * 8u, as_u(s), tag);
-  }
+template <int POL>
+__device__ inline void st1(const Ctx& c, unsigned off, unsigned w) {
+  __builtin_amdgcn_raw_buffer_store_b32(w, c.X, off, 0, POL);
 }
 
 // phase timeline (off unless the handle asked for it)
@@ -459,78 +474,134 @@ __device__ inline void tl_mark(const Ctx& c, int ev) {
   }
 }
 
+// ---------------------------------------------------------------- owners
+// Every workgroup owns residual columns [32 r, 32 r + 32) (its rank's two
+// n-tiles) and keeps them in wave 0's registers: lane l holds row l % 16,
+// columns 32 r + 16 t + 4 g + [0, 4) in h[t].  The owners of the eight XCDs
+// hold the same columns and add the same partial sums in the same order.
+
+// (1 + scale) of the owner's columns for one norm (issue early; use after)
+__device__ inline u32x4 owner_scale_load(const Ctx& c, int k, int norm, int t) {
+  const unsigned off = step_tab(c, k) + (unsigned)((norm * D + 32 * c.rk + 16 * t + 4 * c.g) * 4);
+  return __builtin_amdgcn_raw_buffer_load_b128(c.X, off, 0, 0);
+}
+
+// publishes h * (1 + scale) as pair words and the per-row sums of squares of
+// the owner's 32 columns (wave 0)
+template <int T_N, int T_SS>
+__device__ inline void owner_publish(Ctx& c, const f32x4 (&h)[2], const u32x4 (&sv)[2], const Use& u) {
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = pair_word(h[t][i] * (1.0f + as_f(sv[t][i])), u.gen);
+      s += h[t][i] * h[t][i];
+    }
+    if (c.row < c.R)
+      st4<LST>(c, xb<T_N>(c, u.par) + (unsigned)((c.row * D + 32 * c.rk + 16 * t + 4 * c.g) * 4), w);
+  }
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  if (c.row < c.R && c.g == 0) st1<LST>(c, xb<T_SS>(c, u.par) + (unsigned)((c.row * WX + c.rk) * 4), f32_word(s, u.gen));
+}
+
+// Poll of a normalised activation (pairs [RP][D]) for this wave's 8 k-tiles
+// (loads 0..15: k-tile 8 w + j at loads 2 j, 2 j + 1) plus the owners' sums
+// of squares (loads 16, 17: lane row lane / 4, owners 8 (lane % 4) + [0, 8)).
+template <int T_N, int T_SS>
+__device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const Use& u, u32x4 (&v)[18]) {
+  const unsigned vn = (unsigned)((c.crow * D + 256 * c.wave + 8 * c.g) * 4);
+  const int srow = c.lane >> 2;
+  const int scrow = srow < c.R ? srow : c.R - 1;
+  const unsigned vs = (unsigned)((scrow * WX + 8 * (c.lane & 3)) * 4);
+  const unsigned bn = xb<T_N>(c, u.par), bs = xb<T_SS>(c, u.par);
+  poll<NTP>(c, [&](int i) -> LA {
+    if (i < 16) return LA{vn + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bn};
+    return LA{vs + (unsigned)((i - 16) * 16), bs};
+  }, u.gen, v);
+  if (c.wave == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 16; i < 18; ++i) s += (wf(v[i][0]) + wf(v[i][1])) + (wf(v[i][2]) + wf(v[i][3]));
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if ((c.lane & 3) == 0) c.sh->rrow[srow] = frsq(s / (float)D + c.eps);
+  }
+}
+
 // ------------------------------------------------------------- phases
 // Every phase is entered by all four compute waves; barrier counts match.
 // Each phase issues all the loads it needs (tables first, then the exchange
 // words) before waiting on any of them.
 
-// input projection h = x . W_in for the owner's column block (one k-tile)
-__device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, f32x4& hreg) {
+// input projection h = x . W_in for the owner's two n-tiles (wave 0)
+__device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, f32x4 (&h)[2]) {
   refresh(c);
-  if (c.owner < 0 || c.wave != 0) return;
+  if (c.wave != 0) return;
   const unsigned p0 = (unsigned)k * c.n_step;
-  const u32x4 sv = owner_scale_load(c, k, 0);
-  bf16x8 b;
+  u32x4 sv[2];
+  sv[0] = owner_scale_load(c, k, 0, 0);
+  sv[1] = owner_scale_load(c, k, 0, 1);
+  u32x4 v[2];
+  const unsigned vo = (unsigned)((c.crow * A + 8 * c.g) * 4);
   if (k == 0) {
-    const bool ok = c.row < c.R;
-    const unsigned off = AUX0 + AUX_X + ((unsigned)c.row * A + 8u * (unsigned)c.g) * 4u;
-    const u32x4 v0 = ok ? __builtin_amdgcn_raw_buffer_load_b128(c.X, off, 0, 0) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 v1 = ok ? __builtin_amdgcn_raw_buffer_load_b128(c.X, off + 16u, 0, 0) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      b[i] = (bf16)as_f(v0[i]);
-      b[4 + i] = (bf16)as_f(v1[i]);
-    }
+    v[0] = __builtin_amdgcn_raw_buffer_load_b128(c.X, AUX0 + AUX_X + vo, 0, 0);
+    v[1] = __builtin_amdgcn_raw_buffer_load_b128(c.X, AUX0 + AUX_X + vo + 16u, 0, 0);
   } else {
-    u32x4 v[2];
-    const unsigned slot = slot_of(c, k - 1, c.NL);
-    const PB pb{((unsigned)c.crow * (A / 2) + 4u * (unsigned)c.g) * 8u, 0u, xoff<X_X>(slot), 0u, 0u};
-    ll_poll<2>(c, pb, [](const PB& b, int i) { return frag_la(b.v0, b.s0, 0u, i); }, tag_of(c, slot, X_X), v);
-    b = frag_of(v[0], v[1]);
+    const Use ux = use_state(c, k - 1);
+    const unsigned bx = xb<X_X>(c, ux.par);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vo + 16u * (unsigned)i, bx}; }, ux.gen, v);
   }
-  wait_tiles(c, p0, 1);
-  hreg = mma32(ring_tile(c, p0), b, f32x4{0.f, 0.f, 0.f, 0.f});
-  release_ring(c, p0 + 1);
-  owner_publish<X_HS, X_SS>(c, hreg, sv, slot_of(c, k, 0));
+  bf16x8 xh, xl;
+  frag_split_f32(v[0], v[1], xh, xl);
+  wait_tiles(c, p0, 2);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    h[t] = mma32(ring_tile(c, p0 + t), xh, f32x4{0.f, 0.f, 0.f, 0.f});
+    h[t] = mma32(ring_tile(c, p0 + t), xl, h[t]);
+  }
+  release_ring(c, p0 + 2);
+  owner_publish<X_N, X_SS>(c, h, sv, use_norm(c, k, 0));
 }
 
-// QKV projection of two n-tiles, K = D split over the four waves; epilogue
-// 1/rms, shift . W, RoPE; writes q (per head), k and v of the action rows
+// QKV projection of two n-tiles (K = D split over the four waves), epilogue
+// 1/rms, shift . W and RoPE; writes q of the XCD's head (local) or the
+// XCD's share of the action keys and values (device scope)
 __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int l) {
   refresh(c);
-  if (c.qkv0 < 0) return;
-  const unsigned slot = slot_of(c, k, l);
-  const unsigned p0 = (unsigned)k * c.n_step + c.n_in + (unsigned)l * c.n_layer;
-  // epilogue tables of this wave's n-tile (waves 0 and 1 reduce n-tiles 0 and 1)
-  const int nt = c.qkv0 + (c.wave & 1);
-  const int tt = nt % 16, hh = nt / 16;
+  if (!is_qkv(c)) return;
+  const int i = c.rk - R_QKV;
+  // this workgroup's first QKV n-tile: query head xcd (tiles 2i, 2i + 1), or the
+  // key head's / value head's tiles 2 xcd, 2 xcd + 1
+  const int nt0 = i < 8 ? 16 * c.xcd + 2 * i : (i == 8 ? 16 * H + 2 * c.xcd : 16 * (H + 1) + 2 * c.xcd);
+  const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer;
+  const Use u = use_norm(c, k, l);
+  const Use uo = use_layer(c, k, l);
+  const int nt = nt0 + (c.wave & 1);  // epilogue tables of the n-tile this wave finishes (waves 0, 1)
+  const int tt = nt % 16;
   const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
       c.X, step_tab(c, k) + st_swqkv(c.NL) + (unsigned)((l * NQKV + nt * 16 + 4 * c.g) * 4), 0, 0);
   const u32x4 cs = __builtin_amdgcn_raw_buffer_load_b128(
       c.X, AUX0 + AUX_ROPE + (unsigned)((c.row * (DH / 2) + 8 * tt + 2 * c.g) * 8), 0, 0);
-  u32x4 v[24];
-  poll_normed<X_HS, X_SS>(c, slot, v);
+  u32x4 v[18];
+  poll_normed<X_N, X_SS>(c, u, v);
   wait_tiles(c, p0, 64);
   f32x4 acc[2];
+  gemm_pairs<2, 8>(c, [&](int t, int kk) { return p0 + 32u * t + 8u * c.wave + kk; }, v, acc);
+  f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      acc[t] = mma32(ring_tile(c, p0 + 32u * t + 8u * c.wave + kk), frag_of(v[2 * kk], v[2 * kk + 1]), acc[t]);
-  }
-  f32x4* red = red_take(c);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) red[(c.wave * 4 + t) * 64 + c.lane] = acc[t];
+  for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
   release_ring(c, p0 + 64u);
   if (c.wave < 2) {
-    const f32x4 s = red_sum(red, c.wave, c.lane);
+    const f32x4 s = red_sum(red, 2, c.wave, c.lane);
     const float rr = c.sh->rrow[c.row];
     float y[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = rr * s[i] + as_f(sw[i]);
-    if (hh <= H) {  // q heads and the key head are rotated
+    for (int e = 0; e < 4; ++e) y[e] = rr * s[e] + as_f(sw[e]);
+    if (i < 9) {  // query and key columns are rotated
       const float c0 = as_f(cs[0]), s0 = as_f(cs[1]);
       const float c1 = as_f(cs[2]), s1 = as_f(cs[3]);
       const float x0 = y[0], x1 = y[1], x2 = y[2], x3 = y[3];
@@ -540,65 +611,90 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
       y[3] = x3 * c1 + x1 * s1;
     }
     if (c.row < c.R) {
-      const unsigned tag = tag_of(c, slot, X_Q);
-      const unsigned hb = xoff<X_Q>(slot) + ((unsigned)(hh * RP + c.row) * (DH / 2)) * 8u;
-      ll_store1(c, hb + (unsigned)(4 * tt + c.g) * 8u, pack_bf16(y[0], y[1]), tag);
-      ll_store1(c, hb + (unsigned)(64 + 4 * tt + c.g) * 8u, pack_bf16(y[2], y[3]), tag);
+      // the lane's four columns are head dims j, j + 1, j + 128, j + 129
+      const int j = 8 * tt + 2 * c.g;
+      const u32x2 w01 = {pair_word(y[0], uo.gen), pair_word(y[1], uo.gen)};
+      const u32x2 w23 = {pair_word(y[2], uo.gen), pair_word(y[3], uo.gen)};
+      if (i < 8) {
+        const unsigned o = xb<X_Q>(c, uo.par) + (unsigned)((c.row * DH + j) * 4);
+        st2<LST>(c, o, w01);
+        st2<LST>(c, o + (DH / 2) * 4u, w23);
+      } else {
+        const unsigned o = xb<X_KV>(c, uo.par) + (unsigned)((c.row * 2 * DH + (i - 8) * DH + j) * 4);
+        st2<SC1>(c, o, w01);
+        st2<SC1>(c, o + (DH / 2) * 4u, w23);
+      }
     }
   }
 }
 
-// outputs of one (head, chunk): unnormalised O [row][dim] and (max, sum) per row
-__device__ inline void attn_publish(Ctx& c, unsigned slot, const f32x4 (&oacc)[4], float m_row, float l_row) {
-  const unsigned tag = tag_of(c, slot, X_ATT);
-  const unsigned ob = xoff<X_ATT>(slot);
-  const unsigned hc = (unsigned)(c.attn_h * MAX_CHUNKS + c.attn_c);
+// outputs of one key chunk of the head: unnormalised O [row][dim] (f32 words)
+// and (max, sum) per row
+__device__ inline void attn_publish(Ctx& c, int chunk, const Use& u, const f32x4 (&oacc)[4], float m_row,
+                                    float l_row) {
+  const unsigned ob = xb<X_AO>(c, u.par);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const int dim = 16 * (4 * c.wave + d) + c.row;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rw = 4 * c.g + i;
-      if (rw < c.R) ll_store1(c, ob + ((hc * RP + (unsigned)rw) * DH + (unsigned)dim) * 8u, as_u(oacc[d][i]), tag);
+    for (int e = 0; e < 4; ++e) {
+      const int rw = 4 * c.g + e;
+      if (rw < c.R) st1<LST>(c, ob + (unsigned)(((chunk * RP + rw) * DH + dim) * 4), f32_word(oacc[d][e], u.gen));
     }
   }
-  if (c.wave == 0 && c.g == 0 && c.row < c.R)
-    ll_store2(c, ob + X_ML + ((hc * RP + (unsigned)c.row) * 2u) * 8u, as_u(m_row), as_u(l_row), tag);
+  if (c.wave == 0 && c.g == 0 && c.row < c.R) {
+    const float m = m_row == -INFINITY ? M_EMPTY : m_row;
+    const unsigned wm = f32_word(m, u.gen), wl = f32_word(l_row, u.gen);
+    st4<LST>(c, xb<X_AML>(c, u.par) + (unsigned)((chunk * RP + c.row) * 16), u32x4{wm, wl, wm, wl});
+  }
 }
 
-// attention of head h over one prefix key chunk [64 c, 64 c + 64) from the ring
+// attention of head xcd over prefix key chunk [64 ch, 64 ch + 64) from the ring
 __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int k, int l) {
   refresh(c);
-  const unsigned slot = slot_of(c, k, l);
+  const int ch = c.rk;
+  const Use u = use_layer(c, k, l);
   const float scale = 0.0625f;  // 1/sqrt(256)
-  const unsigned vo = ((unsigned)c.crow * (DH / 2) + 4u * (unsigned)c.g) * 8u;
-  // q of this head as 8 B fragments (dims 32 s + 8 g + [0, 8)): wave w polls
-  // fragments 2w, 2w + 1 and the four waves share them through LDS
-  bf16x8 qf[8];
+  // q fragments (dims 32 s + 8 g + [0, 8), hi and lo): wave w polls slices 2w, 2w + 1
+  // and the four waves share them through LDS
+  bf16x8 qh[8], ql[8];
   {
     u32x4 v[4];
-    const PB pb{vo, 0u, xoff<X_Q>(slot) + (unsigned)(c.attn_h * RP) * (DH / 2) * 8u + 256u * (unsigned)c.wave, 0u, 0u};
-    ll_poll<4>(c, pb, [](const PB& b, int i) { return frag_la(b.v0, b.s0, 128u, i); }, tag_of(c, slot, X_Q), v);
-    u32x4* qs = (u32x4*)red_take(c);  // [8 fragments][64 lanes]
-    qs[(2 * c.wave) * 64 + c.lane] = __builtin_bit_cast(u32x4, frag_of(v[0], v[1]));
-    qs[(2 * c.wave + 1) * 64 + c.lane] = __builtin_bit_cast(u32x4, frag_of(v[2], v[3]));
+    const unsigned vo = (unsigned)((c.crow * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned bq = xb<X_Q>(c, u.par);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, v);
+    u32x4* qs = (u32x4*)red_take(c);  // [8 slices][hi, lo][64 lanes]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int s = 2 * c.wave + j;
+      qs[(2 * s) * 64 + c.lane] = __builtin_bit_cast(u32x4, frag_hi(v[2 * j], v[2 * j + 1]));
+      qs[(2 * s + 1) * 64 + c.lane] = __builtin_bit_cast(u32x4, frag_lo(v[2 * j], v[2 * j + 1]));
+    }
     cw_barrier(c);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, qs[s * 64 + c.lane]);
+    for (int s = 0; s < 8; ++s) {
+      qh[s] = __builtin_bit_cast(bf16x8, qs[(2 * s) * 64 + c.lane]);
+      ql[s] = __builtin_bit_cast(bf16x8, qs[(2 * s + 1) * 64 + c.lane]);
+    }
   }
-  const unsigned p0 = (unsigned)k * c.n_step + c.n_in + (unsigned)l * c.n_layer + c.o_attn;
+  const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_att;
   wait_tiles(c, p0, 64);
-  // S^T for keys [16 w, 16 w + 16) of the chunk: lane holds keys 4g + i of row `row`
-  f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+  // S^T for keys [16 w, 16 w + 16) of the chunk: lane holds keys 4 g + e of row `row`
+  f32x4 sth = f32x4{0.f, 0.f, 0.f, 0.f}, stl = sth;  // hi and lo products in chains of their own
 #pragma unroll
-  for (int s = 0; s < 8; ++s) st = mma32(ring_tile(c, p0 + 8u * c.wave + s), qf[s], st);
+  for (int s = 0; s < 8; ++s) {
+    const bf16x8 kt = ring_tile(c, p0 + 8u * c.wave + s);
+    sth = mma32(kt, qh[s], sth);
+    stl = mma32(kt, ql[s], stl);
+  }
+  const f32x4 st = sth + stl;
   float sv[4];
   float mw = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = CHUNK * c.attn_c + 16 * c.wave + 4 * c.g + i;
-    sv[i] = key < c.L ? st[i] * scale : -INFINITY;
-    mw = fmaxf(mw, sv[i]);
+  for (int e = 0; e < 4; ++e) {
+    const int key = CHUNK * ch + 16 * c.wave + 4 * c.g + e;
+    sv[e] = key < c.L ? st[e] * scale : -INFINITY;
+    mw = fmaxf(mw, sv[e]);
   }
   mw = fmaxf(mw, __shfl_xor(mw, 16));
   mw = fmaxf(mw, __shfl_xor(mw, 32));
@@ -607,86 +703,110 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
   const float m_row = fmaxf(fmaxf(c.sh->att_m[0][c.row], c.sh->att_m[1][c.row]),
                             fmaxf(c.sh->att_m[2][c.row], c.sh->att_m[3][c.row]));
   float lw = 0.f;
-  s16x4 pf;
+  s16x4 ph, pl;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = sv[i] == -INFINITY ? 0.f : fexp(sv[i] - m_row);
+  for (int e = 0; e < 4; ++e) {
+    const float p = sv[e] == -INFINITY ? 0.f : fexp(sv[e] - m_row);
     lw += p;
-    pf[i] = as_s((bf16)p);
+    short a, b;
+    split_bf16(p, a, b);
+    ph[e] = a;
+    pl[e] = b;
   }
   lw += __shfl_xor(lw, 16);
   lw += __shfl_xor(lw, 32);
   if (c.g == 0) c.sh->att_l[c.wave][c.row] = lw;
-  c.sh->att_p[c.wave][c.lane] = pf;
+  c.sh->att_p[c.wave][0][c.lane] = ph;
+  c.sh->att_p[c.wave][1][c.lane] = pl;
   cw_barrier(c);
   const float l_row = (c.sh->att_l[0][c.row] + c.sh->att_l[1][c.row]) + (c.sh->att_l[2][c.row] + c.sh->att_l[3][c.row]);
   // O = P . V for dim tiles [4 w, 4 w + 4), all four key groups
-  f32x4 oacc[4];
+  f32x4 oacc[4], olo[4];  // the lo products of P in accumulators of their own
 #pragma unroll
-  for (int d = 0; d < 4; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < 4; ++d) oacc[d] = olo[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg) {
-    const s16x4 a = c.sh->att_p[kg][c.lane];
+    const s16x4 ah = c.sh->att_p[kg][0][c.lane];
+    const s16x4 al = c.sh->att_p[kg][1][c.lane];
 #pragma unroll
     for (int dp = 0; dp < 2; ++dp) {
       const unsigned pos = p0 + 32u + 8u * kg + 2u * c.wave + dp;
       const u32x4 vv = *(const u32x4*)(c.ring + (pos % RING) * TILE_BYTES + c.lane * 16);
       const s16x4 b0 = __builtin_bit_cast(s16x4, u32x2{vv[0], vv[1]});
       const s16x4 b1 = __builtin_bit_cast(s16x4, u32x2{vv[2], vv[3]});
-      oacc[2 * dp] = mma16(a, b0, oacc[2 * dp]);
-      oacc[2 * dp + 1] = mma16(a, b1, oacc[2 * dp + 1]);
+      oacc[2 * dp] = mma16(ah, b0, oacc[2 * dp]);
+      oacc[2 * dp + 1] = mma16(ah, b1, oacc[2 * dp + 1]);
+      olo[2 * dp] = mma16(al, b0, olo[2 * dp]);
+      olo[2 * dp + 1] = mma16(al, b1, olo[2 * dp + 1]);
     }
   }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) oacc[d] += olo[d];
   cw_barrier(c);
   release_ring(c, p0 + 64u);
-  attn_publish(c, slot, oacc, m_row, l_row);
+  attn_publish(c, ch, u, oacc, m_row, l_row);
 }
 
-// attention of head h over the action rows' own keys and values.  Wave w
-// polls its quarter of the head dims of q and of the keys (k-tiles 2w, 2w + 1)
-// and value rows w, w + 4, w + 8, w + 12; the four partial score tiles are
-// summed in LDS in wave order, and the values are staged there transposed
-// for the P . V fragments.
+// Attention of head xcd over the action rows' own keys and values (chunk
+// nc).  Wave w takes head dims [64 w, 64 w + 64) of q and of the keys for a
+// partial score tile (the four are summed in LDS in wave order) and value
+// rows w, w + 4, w + 8, w + 12, staged in LDS transposed for the P . V
+// fragments.  Products of two low halves (2^-16 of 2^-16) are left out.
 __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int k, int l) {
   refresh(c);
-  const unsigned slot = slot_of(c, k, l);
+  const Use u = use_layer(c, k, l);
   const float scale = 0.0625f;
-  f32x4* red = red_take(c);
-  unsigned short* va = (unsigned short*)red;  // [DH][RP] bf16 values, transposed
-  f32x4* sp = red + DH * RP * 2 / 16;         // [4 waves][64 lanes] partial score tiles
+  unsigned char* red = red_take(c);
+  unsigned short* vh = (unsigned short*)red;             // [DH][RP] hi halves of the values, transposed
+  unsigned short* vl = vh + DH * RP;                     // [DH][RP] lo halves
+  f32x4* sp = (f32x4*)(red + 2 * DH * RP * 2);           // [4 waves][64 lanes] partial score tiles
   {
-    const int t = c.wave * 64 + c.lane;  // 256 threads: thread t clears dims t
+    const int t = c.wave * 64 + c.lane;  // 256 threads: thread t clears dim t
 #pragma unroll
-    for (int key = 0; key < RP; ++key) va[t * RP + key] = 0;
+    for (int key = 0; key < RP; key += 2) {
+      *(unsigned*)(vh + t * RP + key) = 0u;
+      *(unsigned*)(vl + t * RP + key) = 0u;
+    }
   }
-  u32x4 v[12];
+  const int kcrow = c.crow;  // key row of the A fragments (clamped like the query rows)
+  u32x4 kv[8];
   {
-    const unsigned qb = xoff<X_Q>(slot);
-    const int R = c.R, w = c.wave;
-    const PB pb{((unsigned)c.crow * (DH / 2) + 4u * (unsigned)c.g) * 8u,
-                ((unsigned)w * (DH / 2) + 2u * (unsigned)c.lane) * 8u,
-                qb + (unsigned)(c.attn_h * RP) * (DH / 2) * 8u + 256u * (unsigned)w,
-                qb + (unsigned)(H * RP) * (DH / 2) * 8u + 256u * (unsigned)w, qb + (unsigned)((H + 1) * RP) * (DH / 2) * 8u};
-    auto addr = [&](const PB& b, int i) -> LA {
-      if (i < 4) return frag_la(b.v0, b.s0, 128u, i);
-      if (i < 8) return frag_la(b.v0, b.s1, 128u, i - 4);
-      return LA{b.v1, b.s2 + (unsigned)(4 * (i - 8)) * (DH / 2) * 8u, w + 4 * (i - 8) < R};
-    };
-    ll_poll<12>(c, pb, addr, tag_of(c, slot, X_Q), v);
+    const unsigned vk = (unsigned)((kcrow * 2 * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned bkv = xb<X_KV>(c, u.par);
+    poll<SC1>(c, [&](int i) -> LA {
+      if (i < 4) return LA{vk + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bkv};
+      const int key = c.wave + 4 * (i - 4);
+      const int ck = key < c.R ? key : c.R - 1;
+      return LA{(unsigned)((ck * 2 * DH + DH + 4 * c.lane) * 4), bkv};
+    }, u.gen, kv);
   }
-  f32x4 st = mma32(frag_of(v[4], v[5]), frag_of(v[0], v[1]), f32x4{0.f, 0.f, 0.f, 0.f});
-  st = mma32(frag_of(v[6], v[7]), frag_of(v[2], v[3]), st);
+  u32x4 qv[4];
+  {
+    const unsigned vq = (unsigned)((c.crow * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned bq = xb<X_Q>(c, u.par);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vq + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, qv);
+  }
+  f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16x8 kh = frag_hi(kv[2 * j], kv[2 * j + 1]), kl = frag_lo(kv[2 * j], kv[2 * j + 1]);
+    const bf16x8 qhf = frag_hi(qv[2 * j], qv[2 * j + 1]), qlf = frag_lo(qv[2 * j], qv[2 * j + 1]);
+    st = mma32(kh, qhf, st);
+    st = mma32(kh, qlf, st);
+    st = mma32(kl, qhf, st);
+  }
   cw_barrier(c);  // staging area cleared by every wave
   sp[c.wave * 64 + c.lane] = st;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = c.wave + 4 * i;
+  for (int e = 0; e < 4; ++e) {
+    const int key = c.wave + 4 * e;
     if (key < c.R) {
-      const int d0 = 4 * c.lane;  // pair words 2 lane, 2 lane + 1 -> dims 4 lane .. 4 lane + 3
-      va[(d0 + 0) * RP + key] = (unsigned short)(v[8 + i][0] & 0xffffu);
-      va[(d0 + 1) * RP + key] = (unsigned short)(v[8 + i][0] >> 16);
-      va[(d0 + 2) * RP + key] = (unsigned short)(v[8 + i][2] & 0xffffu);
-      va[(d0 + 3) * RP + key] = (unsigned short)(v[8 + i][2] >> 16);
+      const u32x4 w = kv[4 + e];  // dims 4 lane .. 4 lane + 3 of value row `key`
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        vh[(4 * c.lane + q) * RP + key] = (unsigned short)(w[q] >> 16);
+        vl[(4 * c.lane + q) * RP + key] = (unsigned short)(w[q] & 0xfffeu);
+      }
     }
   }
   cw_barrier(c);
@@ -694,21 +814,24 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
   float sv[4];
   float mw = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = 4 * c.g + i;
-    sv[i] = key < c.R ? st[i] * scale : -INFINITY;
-    mw = fmaxf(mw, sv[i]);
+  for (int e = 0; e < 4; ++e) {
+    const int key = 4 * c.g + e;
+    sv[e] = key < c.R ? st[e] * scale : -INFINITY;
+    mw = fmaxf(mw, sv[e]);
   }
   mw = fmaxf(mw, __shfl_xor(mw, 16));
   mw = fmaxf(mw, __shfl_xor(mw, 32));
   const float m_row = mw;
   float lw = 0.f;
-  s16x4 pf;
+  s16x4 ph, pl;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = sv[i] == -INFINITY ? 0.f : fexp(sv[i] - m_row);
+  for (int e = 0; e < 4; ++e) {
+    const float p = sv[e] == -INFINITY ? 0.f : fexp(sv[e] - m_row);
     lw += p;
-    pf[i] = as_s((bf16)p);
+    short a, b;
+    split_bf16(p, a, b);
+    ph[e] = a;
+    pl[e] = b;
   }
   lw += __shfl_xor(lw, 16);
   lw += __shfl_xor(lw, 32);
@@ -716,277 +839,272 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const int dim = 16 * (4 * c.wave + d) + c.row;
-    const s16x4 b = *(const s16x4*)(va + dim * RP + 4 * c.g);
-    oacc[d] = mma16(pf, b, f32x4{0.f, 0.f, 0.f, 0.f});
+    const s16x4 bh = *(const s16x4*)(vh + dim * RP + 4 * c.g);
+    const s16x4 bl = *(const s16x4*)(vl + dim * RP + 4 * c.g);
+    oacc[d] = mma16(ph, bh, f32x4{0.f, 0.f, 0.f, 0.f});
+    oacc[d] = mma16(ph, bl, oacc[d]);
+    oacc[d] = mma16(pl, bh, oacc[d]);
   }
-  attn_publish(c, slot, oacc, m_row, lw);
+  attn_publish(c, c.nc, u, oacc, m_row, lw);
 }
 
-// merges the key chunks of head h for dims [32 s, 32 s + 32) and writes the
-// normalised attention output as bf16 pairs.  Wave w polls chunks w, w + 4,
-// w + 8, w + 12: per chunk one load of the (max, sum) pairs (lane: row
-// lane % 16) and four loads of dims 32 s + 2 dp, + 1 of rows rg + 4 j.  The
-// (max, sum) pairs go to LDS; every lane then forms the row statistics over
-// all chunks and the weight exp(m_c - M) / L of each of its (chunk, row)
-// pairs once, so the merge itself is plain multiply-adds.  The four waves'
-// partial sums meet in LDS and each wave finishes one row group.
-__device__ __attribute__((always_inline)) inline void ph_comb(Ctx& c, int k, int l) {
+// Merges the head's key chunks for dims [32 s, 32 s + 32) and writes the
+// normalised attention output as pairs.  Lane: dims 32 s + 4 q + [0, 4)
+// (q = lane % 8) of rows rb and rb + 8 (rb = lane / 8).  Wave w reads chunks
+// w, w + 4, w + 8, w + 12: per chunk the (max, sum) of row lane % 16 and the
+// two rows' partial outputs.  Every lane forms the statistics over all
+// chunks from LDS, weights its chunks' partials by exp(m_c - M) / L, and the
+// four waves' sums meet in LDS in wave order.
+__device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, int l) {
   refresh(c);
-  if (c.comb_h < 0) return;
-  const int hd = c.comb_h, sl = c.comb_s;
+  if (!is_merge(c)) return;
+  const int s = c.rk - R_MERGE;
   const int nch = c.nc + 1;
-  const unsigned slot = slot_of(c, k, l);
-  const unsigned tag = tag_of(c, slot, X_ATT);
-  const unsigned ob = xoff<X_ATT>(slot);
-  const unsigned mlb = ob + X_ML;
-  const int dp = c.lane & 15, rg = c.lane >> 4;
-  const int R = c.R;
-  f32x4* red = red_take(c);
+  const Use u = use_layer(c, k, l);
+  const int q = c.lane & 7, rb = c.lane >> 3;
+  const int rA = rb < c.R ? rb : c.R - 1, rB = rb + 8 < c.R ? rb + 8 : c.R - 1;
+  unsigned char* red = red_take(c);
   float* mls = (float*)red;                       // [MAX_CHUNKS][RP] max, then [MAX_CHUNKS][RP] sum
-  f32x4* part = red + (2 * MAX_CHUNKS * RP) / 4;  // [4 waves][2][64 lanes] partial sums (rows rg + 4i, 2 dims)
-  const int base = c.wave;
-  u32x4 v[20];
+  f32x4* part = (f32x4*)(red + 2 * MAX_CHUNKS * RP * 4);  // [4 waves][2 rows][64 lanes]
+  u32x4 v[12];
   {
-    const int mrow = dp < R ? dp : R - 1;
-    const PB pb{(unsigned)mrow * 16u, (unsigned)(2 * dp) * 8u, mlb + (unsigned)(hd * MAX_CHUNKS + base) * RP * 16u,
-                ob + ((unsigned)(hd * MAX_CHUNKS + base) * RP * DH + 32u * (unsigned)sl) * 8u, (unsigned)base};
-    auto addr = [&](const PB& b, int i) -> LA {
-      const int q = i / 5, j = i % 5;
-      const bool need = (int)b.s2 + NCOMPUTE * q < nch;
-      if (j == 0) return LA{b.v0, b.s0 + (unsigned)(NCOMPUTE * q) * RP * 16u, need};
-      const int rw = rg + 4 * (j - 1);
-      const unsigned row = (unsigned)(rw < R ? rw : R - 1);
-      return LA{b.v1 + row * DH * 8u, b.s1 + (unsigned)(NCOMPUTE * q) * RP * DH * 8u, need};
-    };
-    ll_poll<20>(c, pb, addr, tag, v);
+    const unsigned bo = xb<X_AO>(c, u.par), bm = xb<X_AML>(c, u.par);
+    const unsigned vA = (unsigned)((rA * DH + 32 * s + 4 * q) * 4), vB = (unsigned)((rB * DH + 32 * s + 4 * q) * 4);
+    const unsigned vm = (unsigned)(c.crow * 16);
+    poll<NTP>(c, [&](int i) -> LA {
+      const int cc0 = c.wave + NCOMPUTE * (i / 3);
+      const int cc = cc0 < nch ? cc0 : nch - 1;  // past the last chunk: read the last one again
+      const int j = i % 3;
+      if (j == 0) return LA{vm, bm + (unsigned)(cc * RP * 16)};
+      return LA{j == 1 ? vA : vB, bo + (unsigned)(cc * RP * DH * 4)};
+    }, u.gen, v);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int cc = base + NCOMPUTE * q;
+  for (int jq = 0; jq < 4; ++jq) {
+    const int cc = c.wave + NCOMPUTE * jq;
     if (cc < nch && c.lane < RP) {
-      mls[cc * RP + c.lane] = as_f(v[5 * q][0]);
-      mls[(MAX_CHUNKS + cc) * RP + c.lane] = as_f(v[5 * q][2]);
+      mls[cc * RP + c.lane] = wf(v[3 * jq][0]);
+      mls[(MAX_CHUNKS + cc) * RP + c.lane] = wf(v[3 * jq][1]);
     }
   }
   cw_barrier(c);
-  // statistics of row lane % 16 over every chunk (a chunk without valid keys has max -inf and sum 0)
-  float M = -INFINITY;
-  for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, mls[cc * RP + dp]);
-  float L = 0.f;
-  for (int cc = 0; cc < nch; ++cc) {
-    const float m = mls[cc * RP + dp];
-    if (m != -INFINITY) L += fexp(m - M) * mls[(MAX_CHUNKS + cc) * RP + dp];
-  }
-  const float invL = frcp(L);
-  float acc0[4], acc1[4];
+  float accA[4] = {0.f, 0.f, 0.f, 0.f}, accB[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = rg + 4 * i;
-    const float Mr = __shfl(M, row), iLr = __shfl(invL, row);
-    acc0[i] = acc1[i] = 0.f;
+  for (int half = 0; half < 2; ++half) {
+    const int r = half == 0 ? rb : rb + 8;
+    float M = M_EMPTY;
+    for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, mls[cc * RP + r]);
+    float L = 0.f;
+    for (int cc = 0; cc < nch; ++cc) L += fexp(mls[cc * RP + r] - M) * mls[(MAX_CHUNKS + cc) * RP + r];
+    const float invL = frcp(L);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cc = base + NCOMPUTE * q;
+    for (int jq = 0; jq < 4; ++jq) {
+      const int cc = c.wave + NCOMPUTE * jq;
       if (cc < nch) {
-        const float m = mls[cc * RP + row];
-        const float wgt = m == -INFINITY ? 0.f : fexp(m - Mr) * iLr;
-        acc0[i] += wgt * as_f(v[5 * q + 1 + i][0]);
-        acc1[i] += wgt * as_f(v[5 * q + 1 + i][2]);
+        const float wgt = fexp(mls[cc * RP + r] - M) * invL;
+        const u32x4 pv = v[3 * jq + 1 + half];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (half == 0)
+            accA[e] += wgt * wf(pv[e]);
+          else
+            accB[e] += wgt * wf(pv[e]);
+        }
       }
     }
   }
-  part[(c.wave * 2 + 0) * 64 + c.lane] = f32x4{acc0[0], acc1[0], acc0[1], acc1[1]};
-  part[(c.wave * 2 + 1) * 64 + c.lane] = f32x4{acc0[2], acc1[2], acc0[3], acc1[3]};
+  part[(c.wave * 2 + 0) * 64 + c.lane] = f32x4{accA[0], accA[1], accA[2], accA[3]};
+  part[(c.wave * 2 + 1) * 64 + c.lane] = f32x4{accB[0], accB[1], accB[2], accB[3]};
   cw_barrier(c);
-  {
-    // wave w finishes rows rg + 4w of every lane's dims, summing the waves in order
-    const int i = c.wave;
-    const float* pf = (const float*)part;
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < NCOMPUTE; ++w) {
-      const float* e = pf + ((w * 2 + (i >> 1)) * 64 + c.lane) * 4 + 2 * (i & 1);
-      a0 += e[0];
-      a1 += e[1];
-    }
-    const int rw = rg + 4 * i;
-    if (rw < R)
-      ll_store1(c, xoff<X_O>(slot) + ((unsigned)rw * (HD / 2) + (unsigned)(hd * (DH / 2) + 16 * sl + dp)) * 8u,
-                pack_bf16(a0, a1), tag_of(c, slot, X_O));
-  }
-}
-
-// out projection of the owner's column block (K = H*DH over the four waves),
-// residual add, and the MLP norm's producer half
-__device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l, f32x4& hreg) {
-  refresh(c);
-  if (c.owner < 0) return;
-  const unsigned slot = slot_of(c, k, l);
-  const unsigned p0 = (unsigned)k * c.n_step + c.n_in + (unsigned)l * c.n_layer + c.o_o;
-  const u32x4 sv = owner_scale_load(c, k, 2 * l + 1);
-  u32x4 v[32];
-  {
-    const PB pb{((unsigned)c.crow * (HD / 2) + 4u * (unsigned)c.g) * 8u, 0u,
-                xoff<X_O>(slot) + (unsigned)(16 * c.wave) * 128u, 0u, 0u};
-    ll_poll<32>(c, pb, [](const PB& b, int i) { return frag_la(b.v0, b.s0, 128u, i); }, tag_of(c, slot, X_O), v);
-  }
-  wait_tiles(c, p0, 64);
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 16; ++kk)
-    acc = mma32(ring_tile(c, p0 + 16u * c.wave + kk), frag_of(v[2 * kk], v[2 * kk + 1]), acc);
-  f32x4* red = red_take(c);
-  red[(c.wave * 4) * 64 + c.lane] = acc;
-  cw_barrier(c);
-  release_ring(c, p0 + 64u);
-  if (c.wave == 0) {
-    hreg += red_sum(red, 0, c.lane);
-    owner_publish<X_HS1, X_SS1>(c, hreg, sv, slot);
-  }
-}
-
-// gate/up projection of two n-tiles with the GeGLU epilogue
-__device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l) {
-  refresh(c);
-  const unsigned slot = slot_of(c, k, l);
-  const unsigned p0 = (unsigned)k * c.n_step + c.n_in + (unsigned)l * c.n_layer + c.o_gu;
-  const int nt = 2 * (int)blockIdx.x + (c.wave & 1);
-  const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
-      c.X, step_tab(c, k) + st_swgu(c.NL) + (unsigned)((l * 2 * F + nt * 16 + 4 * c.g) * 4), 0, 0);
-  u32x4 v[24];
-  poll_normed<X_HS1, X_SS1>(c, slot, v);
-  wait_tiles(c, p0, 64);
-  f32x4 acc[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      acc[t] = mma32(ring_tile(c, p0 + 32u * t + 8u * c.wave + kk), frag_of(v[2 * kk], v[2 * kk + 1]), acc[t]);
-  }
-  f32x4* red = red_take(c);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) red[(c.wave * 4 + t) * 64 + c.lane] = acc[t];
-  cw_barrier(c);
-  release_ring(c, p0 + 64u);
   if (c.wave < 2) {
-    const f32x4 s = red_sum(red, c.wave, c.lane);
-    const float rr = c.sh->rrow[c.row];
-    float y[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = rr * s[i] + as_f(sw[i]);
-    const float a0 = gelu_tanh(y[0]) * y[2];
-    const float a1 = gelu_tanh(y[1]) * y[3];
-    if (c.row < c.R)
-      ll_store1(c, xoff<X_A>(slot) + ((unsigned)c.row * (F / 2) + (unsigned)(4 * nt + c.g)) * 8u, pack_bf16(a0, a1),
-                tag_of(c, slot, X_A));
+    // wave 0 finishes rows rb, wave 1 rows rb + 8, summing the waves in order
+    const int half = c.wave;
+    f32x4 a = part[(0 * 2 + half) * 64 + c.lane];
+    a += part[(1 * 2 + half) * 64 + c.lane];
+    a += part[(2 * 2 + half) * 64 + c.lane];
+    a += part[(3 * 2 + half) * 64 + c.lane];
+    const int r = rb + 8 * half;
+    if (r < c.R) {
+      const Use uo = use_layer(c, k, l);
+      const u32x4 w = {pair_word(a[0], uo.gen), pair_word(a[1], uo.gen), pair_word(a[2], uo.gen),
+                       pair_word(a[3], uo.gen)};
+      st4<LST>(c, xb<X_O>(c, uo.par) + (unsigned)((r * DH + 32 * s + 4 * q) * 4), w);
+    }
   }
 }
 
-// down projection: K group kq (8 k-tiles, two per wave) x N group nq (4 n-tiles)
-__device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int l) {
+// out projection of the head's 256 rows for output columns [64 o, 64 o + 64)
+// (four n-tiles; K split over the four waves): a partial sum of the residual
+// update, published at device scope for the owners of every XCD
+__device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l) {
   refresh(c);
-  const int kq = (int)blockIdx.x / DN_NQ, nqd = (int)blockIdx.x % DN_NQ;
-  const unsigned slot = slot_of(c, k, l);
-  const unsigned p0 = (unsigned)k * c.n_step + c.n_in + (unsigned)l * c.n_layer + c.o_dn;
+  if (!is_o(c)) return;
+  const int o = c.rk - R_O;
+  const Use u = use_layer(c, k, l);
+  const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_o;
   u32x4 v[4];
   {
-    const PB pb{((unsigned)c.crow * (F / 2) + 4u * (unsigned)c.g) * 8u, 0u,
-                xoff<X_A>(slot) + (unsigned)(8 * kq + 2 * c.wave) * 128u, 0u, 0u};
-    ll_poll<4>(c, pb, [](const PB& b, int i) { return frag_la(b.v0, b.s0, 128u, i); }, tag_of(c, slot, X_A), v);
+    const unsigned vo = (unsigned)((c.crow * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned bo = xb<X_O>(c, u.par);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bo}; }, u.gen, v);
   }
   wait_tiles(c, p0, 32);
   f32x4 acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      acc[t] = mma32(ring_tile(c, p0 + 8u * t + 2u * c.wave + kk), frag_of(v[2 * kk], v[2 * kk + 1]), acc[t]);
-  }
-  f32x4* red = red_take(c);
+  gemm_pairs<4, 2>(c, [&](int t, int j) { return p0 + 8u * t + 2u * c.wave + j; }, v, acc);
+  f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 4; ++t) red[(c.wave * 4 + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
   release_ring(c, p0 + 32u);
-  const f32x4 s = red_sum(red, c.wave, c.lane);
+  const f32x4 s = red_sum(red, 4, c.wave, c.lane);  // wave t finishes n-tile t
   if (c.row < c.R) {
-    const int col = 16 * (4 * nqd + c.wave) + 4 * c.g;
-    const unsigned o = xoff<X_DP>(slot) + (((unsigned)kq * RP + (unsigned)c.row) * D + (unsigned)col) * 8u;
-    const unsigned tag = tag_of(c, slot, X_DP);
-    ll_store2(c, o, as_u(s[0]), as_u(s[1]), tag);
-    ll_store2(c, o + 16u, as_u(s[2]), as_u(s[3]), tag);
+    const u32x4 w = {f32_word(s[0], u.gen), f32_word(s[1], u.gen), f32_word(s[2], u.gen), f32_word(s[3], u.gen)};
+    st4<SC1>(c, xb<X_OP>(c, u.par) + (unsigned)(((c.xcd * RP + c.row) * D + 64 * o + 16 * c.wave + 4 * c.g) * 4), w);
   }
 }
 
-// residual add of the 16 down partials of the owner's block, and the next
-// norm's producer half (the next layer's attention norm, or the final norm)
-__device__ __attribute__((always_inline)) inline void ph_owner2(Ctx& c, int k, int l, f32x4& hreg) {
+// All-reduce of a residual update (T_P: the eight XCDs' partial sums), the
+// residual add and the next norm's producer half.  Wave w reads the partials
+// of XCDs 2 w and 2 w + 1; the sum runs over XCDs in order on every XCD.
+template <int T_P, int T_N, int T_SS>
+__device__ __attribute__((always_inline)) inline void ph_own(Ctx& c, int k, int norm, const Use& u, const Use& un,
+                                                             f32x4 (&h)[2]) {
   refresh(c);
-  if (c.owner < 0) return;
-  const int j = c.owner;
-  const unsigned slot = slot_of(c, k, l);
-  const u32x4 sv = owner_scale_load(c, k, 2 * (l + 1));
+  u32x4 sv[2];
+  if (c.wave == 0) {
+    sv[0] = owner_scale_load(c, k, norm, 0);
+    sv[1] = owner_scale_load(c, k, norm, 1);
+  }
+  u32x4 v[4];
+  {
+    const unsigned vo = (unsigned)(((2 * c.wave * RP + c.crow) * D + 32 * c.rk + 4 * c.g) * 4);
+    const unsigned bp = xb<T_P>(c, u.par);
+    // load i: XCD 2 w + (i >> 1), n-tile i & 1
+    poll<SC1>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * RP * D * 4 + (i & 1) * 64), bp}; }, u.gen, v);
+  }
+  f32x4* red = (f32x4*)red_take(c);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4 s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = wf(v[t][e]) + wf(v[2 + t][e]);
+    red[(c.wave * 2 + t) * 64 + c.lane] = s;
+  }
+  cw_barrier(c);
+  if (c.wave == 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) h[t] += red_sum(red, 2, t, c.lane);
+    owner_publish<T_N, T_SS>(c, h, sv, un);
+  }
+}
+
+// gate/up projection of two n-tiles with the GeGLU epilogue: features
+// 16 r + 8 t + 2 g + [0, 2) of the XCD's 512
+__device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l) {
+  refresh(c);
+  const Use u = use_layer(c, k, l);
+  const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_gu;
+  const int nt = 64 * c.xcd + 2 * c.rk + (c.wave & 1);
+  const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
+      c.X, step_tab(c, k) + st_swgu(c.NL) + (unsigned)((l * 2 * F + nt * 16 + 4 * c.g) * 4), 0, 0);
+  u32x4 v[18];
+  poll_normed<X_N2, X_SS2>(c, u, v);
+  wait_tiles(c, p0, 64);
+  f32x4 acc[2];
+  gemm_pairs<2, 8>(c, [&](int t, int kk) { return p0 + 32u * t + 8u * c.wave + kk; }, v, acc);
+  f32x4* red = (f32x4*)red_take(c);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
+  cw_barrier(c);
+  release_ring(c, p0 + 64u);
+  if (c.wave < 2) {
+    const f32x4 s = red_sum(red, 2, c.wave, c.lane);
+    const float rr = c.sh->rrow[c.row];
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = rr * s[e] + as_f(sw[e]);
+    const float a0 = gelu_tanh(y[0]) * y[2];
+    const float a1 = gelu_tanh(y[1]) * y[3];
+    if (c.row < c.R) {
+      const int f = 16 * c.rk + 8 * c.wave + 2 * c.g;
+      st2<LST>(c, xb<X_A>(c, u.par) + (unsigned)((c.row * FX + f) * 4), u32x2{pair_word(a0, u.gen), pair_word(a1, u.gen)});
+    }
+  }
+}
+
+// down projection of the XCD's 512 features (K split over the four waves)
+// for output columns [32 r, 32 r + 32): a partial sum for the owners of
+// every XCD
+__device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int l) {
+  refresh(c);
+  const Use u = use_layer(c, k, l);
+  const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_dn;
   u32x4 v[8];
   {
-    const PB pb{((unsigned)c.crow * D + (unsigned)(16 * j + 4 * c.g)) * 8u, 0u,
-                xoff<X_DP>(slot) + (unsigned)(4 * c.wave) * (RP * D * 8u), 0u, 0u};
-    // partial K groups are RP * D words apart: too far for an immediate, so they step the uniform base
-    ll_poll<8>(c, pb, [](const PB& b, int i) {
-      return LA{b.v0 + (unsigned)(i & 1) * 16u, b.s0 + (unsigned)(i >> 1) * (RP * D * 8u), true};
-    }, tag_of(c, slot, X_DP), v);
+    const unsigned vo = (unsigned)((c.crow * FX + 128 * c.wave + 8 * c.g) * 4);
+    const unsigned ba = xb<X_A>(c, u.par);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), ba}; }, u.gen, v);
   }
-  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  wait_tiles(c, p0, 32);
+  f32x4 acc[2];
+  gemm_pairs<2, 4>(c, [&](int t, int j) { return p0 + 16u * t + 4u * c.wave + j; }, v, acc);
+  f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s[0] += as_f(v[2 * i][0]);
-    s[1] += as_f(v[2 * i][2]);
-    s[2] += as_f(v[2 * i + 1][0]);
-    s[3] += as_f(v[2 * i + 1][2]);
-  }
-  f32x4* red = red_take(c);
-  red[(c.wave * 4) * 64 + c.lane] = s;
+  for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
-  if (c.wave == 0) {
-    hreg += red_sum(red, 0, c.lane);
-    owner_publish<X_HS, X_SS>(c, hreg, sv, slot + 1u);
+  release_ring(c, p0 + 32u);
+  if (c.wave < 2) {
+    const f32x4 s = red_sum(red, 2, c.wave, c.lane);
+    if (c.row < c.R) {
+      const u32x4 w = {f32_word(s[0], u.gen), f32_word(s[1], u.gen), f32_word(s[2], u.gen), f32_word(s[3], u.gen)};
+      st4<SC1>(c, xb<X_DP>(c, u.par) + (unsigned)(((c.xcd * RP + c.row) * D + 32 * c.rk + 16 * c.wave + 4 * c.g) * 4),
+               w);
+    }
   }
 }
 
-// velocity head of one n-tile (K = D over the four waves), final norm's
-// consumer half, and the Euler update of the owned state columns
-__device__ __attribute__((always_inline)) inline void ph_out(Ctx& c, int k, f32x4& xreg) {
+// velocity head (K = D over the four waves), the final norm's consumer half,
+// and the Euler update of every state column (wave 0 holds x); each XCD keeps
+// its own copy of x, XCD 0 writes the actions after the last step
+__device__ __attribute__((always_inline)) inline void ph_vel(Ctx& c, int k, f32x4 (&x)[2]) {
   refresh(c);
-  if (c.out_nt < 0) return;
+  if (!is_vel(c)) return;
   const int NL = c.NL;
-  const unsigned slot = slot_of(c, k, NL);
-  const unsigned p0 = (unsigned)k * c.n_step + c.n_in + (unsigned)NL * c.n_layer;
-  const int t = c.out_nt;
-  const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
-      c.X, step_tab(c, k) + st_swout(NL) + (unsigned)((16 * t + 4 * c.g) * 4), 0, 0);
-  u32x4 v[24];
-  poll_normed<X_HS, X_SS>(c, slot, v);
-  wait_tiles(c, p0, 32);
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const Use u = use_norm(c, k, NL);
+  const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)NL * c.n_layer;
+  u32x4 sw[2];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) acc = mma32(ring_tile(c, p0 + 8u * c.wave + kk), frag_of(v[2 * kk], v[2 * kk + 1]), acc);
-  f32x4* red = red_take(c);
-  red[(c.wave * 4) * 64 + c.lane] = acc;
+  for (int t = 0; t < 2; ++t)
+    sw[t] = __builtin_amdgcn_raw_buffer_load_b128(c.X, step_tab(c, k) + st_swout(NL) + (unsigned)((16 * t + 4 * c.g) * 4),
+                                                  0, 0);
+  u32x4 v[18];
+  poll_normed<X_N, X_SS>(c, u, v);
+  wait_tiles(c, p0, 64);
+  f32x4 acc[2];
+  gemm_pairs<2, 8>(c, [&](int t, int kk) { return p0 + 32u * t + 8u * c.wave + kk; }, v, acc);
+  f32x4* red = (f32x4*)red_take(c);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
-  release_ring(c, p0 + 32u);
+  release_ring(c, p0 + 64u);
   if (c.wave == 0) {
-    const f32x4 s = red_sum(red, 0, c.lane);
     const float rr = c.sh->rrow[c.row];
+    const Use ux = use_state(c, k);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xreg[i] += c.dt * (rr * s[i] + as_f(sw[i]));
-    if (c.row < c.R) {
-      if (k + 1 < c.S) {
-        ll_store2(c, xoff<X_X>(slot) + ((unsigned)c.row * (A / 2) + (unsigned)(8 * t + 2 * c.g)) * 8u,
-                  pack_bf16(xreg[0], xreg[1]), pack_bf16(xreg[2], xreg[3]), tag_of(c, slot, X_X));
-      } else {
-        const u32x4 xv = {as_u(xreg[0]), as_u(xreg[1]), as_u(xreg[2]), as_u(xreg[3])};
-        __builtin_amdgcn_raw_buffer_store_b128(xv, c.X, AUX0 + AUX_X + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4),
-                                               0, 0);
+    for (int t = 0; t < 2; ++t) {
+      const f32x4 s = red_sum(red, 2, t, c.lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[t][e] += c.dt * (rr * s[e] + as_f(sw[t][e]));
+      if (c.row < c.R) {
+        if (k + 1 < c.S) {
+          const u32x4 w = {f32_word(x[t][0], ux.gen), f32_word(x[t][1], ux.gen), f32_word(x[t][2], ux.gen),
+                           f32_word(x[t][3], ux.gen)};
+          st4<LST>(c, xb<X_X>(c, ux.par) + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4), w);
+        } else if (c.xcd == 0) {
+          const u32x4 w = {as_u(x[t][0]), as_u(x[t][1]), as_u(x[t][2]), as_u(x[t][3])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, c.X, AUX0 + AUX_X + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4), 0,
+                                                 0);
+        }
       }
     }
   }
@@ -1004,59 +1122,61 @@ struct Gen {
   int kv;                 // 1: run reads the prefix K/V arena
 };
 
-// run 0: input projection; 1 + 8 l + u: layer l part u (QKV, prefix K/V, O,
-// gate/up, down n-tiles 0..3); 1 + 8 NL: velocity head
+constexpr int RUNS_PER_LAYER = 9;
+// run 0: input projection (W_in n-tiles 2 r, 2 r + 1); 1 + 9 l + u: layer l
+// part u (0 QKV, 1 prefix K/V chunk, 2..5 out projection n-tiles, 6 gate/up,
+// 7..8 down n-tiles); 1 + 9 NL: velocity head
 __device__ inline void run_params(const Ctx& c, int run, unsigned& off, int& cnt, int& kv) {
   kv = 0;
   cnt = 0;
   off = 0;
-  const int NL = c.NL;
+  const int NL = c.NL, x = c.xcd, r = c.rk;
   if (run == 0) {
-    if (c.owner >= 0) {
-      cnt = 1;
-      off = (unsigned)c.owner * TILE_BYTES;
+    cnt = 2;
+    off = (unsigned)(2 * r) * TILE_BYTES;
+    return;
+  }
+  if (run == 1 + RUNS_PER_LAYER * NL) {
+    if (is_vel(c)) {
+      cnt = 64;
+      off = (unsigned)(w_out(NL) * 2ull);
     }
     return;
   }
-  if (run == 1 + 8 * NL) {
-    if (c.out_nt >= 0) {
-      cnt = 32;
-      off = (unsigned)((w_out(NL) + (unsigned long long)c.out_nt * KT_D * TILE_ELEMS) * 2ull);
-    }
-    return;
-  }
-  const int l = (run - 1) / 8, u = (run - 1) % 8;
+  const int l = (run - 1) / RUNS_PER_LAYER, u = (run - 1) % RUNS_PER_LAYER;
   const unsigned long long lo = (unsigned long long)l * W_LAYER;
   if (u == 0) {
-    if (c.qkv0 >= 0) {
+    if (is_qkv(c)) {
+      const int i = r - R_QKV;
+      const int nt0 = i < 8 ? 16 * x + 2 * i : (i == 8 ? 16 * H + 2 * x : 16 * (H + 1) + 2 * x);
       cnt = 64;
-      off = (unsigned)((W_QKV0 + lo + (unsigned long long)c.qkv0 * KT_D * TILE_ELEMS) * 2ull);
+      off = (unsigned)((W_QKV0 + lo + (unsigned long long)nt0 * KT_D * TILE_ELEMS) * 2ull);
     }
   } else if (u == 1) {
-    if (c.attn_c >= 0 && c.attn_c < c.nc) {
+    if (r < c.nc) {
       cnt = 64;
       kv = 1;
-      off = (unsigned)((l * c.nc + c.attn_c) * 64) * TILE_BYTES;
+      off = (unsigned)((l * c.nc + r) * 64) * TILE_BYTES;
     }
-  } else if (u == 2) {
-    if (c.owner >= 0) {
-      cnt = 64;
-      off = (unsigned)((W_O0 + lo + (unsigned long long)c.owner * KT_HD * TILE_ELEMS) * 2ull);
+  } else if (u <= 5) {
+    if (is_o(c)) {
+      const int nt = 4 * (r - R_O) + (u - 2);
+      cnt = 8;
+      off = (unsigned)((W_O0 + lo + ((unsigned long long)nt * KT_HD + 8 * x) * TILE_ELEMS) * 2ull);
     }
-  } else if (u == 3) {
+  } else if (u == 6) {
     cnt = 64;
-    off = (unsigned)((W_GU0 + lo + (unsigned long long)(2 * blockIdx.x) * KT_D * TILE_ELEMS) * 2ull);
+    off = (unsigned)((W_GU0 + lo + (unsigned long long)(64 * x + 2 * r) * KT_D * TILE_ELEMS) * 2ull);
   } else {
-    const int t = u - 4;
-    const int kq = (int)blockIdx.x / DN_NQ, nqd = (int)blockIdx.x % DN_NQ;
-    cnt = 8;
-    off = (unsigned)((W_DN0 + lo + ((unsigned long long)(4 * nqd + t) * KT_F + 8 * kq) * TILE_ELEMS) * 2ull);
+    const int nt = 2 * r + (u - 7);
+    cnt = 16;
+    off = (unsigned)((W_DN0 + lo + ((unsigned long long)nt * KT_F + 16 * x) * TILE_ELEMS) * 2ull);
   }
 }
 
 // next (position, byte offset, source) of loader q; false at the end
 __device__ inline bool gen_next(const Ctx& c, Gen& s, int q, unsigned& pos, unsigned& off, int& kv) {
-  const int runs_per_step = 2 + 8 * c.NL;
+  const int runs_per_step = 2 + RUNS_PER_LAYER * c.NL;
   while (s.j >= s.cnt) {
     s.pos0 += (unsigned)s.cnt;
     s.run += 1;
@@ -1079,8 +1199,7 @@ __device__ inline bool gen_next(const Ctx& c, Gen& s, int q, unsigned& pos, unsi
 // bytes to M0 + 16 * lane).  Issued from inline assembly so the compiler does
 // not guard every later LDS access with a wait for all outstanding loads; the
 // loader waits for its own tiles with explicit vmcnt waits instead.  Weight
-// tiles carry the streaming hint; prefix K/V tiles do not, so the other heads'
-// workgroups on the same XCD find them in L2.
+// tiles carry the streaming hint; prefix K/V tiles do not.
 __device__ inline void dma_tile(u32x4 rs, unsigned voff, unsigned soff, unsigned lds, bool stream) {
   if (stream)
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds" ::"s"(lds), "v"(voff), "s"(rs),
@@ -1097,7 +1216,8 @@ __device__ inline u32x4 rsrc_words(const void* p, unsigned bytes) {
   return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
-constexpr unsigned LOAD_DEPTH = 24;  // tiles in flight per loader wave (16 measured 2% slower; 28, 32 the same)
+constexpr unsigned LOAD_DEPTH = 12;  // tiles in flight per loader wave (24 measured 3% slower: the tile
+                                     // loads crowd the compute waves' exchange loads; 4 and 8 the same as 12)
 
 // Loader waves wait on LDS only: a global load in their wait loop would make
 // the next use of any loaded register wait for the whole batch of tile loads
@@ -1148,7 +1268,7 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
       dma_tile(WR, (unsigned)c.lane * 16u, off, lds, true);
     ++issued;
     if (issued > LOAD_DEPTH) {
-      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
       if (c.lane == 0) lds_store(&c.sh->ready[q], issued - LOAD_DEPTH);
     }
   }
@@ -1177,21 +1297,20 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
   c.dt = a.dt;
   c.eps = a.eps;
   c.tl = a.tl;
+  c.xcd = xcc_id();
+  c.rk = (int)(blockIdx.x / NX);
   if (threadIdx.x < 32) ((unsigned*)&sh)[threadIdx.x] = 0u;
   c.X = rsrc(a.arena, a.arena_bytes);
   c.seq = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(c.X, AUX0 + AUX_SEQ, 0, SC1));
-  c.tagbase = c.seq * exchanges_per_decision(c.S, c.NL);
   c.L = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b32(c.X, AUX0 + AUX_LENS, 0, 0));
-  set_roles(c, (int)blockIdx.x);
   c.crow = c.row < c.R ? c.row : c.R - 1;
   // stream layout of this workgroup (must match run_params)
-  c.n_in = c.owner >= 0 ? 1u : 0u;
-  c.o_attn = c.qkv0 >= 0 ? 64u : 0u;
-  c.o_o = c.o_attn + ((c.attn_c >= 0 && c.attn_c < c.nc) ? 64u : 0u);
-  c.o_gu = c.o_o + (c.owner >= 0 ? 64u : 0u);
+  c.o_att = is_qkv(c) ? 64u : 0u;
+  c.o_o = c.o_att + (c.rk < c.nc ? 64u : 0u);
+  c.o_gu = c.o_o + (is_o(c) ? 32u : 0u);
   c.o_dn = c.o_gu + 64u;
   c.n_layer = c.o_dn + 32u;
-  c.n_step = c.n_in + (unsigned)c.NL * c.n_layer + (c.out_nt >= 0 ? 32u : 0u);
+  c.n_step = 2u + (unsigned)c.NL * c.n_layer + (is_vel(c) ? 64u : 0u);
   __syncthreads();
 
   if (c.wave >= NCOMPUTE) {
@@ -1199,52 +1318,78 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
     if (c.wave == NCOMPUTE) tl_mark(c, timeline_events(c.S, c.NL) - 1);
     return;
   }
-  f32x4 hreg = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 xreg = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (c.out_nt >= 0 && c.wave == 0 && c.row < c.R) {
-    const u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(
-        c.X, AUX0 + AUX_X + (unsigned)((c.row * A + 16 * c.out_nt + 4 * c.g) * 4), 0, 0);
+  f32x4 h[2], x[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xreg[i] = as_f(xv[i]);
+  for (int t = 0; t < 2; ++t) {
+    h[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    x[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (is_vel(c) && c.wave == 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(
+          c.X, AUX0 + AUX_X + (unsigned)((c.crow * A + 16 * t + 4 * c.g) * 4), 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[t][e] = as_f(xv[e]);
+    }
   }
   const bool tl = c.wave == 0;
-  const bool attends = c.attn_c >= 0;
-  const bool action_chunk = c.attn_c == c.nc;
+  const bool attends = c.rk <= c.nc;
+  const bool action_chunk = c.rk == c.nc;
   if (tl) tl_mark(c, 0);
   for (int k = 0; k < c.S; ++k) {
-    const int e0 = 1 + k * (2 + 7 * c.NL);
-    ph_in(c, k, hreg);
+    const int e0 = 1 + k * (2 + PHASES_PER_LAYER * c.NL);
+    ph_in(c, k, h);
     if (tl) tl_mark(c, e0);
     for (int l = 0; l < c.NL; ++l) {
-      const int el = e0 + 1 + 7 * l;
+      const int el = e0 + 1 + PHASES_PER_LAYER * l;
       ph_qkv(c, k, l);
       if (tl) tl_mark(c, el);
-      if (attends) {
-        if (action_chunk)
-          ph_attn_action(c, k, l);
-        else
-          ph_attn_prefix(c, k, l);
-      }
+      // two separate tests: as one if/else the compiler's uniformity analysis loses track of the
+      // context's scalar fields after the join and cannot build the kernel
+      if (attends && !action_chunk) ph_attn_prefix(c, k, l);
+      if (action_chunk) ph_attn_action(c, k, l);
       if (tl) tl_mark(c, el + 1);
-      ph_comb(c, k, l);
+      ph_merge(c, k, l);
       if (tl) tl_mark(c, el + 2);
-      ph_o(c, k, l, hreg);
+      ph_o(c, k, l);
       if (tl) tl_mark(c, el + 3);
-      ph_gu(c, k, l);
+      ph_own<X_OP, X_N2, X_SS2>(c, k, 2 * l + 1, use_layer(c, k, l), use_layer(c, k, l), h);
       if (tl) tl_mark(c, el + 4);
-      ph_down(c, k, l);
+      ph_gu(c, k, l);
       if (tl) tl_mark(c, el + 5);
-      ph_owner2(c, k, l, hreg);
+      ph_down(c, k, l);
       if (tl) tl_mark(c, el + 6);
+      ph_own<X_DP, X_N, X_SS>(c, k, 2 * (l + 1), use_layer(c, k, l), use_norm(c, k, l + 1), h);
+      if (tl) tl_mark(c, el + 7);
     }
-    ph_out(c, k, xreg);
-    if (tl) tl_mark(c, e0 + 1 + 7 * c.NL);
+    ph_vel(c, k, x);
+    if (tl) tl_mark(c, e0 + 1 + PHASES_PER_LAYER * c.NL);
   }
   if (tl) tl_mark(c, timeline_events(c.S, c.NL) - 2);
 }
 
-__global__ void k_decide_advance(unsigned* seq) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) seq[0] = seq[0] + 1u;
+// After a decision (one block): advances the decision counter.  If a wait of
+// the decision gave up, its words may be half written: the block clears the
+// exchange words, starts the counter over at 0 and clears the status, and
+// raises the failure flag the host reads; otherwise it lowers the flag.  The
+// clear only runs after a failed decision.
+constexpr int ADV_THREADS = 1024;
+__global__ __launch_bounds__(ADV_THREADS) void k_decide_advance(unsigned char* arena) {
+  unsigned* aux = (unsigned*)(arena + AUX0);
+  const unsigned st = aux[AUX_STATUS / 4];
+  const unsigned sq = aux[AUX_SEQ / 4];
+  const bool failed = st != 0u && st == sq + 1u;
+  if (failed) {
+    u32x4* ex = (u32x4*)arena;
+    for (unsigned i = threadIdx.x; i < EX_BYTES / 16u; i += ADV_THREADS) ex[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    aux[AUX_SEQ / 4] = failed ? 0u : sq + 1u;
+    if (failed) aux[AUX_STATUS / 4] = 0u;
+    aux[AUX_FAILED / 4] = failed ? 1u : 0u;
+  }
 }
 
 static hipError_t allow_ring_lds() {
@@ -1265,6 +1410,46 @@ hipError_t decide_occupancy(int* blocks_per_cu) {
                                                        RING * TILE_BYTES);
 }
 
+// records the XCD (HW_REG_XCC_ID) each workgroup runs on
+__global__ void k_placement(unsigned* out) {
+  if (threadIdx.x == 0) {
+    unsigned v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    out[blockIdx.x] = v & 15u;
+  }
+}
+
+// true if workgroup b ran on XCD (b + o) mod 8 for one offset o and every b
+static bool round_robin(const unsigned* xcc) {
+  const unsigned o = (xcc[0] + NX) % NX;
+  for (int b = 0; b < G; ++b)
+    if (xcc[b] >= (unsigned)NX || (xcc[b] + (unsigned)(NX * G) - (unsigned)b) % NX != o) return false;
+  return true;
+}
+
+hipError_t decide_placement(bool* ok) {
+  static int cached = -1;  // -1 not yet probed, 0 no, 1 yes
+  if (cached < 0) {
+    unsigned* d = nullptr;
+    hipError_t e = hipMalloc((void**)&d, G * sizeof(unsigned));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_placement, dim3(G), dim3(64), 0, 0, d);
+    unsigned hbuf[G];
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpy(hbuf, d, sizeof(hbuf), hipMemcpyDeviceToHost);
+    (void)hipFree(d);
+    if (e != hipSuccess) return e;
+    cached = round_robin(hbuf) ? 1 : 0;
+    if (std::getenv("PHX_VERBOSE")) {
+      std::fprintf(stderr, "phx: placement probe, XCD of workgroups 0..15:");
+      for (int b = 0; b < 16; ++b) std::fprintf(stderr, " %u", hbuf[b]);
+      std::fprintf(stderr, "\n");
+    }
+  }
+  *ok = cached == 1;
+  return hipSuccess;
+}
+
 hipError_t launch_decide(const Args& a, hipStream_t s) {
   hipError_t e = allow_ring_lds();
   if (e != hipSuccess) return e;
@@ -1273,10 +1458,9 @@ hipError_t launch_decide(const Args& a, hipStream_t s) {
 }
 
 hipError_t launch_decide_advance(void* arena, hipStream_t s) {
-  hipLaunchKernelGGL(k_decide_advance, dim3(1), dim3(64), 0, s, (unsigned*)((char*)arena + AUX0 + AUX_SEQ));
+  hipLaunchKernelGGL(k_decide_advance, dim3(1), dim3(ADV_THREADS), 0, s, (unsigned char*)arena);
   return hipGetLastError();
 }
-
 // ------------------------------------------------------------ set-up kernels
 
 __device__ inline int colmap_dev(int kind, int param, int n) {

@@ -22,6 +22,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdlib>
 #include <string>
 #include <algorithm>
 #include <vector>
@@ -85,6 +86,7 @@ struct TokNode {
   float eps = 0.f;
   void* dst = nullptr;
   int cols = 0;
+  int split = 0;  // TOP_NORM: write paired rows
 };
 
 GemmPlan make_plan(int K, int N, int target_wgs) {
@@ -114,6 +116,8 @@ bool is_device_pointer(const void* p) {
 
 struct phx_expert {
   phx_expert_config cfg{};
+  // large-token plan: the MLP's two GEMMs take paired (hi + lo) bf16 activation rows
+  bool pair_act = false;
   int dtype = 1;
   size_t esz = 2;
   int BM = 0, MT = 1, NTD = 0, ss_ld = 0, Ctot = 0, SMAX = 0, GMP = 0, QT = 1, NN = 0;
@@ -159,8 +163,6 @@ struct phx_expert {
   void* arena = nullptr;      // exchange words, then the auxiliary tables (dec::AUX0)
   void* kvt = nullptr;
   int n_chunks = 0;
-  unsigned seq_host = 0;      // decisions launched since the exchange words were last cleared
-  unsigned seq_limit = 0;     // clear them before the tag space wraps
   // large-token plan (a chunk of many rows, or the DiT-style block)
   bool tokens = false;
   bool batched = false;       // the plan for a batch of requests: large-token GEMMs, per-request caches
@@ -414,7 +416,21 @@ bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop
   // the decision kernel's workgroups wait on each other, so all G of them must be resident at once:
   // one per compute unit, which its LDS ring and register budget have to allow
   int per_cu = 0;
-  if (dec::decide_occupancy(&per_cu) != hipSuccess || per_cu < 1) return false;
+  const hipError_t eo = dec::decide_occupancy(&per_cu);
+  // its ranks inside an XCD need the workgroups dealt to the XCDs round-robin (probed once per process)
+  bool placed = false;
+  const hipError_t ep = eo == hipSuccess && per_cu >= 1 ? dec::decide_placement(&placed) : hipSuccess;
+  if (std::getenv("PHX_VERBOSE"))
+    std::fprintf(stderr, "phx: decision kernel occupancy %d per CU (%s), placement %s (%s)\n", per_cu,
+                 hipGetErrorString(eo), placed ? "round-robin" : "other", hipGetErrorString(ep));
+  if (eo != hipSuccess || per_cu < 1) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (ep != hipSuccess || !placed) {
+    (void)hipGetLastError();
+    return false;
+  }
   return true;
 }
 
@@ -498,9 +514,6 @@ int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t 
   a.n_chunks = h->n_chunks;
   a.dt = c.dt;
   a.eps = c.rms_eps;
-  const unsigned expd = dec::exchanges_per_decision(S, NL);
-  h->seq_limit = (unsigned)((0xffffffffull / expd) - 2);
-  h->seq_host = 0;
 
   // diagnostics node list: the decision kernel (with its tag advance)
   h->node_list.clear();
@@ -554,7 +567,8 @@ int launch_tok(phx_expert* h, const TokNode& nd, hipStream_t s) {
       PHX_HIP(tok::launch_tcvt(nd.src, nd.dst, M, h->Mp, nd.cols, s));
       break;
     case TOP_NORM:
-      PHX_HIP(tok::launch_tnorm(nd.norm_kind, nd.src, nd.scale, nd.shift, nd.eps, nd.dst, M, h->Mp, nd.cols, s));
+      PHX_HIP(tok::launch_tnorm(nd.norm_kind, nd.src, nd.scale, nd.shift, nd.eps, nd.dst, M, h->Mp, nd.cols,
+                                nd.split, s));
       break;
     case TOP_GEMM:
       PHX_HIP(tok::launch_tgemm(nd.epi, nd.g, s));
@@ -596,25 +610,32 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
   const int NL = c.layers, Dh = c.head_dim;
   const int HD = H * Dh, NQKV = (H + 2 * KVH) * Dh, kvd = KVH * Dh;
   const int Mp = h->Mp;
+  const int pm = h->pair_act ? 1 : 0;  // QKV, gate/up and down take paired activation rows
   h->tnodes.clear();
   auto name_of = [](TokNode& nd, const char* name) { std::snprintf(nd.name, sizeof(nd.name), "%s", name); };
+  // pair: bit 0 = the activation rows are paired (hi + lo), bit 1 = the GELU/GeGLU output is written paired
   auto gemm = [&](int kind, int k, int l, int epi, const void* a, size_t w_off, int K, int N, void* out, int ldo,
-                  const float* gate, const char* name) {
+                  const float* gate, const char* name, int pair = 0) {
     TokNode nd{};
     nd.kind = kind; nd.step = k; nd.layer = l; nd.op = TOP_GEMM; nd.epi = epi;
     tok::GemmT& g = nd.g;
     g.a = a; g.w = (const char*)h->wt + w_off * 2; g.out = out; g.gate = gate; g.rope = h->rope;
-    g.rot_cols = dit ? 0 : (H + KVH) * Dh; g.dt = c.dt; g.M = M; g.Mp = Mp; g.K = K; g.N = N; g.ldo = ldo;
+    g.rot_cols = dit ? 0 : (H + KVH) * Dh; g.dt = c.dt; g.M = M; g.Mp = Mp; g.N = N;
+    g.wsh = pair & 1;
+    g.K = K << g.wsh;
+    g.osplit = (pair >> 1) & 1;
+    g.ldo = ldo << g.osplit;
     tok::plan_gemm(g, h->n_cu);
-    std::snprintf(nd.name, sizeof(nd.name), "%s %s/%d", name, tok::tile_name(g.tile), g.splits);
-    const int out_cols = epi == tok::EP_GEGLU ? N / 2 : N;
+    std::snprintf(nd.name, sizeof(nd.name), "%s %s/%d%s", name, tok::tile_name(g.tile), g.splits,
+                  g.wsh ? " pair" : "");
+    const int out_cols = (epi == tok::EP_GEGLU ? N / 2 : N) << g.osplit;
     const int out_esz = (epi == tok::EP_RESID || epi == tok::EP_EULER || epi == tok::EP_F32) ? 4 : 2;
     const uint64_t rmw = (epi == tok::EP_RESID || epi == tok::EP_EULER) ? 2 : 1;
-    nd.bytes = (uint64_t)K * N * 2 + (uint64_t)M * K * 2 + rmw * (uint64_t)M * out_cols * out_esz +
+    nd.bytes = (uint64_t)K * N * 2 + (uint64_t)M * g.K * 2 + rmw * (uint64_t)M * out_cols * out_esz +
                (gate ? (uint64_t)N * 4 : 0);
     h->tnodes.push_back(nd);
   };
-  auto norm = [&](int k, int l, int kind, const float* scale, const float* shift, const char* name) {
+  auto norm = [&](int k, int l, int kind, const float* scale, const float* shift, const char* name, int split = 0) {
     // right after a residual GEMM whose k splits end in a reduction launch, the norm runs in that launch
     if (!h->tnodes.empty()) {
       TokNode& prev = h->tnodes.back();
@@ -622,8 +643,8 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
       if (prev.op == TOP_GEMM && prev.epi == tok::EP_RESID && pg.splits > 1 && pg.out == h->h && pg.N == D &&
           pg.ldo == D && D <= 256 * 16) {
         pg.nrm_on = 1; pg.nrm_kind = kind; pg.nrm_scale = scale; pg.nrm_shift = shift; pg.nrm_eps = c.rms_eps;
-        pg.nrm_out = h->nb;
-        prev.bytes += (uint64_t)Mp * D * 2 + 2ull * D * 4;
+        pg.nrm_out = h->nb; pg.nrm_split = split;
+        prev.bytes += (uint64_t)Mp * D * 2 * (split ? 2 : 1) + 2ull * D * 4;
         const size_t len = std::strlen(prev.name);
         std::snprintf(prev.name + len, sizeof(prev.name) - len, "+norm");
         return;
@@ -632,8 +653,8 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     TokNode nd{};
     nd.kind = PHX_NODE_ROW_NORM; nd.step = k; nd.layer = l; nd.op = TOP_NORM;
     nd.norm_kind = kind; nd.src = h->h; nd.scale = scale; nd.shift = shift; nd.eps = c.rms_eps; nd.dst = h->nb;
-    nd.cols = D;
-    nd.bytes = (uint64_t)M * D * 4 + (uint64_t)Mp * D * 2 + 2ull * D * 4;
+    nd.cols = D; nd.split = split;
+    nd.bytes = (uint64_t)M * D * 4 + (uint64_t)Mp * D * 2 * (split ? 2 : 1) + 2ull * D * 4;
     name_of(nd, name);
     h->tnodes.push_back(nd);
   };
@@ -642,7 +663,7 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
   auto layer_v = [&](int l) { return (char*)h->tv + (dit ? 0 : (size_t)l * R * kvd * 2); };
   auto qkv = [&](int k, int l, const char* name) {
     gemm(PHX_NODE_QKV, k, l, h->batched ? tok::EP_QKV_CACHE : tok::EP_QKV, h->nb, h->off_qkv[l], D, NQKV, h->qkv,
-         HD, nullptr, name);
+         HD, nullptr, name, pm);
     tok::GemmT& g = h->tnodes.back().g;
     g.kj = layer_k(l); g.vt = layer_v(l); g.lens = dit ? nullptr : h->lens; g.H = H; g.KVH = KVH; g.nj = R / 32;
     g.hd = Dh;
@@ -701,15 +722,15 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
   if (dit) {
     for (int l = 0; l < NL; ++l) {
       const float* mod = h->modtab + (size_t)l * 6 * D;  // shift, scale, gate (attention), then (MLP)
-      norm(0, l, 1, mod + D, mod, "layernorm_attn");
+      norm(0, l, 1, mod + D, mod, "layernorm_attn", pm);
       qkv(0, l, "qkv");
       attention(0, l);
       gemm(PHX_NODE_OUT_PROJ_RESID, 0, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, mod + 2 * D,
            "out_proj_gated_resid");
-      norm(0, l, 1, mod + 4 * D, mod + 3 * D, "layernorm_mlp");
-      gemm(PHX_NODE_GATEUP, 0, l, tok::EP_GELU, h->nb, h->off_gu[l], D, F, h->act, F, nullptr, "up_gelu");
+      norm(0, l, 1, mod + 4 * D, mod + 3 * D, "layernorm_mlp", pm);
+      gemm(PHX_NODE_GATEUP, 0, l, tok::EP_GELU, h->nb, h->off_gu[l], D, F, h->act, F, nullptr, "up_gelu", pm * 3);
       gemm(PHX_NODE_DOWN_PROJ_RESID, 0, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, mod + 5 * D,
-           "down_proj_gated_resid");
+           "down_proj_gated_resid", pm);
     }
     return PHX_OK;
   }
@@ -721,16 +742,17 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     for (int l = 0; l < NL; ++l) {
       const float* m1 = h->modtab + (size_t)(2 * l) * 2 * D;
       const float* m2 = h->modtab + (size_t)(2 * l + 1) * 2 * D;
-      norm(0, l, 0, m1, m1 + D, "rmsnorm_attn");
+      norm(0, l, 0, m1, m1 + D, "rmsnorm_attn", pm);
       qkv(0, l, "qkv_rope");
       if (l + 1 == NL) break;
       attention(0, l);
       gemm(PHX_NODE_OUT_PROJ_RESID, 0, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, nullptr,
            "out_proj_resid");
-      norm(0, l, 0, m2, m2 + D, "rmsnorm_mlp");
-      gemm(PHX_NODE_GATEUP, 0, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu");
+      norm(0, l, 0, m2, m2 + D, "rmsnorm_mlp", pm);
+      gemm(PHX_NODE_GATEUP, 0, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu",
+           pm * 3);
       gemm(PHX_NODE_DOWN_PROJ_RESID, 0, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, nullptr,
-           "down_proj_resid");
+           "down_proj_resid", pm);
     }
     return PHX_OK;
   }
@@ -750,16 +772,17 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     for (int l = 0; l < NL; ++l) {
       const float* m1 = mod_k + (size_t)(2 * l) * 2 * D;
       const float* m2 = mod_k + (size_t)(2 * l + 1) * 2 * D;
-      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn");
+      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn", pm);
       qkv(k, l, "qkv_rope");
       if (l + 1 == NL) break;
       attention(k, l);
       gemm(PHX_NODE_OUT_PROJ_RESID, k, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, nullptr,
            "out_proj_resid");
-      norm(k, l, 0, m2, m2 + D, "rmsnorm_mlp");
-      gemm(PHX_NODE_GATEUP, k, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu");
+      norm(k, l, 0, m2, m2 + D, "rmsnorm_mlp", pm);
+      gemm(PHX_NODE_GATEUP, k, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu",
+           pm * 3);
       gemm(PHX_NODE_DOWN_PROJ_RESID, k, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, nullptr,
-           "down_proj_resid");
+           "down_proj_resid", pm);
     }
     return PHX_OK;
   }
@@ -794,15 +817,16 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     for (int l = 0; l < NL; ++l) {
       const float* m1 = mod_k + (size_t)(2 * l) * 2 * D;
       const float* m2 = mod_k + (size_t)(2 * l + 1) * 2 * D;
-      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn");
+      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn", pm);
       qkv(k, l, "qkv_rope");
       attention(k, l);
       gemm(PHX_NODE_OUT_PROJ_RESID, k, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, nullptr,
            "out_proj_resid");
-      norm(k, l, 0, m2, m2 + D, "rmsnorm_mlp");
-      gemm(PHX_NODE_GATEUP, k, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu");
+      norm(k, l, 0, m2, m2 + D, "rmsnorm_mlp", pm);
+      gemm(PHX_NODE_GATEUP, k, l, tok::EP_GEGLU, h->nb, h->off_gu[l], D, 2 * F, h->act, F, nullptr, "gateup_geglu",
+           pm * 3);
       gemm(PHX_NODE_DOWN_PROJ_RESID, k, l, tok::EP_RESID, h->act, h->off_down[l], F, D, h->h, D, nullptr,
-           "down_proj_resid");
+           "down_proj_resid", pm);
     }
     const float* mf = mod_k + (size_t)(2 * NL) * 2 * D;
     norm(k, -1, 0, mf, mf + D, "rmsnorm_final");
@@ -851,6 +875,11 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   const int HD = H * c.head_dim, kvd = KVH * c.head_dim;
   const int Mp = (M + tok::ROW_PAD - 1) / tok::ROW_PAD * tok::ROW_PAD;
   h->Mp = Mp;
+  // paired activations (the inputs of QKV, gate/up and down: both norms' rows and the MLP activation):
+  // the default of the DiT-style block (its gated MLP branch carries the largest rounding of bf16
+  // activations into the residual stream), of the batched plan and of the prefill (these roundings are
+  // most of what a decision, or an 18-layer cache, accumulates); opt-in for the video-action chunk
+  h->pair_act = !(c.flags & PHX_FLAG_BF16_ACT) && (dit || h->batched || prefill || (c.flags & PHX_FLAG_PAIRED_ACT));
   int rc;
   // modulation: decoder [S][2NL+1][2D] (scale | shift per norm); DiT [NL][6D] at tau0
   // (the decoder gets one more step row, at the end flow time tau0 + S dt, for the history update)
@@ -890,10 +919,10 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   struct Buf { void** p; size_t bytes; const char* what; };
   std::vector<Buf> bufs = {
       {(void**)&h->h, (size_t)Mp * D * 4, "residual rows"},
-      {&h->nb, (size_t)Mp * D * 2, "normalised rows"},
+      {&h->nb, (size_t)Mp * D * 2 * (h->pair_act ? 2 : 1), "normalised rows"},
       {&h->qkv, (size_t)Mp * HD * 2, "query rows"},
       {&h->o, (size_t)Mp * HD * 2, "attention output rows"},
-      {&h->act, (size_t)Mp * F * 2, "MLP activation rows"},
+      {&h->act, (size_t)Mp * F * 2 * (h->pair_act ? 2 : 1), "MLP activation rows"},
   };
   if (h->batched) {
     // the multi-kernel path's per-request caches, lengths, position table and attention partials
@@ -1150,8 +1179,11 @@ int phx_expert_validate_config(const phx_expert_config* c) {
   if (c->weight_dtype != PHX_DTYPE_F32 && c->weight_dtype != PHX_DTYPE_BF16)
     return fail(PHX_E_INVALID, "weight_dtype %d unknown", c->weight_dtype);
   if (c->kv_dtype != c->weight_dtype) return fail(PHX_E_SHAPE, "kv_dtype must equal weight_dtype");
-  if (c->flags & ~(PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL | PHX_FLAG_TIMELINE | PHX_FLAG_WEIGHTS_INT8))
+  if (c->flags & ~(PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL | PHX_FLAG_TIMELINE | PHX_FLAG_WEIGHTS_INT8 |
+                   PHX_FLAG_PAIRED_ACT | PHX_FLAG_BF16_ACT))
     return fail(PHX_E_INVALID, "unknown flags 0x%x", c->flags);
+  if ((c->flags & PHX_FLAG_PAIRED_ACT) && (c->flags & PHX_FLAG_BF16_ACT))
+    return fail(PHX_E_INVALID, "PHX_FLAG_PAIRED_ACT and PHX_FLAG_BF16_ACT exclude each other");
   if ((c->flags & PHX_FLAG_WEIGHTS_INT8) &&
       (c->weight_dtype != PHX_DTYPE_BF16 || c->block_kind != PHX_BLOCK_DECODER || (long long)c->rows * c->batch > 160))
     return fail(PHX_E_SHAPE, "the 8-bit weight tier needs bf16 weights, the decoder block and at most 160 rows");
@@ -1521,12 +1553,6 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
     if (!h->loaded[b]) return fail(PHX_E_STATE, "request %d has no prefix loaded", b);
   hipStream_t s = (hipStream_t)stream;
   const size_t xb = (size_t)h->BM * h->cfg.state_dim * sizeof(float);
-  if (h->persistent && h->seq_host >= h->seq_limit) {
-    // exchange tags would wrap: start the tag space over on cleared buffers
-    PHX_HIP(hipMemsetAsync(h->arena, 0, dec::EX_BYTES, s));
-    PHX_HIP(hipMemsetAsync((char*)h->arena + dec::AUX0, 0, dec::AUX_LENS, s));  // status and counter
-    h->seq_host = 0;
-  }
   // the DiT-style block integrates nothing: its state is the residual stream itself
   float* state = (h->tokens && h->cfg.block_kind == PHX_BLOCK_DIT) ? h->h : h->x;
   PHX_HIP(hipMemcpyAsync(state, noise, xb, hipMemcpyDefault, s));
@@ -1536,7 +1562,6 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
     int rc = enqueue_steps(h, s);
     if (rc) return rc;
   }
-  if (h->persistent) ++h->seq_host;
   PHX_HIP(hipMemcpyAsync(actions, state, xb, hipMemcpyDefault, s));
   g_err.clear();
   return PHX_OK;
@@ -1638,10 +1663,10 @@ int phx_expert_launch_node(phx_expert* h, int32_t node, phx_stream_t stream) {
   if (h->persistent && node == 0) {
     rc = enqueue_persistent(h, (hipStream_t)stream);  // the kernel and its tag advance
     if (rc) return rc;
-    ++h->seq_host;
   } else if (h->persistent) {
-    PHX_HIP(dec::launch_decide_advance(h->arena, (hipStream_t)stream));
-    ++h->seq_host;
+    // the counter advance belongs to the decision kernel it follows (its use counters run without a gap
+    // from one decision to the next), so the diagnostic launch of this node alone does nothing
+    (void)stream;
   } else if (h->tokens) {
     rc = launch_tok(h, h->tnodes[(size_t)node], (hipStream_t)stream);
     if (rc) return rc;
@@ -1657,10 +1682,10 @@ int phx_expert_status(const phx_expert* h, uint32_t* status) {
   if (!h || !status) return fail(PHX_E_INVALID, "NULL argument");
   *status = 0;
   if (!h->persistent) return PHX_OK;
-  uint32_t w[2] = {0, 0};  // failing decision + 1, and the counter (already advanced past the last decision)
-  PHX_HIP(hipMemcpy(w, (const char*)h->arena + dec::AUX0 + dec::AUX_STATUS, 2 * sizeof(uint32_t),
+  uint32_t w = 0;  // set after each decision: 1 if a wait of it gave up
+  PHX_HIP(hipMemcpy(&w, (const char*)h->arena + dec::AUX0 + dec::AUX_FAILED, sizeof(uint32_t),
                     hipMemcpyDeviceToHost));
-  *status = (w[0] != 0 && w[0] == w[1]) ? 1u : 0u;
+  *status = w != 0 ? 1u : 0u;
   return PHX_OK;
 }
 

@@ -34,8 +34,15 @@ enum Epi : int {
                      // [B][KVH][hd][Ctot] at slot lens[b] + i (row r = b * req_rows + i)
 };
 
+// Paired activation rows: an activation a is carried as two bf16 values, hi =
+// bf16(a) and lo = bf16(a - hi), so a GEMM against bf16 weights sums hi * w +
+// lo * w and sees a to about 2^-16 instead of bf16's 2^-8.  A paired row of
+// K columns holds 2K bf16: for each 32-column chunk, its 32 hi values, then
+// its 32 lo values.  To the GEMM that is a plain activation of 2K columns
+// whose k-step s meets weight k-tile s / 2 (wsh = 1).
+
 struct GemmT {
-  const void* a;       // bf16 activations [Mp][K], row-major
+  const void* a;       // bf16 activations [Mp][K], row-major (K = twice the weight rows when wsh = 1)
   const void* w;       // tiled bf16 weights of a [K][N] matrix (16-column x 32-row tiles, n-tile major)
   void* out;           // see Epi
   const float* gate;   // EP_RESID: per-column factor, or nullptr
@@ -50,7 +57,9 @@ struct GemmT {
   void* kc;            // EP_QKV_CACHE: this layer's key cache
   void* vtc;           // EP_QKV_CACHE: this layer's transposed value cache
   float dt;            // EP_EULER
-  int M, Mp, K, N;     // real rows, padded rows, reduction length, output columns (tile order)
+  int M, Mp, K, N;     // real rows, padded rows, activation columns, output columns (tile order)
+  int wsh;             // 1: the activation rows are paired (weight rows K / 2, k-step s uses k-tile s >> 1)
+  int osplit;          // EP_GELU / EP_GEGLU: write the output as paired rows (ldo = 2 x output columns)
   int ldo;             // output row stride in elements
   int tile;            // workgroup tile shape (set by plan_gemm)
   int kern;            // 0: LDS-ring kernel, 1: register-fed kernel (set by plan_gemm)
@@ -59,7 +68,7 @@ struct GemmT {
   // EP_RESID with splits > 1 and N <= 4096: the row norm that follows, fused into the split reduction
   // (out = the residual rows [M][N] f32 with ldo = N): nrm_out bf16 [Mp][N] = norm(row) * (1 + scale) + shift,
   // the rows past M zero; kind 0 RMS, 1 LayerNorm (mean subtracted), as launch_tnorm
-  int nrm_on, nrm_kind;
+  int nrm_on, nrm_kind, nrm_split;  // nrm_split: nrm_out is paired ([Mp][2N])
   const float* nrm_scale;
   const float* nrm_shift;
   float nrm_eps;
@@ -94,9 +103,9 @@ struct AttnT {
 hipError_t prepare_gemm();
 hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s);
 // kind 0: RMS, 1: LayerNorm (mean subtracted); out[r][d] = bf16(norm(h[r])[d] * (1 + scale[d]) + shift[d]) for
-// r < M, zeros for M <= r < Mp
+// r < M, zeros for M <= r < Mp; split: out is paired rows [Mp][2D]
 hipError_t launch_tnorm(int kind, const float* h, const float* scale, const float* shift, float eps, void* out, int M,
-                        int Mp, int D, hipStream_t s);
+                        int Mp, int D, int split, hipStream_t s);
 // out[r][d] = bf16(x[r][d]) for r < M, zeros for M <= r < Mp
 hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStream_t s);
 // Lets the attention kernel use its LDS ring (call once per device, outside graph capture).

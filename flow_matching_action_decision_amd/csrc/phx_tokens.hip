@@ -35,6 +35,29 @@ __device__ inline unsigned short bits(bf16 b) { return __builtin_bit_cast(unsign
 __device__ inline unsigned pack2(float a, float b) {
   return (unsigned)bits((bf16)a) | ((unsigned)bits((bf16)b) << 16);
 }
+
+// Paired rows (see phx_tokens.h): columns c .. c + n - 1 (one 32-column
+// chunk, c a multiple of n) of a paired row get hi = bf16(y) and lo =
+// bf16(y - hi); the difference y - hi is exact in float32.
+__device__ inline void store_pair2(bf16* row, int c, float y0, float y1) {
+  const bf16 h0 = (bf16)y0, h1 = (bf16)y1;
+  bf16* p = row + (c >> 5) * 64 + (c & 31);
+  *(unsigned*)p = (unsigned)bits(h0) | ((unsigned)bits(h1) << 16);
+  *(unsigned*)(p + 32) = pack2(y0 - (float)h0, y1 - (float)h1);
+}
+__device__ inline void store_pair4(bf16* row, int c, const float (&y)[4]) {
+  bf16 hb[4];
+  float lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hb[i] = (bf16)y[i];
+    lo[i] = y[i] - (float)hb[i];
+  }
+  bf16* p = row + (c >> 5) * 64 + (c & 31);
+  *(u32x2*)p = u32x2{(unsigned)bits(hb[0]) | ((unsigned)bits(hb[1]) << 16),
+                     (unsigned)bits(hb[2]) | ((unsigned)bits(hb[3]) << 16)};
+  *(u32x2*)(p + 32) = u32x2{pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+}
 // Hardware base-2 exponential (v_exp_f32, about 1 ulp; results below 2^-126
 // flush to zero, which every use here tolerates: softmax terms that small
 // vanish beside the row sum, and tanh saturates long before).  exp2f would
@@ -165,7 +188,10 @@ __device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const 
     float y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = EPI == EP_GELU ? gelu_tanh(v[i]) : v[i];
-    *(u32x2*)((bf16*)g.out + (size_t)row * g.ldo + nt * 16 + 4 * gq) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+    if (EPI == EP_GELU && g.osplit)
+      store_pair4((bf16*)g.out + (size_t)row * g.ldo, nt * 16 + 4 * gq, y);
+    else
+      *(u32x2*)((bf16*)g.out + (size_t)row * g.ldo + nt * 16 + 4 * gq) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
   } else if constexpr (EPI == EP_QKV) {
     // tile order of a head (query heads, then key heads, then value heads) of
     // hd dims: the values are dims j, j + 1, j + hd/2, j + hd/2 + 1 with
@@ -233,7 +259,11 @@ __device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const 
   } else if constexpr (EPI == EP_GEGLU) {
     // features 8 nt + 2 gq + {0, 1}: gate in v[0], v[1], up in v[2], v[3]
     const int f = 8 * nt + 2 * gq;
-    *(unsigned*)((bf16*)g.out + (size_t)row * g.ldo + f) = pack2(gelu_tanh(v[0]) * v[2], gelu_tanh(v[1]) * v[3]);
+    const float a0 = gelu_tanh(v[0]) * v[2], a1 = gelu_tanh(v[1]) * v[3];
+    if (g.osplit)
+      store_pair2((bf16*)g.out + (size_t)row * g.ldo, f, a0, a1);
+    else
+      *(unsigned*)((bf16*)g.out + (size_t)row * g.ldo + f) = pack2(a0, a1);
   } else {
     float* o = (float*)g.out + (size_t)row * g.ldo + nt * 16 + 4 * gq;
     f32x4 cur = EPI == EP_F32 ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)o;
@@ -271,7 +301,8 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   constexpr int NS = T::NS;
   const unsigned lds0 = (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)smem);
   const u32x4 ra = rsrc_words(g.a, (unsigned)((size_t)g.Mp * g.K * 2));
-  const u32x4 rw = rsrc_words(g.w, (unsigned)((size_t)g.K * g.N * 2));
+  const u32x4 rw = rsrc_words(g.w, (unsigned)(((size_t)g.K >> g.wsh) * g.N * 2));
+  const int KTW = KT >> g.wsh;  // weight k-tiles (activation k-step s meets weight k-tile s >> wsh)
   // this wave's activation fragments: m-tiles wave * WM/4 + i; lane: row 16 m + lane % 16, k chunk lane / 16
   unsigned voa[WM / 4];
 #pragma unroll
@@ -292,7 +323,7 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
 #pragma unroll
       for (int n = 0; n < WN; ++n)
         dma_frag(sk + (unsigned)((WM + wave * WN + n) * 1024), vow, rw,
-                 (unsigned)(((size_t)(nt0 + n) * KT + kt) * 1024));
+                 (unsigned)(((size_t)(nt0 + n) * KTW + (kt >> g.wsh)) * 1024));
     }
   };
   f32x4 acc[WN][WM];
@@ -357,8 +388,9 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
   // reused for an address (which would force a wait for every load).
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.a), (short)0, (int)((size_t)g.Mp * g.K * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rw =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.w), (short)0, (int)((size_t)g.K * g.N * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(g.w), (short)0, (int)(((size_t)g.K >> g.wsh) * g.N * 2), 0x00020000);
+  const int wsh = __builtin_amdgcn_readfirstlane(g.wsh);
   // activation pieces of this thread: rows p*64 + tid/4, k chunk tid%4
   int avo[T::AP], aslot[T::AP];
 #pragma unroll
@@ -368,14 +400,17 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
     aslot[p] = (r >> 4) * 64 + (r & 15) + 16 * (tid & 3);
   }
   const int wvo = lane * 16;
+  // weight k-tile of activation k-step kb + s is (kb + s) >> wsh (paired activation rows: each weight
+  // fragment meets the hi and then the lo k-step; kb and the unrolled k-step groups are even)
   int wso[WN];
 #pragma unroll
-  for (int n = 0; n < WN; ++n) wso[n] = (int)(((size_t)(nt0 + n) * KT + kb) * 1024);
+  for (int n = 0; n < WN; ++n) wso[n] = (int)((size_t)(nt0 + n) * (KT >> wsh) * 1024);
   auto ld_a = [&](int p, int s) -> u32x4 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, avo[p], (kb + s) * 64, 0));
   };
   auto ld_w = [&](int n, int s) -> u32x4 {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wvo, wso[n] + s * 1024, 0));
+    return __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(rw, wvo, wso[n] + ((kb + s) >> wsh) * 1024, 0));
   };
   f32x4 acc[WN][WM];
 #pragma unroll
@@ -476,9 +511,10 @@ __global__ __launch_bounds__(256) void k_tsplit_resid_norm(GemmT g) {
   __shared__ float red[8];
   const int row = blockIdx.x, t = threadIdx.x;
   const int N = g.N;
-  bf16* o = (bf16*)g.nrm_out + (size_t)row * N;
+  const int W = g.nrm_split ? 2 * N : N;  // bf16 elements of a norm row
+  bf16* o = (bf16*)g.nrm_out + (size_t)row * W;
   if (row >= g.M) {
-    for (int d = t; d < N; d += 256) o[d] = (bf16)0.0f;
+    for (int d = t; d < W; d += 256) o[d] = (bf16)0.0f;
     return;
   }
   float* hr = (float*)g.out + (size_t)row * g.ldo;
@@ -547,7 +583,10 @@ __global__ __launch_bounds__(256) void k_tsplit_resid_norm(GemmT g) {
       float y[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[i] = (v[q][i] - mean) * inv * (1.0f + sc[i]) + sh[i];
-      *(u32x2*)(o + c) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+      if (g.nrm_split)
+        store_pair4(o, c, y);
+      else
+        *(u32x2*)(o + c) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
     }
   }
 }
@@ -668,6 +707,10 @@ hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
                    !g.nrm_shift || (g.nrm_kind != 0 && g.nrm_kind != 1)))
     return hipErrorInvalidValue;
   if ((size_t)g.Mp * g.K * 2 >= (1ull << 32) || (size_t)g.K * g.N * 2 >= (1ull << 32)) return hipErrorInvalidValue;
+  // paired activations: every k split holds whole (hi, lo) k-step pairs
+  if (g.wsh != 0 && (g.wsh != 1 || ((g.K / 32) / g.splits) % 2)) return hipErrorInvalidValue;
+  if (g.osplit && (epi != EP_GELU && epi != EP_GEGLU)) return hipErrorInvalidValue;
+  if (g.nrm_on && g.nrm_split && g.N % 32) return hipErrorInvalidValue;
   switch (epi) {
     case EP_BF16: return launch_tgemm_e<EP_BF16>(g, s);
     case EP_QKV: return launch_tgemm_e<EP_QKV>(g, s);
@@ -686,15 +729,16 @@ hipError_t launch_tgemm(int epi, const GemmT& g, hipStream_t s) {
 // one workgroup per row; D <= 256 * 16
 __global__ __launch_bounds__(256) void k_tnorm(int kind, const float* __restrict__ h, const float* __restrict__ scale,
                                                const float* __restrict__ shift, float eps, bf16* __restrict__ out,
-                                               int M, int D) {
+                                               int M, int D, int split) {
   // thread t owns the 4-column groups t, t + 256, t + 512, t + 768 of its row (16-byte loads), the same
   // columns and sums as the norm fused into the split reduction (k_tsplit_resid_norm)
   constexpr int GR = 4;
   __shared__ float red[8];
   const int row = blockIdx.x, t = threadIdx.x;
-  bf16* o = out + (size_t)row * D;
+  const int W = split ? 2 * D : D;  // bf16 elements of an output row
+  bf16* o = out + (size_t)row * W;
   if (row >= M) {
-    for (int d = t; d < D; d += 256) o[d] = (bf16)0.0f;
+    for (int d = t; d < W; d += 256) o[d] = (bf16)0.0f;
     return;
   }
   const float* x = h + (size_t)row * D;
@@ -736,15 +780,18 @@ __global__ __launch_bounds__(256) void k_tnorm(int kind, const float* __restrict
       float y[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[i] = (v[q][i] - mean) * inv * (1.0f + sc[i]) + sh[i];
-      *(u32x2*)(o + c) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+      if (split)
+        store_pair4(o, c, y);
+      else
+        *(u32x2*)(o + c) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
     }
   }
 }
 
 hipError_t launch_tnorm(int kind, const float* h, const float* scale, const float* shift, float eps, void* out, int M,
-                        int Mp, int D, hipStream_t s) {
-  if (D > 256 * 16 || D % 4 || M > Mp) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_tnorm, dim3(Mp), dim3(256), 0, s, kind, h, scale, shift, eps, (bf16*)out, M, D);
+                        int Mp, int D, int split, hipStream_t s) {
+  if (D > 256 * 16 || D % 4 || M > Mp || (split && D % 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tnorm, dim3(Mp), dim3(256), 0, s, kind, h, scale, shift, eps, (bf16*)out, M, D, split);
   return hipGetLastError();
 }
 

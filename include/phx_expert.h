@@ -76,6 +76,18 @@ extern "C" {
                                      graph (see phx_expert_weight_codes) */
 #define PHX_FLAG_TIMELINE 4u   /* persistent kernel: record a per-workgroup phase timeline (see
                                   phx_expert_timeline) */
+#define PHX_FLAG_PAIRED_ACT 16u  /* large-token plans (more than 160 rows, the DiT-style block, the prefill):
+                                    the inputs of the QKV, gate/up and down GEMMs (both norms' rows and the
+                                    MLP activation) are carried as pairs of bf16 values, hi = bf16(a) and
+                                    lo = bf16(a - hi), and each GEMM sums hi * w + lo * w against the bf16
+                                    weights, so it sees its activation to ~2^-16 instead of 2^-8 at twice
+                                    the matrix-core work (the attention output stays bf16).  The default of
+                                    PHX_BLOCK_DIT, of PHX_BLOCK_PREFILL and of the batched plan (bf16, 65-160
+                                    rows: the rollout batch): their results accumulate the most bf16
+                                    rounding; opt-in for the large-token decoder plan (the video-action
+                                    chunk) */
+#define PHX_FLAG_BF16_ACT 32u  /* large-token plans: plain bf16 GEMM activations everywhere (faster; more
+                                  rounding in the DiT-style step, the prefill and the rollout batch) */
 
 /* block kinds */
 #define PHX_BLOCK_DECODER 0  /* adaptive RMSNorm (scale, shift), RoPE, GeGLU MLP, residual adds; in- and
@@ -300,8 +312,10 @@ PHX_API int phx_expert_kernels_per_decision(const phx_expert* h, int* count);
 #define PHX_NODE_DOWN_PROJ_RESID 7   /* h += a . W_down */
 #define PHX_NODE_NORM_OUT_EULER 8    /* final adaptive RMSNorm, velocity projection, x += dt * v */
 #define PHX_NODE_DECISION 9          /* the persistent kernel that runs a whole decision (launching it
-                                        diagnostically also advances the exchange tags) */
-#define PHX_NODE_TAG_ADVANCE 10      /* advances the persistent kernel's exchange tags */
+                                        diagnostically also advances the decision counter) */
+#define PHX_NODE_TAG_ADVANCE 10      /* advances the persistent kernel's decision counter (its exchange
+                                        generations); it belongs to the decision it follows, so
+                                        phx_expert_launch_node does nothing for it */
 /* launches of the large-token plan (more than 160 rows, or the DiT-style block) */
 #define PHX_NODE_ROW_NORM 11         /* adaptive RMSNorm or LayerNorm of the residual rows into bf16 rows */
 #define PHX_NODE_QKV 12              /* QKV projection of the normalised rows (RoPE on q and k in the decoder) */
@@ -351,11 +365,12 @@ PHX_API int phx_expert_status(const phx_expert* h, uint32_t* status);
  * PHX_FLAG_TIMELINE (synchronous).  The persistent kernel is one launch, so
  * a profiler sees one kernel; this records, per workgroup, the 100 MHz
  * real-time counter (low 32 bits) when its compute waves finished each phase:
- * out[wg * E + e] with E = 3 + steps * (2 + 7 * layers) events: e = 0 start;
- * for step k, base b = 1 + k * (2 + 7 * layers): b input projection, then
- * b + 1 + 7 l + {0 qkv, 1 attention, 2 combine, 3 out projection, 4 gate/up,
- * 5 down, 6 residual add} for layer l, then b + 1 + 7 * layers velocity head;
- * E - 2 compute end, E - 1 weight streaming end.  256 workgroups.
+ * out[wg * E + e] with E = 3 + steps * (2 + 8 * layers) events: e = 0 start;
+ * for step k, base b = 1 + k * (2 + 8 * layers): b input projection, then
+ * b + 1 + 8 l + {0 qkv, 1 attention, 2 merge, 3 out projection, 4 its
+ * all-reduce across XCDs, 5 gate/up, 6 down, 7 its all-reduce} for layer l,
+ * then b + 1 + 8 * layers velocity head; E - 2 compute end, E - 1 weight
+ * streaming end.  256 workgroups (workgroup b is rank b / 8 on XCD b % 8).
  * If out is NULL or capacity is too small, *count receives the size needed
  * and PHX_E_SHAPE is returned.  Returns PHX_OK, PHX_E_INVALID, PHX_E_STATE
  * (no timeline), PHX_E_SHAPE or PHX_E_HIP.

@@ -13,16 +13,14 @@ import phx_inputs
 # activations with fp32 accumulation vs the double-precision oracle
 TOL_BF16 = dict(max_abs=2e-2, rel_l2=1e-2)
 TOL_F32 = dict(max_abs=1e-4, rel_l2=1e-4)
-# The DiT-style step returns the residual stream itself: 1.6M values of
-# standard deviation ~1.3 in the one-block full-width case (12.7M at full
-# size) instead of a few hundred actions.  Each GEMM whose activation operand
-# is rounded to bf16 (RNE, unit roundoff 2^-8) carries a relative error of
-# about 2^-8/sqrt(3) = 2.3e-3 of its result, so one block's MLP branch is off
-# by ~3e-3 of its size and the output by ~2e-3 (rel-L2); the largest of 1.6M
-# such errors lands near 11 of their standard deviations, ~2.5e-2.  The bar
-# keeps the rel-L2 limit and allows max-abs 5e-2, with every row's cosine
-# similarity at least 0.9999 so that no row can hide a local mistake.
-TOL_TOKENS = dict(max_abs=5e-2, rel_l2=1e-2, worst_row_cos=0.9999)
+# The large-token plans return many more values than the expert's actions
+# (the DiT-style step returns its residual stream: 12.7M values of standard
+# deviation ~1.3 at full size): they are held to the same bar, plus every
+# row's cosine similarity, so that no row can hide a local mistake.  The
+# DiT-style block meets it with paired GEMM activations (its default), which
+# take the bf16 rounding of the QKV, gate/up and down inputs out of the
+# residual stream.
+TOL_TOKENS = dict(max_abs=2e-2, rel_l2=1e-2, worst_row_cos=0.9999)
 
 
 def say(msg: str):
@@ -77,6 +75,25 @@ def assert_close(gpu, ref, tol, what=""):
     assert m["rel_l2"] <= tol["rel_l2"], f"{what}: rel_l2 {m['rel_l2']:.3e} > {tol['rel_l2']}"
     if "worst_row_cos" in tol:
         assert m["cos_worst_row"] >= tol["worst_row_cos"], f"{what}: worst row cosine {m['cos_worst_row']:.6f}"
+    return m
+
+
+def assert_close_bf16_storage(gpu, ref, tol, what=""):
+    """The bar for values the interface stores in bf16 (the prefill's key and
+    value cache): rounding a value r to bf16 (round to nearest even) moves it
+    by up to half an ulp, 2^-9 |r|, so an exact computation stored in bf16
+    already differs from the oracle's double by that much; the max-abs bar
+    applies to what remains, |g - r| - 2^-9 |r|.  rel-L2 and the row cosine
+    are taken as they are."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    excess = float(np.max(np.abs(g - r) - np.abs(r) * 2.0 ** -9))
+    m = compare(gpu, ref)
+    say(f"  {what}: max_abs={m['max_abs']:.3e} beyond storage half-ulp={excess:.3e} rel_l2={m['rel_l2']:.3e} "
+        f"worst_row_cos={m['cos_worst_row']:.6f}")
+    assert m["finite"], f"{what}: non-finite output"
+    assert excess <= tol["max_abs"], f"{what}: max-abs beyond the bf16 storage rounding {excess:.3e} > {tol['max_abs']}"
+    assert m["rel_l2"] <= tol["rel_l2"], f"{what}: rel_l2 {m['rel_l2']:.3e} > {tol['rel_l2']}"
     return m
 
 

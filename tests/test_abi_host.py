@@ -92,6 +92,19 @@ def test_validate_rejects_prefill_shapes(lib, field, value):
     assert binding.phx_last_error()
 
 
+def test_validate_mlp_pairing_flags(lib):
+    """Paired MLP activations (opt-in) and plain bf16 ones (opt-out) are each a valid choice, not both."""
+    from flow_matching_action_decision_amd import binding
+    for name in ("wam_dit_bf16", "va_chunk_bf16", "prefix_prefill_bf16"):
+        for fl in (binding.PHX_FLAG_PAIRED_ACT, binding.PHX_FLAG_BF16_ACT):
+            c = binding.make_config(phx_inputs.workload(name), flags=fl)
+            assert binding.phx_expert_validate_config(c) == 0, binding.phx_last_error()
+        c = binding.make_config(phx_inputs.workload(name),
+                                flags=binding.PHX_FLAG_PAIRED_ACT | binding.PHX_FLAG_BF16_ACT)
+        assert binding.phx_expert_validate_config(c) == -1
+        assert "exclude" in binding.phx_last_error()
+
+
 @pytest.mark.parametrize("workload", ["single_layer_fp32", "va_chunk_bf16", "wam_dit_bf16", "prefix_prefill_bf16"])
 def test_validate_rejects_the_int8_tier_off_its_path(lib, workload):
     """The 8-bit weight tier: bf16 weights, the decoder block, at most 160 rows."""

@@ -96,6 +96,7 @@ def test_pi05_expert_bf16_multi_kernel_path():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(400)
 def test_rollout_b16_every_request():
     """The full rollout batch (16 requests, ragged prefixes drawn from {512,
     640, 768, 800}) in the launch configuration the benchmark times; every

@@ -77,6 +77,17 @@ def test_replays_are_bit_identical_and_tags_advance():
         assert np.array_equal(o, outs[0])
 
 
+def test_replays_many_steps_are_bit_identical():
+    """Ten Euler steps, three decisions in a row: every exchange buffer's uses
+    (per layer-step, per norm input, per state hand-off between steps) run on
+    from one decision to the next without a gap."""
+    cfg = pcfg(layers=2, steps=10, dt=-0.1)
+    inp, outs, _ = _run(cfg, repeats=3)
+    assert_close(outs[0], oracle_decide(cfg, inp), TOL_BF16, what="2 layers x 10 steps")
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
 def test_zero_velocity_head_is_bit_exact():
     cfg = pcfg(layers=1, steps=2)
     inp = phx_inputs.make_inputs(cfg, 2)

@@ -24,7 +24,7 @@ import pytest
 
 import oracle
 import phx_inputs
-from gpu_util import TOL_BF16, assert_close, say
+from gpu_util import TOL_BF16, assert_close, assert_close_bf16_storage, say
 
 pytestmark = pytest.mark.gpu
 
@@ -72,8 +72,8 @@ def _case(cfg, lengths, seed=0, tol=TOL_BF16):
         ref = oracle.prefill(cfg, inp["weights"], x, n)
         kvd = cfg["n_kv_heads"] * cfg["head_dim"]
         assert k.shape == (cfg["layers"], n, kvd) and v.shape == k.shape
-        assert_close(k, ref["k"], tol, what=f"{cfg['name']} keys, {n} tokens")
-        assert_close(v, ref["v"], tol, what=f"{cfg['name']} values, {n} tokens")
+        assert_close_bf16_storage(k, ref["k"], tol, what=f"{cfg['name']} keys, {n} tokens")
+        assert_close_bf16_storage(v, ref["v"], tol, what=f"{cfg['name']} values, {n} tokens")
     return inp, got, nk
 
 
@@ -117,12 +117,12 @@ def test_prefill_full_width_sampled():
     w1 = inp["weights"][:phx_inputs.weight_count(one)].copy()
     phx_inputs.view(w1, one, "G")[:] = phx_inputs.view(inp["weights"], cfg, "G")[:2]
     r0 = oracle.prefill(one, w1, x, n)
-    assert_close(k[:1], r0["k"], TOL_BF16, what="full width, layer 0 keys, all tokens")
-    assert_close(v[:1], r0["v"], TOL_BF16, what="full width, layer 0 values, all tokens")
+    assert_close_bf16_storage(k[:1], r0["k"], TOL_BF16, what="full width, layer 0 keys, all tokens")
+    assert_close_bf16_storage(v[:1], r0["v"], TOL_BF16, what="full width, layer 0 values, all tokens")
     # both layers on the first 64 tokens
     r = oracle.prefill(cfg, inp["weights"], x, 64)
-    assert_close(k[:, :64], r["k"], TOL_BF16, what="full width, both layers, first 64 tokens")
-    assert_close(v[:, :64], r["v"], TOL_BF16, what="full width, both layers, first 64 tokens")
+    assert_close_bf16_storage(k[:, :64], r["k"], TOL_BF16, what="full width, both layers, first 64 tokens")
+    assert_close_bf16_storage(v[:, :64], r["v"], TOL_BF16, what="full width, both layers, first 64 tokens")
 
 
 def test_prefill_feeds_the_expert():
@@ -217,9 +217,9 @@ def test_prefill_full_shape_properties():
     w1 = inp["weights"][:phx_inputs.weight_count(one)].copy()
     phx_inputs.view(w1, one, "G")[:] = phx_inputs.view(inp["weights"], cfg, "G")[:2]
     r0 = oracle.prefill(one, w1, x0, n)
-    assert_close(k0[:1], r0["k"], TOL_BF16, what="full shape, layer 0 keys, all tokens")
-    assert_close(v0[:1], r0["v"], TOL_BF16, what="full shape, layer 0 values, all tokens")
+    assert_close_bf16_storage(k0[:1], r0["k"], TOL_BF16, what="full shape, layer 0 keys, all tokens")
+    assert_close_bf16_storage(v0[:1], r0["v"], TOL_BF16, what="full shape, layer 0 values, all tokens")
     # every layer on the first 64 tokens: under the causal mask their cache is that of a 64-token prefill
     r64 = oracle.prefill(cfg, inp["weights"], x0, 64)
-    assert_close(k0[:, :64], r64["k"], TOL_BF16, what="full shape, all 18 layers' keys, first 64 tokens")
-    assert_close(v0[:, :64], r64["v"], TOL_BF16, what="full shape, all 18 layers' values, first 64 tokens")
+    assert_close_bf16_storage(k0[:, :64], r64["k"], TOL_BF16, what="full shape, all 18 layers' keys, first 64 tokens")
+    assert_close_bf16_storage(v0[:, :64], r64["v"], TOL_BF16, what="full shape, all 18 layers' values, first 64 tokens")

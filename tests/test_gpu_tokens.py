@@ -50,14 +50,15 @@ def _va_case(cfg, seed=0, tol=TOL_BF16):
     return assert_close(outs[0], ref, tol, what=cfg["name"]), inp, outs[0], nk
 
 
-def _dit_gpu(cfg, inp, x=None, repeats=1):
-    return gpu_decide(cfg, inp, noise=inp["noise"] if x is None else x, repeats=repeats)
+def _dit_gpu(cfg, inp, x=None, repeats=1, flags=0):
+    return gpu_decide(cfg, inp, noise=inp["noise"] if x is None else x, repeats=repeats, flags=flags)
 
 
-def _dit_case(cfg, seed=0, tol=TOL_TOKENS):
-    say(f"case {cfg['name']} seed={seed} tokens={cfg['rows']} width={cfg['width']} blocks={cfg['layers']}")
+def _dit_case(cfg, seed=0, tol=TOL_TOKENS, flags=0):
+    say(f"case {cfg['name']} seed={seed} tokens={cfg['rows']} width={cfg['width']} blocks={cfg['layers']} "
+        f"flags={flags}")
     inp = phx_inputs.make_inputs(cfg, seed)
-    outs, nk = _dit_gpu(cfg, inp)
+    outs, nk = _dit_gpu(cfg, inp, flags=flags)
     ref = oracle.dit(cfg, inp["weights"], inp["noise"][0])["out"]
     return assert_close(outs[0][0], ref, tol, what=cfg["name"]), inp, outs[0], nk
 
@@ -163,6 +164,7 @@ def test_va_chunk_full_width_one_layer_one_step():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(400)
 def test_va_chunk_full_every_layer_one_step():
     """Every layer of the video-action chunk (8 layers at full width, heads,
     rows, cache length and capacity) for one Euler step, element by element."""
@@ -238,11 +240,11 @@ def test_dit_full_permutation_equivariance():
     outs, _ = _dit_gpu(cfg, inp, repeats=2)
     assert np.array_equal(outs[0], outs[1]), "replays must be bit-identical"
     outs_p, _ = _dit_gpu(cfg, inp, x=np.ascontiguousarray(inp["noise"][:, perm]))
-    # Both runs carry their own bf16 rounding of the GEMM operands and of the
-    # probabilities (rounded against a running maximum that depends on the key
-    # order): the output-scale bar, doubled on max-abs for the difference of
-    # two such runs over 12.7M values, and rel-L2 at half the bf16 bar.
-    assert_close(outs_p[0][0], outs[0][0][perm], dict(max_abs=1e-1, rel_l2=5e-3, worst_row_cos=0.9999),
+    # Both runs carry their own bf16 rounding of the attention operands and of
+    # the probabilities (rounded against a running maximum that depends on the
+    # key order): the bar doubled on max-abs for the difference of two such
+    # runs, and rel-L2 at half the bar.
+    assert_close(outs_p[0][0], outs[0][0][perm], dict(max_abs=4e-2, rel_l2=5e-3, worst_row_cos=0.9999),
                  what="permuted")
 
 
@@ -254,6 +256,53 @@ def test_dit_full_width_one_block(rows):
     cfg = phx_inputs.workload("wam_dit_bf16", layers=1, rows=rows)
     cfg["name"] = f"dit_1block_{rows}"
     _dit_case(cfg)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(400)
+def test_dit_full_tokens_one_block():
+    """One block of the DiT-style step at its full size (4128 tokens, width
+    3072, 24 heads of 128, MLP 12288), every value against the oracle."""
+    cfg = phx_inputs.workload("wam_dit_bf16", layers=1)
+    cfg["name"] = "dit_1block_4128"
+    _dit_case(cfg)
+
+
+def test_dit_paired_activations_beat_plain_bf16():
+    """The paired GEMM activations (the DiT-style block's default) against
+    plain bf16 ones (PHX_FLAG_BF16_ACT), one full-width block of 528 tokens:
+    both against the oracle, the paired run at the bar and closer than the
+    plain run, which carries the bf16 rounding of the QKV, gate/up and down inputs."""
+    from flow_matching_action_decision_amd import PHX_FLAG_BF16_ACT
+    cfg = phx_inputs.workload("wam_dit_bf16", layers=1, rows=528)
+    cfg["name"] = "dit_1block_528_pairing"
+    inp = phx_inputs.make_inputs(cfg, 0)
+    ref = oracle.dit(cfg, inp["weights"], inp["noise"][0])["out"]
+    say("case dit paired vs plain bf16 GEMM activations (528 tokens, one block)")
+    paired, nk_p = _dit_gpu(cfg, inp)
+    plain, nk_b = _dit_gpu(cfg, inp, flags=PHX_FLAG_BF16_ACT)
+    assert nk_p == nk_b
+    mp = assert_close(paired[0][0], ref, TOL_TOKENS, what="paired GEMM activations")
+    mb = assert_close(plain[0][0], ref, dict(max_abs=1.0, rel_l2=1e-2), what="plain bf16 GEMM activations")
+    assert mp["max_abs"] < mb["max_abs"] and mp["rel_l2"] < mb["rel_l2"]
+
+
+def test_dit_small_plain_bf16_act():
+    """The plain-bf16 opt-out on the small DiT shape (small modulation, so the
+    bf16 rounding of the MLP stays within the bar there)."""
+    from flow_matching_action_decision_amd import PHX_FLAG_BF16_ACT
+    _dit_case(dit_small(name="dit_small_bf16_act"), flags=PHX_FLAG_BF16_ACT)
+
+
+def test_va_paired_activations():
+    """The decoder plan with paired GEMM activations (opt-in): the same
+    oracle bar, and the chunk's QKV, gate/up and down GEMMs at twice the k-steps."""
+    from flow_matching_action_decision_amd import PHX_FLAG_PAIRED_ACT
+    cfg = va_small(name="va_small_paired")
+    inp = phx_inputs.make_inputs(cfg, 0)
+    say("case va_small paired GEMM activations")
+    outs, _ = gpu_decide(cfg, inp, flags=PHX_FLAG_PAIRED_ACT)
+    assert_close(outs[0], oracle_decide(cfg, inp), TOL_BF16, what="va_small paired")
 
 
 # ------------------------------------------------------------ history update
