@@ -32,7 +32,8 @@ PHX_MASK_FULL, PHX_MASK_CAUSAL = 0, 1
 
 # every function include/phx_expert.h declares
 EXPORTED = ("phx_expert_validate_config", "phx_expert_weights_bytes", "phx_expert_create",
-            "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_destroy", "phx_last_error",
+            "phx_expert_load_prefix_kv", "phx_expert_decide", "phx_expert_decide_noalloc", "phx_expert_destroy",
+            "phx_last_error",
             "phx_expert_kernels_per_decision", "phx_expert_node_info", "phx_expert_launch_node",
             "phx_expert_status", "phx_expert_timeline", "phx_expert_capsule_bytes", "phx_expert_capsule_regions",
             "phx_expert_capsule_save", "phx_expert_capsule_restore", "phx_expert_commit_chunk",
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phx_expert_create.argtypes = [CP, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
     lib.phx_expert_load_prefix_kv.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_int32, P]
     lib.phx_expert_decide.argtypes = [P, P, P, P]
+    lib.phx_expert_decide_noalloc.argtypes = [P, P, P, P]
     lib.phx_expert_destroy.argtypes = [P]
     lib.phx_expert_destroy.restype = None
     lib.phx_last_error.restype = ctypes.c_char_p
@@ -159,6 +161,11 @@ def phx_expert_load_prefix_kv(h: int, request: int, k_ptr: int, v_ptr: int, pref
 def phx_expert_decide(h: int, noise_ptr: int, actions_ptr: int, stream: int = 0):
     _check(load_library().phx_expert_decide(ctypes.c_void_p(h), ctypes.c_void_p(noise_ptr),
                                             ctypes.c_void_p(actions_ptr), ctypes.c_void_p(stream)))
+
+
+def phx_expert_decide_noalloc(h: int, noise_ptr: int, actions_ptr: int, stream: int = 0):
+    _check(load_library().phx_expert_decide_noalloc(ctypes.c_void_p(h), ctypes.c_void_p(noise_ptr),
+                                                    ctypes.c_void_p(actions_ptr), ctypes.c_void_p(stream)))
 
 
 def phx_expert_destroy(h: int):

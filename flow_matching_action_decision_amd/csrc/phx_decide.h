@@ -108,15 +108,28 @@ __host__ __device__ constexpr unsigned x_base(int t) {
   return o;
 }
 constexpr unsigned EX_BYTES = x_base(NXT);
+// Control words follow the exchange words and travel with them: the tags the
+// words carry are a function of the decision counter, so whoever owns a set
+// of exchange words owns its counter too.
+constexpr unsigned CT_STATUS = EX_BYTES;      // u32: decision counter + 1 of the last decision in which a wait gave up
+constexpr unsigned CT_SEQ = EX_BYTES + 4u;    // u32 decision counter (tag base), advanced after each decision
+// u32 [4]: rows, prefix chunks, steps, layers of the last decision on these
+// words.  Which words a decision writes, and how many uses of each buffer it
+// counts, depend on exactly these four; a decision of another shape may only
+// follow on cleared words.
+constexpr unsigned CT_SHAPE = EX_BYTES + 16u;
+constexpr unsigned XC_BYTES = EX_BYTES + 256u;  // exchange words and control words
+// Most exchange memory one decision uses: the words and control words above,
+// the same for every configuration the kernel takes.
+constexpr unsigned SCRATCH_BYTES = XC_BYTES;
 
-// Auxiliary arena (device memory, bytes, from AUX0 on in the kernel's arena:
-// it follows the exchange words): counters, state, position table, then one
-// block of per-step tables per Euler step, then the timeline.
-constexpr unsigned AUX0 = EX_BYTES;
-constexpr unsigned AUX_STATUS = 0;   // u32: decision counter + 1 of the last decision in which a wait gave up
-constexpr unsigned AUX_SEQ = 4;      // u32 decision counter (tag base), advanced after each decision
-constexpr unsigned AUX_LENS = 8;     // i32 prefix length
-constexpr unsigned AUX_FAILED = 12;  // u32: 1 if the last decision gave up (set after each decision)
+// Auxiliary tables of one handle (device memory, bytes from the table base;
+// a handle's own arena holds its exchange words at 0 and these tables from
+// AUX0 on): prefix length, failure flag, state, position table, then one block
+// of per-step tables per Euler step, then the timeline.
+constexpr unsigned AUX0 = XC_BYTES;
+constexpr unsigned AUX_LENS = 0;     // i32 prefix length
+constexpr unsigned AUX_FAILED = 4;   // u32: 1 if the handle's last decision gave up (set after each decision)
 constexpr unsigned AUX_X = 256;      // [RP][A] f32: the noise on entry, the actions on exit
 constexpr unsigned AUX_ROPE = AUX_X + RP * A * 4;        // [RP][DH/2] (cos, sin) of the action rows
 constexpr unsigned AUX_TAB = al256(AUX_ROPE + RP * (DH / 2) * 8);
@@ -151,8 +164,9 @@ __host__ __device__ constexpr unsigned long long w_elems(int NL) { return w_out(
 struct Args {
   const void* wt;   // tiled bf16 weights
   const void* kvt;  // attention-tiled prefix K/V: [NL][n_chunks][64 tiles]
-  void* arena;      // exchange words, then the auxiliary arena at AUX0
-  unsigned wt_bytes, kvt_bytes, arena_bytes;
+  void* ex;         // exchange and control words, XC_BYTES
+  void* aux;        // the handle's auxiliary tables
+  unsigned wt_bytes, kvt_bytes, aux_bytes;
   unsigned tl;      // nonzero: record the phase timeline
   int S, NL, R, n_chunks;
   float dt, eps;
@@ -166,7 +180,19 @@ hipError_t decide_occupancy(int* blocks_per_cu);
 // went to the XCDs round-robin in index order (XCD (b + o) mod 8 for one
 // offset o): the kernel's ranks inside an XCD rely on it
 hipError_t decide_placement(bool* ok);
-hipError_t launch_decide_advance(void* arena, hipStream_t s);
+// after a decision: advances the counter in ex, or clears ex's words after a
+// decision that gave up; records the decision's shape in ex; sets the
+// handle's failure flag in aux
+hipError_t launch_decide_advance(const Args& a, hipStream_t s);
+// before a decision on shared words: if the shape recorded in a.ex differs
+// from a's, clears the words and restarts the counter at 0
+hipError_t launch_decide_prepare(const Args& a, hipStream_t s);
+// The static exchange memory of this device (SCRATCH_BYTES, zeroed when first
+// set up): decide_scratch_setup looks up its device address once per device
+// (call it with that device current, outside graph capture); decide_scratch
+// returns the address set up for device dev, or an error if there is none.
+hipError_t decide_scratch_setup();
+hipError_t decide_scratch(int dev, void** ptr);
 // set-up kernels
 // out[k * out_kstride + l * N + n] = sum_d shift(k, norm_stride*l + norm_off)[d] * W_l[d][colmap(n)]
 // for k < S, l < nl, n < N, where W_l = w0 + l * w_lstride is a [D][N] bf16
@@ -175,8 +201,8 @@ hipError_t launch_decide_advance(void* arena, hipStream_t s);
 hipError_t launch_shift_table(const void* w0, long long w_lstride, const float* modtab, int NN, int norm_stride,
                               int norm_off, int S, int nl, int N, int colkind, int colparam, float* out,
                               size_t out_kstride, hipStream_t s);
-// scale[k][norm][d] of the modulation table [S][NN][2D] into each step block
-hipError_t launch_scale_table(const float* modtab, int S, int NN, void* arena, int NL, hipStream_t s);
+// scale[k][norm][d] of the modulation table [S][NN][2D] into each step block of the tables at aux
+hipError_t launch_scale_table(const float* modtab, int S, int NN, void* aux, int NL, hipStream_t s);
 hipError_t launch_attn_tiles(const void* k, const void* v, void* kvt, int NL, int L, int n_chunks, hipStream_t s);
 
 }  // namespace dec

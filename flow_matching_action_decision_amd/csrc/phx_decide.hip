@@ -57,6 +57,7 @@
 #include <math.h>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 namespace phx {
 namespace dec {
@@ -199,7 +200,8 @@ __device__ inline int xcc_id() {
 struct Ctx {
   Shared* sh;
   unsigned char* ring;
-  Rsrc X;                  // arena: exchange words at 0, auxiliary tables at AUX0
+  Rsrc X;                  // exchange words, control words at CT_*
+  Rsrc Y;                  // the handle's auxiliary tables
   unsigned seq;            // this decision's counter
   unsigned redsel;         // which half of the scratch the current phase uses
   unsigned barn;           // compute-wave barriers passed
@@ -269,9 +271,9 @@ template <int T>
 constexpr int pol_of() {
   return x_local(T) ? NTP : SC1;
 }
-// byte offset of step k's table block in the arena
+// byte offset of step k's table block in the auxiliary tables
 __device__ inline unsigned step_tab(const Ctx& c, int k) {
-  return AUX0 + AUX_TAB + (unsigned)k * step_bytes(c.NL);
+  return AUX_TAB + (unsigned)k * step_bytes(c.NL);
 }
 
 __device__ inline void lds_store(unsigned* p, unsigned v) {
@@ -303,13 +305,13 @@ __device__ __attribute__((always_inline)) inline void end_wave() { asm volatile(
 // mark the actions NaN, and ends the wave.
 __device__ __attribute__((always_inline)) inline void leave(Ctx& c, bool record) {
   lds_store(&c.sh->abort, 1u);
-  if (record && c.lane == 0) __builtin_amdgcn_raw_buffer_store_b32(c.seq + 1u, c.X, AUX0 + AUX_STATUS, 0, SC1);
+  if (record && c.lane == 0) __builtin_amdgcn_raw_buffer_store_b32(c.seq + 1u, c.X, CT_STATUS, 0, SC1);
   if (is_vel(c) && c.xcd == 0 && c.wave == 0 && c.row < c.R) {
     const unsigned nanv = 0x7fc00000u;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{nanv, nanv, nanv, nanv}, c.X,
-                                             AUX0 + AUX_X + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{nanv, nanv, nanv, nanv}, c.Y,
+                                             AUX_X + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4), 0, 0);
   }
   end_wave();
 }
@@ -322,7 +324,7 @@ __device__ inline void keep_waiting(Ctx& c, unsigned t0, unsigned& spins) {
   if ((spins & 63u) == 0u) {
     if (now_ticks() - t0 > TIMEOUT_TICKS) leave(c, true);
     const unsigned st =
-        __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(c.X, AUX0 + AUX_STATUS, 0, SC1));
+        __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(c.X, CT_STATUS, 0, SC1));
     if (st == c.seq + 1u) leave(c, false);
   }
 }
@@ -470,7 +472,7 @@ __device__ inline void st1(const Ctx& c, unsigned off, unsigned w) {
 __device__ inline void tl_mark(const Ctx& c, int ev) {
   if (c.tl != 0u && c.lane == 0) {
     const unsigned idx = (blockIdx.x * (unsigned)timeline_events(c.S, c.NL) + (unsigned)ev) * 4u;
-    __builtin_amdgcn_raw_buffer_store_b32(now_ticks(), c.X, AUX0 + aux_timeline(c.S, c.NL) + idx, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(now_ticks(), c.Y, aux_timeline(c.S, c.NL) + idx, 0, 0);
   }
 }
 
@@ -483,7 +485,7 @@ __device__ inline void tl_mark(const Ctx& c, int ev) {
 // (1 + scale) of the owner's columns for one norm (issue early; use after)
 __device__ inline u32x4 owner_scale_load(const Ctx& c, int k, int norm, int t) {
   const unsigned off = step_tab(c, k) + (unsigned)((norm * D + 32 * c.rk + 16 * t + 4 * c.g) * 4);
-  return __builtin_amdgcn_raw_buffer_load_b128(c.X, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(c.Y, off, 0, 0);
 }
 
 // publishes h * (1 + scale) as pair words and the per-row sums of squares of
@@ -547,8 +549,8 @@ __device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, f32x4
   u32x4 v[2];
   const unsigned vo = (unsigned)((c.crow * A + 8 * c.g) * 4);
   if (k == 0) {
-    v[0] = __builtin_amdgcn_raw_buffer_load_b128(c.X, AUX0 + AUX_X + vo, 0, 0);
-    v[1] = __builtin_amdgcn_raw_buffer_load_b128(c.X, AUX0 + AUX_X + vo + 16u, 0, 0);
+    v[0] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, AUX_X + vo, 0, 0);
+    v[1] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, AUX_X + vo + 16u, 0, 0);
   } else {
     const Use ux = use_state(c, k - 1);
     const unsigned bx = xb<X_X>(c, ux.par);
@@ -582,9 +584,9 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
   const int nt = nt0 + (c.wave & 1);  // epilogue tables of the n-tile this wave finishes (waves 0, 1)
   const int tt = nt % 16;
   const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
-      c.X, step_tab(c, k) + st_swqkv(c.NL) + (unsigned)((l * NQKV + nt * 16 + 4 * c.g) * 4), 0, 0);
+      c.Y, step_tab(c, k) + st_swqkv(c.NL) + (unsigned)((l * NQKV + nt * 16 + 4 * c.g) * 4), 0, 0);
   const u32x4 cs = __builtin_amdgcn_raw_buffer_load_b128(
-      c.X, AUX0 + AUX_ROPE + (unsigned)((c.row * (DH / 2) + 8 * tt + 2 * c.g) * 8), 0, 0);
+      c.Y, AUX_ROPE + (unsigned)((c.row * (DH / 2) + 8 * tt + 2 * c.g) * 8), 0, 0);
   u32x4 v[18];
   poll_normed<X_N, X_SS>(c, u, v);
   wait_tiles(c, p0, 64);
@@ -1006,7 +1008,7 @@ __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_gu;
   const int nt = 64 * c.xcd + 2 * c.rk + (c.wave & 1);
   const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
-      c.X, step_tab(c, k) + st_swgu(c.NL) + (unsigned)((l * 2 * F + nt * 16 + 4 * c.g) * 4), 0, 0);
+      c.Y, step_tab(c, k) + st_swgu(c.NL) + (unsigned)((l * 2 * F + nt * 16 + 4 * c.g) * 4), 0, 0);
   u32x4 v[18];
   poll_normed<X_N2, X_SS2>(c, u, v);
   wait_tiles(c, p0, 64);
@@ -1075,7 +1077,7 @@ __device__ __attribute__((always_inline)) inline void ph_vel(Ctx& c, int k, f32x
   u32x4 sw[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
-    sw[t] = __builtin_amdgcn_raw_buffer_load_b128(c.X, step_tab(c, k) + st_swout(NL) + (unsigned)((16 * t + 4 * c.g) * 4),
+    sw[t] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, step_tab(c, k) + st_swout(NL) + (unsigned)((16 * t + 4 * c.g) * 4),
                                                   0, 0);
   u32x4 v[18];
   poll_normed<X_N, X_SS>(c, u, v);
@@ -1102,7 +1104,7 @@ __device__ __attribute__((always_inline)) inline void ph_vel(Ctx& c, int k, f32x
           st4<LST>(c, xb<X_X>(c, ux.par) + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4), w);
         } else if (c.xcd == 0) {
           const u32x4 w = {as_u(x[t][0]), as_u(x[t][1]), as_u(x[t][2]), as_u(x[t][3])};
-          __builtin_amdgcn_raw_buffer_store_b128(w, c.X, AUX0 + AUX_X + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4), 0,
+          __builtin_amdgcn_raw_buffer_store_b128(w, c.Y, AUX_X + (unsigned)((c.row * A + 16 * t + 4 * c.g) * 4), 0,
                                                  0);
         }
       }
@@ -1228,7 +1230,7 @@ __device__ inline void loader_keep_waiting(Ctx& c, unsigned t0, unsigned& spins)
   if (lds_load(&c.sh->abort) != 0u) end_wave();
   if ((spins & 63u) == 0u && now_ticks() - t0 > TIMEOUT_TICKS) {
     lds_store(&c.sh->abort, 1u);
-    if (c.lane == 0) __builtin_amdgcn_raw_buffer_store_b32(c.seq + 1u, c.X, AUX0 + AUX_STATUS, 0, SC1);
+    if (c.lane == 0) __builtin_amdgcn_raw_buffer_store_b32(c.seq + 1u, c.X, CT_STATUS, 0, SC1);
     end_wave();
   }
 }
@@ -1300,9 +1302,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
   c.xcd = xcc_id();
   c.rk = (int)(blockIdx.x / NX);
   if (threadIdx.x < 32) ((unsigned*)&sh)[threadIdx.x] = 0u;
-  c.X = rsrc(a.arena, a.arena_bytes);
-  c.seq = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(c.X, AUX0 + AUX_SEQ, 0, SC1));
-  c.L = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b32(c.X, AUX0 + AUX_LENS, 0, 0));
+  c.X = rsrc(a.ex, XC_BYTES);
+  c.Y = rsrc(a.aux, a.aux_bytes);
+  c.seq = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(c.X, CT_SEQ, 0, SC1));
+  c.L = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b32(c.Y, AUX_LENS, 0, 0));
   c.crow = c.row < c.R ? c.row : c.R - 1;
   // stream layout of this workgroup (must match run_params)
   c.o_att = is_qkv(c) ? 64u : 0u;
@@ -1328,7 +1331,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(
-          c.X, AUX0 + AUX_X + (unsigned)((c.crow * A + 16 * t + 4 * c.g) * 4), 0, 0);
+          c.Y, AUX_X + (unsigned)((c.crow * A + 16 * t + 4 * c.g) * 4), 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[t][e] = as_f(xv[e]);
     }
@@ -1373,23 +1376,52 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
 // the decision gave up, its words may be half written: the block clears the
 // exchange words, starts the counter over at 0 and clears the status, and
 // raises the failure flag the host reads; otherwise it lowers the flag.  The
-// clear only runs after a failed decision.
+// clear only runs after a failed decision.  The decision's shape goes into
+// the control words either way.
 constexpr int ADV_THREADS = 1024;
-__global__ __launch_bounds__(ADV_THREADS) void k_decide_advance(unsigned char* arena) {
-  unsigned* aux = (unsigned*)(arena + AUX0);
-  const unsigned st = aux[AUX_STATUS / 4];
-  const unsigned sq = aux[AUX_SEQ / 4];
+__global__ __launch_bounds__(ADV_THREADS) void k_decide_advance(unsigned char* exw, unsigned char* aux, u32x4 shape) {
+  unsigned* ct = (unsigned*)exw;
+  const unsigned st = ct[CT_STATUS / 4];
+  const unsigned sq = ct[CT_SEQ / 4];
   const bool failed = st != 0u && st == sq + 1u;
   if (failed) {
-    u32x4* ex = (u32x4*)arena;
+    u32x4* ex = (u32x4*)exw;
     for (unsigned i = threadIdx.x; i < EX_BYTES / 16u; i += ADV_THREADS) ex[i] = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    aux[AUX_SEQ / 4] = failed ? 0u : sq + 1u;
-    if (failed) aux[AUX_STATUS / 4] = 0u;
-    aux[AUX_FAILED / 4] = failed ? 1u : 0u;
+    ct[CT_SEQ / 4] = failed ? 0u : sq + 1u;
+    if (failed) ct[CT_STATUS / 4] = 0u;
+    *(u32x4*)(exw + CT_SHAPE) = shape;
+    ((unsigned*)aux)[AUX_FAILED / 4] = failed ? 1u : 0u;
   }
+}
+
+// Before a decision on words that decisions of other shapes may have used
+// (G blocks, each its slice of the words): the tags only tell fresh from
+// stale when every use of a buffer writes every word the next use of that
+// copy reads, and the counter counts the same uses per decision.  Both hold
+// between decisions of one shape (rows, prefix chunks, steps, layers); after
+// a decision of another shape the words are cleared and the counter restarts
+// at 0, as on fresh memory.  The shape record itself is only written after
+// the decision, so every block here reads the same one.
+constexpr int PREP_THREADS = 256;
+constexpr unsigned PREP_SLICE = EX_BYTES / G;
+static_assert(EX_BYTES % (G * 16) == 0, "the words split into G slices of whole 16-byte stores");
+__global__ __launch_bounds__(PREP_THREADS) void k_decide_prepare(unsigned char* exw, u32x4 shape) {
+  const u32x4 last = *(const u32x4*)(exw + CT_SHAPE);
+  if (last[0] == shape[0] && last[1] == shape[1] && last[2] == shape[2] && last[3] == shape[3]) return;
+  u32x4* ex = (u32x4*)(exw + (size_t)blockIdx.x * PREP_SLICE);
+  for (unsigned i = threadIdx.x; i < PREP_SLICE / 16u; i += PREP_THREADS) ex[i] = u32x4{0u, 0u, 0u, 0u};
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    unsigned* ct = (unsigned*)exw;
+    ct[CT_SEQ / 4] = 0u;
+    ct[CT_STATUS / 4] = 0u;
+  }
+}
+
+static u32x4 shape_of(const Args& a) {
+  return u32x4{(unsigned)a.R, (unsigned)a.n_chunks, (unsigned)a.S, (unsigned)a.NL};
 }
 
 static hipError_t allow_ring_lds() {
@@ -1457,9 +1489,53 @@ hipError_t launch_decide(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decide_advance(void* arena, hipStream_t s) {
-  hipLaunchKernelGGL(k_decide_advance, dim3(1), dim3(ADV_THREADS), 0, s, (unsigned char*)arena);
+hipError_t launch_decide_advance(const Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_decide_advance, dim3(1), dim3(ADV_THREADS), 0, s, (unsigned char*)a.ex, (unsigned char*)a.aux,
+                     shape_of(a));
   return hipGetLastError();
+}
+
+hipError_t launch_decide_prepare(const Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_decide_prepare, dim3(G), dim3(PREP_THREADS), 0, s, (unsigned char*)a.ex, shape_of(a));
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- static scratch
+
+// Exchange and control words for decisions that may not allocate: one copy
+// per device, held until the process ends, shared by every such decision on
+// the device (they run one after another on one stream, or they race).
+// Host code uses the address looked up per device, never this name, which on
+// the host is only a stand-in for the device symbol.
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static void* g_scratch[MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+hipError_t decide_scratch_setup() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return hipSuccess;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  // zeroed words carry tag 0, which the first use of every copy (tag 1) never takes as fresh
+  e = hipMemset(ptr, 0, SCRATCH_BYTES);
+  if (e != hipSuccess) return e;
+  g_scratch[dev] = ptr;
+  return hipSuccess;
+}
+
+hipError_t decide_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  *ptr = g_scratch[dev];
+  return *ptr ? hipSuccess : hipErrorNotInitialized;
 }
 // ------------------------------------------------------------ set-up kernels
 
@@ -1503,7 +1579,7 @@ hipError_t launch_shift_table(const void* w0, long long w_lstride, const float* 
   return hipGetLastError();
 }
 
-__global__ void k_scale_table(const float* __restrict__ modtab, int S, int NN, unsigned char* __restrict__ arena,
+__global__ void k_scale_table(const float* __restrict__ modtab, int S, int NN, unsigned char* __restrict__ aux,
                               int NL) {
   const size_t total = (size_t)S * NN * D;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -1511,15 +1587,15 @@ __global__ void k_scale_table(const float* __restrict__ modtab, int S, int NN, u
     const int d = (int)(idx % D);
     const size_t kn = idx / D;
     const int nrm = (int)(kn % NN), k = (int)(kn / NN);
-    float* dst = (float*)(arena + AUX0 + AUX_TAB + (size_t)k * step_bytes(NL));
+    float* dst = (float*)(aux + AUX_TAB + (size_t)k * step_bytes(NL));
     dst[(size_t)nrm * D + d] = modtab[((size_t)k * NN + nrm) * 2 * D + d];
   }
 }
 
-hipError_t launch_scale_table(const float* modtab, int S, int NN, void* arena, int NL, hipStream_t s) {
+hipError_t launch_scale_table(const float* modtab, int S, int NN, void* aux, int NL, hipStream_t s) {
   const size_t total = (size_t)S * NN * D;
   const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
-  hipLaunchKernelGGL(k_scale_table, dim3(blocks), dim3(256), 0, s, modtab, S, NN, (unsigned char*)arena, NL);
+  hipLaunchKernelGGL(k_scale_table, dim3(blocks), dim3(256), 0, s, modtab, S, NN, (unsigned char*)aux, NL);
   return hipGetLastError();
 }
 

@@ -160,7 +160,9 @@ struct phx_expert {
   // persistent decision kernel (pi0.5 shape, one request)
   bool persistent = false;
   dec::Args dargs{};
-  void* arena = nullptr;      // exchange words, then the auxiliary tables (dec::AUX0)
+  void* arena = nullptr;      // exchange and control words, then the auxiliary tables (dec::AUX0)
+  hipError_t scratch_rc = hipErrorNotInitialized;  // set-up of the device's static exchange memory
+  int device = 0;             // the device the handle was created on
   void* kvt = nullptr;
   int n_chunks = 0;
   // large-token plan (a chunk of many rows, or the DiT-style block)
@@ -409,7 +411,7 @@ bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop
   if (prop.maxSharedMemoryPerMultiProcessor < 160 * 1024) return false;
   // every arena must stay within the 32-bit range of a buffer resource
   if (dec::w_elems(c.layers) * 2ull >= (1ull << 32)) return false;
-  const unsigned long long arena = (unsigned long long)dec::AUX0 + dec::AUX_TAB +
+  const unsigned long long arena = (unsigned long long)dec::AUX_TAB +
                                    (unsigned long long)c.steps * dec::step_bytes(c.layers) +
                                    (unsigned long long)dec::G * dec::timeline_events(c.steps, c.layers) * 4ull;
   if (arena >= (1ull << 31)) return false;
@@ -436,13 +438,14 @@ bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop
 
 int enqueue_persistent(phx_expert* h, hipStream_t s) {
   PHX_HIP(dec::launch_decide(h->dargs, s));
-  PHX_HIP(dec::launch_decide_advance(h->arena, s));
+  PHX_HIP(dec::launch_decide_advance(h->dargs, s));
   return PHX_OK;
 }
 
 // Everything the persistent path needs after the weights are tiled: one
-// arena holding the exchange words and then the auxiliary tables (counters,
-// state, position table, per-step scale and shift . W tables, timeline), the
+// arena holding the exchange and control words and then the auxiliary tables
+// (prefix length, failure flag, state, position table, per-step scale and
+// shift . W tables, timeline), the
 // attention-tiled prefix K/V, and a two-node graph (decision kernel, tag
 // advance).  Workgroup roles are a function of the workgroup index and the
 // chunk count, computed in the kernel.
@@ -451,7 +454,8 @@ int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t 
   const int S = c.steps, NL = c.layers, E = c.time_emb_dim;
   h->n_chunks = (c.prefix_capacity + dec::CHUNK - 1) / dec::CHUNK;
   const bool timeline = (c.flags & PHX_FLAG_TIMELINE) != 0;
-  const size_t arena_bytes = (size_t)dec::AUX0 + dec::aux_bytes(S, NL, timeline);
+  const size_t aux_bytes = dec::aux_bytes(S, NL, timeline);
+  const size_t arena_bytes = (size_t)dec::AUX0 + aux_bytes;
   int rc;
   if ((rc = alloc(h, &h->arena, arena_bytes, "decision arena"))) return rc;
   PHX_HIP(hipMemsetAsync(h->arena, 0, arena_bytes, stream));
@@ -469,7 +473,7 @@ int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t 
   PHX_HIP(launch_time_embedding((double*)etab, S, E, c.tau0, c.dt, stream));
   PHX_HIP(launch_modulation(h->dtype, sb + mod_off_elems * h->esz, (const double*)etab, h->modtab, S, h->NN, E,
                             2 * dec::D, stream));
-  PHX_HIP(dec::launch_scale_table(h->modtab, S, h->NN, h->arena, NL, stream));
+  PHX_HIP(dec::launch_scale_table(h->modtab, S, h->NN, aux, NL, stream));
   const long long lstride = (long long)dec::W_LAYER;
   const size_t ks = dec::step_bytes(NL) / sizeof(float);
   char* tab = aux + dec::AUX_TAB;
@@ -503,10 +507,15 @@ int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t 
   dec::Args& a = h->dargs;
   a.wt = h->wt;
   a.kvt = h->kvt;
-  a.arena = h->arena;
+  a.ex = h->arena;
+  a.aux = aux;
   a.wt_bytes = (unsigned)(dec::w_elems(NL) * 2ull);
   a.kvt_bytes = (unsigned)kvt_bytes;
-  a.arena_bytes = (unsigned)arena_bytes;
+  a.aux_bytes = (unsigned)aux_bytes;
+  // the device's static exchange memory, for decisions that may not allocate
+  // (phx_expert_decide_noalloc); the handle's own decisions do not need it
+  h->scratch_rc = dec::decide_scratch_setup();
+  if (h->scratch_rc != hipSuccess) (void)hipGetLastError();
   a.tl = timeline ? 1u : 0u;
   a.S = S;
   a.NL = NL;
@@ -1260,6 +1269,7 @@ static int create_impl(phx_expert* h, const void* weights, hipStream_t stream) {
   hipDeviceProp_t prop;
   int dev = 0;
   PHX_HIP(hipGetDevice(&dev));
+  h->device = dev;
   PHX_HIP(hipGetDeviceProperties(&prop, dev));
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(PHX_E_HIP, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
@@ -1563,6 +1573,42 @@ int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_str
     if (rc) return rc;
   }
   PHX_HIP(hipMemcpyAsync(actions, state, xb, hipMemcpyDefault, s));
+  g_err.clear();
+  return PHX_OK;
+}
+
+// The decision of phx_expert_decide with the exchange and control words in the
+// device's static scratch instead of the handle's arena: stream-ordered
+// copies and three kernel launches (prepare, decision, advance), nothing
+// allocated, no runtime call that allocates.  Every such call on one device
+// shares that scratch; the prepare kernel clears it when the previous
+// decision on it had another shape.
+int phx_expert_decide_noalloc(phx_expert* h, const float* noise, float* actions, phx_stream_t stream) {
+  if (!h) return fail(PHX_E_INVALID, "handle is NULL");
+  if (!noise || !actions) return fail(PHX_E_INVALID, "noise or actions is NULL");
+  if (!h->persistent)
+    return fail(PHX_E_SHAPE,
+                "no allocation-free decision for this handle: its plan's working memory is not the decision "
+                "kernel's %u bytes of exchange words (the most the static scratch holds); use phx_expert_decide",
+                dec::SCRATCH_BYTES);
+  if (dec::XC_BYTES > dec::SCRATCH_BYTES)
+    return fail(PHX_E_SHAPE, "exchange words of %u bytes exceed the static scratch of %u bytes", dec::XC_BYTES,
+                dec::SCRATCH_BYTES);
+  if (!h->loaded[0]) return fail(PHX_E_STATE, "request 0 has no prefix loaded");
+  if (h->scratch_rc != hipSuccess)
+    return fail(PHX_E_HIP, "static scratch of device %d not set up: %s", h->device, hipGetErrorString(h->scratch_rc));
+  void* ex = nullptr;
+  if (dec::decide_scratch(h->device, &ex) != hipSuccess || !ex)
+    return fail(PHX_E_HIP, "static scratch of device %d not set up", h->device);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t xb = (size_t)h->BM * h->cfg.state_dim * sizeof(float);
+  dec::Args a = h->dargs;
+  a.ex = ex;
+  PHX_HIP(hipMemcpyAsync(h->x, noise, xb, hipMemcpyDefault, s));
+  PHX_HIP(dec::launch_decide_prepare(a, s));
+  PHX_HIP(dec::launch_decide(a, s));
+  PHX_HIP(dec::launch_decide_advance(a, s));
+  PHX_HIP(hipMemcpyAsync(actions, h->x, xb, hipMemcpyDefault, s));
   g_err.clear();
   return PHX_OK;
 }

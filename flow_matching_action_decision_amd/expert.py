@@ -75,6 +75,12 @@ class Expert:
         B.phx_expert_decide(self.h, noise.data_ptr(), out.data_ptr(), self.stream)
         return out
 
+    def decide_noalloc(self, noise, out):
+        """As decide, through the allocation-free entry point (the device's
+        static exchange memory); out must be preallocated."""
+        B.phx_expert_decide_noalloc(self.h, noise.data_ptr(), out.data_ptr(), self.stream)
+        return out
+
     def status(self) -> int:
         """0 if the last decision completed; nonzero if the persistent kernel gave up waiting."""
         return B.phx_expert_status(self.h)

@@ -240,6 +240,33 @@ PHX_API int phx_expert_load_prefix_kv(phx_expert* h, int32_t request, const void
 PHX_API int phx_expert_decide(phx_expert* h, const float* noise, float* actions, phx_stream_t stream);
 
 /*
+ * The decision of phx_expert_decide for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arithmetic, same result bit for bit; the decision
+ * kernel's exchange and control words (9,666,816 bytes) live in a static
+ * device array that the library holds once per device until the process
+ * ends, instead of the handle's arena.  The call allocates nothing and makes
+ * no runtime call that allocates: two stream-ordered copies (noise in,
+ * actions out) and three kernel launches (a prepare kernel, the decision
+ * kernel, its tag advance).  The array's address is looked up and the array
+ * cleared when the first handle on the device is created.  When the previous
+ * decision on the array had another shape (rows, prefix chunks, steps,
+ * layers), the prepare kernel clears it first (a few microseconds).
+ *   noise, actions: as phx_expert_decide (device memory, or pinned host
+ *                   memory under capture).
+ * Every call on one device shares that device's array and its decision
+ * counter, and the array keeps what the last call left; calls that overlap
+ * on one device (different streams without ordering between them) race and
+ * give up after the bounded wait.  Only a handle on the persistent decision
+ * kernel (kernels_per_decision == 2) fits the array: any other handle gets
+ * PHX_E_SHAPE with a message naming the limit.  Returns PHX_OK,
+ * PHX_E_INVALID, PHX_E_SHAPE, PHX_E_STATE (no prefix loaded) or PHX_E_HIP
+ * (the array could not be set up on this device).  phx_expert_status
+ * reports the outcome as for phx_expert_decide.
+ */
+PHX_API int phx_expert_decide_noalloc(phx_expert* h, const float* noise, float* actions, phx_stream_t stream);
+
+/*
  * Prefix prefill ("FlashRT-PAI", section 2.1, Figure 1a: the language model
  * reads the prefix tokens and writes the key/value cache the action expert
  * attends to; the cache is written once per observation).  Runs the
@@ -370,7 +397,8 @@ PHX_API int phx_expert_status(const phx_expert* h, uint32_t* status);
  * b + 1 + 8 l + {0 qkv, 1 attention, 2 merge, 3 out projection, 4 its
  * all-reduce across XCDs, 5 gate/up, 6 down, 7 its all-reduce} for layer l,
  * then b + 1 + 8 * layers velocity head; E - 2 compute end, E - 1 weight
- * streaming end.  256 workgroups (workgroup b is rank b / 8 on XCD b % 8).
+ * streaming end.  256 workgroups (workgroup b is rank b / 8 on XCD
+ * (b + o) mod 8, the offset o fixed per launch).
  * If out is NULL or capacity is too small, *count receives the size needed
  * and PHX_E_SHAPE is returned.  Returns PHX_OK, PHX_E_INVALID, PHX_E_STATE
  * (no timeline), PHX_E_SHAPE or PHX_E_HIP.

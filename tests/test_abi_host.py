@@ -139,6 +139,7 @@ def test_weights_bytes_matches_the_input_layout(lib):
 def test_null_handles_are_rejected_without_a_gpu(lib):
     assert lib.phx_expert_load_prefix_kv(None, 0, None, None, 0, None) == -1
     assert lib.phx_expert_decide(None, None, None, None) == -1
+    assert lib.phx_expert_decide_noalloc(None, None, None, None) == -1
     n = ctypes.c_int(0)
     assert lib.phx_expert_kernels_per_decision(None, ctypes.byref(n)) == -1
     assert lib.phx_expert_launch_node(None, 0, None) == -1
