@@ -158,6 +158,7 @@ __device__ inline float wf(unsigned w) { return as_f(w & ~1u); }
 __device__ inline unsigned stale4(const u32x4& v, unsigned gen) {
   return ((v[0] ^ gen) | (v[1] ^ gen) | (v[2] ^ gen) | (v[3] ^ gen)) & 1u;
 }
+__device__ inline unsigned stale4(const u32x2& v, unsigned gen) { return ((v[0] ^ gen) | (v[1] ^ gen)) & 1u; }
 // B fragments (8 consecutive k values) of the hi and lo halves of 8 pair words
 __device__ inline bf16x8 frag_hi(const u32x4& v0, const u32x4& v1) {
   const u32x4 r = {__builtin_amdgcn_perm(v0[1], v0[0], 0x07060302u), __builtin_amdgcn_perm(v0[3], v0[2], 0x07060302u),
@@ -337,23 +338,34 @@ __device__ inline void cw_barrier(Ctx& c) {
   const unsigned target = c.barn * NCOMPUTE;
   const unsigned t0 = now_ticks();
   unsigned spins = 0;
-  while (lds_load(&c.sh->cwbar) < target) keep_waiting(c, t0, spins);
+  // the abort flag and the time limit are checked every 16th spin: a spin is
+  // one LDS read, and the barrier usually ends within a few
+  unsigned n = 0;
+  while (lds_load(&c.sh->cwbar) < target)
+    if ((++n & 15u) == 0u) keep_waiting(c, t0, spins);
   cbar();
 }
 
-// waits until ring positions [p0, p0 + n) hold their tiles
+// waits until ring positions [p0, p0 + n) hold their tiles (the four
+// loaders' counters read together)
 __device__ inline void wait_tiles(Ctx& c, unsigned p0, unsigned n) {
   const unsigned pe = p0 + n;
+  unsigned need[NLOADER];
+#pragma unroll
+  for (int q = 0; q < NLOADER; ++q) need[q] = pe <= (unsigned)q ? 0u : (pe - (unsigned)q + 3u) / 4u;
   const unsigned t0 = now_ticks();
   unsigned spins = 0;
+  while (true) {
+    unsigned r[NLOADER];
 #pragma unroll
-  for (int q = 0; q < NLOADER; ++q) {
-    if (pe <= (unsigned)q) continue;
-    const unsigned need = (pe - (unsigned)q + 3u) / 4u;  // this loader's positions below pe
-    while (lds_load(&c.sh->ready[q]) < need) {
-      __builtin_amdgcn_s_sleep(1);
-      keep_waiting(c, t0, spins);
-    }
+    for (int q = 0; q < NLOADER; ++q)
+      r[q] = __hip_atomic_load(&c.sh->ready[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < NLOADER; ++q) ok = ok && __builtin_amdgcn_readfirstlane(r[q]) >= need[q];
+    if (ok) break;
+    __builtin_amdgcn_s_sleep(1);
+    keep_waiting(c, t0, spins);
   }
   cbar();
 }
@@ -385,15 +397,36 @@ __device__ inline bf16x8 ring_tile(const Ctx& c, unsigned pos) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// ring slot of stream position p0 + off (off < RING), from s0 = p0 mod RING
+__device__ inline unsigned ring_slot(unsigned s0, unsigned off) {
+  const unsigned s = s0 + off;
+  return s >= (unsigned)RING ? s - (unsigned)RING : s;
+}
+__device__ inline u32x4 ring_read(const Ctx& c, unsigned slot) {
+  return *(const u32x4*)(c.ring + slot * TILE_BYTES + c.lane * 16);
+}
+// Keeps the LDS reads issued above it ahead of everything below it: the
+// products that follow then wait for each tile in turn while the later
+// reads are already in flight, instead of each read waiting for the product
+// before it.
+__device__ inline void reads_issued() { asm volatile("" ::: "memory"); }
+
 // acc[t] = sum over k-tiles kk of W(t, kk) . (hi + lo)(kk), the activation
 // pairs of k-tile kk in loads v[2 kk], v[2 kk + 1] and the weight tile at
-// ring position pos(t, kk).  The hi and lo products go to accumulators of
-// their own and the n-tiles are the inner loop, so no MFMA waits for the
-// result of the one before it (2 NT independent chains); the two halves are
-// added at the end.
-template <int NT, int KK, typename PF>
-__device__ __attribute__((always_inline)) inline void gemm_pairs(const Ctx& c, PF pos, const u32x4* v,
+// stream position p0 + off(t, kk).  Every tile read is issued before the
+// first product; the hi and lo products go to accumulators of their own and
+// the n-tiles are the inner loop, so no MFMA waits for the result of the one
+// before it (2 NT independent chains); the two halves are added at the end.
+template <int NT, int KK, typename OF>
+__device__ __attribute__((always_inline)) inline void gemm_pairs(const Ctx& c, unsigned p0, OF off, const u32x4* v,
                                                                  f32x4 (&acc)[NT]) {
+  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
+  u32x4 w[KK][NT];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[kk][t] = ring_read(c, ring_slot(s0, off(t, kk)));
+  reads_issued();
   f32x4 ah[NT], al[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) ah[t] = al[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -403,9 +436,9 @@ __device__ __attribute__((always_inline)) inline void gemm_pairs(const Ctx& c, P
     const bf16x8 bl = frag_lo(v[2 * kk], v[2 * kk + 1]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const bf16x8 w = ring_tile(c, pos(t, kk));
-      ah[t] = mma32(w, bh, ah[t]);
-      al[t] = mma32(w, bl, al[t]);
+      const bf16x8 wt = __builtin_bit_cast(bf16x8, w[kk][t]);
+      ah[t] = mma32(wt, bh, ah[t]);
+      al[t] = mma32(wt, bl, al[t]);
     }
   }
 #pragma unroll
@@ -454,6 +487,38 @@ __device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsi
     }
   }
 }
+// The same for 8-byte loads; loads whose bit in `live` is clear are never
+// issued and never wait (their values are zero).
+template <int POL, int N, typename AF>
+__device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, u32x2 (&v)[N],
+                                                           unsigned live = ~0u) {
+  static_assert(N <= 32, "a poll tracks at most 32 loads");
+  const unsigned t0 = now_ticks();
+  unsigned spins = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const LA la = addr(i);
+    v[i] = __builtin_amdgcn_raw_buffer_load_b64(c.X, ((live >> i) & 1u) ? la.vo : OOB,
+                                                __builtin_amdgcn_readfirstlane(la.so), POL);
+  }
+  while (true) {
+    unsigned stale = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) stale |= stale4(v[i], gen) << i;
+    stale &= live;
+    if (__ballot(stale != 0u) == 0ull) return;
+    keep_waiting(c, t0, spins);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const LA la = addr(i);
+      const bool st = (stale >> i) & 1u;
+      const u32x2 n =
+          __builtin_amdgcn_raw_buffer_load_b64(c.X, st ? la.vo : OOB, __builtin_amdgcn_readfirstlane(la.so), POL);
+      v[i] = st ? n : v[i];
+    }
+  }
+}
 
 template <int POL>
 __device__ inline void st4(const Ctx& c, unsigned off, const u32x4& w) {
@@ -478,35 +543,37 @@ __device__ inline void tl_mark(const Ctx& c, int ev) {
 
 // ---------------------------------------------------------------- owners
 // Every workgroup owns residual columns [32 r, 32 r + 32) (its rank's two
-// n-tiles) and keeps them in wave 0's registers: lane l holds row l % 16,
-// columns 32 r + 16 t + 4 g + [0, 4) in h[t].  The owners of the eight XCDs
-// hold the same columns and add the same partial sums in the same order.
+// n-tiles) and keeps them in registers, four rows per wave: lane l of wave w
+// holds row 4 w + l / 16, columns 32 r + 2 (l % 16) + [0, 2).  Each wave
+// updates and publishes its own rows, so no owner step waits for another
+// wave.  The owners of the eight XCDs hold the same columns and add the same
+// partial sums in the same order.  Rows past R repeat row R - 1.
+struct Own {
+  int row, crow;  // row of the lane, clamped to the last action row
+  unsigned col;   // first of the lane's two columns
+};
+__device__ inline Own own_of(const Ctx& c) {
+  const int r = 4 * c.wave + (c.lane >> 4);
+  return Own{r, r < c.R ? r : c.R - 1, (unsigned)(32 * c.rk + 2 * (c.lane & 15))};
+}
 
-// (1 + scale) of the owner's columns for one norm (issue early; use after)
-__device__ inline u32x4 owner_scale_load(const Ctx& c, int k, int norm, int t) {
-  const unsigned off = step_tab(c, k) + (unsigned)((norm * D + 32 * c.rk + 16 * t + 4 * c.g) * 4);
-  return __builtin_amdgcn_raw_buffer_load_b128(c.Y, off, 0, 0);
+// (1 + scale) of the lane's two columns for one norm (issue early; use after)
+__device__ inline u32x2 owner_scale_load(const Ctx& c, const Own& o, int k, int norm) {
+  return __builtin_amdgcn_raw_buffer_load_b64(c.Y, step_tab(c, k) + (unsigned)((norm * D) * 4) + o.col * 4u, 0, 0);
 }
 
 // publishes h * (1 + scale) as pair words and the per-row sums of squares of
-// the owner's 32 columns (wave 0)
+// the owner's 32 columns (every wave, its four rows)
 template <int T_N, int T_SS>
-__device__ inline void owner_publish(Ctx& c, const f32x4 (&h)[2], const u32x4 (&sv)[2], const Use& u) {
-  float s = 0.f;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w[i] = pair_word(h[t][i] * (1.0f + as_f(sv[t][i])), u.gen);
-      s += h[t][i] * h[t][i];
-    }
-    if (c.row < c.R)
-      st4<LST>(c, xb<T_N>(c, u.par) + (unsigned)((c.row * D + 32 * c.rk + 16 * t + 4 * c.g) * 4), w);
-  }
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
-  if (c.row < c.R && c.g == 0) st1<LST>(c, xb<T_SS>(c, u.par) + (unsigned)((c.row * WX + c.rk) * 4), f32_word(s, u.gen));
+__device__ inline void owner_publish(Ctx& c, const Own& o, const float (&h)[2], const u32x2& sv, const Use& u) {
+  const u32x2 w = {pair_word(h[0] * (1.0f + as_f(sv[0])), u.gen), pair_word(h[1] * (1.0f + as_f(sv[1])), u.gen)};
+  st2<LST>(c, xb<T_N>(c, u.par) + (unsigned)(o.row * D * 4) + o.col * 4u, w);
+  float s = h[0] * h[0] + h[1] * h[1];
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 8);
+  if ((c.lane & 15) == 0) st1<LST>(c, xb<T_SS>(c, u.par) + (unsigned)((o.row * WX + c.rk) * 4), f32_word(s, u.gen));
 }
 
 // Poll of a normalised activation (pairs [RP][D]) for this wave's 8 k-tiles
@@ -538,34 +605,42 @@ __device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const 
 // Each phase issues all the loads it needs (tables first, then the exchange
 // words) before waiting on any of them.
 
-// input projection h = x . W_in for the owner's two n-tiles (wave 0)
-__device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, f32x4 (&h)[2]) {
+// input projection h = x . W_in for the owner's two n-tiles: wave 0 forms
+// them, the waves take their rows through LDS
+__device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, float (&h)[2]) {
   refresh(c);
-  if (c.wave != 0) return;
-  const unsigned p0 = (unsigned)k * c.n_step;
-  u32x4 sv[2];
-  sv[0] = owner_scale_load(c, k, 0, 0);
-  sv[1] = owner_scale_load(c, k, 0, 1);
-  u32x4 v[2];
-  const unsigned vo = (unsigned)((c.crow * A + 8 * c.g) * 4);
-  if (k == 0) {
-    v[0] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, AUX_X + vo, 0, 0);
-    v[1] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, AUX_X + vo + 16u, 0, 0);
-  } else {
-    const Use ux = use_state(c, k - 1);
-    const unsigned bx = xb<X_X>(c, ux.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vo + 16u * (unsigned)i, bx}; }, ux.gen, v);
-  }
-  bf16x8 xh, xl;
-  frag_split_f32(v[0], v[1], xh, xl);
-  wait_tiles(c, p0, 2);
+  const Own o = own_of(c);
+  const u32x2 sv = owner_scale_load(c, o, k, 0);
+  float* hs = (float*)red_take(c);  // [RP][32] f32
+  if (c.wave == 0) {
+    const unsigned p0 = (unsigned)k * c.n_step;
+    u32x4 v[2];
+    const unsigned vo = (unsigned)((c.crow * A + 8 * c.g) * 4);
+    if (k == 0) {
+      v[0] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, AUX_X + vo, 0, 0);
+      v[1] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, AUX_X + vo + 16u, 0, 0);
+    } else {
+      const Use ux = use_state(c, k - 1);
+      const unsigned bx = xb<X_X>(c, ux.par);
+      poll<NTP>(c, [&](int i) -> LA { return LA{vo + 16u * (unsigned)i, bx}; }, ux.gen, v);
+    }
+    bf16x8 xh, xl;
+    frag_split_f32(v[0], v[1], xh, xl);
+    wait_tiles(c, p0, 2);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    h[t] = mma32(ring_tile(c, p0 + t), xh, f32x4{0.f, 0.f, 0.f, 0.f});
-    h[t] = mma32(ring_tile(c, p0 + t), xl, h[t]);
+    for (int t = 0; t < 2; ++t) {
+      f32x4 a = mma32(ring_tile(c, p0 + t), xh, f32x4{0.f, 0.f, 0.f, 0.f});
+      a = mma32(ring_tile(c, p0 + t), xl, a);
+      // lane: row lane % 16, columns 16 t + 4 g + [0, 4)
+      *(f32x4*)(hs + c.row * 32 + 16 * t + 4 * c.g) = a;
+    }
+    release_ring(c, p0 + 2);
   }
-  release_ring(c, p0 + 2);
-  owner_publish<X_N, X_SS>(c, h, sv, use_norm(c, k, 0));
+  cw_barrier(c);
+  const float2 hv = *(const float2*)(hs + o.row * 32 + 2 * (c.lane & 15));
+  h[0] = hv.x;
+  h[1] = hv.y;
+  owner_publish<X_N, X_SS>(c, o, h, sv, use_norm(c, k, 0));
 }
 
 // QKV projection of two n-tiles (K = D split over the four waves), epilogue
@@ -591,7 +666,7 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
   poll_normed<X_N, X_SS>(c, u, v);
   wait_tiles(c, p0, 64);
   f32x4 acc[2];
-  gemm_pairs<2, 8>(c, [&](int t, int kk) { return p0 + 32u * t + 8u * c.wave + kk; }, v, acc);
+  gemm_pairs<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
@@ -682,12 +757,16 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_att;
   wait_tiles(c, p0, 64);
   // S^T for keys [16 w, 16 w + 16) of the chunk: lane holds keys 4 g + e of row `row`
+  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
+  u32x4 kt[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kt[s] = ring_read(c, ring_slot(s0, 8u * c.wave + s));
+  reads_issued();
   f32x4 sth = f32x4{0.f, 0.f, 0.f, 0.f}, stl = sth;  // hi and lo products in chains of their own
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const bf16x8 kt = ring_tile(c, p0 + 8u * c.wave + s);
-    sth = mma32(kt, qh[s], sth);
-    stl = mma32(kt, ql[s], stl);
+    sth = mma32(__builtin_bit_cast(bf16x8, kt[s]), qh[s], sth);
+    stl = mma32(__builtin_bit_cast(bf16x8, kt[s]), ql[s], stl);
   }
   const f32x4 st = sth + stl;
   float sv[4];
@@ -726,14 +805,23 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
   f32x4 oacc[4], olo[4];  // the lo products of P in accumulators of their own
 #pragma unroll
   for (int d = 0; d < 4; ++d) oacc[d] = olo[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 vt[4][2];
+  s16x4 pah[4], pal[4];
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg) {
-    const s16x4 ah = c.sh->att_p[kg][0][c.lane];
-    const s16x4 al = c.sh->att_p[kg][1][c.lane];
+    pah[kg] = c.sh->att_p[kg][0][c.lane];
+    pal[kg] = c.sh->att_p[kg][1][c.lane];
+#pragma unroll
+    for (int dp = 0; dp < 2; ++dp) vt[kg][dp] = ring_read(c, ring_slot(s0, 32u + 8u * kg + 2u * c.wave + dp));
+  }
+  reads_issued();
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) {
+    const s16x4 ah = pah[kg];
+    const s16x4 al = pal[kg];
 #pragma unroll
     for (int dp = 0; dp < 2; ++dp) {
-      const unsigned pos = p0 + 32u + 8u * kg + 2u * c.wave + dp;
-      const u32x4 vv = *(const u32x4*)(c.ring + (pos % RING) * TILE_BYTES + c.lane * 16);
+      const u32x4 vv = vt[kg][dp];
       const s16x4 b0 = __builtin_bit_cast(s16x4, u32x2{vv[0], vv[1]});
       const s16x4 b1 = __builtin_bit_cast(s16x4, u32x2{vv[2], vv[3]});
       oacc[2 * dp] = mma16(ah, b0, oacc[2 * dp]);
@@ -851,88 +939,48 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
 }
 
 // Merges the head's key chunks for dims [32 s, 32 s + 32) and writes the
-// normalised attention output as pairs.  Lane: dims 32 s + 4 q + [0, 4)
-// (q = lane % 8) of rows rb and rb + 8 (rb = lane / 8).  Wave w reads chunks
-// w, w + 4, w + 8, w + 12: per chunk the (max, sum) of row lane % 16 and the
-// two rows' partial outputs.  Every lane forms the statistics over all
-// chunks from LDS, weights its chunks' partials by exp(m_c - M) / L, and the
-// four waves' sums meet in LDS in wave order.
+// normalised attention output as pairs.  Wave w finishes rows 4 w .. 4 w + 3
+// on its own, with no exchange between the waves: lane l takes row
+// 4 w + l / 16 and dims 32 s + 2 (l % 16) + [0, 2), reads that row's
+// (max, sum) and its two partial outputs of every chunk, and merges the
+// chunks in chunk order.  Rows past R repeat row R - 1 (nobody reads them).
 __device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, int l) {
   refresh(c);
   if (!is_merge(c)) return;
   const int s = c.rk - R_MERGE;
   const int nch = c.nc + 1;
   const Use u = use_layer(c, k, l);
-  const int q = c.lane & 7, rb = c.lane >> 3;
-  const int rA = rb < c.R ? rb : c.R - 1, rB = rb + 8 < c.R ? rb + 8 : c.R - 1;
-  unsigned char* red = red_take(c);
-  float* mls = (float*)red;                       // [MAX_CHUNKS][RP] max, then [MAX_CHUNKS][RP] sum
-  f32x4* part = (f32x4*)(red + 2 * MAX_CHUNKS * RP * 4);  // [4 waves][2 rows][64 lanes]
-  u32x4 v[12];
+  const int r = 4 * c.wave + (c.lane >> 4);
+  const int rc = r < c.R ? r : c.R - 1;
+  const int dd = 32 * s + 2 * (c.lane & 15);
+  u32x2 v[2 * MAX_CHUNKS];  // chunk cc: (max, sum) at 2 cc, the two partial outputs at 2 cc + 1
   {
     const unsigned bo = xb<X_AO>(c, u.par), bm = xb<X_AML>(c, u.par);
-    const unsigned vA = (unsigned)((rA * DH + 32 * s + 4 * q) * 4), vB = (unsigned)((rB * DH + 32 * s + 4 * q) * 4);
-    const unsigned vm = (unsigned)(c.crow * 16);
+    const unsigned vo = (unsigned)((rc * DH + dd) * 4), vm = (unsigned)(rc * 16);
+    const unsigned live = nch >= MAX_CHUNKS ? ~0u : (1u << (2 * nch)) - 1u;
     poll<NTP>(c, [&](int i) -> LA {
-      const int cc0 = c.wave + NCOMPUTE * (i / 3);
-      const int cc = cc0 < nch ? cc0 : nch - 1;  // past the last chunk: read the last one again
-      const int j = i % 3;
-      if (j == 0) return LA{vm, bm + (unsigned)(cc * RP * 16)};
-      return LA{j == 1 ? vA : vB, bo + (unsigned)(cc * RP * DH * 4)};
-    }, u.gen, v);
+      const int cc = i >> 1;
+      if (i & 1) return LA{vo, bo + (unsigned)(cc * RP * DH * 4)};
+      return LA{vm, bm + (unsigned)(cc * RP * 16)};
+    }, u.gen, v, live);
   }
+  float M = M_EMPTY;
 #pragma unroll
-  for (int jq = 0; jq < 4; ++jq) {
-    const int cc = c.wave + NCOMPUTE * jq;
-    if (cc < nch && c.lane < RP) {
-      mls[cc * RP + c.lane] = wf(v[3 * jq][0]);
-      mls[(MAX_CHUNKS + cc) * RP + c.lane] = wf(v[3 * jq][1]);
+  for (int cc = 0; cc < MAX_CHUNKS; ++cc)
+    if (cc < nch) M = fmaxf(M, wf(v[2 * cc][0]));
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < MAX_CHUNKS; ++cc) {
+    if (cc < nch) {
+      const float e = fexp(wf(v[2 * cc][0]) - M);
+      L += e * wf(v[2 * cc][1]);
+      o0 += e * wf(v[2 * cc + 1][0]);
+      o1 += e * wf(v[2 * cc + 1][1]);
     }
   }
-  cw_barrier(c);
-  float accA[4] = {0.f, 0.f, 0.f, 0.f}, accB[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int r = half == 0 ? rb : rb + 8;
-    float M = M_EMPTY;
-    for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, mls[cc * RP + r]);
-    float L = 0.f;
-    for (int cc = 0; cc < nch; ++cc) L += fexp(mls[cc * RP + r] - M) * mls[(MAX_CHUNKS + cc) * RP + r];
-    const float invL = frcp(L);
-#pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      const int cc = c.wave + NCOMPUTE * jq;
-      if (cc < nch) {
-        const float wgt = fexp(mls[cc * RP + r] - M) * invL;
-        const u32x4 pv = v[3 * jq + 1 + half];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (half == 0)
-            accA[e] += wgt * wf(pv[e]);
-          else
-            accB[e] += wgt * wf(pv[e]);
-        }
-      }
-    }
-  }
-  part[(c.wave * 2 + 0) * 64 + c.lane] = f32x4{accA[0], accA[1], accA[2], accA[3]};
-  part[(c.wave * 2 + 1) * 64 + c.lane] = f32x4{accB[0], accB[1], accB[2], accB[3]};
-  cw_barrier(c);
-  if (c.wave < 2) {
-    // wave 0 finishes rows rb, wave 1 rows rb + 8, summing the waves in order
-    const int half = c.wave;
-    f32x4 a = part[(0 * 2 + half) * 64 + c.lane];
-    a += part[(1 * 2 + half) * 64 + c.lane];
-    a += part[(2 * 2 + half) * 64 + c.lane];
-    a += part[(3 * 2 + half) * 64 + c.lane];
-    const int r = rb + 8 * half;
-    if (r < c.R) {
-      const Use uo = use_layer(c, k, l);
-      const u32x4 w = {pair_word(a[0], uo.gen), pair_word(a[1], uo.gen), pair_word(a[2], uo.gen),
-                       pair_word(a[3], uo.gen)};
-      st4<LST>(c, xb<X_O>(c, uo.par) + (unsigned)((r * DH + 32 * s + 4 * q) * 4), w);
-    }
-  }
+  const float inv = frcp(L);
+  const u32x2 w = {pair_word(o0 * inv, u.gen), pair_word(o1 * inv, u.gen)};
+  st2<LST>(c, xb<X_O>(c, u.par) + (unsigned)((r * DH + dd) * 4), w);
 }
 
 // out projection of the head's 256 rows for output columns [64 o, 64 o + 64)
@@ -952,7 +1000,7 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
   }
   wait_tiles(c, p0, 32);
   f32x4 acc[4];
-  gemm_pairs<4, 2>(c, [&](int t, int j) { return p0 + 8u * t + 2u * c.wave + j; }, v, acc);
+  gemm_pairs<4, 2>(c, p0, [&](int t, int j) { return 8u * t + 2u * c.wave + j; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 4; ++t) red[(c.wave * 4 + t) * 64 + c.lane] = acc[t];
@@ -966,38 +1014,28 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
 }
 
 // All-reduce of a residual update (T_P: the eight XCDs' partial sums), the
-// residual add and the next norm's producer half.  Wave w reads the partials
-// of XCDs 2 w and 2 w + 1; the sum runs over XCDs in order on every XCD.
+// residual add and the next norm's producer half.  Every wave reads the
+// eight partials of its own rows and adds them in the same order on every
+// XCD.
 template <int T_P, int T_N, int T_SS>
 __device__ __attribute__((always_inline)) inline void ph_own(Ctx& c, int k, int norm, const Use& u, const Use& un,
-                                                             f32x4 (&h)[2]) {
+                                                             float (&h)[2]) {
   refresh(c);
-  u32x4 sv[2];
-  if (c.wave == 0) {
-    sv[0] = owner_scale_load(c, k, norm, 0);
-    sv[1] = owner_scale_load(c, k, norm, 1);
-  }
-  u32x4 v[4];
+  const Own o = own_of(c);
+  const u32x2 sv = owner_scale_load(c, o, k, norm);
+  u32x2 v[NX];
   {
-    const unsigned vo = (unsigned)(((2 * c.wave * RP + c.crow) * D + 32 * c.rk + 4 * c.g) * 4);
+    const unsigned vo = (unsigned)(o.crow * D * 4) + o.col * 4u;
     const unsigned bp = xb<T_P>(c, u.par);
-    // load i: XCD 2 w + (i >> 1), n-tile i & 1
-    poll<SC1>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * RP * D * 4 + (i & 1) * 64), bp}; }, u.gen, v);
+    poll<SC1>(c, [&](int i) -> LA { return LA{vo + (unsigned)(i * RP * D * 4), bp}; }, u.gen, v);
   }
-  f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    f32x4 s;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] = wf(v[t][e]) + wf(v[2 + t][e]);
-    red[(c.wave * 2 + t) * 64 + c.lane] = s;
+  for (int e = 0; e < 2; ++e) {
+    const float s01 = wf(v[0][e]) + wf(v[1][e]), s23 = wf(v[2][e]) + wf(v[3][e]);
+    const float s45 = wf(v[4][e]) + wf(v[5][e]), s67 = wf(v[6][e]) + wf(v[7][e]);
+    h[e] += ((s01 + s23) + s45) + s67;
   }
-  cw_barrier(c);
-  if (c.wave == 0) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) h[t] += red_sum(red, 2, t, c.lane);
-    owner_publish<T_N, T_SS>(c, h, sv, un);
-  }
+  owner_publish<T_N, T_SS>(c, o, h, sv, un);
 }
 
 // gate/up projection of two n-tiles with the GeGLU epilogue: features
@@ -1013,7 +1051,7 @@ __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l
   poll_normed<X_N2, X_SS2>(c, u, v);
   wait_tiles(c, p0, 64);
   f32x4 acc[2];
-  gemm_pairs<2, 8>(c, [&](int t, int kk) { return p0 + 32u * t + 8u * c.wave + kk; }, v, acc);
+  gemm_pairs<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
@@ -1049,7 +1087,7 @@ __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int
   }
   wait_tiles(c, p0, 32);
   f32x4 acc[2];
-  gemm_pairs<2, 4>(c, [&](int t, int j) { return p0 + 16u * t + 4u * c.wave + j; }, v, acc);
+  gemm_pairs<2, 4>(c, p0, [&](int t, int j) { return 16u * t + 4u * c.wave + j; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
@@ -1083,7 +1121,7 @@ __device__ __attribute__((always_inline)) inline void ph_vel(Ctx& c, int k, f32x
   poll_normed<X_N, X_SS>(c, u, v);
   wait_tiles(c, p0, 64);
   f32x4 acc[2];
-  gemm_pairs<2, 8>(c, [&](int t, int kk) { return p0 + 32u * t + 8u * c.wave + kk; }, v, acc);
+  gemm_pairs<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
@@ -1321,12 +1359,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
     if (c.wave == NCOMPUTE) tl_mark(c, timeline_events(c.S, c.NL) - 1);
     return;
   }
-  f32x4 h[2], x[2];
+  float h[2] = {0.f, 0.f};
+  f32x4 x[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    h[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    x[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < 2; ++t) x[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (is_vel(c) && c.wave == 0) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
