@@ -55,10 +55,10 @@ constexpr int NCOMPUTE = 4;         // compute waves (waves 0..3); waves 4..7 lo
 constexpr int NLOADER = 4;
 constexpr int THREADS = 64 * (NCOMPUTE + NLOADER);
 // roles by rank r = b / 8 inside an XCD
-constexpr int R_QKV = 16;           // ranks 16..25: QKV n-tile pairs of the XCD's 20 QKV n-tiles
-constexpr int N_QKV = 10;
+constexpr int R_QKV = 12;           // ranks 12..31: one QKV n-tile each of the XCD's 20 (16 of query head
+constexpr int N_QKV = 20;           // x, 2 of its key share, 2 of its value share)
 constexpr int R_MERGE = 16;         // ranks 16..23: merge of the head's key chunks, 32 dims each
-constexpr int R_O = 16;             // ranks 16..31: out projection, 4 n-tiles each
+constexpr int O_NT = 2;             // out projection: every rank, 2 n-tiles each
 constexpr int R_VEL = 31;           // velocity head and Euler update (each XCD keeps its own copy of x)
 
 __host__ __device__ constexpr unsigned al256(unsigned x) { return (x + 255u) & ~255u; }

@@ -119,6 +119,57 @@ __device__ inline float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426
 __device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ inline float frsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// Cross-lane reductions without the LDS unit.  DPP moves within rows of 16
+// lanes (quad permutations, half-row and row mirrors); the permlane swaps
+// pair lanes l and l ^ 16, or l and l ^ 32, and every lane adds the two in
+// the same order, so all lanes of a group hold identical bits.
+template <int CTRL>
+__device__ inline float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+// sum over the 4 lanes of a quad
+__device__ inline float sum_quad(float v) {
+  v += dppf<DPP_XOR1>(v);
+  return v + dppf<DPP_XOR2>(v);
+}
+// sum over the 16 lanes of a row
+__device__ inline float sum_row16(float v) {
+  v = sum_quad(v);
+  v += dppf<DPP_HALF_MIRROR>(v);
+  return v + dppf<DPP_MIRROR>(v);
+}
+// sum and maximum over lanes l, l ^ 16, l ^ 32, l ^ 48
+// (the value of lane l, that of lane l ^ 16) in the order (lower lane, upper
+// lane) for every lane; the same with l ^ 32.  Written as assembly: the
+// swap writes both of its registers, and the compiler's form of it has been
+// seen to hand back one of the two results for both.
+__device__ inline float2 swap16(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return float2{a, b};
+}
+__device__ inline float2 swap32(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return float2{a, b};
+}
+__device__ inline float sum_x16_x32(float v) {
+  const float2 a = swap16(v);
+  v = a.x + a.y;
+  const float2 b = swap32(v);
+  return b.x + b.y;
+}
+__device__ inline float max_x16_x32(float v) {
+  const float2 a = swap16(v);
+  v = fmaxf(a.x, a.y);
+  const float2 b = swap32(v);
+  return fmaxf(b.x, b.y);
+}
+
 // GeGLU's tanh-approximated GELU, with tanh(u) = 1 - 2 / (exp(2u) + 1)
 __device__ inline float gelu_tanh(float z) {
   const float k = 0.7978845608028654f;  // sqrt(2/pi)
@@ -219,8 +270,12 @@ struct Ctx {
 __device__ inline bool is_qkv(const Ctx& c) { return c.rk >= R_QKV && c.rk < R_QKV + N_QKV; }
 __device__ inline bool is_att(const Ctx& c) { return c.rk <= c.nc; }
 __device__ inline bool is_merge(const Ctx& c) { return c.rk >= R_MERGE && c.rk < R_MERGE + DH / 32; }
-__device__ inline bool is_o(const Ctx& c) { return c.rk >= R_O; }
 __device__ inline bool is_vel(const Ctx& c) { return c.rk == R_VEL; }
+// QKV n-tile of QKV workgroup i on XCD x: query head x's tiles, then this
+// XCD's two tiles of the key head and two of the value head
+__device__ inline int qkv_ntile(int i, int x) {
+  return i < 16 ? 16 * x + i : (i < 18 ? 16 * H + 2 * x + (i - 16) : 16 * (H + 1) + 2 * x + (i - 18));
+}
 
 // Passes the context's uniform fields through an empty asm statement.  Every
 // phase starts with it, so that what a phase derives from them (role tests,
@@ -569,10 +624,7 @@ __device__ inline void owner_publish(Ctx& c, const Own& o, const float (&h)[2], 
   const u32x2 w = {pair_word(h[0] * (1.0f + as_f(sv[0])), u.gen), pair_word(h[1] * (1.0f + as_f(sv[1])), u.gen)};
   st2<LST>(c, xb<T_N>(c, u.par) + (unsigned)(o.row * D * 4) + o.col * 4u, w);
   float s = h[0] * h[0] + h[1] * h[1];
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
-  s += __shfl_xor(s, 8);
+  s = sum_row16(s);
   if ((c.lane & 15) == 0) st1<LST>(c, xb<T_SS>(c, u.par) + (unsigned)((o.row * WX + c.rk) * 4), f32_word(s, u.gen));
 }
 
@@ -594,8 +646,7 @@ __device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const 
     float s = 0.f;
 #pragma unroll
     for (int i = 16; i < 18; ++i) s += (wf(v[i][0]) + wf(v[i][1])) + (wf(v[i][2]) + wf(v[i][3]));
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
+    s = sum_quad(s);
     if ((c.lane & 3) == 0) c.sh->rrow[srow] = frsq(s / (float)D + c.eps);
   }
 }
@@ -643,20 +694,17 @@ __device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, float
   owner_publish<X_N, X_SS>(c, o, h, sv, use_norm(c, k, 0));
 }
 
-// QKV projection of two n-tiles (K = D split over the four waves), epilogue
-// 1/rms, shift . W and RoPE; writes q of the XCD's head (local) or the
-// XCD's share of the action keys and values (device scope)
+// QKV projection of one n-tile (K = D split over the four waves), epilogue
+// 1/rms, shift . W and RoPE (wave 0); writes q of the XCD's head (local) or
+// the XCD's share of the action keys and values (device scope)
 __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int l) {
   refresh(c);
   if (!is_qkv(c)) return;
   const int i = c.rk - R_QKV;
-  // this workgroup's first QKV n-tile: query head xcd (tiles 2i, 2i + 1), or the
-  // key head's / value head's tiles 2 xcd, 2 xcd + 1
-  const int nt0 = i < 8 ? 16 * c.xcd + 2 * i : (i == 8 ? 16 * H + 2 * c.xcd : 16 * (H + 1) + 2 * c.xcd);
+  const int nt = qkv_ntile(i, c.xcd);
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer;
   const Use u = use_norm(c, k, l);
   const Use uo = use_layer(c, k, l);
-  const int nt = nt0 + (c.wave & 1);  // epilogue tables of the n-tile this wave finishes (waves 0, 1)
   const int tt = nt % 16;
   const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
       c.Y, step_tab(c, k) + st_swqkv(c.NL) + (unsigned)((l * NQKV + nt * 16 + 4 * c.g) * 4), 0, 0);
@@ -664,21 +712,20 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
       c.Y, AUX_ROPE + (unsigned)((c.row * (DH / 2) + 8 * tt + 2 * c.g) * 8), 0, 0);
   u32x4 v[18];
   poll_normed<X_N, X_SS>(c, u, v);
-  wait_tiles(c, p0, 64);
-  f32x4 acc[2];
-  gemm_pairs<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
+  wait_tiles(c, p0, 32);
+  f32x4 acc[1];
+  gemm_pairs<1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
+  red[c.wave * 64 + c.lane] = acc[0];
   cw_barrier(c);
-  release_ring(c, p0 + 64u);
-  if (c.wave < 2) {
-    const f32x4 s = red_sum(red, 2, c.wave, c.lane);
+  release_ring(c, p0 + 32u);
+  if (c.wave == 0) {
+    const f32x4 s = red_sum(red, 1, 0, c.lane);
     const float rr = c.sh->rrow[c.row];
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = rr * s[e] + as_f(sw[e]);
-    if (i < 9) {  // query and key columns are rotated
+    if (i < 18) {  // query and key columns are rotated
       const float c0 = as_f(cs[0]), s0 = as_f(cs[1]);
       const float c1 = as_f(cs[2]), s1 = as_f(cs[3]);
       const float x0 = y[0], x1 = y[1], x2 = y[2], x3 = y[3];
@@ -692,12 +739,12 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
       const int j = 8 * tt + 2 * c.g;
       const u32x2 w01 = {pair_word(y[0], uo.gen), pair_word(y[1], uo.gen)};
       const u32x2 w23 = {pair_word(y[2], uo.gen), pair_word(y[3], uo.gen)};
-      if (i < 8) {
+      if (i < 16) {
         const unsigned o = xb<X_Q>(c, uo.par) + (unsigned)((c.row * DH + j) * 4);
         st2<LST>(c, o, w01);
         st2<LST>(c, o + (DH / 2) * 4u, w23);
       } else {
-        const unsigned o = xb<X_KV>(c, uo.par) + (unsigned)((c.row * 2 * DH + (i - 8) * DH + j) * 4);
+        const unsigned o = xb<X_KV>(c, uo.par) + (unsigned)((c.row * 2 * DH + (i >= 18 ? DH : 0) + j) * 4);
         st2<SC1>(c, o, w01);
         st2<SC1>(c, o + (DH / 2) * 4u, w23);
       }
@@ -777,8 +824,7 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
     sv[e] = key < c.L ? st[e] * scale : -INFINITY;
     mw = fmaxf(mw, sv[e]);
   }
-  mw = fmaxf(mw, __shfl_xor(mw, 16));
-  mw = fmaxf(mw, __shfl_xor(mw, 32));
+  mw = max_x16_x32(mw);
   if (c.g == 0) c.sh->att_m[c.wave][c.row] = mw;
   cw_barrier(c);
   const float m_row = fmaxf(fmaxf(c.sh->att_m[0][c.row], c.sh->att_m[1][c.row]),
@@ -794,8 +840,7 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
     ph[e] = a;
     pl[e] = b;
   }
-  lw += __shfl_xor(lw, 16);
-  lw += __shfl_xor(lw, 32);
+  lw = sum_x16_x32(lw);
   if (c.g == 0) c.sh->att_l[c.wave][c.row] = lw;
   c.sh->att_p[c.wave][0][c.lane] = ph;
   c.sh->att_p[c.wave][1][c.lane] = pl;
@@ -909,8 +954,7 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
     sv[e] = key < c.R ? st[e] * scale : -INFINITY;
     mw = fmaxf(mw, sv[e]);
   }
-  mw = fmaxf(mw, __shfl_xor(mw, 16));
-  mw = fmaxf(mw, __shfl_xor(mw, 32));
+  mw = max_x16_x32(mw);
   const float m_row = mw;
   float lw = 0.f;
   s16x4 ph, pl;
@@ -923,8 +967,7 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
     ph[e] = a;
     pl[e] = b;
   }
-  lw += __shfl_xor(lw, 16);
-  lw += __shfl_xor(lw, 32);
+  lw = sum_x16_x32(lw);
   f32x4 oacc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -983,13 +1026,13 @@ __device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, in
   st2<LST>(c, xb<X_O>(c, u.par) + (unsigned)((r * DH + dd) * 4), w);
 }
 
-// out projection of the head's 256 rows for output columns [64 o, 64 o + 64)
-// (four n-tiles; K split over the four waves): a partial sum of the residual
-// update, published at device scope for the owners of every XCD
+// out projection of the head's 256 rows for output columns
+// [32 o, 32 o + 32) (two n-tiles; K split over the four waves): a partial
+// sum of the residual update, published at device scope for the owners of
+// every XCD
 __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l) {
   refresh(c);
-  if (!is_o(c)) return;
-  const int o = c.rk - R_O;
+  const int o = c.rk;
   const Use u = use_layer(c, k, l);
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_o;
   u32x4 v[4];
@@ -998,18 +1041,21 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
     const unsigned bo = xb<X_O>(c, u.par);
     poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bo}; }, u.gen, v);
   }
-  wait_tiles(c, p0, 32);
-  f32x4 acc[4];
-  gemm_pairs<4, 2>(c, p0, [&](int t, int j) { return 8u * t + 2u * c.wave + j; }, v, acc);
+  wait_tiles(c, p0, 8 * O_NT);
+  f32x4 acc[O_NT];
+  gemm_pairs<O_NT, 2>(c, p0, [&](int t, int j) { return 8u * t + 2u * c.wave + j; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) red[(c.wave * 4 + t) * 64 + c.lane] = acc[t];
+  for (int t = 0; t < O_NT; ++t) red[(c.wave * O_NT + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
-  release_ring(c, p0 + 32u);
-  const f32x4 s = red_sum(red, 4, c.wave, c.lane);  // wave t finishes n-tile t
-  if (c.row < c.R) {
-    const u32x4 w = {f32_word(s[0], u.gen), f32_word(s[1], u.gen), f32_word(s[2], u.gen), f32_word(s[3], u.gen)};
-    st4<SC1>(c, xb<X_OP>(c, u.par) + (unsigned)(((c.xcd * RP + c.row) * D + 64 * o + 16 * c.wave + 4 * c.g) * 4), w);
+  release_ring(c, p0 + 8u * O_NT);
+  if (c.wave < O_NT) {
+    const f32x4 s = red_sum(red, O_NT, c.wave, c.lane);  // wave t finishes n-tile t
+    if (c.row < c.R) {
+      const u32x4 w = {f32_word(s[0], u.gen), f32_word(s[1], u.gen), f32_word(s[2], u.gen), f32_word(s[3], u.gen)};
+      st4<SC1>(c, xb<X_OP>(c, u.par) +
+                      (unsigned)(((c.xcd * RP + c.row) * D + 16 * O_NT * o + 16 * c.wave + 4 * c.g) * 4), w);
+    }
   }
 }
 
@@ -1187,10 +1233,8 @@ __device__ inline void run_params(const Ctx& c, int run, unsigned& off, int& cnt
   const unsigned long long lo = (unsigned long long)l * W_LAYER;
   if (u == 0) {
     if (is_qkv(c)) {
-      const int i = r - R_QKV;
-      const int nt0 = i < 8 ? 16 * x + 2 * i : (i == 8 ? 16 * H + 2 * x : 16 * (H + 1) + 2 * x);
-      cnt = 64;
-      off = (unsigned)((W_QKV0 + lo + (unsigned long long)nt0 * KT_D * TILE_ELEMS) * 2ull);
+      cnt = KT_D;
+      off = (unsigned)((W_QKV0 + lo + (unsigned long long)qkv_ntile(r - R_QKV, x) * KT_D * TILE_ELEMS) * 2ull);
     }
   } else if (u == 1) {
     if (r < c.nc) {
@@ -1199,8 +1243,8 @@ __device__ inline void run_params(const Ctx& c, int run, unsigned& off, int& cnt
       off = (unsigned)((l * c.nc + r) * 64) * TILE_BYTES;
     }
   } else if (u <= 5) {
-    if (is_o(c)) {
-      const int nt = 4 * (r - R_O) + (u - 2);
+    if (u - 2 < O_NT) {
+      const int nt = O_NT * r + (u - 2);
       cnt = 8;
       off = (unsigned)((W_O0 + lo + ((unsigned long long)nt * KT_HD + 8 * x) * TILE_ELEMS) * 2ull);
     }
@@ -1346,9 +1390,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
   c.L = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b32(c.Y, AUX_LENS, 0, 0));
   c.crow = c.row < c.R ? c.row : c.R - 1;
   // stream layout of this workgroup (must match run_params)
-  c.o_att = is_qkv(c) ? 64u : 0u;
+  c.o_att = is_qkv(c) ? (unsigned)KT_D : 0u;
   c.o_o = c.o_att + (c.rk < c.nc ? 64u : 0u);
-  c.o_gu = c.o_o + (is_o(c) ? 32u : 0u);
+  c.o_gu = c.o_o + 8u * O_NT;
   c.o_dn = c.o_gu + 64u;
   c.n_layer = c.o_dn + 32u;
   c.n_step = 2u + (unsigned)c.NL * c.n_layer + (is_vel(c) ? 64u : 0u);
