@@ -81,7 +81,7 @@ enum ExType : int {
   X_SS2 = 7,  // local: [RP][WX]
   X_A = 8,    // local: GeGLU output of the XCD's features, pairs [RP][FX]
   X_X = 9,    // local: state x [RP][A] f32
-  X_KV = 10,  // device: action keys and values, pairs [RP][2 DH] (k dims 0..255, v dims 256..511)
+  X_KV = 10,  // device: action keys, pairs [RP][DH], then action values transposed, pairs [DH][RP]
   X_OP = 11,  // device: out-projection partial sums per XCD [NX][RP][D] f32
   X_DP = 12,  // device: down-projection partial sums per XCD [NX][RP][D] f32
   NXT = 13

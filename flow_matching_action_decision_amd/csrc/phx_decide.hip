@@ -734,39 +734,44 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
       y[1] = x1 * c1 - x3 * s1;
       y[3] = x3 * c1 + x1 * s1;
     }
-    if (c.row < c.R) {
-      // the lane's four columns are head dims j, j + 1, j + 128, j + 129
-      const int j = 8 * tt + 2 * c.g;
-      const u32x2 w01 = {pair_word(y[0], uo.gen), pair_word(y[1], uo.gen)};
-      const u32x2 w23 = {pair_word(y[2], uo.gen), pair_word(y[3], uo.gen)};
-      if (i < 16) {
-        const unsigned o = xb<X_Q>(c, uo.par) + (unsigned)((c.row * DH + j) * 4);
-        st2<LST>(c, o, w01);
-        st2<LST>(c, o + (DH / 2) * 4u, w23);
-      } else {
-        const unsigned o = xb<X_KV>(c, uo.par) + (unsigned)((c.row * 2 * DH + (i >= 18 ? DH : 0) + j) * 4);
-        st2<SC1>(c, o, w01);
-        st2<SC1>(c, o + (DH / 2) * 4u, w23);
-      }
+    // the lane's four columns are head dims j, j + 1, j + 128, j + 129; every
+    // row is written (rows past R repeat row R - 1)
+    const int j = 8 * tt + 2 * c.g;
+    const u32x2 w01 = {pair_word(y[0], uo.gen), pair_word(y[1], uo.gen)};
+    const u32x2 w23 = {pair_word(y[2], uo.gen), pair_word(y[3], uo.gen)};
+    if (i < 16) {
+      const unsigned o = xb<X_Q>(c, uo.par) + (unsigned)((c.row * DH + j) * 4);
+      st2<LST>(c, o, w01);
+      st2<LST>(c, o + (DH / 2) * 4u, w23);
+    } else if (i < 18) {
+      const unsigned o = xb<X_KV>(c, uo.par) + (unsigned)((c.row * DH + j) * 4);
+      st2<SC1>(c, o, w01);
+      st2<SC1>(c, o + (DH / 2) * 4u, w23);
+    } else {
+      // values transposed: [dim][key]
+      const unsigned o = xb<X_KV>(c, uo.par) + (unsigned)(RP * DH * 4) + (unsigned)((j * RP + c.row) * 4);
+      st1<SC1>(c, o, w01[0]);
+      st1<SC1>(c, o + RP * 4u, w01[1]);
+      st1<SC1>(c, o + (DH / 2) * RP * 4u, w23[0]);
+      st1<SC1>(c, o + (DH / 2 + 1) * RP * 4u, w23[1]);
     }
   }
 }
 
 // outputs of one key chunk of the head: unnormalised O [row][dim] (f32 words)
-// and (max, sum) per row
+// and (max, sum) per row.  oacc[d] holds O transposed (the P . V products
+// run as V^T P^T): lane l has row l % 16, dims 16 (4 w + d) + 4 g + [0, 4).
+// Every row is written (rows past R repeat row R - 1).
 __device__ inline void attn_publish(Ctx& c, int chunk, const Use& u, const f32x4 (&oacc)[4], float m_row,
                                     float l_row) {
-  const unsigned ob = xb<X_AO>(c, u.par);
+  const unsigned ob = xb<X_AO>(c, u.par) + (unsigned)(((chunk * RP + c.row) * DH + 4 * c.g) * 4);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const int dim = 16 * (4 * c.wave + d) + c.row;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rw = 4 * c.g + e;
-      if (rw < c.R) st1<LST>(c, ob + (unsigned)(((chunk * RP + rw) * DH + dim) * 4), f32_word(oacc[d][e], u.gen));
-    }
+    const u32x4 w = {f32_word(oacc[d][0], u.gen), f32_word(oacc[d][1], u.gen), f32_word(oacc[d][2], u.gen),
+                     f32_word(oacc[d][3], u.gen)};
+    st4<LST>(c, ob + (unsigned)(16 * (4 * c.wave + d) * 4), w);
   }
-  if (c.wave == 0 && c.g == 0 && c.row < c.R) {
+  if (c.wave == 0 && c.g == 0) {
     const float m = m_row == -INFINITY ? M_EMPTY : m_row;
     const unsigned wm = f32_word(m, u.gen), wl = f32_word(l_row, u.gen);
     st4<LST>(c, xb<X_AML>(c, u.par) + (unsigned)((chunk * RP + c.row) * 16), u32x4{wm, wl, wm, wl});
@@ -846,7 +851,7 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
   c.sh->att_p[c.wave][1][c.lane] = pl;
   cw_barrier(c);
   const float l_row = (c.sh->att_l[0][c.row] + c.sh->att_l[1][c.row]) + (c.sh->att_l[2][c.row] + c.sh->att_l[3][c.row]);
-  // O = P . V for dim tiles [4 w, 4 w + 4), all four key groups
+  // O^T = V^T . P^T for dim tiles [4 w, 4 w + 4), all four key groups
   f32x4 oacc[4], olo[4];  // the lo products of P in accumulators of their own
 #pragma unroll
   for (int d = 0; d < 4; ++d) oacc[d] = olo[d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -869,10 +874,10 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
       const u32x4 vv = vt[kg][dp];
       const s16x4 b0 = __builtin_bit_cast(s16x4, u32x2{vv[0], vv[1]});
       const s16x4 b1 = __builtin_bit_cast(s16x4, u32x2{vv[2], vv[3]});
-      oacc[2 * dp] = mma16(ah, b0, oacc[2 * dp]);
-      oacc[2 * dp + 1] = mma16(ah, b1, oacc[2 * dp + 1]);
-      olo[2 * dp] = mma16(al, b0, olo[2 * dp]);
-      olo[2 * dp + 1] = mma16(al, b1, olo[2 * dp + 1]);
+      oacc[2 * dp] = mma16(b0, ah, oacc[2 * dp]);
+      oacc[2 * dp + 1] = mma16(b1, ah, oacc[2 * dp + 1]);
+      olo[2 * dp] = mma16(b0, al, olo[2 * dp]);
+      olo[2 * dp + 1] = mma16(b1, al, olo[2 * dp + 1]);
     }
   }
 #pragma unroll
@@ -884,35 +889,31 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
 
 // Attention of head xcd over the action rows' own keys and values (chunk
 // nc).  Wave w takes head dims [64 w, 64 w + 64) of q and of the keys for a
-// partial score tile (the four are summed in LDS in wave order) and value
-// rows w, w + 4, w + 8, w + 12, staged in LDS transposed for the P . V
-// fragments.  Products of two low halves (2^-16 of 2^-16) are left out.
+// partial score tile (the four are summed in LDS in wave order), and the
+// value fragments of dim tiles 4 w .. 4 w + 3 straight from the transposed
+// value words (keys 4 g .. 4 g + 3 of one dim per lane).  Products of two
+// low halves (2^-16 of 2^-16) are left out.
+__device__ inline s16x4 pairs_hi(const u32x4& w) {
+  return __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
+                                         __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)});
+}
+__device__ inline s16x4 pairs_lo(const u32x4& w) {
+  return __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x05040100u) & 0xfffefffeu,
+                                         __builtin_amdgcn_perm(w[3], w[2], 0x05040100u) & 0xfffefffeu});
+}
 __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int k, int l) {
   refresh(c);
   const Use u = use_layer(c, k, l);
   const float scale = 0.0625f;
-  unsigned char* red = red_take(c);
-  unsigned short* vh = (unsigned short*)red;             // [DH][RP] hi halves of the values, transposed
-  unsigned short* vl = vh + DH * RP;                     // [DH][RP] lo halves
-  f32x4* sp = (f32x4*)(red + 2 * DH * RP * 2);           // [4 waves][64 lanes] partial score tiles
+  f32x4* sp = (f32x4*)red_take(c);  // [4 waves][64 lanes] partial score tiles
+  u32x4 kv[8];  // 0..3: the lane's key dims; 4..7: value fragments of dim tiles 4 w + (i - 4)
   {
-    const int t = c.wave * 64 + c.lane;  // 256 threads: thread t clears dim t
-#pragma unroll
-    for (int key = 0; key < RP; key += 2) {
-      *(unsigned*)(vh + t * RP + key) = 0u;
-      *(unsigned*)(vl + t * RP + key) = 0u;
-    }
-  }
-  const int kcrow = c.crow;  // key row of the A fragments (clamped like the query rows)
-  u32x4 kv[8];
-  {
-    const unsigned vk = (unsigned)((kcrow * 2 * DH + 64 * c.wave + 8 * c.g) * 4);
     const unsigned bkv = xb<X_KV>(c, u.par);
+    const unsigned vk = (unsigned)((c.crow * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned vv = (unsigned)(RP * DH * 4) + (unsigned)(((64 * c.wave + c.row) * RP + 4 * c.g) * 4);
     poll<SC1>(c, [&](int i) -> LA {
       if (i < 4) return LA{vk + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bkv};
-      const int key = c.wave + 4 * (i - 4);
-      const int ck = key < c.R ? key : c.R - 1;
-      return LA{(unsigned)((ck * 2 * DH + DH + 4 * c.lane) * 4), bkv};
+      return LA{vv + (unsigned)((i - 4) * 16 * RP * 4), bkv};
     }, u.gen, kv);
   }
   u32x4 qv[4];
@@ -930,20 +931,7 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
     st = mma32(kh, qlf, st);
     st = mma32(kl, qhf, st);
   }
-  cw_barrier(c);  // staging area cleared by every wave
   sp[c.wave * 64 + c.lane] = st;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int key = c.wave + 4 * e;
-    if (key < c.R) {
-      const u32x4 w = kv[4 + e];  // dims 4 lane .. 4 lane + 3 of value row `key`
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        vh[(4 * c.lane + q) * RP + key] = (unsigned short)(w[q] >> 16);
-        vl[(4 * c.lane + q) * RP + key] = (unsigned short)(w[q] & 0xfffeu);
-      }
-    }
-  }
   cw_barrier(c);
   st = ((sp[0 * 64 + c.lane] + sp[1 * 64 + c.lane]) + sp[2 * 64 + c.lane]) + sp[3 * 64 + c.lane];
   float sv[4];
@@ -971,12 +959,10 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
   f32x4 oacc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const int dim = 16 * (4 * c.wave + d) + c.row;
-    const s16x4 bh = *(const s16x4*)(vh + dim * RP + 4 * c.g);
-    const s16x4 bl = *(const s16x4*)(vl + dim * RP + 4 * c.g);
-    oacc[d] = mma16(ph, bh, f32x4{0.f, 0.f, 0.f, 0.f});
-    oacc[d] = mma16(ph, bl, oacc[d]);
-    oacc[d] = mma16(pl, bh, oacc[d]);
+    const s16x4 vh = pairs_hi(kv[4 + d]), vl = pairs_lo(kv[4 + d]);
+    oacc[d] = mma16(vh, ph, f32x4{0.f, 0.f, 0.f, 0.f});
+    oacc[d] = mma16(vl, ph, oacc[d]);
+    oacc[d] = mma16(vh, pl, oacc[d]);
   }
   attn_publish(c, c.nc, u, oacc, m_row, lw);
 }
