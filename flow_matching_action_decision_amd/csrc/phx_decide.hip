@@ -271,6 +271,12 @@ __device__ inline bool is_qkv(const Ctx& c) { return c.rk >= R_QKV && c.rk < R_Q
 __device__ inline bool is_att(const Ctx& c) { return c.rk <= c.nc; }
 __device__ inline bool is_merge(const Ctx& c) { return c.rk >= R_MERGE && c.rk < R_MERGE + DH / 32; }
 __device__ inline bool is_vel(const Ctx& c) { return c.rk == R_VEL; }
+// Byte offset of a lane's load from its own action row (row = lane % 16), or
+// past every buffer's range for rows past R: those lanes move nothing, read
+// zeros and are left out of the poll (their live mask is 0).  The padded
+// rows then compute on zeros; no real row ever reads them.
+__device__ inline unsigned row_off(const Ctx& c, unsigned off) { return c.row < c.R ? off : OOB; }
+__device__ inline unsigned row_live(const Ctx& c, unsigned mask) { return c.row < c.R ? mask : 0u; }
 // QKV n-tile of QKV workgroup i on XCD x: query head x's tiles, then this
 // XCD's two tiles of the key head and two of the value head
 __device__ inline int qkv_ntile(int i, int x) {
@@ -515,9 +521,12 @@ struct LA {
 // whose words of load i are already fresh points load i past the buffer's
 // range (no memory access), so a round moves only what is still stale.
 // Every load of a round is in flight before the first is checked, and no
-// branch separates them.
+// branch separates them.  Loads whose bit in the lane's `live` mask is clear
+// never wait: the callers point them past the buffer's range (rows past R),
+// so they move nothing and read zeros.
 template <int POL, int N, typename AF>
-__device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, u32x4 (&v)[N]) {
+__device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, u32x4 (&v)[N],
+                                                           unsigned live = ~0u) {
   const unsigned t0 = now_ticks();
   unsigned spins = 0;
 #pragma unroll
@@ -529,6 +538,7 @@ __device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsi
     unsigned stale = 0;
 #pragma unroll
     for (int i = 0; i < N; ++i) stale |= stale4(v[i], gen) << i;
+    stale &= live;
     if (__ballot(stale != 0u) == 0ull) return;
     keep_waiting(c, t0, spins);
     asm volatile("" ::: "memory");
@@ -543,7 +553,8 @@ __device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsi
   }
 }
 // The same for 8-byte loads; loads whose bit in `live` is clear are never
-// issued and never wait (their values are zero).
+// issued and never wait (their values are zero).  `live` may differ between
+// lanes.
 template <int POL, int N, typename AF>
 __device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, u32x2 (&v)[N],
                                                            unsigned live = ~0u) {
@@ -633,7 +644,7 @@ __device__ inline void owner_publish(Ctx& c, const Own& o, const float (&h)[2], 
 // of squares (loads 16, 17: lane row lane / 4, owners 8 (lane % 4) + [0, 8)).
 template <int T_N, int T_SS>
 __device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const Use& u, u32x4 (&v)[18]) {
-  const unsigned vn = (unsigned)((c.crow * D + 256 * c.wave + 8 * c.g) * 4);
+  const unsigned vn = row_off(c, (unsigned)((c.row * D + 256 * c.wave + 8 * c.g) * 4));
   const int srow = c.lane >> 2;
   const int scrow = srow < c.R ? srow : c.R - 1;
   const unsigned vs = (unsigned)((scrow * WX + 8 * (c.lane & 3)) * 4);
@@ -641,7 +652,7 @@ __device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const 
   poll<NTP>(c, [&](int i) -> LA {
     if (i < 16) return LA{vn + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bn};
     return LA{vs + (unsigned)((i - 16) * 16), bs};
-  }, u.gen, v);
+  }, u.gen, v, row_live(c, 0xffffu) | 0x30000u);
   if (c.wave == 0) {
     float s = 0.f;
 #pragma unroll
@@ -673,7 +684,8 @@ __device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, float
     } else {
       const Use ux = use_state(c, k - 1);
       const unsigned bx = xb<X_X>(c, ux.par);
-      poll<NTP>(c, [&](int i) -> LA { return LA{vo + 16u * (unsigned)i, bx}; }, ux.gen, v);
+      const unsigned vr = row_off(c, vo);
+      poll<NTP>(c, [&](int i) -> LA { return LA{vr + 16u * (unsigned)i, bx}; }, ux.gen, v, row_live(c, ~0u));
     }
     bf16x8 xh, xl;
     frag_split_f32(v[0], v[1], xh, xl);
@@ -789,9 +801,10 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
   bf16x8 qh[8], ql[8];
   {
     u32x4 v[4];
-    const unsigned vo = (unsigned)((c.crow * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned vo = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
     const unsigned bq = xb<X_Q>(c, u.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, v);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, v,
+              row_live(c, ~0u));
     u32x4* qs = (u32x4*)red_take(c);  // [8 slices][hi, lo][64 lanes]
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -909,18 +922,19 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
   u32x4 kv[8];  // 0..3: the lane's key dims; 4..7: value fragments of dim tiles 4 w + (i - 4)
   {
     const unsigned bkv = xb<X_KV>(c, u.par);
-    const unsigned vk = (unsigned)((c.crow * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned vk = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
     const unsigned vv = (unsigned)(RP * DH * 4) + (unsigned)(((64 * c.wave + c.row) * RP + 4 * c.g) * 4);
     poll<SC1>(c, [&](int i) -> LA {
       if (i < 4) return LA{vk + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bkv};
       return LA{vv + (unsigned)((i - 4) * 16 * RP * 4), bkv};
-    }, u.gen, kv);
+    }, u.gen, kv, row_live(c, 0x0fu) | 0xf0u);
   }
   u32x4 qv[4];
   {
-    const unsigned vq = (unsigned)((c.crow * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned vq = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
     const unsigned bq = xb<X_Q>(c, u.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vq + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, qv);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vq + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, qv,
+              row_live(c, ~0u));
   }
   f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -980,13 +994,13 @@ __device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, in
   const int nch = c.nc + 1;
   const Use u = use_layer(c, k, l);
   const int r = 4 * c.wave + (c.lane >> 4);
-  const int rc = r < c.R ? r : c.R - 1;
+  const bool act = r < c.R;
   const int dd = 32 * s + 2 * (c.lane & 15);
   u32x2 v[2 * MAX_CHUNKS];  // chunk cc: (max, sum) at 2 cc, the two partial outputs at 2 cc + 1
   {
     const unsigned bo = xb<X_AO>(c, u.par), bm = xb<X_AML>(c, u.par);
-    const unsigned vo = (unsigned)((rc * DH + dd) * 4), vm = (unsigned)(rc * 16);
-    const unsigned live = nch >= MAX_CHUNKS ? ~0u : (1u << (2 * nch)) - 1u;
+    const unsigned vo = act ? (unsigned)((r * DH + dd) * 4) : OOB, vm = act ? (unsigned)(r * 16) : OOB;
+    const unsigned live = !act ? 0u : nch >= MAX_CHUNKS ? ~0u : (1u << (2 * nch)) - 1u;
     poll<NTP>(c, [&](int i) -> LA {
       const int cc = i >> 1;
       if (i & 1) return LA{vo, bo + (unsigned)(cc * RP * DH * 4)};
@@ -1009,7 +1023,7 @@ __device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, in
   }
   const float inv = frcp(L);
   const u32x2 w = {pair_word(o0 * inv, u.gen), pair_word(o1 * inv, u.gen)};
-  st2<LST>(c, xb<X_O>(c, u.par) + (unsigned)((r * DH + dd) * 4), w);
+  if (act) st2<LST>(c, xb<X_O>(c, u.par) + (unsigned)((r * DH + dd) * 4), w);
 }
 
 // out projection of the head's 256 rows for output columns
@@ -1023,9 +1037,10 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_o;
   u32x4 v[4];
   {
-    const unsigned vo = (unsigned)((c.crow * DH + 64 * c.wave + 8 * c.g) * 4);
+    const unsigned vo = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
     const unsigned bo = xb<X_O>(c, u.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bo}; }, u.gen, v);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bo}; }, u.gen, v,
+              row_live(c, ~0u));
   }
   wait_tiles(c, p0, 8 * O_NT);
   f32x4 acc[O_NT];
@@ -1057,9 +1072,10 @@ __device__ __attribute__((always_inline)) inline void ph_own(Ctx& c, int k, int 
   const u32x2 sv = owner_scale_load(c, o, k, norm);
   u32x2 v[NX];
   {
-    const unsigned vo = (unsigned)(o.crow * D * 4) + o.col * 4u;
+    const bool act = o.row < c.R;
+    const unsigned vo = act ? (unsigned)(o.row * D * 4) + o.col * 4u : OOB;
     const unsigned bp = xb<T_P>(c, u.par);
-    poll<SC1>(c, [&](int i) -> LA { return LA{vo + (unsigned)(i * RP * D * 4), bp}; }, u.gen, v);
+    poll<SC1>(c, [&](int i) -> LA { return LA{vo + (unsigned)(i * RP * D * 4), bp}; }, u.gen, v, act ? ~0u : 0u);
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -1113,9 +1129,10 @@ __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_dn;
   u32x4 v[8];
   {
-    const unsigned vo = (unsigned)((c.crow * FX + 128 * c.wave + 8 * c.g) * 4);
+    const unsigned vo = row_off(c, (unsigned)((c.row * FX + 128 * c.wave + 8 * c.g) * 4));
     const unsigned ba = xb<X_A>(c, u.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), ba}; }, u.gen, v);
+    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), ba}; }, u.gen, v,
+              row_live(c, ~0u));
   }
   wait_tiles(c, p0, 32);
   f32x4 acc[2];
@@ -1317,15 +1334,17 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
   unsigned issued = 0;
   unsigned pos, off;
   int kv;
+  unsigned cons = 0;  // the compute waves' release position, re-read only when the ring looks full
   while (gen_next(c, s, q, pos, off, kv)) {
-    if (pos >= lds_load(&c.sh->consumed) + RING) {
+    if (pos >= cons + RING) cons = lds_load(&c.sh->consumed);
+    if (pos >= cons + RING) {
       // the ring is full: publish every tile in flight before waiting, since
       // the compute waves may be waiting for exactly those
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (c.lane == 0) lds_store(&c.sh->ready[q], issued);
       const unsigned t0 = now_ticks();
       unsigned spins = 0;
-      while (pos >= lds_load(&c.sh->consumed) + RING) {
+      while (pos >= (cons = lds_load(&c.sh->consumed)) + RING) {
         __builtin_amdgcn_s_sleep(2);
         loader_keep_waiting(c, t0, spins);
       }
