@@ -790,14 +790,19 @@ __device__ inline void attn_publish(Ctx& c, int chunk, const Use& u, const f32x4
   }
 }
 
-// attention of head xcd over prefix key chunk [64 ch, 64 ch + 64) from the ring
+// Attention of head xcd over prefix key chunk [64 ch, 64 ch + 64) from the
+// ring.  Wave w reads q dims [64 w, 64 w + 64) and the waves share them
+// through LDS.  Wave w scores keys [16 w, 16 w + 16) and forms their
+// probabilities against its own row maximum; after one more exchange between
+// the waves (maxima, sums and probabilities through LDS) each wave rescales
+// the four key groups' products to the common maximum for its four dim
+// tiles.  The ring is released after the outputs are published.
 __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int k, int l) {
   refresh(c);
   const int ch = c.rk;
   const Use u = use_layer(c, k, l);
   const float scale = 0.0625f;  // 1/sqrt(256)
-  // q fragments (dims 32 s + 8 g + [0, 8), hi and lo): wave w polls slices 2w, 2w + 1
-  // and the four waves share them through LDS
+  // q fragments of dims 32 s + 8 g + [0, 8) (hi and lo), s = 0 .. 7
   bf16x8 qh[8], ql[8];
   {
     u32x4 v[4];
@@ -842,16 +847,12 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
     sv[e] = key < c.L ? st[e] * scale : -INFINITY;
     mw = fmaxf(mw, sv[e]);
   }
-  mw = max_x16_x32(mw);
-  if (c.g == 0) c.sh->att_m[c.wave][c.row] = mw;
-  cw_barrier(c);
-  const float m_row = fmaxf(fmaxf(c.sh->att_m[0][c.row], c.sh->att_m[1][c.row]),
-                            fmaxf(c.sh->att_m[2][c.row], c.sh->att_m[3][c.row]));
+  mw = max_x16_x32(mw);  // this wave's row maximum
   float lw = 0.f;
   s16x4 ph, pl;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float p = sv[e] == -INFINITY ? 0.f : fexp(sv[e] - m_row);
+    const float p = sv[e] == -INFINITY ? 0.f : fexp(sv[e] - mw);
     lw += p;
     short a, b;
     split_bf16(p, a, b);
@@ -859,15 +860,24 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
     pl[e] = b;
   }
   lw = sum_x16_x32(lw);
-  if (c.g == 0) c.sh->att_l[c.wave][c.row] = lw;
+  if (c.g == 0) {
+    c.sh->att_m[c.wave][c.row] = mw;
+    c.sh->att_l[c.wave][c.row] = lw;
+  }
   c.sh->att_p[c.wave][0][c.lane] = ph;
   c.sh->att_p[c.wave][1][c.lane] = pl;
   cw_barrier(c);
-  const float l_row = (c.sh->att_l[0][c.row] + c.sh->att_l[1][c.row]) + (c.sh->att_l[2][c.row] + c.sh->att_l[3][c.row]);
-  // O^T = V^T . P^T for dim tiles [4 w, 4 w + 4), all four key groups
-  f32x4 oacc[4], olo[4];  // the lo products of P in accumulators of their own
+  // the four key groups against the row's maximum
+  float mk[NCOMPUTE], sc[NCOMPUTE];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) oacc[d] = olo[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kg = 0; kg < NCOMPUTE; ++kg) mk[kg] = c.sh->att_m[kg][c.row];
+  const float m_row = fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3]));
+#pragma unroll
+  for (int kg = 0; kg < NCOMPUTE; ++kg) sc[kg] = mk[kg] == -INFINITY ? 0.f : fexp(mk[kg] - m_row);
+  const float l_row = (sc[0] * c.sh->att_l[0][c.row] + sc[1] * c.sh->att_l[1][c.row]) +
+                      (sc[2] * c.sh->att_l[2][c.row] + sc[3] * c.sh->att_l[3][c.row]);
+  // O^T = V^T . P^T for dim tiles [4 w, 4 w + 4): each key group's products
+  // (hi and lo halves of P in chains of their own), scaled to the row maximum
   u32x4 vt[4][2];
   s16x4 pah[4], pal[4];
 #pragma unroll
@@ -878,26 +888,30 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
     for (int dp = 0; dp < 2; ++dp) vt[kg][dp] = ring_read(c, ring_slot(s0, 32u + 8u * kg + 2u * c.wave + dp));
   }
   reads_issued();
+  f32x4 oacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg) {
     const s16x4 ah = pah[kg];
     const s16x4 al = pal[kg];
+    f32x4 th[4], tl[4];
 #pragma unroll
     for (int dp = 0; dp < 2; ++dp) {
       const u32x4 vv = vt[kg][dp];
       const s16x4 b0 = __builtin_bit_cast(s16x4, u32x2{vv[0], vv[1]});
       const s16x4 b1 = __builtin_bit_cast(s16x4, u32x2{vv[2], vv[3]});
-      oacc[2 * dp] = mma16(b0, ah, oacc[2 * dp]);
-      oacc[2 * dp + 1] = mma16(b1, ah, oacc[2 * dp + 1]);
-      olo[2 * dp] = mma16(b0, al, olo[2 * dp]);
-      olo[2 * dp + 1] = mma16(b1, al, olo[2 * dp + 1]);
+      th[2 * dp] = mma16(b0, ah, f32x4{0.f, 0.f, 0.f, 0.f});
+      th[2 * dp + 1] = mma16(b1, ah, f32x4{0.f, 0.f, 0.f, 0.f});
+      tl[2 * dp] = mma16(b0, al, f32x4{0.f, 0.f, 0.f, 0.f});
+      tl[2 * dp + 1] = mma16(b1, al, f32x4{0.f, 0.f, 0.f, 0.f});
     }
-  }
 #pragma unroll
-  for (int d = 0; d < 4; ++d) oacc[d] += olo[d];
+    for (int d = 0; d < 4; ++d) oacc[d] += sc[kg] * (th[d] + tl[d]);
+  }
+  attn_publish(c, ch, u, oacc, m_row, l_row);
   cw_barrier(c);
   release_ring(c, p0 + 64u);
-  attn_publish(c, ch, u, oacc, m_row, l_row);
 }
 
 // Attention of head xcd over the action rows' own keys and values (chunk
