@@ -194,6 +194,22 @@ __device__ inline unsigned pair_word(float a, unsigned gen) {
   return ((unsigned)bits16(h) << 16) | ((unsigned)bits16(l) & 0xfffeu) | gen;
 }
 // float32 word with the generation bit in the last mantissa bit
+// Norm inputs of the QKV projection and the velocity head travel as plain
+// bf16, two columns per word: the odd column rounded to bf16 in the upper
+// half, the even column rounded to 7 fraction bits in the lower half, whose
+// last bit then carries the generation.  (The MLP's norm input keeps pairs.)
+constexpr bool PLAIN_N = true;
+__device__ inline unsigned bf16x2_word(float a0, float a1, unsigned gen) {
+  const unsigned u0 = as_u(a0), u1 = as_u(a1);
+  const unsigned lo = ((u0 + 0xffffu + ((u0 >> 17) & 1u)) >> 16) & 0xfffeu;
+  const unsigned hi = (u1 + 0x7fffu + ((u1 >> 16) & 1u)) >> 16;
+  return (hi << 16) | lo | gen;
+}
+// B fragment (8 consecutive k values) of 4 such words
+__device__ inline bf16x8 frag_plain(const u32x4& v) {
+  const u32x4 r = {v[0] & ~1u, v[1] & ~1u, v[2] & ~1u, v[3] & ~1u};
+  return __builtin_bit_cast(bf16x8, r);
+}
 __device__ inline unsigned f32_word(float a, unsigned gen) { return (as_u(a) & ~1u) | gen; }
 // bf16 probability pair (hi, lo) for the P . V products
 __device__ inline void split_bf16(float a, short& hi, short& lo) {
@@ -506,6 +522,37 @@ __device__ __attribute__((always_inline)) inline void gemm_pairs(const Ctx& c, u
   for (int t = 0; t < NT; ++t) acc[t] = ah[t] + al[t];
 }
 
+// acc[t] = sum over k-tiles kk of W(t, kk) . b(kk) for plain bf16 words (one
+// load v[kk] per k-tile); two chains per n-tile (even and odd k-tiles)
+template <int NT, int KK, typename OF>
+__device__ __attribute__((always_inline)) inline void gemm_plain(const Ctx& c, unsigned p0, OF off, const u32x4* v,
+                                                                 f32x4 (&acc)[NT]) {
+  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
+  u32x4 w[KK][NT];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[kk][t] = ring_read(c, ring_slot(s0, off(t, kk)));
+  reads_issued();
+  f32x4 ae[NT], ao[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ae[t] = ao[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 b = frag_plain(v[kk]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bf16x8 wt = __builtin_bit_cast(bf16x8, w[kk][t]);
+      if (kk & 1)
+        ao[t] = mma32(wt, b, ao[t]);
+      else
+        ae[t] = mma32(wt, b, ae[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = ae[t] + ao[t];
+}
+
 // ------------------------------------------------------------- exchange
 
 // Where load i of a poll reads: per-lane byte offset vo and uniform so in the
@@ -632,8 +679,13 @@ __device__ inline u32x2 owner_scale_load(const Ctx& c, const Own& o, int k, int 
 // the owner's 32 columns (every wave, its four rows)
 template <int T_N, int T_SS>
 __device__ inline void owner_publish(Ctx& c, const Own& o, const float (&h)[2], const u32x2& sv, const Use& u) {
-  const u32x2 w = {pair_word(h[0] * (1.0f + as_f(sv[0])), u.gen), pair_word(h[1] * (1.0f + as_f(sv[1])), u.gen)};
-  st2<LST>(c, xb<T_N>(c, u.par) + (unsigned)(o.row * D * 4) + o.col * 4u, w);
+  const float n0 = h[0] * (1.0f + as_f(sv[0])), n1 = h[1] * (1.0f + as_f(sv[1]));
+  if constexpr (T_N == X_N && PLAIN_N) {
+    st1<LST>(c, xb<T_N>(c, u.par) + (unsigned)(o.row * (D / 2) * 4) + (o.col / 2u) * 4u, bf16x2_word(n0, n1, u.gen));
+  } else {
+    const u32x2 w = {pair_word(n0, u.gen), pair_word(n1, u.gen)};
+    st2<LST>(c, xb<T_N>(c, u.par) + (unsigned)(o.row * D * 4) + o.col * 4u, w);
+  }
   float s = h[0] * h[0] + h[1] * h[1];
   s = sum_row16(s);
   if ((c.lane & 15) == 0) st1<LST>(c, xb<T_SS>(c, u.par) + (unsigned)((o.row * WX + c.rk) * 4), f32_word(s, u.gen));
@@ -642,21 +694,30 @@ __device__ inline void owner_publish(Ctx& c, const Own& o, const float (&h)[2], 
 // Poll of a normalised activation (pairs [RP][D]) for this wave's 8 k-tiles
 // (loads 0..15: k-tile 8 w + j at loads 2 j, 2 j + 1) plus the owners' sums
 // of squares (loads 16, 17: lane row lane / 4, owners 8 (lane % 4) + [0, 8)).
+// loads of a poll_normed: 16 (pairs) or 8 (plain words) for the wave's k-tiles, then 2
+template <int T_N>
+constexpr int normed_loads() {
+  return (T_N == X_N && PLAIN_N ? 8 : 16) + 2;
+}
 template <int T_N, int T_SS>
-__device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const Use& u, u32x4 (&v)[18]) {
-  const unsigned vn = row_off(c, (unsigned)((c.row * D + 256 * c.wave + 8 * c.g) * 4));
+__device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const Use& u,
+                                                                  u32x4 (&v)[normed_loads<T_N>()]) {
+  constexpr int NA = normed_loads<T_N>() - 2;
+  constexpr bool plain = NA == 8;
+  const unsigned vn = plain ? row_off(c, (unsigned)((c.row * (D / 2) + 128 * c.wave + 4 * c.g) * 4))
+                            : row_off(c, (unsigned)((c.row * D + 256 * c.wave + 8 * c.g) * 4));
   const int srow = c.lane >> 2;
   const int scrow = srow < c.R ? srow : c.R - 1;
   const unsigned vs = (unsigned)((scrow * WX + 8 * (c.lane & 3)) * 4);
   const unsigned bn = xb<T_N>(c, u.par), bs = xb<T_SS>(c, u.par);
   poll<NTP>(c, [&](int i) -> LA {
-    if (i < 16) return LA{vn + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bn};
-    return LA{vs + (unsigned)((i - 16) * 16), bs};
-  }, u.gen, v, row_live(c, 0xffffu) | 0x30000u);
+    if (i < NA) return plain ? LA{vn + (unsigned)(i * 16 * 4), bn} : LA{vn + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bn};
+    return LA{vs + (unsigned)((i - NA) * 16), bs};
+  }, u.gen, v, row_live(c, (1u << NA) - 1u) | (3u << NA));
   if (c.wave == 0) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 16; i < 18; ++i) s += (wf(v[i][0]) + wf(v[i][1])) + (wf(v[i][2]) + wf(v[i][3]));
+    for (int i = NA; i < NA + 2; ++i) s += (wf(v[i][0]) + wf(v[i][1])) + (wf(v[i][2]) + wf(v[i][3]));
     s = sum_quad(s);
     if ((c.lane & 3) == 0) c.sh->rrow[srow] = frsq(s / (float)D + c.eps);
   }
@@ -722,11 +783,14 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
       c.Y, step_tab(c, k) + st_swqkv(c.NL) + (unsigned)((l * NQKV + nt * 16 + 4 * c.g) * 4), 0, 0);
   const u32x4 cs = __builtin_amdgcn_raw_buffer_load_b128(
       c.Y, AUX_ROPE + (unsigned)((c.row * (DH / 2) + 8 * tt + 2 * c.g) * 8), 0, 0);
-  u32x4 v[18];
+  u32x4 v[normed_loads<X_N>()];
   poll_normed<X_N, X_SS>(c, u, v);
   wait_tiles(c, p0, 32);
   f32x4 acc[1];
-  gemm_pairs<1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, v, acc);
+  if constexpr (PLAIN_N)
+    gemm_plain<1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, v, acc);
+  else
+    gemm_pairs<1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
   red[c.wave * 64 + c.lane] = acc[0];
   cw_barrier(c);
@@ -1109,7 +1173,7 @@ __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l
   const int nt = 64 * c.xcd + 2 * c.rk + (c.wave & 1);
   const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
       c.Y, step_tab(c, k) + st_swgu(c.NL) + (unsigned)((l * 2 * F + nt * 16 + 4 * c.g) * 4), 0, 0);
-  u32x4 v[18];
+  u32x4 v[normed_loads<X_N2>()];
   poll_normed<X_N2, X_SS2>(c, u, v);
   wait_tiles(c, p0, 64);
   f32x4 acc[2];
@@ -1180,11 +1244,14 @@ __device__ __attribute__((always_inline)) inline void ph_vel(Ctx& c, int k, f32x
   for (int t = 0; t < 2; ++t)
     sw[t] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, step_tab(c, k) + st_swout(NL) + (unsigned)((16 * t + 4 * c.g) * 4),
                                                   0, 0);
-  u32x4 v[18];
+  u32x4 v[normed_loads<X_N>()];
   poll_normed<X_N, X_SS>(c, u, v);
   wait_tiles(c, p0, 64);
   f32x4 acc[2];
-  gemm_pairs<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
+  if constexpr (PLAIN_N)
+    gemm_plain<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
+  else
+    gemm_pairs<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];

@@ -131,3 +131,37 @@ def test_restore_is_bit_exact():
         ex.close()
     assert not np.array_equal(first, other)
     assert np.array_equal(first, again)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(400)
+def test_every_rollout_request_on_the_decision_kernel():
+    """Each request of the 16-request rollout batch (prefix lengths drawn from
+    {512, 640, 768, 800}) decided alone on the persistent kernel, against the
+    oracle's decision of the whole batch (requests are independent)."""
+    import torch
+    from flow_matching_action_decision_amd.expert import Expert
+    rcfg = phx_inputs.workload("rollout_b16_bf16")
+    rin = phx_inputs.make_inputs(rcfg, 0)
+    ref = oracle_decide(rcfg, rin)
+    cfg = pcfg(layers=rcfg["layers"], steps=rcfg["steps"], dt=rcfg["dt"], rows=rcfg["rows"],
+               capacity=rcfg["capacity"], prefix_lens=[int(rin["lens"][0])])
+    ex = Expert(cfg, rin["weights"], rin["weights_bits"])
+    try:
+        assert ex.kernels_per_decision() == 2
+        worst = 0.0
+        for r in range(rcfg["batch"]):
+            L = int(rin["lens"][r])
+            say(f"case rollout request {r} on the decision kernel, L={L}")
+            one = dict(rin, kv_k=rin["kv_k"][r:r + 1], kv_v=rin["kv_v"][r:r + 1], kv_k_bits=rin["kv_k_bits"][r:r + 1],
+                       kv_v_bits=rin["kv_v_bits"][r:r + 1], lens=rin["lens"][r:r + 1], noise=rin["noise"][r:r + 1])
+            keep = ex.load_all(one)
+            out = ex.decide(torch.from_numpy(np.ascontiguousarray(one["noise"])).cuda())
+            torch.cuda.synchronize()
+            assert ex.status() == 0
+            m = assert_close(out.cpu().numpy(), ref[r:r + 1], TOL_BF16, what=f"request {r} (L={L})")
+            worst = max(worst, m["max_abs"])
+            del keep
+        say(f"  worst max_abs over the 16 requests: {worst:.3e}")
+    finally:
+        ex.close()
