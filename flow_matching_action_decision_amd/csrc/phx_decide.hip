@@ -221,11 +221,6 @@ __device__ inline void split_bf16(float a, short& hi, short& lo) {
 // not depend on which use of its buffer it travelled in (replays stay
 // bit-identical)
 __device__ inline float wf(unsigned w) { return as_f(w & ~1u); }
-// nonzero if any of the four words of a 16-byte load is not of generation gen
-__device__ inline unsigned stale4(const u32x4& v, unsigned gen) {
-  return ((v[0] ^ gen) | (v[1] ^ gen) | (v[2] ^ gen) | (v[3] ^ gen)) & 1u;
-}
-__device__ inline unsigned stale4(const u32x2& v, unsigned gen) { return ((v[0] ^ gen) | (v[1] ^ gen)) & 1u; }
 // B fragments (8 consecutive k values) of the hi and lo halves of 8 pair words
 __device__ inline bf16x8 frag_hi(const u32x4& v0, const u32x4& v1) {
   const u32x4 r = {__builtin_amdgcn_perm(v0[1], v0[0], 0x07060302u), __builtin_amdgcn_perm(v0[3], v0[2], 0x07060302u),
@@ -292,7 +287,6 @@ __device__ inline bool is_vel(const Ctx& c) { return c.rk == R_VEL; }
 // zeros and are left out of the poll (their live mask is 0).  The padded
 // rows then compute on zeros; no real row ever reads them.
 __device__ inline unsigned row_off(const Ctx& c, unsigned off) { return c.row < c.R ? off : OOB; }
-__device__ inline unsigned row_live(const Ctx& c, unsigned mask) { return c.row < c.R ? mask : 0u; }
 // QKV n-tile of QKV workgroup i on XCD x: query head x's tiles, then this
 // XCD's two tiles of the key head and two of the value head
 __device__ inline int qkv_ntile(int i, int x) {
@@ -563,73 +557,76 @@ struct LA {
   unsigned vo, so;
 };
 
-// Polls N 16-byte loads until every word carries generation gen.  The first
-// round issues every load; each later round issues them again, but a lane
-// whose words of load i are already fresh points load i past the buffer's
-// range (no memory access), so a round moves only what is still stale.
-// Every load of a round is in flight before the first is checked, and no
-// branch separates them.  Loads whose bit in the lane's `live` mask is clear
-// never wait: the callers point them past the buffer's range (rows past R),
-// so they move nothing and read zeros.
-template <int POL, int N, typename AF>
-__device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, u32x4 (&v)[N],
-                                                           unsigned live = ~0u) {
-  const unsigned t0 = now_ticks();
-  unsigned spins = 0;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const LA la = addr(i);
-    v[i] = __builtin_amdgcn_raw_buffer_load_b128(c.X, la.vo, __builtin_amdgcn_readfirstlane(la.so), POL);
-  }
-  while (true) {
-    unsigned stale = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) stale |= stale4(v[i], gen) << i;
-    stale &= live;
-    if (__ballot(stale != 0u) == 0ull) return;
-    keep_waiting(c, t0, spins);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const LA la = addr(i);
-      const bool st = (stale >> i) & 1u;
-      const u32x4 n =
-          __builtin_amdgcn_raw_buffer_load_b128(c.X, st ? la.vo : OOB, __builtin_amdgcn_readfirstlane(la.so), POL);
-      v[i] = st ? n : v[i];
-    }
-  }
+// Polls N loads (16-byte u32x4 or 8-byte u32x2) until every word carries
+// generation gen.  Every round issues all N loads and then tests all their
+// words at once: with generation 1 a round is done when the AND of every
+// word has its lowest bit set, with generation 0 when their OR has it clear.
+// (A word stays fresh once it is: its next writer waits for this reader.)
+// Loads [0, NR) come from the lane's own row; in lanes whose row is past R
+// (act false) the callers point them past the buffer's range, where they
+// read zeros, and they are left out of the test.  Loads [NR, N) are valid in
+// every lane.  Only the first nl loads (nl the same in every lane) are
+// issued and tested; the rest read zeros.
+template <int POL, typename V>
+__device__ inline V xload(const Ctx& c, unsigned vo, unsigned so) {
+  if constexpr (sizeof(V) == 16)
+    return __builtin_amdgcn_raw_buffer_load_b128(c.X, vo, so, POL);
+  else
+    return __builtin_amdgcn_raw_buffer_load_b64(c.X, vo, so, POL);
 }
-// The same for 8-byte loads; loads whose bit in `live` is clear are never
-// issued and never wait (their values are zero).  `live` may differ between
-// lanes.
-template <int POL, int N, typename AF>
-__device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, u32x2 (&v)[N],
-                                                           unsigned live = ~0u) {
-  static_assert(N <= 32, "a poll tracks at most 32 loads");
+template <typename V>
+__device__ inline unsigned and_words(const V& x) {
+  if constexpr (sizeof(V) == 16)
+    return x[0] & x[1] & x[2] & x[3];
+  else
+    return x[0] & x[1];
+}
+template <typename V>
+__device__ inline unsigned or_words(const V& x) {
+  if constexpr (sizeof(V) == 16)
+    return x[0] | x[1] | x[2] | x[3];
+  else
+    return x[0] | x[1];
+}
+template <int POL, int N, int NR, typename V, typename AF>
+__device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, V (&v)[N], bool act,
+                                                           int nl = N) {
+  static_assert(NR <= N, "row loads come first");
   const unsigned t0 = now_ticks();
   unsigned spins = 0;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const LA la = addr(i);
-    v[i] = __builtin_amdgcn_raw_buffer_load_b64(c.X, ((live >> i) & 1u) ? la.vo : OOB,
-                                                __builtin_amdgcn_readfirstlane(la.so), POL);
-  }
   while (true) {
-    unsigned stale = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) stale |= stale4(v[i], gen) << i;
-    stale &= live;
-    if (__ballot(stale != 0u) == 0ull) return;
-    keep_waiting(c, t0, spins);
-    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const LA la = addr(i);
-      const bool st = (stale >> i) & 1u;
-      const u32x2 n =
-          __builtin_amdgcn_raw_buffer_load_b64(c.X, st ? la.vo : OOB, __builtin_amdgcn_readfirstlane(la.so), POL);
-      v[i] = st ? n : v[i];
+      v[i] = xload<POL, V>(c, i < nl ? la.vo : OOB, __builtin_amdgcn_readfirstlane(la.so));
     }
+    unsigned stale;
+    if (gen) {
+      unsigned ar = ~0u, aa = ~0u;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const unsigned w = i < nl ? and_words(v[i]) : ~0u;
+        if (i < NR)
+          ar &= w;
+        else
+          aa &= w;
+      }
+      stale = ~(aa & (act ? ar : ~0u)) & 1u;
+    } else {
+      unsigned orr = 0u, oa = 0u;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const unsigned w = i < nl ? or_words(v[i]) : 0u;
+        if (i < NR)
+          orr |= w;
+        else
+          oa |= w;
+      }
+      stale = (oa | (act ? orr : 0u)) & 1u;
+    }
+    if (__ballot(stale != 0u) == 0ull) return;
+    keep_waiting(c, t0, spins);
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -710,10 +707,10 @@ __device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const 
   const int scrow = srow < c.R ? srow : c.R - 1;
   const unsigned vs = (unsigned)((scrow * WX + 8 * (c.lane & 3)) * 4);
   const unsigned bn = xb<T_N>(c, u.par), bs = xb<T_SS>(c, u.par);
-  poll<NTP>(c, [&](int i) -> LA {
+  poll<NTP, NA + 2, NA>(c, [&](int i) -> LA {
     if (i < NA) return plain ? LA{vn + (unsigned)(i * 16 * 4), bn} : LA{vn + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bn};
     return LA{vs + (unsigned)((i - NA) * 16), bs};
-  }, u.gen, v, row_live(c, (1u << NA) - 1u) | (3u << NA));
+  }, u.gen, v, c.row < c.R);
   if (c.wave == 0) {
     float s = 0.f;
 #pragma unroll
@@ -746,7 +743,7 @@ __device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, float
       const Use ux = use_state(c, k - 1);
       const unsigned bx = xb<X_X>(c, ux.par);
       const unsigned vr = row_off(c, vo);
-      poll<NTP>(c, [&](int i) -> LA { return LA{vr + 16u * (unsigned)i, bx}; }, ux.gen, v, row_live(c, ~0u));
+      poll<NTP, 2, 2>(c, [&](int i) -> LA { return LA{vr + 16u * (unsigned)i, bx}; }, ux.gen, v, c.row < c.R);
     }
     bf16x8 xh, xl;
     frag_split_f32(v[0], v[1], xh, xl);
@@ -872,8 +869,8 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
     u32x4 v[4];
     const unsigned vo = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
     const unsigned bq = xb<X_Q>(c, u.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, v,
-              row_live(c, ~0u));
+    poll<NTP, 4, 4>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, v,
+              c.row < c.R);
     u32x4* qs = (u32x4*)red_take(c);  // [8 slices][hi, lo][64 lanes]
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -1002,17 +999,17 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
     const unsigned bkv = xb<X_KV>(c, u.par);
     const unsigned vk = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
     const unsigned vv = (unsigned)(RP * DH * 4) + (unsigned)(((64 * c.wave + c.row) * RP + 4 * c.g) * 4);
-    poll<SC1>(c, [&](int i) -> LA {
+    poll<SC1, 8, 4>(c, [&](int i) -> LA {
       if (i < 4) return LA{vk + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bkv};
       return LA{vv + (unsigned)((i - 4) * 16 * RP * 4), bkv};
-    }, u.gen, kv, row_live(c, 0x0fu) | 0xf0u);
+    }, u.gen, kv, c.row < c.R);
   }
   u32x4 qv[4];
   {
     const unsigned vq = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
     const unsigned bq = xb<X_Q>(c, u.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vq + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, qv,
-              row_live(c, ~0u));
+    poll<NTP, 4, 4>(c, [&](int i) -> LA { return LA{vq + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, qv,
+              c.row < c.R);
   }
   f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1078,12 +1075,11 @@ __device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, in
   {
     const unsigned bo = xb<X_AO>(c, u.par), bm = xb<X_AML>(c, u.par);
     const unsigned vo = act ? (unsigned)((r * DH + dd) * 4) : OOB, vm = act ? (unsigned)(r * 16) : OOB;
-    const unsigned live = !act ? 0u : nch >= MAX_CHUNKS ? ~0u : (1u << (2 * nch)) - 1u;
-    poll<NTP>(c, [&](int i) -> LA {
+    poll<NTP, 2 * MAX_CHUNKS, 2 * MAX_CHUNKS>(c, [&](int i) -> LA {
       const int cc = i >> 1;
       if (i & 1) return LA{vo, bo + (unsigned)(cc * RP * DH * 4)};
       return LA{vm, bm + (unsigned)(cc * RP * 16)};
-    }, u.gen, v, live);
+    }, u.gen, v, act, 2 * nch);
   }
   float M = M_EMPTY;
 #pragma unroll
@@ -1117,8 +1113,8 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
   {
     const unsigned vo = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
     const unsigned bo = xb<X_O>(c, u.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bo}; }, u.gen, v,
-              row_live(c, ~0u));
+    poll<NTP, 4, 4>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bo}; }, u.gen, v,
+              c.row < c.R);
   }
   wait_tiles(c, p0, 8 * O_NT);
   f32x4 acc[O_NT];
@@ -1153,7 +1149,7 @@ __device__ __attribute__((always_inline)) inline void ph_own(Ctx& c, int k, int 
     const bool act = o.row < c.R;
     const unsigned vo = act ? (unsigned)(o.row * D * 4) + o.col * 4u : OOB;
     const unsigned bp = xb<T_P>(c, u.par);
-    poll<SC1>(c, [&](int i) -> LA { return LA{vo + (unsigned)(i * RP * D * 4), bp}; }, u.gen, v, act ? ~0u : 0u);
+    poll<SC1, NX, NX>(c, [&](int i) -> LA { return LA{vo + (unsigned)(i * RP * D * 4), bp}; }, u.gen, v, act);
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -1209,8 +1205,8 @@ __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int
   {
     const unsigned vo = row_off(c, (unsigned)((c.row * FX + 128 * c.wave + 8 * c.g) * 4));
     const unsigned ba = xb<X_A>(c, u.par);
-    poll<NTP>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), ba}; }, u.gen, v,
-              row_live(c, ~0u));
+    poll<NTP, 8, 8>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), ba}; }, u.gen, v,
+              c.row < c.R);
   }
   wait_tiles(c, p0, 32);
   f32x4 acc[2];
@@ -1413,6 +1409,7 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
   run_params(c, 0, s.off0, s.cnt, s.kv);
   s.j = q;
   unsigned issued = 0;
+  unsigned pub = 0;  // tiles published as ready; never decreases
   unsigned pos, off;
   int kv;
   unsigned cons = 0;  // the compute waves' release position, re-read only when the ring looks full
@@ -1422,7 +1419,8 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
       // the ring is full: publish every tile in flight before waiting, since
       // the compute waves may be waiting for exactly those
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (c.lane == 0) lds_store(&c.sh->ready[q], issued);
+      pub = issued;
+      if (c.lane == 0) lds_store(&c.sh->ready[q], pub);
       const unsigned t0 = now_ticks();
       unsigned spins = 0;
       while (pos >= (cons = lds_load(&c.sh->consumed)) + RING) {
@@ -1437,9 +1435,12 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
     else
       dma_tile(WR, (unsigned)c.lane * 16u, off, lds, true);
     ++issued;
-    if (issued > LOAD_DEPTH) {
+    // every tile but the last LOAD_DEPTH has landed; after a full publish
+    // (above) the count only moves on once it passes what was published
+    if (issued > LOAD_DEPTH + pub) {
       asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      if (c.lane == 0) lds_store(&c.sh->ready[q], issued - LOAD_DEPTH);
+      pub = issued - LOAD_DEPTH;
+      if (c.lane == 0) lds_store(&c.sh->ready[q], pub);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
