@@ -482,22 +482,29 @@ __device__ inline u32x4 ring_read(const Ctx& c, unsigned slot) {
 // before it.
 __device__ inline void reads_issued() { asm volatile("" ::: "memory"); }
 
-// acc[t] = sum over k-tiles kk of W(t, kk) . (hi + lo)(kk), the activation
-// pairs of k-tile kk in loads v[2 kk], v[2 kk + 1] and the weight tile at
-// stream position p0 + off(t, kk).  Every tile read is issued before the
-// first product; the hi and lo products go to accumulators of their own and
-// the n-tiles are the inner loop, so no MFMA waits for the result of the one
-// before it (2 NT independent chains); the two halves are added at the end.
+// A phase's weight tiles come out of the ring before it polls for its
+// activation: ring_fetch reads the tile at stream position p0 + off(t, kk)
+// into w[kk][t], and those reads (and any wait for the loaders) overlap the
+// poll, so only the products are left once the activation has arrived.
+//
+// gemm_pairs: acc[t] = sum over k-tiles kk of W(t, kk) . (hi + lo)(kk), the
+// activation pairs of k-tile kk in loads v[2 kk], v[2 kk + 1].  The hi and
+// lo products go to accumulators of their own and the n-tiles are the inner
+// loop, so no MFMA waits for the result of the one before it (2 NT
+// independent chains); the two halves are added at the end.
 template <int NT, int KK, typename OF>
-__device__ __attribute__((always_inline)) inline void gemm_pairs(const Ctx& c, unsigned p0, OF off, const u32x4* v,
-                                                                 f32x4 (&acc)[NT]) {
+__device__ __attribute__((always_inline)) inline void ring_fetch(const Ctx& c, unsigned p0, OF off,
+                                                                 u32x4 (&w)[KK][NT]) {
   const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
-  u32x4 w[KK][NT];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
     for (int t = 0; t < NT; ++t) w[kk][t] = ring_read(c, ring_slot(s0, off(t, kk)));
   reads_issued();
+}
+template <int NT, int KK>
+__device__ __attribute__((always_inline)) inline void gemm_pairs(const u32x4 (&w)[KK][NT], const u32x4* v,
+                                                                 f32x4 (&acc)[NT]) {
   f32x4 ah[NT], al[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) ah[t] = al[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -518,16 +525,9 @@ __device__ __attribute__((always_inline)) inline void gemm_pairs(const Ctx& c, u
 
 // acc[t] = sum over k-tiles kk of W(t, kk) . b(kk) for plain bf16 words (one
 // load v[kk] per k-tile); two chains per n-tile (even and odd k-tiles)
-template <int NT, int KK, typename OF>
-__device__ __attribute__((always_inline)) inline void gemm_plain(const Ctx& c, unsigned p0, OF off, const u32x4* v,
+template <int NT, int KK>
+__device__ __attribute__((always_inline)) inline void gemm_plain(const u32x4 (&w)[KK][NT], const u32x4* v,
                                                                  f32x4 (&acc)[NT]) {
-  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
-  u32x4 w[KK][NT];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) w[kk][t] = ring_read(c, ring_slot(s0, off(t, kk)));
-  reads_issued();
   f32x4 ae[NT], ao[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) ae[t] = ao[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -780,14 +780,16 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
       c.Y, step_tab(c, k) + st_swqkv(c.NL) + (unsigned)((l * NQKV + nt * 16 + 4 * c.g) * 4), 0, 0);
   const u32x4 cs = __builtin_amdgcn_raw_buffer_load_b128(
       c.Y, AUX_ROPE + (unsigned)((c.row * (DH / 2) + 8 * tt + 2 * c.g) * 8), 0, 0);
+  wait_tiles(c, p0, 32);
+  u32x4 w[8][1];
+  ring_fetch<1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, w);
   u32x4 v[normed_loads<X_N>()];
   poll_normed<X_N, X_SS>(c, u, v);
-  wait_tiles(c, p0, 32);
   f32x4 acc[1];
   if constexpr (PLAIN_N)
-    gemm_plain<1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, v, acc);
+    gemm_plain<1, 8>(w, v, acc);
   else
-    gemm_pairs<1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, v, acc);
+    gemm_pairs<1, 8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
   red[c.wave * 64 + c.lane] = acc[0];
   cw_barrier(c);
@@ -863,6 +865,19 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
   const int ch = c.rk;
   const Use u = use_layer(c, k, l);
   const float scale = 0.0625f;  // 1/sqrt(256)
+  // the chunk's key and value tiles out of the ring first (they overlap the
+  // wait for q)
+  const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_att;
+  wait_tiles(c, p0, 64);
+  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
+  u32x4 kt[8], vt[4][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kt[s] = ring_read(c, ring_slot(s0, 8u * c.wave + s));
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+    for (int dp = 0; dp < 2; ++dp) vt[kg][dp] = ring_read(c, ring_slot(s0, 32u + 8u * kg + 2u * c.wave + dp));
+  reads_issued();
   // q fragments of dims 32 s + 8 g + [0, 8) (hi and lo), s = 0 .. 7
   bf16x8 qh[8], ql[8];
   {
@@ -885,14 +900,7 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
       ql[s] = __builtin_bit_cast(bf16x8, qs[(2 * s + 1) * 64 + c.lane]);
     }
   }
-  const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_att;
-  wait_tiles(c, p0, 64);
   // S^T for keys [16 w, 16 w + 16) of the chunk: lane holds keys 4 g + e of row `row`
-  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
-  u32x4 kt[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) kt[s] = ring_read(c, ring_slot(s0, 8u * c.wave + s));
-  reads_issued();
   f32x4 sth = f32x4{0.f, 0.f, 0.f, 0.f}, stl = sth;  // hi and lo products in chains of their own
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -939,16 +947,12 @@ __device__ __attribute__((always_inline)) inline void ph_attn_prefix(Ctx& c, int
                       (sc[2] * c.sh->att_l[2][c.row] + sc[3] * c.sh->att_l[3][c.row]);
   // O^T = V^T . P^T for dim tiles [4 w, 4 w + 4): each key group's products
   // (hi and lo halves of P in chains of their own), scaled to the row maximum
-  u32x4 vt[4][2];
   s16x4 pah[4], pal[4];
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg) {
     pah[kg] = c.sh->att_p[kg][0][c.lane];
     pal[kg] = c.sh->att_p[kg][1][c.lane];
-#pragma unroll
-    for (int dp = 0; dp < 2; ++dp) vt[kg][dp] = ring_read(c, ring_slot(s0, 32u + 8u * kg + 2u * c.wave + dp));
   }
-  reads_issued();
   f32x4 oacc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1109,6 +1113,9 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
   const int o = c.rk;
   const Use u = use_layer(c, k, l);
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_o;
+  wait_tiles(c, p0, 8 * O_NT);
+  u32x4 w[2][O_NT];
+  ring_fetch<O_NT, 2>(c, p0, [&](int t, int j) { return 8u * t + 2u * c.wave + j; }, w);
   u32x4 v[4];
   {
     const unsigned vo = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
@@ -1116,9 +1123,8 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
     poll<NTP, 4, 4>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bo}; }, u.gen, v,
               c.row < c.R);
   }
-  wait_tiles(c, p0, 8 * O_NT);
   f32x4 acc[O_NT];
-  gemm_pairs<O_NT, 2>(c, p0, [&](int t, int j) { return 8u * t + 2u * c.wave + j; }, v, acc);
+  gemm_pairs<O_NT, 2>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < O_NT; ++t) red[(c.wave * O_NT + t) * 64 + c.lane] = acc[t];
@@ -1169,11 +1175,13 @@ __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l
   const int nt = 64 * c.xcd + 2 * c.rk + (c.wave & 1);
   const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
       c.Y, step_tab(c, k) + st_swgu(c.NL) + (unsigned)((l * 2 * F + nt * 16 + 4 * c.g) * 4), 0, 0);
+  wait_tiles(c, p0, 64);
+  u32x4 w[8][2];
+  ring_fetch<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, w);
   u32x4 v[normed_loads<X_N2>()];
   poll_normed<X_N2, X_SS2>(c, u, v);
-  wait_tiles(c, p0, 64);
   f32x4 acc[2];
-  gemm_pairs<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
+  gemm_pairs<2, 8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
@@ -1201,6 +1209,9 @@ __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int
   refresh(c);
   const Use u = use_layer(c, k, l);
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_dn;
+  wait_tiles(c, p0, 32);
+  u32x4 w[4][2];
+  ring_fetch<2, 4>(c, p0, [&](int t, int j) { return 16u * t + 4u * c.wave + j; }, w);
   u32x4 v[8];
   {
     const unsigned vo = row_off(c, (unsigned)((c.row * FX + 128 * c.wave + 8 * c.g) * 4));
@@ -1208,9 +1219,8 @@ __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int
     poll<NTP, 8, 8>(c, [&](int i) -> LA { return LA{vo + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), ba}; }, u.gen, v,
               c.row < c.R);
   }
-  wait_tiles(c, p0, 32);
   f32x4 acc[2];
-  gemm_pairs<2, 4>(c, p0, [&](int t, int j) { return 16u * t + 4u * c.wave + j; }, v, acc);
+  gemm_pairs<2, 4>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
@@ -1240,14 +1250,16 @@ __device__ __attribute__((always_inline)) inline void ph_vel(Ctx& c, int k, f32x
   for (int t = 0; t < 2; ++t)
     sw[t] = __builtin_amdgcn_raw_buffer_load_b128(c.Y, step_tab(c, k) + st_swout(NL) + (unsigned)((16 * t + 4 * c.g) * 4),
                                                   0, 0);
+  wait_tiles(c, p0, 64);
+  u32x4 w[8][2];
+  ring_fetch<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, w);
   u32x4 v[normed_loads<X_N>()];
   poll_normed<X_N, X_SS>(c, u, v);
-  wait_tiles(c, p0, 64);
   f32x4 acc[2];
   if constexpr (PLAIN_N)
-    gemm_plain<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
+    gemm_plain<2, 8>(w, v, acc);
   else
-    gemm_pairs<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, v, acc);
+    gemm_pairs<2, 8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
