@@ -131,6 +131,7 @@ constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1, 0, 3, 2]
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2, 3, 0, 1]
 constexpr int DPP_HALF_MIRROR = 0x141;
 constexpr int DPP_MIRROR = 0x140;
+constexpr int DPP_ROW_SHARE0 = 0x150;  // row_share:n = 0x150 + n: lane n of each row to the row's 16 lanes
 // sum over the 4 lanes of a quad
 __device__ inline float sum_quad(float v) {
   v += dppf<DPP_XOR1>(v);
@@ -141,6 +142,13 @@ __device__ inline float sum_row16(float v) {
   v = sum_quad(v);
   v += dppf<DPP_HALF_MIRROR>(v);
   return v + dppf<DPP_MIRROR>(v);
+}
+// maximum over the 16 lanes of a row
+__device__ inline float max_row16(float v) {
+  v = fmaxf(v, dppf<DPP_XOR1>(v));
+  v = fmaxf(v, dppf<DPP_XOR2>(v));
+  v = fmaxf(v, dppf<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dppf<DPP_MIRROR>(v));
 }
 // sum and maximum over lanes l, l ^ 16, l ^ 32, l ^ 48
 // (the value of lane l, that of lane l ^ 16) in the order (lower lane, upper
@@ -707,10 +715,11 @@ __device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const 
   const int scrow = srow < c.R ? srow : c.R - 1;
   const unsigned vs = (unsigned)((scrow * WX + 8 * (c.lane & 3)) * 4);
   const unsigned bn = xb<T_N>(c, u.par), bs = xb<T_SS>(c, u.par);
+  // only wave 0 forms the row scales, so only wave 0 polls the sums
   poll<NTP, NA + 2, NA>(c, [&](int i) -> LA {
     if (i < NA) return plain ? LA{vn + (unsigned)(i * 16 * 4), bn} : LA{vn + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bn};
     return LA{vs + (unsigned)((i - NA) * 16), bs};
-  }, u.gen, v, c.row < c.R);
+  }, u.gen, v, c.row < c.R, c.wave == 0 ? NA + 2 : NA);
   if (c.wave == 0) {
     float s = 0.f;
 #pragma unroll
@@ -1063,9 +1072,30 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
 // Merges the head's key chunks for dims [32 s, 32 s + 32) and writes the
 // normalised attention output as pairs.  Wave w finishes rows 4 w .. 4 w + 3
 // on its own, with no exchange between the waves: lane l takes row
-// 4 w + l / 16 and dims 32 s + 2 (l % 16) + [0, 2), reads that row's
-// (max, sum) and its two partial outputs of every chunk, and merges the
-// chunks in chunk order.  Rows past R repeat row R - 1 (nobody reads them).
+// 4 w + l / 16 and dims 32 s + 2 (l % 16) + [0, 2) and reads that row's two
+// partial outputs of every chunk; the 16 lanes of the row share out the
+// chunks' (max, sum) pairs, lane j reading chunk j's.  The row maximum and
+// the weighted sum come from reductions over the 16 lanes, and each chunk's
+// weight reaches the row's lanes by a DPP row broadcast, so the chunks are
+// added in chunk order.  Rows past R repeat row R - 1 (nobody reads them).
+static_assert(MAX_CHUNKS <= 16, "one (max, sum) pair per lane of a row");
+template <int CC>
+__device__ inline float row_share(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), DPP_ROW_SHARE0 + CC, 0xf, 0xf,
+                                                            false));
+}
+template <int CC>
+__device__ __attribute__((always_inline)) inline void merge_add(float e, const u32x2 (&v)[MAX_CHUNKS + 1], int nch,
+                                                                float& o0, float& o1) {
+  if constexpr (CC < MAX_CHUNKS) {
+    if (CC < nch) {
+      const float ec = row_share<CC>(e);
+      o0 += ec * wf(v[1 + CC][0]);
+      o1 += ec * wf(v[1 + CC][1]);
+      merge_add<CC + 1>(e, v, nch, o0, o1);
+    }
+  }
+}
 __device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, int l) {
   refresh(c);
   if (!is_merge(c)) return;
@@ -1074,31 +1104,24 @@ __device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, in
   const Use u = use_layer(c, k, l);
   const int r = 4 * c.wave + (c.lane >> 4);
   const bool act = r < c.R;
-  const int dd = 32 * s + 2 * (c.lane & 15);
-  u32x2 v[2 * MAX_CHUNKS];  // chunk cc: (max, sum) at 2 cc, the two partial outputs at 2 cc + 1
+  const int j = c.lane & 15;
+  const int dd = 32 * s + 2 * j;
+  u32x2 v[1 + MAX_CHUNKS];  // 0: (max, sum) of chunk min(j, nch - 1); 1 + cc: the two partial outputs of chunk cc
   {
     const unsigned bo = xb<X_AO>(c, u.par), bm = xb<X_AML>(c, u.par);
-    const unsigned vo = act ? (unsigned)((r * DH + dd) * 4) : OOB, vm = act ? (unsigned)(r * 16) : OOB;
-    poll<NTP, 2 * MAX_CHUNKS, 2 * MAX_CHUNKS>(c, [&](int i) -> LA {
-      const int cc = i >> 1;
-      if (i & 1) return LA{vo, bo + (unsigned)(cc * RP * DH * 4)};
-      return LA{vm, bm + (unsigned)(cc * RP * 16)};
-    }, u.gen, v, act, 2 * nch);
+    const unsigned vo = act ? (unsigned)((r * DH + dd) * 4) : OOB;
+    const unsigned vm = act ? (unsigned)(((j < nch ? j : nch - 1) * RP + r) * 16) : OOB;
+    poll<NTP, 1 + MAX_CHUNKS, 1 + MAX_CHUNKS>(c, [&](int i) -> LA {
+      if (i == 0) return LA{vm, bm};
+      return LA{vo, bo + (unsigned)((i - 1) * RP * DH * 4)};
+    }, u.gen, v, act, 1 + nch);
   }
-  float M = M_EMPTY;
-#pragma unroll
-  for (int cc = 0; cc < MAX_CHUNKS; ++cc)
-    if (cc < nch) M = fmaxf(M, wf(v[2 * cc][0]));
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll
-  for (int cc = 0; cc < MAX_CHUNKS; ++cc) {
-    if (cc < nch) {
-      const float e = fexp(wf(v[2 * cc][0]) - M);
-      L += e * wf(v[2 * cc][1]);
-      o0 += e * wf(v[2 * cc + 1][0]);
-      o1 += e * wf(v[2 * cc + 1][1]);
-    }
-  }
+  const float mj = j < nch ? wf(v[0][0]) : M_EMPTY;
+  const float M = max_row16(mj);
+  const float e = j < nch ? fexp(mj - M) : 0.f;
+  const float L = sum_row16(e * wf(v[0][1]));
+  float o0 = 0.f, o1 = 0.f;
+  merge_add<0>(e, v, nch, o0, o1);
   const float inv = frcp(L);
   const u32x2 w = {pair_word(o0 * inv, u.gen), pair_word(o1 * inv, u.gen)};
   if (act) st2<LST>(c, xb<X_O>(c, u.par) + (unsigned)((r * DH + dd) * 4), w);
