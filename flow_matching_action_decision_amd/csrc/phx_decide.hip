@@ -574,7 +574,8 @@ struct LA {
 // (act false) the callers point them past the buffer's range, where they
 // read zeros, and they are left out of the test.  Loads [NR, N) are valid in
 // every lane.  Only the first nl loads (nl the same in every lane) are
-// issued and tested; the rest read zeros.
+// issued and tested; the rest read zeros.  Loads [A2, B2) take cache policy
+// POL2, the others POL.
 template <int POL, typename V>
 __device__ inline V xload(const Ctx& c, unsigned vo, unsigned so) {
   if constexpr (sizeof(V) == 16)
@@ -596,7 +597,7 @@ __device__ inline unsigned or_words(const V& x) {
   else
     return x[0] | x[1];
 }
-template <int POL, int N, int NR, typename V, typename AF>
+template <int POL, int N, int NR, int POL2 = POL, int A2 = 0, int B2 = 0, typename V, typename AF>
 __device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsigned gen, V (&v)[N], bool act,
                                                            int nl = N) {
   static_assert(NR <= N, "row loads come first");
@@ -606,7 +607,11 @@ __device__ __attribute__((always_inline)) inline void poll(Ctx& c, AF addr, unsi
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const LA la = addr(i);
-      v[i] = xload<POL, V>(c, i < nl ? la.vo : OOB, __builtin_amdgcn_readfirstlane(la.so));
+      const unsigned vo = i < nl ? la.vo : OOB, so = __builtin_amdgcn_readfirstlane(la.so);
+      if (i >= A2 && i < B2)
+        v[i] = xload<POL2, V>(c, vo, so);
+      else
+        v[i] = xload<POL, V>(c, vo, so);
     }
     unsigned stale;
     if (gen) {
@@ -1007,22 +1012,26 @@ __device__ __attribute__((always_inline)) inline void ph_attn_action(Ctx& c, int
   const Use u = use_layer(c, k, l);
   const float scale = 0.0625f;
   f32x4* sp = (f32x4*)red_take(c);  // [4 waves][64 lanes] partial score tiles
+  // one poll for the keys (device scope, loads 0..3), q (XCD-local, 4..7)
+  // and the value fragments of dim tiles 4 w + (i - 8) (device scope, 8..11)
   u32x4 kv[8];  // 0..3: the lane's key dims; 4..7: value fragments of dim tiles 4 w + (i - 4)
-  {
-    const unsigned bkv = xb<X_KV>(c, u.par);
-    const unsigned vk = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
-    const unsigned vv = (unsigned)(RP * DH * 4) + (unsigned)(((64 * c.wave + c.row) * RP + 4 * c.g) * 4);
-    poll<SC1, 8, 4>(c, [&](int i) -> LA {
-      if (i < 4) return LA{vk + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bkv};
-      return LA{vv + (unsigned)((i - 4) * 16 * RP * 4), bkv};
-    }, u.gen, kv, c.row < c.R);
-  }
   u32x4 qv[4];
   {
-    const unsigned vq = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
-    const unsigned bq = xb<X_Q>(c, u.par);
-    poll<NTP, 4, 4>(c, [&](int i) -> LA { return LA{vq + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bq}; }, u.gen, qv,
-              c.row < c.R);
+    const unsigned bkv = xb<X_KV>(c, u.par), bq = xb<X_Q>(c, u.par);
+    const unsigned vk = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
+    const unsigned vv = (unsigned)(RP * DH * 4) + (unsigned)(((64 * c.wave + c.row) * RP + 4 * c.g) * 4);
+    u32x4 a[12];
+    poll<SC1, 12, 8, NTP, 4, 8>(c, [&](int i) -> LA {
+      if (i < 4) return LA{vk + (unsigned)((i >> 1) * 32 * 4 + (i & 1) * 16), bkv};
+      if (i < 8) return LA{vk + (unsigned)(((i - 4) >> 1) * 32 * 4 + ((i - 4) & 1) * 16), bq};
+      return LA{vv + (unsigned)((i - 8) * 16 * RP * 4), bkv};
+    }, u.gen, a, c.row < c.R);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kv[i] = a[i];
+      qv[i] = a[4 + i];
+      kv[4 + i] = a[8 + i];
+    }
   }
   f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
