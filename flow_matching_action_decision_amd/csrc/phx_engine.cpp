@@ -619,7 +619,13 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
   const int NL = c.layers, Dh = c.head_dim;
   const int HD = H * Dh, NQKV = (H + 2 * KVH) * Dh, kvd = KVH * Dh;
   const int Mp = h->Mp;
-  const int pm = h->pair_act ? 1 : 0;  // QKV, gate/up and down take paired activation rows
+  // paired activation rows (hi + lo bf16) for the MLP's two GEMMs, gate/up and down, and for the prefill's
+  // QKV (its keys and values are the prefill's output).  Elsewhere the QKV input stays plain bf16, whose
+  // rounding measured well inside the bar: one DiT-style block 9.7e-3 with only the MLP paired against
+  // 7.8e-3 with QKV paired too, at 7.83 against 8.60 ms per step; the prefill's 18-layer cache reached
+  // 2.2e-2 with a plain QKV input
+  const int pm = h->pair_act ? 1 : 0;
+  const int pq = prefill ? pm : 0;
   h->tnodes.clear();
   auto name_of = [](TokNode& nd, const char* name) { std::snprintf(nd.name, sizeof(nd.name), "%s", name); };
   // pair: bit 0 = the activation rows are paired (hi + lo), bit 1 = the GELU/GeGLU output is written paired
@@ -672,7 +678,7 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
   auto layer_v = [&](int l) { return (char*)h->tv + (dit ? 0 : (size_t)l * R * kvd * 2); };
   auto qkv = [&](int k, int l, const char* name) {
     gemm(PHX_NODE_QKV, k, l, h->batched ? tok::EP_QKV_CACHE : tok::EP_QKV, h->nb, h->off_qkv[l], D, NQKV, h->qkv,
-         HD, nullptr, name, pm);
+         HD, nullptr, name, pq);
     tok::GemmT& g = h->tnodes.back().g;
     g.kj = layer_k(l); g.vt = layer_v(l); g.lens = dit ? nullptr : h->lens; g.H = H; g.KVH = KVH; g.nj = R / 32;
     g.hd = Dh;
@@ -731,7 +737,7 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
   if (dit) {
     for (int l = 0; l < NL; ++l) {
       const float* mod = h->modtab + (size_t)l * 6 * D;  // shift, scale, gate (attention), then (MLP)
-      norm(0, l, 1, mod + D, mod, "layernorm_attn", pm);
+      norm(0, l, 1, mod + D, mod, "layernorm_attn", pq);
       qkv(0, l, "qkv");
       attention(0, l);
       gemm(PHX_NODE_OUT_PROJ_RESID, 0, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, mod + 2 * D,
@@ -751,7 +757,7 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     for (int l = 0; l < NL; ++l) {
       const float* m1 = h->modtab + (size_t)(2 * l) * 2 * D;
       const float* m2 = h->modtab + (size_t)(2 * l + 1) * 2 * D;
-      norm(0, l, 0, m1, m1 + D, "rmsnorm_attn", pm);
+      norm(0, l, 0, m1, m1 + D, "rmsnorm_attn", pq);
       qkv(0, l, "qkv_rope");
       if (l + 1 == NL) break;
       attention(0, l);
@@ -781,7 +787,7 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     for (int l = 0; l < NL; ++l) {
       const float* m1 = mod_k + (size_t)(2 * l) * 2 * D;
       const float* m2 = mod_k + (size_t)(2 * l + 1) * 2 * D;
-      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn", pm);
+      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn", pq);
       qkv(k, l, "qkv_rope");
       if (l + 1 == NL) break;
       attention(k, l);
@@ -826,7 +832,7 @@ int build_tok_nodes(phx_expert* h, bool commit = false) {
     for (int l = 0; l < NL; ++l) {
       const float* m1 = mod_k + (size_t)(2 * l) * 2 * D;
       const float* m2 = mod_k + (size_t)(2 * l + 1) * 2 * D;
-      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn", pm);
+      norm(k, l, 0, m1, m1 + D, "rmsnorm_attn", pq);
       qkv(k, l, "qkv_rope");
       attention(k, l);
       gemm(PHX_NODE_OUT_PROJ_RESID, k, l, tok::EP_RESID, h->o, h->off_o[l], HD, D, h->h, D, nullptr,

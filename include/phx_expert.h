@@ -77,11 +77,13 @@ extern "C" {
 #define PHX_FLAG_TIMELINE 4u   /* persistent kernel: record a per-workgroup phase timeline (see
                                   phx_expert_timeline) */
 #define PHX_FLAG_PAIRED_ACT 16u  /* large-token plans (more than 160 rows, the DiT-style block, the prefill):
-                                    the inputs of the QKV, gate/up and down GEMMs (both norms' rows and the
-                                    MLP activation) are carried as pairs of bf16 values, hi = bf16(a) and
-                                    lo = bf16(a - hi), and each GEMM sums hi * w + lo * w against the bf16
-                                    weights, so it sees its activation to ~2^-16 instead of 2^-8 at twice
-                                    the matrix-core work (the attention output stays bf16).  The default of
+                                    the inputs of the MLP's two GEMMs, gate/up and down (the MLP norm's rows
+                                    and the MLP activation), are carried as pairs of bf16 values,
+                                    hi = bf16(a) and lo = bf16(a - hi), and each GEMM sums hi * w + lo * w
+                                    against the bf16 weights, so it sees its activation to ~2^-16 instead
+                                    of 2^-8 at twice the matrix-core work; the prefill pairs its QKV
+                                    input too (its keys and values are its output), the other plans keep
+                                    it, like the attention output, bf16.  The default of
                                     PHX_BLOCK_DIT, of PHX_BLOCK_PREFILL and of the batched plan (bf16, 65-160
                                     rows: the rollout batch): their results accumulate the most bf16
                                     rounding; opt-in for the large-token decoder plan (the video-action
