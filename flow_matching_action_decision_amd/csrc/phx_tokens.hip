@@ -370,7 +370,9 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   }
 }
 
-template <int WN, int WM, int EPI>
+// PAIR: paired activation rows (wsh = 1): k-steps 2 i (hi) and 2 i + 1 (lo)
+// meet the same weight fragment, which is loaded once and kept for both.
+template <int WN, int WM, int EPI, bool PAIR>
 __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
   using T = Tile<WN, WM>;
   __shared__ u32x4 as[2][WM * 64];
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.a), (short)0, (int)((size_t)g.Mp * g.K * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(g.w), (short)0, (int)(((size_t)g.K >> g.wsh) * g.N * 2), 0x00020000);
-  const int wsh = __builtin_amdgcn_readfirstlane(g.wsh);
+  const int wsh = PAIR ? 1 : __builtin_amdgcn_readfirstlane(g.wsh);
   // activation pieces of this thread: rows p*64 + tid/4, k chunk tid%4
   int avo[T::AP], aslot[T::AP];
 #pragma unroll
@@ -417,7 +419,10 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
   for (int n = 0; n < WN; ++n)
 #pragma unroll
     for (int m = 0; m < WM; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 wr[UNR][WN];    // weight fragments, k-step s in slot s % UNR
+  constexpr int WS = PAIR ? UNR / 2 : UNR;
+  // weight fragments: k-step s in slot s % UNR, or (PAIR) k-step pair s / 2 in slot (s / 2) % (UNR / 2)
+  u32x4 wr[WS][WN];
+  auto wslot = [](int j) { return PAIR ? (j / 2) % (UNR / 2) : j % UNR; };
   u32x4 ar[2][T::AP];   // activation pieces, k-step s in slot s % 2
   // prologue: activations of k-steps 0 and 1, weights of k-steps 0 .. WPD-1
 #pragma unroll
@@ -428,9 +433,9 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
   }
 #pragma unroll
   for (int j = 0; j < WPD; ++j)
-    if (j < per) {
+    if (j < per && (!PAIR || (j & 1) == 0)) {
 #pragma unroll
-      for (int n = 0; n < WN; ++n) wr[j][n] = ld_w(n, j);
+      for (int n = 0; n < WN; ++n) wr[wslot(j)][n] = ld_w(n, j);
     }
 #pragma unroll
   for (int p = 0; p < T::AP; ++p) as[0][aslot[p]] = ar[0][p];
@@ -441,8 +446,10 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
       // activations of s + 2 (into the slot k-step s has left), weights of s + WPD
 #pragma unroll
       for (int p = 0; p < T::AP; ++p) ar[j & 1][p] = ld_a(p, s + 2);
+      if (!PAIR || ((j + WPD) & 1) == 0) {
 #pragma unroll
-      for (int n = 0; n < WN; ++n) wr[(j + WPD) % UNR][n] = ld_w(n, s + WPD);
+        for (int n = 0; n < WN; ++n) wr[wslot(j + WPD)][n] = ld_w(n, s + WPD);
+      }
     }
     if (stage) {
 #pragma unroll
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
     for (int m = 0; m < WM; ++m) {
       const bf16x8 af = __builtin_bit_cast(bf16x8, st[m * 64 + lane]);
 #pragma unroll
-      for (int n = 0; n < WN; ++n) acc[n][m] = mma32(__builtin_bit_cast(bf16x8, wr[j][n]), af, acc[n][m]);
+      for (int n = 0; n < WN; ++n) acc[n][m] = mma32(__builtin_bit_cast(bf16x8, wr[wslot(j)][n]), af, acc[n][m]);
     }
     __syncthreads();
   };
@@ -673,8 +680,10 @@ hipError_t launch_tile(const GemmT& g, hipStream_t s) {
   const dim3 grid((g.N / T::BN) * (g.Mp / T::BM) * g.splits);
   if (g.kern == 0)
     hipLaunchKernelGGL((k_tgemm_ring<WN, WM, EPI>), grid, dim3(256), T::LDS, s, g);
+  else if (g.wsh)
+    hipLaunchKernelGGL((k_tgemm_reg<WN, WM, EPI, true>), grid, dim3(256), 0, s, g);
   else
-    hipLaunchKernelGGL((k_tgemm_reg<WN, WM, EPI>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_tgemm_reg<WN, WM, EPI, false>), grid, dim3(256), 0, s, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.splits == 1) return e;
   if (g.nrm_on) {
