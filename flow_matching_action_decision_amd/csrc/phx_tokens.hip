@@ -283,9 +283,22 @@ __device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const 
   }
 }
 
-template <int WN, int WM, int EPI>
+// PAIR: paired activation rows (wsh = 1).  A stage then holds only its
+// k-step's activation fragments; the weight fragments of k-step pair p (hi
+// 2 p, lo 2 p + 1) arrive once, with stage 2 p, in weight buffer p mod 3 (the
+// pair read two stages before p's issue is done by then), and both stages
+// multiply them.
+template <int WN, int WM>
+struct PairRing {
+  static constexpr int WB = 3;                          // weight buffers
+  static constexpr int ACT = Tile<WN, WM>::NS * WM;     // activation fragments of the NS stages
+  static constexpr int LDS = (ACT + WB * 4 * WN) * 1024;
+  static_assert(LDS <= Tile<WN, WM>::LDS, "no more LDS than the plain ring");
+};
+template <int WN, int WM, int EPI, bool PAIR>
 __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   using T = Tile<WN, WM>;
+  using P = PairRing<WN, WM>;
   constexpr int KS = 1;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
@@ -311,7 +324,24 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
     voa[i] = (unsigned)(((size_t)(m0 + 16 * m + (lane & 15)) * g.K + 8 * (lane >> 4)) * 2);
   }
   const unsigned vow = (unsigned)lane * 16u;
+  auto issue_pair = [&](int s) {
+    const int kt = kb + s;
+    const unsigned st = lds0 + (unsigned)((s % NS) * WM * 1024);
+#pragma unroll
+    for (int i = 0; i < WM / 4; ++i)
+      dma_frag(st + (unsigned)((wave * (WM / 4) + i) * 1024), voa[i], ra, (unsigned)(kt * 64));
+    if ((s & 1) == 0) {
+      const unsigned sw = lds0 + (unsigned)((P::ACT + ((s >> 1) % P::WB) * 4 * WN) * 1024);
+#pragma unroll
+      for (int n = 0; n < WN; ++n)
+        dma_frag(sw + (unsigned)((wave * WN + n) * 1024), vow, rw, (unsigned)(((size_t)(nt0 + n) * KTW + (kt >> 1)) * 1024));
+    }
+  };
   auto issue = [&](int s) {
+    if constexpr (PAIR) {
+      issue_pair(s);
+      return;
+    }
     const unsigned st = lds0 + (unsigned)((s % NS) * T::STAGE);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -336,6 +366,32 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
     if (s < ns) issue(s);
   for (int s = 0; s < ns; ++s) {
     // stage s must be in; the later stages already issued may still be in flight
+    if constexpr (PAIR) {
+      // of the two stages after s, one carries weights: 2 (WM / 4) + WN loads; one stage after s: at
+      // least WM / 4
+      static_assert(NS == 4, "the pair ring counts two stages in flight");
+      const int ahead = ns - 1 - s;
+      if (ahead >= 2)
+        wait_vm<2 * (WM / 4) + WN>();
+      else if (ahead == 1)
+        wait_vm<WM / 4>();
+      else
+        wait_vm<0>();
+      wg_barrier();
+      if (s + NS - 1 < ns) issue(s + NS - 1);
+      const unsigned char* st = smem + (s % NS) * WM * 1024;
+      const unsigned char* sw = smem + (P::ACT + ((s >> 1) % P::WB) * 4 * WN) * 1024;
+      bf16x8 wf[WN];
+#pragma unroll
+      for (int n = 0; n < WN; ++n) wf[n] = *(const bf16x8*)(sw + (wave * WN + n) * 1024 + lane * 16);
+#pragma unroll
+      for (int m = 0; m < WM; ++m) {
+        const bf16x8 af = *(const bf16x8*)(st + m * 1024 + lane * 16);
+#pragma unroll
+        for (int n = 0; n < WN; ++n) acc[n][m] = mma32(wf[n], af, acc[n][m]);
+      }
+      continue;
+    }
     wait_ahead<KS * T::PW, NS - 2>(ns - 1 - s);
     wg_barrier();  // stage s is in LDS for every wave; every wave is done with stage s - 1
     if (s + NS - 1 < ns) issue(s + NS - 1);
@@ -646,8 +702,11 @@ size_t gemm_part_elems(const GemmT& g) { return g.splits > 1 ? (size_t)g.splits 
 
 template <int WN, int WM, int EPI>
 hipError_t allow_lds() {
-  return hipFuncSetAttribute((const void*)k_tgemm_ring<WN, WM, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             Tile<WN, WM>::LDS);
+  hipError_t e = hipFuncSetAttribute((const void*)k_tgemm_ring<WN, WM, EPI, false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, Tile<WN, WM>::LDS);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)k_tgemm_ring<WN, WM, EPI, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             PairRing<WN, WM>::LDS);
 }
 
 template <int EPI>
@@ -678,8 +737,11 @@ hipError_t launch_tile(const GemmT& g, hipStream_t s) {
   using T = Tile<WN, WM>;
   if (g.N % T::BN || g.Mp % T::BM) return hipErrorInvalidValue;  // the grid covers whole tiles only
   const dim3 grid((g.N / T::BN) * (g.Mp / T::BM) * g.splits);
-  if (g.kern == 0)
-    hipLaunchKernelGGL((k_tgemm_ring<WN, WM, EPI>), grid, dim3(256), T::LDS, s, g);
+  constexpr int PAIR_LDS = PairRing<WN, WM>::LDS;
+  if (g.kern == 0 && g.wsh)
+    hipLaunchKernelGGL((k_tgemm_ring<WN, WM, EPI, true>), grid, dim3(256), PAIR_LDS, s, g);
+  else if (g.kern == 0)
+    hipLaunchKernelGGL((k_tgemm_ring<WN, WM, EPI, false>), grid, dim3(256), T::LDS, s, g);
   else if (g.wsh)
     hipLaunchKernelGGL((k_tgemm_reg<WN, WM, EPI, true>), grid, dim3(256), 0, s, g);
   else
