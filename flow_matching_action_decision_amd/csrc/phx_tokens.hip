@@ -105,6 +105,7 @@ __device__ inline f32x4 mma16(const s16x4& a, const s16x4& b, const f32x4& c) {
 // With split > 1 workgroup z multiplies k-steps [z KT/split, (z+1) KT/split)
 // and stores its raw sums for an ordered reduction.
 constexpr int WPD = 2;     // weight prefetch distance in k-steps (k_tgemm_reg)
+constexpr int PAIR_STAGES = 6;  // stages of the ring GEMM on paired activation rows (4: the rollout 1% slower)
 constexpr int UNR = 4;     // k_tgemm_reg main-loop unroll: its register rings rotate with it
 static_assert(WPD < UNR && UNR % 2 == 0, "the weight ring holds UNR k-steps, the activation ring 2");
 
@@ -285,16 +286,29 @@ __device__ inline void epi_store(const GemmT& g, int row, int nt, int gq, const 
 
 // PAIR: paired activation rows (wsh = 1).  A stage then holds only its
 // k-step's activation fragments; the weight fragments of k-step pair p (hi
-// 2 p, lo 2 p + 1) arrive once, with stage 2 p, in weight buffer p mod 3 (the
-// pair read two stages before p's issue is done by then), and both stages
-// multiply them.
+// 2 p, lo 2 p + 1) arrive once, with stage 2 p, in weight buffer p mod WB,
+// and both stages multiply them.  Stage 2 p is issued NS - 1 stages ahead,
+// when the pairs p - NS / 2 .. p - 1 are still to be read: WB = NS / 2 + 1.
 template <int WN, int WM>
 struct PairRing {
-  static constexpr int WB = 3;                          // weight buffers
-  static constexpr int ACT = Tile<WN, WM>::NS * WM;     // activation fragments of the NS stages
+  static constexpr int NS = PAIR_STAGES;
+  static constexpr int WB = NS / 2 + 1;                 // weight buffers
+  static constexpr int ACT = NS * WM;                   // activation fragments of the NS stages
   static constexpr int LDS = (ACT + WB * 4 * WN) * 1024;
-  static_assert(LDS <= Tile<WN, WM>::LDS, "no more LDS than the plain ring");
+  static_assert(NS % 2 == 0 && LDS <= 160 * 1024, "stages in pairs, within one workgroup's LDS");
 };
+// waits until stage s of a pair ring is in: of the a = min(ahead, A) stages
+// issued after it, at least a PA activation loads and a / 2 weight groups of
+// WN loads may stay in flight (exactly that many when a = A, A even)
+template <int PA, int WN, int A>
+__device__ inline void wait_pair(int ahead) {
+  if constexpr (A <= 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= A) wait_vm<A * PA + (A / 2) * WN>();
+    else wait_pair<PA, WN, A - 1>(ahead);
+  }
+}
 template <int WN, int WM, int EPI, bool PAIR>
 __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   using T = Tile<WN, WM>;
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   const unsigned vow = (unsigned)lane * 16u;
   auto issue_pair = [&](int s) {
     const int kt = kb + s;
-    const unsigned st = lds0 + (unsigned)((s % NS) * WM * 1024);
+    const unsigned st = lds0 + (unsigned)((s % P::NS) * WM * 1024);
 #pragma unroll
     for (int i = 0; i < WM / 4; ++i)
       dma_frag(st + (unsigned)((wave * (WM / 4) + i) * 1024), voa[i], ra, (unsigned)(kt * 64));
@@ -361,25 +375,18 @@ __global__ __launch_bounds__(256) void k_tgemm_ring(GemmT g) {
   for (int n = 0; n < WN; ++n)
 #pragma unroll
     for (int m = 0; m < WM; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int NI = PAIR ? P::NS : NS;  // stages of the ring
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
+  for (int s = 0; s < NI - 1; ++s)
     if (s < ns) issue(s);
   for (int s = 0; s < ns; ++s) {
     // stage s must be in; the later stages already issued may still be in flight
     if constexpr (PAIR) {
-      // of the two stages after s, one carries weights: 2 (WM / 4) + WN loads; one stage after s: at
-      // least WM / 4
-      static_assert(NS == 4, "the pair ring counts two stages in flight");
-      const int ahead = ns - 1 - s;
-      if (ahead >= 2)
-        wait_vm<2 * (WM / 4) + WN>();
-      else if (ahead == 1)
-        wait_vm<WM / 4>();
-      else
-        wait_vm<0>();
+      static_assert(P::NS * (WM / 4) + P::NS / 2 * WN <= 63, "vmcnt holds at most 63 loads");
+      wait_pair<WM / 4, WN, P::NS - 2>(ns - 1 - s);
       wg_barrier();
-      if (s + NS - 1 < ns) issue(s + NS - 1);
-      const unsigned char* st = smem + (s % NS) * WM * 1024;
+      if (s + P::NS - 1 < ns) issue(s + P::NS - 1);
+      const unsigned char* st = smem + (s % P::NS) * WM * 1024;
       const unsigned char* sw = smem + (P::ACT + ((s >> 1) % P::WB) * 4 * WN) * 1024;
       bf16x8 wf[WN];
 #pragma unroll
