@@ -456,14 +456,20 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(g.w), (short)0, (int)(((size_t)g.K >> g.wsh) * g.N * 2), 0x00020000);
   const int wsh = PAIR ? 1 : __builtin_amdgcn_readfirstlane(g.wsh);
-  // activation pieces of this thread: rows p*64 + tid/4, k chunk tid%4
+  // activation pieces of this thread: rows p*64 + tid/4, k chunk tid%4.  In
+  // LDS, the 16-byte piece (row r of an m-tile, chunk c) sits at slot
+  // 16 c + ((r + 4 c) mod 16) of the tile's 64: the four chunks of one row,
+  // which four neighbouring threads store together, fall in different banks
+  // (unrotated, 256 bytes apart, they shared one), and a lane's MFMA fragment
+  // (row lane mod 16, chunk lane / 16) reads back as before.
   int avo[T::AP], aslot[T::AP];
 #pragma unroll
   for (int p = 0; p < T::AP; ++p) {
-    const int r = p * 64 + (tid >> 2);
-    avo[p] = (int)(((size_t)(m0 + r) * g.K + 8 * (tid & 3)) * 2);
-    aslot[p] = (r >> 4) * 64 + (r & 15) + 16 * (tid & 3);
+    const int r = p * 64 + (tid >> 2), c = tid & 3;
+    avo[p] = (int)(((size_t)(m0 + r) * g.K + 8 * c) * 2);
+    aslot[p] = (r >> 4) * 64 + 16 * c + (((r & 15) + 4 * c) & 15);
   }
+  const int fslot = 16 * (lane >> 4) + (((lane & 15) + 4 * (lane >> 4)) & 15);
   const int wvo = lane * 16;
   // weight k-tile of activation k-step kb + s is (kb + s) >> wsh (paired activation rows: each weight
   // fragment meets the hi and then the lo k-step; kb and the unrolled k-step groups are even)
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void k_tgemm_reg(GemmT g) {
     const u32x4* st = as[j & 1];
 #pragma unroll
     for (int m = 0; m < WM; ++m) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, st[m * 64 + lane]);
+      const bf16x8 af = __builtin_bit_cast(bf16x8, st[m * 64 + fslot]);
 #pragma unroll
       for (int n = 0; n < WN; ++n) acc[n][m] = mma32(__builtin_bit_cast(bf16x8, wr[wslot(j)][n]), af, acc[n][m]);
     }
