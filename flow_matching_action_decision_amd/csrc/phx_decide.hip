@@ -201,12 +201,10 @@ __device__ inline unsigned pair_word(float a, unsigned gen) {
   const bf16 l = (bf16)(a - (float)h);
   return ((unsigned)bits16(h) << 16) | ((unsigned)bits16(l) & 0xfffeu) | gen;
 }
-// float32 word with the generation bit in the last mantissa bit
 // Norm inputs of the QKV projection and the velocity head travel as plain
 // bf16, two columns per word: the odd column rounded to bf16 in the upper
-// half, the even column rounded to 7 fraction bits in the lower half, whose
-// last bit then carries the generation.  (The MLP's norm input keeps pairs.)
-constexpr bool PLAIN_N = true;
+// half, the even column in the lower half rounded to 6 fraction bits, the
+// seventh carrying the generation.  (The MLP's norm input keeps pairs.)
 __device__ inline unsigned bf16x2_word(float a0, float a1, unsigned gen) {
   const unsigned u0 = as_u(a0), u1 = as_u(a1);
   const unsigned lo = ((u0 + 0xffffu + ((u0 >> 17) & 1u)) >> 16) & 0xfffeu;
@@ -218,6 +216,7 @@ __device__ inline bf16x8 frag_plain(const u32x4& v) {
   const u32x4 r = {v[0] & ~1u, v[1] & ~1u, v[2] & ~1u, v[3] & ~1u};
   return __builtin_bit_cast(bf16x8, r);
 }
+// float32 word with the generation bit in the last mantissa bit
 __device__ inline unsigned f32_word(float a, unsigned gen) { return (as_u(a) & ~1u) | gen; }
 // bf16 probability pair (hi, lo) for the P . V products
 __device__ inline void split_bf16(float a, short& hi, short& lo) {
@@ -690,7 +689,7 @@ __device__ inline u32x2 owner_scale_load(const Ctx& c, const Own& o, int k, int 
 template <int T_N, int T_SS>
 __device__ inline void owner_publish(Ctx& c, const Own& o, const float (&h)[2], const u32x2& sv, const Use& u) {
   const float n0 = h[0] * (1.0f + as_f(sv[0])), n1 = h[1] * (1.0f + as_f(sv[1]));
-  if constexpr (T_N == X_N && PLAIN_N) {
+  if constexpr (T_N == X_N) {
     st1<LST>(c, xb<T_N>(c, u.par) + (unsigned)(o.row * (D / 2) * 4) + (o.col / 2u) * 4u, bf16x2_word(n0, n1, u.gen));
   } else {
     const u32x2 w = {pair_word(n0, u.gen), pair_word(n1, u.gen)};
@@ -707,7 +706,7 @@ __device__ inline void owner_publish(Ctx& c, const Own& o, const float (&h)[2], 
 // loads of a poll_normed: 16 (pairs) or 8 (plain words) for the wave's k-tiles, then 2
 template <int T_N>
 constexpr int normed_loads() {
-  return (T_N == X_N && PLAIN_N ? 8 : 16) + 2;
+  return (T_N == X_N ? 8 : 16) + 2;
 }
 template <int T_N, int T_SS>
 __device__ __attribute__((always_inline)) inline void poll_normed(Ctx& c, const Use& u,
@@ -800,10 +799,7 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
   u32x4 v[normed_loads<X_N>()];
   poll_normed<X_N, X_SS>(c, u, v);
   f32x4 acc[1];
-  if constexpr (PLAIN_N)
-    gemm_plain<1, 8>(w, v, acc);
-  else
-    gemm_pairs<1, 8>(w, v, acc);
+  gemm_plain<1, 8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
   red[c.wave * 64 + c.lane] = acc[0];
   cw_barrier(c);
@@ -1288,10 +1284,7 @@ __device__ __attribute__((always_inline)) inline void ph_vel(Ctx& c, int k, f32x
   u32x4 v[normed_loads<X_N>()];
   poll_normed<X_N, X_SS>(c, u, v);
   f32x4 acc[2];
-  if constexpr (PLAIN_N)
-    gemm_plain<2, 8>(w, v, acc);
-  else
-    gemm_pairs<2, 8>(w, v, acc);
+  gemm_plain<2, 8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
