@@ -161,6 +161,10 @@ constexpr unsigned long long W_DN0 = W_GU0 + (unsigned long long)D * 2 * F;
 __host__ __device__ constexpr unsigned long long w_out(int NL) { return W_QKV0 + (unsigned long long)NL * W_LAYER; }
 __host__ __device__ constexpr unsigned long long w_elems(int NL) { return w_out(NL) + (unsigned long long)D * A; }
 
+// 8-bit tier: column scales per layer, [NQKV][D][2F][D] f32 in tile column order
+constexpr int SC_LAYER = NQKV + D + 2 * F + D;
+constexpr int SC_QKV = 0, SC_O = NQKV, SC_GU = NQKV + D, SC_DN = NQKV + D + 2 * F;
+
 struct Args {
   const void* wt;   // tiled bf16 weights
   const void* kvt;  // attention-tiled prefix K/V: [NL][n_chunks][64 tiles]
@@ -170,6 +174,13 @@ struct Args {
   unsigned tl;      // nonzero: record the phase timeline
   int S, NL, R, n_chunks;
   float dt, eps;
+  // the 8-bit weight tier (null: bf16): int8 codes of every layer's four
+  // projections at the element offsets of wt (a 512-byte tile per 16 x 32
+  // block), and their per-column scales, per layer [NQKV][D][2F][D] f32 in
+  // tile column order
+  const void* wq;
+  const float* wsc;
+  unsigned wq_bytes, wsc_bytes;
 };
 
 hipError_t launch_decide(const Args& a, hipStream_t s);
@@ -197,10 +208,12 @@ hipError_t decide_scratch(int dev, void** ptr);
 // out[k * out_kstride + l * N + n] = sum_d shift(k, norm_stride*l + norm_off)[d] * W_l[d][colmap(n)]
 // for k < S, l < nl, n < N, where W_l = w0 + l * w_lstride is a [D][N] bf16
 // matrix of the caller's blob and colmap is the tile column order of the tiled
-// arena (colkind: 0 identity, 1 RoPE pairs, 2 GeGLU pairs)
+// arena (colkind: 0 identity, 1 RoPE pairs, 2 GeGLU pairs).  With column
+// scales sc (non-null: the 8-bit tier, layer l's at sc + l * sc_lstride, tile
+// column order) W_l is replaced by s q, the tier's quantised weights.
 hipError_t launch_shift_table(const void* w0, long long w_lstride, const float* modtab, int NN, int norm_stride,
-                              int norm_off, int S, int nl, int N, int colkind, int colparam, float* out,
-                              size_t out_kstride, hipStream_t s);
+                              int norm_off, int S, int nl, int N, int colkind, int colparam, const float* sc,
+                              long long sc_lstride, float* out, size_t out_kstride, hipStream_t s);
 // scale[k][norm][d] of the modulation table [S][NN][2D] into each step block of the tables at aux
 hipError_t launch_scale_table(const float* modtab, int S, int NN, void* aux, int NL, hipStream_t s);
 hipError_t launch_attn_tiles(const void* k, const void* v, void* kvt, int NL, int L, int n_chunks, hipStream_t s);

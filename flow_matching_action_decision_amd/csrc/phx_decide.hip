@@ -272,6 +272,8 @@ struct Ctx {
   unsigned char* ring;
   Rsrc X;                  // exchange words, control words at CT_*
   Rsrc Y;                  // the handle's auxiliary tables
+  Rsrc SC;                 // 8-bit tier: column scales
+  bool w8;                 // 8-bit tier: the four projections stream int8 tiles, two per ring slot
   unsigned seq;            // this decision's counter
   unsigned redsel;         // which half of the scratch the current phase uses
   unsigned barn;           // compute-wave barriers passed
@@ -554,6 +556,64 @@ __device__ __attribute__((always_inline)) inline void gemm_plain(const u32x4 (&w
   for (int t = 0; t < NT; ++t) acc[t] = ae[t] + ao[t];
 }
 
+// 8-bit tier: a lane's 8 int8 codes of one tile (k order) as its bf16
+// fragment; exact, since |q| <= 127 fits bf16's significand (the float's
+// upper half is the bf16)
+__device__ inline u32x4 i8_frag(const u32x2& q) {
+  u32x4 r;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const unsigned wd = q[m >> 1];
+    const int sh = 16 * (m & 1);
+    const float f0 = (float)(int)(signed char)(wd >> sh);
+    const float f1 = (float)(int)(signed char)(wd >> (sh + 8));
+    r[m] = __builtin_amdgcn_perm(as_u(f1), as_u(f0), 0x07060302u);
+  }
+  return r;
+}
+// ring_fetch for int8 tiles: tile i of the phase's run sits in slot i / 2,
+// half i % 2 (512 bytes: 8 codes per lane)
+template <int NT, int KK, typename OF>
+__device__ __attribute__((always_inline)) inline void ring_fetch_i8(const Ctx& c, unsigned p0, OF off,
+                                                                    u32x4 (&w)[KK][NT]) {
+  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
+  u32x2 q[KK][NT];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const unsigned i = off(t, kk);
+      q[kk][t] = *(const u32x2*)(c.ring + ring_slot(s0, i >> 1) * TILE_BYTES + (i & 1u) * 512u + c.lane * 8);
+    }
+  reads_issued();
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[kk][t] = i8_frag(q[kk][t]);
+}
+// a phase's tiles: bf16, or int8 in the 8-bit tier (n tiles take n / 2 slots)
+template <bool W8, int NT, int KK, typename OF>
+__device__ __attribute__((always_inline)) inline void fetch_tiles(const Ctx& c, unsigned p0, OF off,
+                                                                  u32x4 (&w)[KK][NT]) {
+  if constexpr (W8)
+    ring_fetch_i8<NT, KK>(c, p0, off, w);
+  else
+    ring_fetch<NT, KK>(c, p0, off, w);
+}
+template <bool W8>
+constexpr unsigned slots(unsigned tiles) {
+  return W8 ? tiles / 2u : tiles;
+}
+// column scales of 4 columns (n-tile nt, columns 4 g + [0, 4)) of matrix
+// block `which` of layer l; ones outside the 8-bit tier
+template <bool W8>
+__device__ inline u32x4 col_scales(const Ctx& c, int l, int which, int nt) {
+  if constexpr (W8)
+    return __builtin_amdgcn_raw_buffer_load_b128(c.SC, (unsigned)((l * SC_LAYER + which + nt * 16 + 4 * c.g) * 4), 0, 0);
+  else
+    return u32x4{0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u};
+}
+
 // ------------------------------------------------------------- exchange
 
 // Where load i of a poll reads: per-lane byte offset vo and uniform so in the
@@ -780,6 +840,7 @@ __device__ __attribute__((always_inline)) inline void ph_in(Ctx& c, int k, float
 // QKV projection of one n-tile (K = D split over the four waves), epilogue
 // 1/rms, shift . W and RoPE (wave 0); writes q of the XCD's head (local) or
 // the XCD's share of the action keys and values (device scope)
+template <bool W8>
 __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int l) {
   refresh(c);
   if (!is_qkv(c)) return;
@@ -793,9 +854,10 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
       c.Y, step_tab(c, k) + st_swqkv(c.NL) + (unsigned)((l * NQKV + nt * 16 + 4 * c.g) * 4), 0, 0);
   const u32x4 cs = __builtin_amdgcn_raw_buffer_load_b128(
       c.Y, AUX_ROPE + (unsigned)((c.row * (DH / 2) + 8 * tt + 2 * c.g) * 8), 0, 0);
-  wait_tiles(c, p0, 32);
+  const u32x4 sq = col_scales<W8>(c, l, SC_QKV, nt);
+  wait_tiles(c, p0, slots<W8>(32));
   u32x4 w[8][1];
-  ring_fetch<1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, w);
+  fetch_tiles<W8, 1, 8>(c, p0, [&](int, int kk) { return 8u * c.wave + kk; }, w);
   u32x4 v[normed_loads<X_N>()];
   poll_normed<X_N, X_SS>(c, u, v);
   f32x4 acc[1];
@@ -803,9 +865,13 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
   f32x4* red = (f32x4*)red_take(c);
   red[c.wave * 64 + c.lane] = acc[0];
   cw_barrier(c);
-  release_ring(c, p0 + 32u);
+  release_ring(c, p0 + slots<W8>(32));
   if (c.wave == 0) {
-    const f32x4 s = red_sum(red, 1, 0, c.lane);
+    f32x4 s = red_sum(red, 1, 0, c.lane);
+    if constexpr (W8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] *= as_f(sq[e]);
+    }
     const float rr = c.sh->rrow[c.row];
     float y[4];
 #pragma unroll
@@ -1136,14 +1202,16 @@ __device__ __attribute__((always_inline)) inline void ph_merge(Ctx& c, int k, in
 // [32 o, 32 o + 32) (two n-tiles; K split over the four waves): a partial
 // sum of the residual update, published at device scope for the owners of
 // every XCD
+template <bool W8>
 __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l) {
   refresh(c);
   const int o = c.rk;
   const Use u = use_layer(c, k, l);
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_o;
-  wait_tiles(c, p0, 8 * O_NT);
+  const u32x4 sq = col_scales<W8>(c, l, SC_O, O_NT * o + (c.wave & (O_NT - 1)));
+  wait_tiles(c, p0, slots<W8>(8 * O_NT));
   u32x4 w[2][O_NT];
-  ring_fetch<O_NT, 2>(c, p0, [&](int t, int j) { return 8u * t + 2u * c.wave + j; }, w);
+  fetch_tiles<W8, O_NT, 2>(c, p0, [&](int t, int j) { return 8u * t + 2u * c.wave + j; }, w);
   u32x4 v[4];
   {
     const unsigned vo = row_off(c, (unsigned)((c.row * DH + 64 * c.wave + 8 * c.g) * 4));
@@ -1157,9 +1225,13 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
 #pragma unroll
   for (int t = 0; t < O_NT; ++t) red[(c.wave * O_NT + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
-  release_ring(c, p0 + 8u * O_NT);
+  release_ring(c, p0 + slots<W8>(8 * O_NT));
   if (c.wave < O_NT) {
-    const f32x4 s = red_sum(red, O_NT, c.wave, c.lane);  // wave t finishes n-tile t
+    f32x4 s = red_sum(red, O_NT, c.wave, c.lane);  // wave t finishes n-tile t
+    if constexpr (W8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] *= as_f(sq[e]);
+    }
     if (c.row < c.R) {
       const u32x4 w = {f32_word(s[0], u.gen), f32_word(s[1], u.gen), f32_word(s[2], u.gen), f32_word(s[3], u.gen)};
       st4<SC1>(c, xb<X_OP>(c, u.par) +
@@ -1196,6 +1268,7 @@ __device__ __attribute__((always_inline)) inline void ph_own(Ctx& c, int k, int 
 
 // gate/up projection of two n-tiles with the GeGLU epilogue: features
 // 16 r + 8 t + 2 g + [0, 2) of the XCD's 512
+template <bool W8>
 __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l) {
   refresh(c);
   const Use u = use_layer(c, k, l);
@@ -1203,9 +1276,10 @@ __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l
   const int nt = 64 * c.xcd + 2 * c.rk + (c.wave & 1);
   const u32x4 sw = __builtin_amdgcn_raw_buffer_load_b128(
       c.Y, step_tab(c, k) + st_swgu(c.NL) + (unsigned)((l * 2 * F + nt * 16 + 4 * c.g) * 4), 0, 0);
-  wait_tiles(c, p0, 64);
+  const u32x4 sq = col_scales<W8>(c, l, SC_GU, nt);
+  wait_tiles(c, p0, slots<W8>(64));
   u32x4 w[8][2];
-  ring_fetch<2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, w);
+  fetch_tiles<W8, 2, 8>(c, p0, [&](int t, int kk) { return 32u * t + 8u * c.wave + kk; }, w);
   u32x4 v[normed_loads<X_N2>()];
   poll_normed<X_N2, X_SS2>(c, u, v);
   f32x4 acc[2];
@@ -1214,9 +1288,13 @@ __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
-  release_ring(c, p0 + 64u);
+  release_ring(c, p0 + slots<W8>(64));
   if (c.wave < 2) {
-    const f32x4 s = red_sum(red, 2, c.wave, c.lane);
+    f32x4 s = red_sum(red, 2, c.wave, c.lane);
+    if constexpr (W8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] *= as_f(sq[e]);
+    }
     const float rr = c.sh->rrow[c.row];
     float y[4];
 #pragma unroll
@@ -1233,13 +1311,15 @@ __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l
 // down projection of the XCD's 512 features (K split over the four waves)
 // for output columns [32 r, 32 r + 32): a partial sum for the owners of
 // every XCD
+template <bool W8>
 __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int l) {
   refresh(c);
   const Use u = use_layer(c, k, l);
   const unsigned p0 = (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_dn;
-  wait_tiles(c, p0, 32);
+  const u32x4 sq = col_scales<W8>(c, l, SC_DN, 2 * c.rk + (c.wave & 1));
+  wait_tiles(c, p0, slots<W8>(32));
   u32x4 w[4][2];
-  ring_fetch<2, 4>(c, p0, [&](int t, int j) { return 16u * t + 4u * c.wave + j; }, w);
+  fetch_tiles<W8, 2, 4>(c, p0, [&](int t, int j) { return 16u * t + 4u * c.wave + j; }, w);
   u32x4 v[8];
   {
     const unsigned vo = row_off(c, (unsigned)((c.row * FX + 128 * c.wave + 8 * c.g) * 4));
@@ -1253,9 +1333,13 @@ __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
-  release_ring(c, p0 + 32u);
+  release_ring(c, p0 + slots<W8>(32));
   if (c.wave < 2) {
-    const f32x4 s = red_sum(red, 2, c.wave, c.lane);
+    f32x4 s = red_sum(red, 2, c.wave, c.lane);
+    if constexpr (W8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] *= as_f(sq[e]);
+    }
     if (c.row < c.R) {
       const u32x4 w = {f32_word(s[0], u.gen), f32_word(s[1], u.gen), f32_word(s[2], u.gen), f32_word(s[3], u.gen)};
       st4<SC1>(c, xb<X_DP>(c, u.par) + (unsigned)(((c.xcd * RP + c.row) * D + 32 * c.rk + 16 * c.wave + 4 * c.g) * 4),
@@ -1322,7 +1406,7 @@ struct Gen {
   unsigned pos0;          // stream position of the run's first tile
   unsigned off0;          // byte offset of the run's first tile
   int cnt;                // tiles in the run
-  int kv;                 // 1: run reads the prefix K/V arena
+  int kv;                 // source: 0 bf16 weights, 1 the prefix K/V arena, 2 int8 codes (two tiles per slot)
 };
 
 constexpr int RUNS_PER_LAYER = 9;
@@ -1348,10 +1432,16 @@ __device__ inline void run_params(const Ctx& c, int run, unsigned& off, int& cnt
   }
   const int l = (run - 1) / RUNS_PER_LAYER, u = (run - 1) % RUNS_PER_LAYER;
   const unsigned long long lo = (unsigned long long)l * W_LAYER;
+  // a layer projection's run: tiles (bf16, 2 bytes per element) or, in the
+  // 8-bit tier, slots of two int8 tiles (codes at the same element offsets)
+  const unsigned esz = c.w8 ? 1u : 2u;
+  const int div = c.w8 ? 2 : 1;
+  const int src = c.w8 ? 2 : 0;
   if (u == 0) {
     if (is_qkv(c)) {
-      cnt = KT_D;
-      off = (unsigned)((W_QKV0 + lo + (unsigned long long)qkv_ntile(r - R_QKV, x) * KT_D * TILE_ELEMS) * 2ull);
+      cnt = KT_D / div;
+      kv = src;
+      off = (unsigned)((W_QKV0 + lo + (unsigned long long)qkv_ntile(r - R_QKV, x) * KT_D * TILE_ELEMS) * esz);
     }
   } else if (u == 1) {
     if (r < c.nc) {
@@ -1362,16 +1452,19 @@ __device__ inline void run_params(const Ctx& c, int run, unsigned& off, int& cnt
   } else if (u <= 5) {
     if (u - 2 < O_NT) {
       const int nt = O_NT * r + (u - 2);
-      cnt = 8;
-      off = (unsigned)((W_O0 + lo + ((unsigned long long)nt * KT_HD + 8 * x) * TILE_ELEMS) * 2ull);
+      cnt = 8 / div;
+      kv = src;
+      off = (unsigned)((W_O0 + lo + ((unsigned long long)nt * KT_HD + 8 * x) * TILE_ELEMS) * esz);
     }
   } else if (u == 6) {
-    cnt = 64;
-    off = (unsigned)((W_GU0 + lo + (unsigned long long)(64 * x + 2 * r) * KT_D * TILE_ELEMS) * 2ull);
+    cnt = 64 / div;
+    kv = src;
+    off = (unsigned)((W_GU0 + lo + (unsigned long long)(64 * x + 2 * r) * KT_D * TILE_ELEMS) * esz);
   } else {
     const int nt = 2 * r + (u - 7);
-    cnt = 16;
-    off = (unsigned)((W_DN0 + lo + ((unsigned long long)nt * KT_F + 16 * x) * TILE_ELEMS) * 2ull);
+    cnt = 16 / div;
+    kv = src;
+    off = (unsigned)((W_DN0 + lo + ((unsigned long long)nt * KT_F + 16 * x) * TILE_ELEMS) * esz);
   }
 }
 
@@ -1434,9 +1527,11 @@ __device__ inline void loader_keep_waiting(Ctx& c, unsigned t0, unsigned& spins)
   }
 }
 
+template <bool W8>
 __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, const Args& a) {
-  const u32x4 WR = rsrc_words(a.wt, a.wt_bytes);
+  const u32x4 WR = rsrc_words(W8 ? a.wq : a.wt, W8 ? a.wq_bytes : a.wt_bytes);  // W8: the codes
   const u32x4 KR = rsrc_words(a.kvt, a.kvt_bytes);
+  const u32x4 BR = rsrc_words(a.wt, a.wt_bytes);  // W8: the bf16 in- and out-projections
   const unsigned ring_lds =
       (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)c.ring);
   Gen s;
@@ -1467,8 +1562,10 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
     }
     cbar();
     const unsigned lds = __builtin_amdgcn_readfirstlane(ring_lds + (pos % RING) * TILE_BYTES);
-    if (kv)
+    if (kv == 1)
       dma_tile(KR, (unsigned)c.lane * 16u, off, lds, false);
+    else if (W8 && kv == 0)
+      dma_tile(BR, (unsigned)c.lane * 16u, off, lds, true);
     else
       dma_tile(WR, (unsigned)c.lane * 16u, off, lds, true);
     ++issued;
@@ -1486,6 +1583,7 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
 
 // ---------------------------------------------------------------- kernel
 
+template <bool W8>
 __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char ring_mem[];
   __shared__ Shared sh;
@@ -1510,20 +1608,22 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
   if (threadIdx.x < 32) ((unsigned*)&sh)[threadIdx.x] = 0u;
   c.X = rsrc(a.ex, XC_BYTES);
   c.Y = rsrc(a.aux, a.aux_bytes);
+  c.w8 = W8;
+  if constexpr (W8) c.SC = rsrc(const_cast<float*>(a.wsc), a.wsc_bytes);
   c.seq = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(c.X, CT_SEQ, 0, SC1));
   c.L = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b32(c.Y, AUX_LENS, 0, 0));
   c.crow = c.row < c.R ? c.row : c.R - 1;
   // stream layout of this workgroup (must match run_params)
-  c.o_att = is_qkv(c) ? (unsigned)KT_D : 0u;
+  c.o_att = is_qkv(c) ? slots<W8>(KT_D) : 0u;
   c.o_o = c.o_att + (c.rk < c.nc ? 64u : 0u);
-  c.o_gu = c.o_o + 8u * O_NT;
-  c.o_dn = c.o_gu + 64u;
-  c.n_layer = c.o_dn + 32u;
+  c.o_gu = c.o_o + slots<W8>(8u * O_NT);
+  c.o_dn = c.o_gu + slots<W8>(64u);
+  c.n_layer = c.o_dn + slots<W8>(32u);
   c.n_step = 2u + (unsigned)c.NL * c.n_layer + (is_vel(c) ? 64u : 0u);
   __syncthreads();
 
   if (c.wave >= NCOMPUTE) {
-    loader(c, c.wave - NCOMPUTE, a);
+    loader<W8>(c, c.wave - NCOMPUTE, a);
     if (c.wave == NCOMPUTE) tl_mark(c, timeline_events(c.S, c.NL) - 1);
     return;
   }
@@ -1550,7 +1650,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
     if (tl) tl_mark(c, e0);
     for (int l = 0; l < c.NL; ++l) {
       const int el = e0 + 1 + PHASES_PER_LAYER * l;
-      ph_qkv(c, k, l);
+      ph_qkv<W8>(c, k, l);
       if (tl) tl_mark(c, el);
       // two separate tests: as one if/else the compiler's uniformity analysis loses track of the
       // context's scalar fields after the join and cannot build the kernel
@@ -1559,13 +1659,13 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
       if (tl) tl_mark(c, el + 1);
       ph_merge(c, k, l);
       if (tl) tl_mark(c, el + 2);
-      ph_o(c, k, l);
+      ph_o<W8>(c, k, l);
       if (tl) tl_mark(c, el + 3);
       ph_own<X_OP, X_N2, X_SS2>(c, k, 2 * l + 1, use_layer(c, k, l), use_layer(c, k, l), h);
       if (tl) tl_mark(c, el + 4);
-      ph_gu(c, k, l);
+      ph_gu<W8>(c, k, l);
       if (tl) tl_mark(c, el + 5);
-      ph_down(c, k, l);
+      ph_down<W8>(c, k, l);
       if (tl) tl_mark(c, el + 6);
       ph_own<X_DP, X_N, X_SS>(c, k, 2 * (l + 1), use_layer(c, k, l), use_norm(c, k, l + 1), h);
       if (tl) tl_mark(c, el + 7);
@@ -1631,8 +1731,11 @@ static u32x4 shape_of(const Args& a) {
 static hipError_t allow_ring_lds() {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_decide, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)k_decide<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        RING * TILE_BYTES);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)k_decide<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            RING * TILE_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -1642,7 +1745,7 @@ static hipError_t allow_ring_lds() {
 hipError_t decide_occupancy(int* blocks_per_cu) {
   hipError_t e = allow_ring_lds();
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)k_decide, THREADS,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)k_decide<false>, THREADS,
                                                        RING * TILE_BYTES);
 }
 
@@ -1689,7 +1792,10 @@ hipError_t decide_placement(bool* ok) {
 hipError_t launch_decide(const Args& a, hipStream_t s) {
   hipError_t e = allow_ring_lds();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decide, dim3(G), dim3(THREADS), RING * TILE_BYTES, s, a);
+  if (a.wq)
+    hipLaunchKernelGGL(k_decide<true>, dim3(G), dim3(THREADS), RING * TILE_BYTES, s, a);
+  else
+    hipLaunchKernelGGL(k_decide<false>, dim3(G), dim3(THREADS), RING * TILE_BYTES, s, a);
   return hipGetLastError();
 }
 
@@ -1755,9 +1861,13 @@ __device__ inline int colmap_dev(int kind, int param, int n) {
   return 8 * nt + 2 * g + (i & 1) + (i >> 1) * param;
 }
 
+// With column scales sc (the 8-bit tier; per layer, sc_lstride apart, tile
+// column order) the weights are s q, q = rint(w / s) clamped to +-127 as the
+// tier's quantiser takes them.
 __global__ void k_shift_table(const bf16* __restrict__ w0, long long w_lstride, const float* __restrict__ modtab,
                               int NN, int norm_stride, int norm_off, int S, int nl, int N, int colkind, int colparam,
-                              float* __restrict__ out, size_t out_kstride) {
+                              const float* __restrict__ sc, long long sc_lstride, float* __restrict__ out,
+                              size_t out_kstride) {
   const size_t total = (size_t)S * nl * N;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
@@ -1768,18 +1878,27 @@ __global__ void k_shift_table(const bf16* __restrict__ w0, long long w_lstride, 
     const float* shift = modtab + ((size_t)k * NN + (size_t)(norm_stride * l + norm_off)) * 2 * D + D;
     const bf16* w = w0 + (size_t)l * w_lstride + col;
     double acc = 0.0;
-    for (int d = 0; d < D; ++d) acc += (double)shift[d] * (double)(float)w[(size_t)d * N];
+    if (sc) {
+      const float s = sc[(size_t)l * sc_lstride + n];
+      for (int d = 0; d < D; ++d) {
+        float q = s > 0.f ? rintf((float)w[(size_t)d * N] / s) : 0.f;
+        q = fminf(fmaxf(q, -127.f), 127.f);
+        acc += (double)shift[d] * ((double)s * (double)q);
+      }
+    } else {
+      for (int d = 0; d < D; ++d) acc += (double)shift[d] * (double)(float)w[(size_t)d * N];
+    }
     out[(size_t)k * out_kstride + (size_t)l * N + n] = (float)acc;
   }
 }
 
 hipError_t launch_shift_table(const void* w0, long long w_lstride, const float* modtab, int NN, int norm_stride,
-                              int norm_off, int S, int nl, int N, int colkind, int colparam, float* out,
-                              size_t out_kstride, hipStream_t s) {
+                              int norm_off, int S, int nl, int N, int colkind, int colparam, const float* sc,
+                              long long sc_lstride, float* out, size_t out_kstride, hipStream_t s) {
   const size_t total = (size_t)S * nl * N;
   const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
   hipLaunchKernelGGL(k_shift_table, dim3(blocks), dim3(256), 0, s, (const bf16*)w0, w_lstride, modtab, NN,
-                     norm_stride, norm_off, S, nl, N, colkind, colparam, out, out_kstride);
+                     norm_stride, norm_off, S, nl, N, colkind, colparam, sc, sc_lstride, out, out_kstride);
   return hipGetLastError();
 }
 

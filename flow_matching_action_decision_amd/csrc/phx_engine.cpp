@@ -399,7 +399,7 @@ int mt_for_rows(int rows) {
 // request of up to 16 action rows in bf16; every other configuration runs the
 // multi-kernel graph.
 bool persistent_eligible(const phx_expert_config& c, const hipDeviceProp_t& prop) {
-  if (c.flags & (PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL | PHX_FLAG_WEIGHTS_INT8)) return false;
+  if (c.flags & (PHX_FLAG_NO_GRAPH | PHX_FLAG_MULTI_KERNEL)) return false;
   if (c.block_kind != PHX_BLOCK_DECODER) return false;
   if (c.weight_dtype != PHX_DTYPE_BF16 || c.kv_dtype != PHX_DTYPE_BF16) return false;
   if (c.width != dec::D || c.n_heads != dec::H || c.head_dim != dec::DH || c.n_kv_heads != 1) return false;
@@ -477,12 +477,22 @@ int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t 
   const long long lstride = (long long)dec::W_LAYER;
   const size_t ks = dec::step_bytes(NL) / sizeof(float);
   char* tab = aux + dec::AUX_TAB;
+  // the 8-bit tier's scales: every layer's four projections, [NQKV][D][2F][D] per layer
+  const bool w8 = h->wq != nullptr;
+  if (w8 && (h->sc_qkv.size() != (size_t)NL || h->sc_qkv[0] != (size_t)dec::SC_QKV || h->sc_o[0] != (size_t)dec::SC_O ||
+             h->sc_gu[0] != (size_t)dec::SC_GU || h->sc_down[0] != (size_t)dec::SC_DN ||
+             (NL > 1 && h->sc_qkv[1] != (size_t)dec::SC_LAYER)))
+    return fail(PHX_E_SHAPE, "int8 scale layout differs from the decision kernel's");
+  const float* sc_qkv = w8 ? h->wsc + dec::SC_QKV : nullptr;
+  const float* sc_gu = w8 ? h->wsc + dec::SC_GU : nullptr;
   PHX_HIP(dec::launch_shift_table(sb + h->off_qkv[0] * h->esz, lstride, h->modtab, h->NN, 2, 0, S, NL, dec::NQKV,
-                                  COL_ROPE, dec::DH, (float*)(tab + dec::st_swqkv(NL)), ks, stream));
+                                  COL_ROPE, dec::DH, sc_qkv, dec::SC_LAYER, (float*)(tab + dec::st_swqkv(NL)), ks,
+                                  stream));
   PHX_HIP(dec::launch_shift_table(sb + h->off_gu[0] * h->esz, lstride, h->modtab, h->NN, 2, 1, S, NL, 2 * dec::F,
-                                  COL_GEGLU, dec::F, (float*)(tab + dec::st_swgu(NL)), ks, stream));
+                                  COL_GEGLU, dec::F, sc_gu, dec::SC_LAYER, (float*)(tab + dec::st_swgu(NL)), ks,
+                                  stream));
   PHX_HIP(dec::launch_shift_table(sb + h->off_out * h->esz, 0, h->modtab, h->NN, 0, 2 * NL, S, 1, dec::A, COL_IDENT,
-                                  0, (float*)(tab + dec::st_swout(NL)), ks, stream));
+                                  0, nullptr, 0, (float*)(tab + dec::st_swout(NL)), ks, stream));
 
   // attention-tiled prefix K/V
   const size_t kvt_bytes = (size_t)NL * h->n_chunks * 64 * dec::TILE_BYTES;
@@ -512,6 +522,10 @@ int create_persistent(phx_expert* h, const char* sb, hipStream_t stream, size_t 
   a.wt_bytes = (unsigned)(dec::w_elems(NL) * 2ull);
   a.kvt_bytes = (unsigned)kvt_bytes;
   a.aux_bytes = (unsigned)aux_bytes;
+  a.wq = w8 ? h->wq : nullptr;
+  a.wsc = w8 ? h->wsc : nullptr;
+  a.wq_bytes = w8 ? (unsigned)dec::w_elems(NL) : 0u;
+  a.wsc_bytes = w8 ? (unsigned)((size_t)NL * dec::SC_LAYER * sizeof(float)) : 0u;
   // the device's static exchange memory, for decisions that may not allocate
   // (phx_expert_decide_noalloc); the handle's own decisions do not need it
   h->scratch_rc = dec::decide_scratch_setup();
@@ -1684,11 +1698,14 @@ int phx_expert_node_info(const phx_expert* h, int32_t node, phx_node_info* info)
   info->bytes = nd.bytes;
   if (nd.kind == PHX_NODE_DECISION) {
     // every weight matrix of the step loop, the valid prefix K/V and the
-    // modulation rows, once per Euler step
+    // modulation rows, once per Euler step; on the 8-bit tier a layer
+    // projection is one byte per code plus a float scale per output column
     const phx_expert_config& c = h->cfg;
     const uint64_t D = (uint64_t)c.width, F = (uint64_t)c.mlp_hidden, A = (uint64_t)c.state_dim;
     const uint64_t qkv = (uint64_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim, hd = (uint64_t)c.n_heads * c.head_dim;
-    const uint64_t w = ((uint64_t)c.layers * (D * qkv + hd * D + D * 2 * F + F * D) + 2 * A * D) * h->esz;
+    const uint64_t proj = D * qkv + hd * D + D * 2 * F + F * D;
+    const uint64_t w_layer = h->wq ? proj + sizeof(float) * (qkv + D + 2 * F + D) : proj * h->esz;
+    const uint64_t w = (uint64_t)c.layers * w_layer + 2 * A * D * h->esz;
     uint64_t kv = 0;
     for (int b = 0; b < c.batch; ++b)
       kv += 2ull * c.layers * (uint64_t)h->lens_host[(size_t)b] * c.n_kv_heads * c.head_dim * h->esz;

@@ -72,8 +72,10 @@ extern "C" {
                                      round-to-nearest per output column (s = max|w| / 127, q =
                                      rint(w / s), ties to even, float32 arithmetic); activations stay
                                      bf16 and each projection's sum is scaled by s in fp32.  bf16
-                                     weights, decoder block, batch * rows <= 160; runs the multi-kernel
-                                     graph (see phx_expert_weight_codes) */
+                                     weights, decoder block, batch * rows <= 160; runs on the persistent
+                                     decision kernel where that kernel applies (its tile ring then
+                                     carries the codes), otherwise on the multi-kernel graph (see
+                                     phx_expert_weight_codes) */
 #define PHX_FLAG_TIMELINE 4u   /* persistent kernel: record a per-workgroup phase timeline (see
                                   phx_expert_timeline) */
 #define PHX_FLAG_PAIRED_ACT 16u  /* large-token plans (more than 160 rows, the DiT-style block, the prefill):

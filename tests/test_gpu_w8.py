@@ -7,7 +7,9 @@ bf16 activations; "PhyAI" section 4.2 Quantization) through the C ABI.
     the bf16 bar (the two compute with the same weights);
   * against the unquantised weights the decision moves by the quantisation
     error, held to the tier's own looser bar (derived below);
-  * the full pi0.5 shape on the tier, the same two checks;
+  * the full pi0.5 shape on the tier (the persistent decision kernel), the
+    same two checks; at the pi0.5 width the persistent kernel and the
+    multi-kernel graph both against the oracle on s * q;
   * replays are bit-identical; a handle without the tier has no codes.
 """
 import numpy as np
@@ -90,7 +92,29 @@ def test_w8_pi05_shape():
     cfg = phx_inputs.workload("pi05_expert_w8a16")
     say("case pi05_expert_w8a16: 18 layers x 10 steps, 768-token prefix, int8 layer projections")
     nk = _w8_case(cfg)
-    assert nk > 18 * 10  # the multi-kernel graph
+    assert nk == 2  # the persistent decision kernel (with its tag advance), int8 tiles in its ring
+
+
+@pytest.mark.parametrize("rows,L", [(10, 768), (3, 100), (16, 1)])
+def test_w8_persistent_and_graph(rows, L):
+    """The tier on the persistent decision kernel (int8 tiles in its ring,
+    column scales in its epilogues) and on the multi-kernel graph, at the
+    pi0.5 width with 2 layers x 2 steps: each against the oracle on s * q, and
+    the two paths agree with each other to the same bar."""
+    cfg = phx_inputs.workload("pi05_expert_w8a16", id=81, layers=2, steps=2, dt=-0.5, rows=rows, prefix_lens=[L])
+    cfg["name"] = f"w8_persistent_r{rows}_L{L}"
+    say(f"case {cfg['name']}")
+    inp = phx_inputs.make_inputs(cfg, 0)
+    outs_p, nk_p = gpu_decide(cfg, inp, repeats=2)
+    outs_g, nk_g = gpu_decide(cfg, inp, flags=2)  # PHX_FLAG_MULTI_KERNEL
+    assert nk_p == 2 and nk_g > 2
+    assert np.array_equal(outs_p[0], outs_p[1]), "replays must be bit-identical"
+    sl = phx_inputs.weight_slices(cfg)
+    ref_q = oracle.decide(cfg, oracle.w8_weights(cfg, inp["weights"], sl), inp["kv_k"], inp["kv_v"], inp["lens"],
+                          inp["noise"])["actions"]
+    assert_close(outs_p[0], ref_q, TOL_BF16, what=f"{cfg['name']} persistent vs the oracle on s * q")
+    assert_close(outs_g[0], ref_q, TOL_BF16, what=f"{cfg['name']} graph vs the oracle on s * q")
+    assert_close(outs_p[0], outs_g[0], TOL_BF16, what=f"{cfg['name']} persistent vs graph")
 
 
 def test_codes_need_the_tier():
