@@ -9,7 +9,7 @@ before the timed region starts.
 
 --workload pi05_expert_w8a16 runs the same decision on the 8-bit weight tier
 (int8 codes per output column for every layer projection, bf16 activations;
-the multi-kernel graph).
+the tier's instance of the persistent decision kernel).
 --workload va_chunk_bf16 (256-row video-action chunk over a 4096-row cache,
 8 layers x 5 steps) or wam_dit_bf16 (DiT-style step over 4128 tokens, 4
 blocks) measures the large-token plan instead; those are MFMA-bound, so their
@@ -17,8 +17,8 @@ roofline is the dominant GEMM's TFLOP/s against the bf16 dense peak.
 --workload prefix_prefill_bf16 times the prefix prefill (18 causal layers of
 width 2048 over 768 tokens in an 800-row bucket, writing the K/V cache), one
 phx_expert_prefill call per step.
---multi-kernel runs the pi0.5 decision on the captured multi-kernel graph
-instead of the persistent decision kernel.
+--multi-kernel runs the pi0.5 decision (bf16 or the 8-bit tier) on the
+captured multi-kernel graph instead of the persistent decision kernel.
 --timeline prints, instead of the benchmark line, the persistent kernel's
 critical path per phase of a layer-step (from its per-workgroup timeline).
 
@@ -235,8 +235,8 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=50, help="timed launches of the dominant kernel")
     ap.add_argument("--multi-kernel", action="store_true",
-                    help="pi05_expert_bf16 on the captured multi-kernel graph (2 + 6 NL launches per Euler step) "
-                         "instead of the persistent decision kernel")
+                    help="pi05_expert_bf16 or pi05_expert_w8a16 on the captured multi-kernel graph (2 + 6 NL "
+                         "launches per Euler step) instead of the persistent decision kernel")
     ap.add_argument("--timeline", action="store_true",
                     help="pi05_expert_bf16 on the persistent kernel with its phase timeline on: prints one JSON "
                          "line of per-phase critical-path microseconds instead of the benchmark line")
@@ -263,9 +263,9 @@ def main():
     from flow_matching_action_decision_amd.expert import Expert
     from flow_matching_action_decision_amd import binding
 
-    if args.multi_kernel and args.workload != WORKLOAD:
-        print("--multi-kernel applies to pi05_expert_bf16 (the other workloads have one execution path)",
-              file=sys.stderr)
+    if args.multi_kernel and args.workload != WORKLOAD and args.workload not in W8_WORKLOADS:
+        print("--multi-kernel applies to pi05_expert_bf16 and pi05_expert_w8a16 (the other workloads have one "
+              "execution path)", file=sys.stderr)
         sys.exit(2)
     if args.timeline:
         if args.workload != WORKLOAD or args.multi_kernel:
@@ -317,10 +317,12 @@ def main():
     # dominant kernel: duration of its launches, timed with HIP events on the
     # stream it runs on
     dom = ex.time_dominant_kernel(args.kernel_reps)
-    batch = name != WORKLOAD or mk  # the rollout batch runs the multi-kernel graph
-    kernel_hash = kernel_source_hash(("phx_kernels.hip", "phx_internal.h") + TOKEN_KERNEL_SOURCES if batch
-                                     else DECISION_KERNEL_SOURCES)
-    traffic = None if batch else measured_traffic(kernel_hash)
+    # the persistent decision kernel (bf16 or the 8-bit tier's instance), else the multi-kernel graph (the
+    # rollout batch, --multi-kernel); the committed counter record covers the bf16 instance only
+    persistent = dom["name"] == "decision_kernel"
+    kernel_hash = kernel_source_hash(DECISION_KERNEL_SOURCES if persistent
+                                     else ("phx_kernels.hip", "phx_internal.h") + TOKEN_KERNEL_SOURCES)
+    traffic = measured_traffic(kernel_hash) if persistent and name == WORKLOAD else None
     achieved = dom["bytes_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -355,8 +357,10 @@ def main():
     copy_gbs = measured_copy_gbs()
     lens = [int(L) for L in inp["lens"]]
     w8 = name in W8_WORKLOADS
+    batch = name in BATCH_WORKLOADS
     if w8:
-        metric = "ms/decision (pi0.5-shape, 18L x 10 steps, 8-bit weight tier) + % peak HBM GB/s, 1 GPU"
+        metric = ("ms/decision (pi0.5-shape, 18L x 10 steps, 8-bit weight tier" + (", multi-kernel graph" if mk else "")
+                  + ") + % peak HBM GB/s, 1 GPU")
     elif mk:
         metric = "ms/decision (pi0.5-shape, 18L x 10 steps, multi-kernel graph) + % peak HBM GB/s, 1 GPU"
     elif batch:
