@@ -865,7 +865,7 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
   f32x4* red = (f32x4*)red_take(c);
   red[c.wave * 64 + c.lane] = acc[0];
   cw_barrier(c);
-  release_ring(c, p0 + slots<W8>(32));
+  // the tiles are released after the attention phase (see the loop)
   if (c.wave == 0) {
     f32x4 s = red_sum(red, 1, 0, c.lane);
     if constexpr (W8) {
@@ -1225,7 +1225,7 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
 #pragma unroll
   for (int t = 0; t < O_NT; ++t) red[(c.wave * O_NT + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
-  release_ring(c, p0 + slots<W8>(8 * O_NT));
+  // the tiles are released after the all-reduce that follows (see the loop)
   if (c.wave < O_NT) {
     f32x4 s = red_sum(red, O_NT, c.wave, c.lane);  // wave t finishes n-tile t
     if constexpr (W8) {
@@ -1333,7 +1333,7 @@ __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
   cw_barrier(c);
-  release_ring(c, p0 + slots<W8>(32));
+  // the tiles are released after the all-reduce that follows (see the loop)
   if (c.wave < 2) {
     f32x4 s = red_sum(red, 2, c.wave, c.lane);
     if constexpr (W8) {
@@ -1651,23 +1651,45 @@ __global__ __launch_bounds__(THREADS, 1) void k_decide(Args a) {
     for (int l = 0; l < c.NL; ++l) {
       const int el = e0 + 1 + PHASES_PER_LAYER * l;
       ph_qkv<W8>(c, k, l);
+      // the rest of the previous layer's down-projection tiles (see below)
+      release_ring(c, (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer);
       if (tl) tl_mark(c, el);
       // two separate tests: as one if/else the compiler's uniformity analysis loses track of the
       // context's scalar fields after the join and cannot build the kernel
       if (attends && !action_chunk) ph_attn_prefix(c, k, l);
       if (action_chunk) ph_attn_action(c, k, l);
+      // The QKV tiles go back to the loaders only after the attention phase,
+      // whose action chunk polls keys and values at device scope: the tile
+      // loads they let through stream during the merge instead.
+      if (is_qkv(c)) release_ring(c, (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + slots<W8>(32));
       if (tl) tl_mark(c, el + 1);
       ph_merge(c, k, l);
       if (tl) tl_mark(c, el + 2);
       ph_o<W8>(c, k, l);
       if (tl) tl_mark(c, el + 3);
       ph_own<X_OP, X_N2, X_SS2>(c, k, 2 * l + 1, use_layer(c, k, l), use_layer(c, k, l), h);
+      // Likewise the out-projection tiles go back only after the all-reduce
+      // behind them, so that the tile loads they let through stream during
+      // XCD-local phases instead of crowding the all-reduce's device-scope
+      // polls.
+      release_ring(c, (unsigned)k * c.n_step + 2u + (unsigned)l * c.n_layer + c.o_o + slots<W8>(8u * O_NT));
       if (tl) tl_mark(c, el + 4);
       ph_gu<W8>(c, k, l);
       if (tl) tl_mark(c, el + 5);
       ph_down<W8>(c, k, l);
       if (tl) tl_mark(c, el + 6);
       ph_own<X_DP, X_N, X_SS>(c, k, 2 * (l + 1), use_layer(c, k, l), use_norm(c, k, l + 1), h);
+      {
+        // The down-projection tiles: after the all-reduce only as many as
+        // the next layer's attention tiles need to be loadable (its keys and
+        // values); the rest after the next layer's QKV phase, so that the
+        // loads of later tiles do not crowd the all-reduce's polls or the
+        // QKV phase.  The last layer hands back all of them.
+        const unsigned nxt = (unsigned)k * c.n_step + 2u + (unsigned)(l + 1) * c.n_layer;
+        const unsigned cur = nxt - slots<W8>(32);
+        const unsigned need = nxt + c.o_o > (unsigned)RING ? nxt + c.o_o - (unsigned)RING : 0u;
+        release_ring(c, l + 1 == c.NL ? nxt : (need < cur ? cur : (need > nxt ? nxt : need)));
+      }
       if (tl) tl_mark(c, el + 7);
     }
     ph_vel(c, k, x);
