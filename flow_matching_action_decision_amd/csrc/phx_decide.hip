@@ -1510,8 +1510,9 @@ __device__ inline u32x4 rsrc_words(const void* p, unsigned bytes) {
   return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
-constexpr unsigned LOAD_DEPTH = 12;  // tiles in flight per loader wave (24 measured 3% slower: the tile
-                                     // loads crowd the compute waves' exchange loads; 4 and 8 the same as 12)
+constexpr unsigned LOAD_DEPTH = 16;  // tiles in flight per loader wave (with the tiles handed back after
+                                     // the device-scope phases: 6 and 8 slower, 12 0.5% slower, 20-32 the
+                                     // same as 16)
 
 // Loader waves wait on LDS only: a global load in their wait loop would make
 // the next use of any loaded register wait for the whole batch of tile loads
@@ -1572,7 +1573,7 @@ __device__ __attribute__((always_inline)) inline void loader(Ctx& c, int q, cons
     // every tile but the last LOAD_DEPTH has landed; after a full publish
     // (above) the count only moves on once it passes what was published
     if (issued > LOAD_DEPTH + pub) {
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOAD_DEPTH) : "memory");
       pub = issued - LOAD_DEPTH;
       if (c.lane == 0) lds_store(&c.sh->ready[q], pub);
     }
