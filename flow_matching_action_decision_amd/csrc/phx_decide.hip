@@ -450,6 +450,13 @@ __device__ inline void wait_tiles(Ctx& c, unsigned p0, unsigned n) {
   cbar();
 }
 
+// Hands ring positions below `upto` back to the loader waves.  Callers keep
+// `upto` non-decreasing over a decision: the loaders only ever compare
+// against the latest value, so a smaller one would stall them until the next
+// release.  Every phase's tiles are released by the end of the phase that
+// follows the next device-scope phase at the latest (see the layer loop), and
+// a tile range is released only after the phase that reads it has passed its
+// barrier.
 __device__ inline void release_ring(Ctx& c, unsigned upto) {
   cbar();
   if (c.wave == 0 && c.lane == 0) lds_store(&c.sh->consumed, upto);
