@@ -498,71 +498,6 @@ __device__ inline u32x4 ring_read(const Ctx& c, unsigned slot) {
 // before it.
 __device__ inline void reads_issued() { asm volatile("" ::: "memory"); }
 
-// A phase's weight tiles come out of the ring before it polls for its
-// activation: ring_fetch reads the tile at stream position p0 + off(t, kk)
-// into w[kk][t], and those reads (and any wait for the loaders) overlap the
-// poll, so only the products are left once the activation has arrived.
-//
-// gemm_pairs: acc[t] = sum over k-tiles kk of W(t, kk) . (hi + lo)(kk), the
-// activation pairs of k-tile kk in loads v[2 kk], v[2 kk + 1].  The hi and
-// lo products go to accumulators of their own and the n-tiles are the inner
-// loop, so no MFMA waits for the result of the one before it (2 NT
-// independent chains); the two halves are added at the end.
-template <int NT, int KK, typename OF>
-__device__ __attribute__((always_inline)) inline void ring_fetch(const Ctx& c, unsigned p0, OF off,
-                                                                 u32x4 (&w)[KK][NT]) {
-  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) w[kk][t] = ring_read(c, ring_slot(s0, off(t, kk)));
-  reads_issued();
-}
-template <int NT, int KK>
-__device__ __attribute__((always_inline)) inline void gemm_pairs(const u32x4 (&w)[KK][NT], const u32x4* v,
-                                                                 f32x4 (&acc)[NT]) {
-  f32x4 ah[NT], al[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) ah[t] = al[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const bf16x8 bh = frag_hi(v[2 * kk], v[2 * kk + 1]);
-    const bf16x8 bl = frag_lo(v[2 * kk], v[2 * kk + 1]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const bf16x8 wt = __builtin_bit_cast(bf16x8, w[kk][t]);
-      ah[t] = mma32(wt, bh, ah[t]);
-      al[t] = mma32(wt, bl, al[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = ah[t] + al[t];
-}
-
-// acc[t] = sum over k-tiles kk of W(t, kk) . b(kk) for plain bf16 words (one
-// load v[kk] per k-tile); two chains per n-tile (even and odd k-tiles)
-template <int NT, int KK>
-__device__ __attribute__((always_inline)) inline void gemm_plain(const u32x4 (&w)[KK][NT], const u32x4* v,
-                                                                 f32x4 (&acc)[NT]) {
-  f32x4 ae[NT], ao[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) ae[t] = ao[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const bf16x8 b = frag_plain(v[kk]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const bf16x8 wt = __builtin_bit_cast(bf16x8, w[kk][t]);
-      if (kk & 1)
-        ao[t] = mma32(wt, b, ao[t]);
-      else
-        ae[t] = mma32(wt, b, ae[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = ae[t] + ao[t];
-}
-
 // 8-bit tier: a lane's 8 int8 codes of one tile (k order) as its bf16
 // fragment; exact, since |q| <= 127 fits bf16's significand (the float's
 // upper half is the bf16)
@@ -578,8 +513,78 @@ __device__ inline u32x4 i8_frag(const u32x2& q) {
   }
   return r;
 }
+
+// A phase's weight tiles come out of the ring before it polls for its
+// activation: ring_fetch reads the tile at stream position p0 + off(t, kk)
+// into w[kk][t], and those reads (and any wait for the loaders) overlap the
+// poll, so only the products are left once the activation has arrived.
+//
+// gemm_pairs: acc[t] = sum over k-tiles kk of W(t, kk) . (hi + lo)(kk), the
+// activation pairs of k-tile kk in loads v[2 kk], v[2 kk + 1].  The hi and
+// lo products go to accumulators of their own and the n-tiles are the inner
+// loop, so no MFMA waits for the result of the one before it (2 NT
+// independent chains); the two halves are added at the end.  In the 8-bit
+// tier (W8) w[kk][t] holds the tile's raw int8 codes (words 0, 1), widened
+// next to their products.
+template <int NT, int KK, typename OF>
+__device__ __attribute__((always_inline)) inline void ring_fetch(const Ctx& c, unsigned p0, OF off,
+                                                                 u32x4 (&w)[KK][NT]) {
+  const unsigned s0 = __builtin_amdgcn_readfirstlane(p0 % (unsigned)RING);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[kk][t] = ring_read(c, ring_slot(s0, off(t, kk)));
+  reads_issued();
+}
+template <int NT, int KK, bool W8 = false>
+__device__ __attribute__((always_inline)) inline void gemm_pairs(const u32x4 (&w)[KK][NT], const u32x4* v,
+                                                                 f32x4 (&acc)[NT]) {
+  f32x4 ah[NT], al[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ah[t] = al[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 bh = frag_hi(v[2 * kk], v[2 * kk + 1]);
+    const bf16x8 bl = frag_lo(v[2 * kk], v[2 * kk + 1]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bf16x8 wt = __builtin_bit_cast(bf16x8, W8 ? i8_frag(u32x2{w[kk][t][0], w[kk][t][1]}) : w[kk][t]);
+      ah[t] = mma32(wt, bh, ah[t]);
+      al[t] = mma32(wt, bl, al[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = ah[t] + al[t];
+}
+
+// acc[t] = sum over k-tiles kk of W(t, kk) . b(kk) for plain bf16 words (one
+// load v[kk] per k-tile); two chains per n-tile (even and odd k-tiles)
+template <int NT, int KK, bool W8 = false>
+__device__ __attribute__((always_inline)) inline void gemm_plain(const u32x4 (&w)[KK][NT], const u32x4* v,
+                                                                 f32x4 (&acc)[NT]) {
+  f32x4 ae[NT], ao[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ae[t] = ao[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 b = frag_plain(v[kk]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bf16x8 wt = __builtin_bit_cast(bf16x8, W8 ? i8_frag(u32x2{w[kk][t][0], w[kk][t][1]}) : w[kk][t]);
+      if (kk & 1)
+        ao[t] = mma32(wt, b, ao[t]);
+      else
+        ae[t] = mma32(wt, b, ae[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = ae[t] + ao[t];
+}
+
 // ring_fetch for int8 tiles: tile i of the phase's run sits in slot i / 2,
-// half i % 2 (512 bytes: 8 codes per lane)
+// half i % 2 (512 bytes: 8 codes per lane).  The codes stay raw (words 0, 1
+// of w[kk][t]) until the products widen them next to their MFMAs: widened
+// here, ahead of the poll, they held back the poll's first loads.
 template <int NT, int KK, typename OF>
 __device__ __attribute__((always_inline)) inline void ring_fetch_i8(const Ctx& c, unsigned p0, OF off,
                                                                     u32x4 (&w)[KK][NT]) {
@@ -596,7 +601,7 @@ __device__ __attribute__((always_inline)) inline void ring_fetch_i8(const Ctx& c
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[kk][t] = i8_frag(q[kk][t]);
+    for (int t = 0; t < NT; ++t) w[kk][t] = u32x4{q[kk][t][0], q[kk][t][1], 0u, 0u};
 }
 // a phase's tiles: bf16, or int8 in the 8-bit tier (n tiles take n / 2 slots)
 template <bool W8, int NT, int KK, typename OF>
@@ -868,7 +873,7 @@ __device__ __attribute__((always_inline)) inline void ph_qkv(Ctx& c, int k, int 
   u32x4 v[normed_loads<X_N>()];
   poll_normed<X_N, X_SS>(c, u, v);
   f32x4 acc[1];
-  gemm_plain<1, 8>(w, v, acc);
+  gemm_plain<1, 8, W8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
   red[c.wave * 64 + c.lane] = acc[0];
   cw_barrier(c);
@@ -1227,7 +1232,7 @@ __device__ __attribute__((always_inline)) inline void ph_o(Ctx& c, int k, int l)
               c.row < c.R);
   }
   f32x4 acc[O_NT];
-  gemm_pairs<O_NT, 2>(w, v, acc);
+  gemm_pairs<O_NT, 2, W8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < O_NT; ++t) red[(c.wave * O_NT + t) * 64 + c.lane] = acc[t];
@@ -1290,7 +1295,7 @@ __device__ __attribute__((always_inline)) inline void ph_gu(Ctx& c, int k, int l
   u32x4 v[normed_loads<X_N2>()];
   poll_normed<X_N2, X_SS2>(c, u, v);
   f32x4 acc[2];
-  gemm_pairs<2, 8>(w, v, acc);
+  gemm_pairs<2, 8, W8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
@@ -1335,7 +1340,7 @@ __device__ __attribute__((always_inline)) inline void ph_down(Ctx& c, int k, int
               c.row < c.R);
   }
   f32x4 acc[2];
-  gemm_pairs<2, 4>(w, v, acc);
+  gemm_pairs<2, 4, W8>(w, v, acc);
   f32x4* red = (f32x4*)red_take(c);
 #pragma unroll
   for (int t = 0; t < 2; ++t) red[(c.wave * 2 + t) * 64 + c.lane] = acc[t];
