@@ -1995,6 +1995,7 @@ __global__ void k_attn_tiles(const bf16* __restrict__ k, const bf16* __restrict_
 
 hipError_t launch_attn_tiles(const void* k, const void* v, void* kvt, int NL, int L, int n_chunks, hipStream_t s) {
   const size_t total = (size_t)NL * n_chunks * 64 * 512;
+  if (total == 0) return hipSuccess;  // capacity 0: no prefix chunk to tile
   const int blocks = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
   hipLaunchKernelGGL(k_attn_tiles, dim3(blocks), dim3(256), 0, s, (const bf16*)k, (const bf16*)v, (bf16*)kvt, NL, L,
                      n_chunks);

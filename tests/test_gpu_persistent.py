@@ -54,6 +54,18 @@ def test_largest_capacity(L):
     assert_close(outs[0], oracle_decide(cfg, inp), TOL_BF16, what=f"C=960 L={L}")
 
 
+@pytest.mark.parametrize("C,L", [(0, 0), (1, 1), (64, 64), (65, 33)])
+def test_small_capacities(C, L):
+    """No prefix chunk at all (capacity 0: the action rows attend to
+    themselves only), one chunk (capacities 1 and 64) and two chunks with the
+    second empty: the merge and the ring schedule with the fewest roles."""
+    cfg = pcfg(capacity=C, prefix_lens=[L])
+    inp, outs, nk = _run(cfg, repeats=2)
+    assert nk == 2
+    assert np.array_equal(outs[0], outs[1]), "replays must be bit-identical"
+    assert_close(outs[0], oracle_decide(cfg, inp), TOL_BF16, what=f"C={C} L={L}")
+
+
 @pytest.mark.parametrize("rows", [1, 7, 16])
 def test_row_counts(rows):
     cfg = pcfg(rows=rows, capacity=320, prefix_lens=[300])

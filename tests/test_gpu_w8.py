@@ -95,14 +95,16 @@ def test_w8_pi05_shape():
     assert nk == 2  # the persistent decision kernel (with its tag advance), int8 tiles in its ring
 
 
-@pytest.mark.parametrize("rows,L", [(10, 768), (3, 100), (16, 1)])
-def test_w8_persistent_and_graph(rows, L):
+@pytest.mark.parametrize("rows,L,C", [(10, 768, 768), (3, 100, 768), (16, 1, 768), (10, 960, 960)])
+def test_w8_persistent_and_graph(rows, L, C):
     """The tier on the persistent decision kernel (int8 tiles in its ring,
     column scales in its epilogues) and on the multi-kernel graph, at the
     pi0.5 width with 2 layers x 2 steps: each against the oracle on s * q, and
-    the two paths agree with each other to the same bar."""
-    cfg = phx_inputs.workload("pi05_expert_w8a16", id=81, layers=2, steps=2, dt=-0.5, rows=rows, prefix_lens=[L])
-    cfg["name"] = f"w8_persistent_r{rows}_L{L}"
+    the two paths agree with each other to the same bar.  Capacity 960 gives
+    some workgroups both a QKV and a prefix-attention role."""
+    cfg = phx_inputs.workload("pi05_expert_w8a16", id=81, layers=2, steps=2, dt=-0.5, rows=rows, capacity=C,
+                              prefix_lens=[L])
+    cfg["name"] = f"w8_persistent_r{rows}_L{L}_C{C}"
     say(f"case {cfg['name']}")
     inp = phx_inputs.make_inputs(cfg, 0)
     outs_p, nk_p = gpu_decide(cfg, inp, repeats=2)
