@@ -53,7 +53,7 @@ extern "C" {
 #define PHX_E_INVALID (-1)     /* NULL pointer or a bad argument value */
 #define PHX_E_VERSION (-2)     /* abi_version or struct_size does not match this library */
 #define PHX_E_SHAPE (-3)       /* outside the prepared plan: prefix_len > capacity, bad request index,
-                                  or a shape this build does not support */
+                                  or a shape the library does not support */
 #define PHX_E_STATE (-4)       /* a prerequisite is missing: decide before every request has a prefix */
 #define PHX_E_NOMEM (-5)       /* device allocation failed */
 #define PHX_E_HIP (-6)         /* a HIP runtime call failed; the message names it */

@@ -9,7 +9,7 @@ import numpy as np
 import oracle
 import phx_inputs
 
-# tolerances on the final actions (spec bar): bf16 weights and
+# tolerances on the final actions (the accuracy bar of the workloads): bf16 weights and
 # activations with fp32 accumulation vs the double-precision oracle
 TOL_BF16 = dict(max_abs=2e-2, rel_l2=1e-2)
 TOL_F32 = dict(max_abs=1e-4, rel_l2=1e-4)
