@@ -61,7 +61,9 @@ W8_WORKLOADS = ("pi05_expert_w8a16",)
 TOKEN_WORKLOADS = ("va_chunk_bf16", "wam_dit_bf16")
 PREFILL_WORKLOADS = ("prefix_prefill_bf16",)
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "traffic_pi05_expert_bf16.json")
+# HBM counter records of the decision kernel, per workload (its bf16 and 8-bit instances)
+TRAFFIC_FILES = {WORKLOAD: os.path.join(PROFILES, "traffic_pi05_expert_bf16.json"),
+                 "pi05_expert_w8a16": os.path.join(PROFILES, "traffic_pi05_expert_w8a16.json")}
 
 
 def log(msg: str):
@@ -135,11 +137,11 @@ def kernel_source_hash(files=DECISION_KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_hash: str):
+def measured_traffic(kernel_hash: str, name: str = WORKLOAD):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC_FILES[name]) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -318,11 +320,11 @@ def main():
     # stream it runs on
     dom = ex.time_dominant_kernel(args.kernel_reps)
     # the persistent decision kernel (bf16 or the 8-bit tier's instance), else the multi-kernel graph (the
-    # rollout batch, --multi-kernel); the committed counter record covers the bf16 instance only
+    # rollout batch, --multi-kernel); the committed counter records cover the persistent kernel
     persistent = dom["name"] == "decision_kernel"
     kernel_hash = kernel_source_hash(DECISION_KERNEL_SOURCES if persistent
                                      else ("phx_kernels.hip", "phx_internal.h") + TOKEN_KERNEL_SOURCES)
-    traffic = measured_traffic(kernel_hash) if persistent and name == WORKLOAD else None
+    traffic = measured_traffic(kernel_hash, name) if persistent and name in TRAFFIC_FILES else None
     achieved = dom["bytes_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
