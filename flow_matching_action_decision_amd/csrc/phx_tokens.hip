@@ -914,7 +914,8 @@ hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStrea
 // used.  Workgroups of one head run on one XCD so its keys and values stay in
 // that XCD's L2.
 constexpr int KB = 64;     // keys per block
-constexpr int AQ = 128;    // queries per workgroup
+constexpr int AQ = 128;    // queries per workgroup (four waves)
+constexpr int WIDE_ATTN_ROWS = 2048;  // from this many queries on, eight waves and 256 queries per workgroup
 constexpr int ASTAGE = 2;  // LDS stages
 
 template <int HD>
@@ -925,14 +926,16 @@ struct AttnShape {
   static constexpr int STAGE = 2 * KBYTES;          // K and V^T of one block
 };
 
-template <int HD>
-__global__ __launch_bounds__(256) void k_tattn(AttnT a) {
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void k_tattn(AttnT a) {
   using S = AttnShape<HD>;
   constexpr int NDS = S::NDS, NDT = S::NDT;
+  constexpr int QW = 32 * NW;                              // queries per workgroup
+  constexpr int KF = 4 * NDS / NW, VF = 2 * NDT / NW;      // K and V^T fragments each wave moves per block
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int nqb = (a.M + AQ - 1) / AQ;
+  const int nqb = (a.M + QW - 1) / QW;
   const int per_head = nqb * a.splits;
   const int bid = blockIdx.x;
   int h, r;
@@ -953,9 +956,9 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
   const int per = (nblk + a.splits - 1) / a.splits;
   const int b0 = split * per;
   int b1 = min(nblk, b0 + per);
-  if (a.causal) b1 = min(b1, (L + min(qb * AQ + AQ, a.M) - 1) / KB + 1);  // no key past the last query
+  if (a.causal) b1 = min(b1, (L + min(qb * QW + QW, a.M) - 1) / KB + 1);  // no key past the last query
   const int g4 = lane >> 4, qr = lane & 15;
-  const int q0 = qb * AQ + 32 * wave;
+  const int q0 = qb * QW + 32 * wave;
   // queries as B fragments of Q^T: dims 32 ds + 8 g4 + [0, 8) of query q0 + 16 qt + qr
   bf16x8 qf[2][NDS];
 #pragma unroll
@@ -975,22 +978,25 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
   const unsigned lds0 = (unsigned)(unsigned long long)((__attribute__((address_space(3))) unsigned char*)smem);
   const u32x4 rk = rsrc_words(a.kj, (unsigned)((size_t)a.R * kvd * 2));
   const u32x4 rv = rsrc_words(a.vt, (unsigned)((size_t)a.KVH * a.R * HD * 2));
-  // wave w moves the K fragments of key tile w (all dim steps) and value fragments w NDT/2 .. (w+1) NDT/2 - 1
-  unsigned vok[NDS];
+  // wave w moves K fragments KF w .. KF (w + 1) - 1 (fragment kt NDS + ds: key tile kt, dim step ds)
+  // and value fragments VF w .. VF (w + 1) - 1
+  unsigned vok[KF];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds)
-    vok[ds] = (unsigned)(((16 * wave + qr) * kvd + kvh * HD + 32 * ds + 8 * g4) * 2);
+  for (int f = 0; f < KF; ++f) {
+    const int kf = KF * wave + f, kt = kf / NDS, ds = kf % NDS;
+    vok[f] = (unsigned)(((16 * kt + qr) * kvd + kvh * HD + 32 * ds + 8 * g4) * 2);
+  }
   const unsigned vov = (unsigned)lane * 16u;
   const int nj = a.R / 32;
   auto issue = [&](int b) {
     const unsigned st = lds0 + (unsigned)((b % ASTAGE) * S::STAGE);
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-      dma_frag(st + (unsigned)((NDS * wave + ds) * 1024), vok[ds], rk, (unsigned)(b * KB * kvd * 2));
+    for (int f = 0; f < KF; ++f)
+      dma_frag(st + (unsigned)((KF * wave + f) * 1024), vok[f], rk, (unsigned)(b * KB * kvd * 2));
 #pragma unroll
-    for (int f = 0; f < NDT / 2; ++f)
-      dma_frag(st + (unsigned)(S::KBYTES + ((NDT / 2) * wave + f) * 1024), vov, rv,
-               (unsigned)((((size_t)kvh * nj + 2 * b) * NDT + (NDT / 2) * wave + f) * 1024));
+    for (int f = 0; f < VF; ++f)
+      dma_frag(st + (unsigned)(S::KBYTES + (VF * wave + f) * 1024), vov, rv,
+               (unsigned)((((size_t)kvh * nj + 2 * b) * NDT + VF * wave + f) * 1024));
   };
   const float sl2 = a.scale * 1.4426950408889634f;  // scores in base 2
   f32x4 oacc[2][NDT];
@@ -1118,23 +1124,36 @@ __global__ __launch_bounds__(256) void k_tattn(AttnT a) {
   }
 }
 
-hipError_t prepare_attention() {
-  hipError_t e = hipFuncSetAttribute((const void*)k_tattn<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+template <int NW>
+hipError_t prepare_attention_nw() {
+  hipError_t e = hipFuncSetAttribute((const void*)k_tattn<128, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      ASTAGE * AttnShape<128>::STAGE);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)k_tattn<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  return hipFuncSetAttribute((const void*)k_tattn<256, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
                              ASTAGE * AttnShape<256>::STAGE);
+}
+hipError_t prepare_attention() {
+  const hipError_t e = prepare_attention_nw<4>();
+  return e != hipSuccess ? e : prepare_attention_nw<8>();
 }
 
 hipError_t launch_tattn(const AttnT& a, hipStream_t s) {
   if (a.M < 1 || a.H % a.KVH || a.splits < 1 || a.R % KB || a.R < a.M) return hipErrorInvalidValue;
   if (a.hd != 128 && a.hd != 256) return hipErrorInvalidValue;
   if ((size_t)a.R * a.KVH * a.hd * 2 >= (1ull << 32)) return hipErrorInvalidValue;
-  const int blocks = ((a.M + AQ - 1) / AQ) * a.splits * a.H;
-  if (a.hd == 128)
-    hipLaunchKernelGGL(k_tattn<128>, dim3(blocks), dim3(256), ASTAGE * AttnShape<128>::STAGE, s, a);
+  // many queries: eight waves (256 queries) share each key/value block in LDS, which halves the blocks'
+  // reads from L2
+  const bool wide = a.M >= WIDE_ATTN_ROWS;
+  const int qw = wide ? 256 : AQ;
+  const int blocks = ((a.M + qw - 1) / qw) * a.splits * a.H;
+  if (a.hd == 128 && wide)
+    hipLaunchKernelGGL((k_tattn<128, 8>), dim3(blocks), dim3(512), ASTAGE * AttnShape<128>::STAGE, s, a);
+  else if (a.hd == 128)
+    hipLaunchKernelGGL((k_tattn<128, 4>), dim3(blocks), dim3(256), ASTAGE * AttnShape<128>::STAGE, s, a);
+  else if (wide)
+    hipLaunchKernelGGL((k_tattn<256, 8>), dim3(blocks), dim3(512), ASTAGE * AttnShape<256>::STAGE, s, a);
   else
-    hipLaunchKernelGGL(k_tattn<256>, dim3(blocks), dim3(256), ASTAGE * AttnShape<256>::STAGE, s, a);
+    hipLaunchKernelGGL((k_tattn<256, 4>), dim3(blocks), dim3(256), ASTAGE * AttnShape<256>::STAGE, s, a);
   return hipGetLastError();
 }
 
