@@ -940,7 +940,8 @@ int create_tokens(phx_expert* h, const char* sb, hipStream_t stream, size_t mod_
   h->R = (C + M + 63) / 64 * 64;
   const int R = h->R;
   // attention key splits: enough workgroups to cover the chip, at least two key blocks per split
-  const long long q_wgs = (long long)((M + 127) / 128) * H;
+  const int qw = tok::attn_queries_per_wg(M, c.head_dim);
+  const long long q_wgs = (long long)((M + qw - 1) / qw) * H;
   const int max_blocks = R / 64;
   h->splits = 1;
   while (q_wgs * h->splits < 256 && max_blocks / (h->splits * 2) >= 2) h->splits *= 2;

@@ -110,6 +110,9 @@ hipError_t launch_tnorm(int kind, const float* h, const float* scale, const floa
 hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStream_t s);
 // Lets the attention kernel use its LDS ring (call once per device, outside graph capture).
 hipError_t prepare_attention();
+// queries per attention workgroup for M query rows of head_dim hd: 256 (eight waves) from 2048 rows on at
+// head_dim 128, else 128 (four waves); the host sizes the key splits with it
+int attn_queries_per_wg(int M, int hd);
 hipError_t launch_tattn(const AttnT& a, hipStream_t s);
 // merges the key splits into the normalised bf16 output
 hipError_t launch_tcombine(const AttnT& a, hipStream_t s);

@@ -915,7 +915,7 @@ hipError_t launch_tcvt(const float* x, void* out, int M, int Mp, int D, hipStrea
 // that XCD's L2.
 constexpr int KB = 64;     // keys per block
 constexpr int AQ = 128;    // queries per workgroup (four waves)
-constexpr int WIDE_ATTN_ROWS = 2048;  // from this many queries on, eight waves and 256 queries per workgroup
+
 constexpr int ASTAGE = 2;  // LDS stages
 
 template <int HD>
@@ -1137,14 +1137,18 @@ hipError_t prepare_attention() {
   return e != hipSuccess ? e : prepare_attention_nw<8>();
 }
 
+// eight waves from 2048 queries on (the DiT-style step: 7.35 -> 7.20 ms); on the 256-row chunk the doubled
+// key splits and their combine cost more than the halved block reads (5.33 -> 5.69 ms)
+int attn_queries_per_wg(int M, int hd) { return M >= 2048 && hd == 128 ? 256 : AQ; }
+
 hipError_t launch_tattn(const AttnT& a, hipStream_t s) {
   if (a.M < 1 || a.H % a.KVH || a.splits < 1 || a.R % KB || a.R < a.M) return hipErrorInvalidValue;
   if (a.hd != 128 && a.hd != 256) return hipErrorInvalidValue;
   if ((size_t)a.R * a.KVH * a.hd * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   // many queries: eight waves (256 queries) share each key/value block in LDS, which halves the blocks'
   // reads from L2
-  const bool wide = a.M >= WIDE_ATTN_ROWS;
-  const int qw = wide ? 256 : AQ;
+  const int qw = attn_queries_per_wg(a.M, a.hd);
+  const bool wide = qw == 256;
   const int blocks = ((a.M + qw - 1) / qw) * a.splits * a.H;
   if (a.hd == 128 && wide)
     hipLaunchKernelGGL((k_tattn<128, 8>), dim3(blocks), dim3(512), ASTAGE * AttnShape<128>::STAGE, s, a);
